@@ -1,0 +1,185 @@
+/*
+ * wall_oracle.c -- plain fp64 CPU oracle for the Wall Attention forward pass.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  It shares no code,
+ * header, table or constant with the HIP implementation and must never be
+ * used as a fallback for it.
+ *
+ * What it computes (the plain definition, written out):
+ *
+ *   Wall Attention blog, section "Definition: Wall Attention", product form:
+ *       o_i = sum_j softmax_j( sum_n F_{ij,n} q_{i,n} k_{j,n} ) v_j,
+ *       F_{ij,n} = prod_{r=j+1..i} gate_{r,n}.
+ *   wall-attention-release README ("Usage: Training / prefill"): the API
+ *   argument g is the natural log of the gate (g = 0 is vanilla softmax
+ *   attention), so gate_{r,n} = exp(g_{r,n}); `scale` multiplies the whole
+ *   decayed dot product; HQ query heads share H key/value heads (HQ % H == 0).
+ *   Optional arguments from the same README:
+ *     g_scalar [B,T,HQ]  FoX-style additive gate: the logit of pair (i,j)
+ *                        gains sum_{r=j+1..i} g_scalar_r (the blog's FoX
+ *                        formula exp(q.k + log F_ij) in the section "Diagonal
+ *                        forget gates in infinite dimensions"), unscaled;
+ *     sink_bias [HQ]     one extra logit per query head with a zero value
+ *                        vector; it takes part in the normalisation only;
+ *     window_size W      key j is visible from query i iff 0 <= i-j < W;
+ *     cu_seqlens         packed sequences (B == 1); no pair crosses a
+ *                        sequence boundary.
+ *   lse is the natural-log normaliser of each row, sink included, so that
+ *   o_i = sum_j exp(logit_ij - lse_i) v_j.
+ *
+ * The loop below walks j from i down to the first visible key and keeps the
+ * running product F (one factor exp(g_{j+1,n}) per step) and the running FoX
+ * sum, so each logit is the literal product-form value.  Everything is fp64;
+ * the softmax is the two-pass max / sum form.  OpenMP splits the (token,
+ * head) rows; each row is computed independently and identically.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Returns 0 on success, a negative code on invalid arguments. */
+int wall_oracle_fwd(const double *q,        /* [B,T,HQ,K] */
+                    const double *k,        /* [B,T,H,K]  */
+                    const double *v,        /* [B,T,H,V]  */
+                    const double *g,        /* [B,T,HQ,K] natural-log gate */
+                    const double *g_scalar, /* [B,T,HQ] or NULL */
+                    const double *sink,     /* [HQ] or NULL */
+                    double *o,              /* [B,T,HQ,V] */
+                    double *lse,            /* [B,T,HQ] or NULL */
+                    int64_t B, int64_t T, int64_t HQ, int64_t H, int64_t K,
+                    int64_t V, double scale, int64_t window,
+                    const int64_t *cu_seqlens, /* [nseq+1] or NULL (then B rows of T) */
+                    int64_t nseq,
+                    const int64_t *rows, /* flat token ids b*T+t to compute, or NULL = all */
+                    int64_t nrows)
+{
+    if (!q || !k || !v || !g || !o) return -1;
+    if (B < 1 || T < 1 || HQ < 1 || H < 1 || K < 1 || V < 1) return -2;
+    if (HQ % H != 0) return -3;
+    if (cu_seqlens && (B != 1 || nseq < 1)) return -4;
+    if (cu_seqlens) {
+        if (cu_seqlens[0] != 0 || cu_seqlens[nseq] != T) return -5;
+        for (int64_t s = 0; s < nseq; ++s)
+            if (cu_seqlens[s + 1] < cu_seqlens[s]) return -5;
+    }
+    const int64_t group = HQ / H;
+    const int64_t ntok = B * T;
+    const int64_t nr = rows ? nrows : ntok;
+    if (rows)
+        for (int64_t r = 0; r < nrows; ++r)
+            if (rows[r] < 0 || rows[r] >= ntok) return -6;
+
+    int fail = 0;
+#pragma omp parallel
+    {
+        double *F = (double *)malloc(sizeof(double) * (size_t)K);
+        double *logit = (double *)malloc(sizeof(double) * (size_t)T);
+        double *acc = (double *)malloc(sizeof(double) * (size_t)V);
+        if (!F || !logit || !acc) {
+#pragma omp atomic write
+            fail = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1) collapse(2)
+            for (int64_t r = 0; r < nr; ++r) {
+                for (int64_t hq = 0; hq < HQ; ++hq) {
+                    const int64_t tok = rows ? rows[r] : r;
+                    const int64_t b = tok / T, i = tok % T;
+                    /* start of the sequence that holds token i */
+                    int64_t s0 = 0;
+                    if (cu_seqlens) {
+                        for (int64_t s = 0; s < nseq; ++s)
+                            if (cu_seqlens[s] <= i && i < cu_seqlens[s + 1]) s0 = cu_seqlens[s];
+                    }
+                    int64_t lo = s0;
+                    if (window > 0 && i - window + 1 > lo) lo = i - window + 1;
+                    const int64_t h = hq / group;
+                    const double *qi = q + ((b * T + i) * HQ + hq) * K;
+
+                    for (int64_t n = 0; n < K; ++n) F[n] = 1.0;
+                    double fox = 0.0;
+                    int64_t cnt = 0;
+                    for (int64_t j = i; j >= lo; --j) {
+                        if (j < i) {
+                            /* one more factor of the product over r = j+1 .. i */
+                            const double *gr = g + ((b * T + (j + 1)) * HQ + hq) * K;
+                            for (int64_t n = 0; n < K; ++n) F[n] *= exp(gr[n]);
+                            if (g_scalar) fox += g_scalar[(b * T + (j + 1)) * HQ + hq];
+                        }
+                        const double *kj = k + ((b * T + j) * H + h) * K;
+                        double dot = 0.0;
+                        for (int64_t n = 0; n < K; ++n) dot += F[n] * qi[n] * kj[n];
+                        logit[cnt++] = scale * dot + fox;
+                    }
+                    /* softmax over the visible keys (j = i, i-1, ..., lo) and the sink */
+                    double m = -INFINITY;
+                    for (int64_t c = 0; c < cnt; ++c) m = logit[c] > m ? logit[c] : m;
+                    if (sink && sink[hq] > m) m = sink[hq];
+                    double Z = 0.0;
+                    for (int64_t d = 0; d < V; ++d) acc[d] = 0.0;
+                    for (int64_t c = 0; c < cnt; ++c) {
+                        const int64_t j = i - c;
+                        const double p = exp(logit[c] - m);
+                        Z += p;
+                        const double *vj = v + ((b * T + j) * H + h) * V;
+                        for (int64_t d = 0; d < V; ++d) acc[d] += p * vj[d];
+                    }
+                    if (sink) Z += exp(sink[hq] - m); /* value vector of the sink is zero */
+                    double *oi = o + ((b * T + i) * HQ + hq) * V;
+                    for (int64_t d = 0; d < V; ++d) oi[d] = acc[d] / Z;
+                    if (lse) lse[(b * T + i) * HQ + hq] = m + log(Z);
+                }
+            }
+        }
+        free(F);
+        free(logit);
+        free(acc);
+    }
+    return fail ? -7 : 0;
+}
+
+/* Per-segment prefix sum along T, times `scale`:
+ *   out[b,t,c] = scale * sum_{u = s(t) .. t} x[b,u,c]
+ * where s(t) is the first token of the sequence holding t.  This is the
+ * log-space prefix P_t = sum_{u<=t} log gate_u of the blog's factored form
+ * ("Definition: Wall Attention"), expressed in log2 units when
+ * scale = 1/ln 2 as the README's decode example does.  Rows are [C]
+ * contiguous channels (C = HQ*K for g, HQ for g_scalar). */
+int wall_oracle_prefix_scan(const double *x, double *out, int64_t B, int64_t T, int64_t C,
+                            const int64_t *cu_seqlens, int64_t nseq, double scale)
+{
+    if (!x || !out || B < 1 || T < 1 || C < 1) return -1;
+    if (cu_seqlens && (B != 1 || nseq < 1)) return -4;
+#pragma omp parallel for collapse(2)
+    for (int64_t b = 0; b < B; ++b) {
+        for (int64_t c = 0; c < C; ++c) {
+            double run = 0.0;
+            int64_t s = 0;
+            for (int64_t t = 0; t < T; ++t) {
+                if (cu_seqlens) {
+                    while (s < nseq && t >= cu_seqlens[s + 1]) ++s;
+                    if (t == cu_seqlens[s]) run = 0.0;
+                } else if (t == 0) {
+                    run = 0.0;
+                }
+                run += x[(b * T + t) * C + c];
+                out[(b * T + t) * C + c] = scale * run;
+            }
+        }
+    }
+    return 0;
+}
+
+int wall_oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,92 @@
+"""The oracle's pins must catch plausible mistakes.
+
+Each case below copies wall_oracle.c to a temporary directory, plants one
+mistake in the copy (a dropped term, a wrong sign, a shifted index, a wrong
+head map, ...), builds it with gcc and runs every pin of test_oracle_pins.py
+against the mutant.  At least one pin has to fail.  CPU only; the committed
+oracle is never modified.
+"""
+
+import ctypes
+import inspect
+import os
+import subprocess
+
+import pytest
+
+import oracle
+from tests import test_oracle_pins as pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "wall_oracle.c")
+
+MUTANTS = {
+    "gate_index_j_instead_of_j_plus_1": (
+        "const double *gr = g + ((b * T + (j + 1)) * HQ + hq) * K;",
+        "const double *gr = g + ((b * T + j) * HQ + hq) * K;"),
+    "gate_sign": ("F[n] *= exp(gr[n]);", "F[n] *= exp(-gr[n]);"),
+    "sink_dropped_from_normaliser": ("if (sink) Z += exp(sink[hq] - m);", ";"),
+    "gqa_head_map_modulo": ("const int64_t h = hq / group;", "const int64_t h = hq % H;"),
+    "window_off_by_one": ("i - window + 1 > lo) lo = i - window + 1;",
+                          "i - window > lo) lo = i - window;"),
+    "scale_applied_to_fox_bias": ("logit[cnt++] = scale * dot + fox;",
+                                  "logit[cnt++] = scale * (dot + fox);"),
+    "fox_index_j": ("fox += g_scalar[(b * T + (j + 1)) * HQ + hq];",
+                    "fox += g_scalar[(b * T + j) * HQ + hq];"),
+    "sequence_start_ignored": ("if (cu_seqlens[s] <= i && i < cu_seqlens[s + 1]) s0 = cu_seqlens[s];",
+                               "(void)s;"),
+    "value_of_wrong_key": ("const double *vj = v + ((b * T + j) * H + h) * V;",
+                           "const double *vj = v + ((b * T + i) * H + h) * V;"),
+    "lse_without_max": ("lse[(b * T + i) * HQ + hq] = m + log(Z);",
+                        "lse[(b * T + i) * HQ + hq] = log(Z);"),
+    "query_key_swapped_heads": ("const double *kj = k + ((b * T + j) * H + h) * K;",
+                                "const double *kj = k + ((b * T + j) * H + (hq % H)) * K;"),
+    "scan_scale_dropped": ("out[(b * T + t) * C + c] = scale * run;",
+                           "out[(b * T + t) * C + c] = run;"),
+    "scan_no_reset_at_sequence_start": ("if (t == cu_seqlens[s]) run = 0.0;", ";"),
+}
+
+
+def _pin_calls():
+    """Every (name, zero-arg callable(oracle_module)) pin in test_oracle_pins."""
+    calls = []
+    for name, fn in inspect.getmembers(pins, inspect.isfunction):
+        if not name.startswith("test_"):
+            continue
+        marks = getattr(fn, "pytestmark", [])
+        params = [m for m in marks if m.name == "parametrize"]
+        if params:
+            argname, values = params[0].args
+            for val in values:
+                calls.append((f"{name}[{val}]", lambda mod, fn=fn, a=argname, v=val: fn(mod, **{a: v})))
+        else:
+            calls.append((name, lambda mod, fn=fn: fn(mod)))
+    return calls
+
+
+@pytest.mark.parametrize("mutant", sorted(MUTANTS))
+def test_pins_catch_mutant(mutant, tmp_path, monkeypatch):
+    old, new = MUTANTS[mutant]
+    text = open(SRC).read()
+    assert text.count(old) == 1, f"mutation anchor not found once: {old!r}"
+    mpath = tmp_path / "wall_oracle_mutant.c"
+    mpath.write_text(text.replace(old, new))
+    lib = tmp_path / "libmutant.so"
+    subprocess.run(["gcc", "-O1", "-fopenmp", "-shared", "-fPIC", "-std=c11", "-o", str(lib),
+                    str(mpath), "-lm"], check=True, capture_output=True)
+    monkeypatch.setattr(oracle, "_lib", oracle._bind(str(lib)))
+    caught = []
+    for name, call in _pin_calls():
+        try:
+            call(oracle)
+        except (AssertionError, ValueError):
+            caught.append(name)
+    assert caught, f"no pin caught the planted mistake {mutant}"
+
+
+def test_unmutated_copy_passes_every_pin(tmp_path, monkeypatch):
+    lib = tmp_path / "libcopy.so"
+    subprocess.run(["gcc", "-O1", "-fopenmp", "-shared", "-fPIC", "-std=c11", "-o", str(lib),
+                    SRC, "-lm"], check=True, capture_output=True)
+    monkeypatch.setattr(oracle, "_lib", oracle._bind(str(lib)))
+    for name, call in _pin_calls():
+        call(oracle)
