@@ -1,0 +1,258 @@
+"""ctypes binding of libwall.so (declared in include/wall.h).
+
+Argument marshalling only: torch supplies device memory and the current
+stream; every step of the computation runs in the library's HIP kernels.
+There is no fallback of any kind -- if the library is missing or the tensors
+are not on a GPU, the call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libwall.so")
+
+WALL_F32, WALL_BF16 = 0, 1
+WALL_OK, WALL_ERR_INVALID_ARG, WALL_ERR_UNSUPPORTED, WALL_ERR_LAUNCH = 0, 1, 2, 3
+
+#: every symbol include/wall.h declares
+EXPORTS = (
+    "wall_status_string", "wall_version",
+    "wall_prefix_scan_workspace_size", "wall_prefix_scan",
+    "wall_attn_fwd_workspace_size", "wall_attn_fwd",
+    "wall_attn_fwd_prepare", "wall_attn_fwd_run",
+)
+
+_lib = None
+
+
+class WallError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)}")
+
+
+def lib() -> ctypes.CDLL:
+    """Load libwall.so (built by ``python -m channel_decay_softmax_amd.build``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is missing: build it with `python -m channel_decay_softmax_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I, S, F = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+        E = ctypes.c_int
+        L.wall_status_string.argtypes = [E]
+        L.wall_status_string.restype = ctypes.c_char_p
+        L.wall_version.argtypes = []
+        L.wall_version.restype = ctypes.c_int
+        L.wall_prefix_scan_workspace_size.argtypes = [I, I, I]
+        L.wall_prefix_scan_workspace_size.restype = S
+        L.wall_prefix_scan.argtypes = [P, E, P, I, I, I, P, I, F, P, S, P]
+        L.wall_prefix_scan.restype = E
+        L.wall_attn_fwd_workspace_size.argtypes = [E, I, I, I, I, I, I, I]
+        L.wall_attn_fwd_workspace_size.restype = S
+        L.wall_attn_fwd.argtypes = [P, P, P, E, P, P, P, P, P, I, I, I, I, I, I, F, I, P, I, I,
+                                    P, S, P]
+        L.wall_attn_fwd.restype = E
+        L.wall_attn_fwd_prepare.argtypes = [P, P, E, P, I, I, I, I, I, I, P, I, P, S, P]
+        L.wall_attn_fwd_prepare.restype = E
+        L.wall_attn_fwd_run.argtypes = [P, E, P, P, P, P, P, I, I, I, I, I, I, F, I, P, I, I, P, S,
+                                        P]
+        L.wall_attn_fwd_run.restype = E
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().wall_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != WALL_OK:
+        raise WallError(status, where)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return WALL_BF16
+    if t.dtype == torch.float32:
+        return WALL_F32
+    raise TypeError(f"unsupported dtype {t.dtype}: Wall Attention takes bfloat16 or float32")
+
+
+def _on_gpu(*ts: Optional[torch.Tensor]) -> torch.device:
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("Wall Attention runs on the GPU only: every tensor must be on a HIP device")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("all tensors must be on the same device")
+    return dev
+
+
+def _stream(dev: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _dense(t: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
+    if t is None:
+        return None
+    if not t.is_contiguous() or t.data_ptr() % 16:
+        t = t.contiguous().clone() if t.is_contiguous() else t.contiguous()
+    return t
+
+
+def prefix_scan_workspace_size(B: int, T: int, C: int) -> int:
+    return int(lib().wall_prefix_scan_workspace_size(B, T, C))
+
+
+def attn_fwd_workspace_size(dtype: torch.dtype, B: int, T: int, HQ: int, H: int, K: int, V: int,
+                            num_seqs: int = 0) -> int:
+    d = WALL_BF16 if dtype == torch.bfloat16 else WALL_F32
+    return int(lib().wall_attn_fwd_workspace_size(d, B, T, HQ, H, K, V, num_seqs))
+
+
+def wall_prefix_scan(x: torch.Tensor, cu_seqlens: Optional[torch.Tensor] = None,
+                     scale: float = 1.0 / math.log(2.0), out: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """out[b,t,...] = scale * sum of x[b,u,...] from the start of t's sequence to t (float32).
+
+    x is [B, T, ...] bfloat16/float32; cu_seqlens (int32 [N+1], B == 1) packs sequences."""
+    dev = _on_gpu(x, cu_seqlens, out, workspace)
+    x = _dense(x)
+    B, T = x.shape[0], x.shape[1]
+    C = x.numel() // (B * T)
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.float32, device=dev)
+    nbytes = prefix_scan_workspace_size(B, T, C)
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    cu = None if cu_seqlens is None else _dense(cu_seqlens.to(torch.int32))
+    nseq = 0 if cu is None else cu.numel() - 1
+    _check(lib().wall_prefix_scan(_ptr(x), _dtype(x), _ptr(out), B, T, C, _ptr(cu), nseq,
+                                  float(scale), _ptr(workspace), workspace.numel(), _stream(dev)),
+           "wall_prefix_scan")
+    return out
+
+
+def wall_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, P: torch.Tensor,
+                  G: Optional[torch.Tensor] = None, sink_bias: Optional[torch.Tensor] = None,
+                  scale: Optional[float] = None, window_size: Optional[int] = None,
+                  cu_seqlens: Optional[torch.Tensor] = None, max_seqlen: Optional[int] = None,
+                  out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                  return_lse: bool = True, workspace: Optional[torch.Tensor] = None
+                  ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Fused causal forward from the log2 prefixes P (and G).  Returns (o, lse)."""
+    dev = _on_gpu(q, k, v, P, G, sink_bias, cu_seqlens, out, lse, workspace)
+    q, k, v, P, G = _dense(q), _dense(k), _dense(v), _dense(P), _dense(G)
+    B, T, HQ, K = q.shape
+    H, V = k.shape[2], v.shape[3]
+    if k.shape != (B, T, H, K) or v.shape != (B, T, H, V) or P.shape != (B, T, HQ, K):
+        raise ValueError("shapes must be q [B,T,HQ,K], k [B,T,H,K], v [B,T,H,V], P [B,T,HQ,K]")
+    if not (q.dtype == k.dtype == v.dtype) or P.dtype != torch.float32:
+        raise TypeError("q, k, v share one dtype; P is float32")
+    if G is not None and (G.shape != (B, T, HQ) or G.dtype != torch.float32):
+        raise ValueError("G must be float32 [B,T,HQ]")
+    if sink_bias is not None:
+        sink_bias = _dense(sink_bias.to(torch.float32))
+        if sink_bias.shape != (HQ,):
+            raise ValueError("sink_bias must be [HQ]")
+    if scale is None:
+        scale = K ** -0.5
+    cu = None if cu_seqlens is None else _dense(cu_seqlens.to(torch.int32))
+    nseq = 0 if cu is None else cu.numel() - 1
+    if cu is not None and max_seqlen is None:
+        max_seqlen = int((cu[1:] - cu[:-1]).max().item())
+    if out is None:
+        out = torch.empty((B, T, HQ, V), dtype=q.dtype, device=dev)
+    if lse is None and return_lse:
+        lse = torch.empty((B, T, HQ), dtype=torch.float32, device=dev)
+    nbytes = attn_fwd_workspace_size(q.dtype, B, T, HQ, H, K, V, nseq)
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    _check(lib().wall_attn_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _dtype(q), _ptr(P), _ptr(G), _ptr(sink_bias), _ptr(out),
+        _ptr(lse), B, T, HQ, H, K, V, float(scale), int(window_size or 0), _ptr(cu), nseq,
+        int(max_seqlen or 0), _ptr(workspace), workspace.numel(), _stream(dev)), "wall_attn_fwd")
+    return out, lse
+
+
+def check_cu_seqlens(cu_seqlens: torch.Tensor, B: int, T: int) -> int:
+    """Validate packed-sequence offsets on the host (one device-to-host copy).
+    Returns the longest sequence length."""
+    if B != 1:
+        raise ValueError("cu_seqlens requires B == 1")
+    cu = cu_seqlens.detach().to("cpu", torch.int64)
+    if cu.ndim != 1 or cu.numel() < 2:
+        raise ValueError("cu_seqlens must be 1-D with at least two entries")
+    if int(cu[0]) != 0 or int(cu[-1]) != T or bool((cu[1:] < cu[:-1]).any()):
+        raise ValueError("cu_seqlens must start at 0, be non-decreasing and end at T")
+    return int((cu[1:] - cu[:-1]).max())
+
+
+def wall_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+              scale: Optional[float] = None, g_scalar: Optional[torch.Tensor] = None,
+              sink_bias: Optional[torch.Tensor] = None, window_size: Optional[int] = None,
+              cu_seqlens: Optional[torch.Tensor] = None, return_lse: bool = False):
+    """Wall Attention forward, with the README's signature (wall_attn usage,
+    "Training / prefill"): q [B,T,HQ,K], k [B,T,H,K], v [B,T,H,V], g [B,T,HQ,K]
+    natural-log decay (g = 0 is softmax attention), scale default K**-0.5;
+    optional g_scalar [B,T,HQ], sink_bias [HQ], window_size, cu_seqlens (B == 1).
+    Runs wall_prefix_scan (g -> P, g_scalar -> G) and wall_attn_fwd on the
+    current stream.  Returns o [B,T,HQ,V] (and lse [B,T,HQ] if asked)."""
+    _on_gpu(q, k, v, g, g_scalar, sink_bias, cu_seqlens)
+    B, T = q.shape[:2]
+    max_seqlen = None
+    if cu_seqlens is not None:
+        max_seqlen = check_cu_seqlens(cu_seqlens, B, T)
+    P = wall_prefix_scan(g, cu_seqlens)
+    G = None if g_scalar is None else wall_prefix_scan(g_scalar, cu_seqlens)
+    o, lse = wall_attn_fwd(q, k, v, P, G, sink_bias, scale, window_size, cu_seqlens, max_seqlen,
+                           return_lse=return_lse)
+    return (o, lse) if return_lse else o
+
+
+def wall_attn_fwd_prepare(k: torch.Tensor, v: torch.Tensor, P: torch.Tensor, HQ: int,
+                          workspace: torch.Tensor, cu_seqlens: Optional[torch.Tensor] = None) -> None:
+    """Stage 1 of wall_attn_fwd: build the anchored key cache and value tiles in ``workspace``.
+    All tensors must already be dense and on one device (no copies are made here)."""
+    dev = _on_gpu(k, v, P, workspace, cu_seqlens)
+    B, T, H, K = k.shape
+    V = v.shape[3]
+    nseq = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
+    _check(lib().wall_attn_fwd_prepare(_ptr(k), _ptr(v), _dtype(k), _ptr(P), B, T, HQ, H, K, V,
+                                       _ptr(cu_seqlens), nseq, _ptr(workspace), workspace.numel(),
+                                       _stream(dev)), "wall_attn_fwd_prepare")
+
+
+def wall_attn_fwd_run(q: torch.Tensor, P: torch.Tensor, H: int, V: int, workspace: torch.Tensor,
+                      out: torch.Tensor, lse: Optional[torch.Tensor] = None,
+                      G: Optional[torch.Tensor] = None, sink_bias: Optional[torch.Tensor] = None,
+                      scale: Optional[float] = None, window_size: Optional[int] = None,
+                      cu_seqlens: Optional[torch.Tensor] = None,
+                      max_seqlen: Optional[int] = None) -> None:
+    """Stage 2 of wall_attn_fwd: the fused kernel, reading the prepared ``workspace``.
+    All tensors must already be dense and on one device (no copies are made here)."""
+    dev = _on_gpu(q, P, workspace, out, lse, G, sink_bias, cu_seqlens)
+    B, T, HQ, K = q.shape
+    nseq = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
+    _check(lib().wall_attn_fwd_run(
+        _ptr(q), _dtype(q), _ptr(P), _ptr(G), _ptr(sink_bias), _ptr(out), _ptr(lse), B, T, HQ, H,
+        K, V, float(K ** -0.5 if scale is None else scale), int(window_size or 0),
+        _ptr(cu_seqlens), nseq, int(max_seqlen or 0), _ptr(workspace), workspace.numel(),
+        _stream(dev)), "wall_attn_fwd_run")

@@ -1,0 +1,190 @@
+// wall_api.cpp -- the extern "C" boundary of the Wall Attention forward library.
+//
+// Every argument check below runs before the first HIP call, so invalid
+// calls return their status without touching the device (and can be tested
+// on a machine without a GPU).  The entry points then enqueue kernels on the
+// caller's stream and return; nothing is allocated or synchronised here.
+#include "wall.h"
+
+#include "wall_common.h"
+
+using namespace wall;
+
+namespace {
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+wall_status_t launched(hipError_t e) {
+    if (e != hipSuccess) return WALL_ERR_LAUNCH;
+    return hipGetLastError() == hipSuccess ? WALL_OK : WALL_ERR_LAUNCH;
+}
+
+int64_t esize_of(wall_dtype_t d) { return d == WALL_BF16 ? 2 : (d == WALL_F32 ? 4 : 0); }
+
+}  // namespace
+
+extern "C" {
+
+const char *wall_status_string(wall_status_t s) {
+    switch (s) {
+        case WALL_OK: return "WALL_OK";
+        case WALL_ERR_INVALID_ARG: return "WALL_ERR_INVALID_ARG";
+        case WALL_ERR_UNSUPPORTED: return "WALL_ERR_UNSUPPORTED";
+        case WALL_ERR_LAUNCH: return "WALL_ERR_LAUNCH";
+    }
+    return "WALL_ERR_UNKNOWN";
+}
+
+int wall_version(void) { return 100; }  // 0.1.0
+
+size_t wall_prefix_scan_workspace_size(int64_t B, int64_t T, int64_t C) {
+    if (B < 1 || T < 1 || C < 1) return 0;
+    return scan_layout(B, T, C).total;
+}
+
+wall_status_t wall_prefix_scan(const void *x, wall_dtype_t x_dtype, float *out, int64_t B,
+                               int64_t T, int64_t C, const int32_t *cu_seqlens, int64_t num_seqs,
+                               float scale, void *workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+    if (!x || !out || !workspace) return WALL_ERR_INVALID_ARG;
+    if (B < 1 || T < 1 || C < 1) return WALL_ERR_INVALID_ARG;
+    if (B * T > INT32_MAX || B * T * C > (int64_t)1 << 40) return WALL_ERR_INVALID_ARG;
+    if (cu_seqlens && (B != 1 || num_seqs < 1 || num_seqs > T)) return WALL_ERR_INVALID_ARG;
+    if (x_dtype != WALL_BF16 && x_dtype != WALL_F32) return WALL_ERR_UNSUPPORTED;
+    if (!aligned(x, 16) || !aligned(out, 16) || !aligned(workspace, 256) ||
+        (cu_seqlens && !aligned(cu_seqlens, 4)))
+        return WALL_ERR_INVALID_ARG;
+    if (workspace_bytes < scan_layout(B, T, C).total) return WALL_ERR_INVALID_ARG;
+    if ((const void *)out == x) return WALL_ERR_INVALID_ARG;
+    return launched(launch_scan(x, x_dtype == WALL_BF16, out, B, T, C,
+                                cu_seqlens, cu_seqlens ? num_seqs : 0, scale, workspace, stream));
+}
+
+size_t wall_attn_fwd_workspace_size(wall_dtype_t dtype, int64_t B, int64_t T, int64_t HQ,
+                                    int64_t H, int64_t K, int64_t V, int64_t num_seqs) {
+    const int64_t es = esize_of(dtype);
+    if (!es || B < 1 || T < 1 || HQ < 1 || H < 1 || K < 1 || V < 1) return 0;
+    return fwd_layout(es, B, T, HQ, H, K, V, num_seqs).total;
+}
+
+namespace {
+
+struct FwdShape {
+    int64_t B, T, HQ, H, K, V, nseq, maxlen;
+};
+
+// Checks shared by the forward entry points; returns WALL_OK or the status to report.
+wall_status_t check_fwd(wall_dtype_t dtype, const FwdShape &s, const int32_t *cu,
+                        int64_t num_seqs, int64_t max_seqlen, const void *workspace,
+                        size_t workspace_bytes) {
+    if (!workspace) return WALL_ERR_INVALID_ARG;
+    if (s.B < 1 || s.T < 1 || s.HQ < 1 || s.H < 1 || s.K < 1 || s.V < 1) return WALL_ERR_INVALID_ARG;
+    if (s.HQ % s.H != 0) return WALL_ERR_INVALID_ARG;
+    if (s.B * s.T > INT32_MAX / 2 || s.B * s.T * s.HQ * (s.K > s.V ? s.K : s.V) > ((int64_t)1 << 40))
+        return WALL_ERR_INVALID_ARG;
+    if (cu && (s.B != 1 || num_seqs < 1 || num_seqs > s.T || max_seqlen < 1 || max_seqlen > s.T))
+        return WALL_ERR_INVALID_ARG;
+    if (dtype != WALL_BF16 && dtype != WALL_F32) return WALL_ERR_UNSUPPORTED;
+    if ((s.K != 64 && s.K != 128) || (s.V != 64 && s.V != 128)) return WALL_ERR_UNSUPPORTED;
+    if (cu && !aligned(cu, 4)) return WALL_ERR_INVALID_ARG;
+    if (!aligned(workspace, 256)) return WALL_ERR_INVALID_ARG;
+    const FwdLayout L = fwd_layout(esize_of(dtype), s.B, s.T, s.HQ, s.H, s.K, s.V, cu ? num_seqs : 0);
+    if (workspace_bytes < L.total) return WALL_ERR_INVALID_ARG;
+    return WALL_OK;
+}
+
+wall_status_t enqueue_prepare(const void *k, const void *v, wall_dtype_t dtype, const float *P,
+                              const FwdShape &s, const int32_t *cu, void *workspace,
+                              hipStream_t stream) {
+    const FwdLayout L = fwd_layout(esize_of(dtype), s.B, s.T, s.HQ, s.H, s.K, s.V, s.nseq);
+    char *ws = static_cast<char *>(workspace);
+    SegInfo *seg = reinterpret_cast<SegInfo *>(ws + L.off_seg);
+    if (launch_seg_table(seg, cu, L.nseg, s.B, s.T, stream) != hipSuccess) return WALL_ERR_LAUNCH;
+    PrepArgs pa{k, v, P, seg, reinterpret_cast<float *>(ws + L.off_anchor), ws + L.off_kt,
+                ws + L.off_vt, L.nseg, L.tiles, s.HQ, s.H, s.K, s.V};
+    return launched(launch_prep(pa, dtype == WALL_BF16, stream));
+}
+
+wall_status_t enqueue_run(const void *q, wall_dtype_t dtype, const float *P, const float *G,
+                          const float *sink_bias, void *o, float *lse, const FwdShape &s,
+                          float scale, int64_t window_size, const void *workspace,
+                          hipStream_t stream) {
+    const FwdLayout L = fwd_layout(esize_of(dtype), s.B, s.T, s.HQ, s.H, s.K, s.V, s.nseq);
+    const char *ws = static_cast<const char *>(workspace);
+    FwdArgs fa{};
+    fa.q = q;
+    fa.P = P;
+    fa.G = G;
+    fa.sink = sink_bias;
+    fa.kt = ws + L.off_kt;
+    fa.vt = ws + L.off_vt;
+    fa.anchor = reinterpret_cast<const float *>(ws + L.off_anchor);
+    fa.seg = reinterpret_cast<const SegInfo *>(ws + L.off_seg);
+    fa.o = o;
+    fa.lse = lse;
+    fa.nseg = (int32_t)L.nseg;
+    fa.max_tiles = (int32_t)cdiv(s.maxlen, TILE);
+    fa.HQ = (int32_t)s.HQ;
+    fa.H = (int32_t)s.H;
+    fa.K = (int32_t)s.K;
+    fa.V = (int32_t)s.V;
+    fa.window = window_size > 0 ? (int32_t)(window_size > s.T ? s.T : window_size) : 0;
+    fa.qscale = scale * LOG2E;
+    return launched(dtype == WALL_BF16 ? launch_fwd_bf16(fa, stream) : launch_fwd_f32(fa, stream));
+}
+
+}  // namespace
+
+wall_status_t wall_attn_fwd_prepare(const void *k, const void *v, wall_dtype_t dtype,
+                                    const float *P, int64_t B, int64_t T, int64_t HQ, int64_t H,
+                                    int64_t K, int64_t V, const int32_t *cu_seqlens,
+                                    int64_t num_seqs, void *workspace, size_t workspace_bytes,
+                                    hipStream_t stream) {
+    if (!k || !v || !P) return WALL_ERR_INVALID_ARG;
+    const FwdShape s{B, T, HQ, H, K, V, cu_seqlens ? num_seqs : 0, T};
+    // max_seqlen plays no part in the preparation: pass T to the shared checks
+    const wall_status_t st = check_fwd(dtype, s, cu_seqlens, num_seqs, T, workspace, workspace_bytes);
+    if (st != WALL_OK) return st;
+    const void *ptrs[] = {k, v, P};
+    for (const void *p : ptrs)
+        if (!aligned(p, 16)) return WALL_ERR_INVALID_ARG;
+    return enqueue_prepare(k, v, dtype, P, s, cu_seqlens, workspace, stream);
+}
+
+wall_status_t wall_attn_fwd_run(const void *q, wall_dtype_t dtype, const float *P, const float *G,
+                                const float *sink_bias, void *o, float *lse, int64_t B, int64_t T,
+                                int64_t HQ, int64_t H, int64_t K, int64_t V, float scale,
+                                int64_t window_size, const int32_t *cu_seqlens, int64_t num_seqs,
+                                int64_t max_seqlen, const void *workspace, size_t workspace_bytes,
+                                hipStream_t stream) {
+    if (!q || !P || !o) return WALL_ERR_INVALID_ARG;
+    const FwdShape s{B, T, HQ, H, K, V, cu_seqlens ? num_seqs : 0, cu_seqlens ? max_seqlen : T};
+    const wall_status_t st =
+        check_fwd(dtype, s, cu_seqlens, num_seqs, max_seqlen, workspace, workspace_bytes);
+    if (st != WALL_OK) return st;
+    const void *ptrs[] = {q, P, o, G, sink_bias, lse};
+    for (const void *p : ptrs)
+        if (p && !aligned(p, 16)) return WALL_ERR_INVALID_ARG;
+    return enqueue_run(q, dtype, P, G, sink_bias, o, lse, s, scale, window_size, workspace, stream);
+}
+
+wall_status_t wall_attn_fwd(const void *q, const void *k, const void *v, wall_dtype_t dtype,
+                            const float *P, const float *G, const float *sink_bias, void *o,
+                            float *lse, int64_t B, int64_t T, int64_t HQ, int64_t H, int64_t K,
+                            int64_t V, float scale, int64_t window_size,
+                            const int32_t *cu_seqlens, int64_t num_seqs, int64_t max_seqlen,
+                            void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!q || !k || !v || !P || !o) return WALL_ERR_INVALID_ARG;
+    const FwdShape s{B, T, HQ, H, K, V, cu_seqlens ? num_seqs : 0, cu_seqlens ? max_seqlen : T};
+    const wall_status_t st =
+        check_fwd(dtype, s, cu_seqlens, num_seqs, max_seqlen, workspace, workspace_bytes);
+    if (st != WALL_OK) return st;
+    const void *ptrs[] = {q, k, v, P, o, G, sink_bias, lse};
+    for (const void *p : ptrs)
+        if (p && !aligned(p, 16)) return WALL_ERR_INVALID_ARG;
+    const wall_status_t sp = enqueue_prepare(k, v, dtype, P, s, cu_seqlens, workspace, stream);
+    if (sp != WALL_OK) return sp;
+    return enqueue_run(q, dtype, P, G, sink_bias, o, lse, s, scale, window_size, workspace, stream);
+}
+
+}  // extern "C"

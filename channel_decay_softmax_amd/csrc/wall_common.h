@@ -1,0 +1,134 @@
+// wall_common.h -- types, tile geometry and workspace layout shared by the
+// HIP sources of the Wall Attention forward library (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace wall {
+
+// ----------------------------------------------------------------- vector types
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(8))) float f32x8;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+
+// ----------------------------------------------------------------- geometry
+// Rows of one key / query tile.  Anchors are chosen per TILE rows, per query
+// head and per channel, so this is also the anchor granularity.
+constexpr int TILE = 128;
+// Row of the tile whose floored prefix is the anchor: the middle row keeps
+// both exp2 factors of every pair inside the tile within half the tile's
+// prefix range.
+constexpr int ANCHOR_ROW = 64;
+// Rows per chunk of the two-level prefix scan.
+constexpr int SCAN_CHUNK = 128;
+
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+
+// Exponent clamp for the anchored factors: exp2 of anything below -150 is 0
+// in float32, and 126 keeps every factor finite.
+constexpr float EXP2_LO = -150.0f;
+constexpr float EXP2_HI = 126.0f;
+
+// One packed sequence (or one batch row).
+struct SegInfo {
+    int32_t start;      // first flat token row
+    int32_t len;        // rows
+    int32_t tile_base;  // index of the sequence's first tile in the tiled workspace
+    int32_t pad;
+};
+
+inline __host__ __device__ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline __host__ __device__ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// ----------------------------------------------------------------- workspace layouts
+// Forward workspace: segment table | anchors | rescaled key tiles | transposed value tiles.
+struct FwdLayout {
+    int64_t nseg;        // sequences (num_seqs with packing, else B)
+    int64_t tiles;       // upper bound on sum_s ceil(len_s / TILE)
+    size_t off_seg, off_anchor, off_kt, off_vt, total;
+};
+
+inline FwdLayout fwd_layout(int64_t esize, int64_t B, int64_t T, int64_t HQ, int64_t H,
+                            int64_t K, int64_t V, int64_t num_seqs) {
+    FwdLayout L;
+    L.nseg = num_seqs > 0 ? num_seqs : B;
+    L.tiles = cdiv(B * T, TILE) + L.nseg;
+    size_t o = 0;
+    L.off_seg = o;
+    o = align_up(o + sizeof(SegInfo) * (size_t)L.nseg, 256);
+    L.off_anchor = o;
+    o = align_up(o + sizeof(float) * (size_t)(L.tiles * HQ * K), 256);
+    L.off_kt = o;
+    o = align_up(o + (size_t)esize * (size_t)(L.tiles * HQ * TILE * K), 256);
+    L.off_vt = o;
+    o = align_up(o + (size_t)esize * (size_t)(L.tiles * H * V * TILE), 256);
+    L.total = o;
+    return L;
+}
+
+// Scan workspace: chunk tail sums | exclusive chunk carries | chunk flags.
+struct ScanLayout {
+    int64_t nchunk;
+    size_t off_sum, off_carry, off_flag, total;
+};
+
+inline ScanLayout scan_layout(int64_t B, int64_t T, int64_t C) {
+    ScanLayout L;
+    L.nchunk = cdiv(B * T, SCAN_CHUNK);
+    size_t o = 0;
+    L.off_sum = o;
+    o = align_up(o + sizeof(float) * (size_t)(L.nchunk * C), 256);
+    L.off_carry = o;
+    o = align_up(o + sizeof(float) * (size_t)(L.nchunk * C), 256);
+    L.off_flag = o;
+    o = align_up(o + sizeof(int32_t) * (size_t)L.nchunk, 256);
+    L.total = o;
+    return L;
+}
+
+// ----------------------------------------------------------------- launchers (internal)
+// Each returns hipSuccess or the launch error; arguments were validated by the C API.
+hipError_t launch_seg_table(SegInfo *seg, const int32_t *cu, int64_t nseg, int64_t B, int64_t T,
+                            hipStream_t st);
+
+hipError_t launch_scan(const void *x, bool x_bf16, float *out, int64_t B, int64_t T, int64_t C,
+                       const int32_t *cu, int64_t nseq, float scale, void *ws, hipStream_t st);
+
+struct PrepArgs {
+    const void *k;     // [rows, H, K]
+    const void *v;     // [rows, H, V]
+    const float *P;    // [rows, HQ, K]
+    const SegInfo *seg;
+    float *anchor;     // [tiles, HQ, K]
+    void *kt;          // [tiles, HQ, TILE, K]
+    void *vt;          // [tiles, H, V, TILE]
+    int64_t nseg, tiles, HQ, H, K, V;
+};
+hipError_t launch_prep(const PrepArgs &a, bool bf16, hipStream_t st);
+
+struct FwdArgs {
+    const void *q;          // [rows, HQ, K]
+    const float *P;         // [rows, HQ, K]
+    const float *G;         // [rows, HQ] or null
+    const float *sink;      // [HQ] or null
+    const void *kt;         // [tiles, HQ, TILE, K]
+    const void *vt;         // [tiles, H, V, TILE]
+    const float *anchor;    // [tiles, HQ, K]
+    const SegInfo *seg;     // [nseg]
+    void *o;                // [rows, HQ, V]
+    float *lse;             // [rows, HQ] or null
+    int32_t nseg, max_tiles, HQ, H, K, V;
+    int32_t window;         // <= 0: none
+    float qscale;           // scale * log2(e)
+};
+hipError_t launch_fwd_bf16(const FwdArgs &a, hipStream_t st);
+hipError_t launch_fwd_f32(const FwdArgs &a, hipStream_t st);
+
+}  // namespace wall

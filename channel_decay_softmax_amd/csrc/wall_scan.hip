@@ -1,0 +1,242 @@
+// wall_scan.hip -- per-sequence prefix sum along T (the log2 prefix P of the
+// Wall Attention blog's factored form, "Definition: Wall Attention", built
+// in log2 units as the README's decode example does with a scaled cumsum).
+//
+// x is viewed as [rows, C] with rows = B*T.  Three kernels, float32 throughout:
+//   A  chunk_sums : per 128-row chunk and channel, the sum since the chunk's
+//                   last sequence start (or the whole chunk), plus a flag
+//                   telling whether the chunk holds a start;
+//   B  chunk_carry: a segmented exclusive scan of those sums over the chunks
+//                   (a flag resets the running value), one thread per channel
+//                   group and chunk range;
+//   C  finish     : each 32-row group re-sums its rows, takes the carry of its
+//                   chunk plus the groups before it, and writes scale * prefix.
+// Every load and store is coalesced along the channel axis (4 channels per
+// thread when C % 4 == 0).
+#include "wall_common.h"
+
+namespace wall {
+namespace {
+
+constexpr int ROWS_PER_GROUP = 32;              // rows per thread
+constexpr int GROUPS = SCAN_CHUNK / ROWS_PER_GROUP;  // 4 row groups per chunk
+constexpr int CV = 64;                          // channel vectors per block (one wave)
+constexpr int CARRY_GROUPS = 16;                // chunk ranges per block in kernel B
+
+template <typename Tin, int VEC>
+struct Loader;
+
+template <>
+struct Loader<float, 4> {
+    static __device__ inline f32x4 load(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
+};
+template <>
+struct Loader<float, 1> {
+    static __device__ inline f32x4 load(const float *p) { return f32x4{p[0], 0.f, 0.f, 0.f}; }
+};
+template <>
+struct Loader<__bf16, 4> {
+    static __device__ inline f32x4 load(const __bf16 *p) {
+        const uint2 u = *reinterpret_cast<const uint2 *>(p);
+        return f32x4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                     __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u)};
+    }
+};
+template <>
+struct Loader<__bf16, 1> {
+    static __device__ inline f32x4 load(const __bf16 *p) {
+        const uint16_t u = *reinterpret_cast<const uint16_t *>(p);
+        return f32x4{__uint_as_float((uint32_t)u << 16), 0.f, 0.f, 0.f};
+    }
+};
+
+// Bit i of word w is set when row row0 + 32*w + i starts a sequence.
+__device__ inline void start_mask(uint32_t *smask, int64_t row0, int64_t rows, int T,
+                                  const int32_t *cu, int nseq) {
+    const int w = threadIdx.x;
+    if (w >= GROUPS) return;
+    const int64_t a = row0 + ROWS_PER_GROUP * w, b = a + ROWS_PER_GROUP;
+    uint32_t m = 0;
+    if (!cu) {
+        int64_t first = (a + T - 1) / T * T;  // first multiple of T at or after a
+        for (int64_t r = first; r < b && r < rows; r += T) m |= 1u << (r - a);
+    } else {
+        int lo = 0, hi = nseq;  // first s with cu[s] >= a
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (cu[mid] < a) lo = mid + 1; else hi = mid;
+        }
+        for (int s = lo; s < nseq && cu[s] < b; ++s)
+            if (cu[s] < rows) m |= 1u << (cu[s] - a);
+    }
+    smask[w] = m;
+}
+
+template <typename Tin, int VEC>
+__global__ __launch_bounds__(256) void scan_chunk_sums(const Tin *__restrict__ x,
+                                                       float *__restrict__ csum,
+                                                       int32_t *__restrict__ cflag, int64_t rows,
+                                                       int64_t C, const int32_t *cu, int nseq,
+                                                       int T) {
+    __shared__ uint32_t smask[GROUPS];
+    __shared__ f32x4 ssum[GROUPS][CV];
+    __shared__ int sflag[GROUPS];
+    const int chunk = blockIdx.x;
+    const int64_t row0 = (int64_t)chunk * SCAN_CHUNK;
+    start_mask(smask, row0, rows, T, cu, nseq);
+    __syncthreads();
+    const int rg = threadIdx.x / CV, cv = threadIdx.x % CV;
+    const int64_t ch = ((int64_t)blockIdx.y * CV + cv) * VEC;
+    const uint32_t mask = smask[rg];
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    if (ch < C) {
+        const int64_t r0 = row0 + ROWS_PER_GROUP * rg;
+#pragma unroll 8
+        for (int i = 0; i < ROWS_PER_GROUP; ++i) {
+            if (r0 + i >= rows) break;
+            if ((mask >> i) & 1u) s = f32x4{0.f, 0.f, 0.f, 0.f};
+            s += Loader<Tin, VEC>::load(x + (r0 + i) * C + ch);
+        }
+    }
+    ssum[rg][cv] = s;
+    if (cv == 0) sflag[rg] = mask != 0;
+    __syncthreads();
+    if (rg == 0 && ch < C) {
+        f32x4 S = ssum[0][cv];
+        int F = sflag[0];
+        for (int g = 1; g < GROUPS; ++g) {
+            S = sflag[g] ? ssum[g][cv] : S + ssum[g][cv];
+            F |= sflag[g];
+        }
+        for (int e = 0; e < VEC; ++e) csum[(int64_t)chunk * C + ch + e] = S[e];
+        if (blockIdx.y == 0 && cv == 0) cflag[chunk] = F;
+    }
+}
+
+// Exclusive segmented scan of the chunk sums: carry[c] is the running sum
+// (since the last sequence start) just before chunk c begins.
+template <int VEC>
+__global__ __launch_bounds__(1024) void scan_chunk_carry(const float *__restrict__ csum,
+                                                         const int32_t *__restrict__ cflag,
+                                                         float *__restrict__ carry, int64_t nchunk,
+                                                         int64_t C) {
+    __shared__ f32x4 gS[CARRY_GROUPS][CV];
+    __shared__ int gF[CARRY_GROUPS];
+    const int gi = threadIdx.x / CV, cv = threadIdx.x % CV;
+    const int64_t ch = ((int64_t)blockIdx.x * CV + cv) * VEC;
+    const int64_t per = (nchunk + CARRY_GROUPS - 1) / CARRY_GROUPS;
+    const int64_t c0 = gi * per, c1 = c0 + per < nchunk ? c0 + per : nchunk;
+    f32x4 S = {0.f, 0.f, 0.f, 0.f};
+    int F = 0;
+    if (ch < C) {
+        for (int64_t c = c0; c < c1; ++c) {
+            f32x4 v = {0.f, 0.f, 0.f, 0.f};
+            for (int e = 0; e < VEC; ++e) v[e] = csum[c * C + ch + e];
+            const int f = cflag[c];
+            S = f ? v : S + v;
+            F |= f;
+        }
+    } else {
+        for (int64_t c = c0; c < c1; ++c) F |= cflag[c];
+    }
+    gS[gi][cv] = S;
+    if (cv == 0) gF[gi] = F;
+    __syncthreads();
+    if (ch >= C) return;
+    f32x4 run = {0.f, 0.f, 0.f, 0.f};
+    for (int g = 0; g < gi; ++g) run = gF[g] ? gS[g][cv] : run + gS[g][cv];
+    for (int64_t c = c0; c < c1; ++c) {
+        f32x4 v = {0.f, 0.f, 0.f, 0.f};
+        for (int e = 0; e < VEC; ++e) {
+            carry[c * C + ch + e] = run[e];
+            v[e] = csum[c * C + ch + e];
+        }
+        run = cflag[c] ? v : run + v;
+    }
+}
+
+template <typename Tin, int VEC>
+__global__ __launch_bounds__(256) void scan_finish(const Tin *__restrict__ x,
+                                                   const float *__restrict__ carry,
+                                                   float *__restrict__ out, int64_t rows, int64_t C,
+                                                   const int32_t *cu, int nseq, int T, float scale) {
+    __shared__ uint32_t smask[GROUPS];
+    __shared__ f32x4 ssum[GROUPS][CV];
+    __shared__ int sflag[GROUPS];
+    const int chunk = blockIdx.x;
+    const int64_t row0 = (int64_t)chunk * SCAN_CHUNK;
+    start_mask(smask, row0, rows, T, cu, nseq);
+    __syncthreads();
+    const int rg = threadIdx.x / CV, cv = threadIdx.x % CV;
+    const int64_t ch = ((int64_t)blockIdx.y * CV + cv) * VEC;
+    const uint32_t mask = smask[rg];
+    const int64_t r0 = row0 + ROWS_PER_GROUP * rg;
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    if (ch < C) {
+#pragma unroll 8
+        for (int i = 0; i < ROWS_PER_GROUP; ++i) {
+            if (r0 + i >= rows) break;
+            if ((mask >> i) & 1u) s = f32x4{0.f, 0.f, 0.f, 0.f};
+            s += Loader<Tin, VEC>::load(x + (r0 + i) * C + ch);
+        }
+    }
+    ssum[rg][cv] = s;
+    if (cv == 0) sflag[rg] = mask != 0;
+    __syncthreads();
+    if (ch >= C) return;
+    f32x4 run;
+    for (int e = 0; e < VEC; ++e) run[e] = carry[(int64_t)chunk * C + ch + e];
+    for (int g = 0; g < rg; ++g) run = sflag[g] ? ssum[g][cv] : run + ssum[g][cv];
+#pragma unroll 8
+    for (int i = 0; i < ROWS_PER_GROUP; ++i) {
+        if (r0 + i >= rows) break;
+        if ((mask >> i) & 1u) run = f32x4{0.f, 0.f, 0.f, 0.f};
+        run += Loader<Tin, VEC>::load(x + (r0 + i) * C + ch);
+        float *dst = out + (r0 + i) * C + ch;
+        if (VEC == 4) {
+            *reinterpret_cast<f32x4 *>(dst) = run * scale;
+        } else {
+            dst[0] = run[0] * scale;
+        }
+    }
+}
+
+template <typename Tin, int VEC>
+hipError_t run_scan(const Tin *x, float *out, int64_t B, int64_t T, int64_t C, const int32_t *cu,
+                    int64_t nseq, float scale, void *ws, hipStream_t st) {
+    const ScanLayout L = scan_layout(B, T, C);
+    char *w = static_cast<char *>(ws);
+    float *csum = reinterpret_cast<float *>(w + L.off_sum);
+    float *carry = reinterpret_cast<float *>(w + L.off_carry);
+    int32_t *cflag = reinterpret_cast<int32_t *>(w + L.off_flag);
+    const int64_t rows = B * T;
+    const dim3 grid((unsigned)L.nchunk, (unsigned)cdiv(C, (int64_t)CV * VEC));
+    hipLaunchKernelGGL((scan_chunk_sums<Tin, VEC>), grid, dim3(256), 0, st, x, csum, cflag, rows, C,
+                       cu, (int)nseq, (int)T);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((scan_chunk_carry<VEC>), dim3((unsigned)cdiv(C, (int64_t)CV * VEC)),
+                       dim3(CV * CARRY_GROUPS), 0, st, csum, cflag, carry, L.nchunk, C);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((scan_finish<Tin, VEC>), grid, dim3(256), 0, st, x, carry, out, rows, C, cu,
+                       (int)nseq, (int)T, scale);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_scan(const void *x, bool x_bf16, float *out, int64_t B, int64_t T, int64_t C,
+                       const int32_t *cu, int64_t nseq, float scale, void *ws, hipStream_t st) {
+    const bool vec = (C % 4) == 0;
+    if (x_bf16) {
+        const __bf16 *xb = static_cast<const __bf16 *>(x);
+        return vec ? run_scan<__bf16, 4>(xb, out, B, T, C, cu, nseq, scale, ws, st)
+                   : run_scan<__bf16, 1>(xb, out, B, T, C, cu, nseq, scale, ws, st);
+    }
+    const float *xf = static_cast<const float *>(x);
+    return vec ? run_scan<float, 4>(xf, out, B, T, C, cu, nseq, scale, ws, st)
+               : run_scan<float, 1>(xf, out, B, T, C, cu, nseq, scale, ws, st);
+}
+
+}  // namespace wall

@@ -1,0 +1,193 @@
+/*
+ * wall.h -- C ABI of the MI355X (gfx950) Wall Attention forward library.
+ *
+ * Wall Attention (wall-attention-release README, introduction; Wall Attention
+ * blog, "Definition: Wall Attention") is softmax attention whose QK inner
+ * product carries a per-channel, per-timestep decay accumulated between the
+ * two positions:
+ *
+ *   o_i = sum_{j<=i} softmax_j( scale * sum_n exp2(P_{i,n} - P_{j,n}) q_{i,n} k_{j,n}
+ *                               + G_i - G_j ) v_j,
+ *   P_t = (1/ln 2) * sum_{u<=t} g_u      (log2-unit prefix of the log gate g),
+ *
+ * g = 0 giving vanilla softmax attention.  The library exports the two steps
+ * of the README's prefill path: the prefix scan (its decode example builds P
+ * with a global cumsum scaled by 1/ln 2) and the fused causal forward.
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor argument is a caller-owned, dense, row-major DEVICE pointer
+ *     on the current HIP device, aligned to 16 bytes.  The library keeps no
+ *     pointer after a call returns, allocates nothing, never synchronises and
+ *     never aborts.
+ *   - Work is enqueued on `stream` (0 = the legacy default stream) and runs
+ *     asynchronously; outputs are valid once the stream reaches that point.
+ *   - Token-major layouts: a token row is (b, t) with flat id b*T + t; with
+ *     cu_seqlens (B == 1) the flat id is the packed position t.
+ *   - Argument checks run before any HIP call, so an invalid call returns its
+ *     status without touching the device.  Contents of device buffers (e.g.
+ *     cu_seqlens) cannot be checked without a synchronisation and are the
+ *     caller's responsibility; they are listed under each call.
+ *   - Two calls that share a workspace or an output buffer must be ordered on
+ *     one stream; calls on different streams with separate buffers are
+ *     independent.
+ */
+#ifndef WALL_H
+#define WALL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    WALL_F32 = 0,  /* IEEE binary32 */
+    WALL_BF16 = 1, /* bfloat16 (1-8-7) */
+} wall_dtype_t;
+
+typedef enum {
+    WALL_OK = 0,
+    WALL_ERR_INVALID_ARG = 1, /* null required pointer, bad size, bad alignment, short workspace */
+    WALL_ERR_UNSUPPORTED = 2, /* valid but not implemented: a head size or dtype with no kernel */
+    WALL_ERR_LAUNCH = 3,      /* a kernel launch failed; hipGetLastError() is reported */
+} wall_status_t;
+
+/* Human-readable name of a status (static storage, never NULL). */
+const char *wall_status_string(wall_status_t s);
+
+/* Library version as 10000*major + 100*minor + patch. */
+int wall_version(void);
+
+/* ------------------------------------------------------------------ prefix scan
+ *
+ * out[r, c] = scale * sum_{u = s(r) .. r} x[u, c]
+ *
+ * over token rows r of x viewed as [B*T, C], where s(r) is the first row of
+ * the sequence that holds r (row b*T for batch b, or cu_seqlens[k] with
+ * packing).  With x = g [B,T,HQ,K] (C = HQ*K) and scale = 1/ln 2 this is the
+ * per-channel log2 prefix P of the Wall Attention blog's factored form
+ * ("Definition: Wall Attention": P_t = sum_{u<=t} log gate_u) in the units
+ * of the README's decode example.  With x = g_scalar [B,T,HQ] (C = HQ) it
+ * is the prefix G of the FoX-style scalar gate.
+ *
+ *   x            [B, T, C] in x_dtype (WALL_BF16 or WALL_F32)
+ *   out          [B, T, C] float32; may not alias x
+ *   cu_seqlens   NULL, or int32 [num_seqs + 1] on the device with B == 1,
+ *                cu[0] = 0, non-decreasing, cu[num_seqs] = T (empty
+ *                sequences allowed).  Caller-checked contents.
+ *   workspace    device scratch of at least
+ *                wall_prefix_scan_workspace_size(B, T, C) bytes, 256-byte
+ *                aligned; its contents on entry are ignored.
+ * Accumulation is float32 along T (two-level: 128-row chunks, then a
+ * segmented scan of chunk sums), so |error| grows like eps32 * |out|.
+ * Errors: INVALID_ARG for a null x/out/workspace, B, T or C < 1, cu_seqlens
+ * with B != 1 or num_seqs < 1, misalignment, a short workspace;
+ * UNSUPPORTED for another dtype; LAUNCH on a failed launch. */
+size_t wall_prefix_scan_workspace_size(int64_t B, int64_t T, int64_t C);
+
+wall_status_t wall_prefix_scan(const void *x, wall_dtype_t x_dtype, float *out,
+                               int64_t B, int64_t T, int64_t C,
+                               const int32_t *cu_seqlens, int64_t num_seqs,
+                               float scale,
+                               void *workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
+/* ------------------------------------------------------------------ fused forward
+ *
+ * The causal Wall Attention forward of the README's `wall_attn` (usage
+ * "Training / prefill"), forward half only, with its optional arguments:
+ *
+ *   logit_ij (log2 units) = scale*log2(e) * sum_n exp2(P_in - P_jn) q_in k_jn
+ *                           + (G_i - G_j)
+ *   visible(i, j) = j <= i, same sequence, and (window_size <= 0 or i-j < window_size)
+ *   sink: one extra logit sink_bias[hq] (natural log) with a zero value
+ *   o_i  = sum_j 2^(logit_ij - M_i) v_j / Z_i   (M_i the row max, sink included)
+ *   lse_i = ln 2 * (M_i + log2 Z_i)              (natural log, sink included)
+ *
+ * GQA: HQ query heads share H key/value heads, HQ % H == 0, query head hq
+ * reads key/value head hq / (HQ / H) (README features list).  The decay P and
+ * the scalar prefix G are per QUERY head.
+ *
+ *   q          [B, T, HQ, K]  dtype
+ *   k          [B, T, H,  K]  dtype
+ *   v          [B, T, H,  V]  dtype
+ *   P          [B, T, HQ, K]  float32, log2 prefix of g (wall_prefix_scan with
+ *                             scale 1/ln 2 and the same cu_seqlens)
+ *   G          NULL or [B, T, HQ] float32, log2 prefix of g_scalar
+ *   sink_bias  NULL or [HQ] float32, natural-log logit of the sink
+ *   o          [B, T, HQ, V]  dtype (written)
+ *   lse        NULL or [B, T, HQ] float32 (written)
+ *   scale      multiplies the decayed dot product (the README passes K**-0.5)
+ *   window_size  <= 0: no window; else W keys including the query itself
+ *   cu_seqlens NULL, or as for wall_prefix_scan (B == 1); max_seqlen must be
+ *              >= the longest sequence (unused without cu_seqlens).
+ *   workspace  device scratch of at least wall_attn_fwd_workspace_size(...)
+ *              bytes, 256-byte aligned; contents on entry are ignored.  It
+ *              holds the decay-rescaled key cache, the transposed values and
+ *              the per-tile anchors of this call.
+ * Numerics: exp2(P_i - P_j) is split at an integer per-tile, per-channel
+ * anchor R (the blog's "per-tile anchors", section "Fast training and
+ * inference") as exp2(P_i - R) * exp2(R - P_j), so no factor leaves the
+ * float range while the per-channel change of P within one 64-row half of a
+ * 128-row key tile stays below about 120 (log2 units).  bf16 inputs use bf16
+ * MFMA operands with float32 accumulation and a float32 online softmax;
+ * float32 inputs are computed in float32 throughout.
+ * Errors: INVALID_ARG for a null required pointer, a size < 1, HQ % H != 0,
+ * cu_seqlens with B != 1 or num_seqs < 1 or max_seqlen < 1, misalignment, a
+ * short workspace; UNSUPPORTED for K or V not in {64, 128} or another dtype;
+ * LAUNCH on a failed launch. */
+size_t wall_attn_fwd_workspace_size(wall_dtype_t dtype, int64_t B, int64_t T,
+                                    int64_t HQ, int64_t H, int64_t K, int64_t V,
+                                    int64_t num_seqs);
+
+wall_status_t wall_attn_fwd(const void *q, const void *k, const void *v, wall_dtype_t dtype,
+                            const float *P, const float *G, const float *sink_bias,
+                            void *o, float *lse,
+                            int64_t B, int64_t T, int64_t HQ, int64_t H, int64_t K, int64_t V,
+                            float scale, int64_t window_size,
+                            const int32_t *cu_seqlens, int64_t num_seqs, int64_t max_seqlen,
+                            void *workspace, size_t workspace_bytes,
+                            hipStream_t stream);
+
+/* ------------------------------------------------------------------ the forward in two stages
+ *
+ * wall_attn_fwd is exactly wall_attn_fwd_prepare followed by
+ * wall_attn_fwd_run on the same stream and workspace.  The split lets a
+ * caller time or reuse the stages:
+ *
+ * wall_attn_fwd_prepare folds the decay into the keys once per 128-row tile
+ * and query head -- the prefill counterpart of the README's
+ * build_wall_kv_cache (k_tilde[j] = k[j] * exp2(R_c - P[j]) with a per-chunk
+ * anchor R_c) -- and stores, in `workspace`, the sequence table, the
+ * anchors, the rescaled keys and the value tiles.  Arguments mean what they
+ * mean for wall_attn_fwd (no q, G, sink, window or max_seqlen here).
+ *
+ * wall_attn_fwd_run reads that workspace (unchanged since a prepare call
+ * with the same k, v, P, shapes and cu_seqlens, ordered before it on the
+ * stream) together with q, P, G and sink_bias, and writes o and lse.
+ * `workspace` is read only.
+ * Errors are those of wall_attn_fwd for the arguments each stage takes. */
+wall_status_t wall_attn_fwd_prepare(const void *k, const void *v, wall_dtype_t dtype,
+                                    const float *P,
+                                    int64_t B, int64_t T, int64_t HQ, int64_t H, int64_t K, int64_t V,
+                                    const int32_t *cu_seqlens, int64_t num_seqs,
+                                    void *workspace, size_t workspace_bytes,
+                                    hipStream_t stream);
+
+wall_status_t wall_attn_fwd_run(const void *q, wall_dtype_t dtype,
+                                const float *P, const float *G, const float *sink_bias,
+                                void *o, float *lse,
+                                int64_t B, int64_t T, int64_t HQ, int64_t H, int64_t K, int64_t V,
+                                float scale, int64_t window_size,
+                                const int32_t *cu_seqlens, int64_t num_seqs, int64_t max_seqlen,
+                                const void *workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WALL_H */

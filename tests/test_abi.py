@@ -1,0 +1,127 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol
+include/wall.h declares, and rejects invalid arguments before any HIP call
+(so these calls never touch a device)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import channel_decay_softmax_amd as wall
+from channel_decay_softmax_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "wall.h")
+
+OK, INVALID, UNSUPPORTED = wall.WALL_OK, wall.WALL_ERR_INVALID_ARG, wall.WALL_ERR_UNSUPPORTED
+FAKE = 1 << 20  # a non-null, 256-byte aligned address that is never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(wall_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_binding_exports():
+    assert declared_functions() == sorted(B.EXPORTS)
+
+
+def test_library_loads_and_exports_every_symbol():
+    L = wall.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    assert L.wall_version() == 100
+    assert wall.status_string(OK) == "WALL_OK"
+    assert wall.status_string(INVALID) == "WALL_ERR_INVALID_ARG"
+    assert wall.status_string(UNSUPPORTED) == "WALL_ERR_UNSUPPORTED"
+    assert wall.status_string(wall.WALL_ERR_LAUNCH) == "WALL_ERR_LAUNCH"
+    assert wall.status_string(99) == "WALL_ERR_UNKNOWN"
+
+
+def P(x):
+    return None if x is None else ctypes.c_void_p(x)
+
+
+def scan(x=FAKE, dtype=B.WALL_BF16, out=FAKE * 2, b=1, t=64, c=8, cu=None, nseq=0, ws=FAKE * 3,
+         wsb=None):
+    L = wall.lib()
+    if wsb is None:
+        wsb = L.wall_prefix_scan_workspace_size(b, t, c)
+    return L.wall_prefix_scan(P(x), dtype, P(out), b, t, c, P(cu), nseq, 1.4426950408889634,
+                              P(ws), wsb, None)
+
+
+def fwd(q=FAKE, k=FAKE, v=FAKE, dtype=B.WALL_BF16, Pp=FAKE, G=None, sink=None, o=FAKE, lse=None,
+        b=1, t=256, hq=4, h=2, kk=128, vv=128, window=0, cu=None, nseq=0, maxlen=0, ws=FAKE,
+        wsb=None):
+    L = wall.lib()
+    if wsb is None:
+        wsb = L.wall_attn_fwd_workspace_size(dtype if dtype in (0, 1) else 1, b, t, hq, h, kk, vv,
+                                             nseq)
+    return L.wall_attn_fwd(P(q), P(k), P(v), dtype, P(Pp), P(G), P(sink), P(o), P(lse), b, t, hq,
+                           h, kk, vv, 0.088, window, P(cu), nseq, maxlen, P(ws), wsb, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(x=None), dict(out=None), dict(ws=None), dict(b=0), dict(t=0), dict(c=0),
+    dict(cu=FAKE, nseq=2, b=2), dict(cu=FAKE, nseq=0), dict(x=FAKE + 8), dict(out=FAKE + 4),
+    dict(ws=FAKE + 128), dict(wsb=16), dict(out=FAKE),
+])
+def test_prefix_scan_rejects_invalid_arguments(kw):
+    assert scan(**kw) == INVALID
+
+
+def test_prefix_scan_rejects_unsupported_dtype():
+    assert scan(dtype=7) == UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw", [
+    dict(q=None), dict(k=None), dict(v=None), dict(Pp=None), dict(o=None), dict(ws=None),
+    dict(b=0), dict(t=0), dict(hq=0), dict(h=0), dict(hq=6, h=4),
+    dict(cu=FAKE, nseq=2, b=2, maxlen=128), dict(cu=FAKE, nseq=0, maxlen=128),
+    dict(cu=FAKE, nseq=2, maxlen=0), dict(cu=FAKE, nseq=2, maxlen=1000),
+    dict(q=FAKE + 2), dict(G=FAKE + 4), dict(sink=FAKE + 8), dict(lse=FAKE + 12),
+    dict(ws=FAKE + 16), dict(wsb=1024), dict(cu=FAKE + 2, nseq=2, maxlen=128),
+])
+def test_fwd_rejects_invalid_arguments(kw):
+    assert fwd(**kw) == INVALID
+
+
+@pytest.mark.parametrize("kw", [dict(kk=96), dict(vv=32), dict(kk=256), dict(dtype=5)])
+def test_fwd_rejects_unsupported_shapes(kw):
+    assert fwd(**kw) == UNSUPPORTED
+
+
+def test_workspace_sizes():
+    L = wall.lib()
+    assert L.wall_prefix_scan_workspace_size(0, 10, 10) == 0
+    a = L.wall_prefix_scan_workspace_size(1, 8192, 2048)
+    assert a >= 2 * 64 * 2048 * 4 and a % 256 == 0
+    assert L.wall_attn_fwd_workspace_size(7, 1, 10, 1, 1, 64, 64, 0) == 0
+    b16 = L.wall_attn_fwd_workspace_size(1, 1, 8192, 16, 4, 128, 128, 0)
+    f32 = L.wall_attn_fwd_workspace_size(0, 1, 8192, 16, 4, 128, 128, 0)
+    # key cache per query head + value tiles per kv head, 65 tiles bound
+    assert b16 >= 65 * 128 * (16 * 128 + 4 * 128) * 2 and f32 > b16
+    assert L.wall_attn_fwd_workspace_size(1, 1, 1000, 2, 1, 64, 64, 9) > \
+        L.wall_attn_fwd_workspace_size(1, 1, 1000, 2, 1, 64, 64, 1)
+
+
+def test_python_wrappers_refuse_cpu_tensors():
+    x = torch.zeros(1, 8, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU only"):
+        wall.wall_prefix_scan(x)
+    with pytest.raises(ValueError, match="GPU only"):
+        wall.wall_attn(x, x[:, :, :1], x[:, :, :1], x)
+
+
+def test_cu_seqlens_host_checks():
+    T = 10
+    assert wall.check_cu_seqlens(torch.tensor([0, 3, 3, 10], dtype=torch.int32), 1, T) == 7
+    for bad in ([1, 10], [0, 5, 4, 10], [0, 9], [0]):
+        with pytest.raises(ValueError):
+            wall.check_cu_seqlens(torch.tensor(bad, dtype=torch.int32), 1, T)
+    with pytest.raises(ValueError):
+        wall.check_cu_seqlens(torch.tensor([0, 10], dtype=torch.int32), 2, T)
