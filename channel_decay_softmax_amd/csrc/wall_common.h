@@ -31,10 +31,20 @@ constexpr int SCAN_CHUNK = 128;
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
-// Exponent clamp for the anchored factors: exp2 of anything below -150 is 0
-// in float32, and 126 keeps every factor finite.
-constexpr float EXP2_LO = -150.0f;
+// Exponent clamp for exp2 of a real-valued anchored exponent: exp2 below
+// -160 is exactly 0 in float32 (clamping any closer to -150 could round up to
+// the smallest denormal), and 126 keeps every factor finite.
+constexpr float EXP2_LO = -160.0f;
 constexpr float EXP2_HI = 126.0f;
+
+// Integer exponent that moves a value anchored at one tile to another tile's
+// anchor (the difference of two integer anchors).  It is applied with ldexp
+// to the anchored value itself, never materialised as a factor 2^d: such a
+// factor is often below the float32 normal range (a fast channel's anchors
+// are ~150 apart per tile) while the product it would form is a normal
+// number, and a denormal factor is not reliably kept.  Capped at +127, which
+// only a prefix that grows (gates above 1) by more than that can reach.
+__device__ inline int anchor_shift(float d) { return (int)fminf(fmaxf(d, -1024.0f), 127.0f); }
 
 // One packed sequence (or one batch row).
 struct SegInfo {

@@ -5,7 +5,7 @@
 // same number of tile pairs.  Each wave owns 32 query rows.  For every key
 // tile c (from the diagonal tile down to the first tile the window reaches):
 //
-//   anchors   q~ = q^ * exp2(Rdiag - Rc), where q^ = q * scale*log2e *
+//   anchors   q~ = ldexp(q^, Rdiag - Rc), where q^ = q * scale*log2e *
 //             exp2(P_i - Rdiag) was built once per query tile (float32) and
 //             Rd, Rc are the integer per-channel anchors of the diagonal and
 //             of tile c, so exp2(P_i - P_j) = exp2(P_i - Rc) * exp2(Rc - P_j)
@@ -46,7 +46,7 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdArgs a) {
     constexpr int VT = V / 32;    // 32-wide value blocks
     __shared__ __attribute__((aligned(16))) __bf16 sK[TILE * KP];
     __shared__ __attribute__((aligned(16))) __bf16 sV[V * TP];
-    __shared__ __attribute__((aligned(16))) float sScale[K];
+    __shared__ __attribute__((aligned(16))) int sShift[K];
     __shared__ __attribute__((aligned(16))) float sBias[TILE];
 
     const int npairs = (a.max_tiles + 1) / 2;
@@ -121,7 +121,7 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdArgs a) {
             }
             if (tid < K) {
                 const float rc = a.anchor[((int64_t)(sg.tile_base + c) * a.HQ + hq) * K + tid];
-                sScale[tid] = exp2f(fminf(fmaxf(rdiag_t - rc, EXP2_LO), EXP2_HI));
+                sShift[tid] = anchor_shift(rdiag_t - rc);
             }
             if (a.G) {
                 for (int x = tid; x < TILE; x += 256) {
@@ -138,10 +138,12 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
             for (int s8 = 0; s8 < KS; ++s8) {
                 const int ch0 = 16 * s8 + 8 * hl;
-                const f32x8 sc = *reinterpret_cast<const f32x8 *>(&sScale[ch0]);
+                const int4 sh0 = *reinterpret_cast<const int4 *>(&sShift[ch0]);
+                const int4 sh1 = *reinterpret_cast<const int4 *>(&sShift[ch0 + 4]);
+                const int sh[8] = {sh0.x, sh0.y, sh0.z, sh0.w, sh1.x, sh1.y, sh1.z, sh1.w};
                 f32x8 qs;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) qs[e] = qh[s8][e] * sc[e];
+                for (int e = 0; e < 8; ++e) qs[e] = __builtin_ldexpf(qh[s8][e], sh[e]);
                 const bf16x8 qop = __builtin_convertvector(qs, bf16x8);
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt) {

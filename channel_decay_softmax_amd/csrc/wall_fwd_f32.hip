@@ -26,8 +26,8 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdArgs a, int qtiles) {
     float *sK = sQ + BQ * QP;       // [BK][KPT]
     float *sV = sK + BK * KPT;      // [BK][V]
     float *sP = sV + BK * V;        // [BQ][PP]
-    float *sScale = sP + BQ * PP;   // [K]
-    float *sBias = sScale + K;      // [BK]
+    int *sShift = reinterpret_cast<int *>(sP + BQ * PP);  // [K]
+    float *sBias = reinterpret_cast<float *>(sShift + K);  // [BK]
 
     const int bid = blockIdx.x;
     const int hq = bid / (a.nseg * qtiles);
@@ -76,12 +76,12 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdArgs a, int qtiles) {
         __syncthreads();
         if (tid < K) {
             const float rc = a.anchor[((int64_t)(sg.tile_base + c) * a.HQ + hq) * K + tid];
-            sScale[tid] = exp2f(fminf(fmaxf(Rd[tid] - rc, EXP2_LO), EXP2_HI));
+            sShift[tid] = anchor_shift(Rd[tid] - rc);
         }
         __syncthreads();
         for (int x = tid; x < BQ * K; x += 256) {
             const int r = x / K, n = x % K;
-            sQ[r * QP + n] = sQh[r * QP + n] * sScale[n];
+            sQ[r * QP + n] = __builtin_ldexpf(sQh[r * QP + n], sShift[n]);
         }
         const float *ktile = ktg + ((int64_t)(sg.tile_base + c) * a.HQ + hq) * TILE * K;
         const float *vtile = vtg + ((int64_t)(sg.tile_base + c) * a.H + h) * TILE * V;
