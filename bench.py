@@ -141,6 +141,9 @@ def main():
     ap.add_argument("--workload", default="long_bf16")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mb", type=int, default=0,
+                    help="run a plain device copy of this many MiB (read + write) before the "
+                         "timed region, as the reference kernel for HBM byte counters")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -197,6 +200,13 @@ def main():
         if marks:
             marks[3].record()
 
+    if args.copy_mb:
+        n = args.copy_mb * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.mul(src, 1.0, out=dst)  # reads and writes copy_mb MiB each
+        torch.cuda.synchronize()
+        del src, dst
     print(f"[bench] {args.workload}: B={B} T={T} HQ={HQ} H={H} K={K} V={V} {d.q.dtype} "
           f"pairs={pairs} flop={flop:.4e}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
