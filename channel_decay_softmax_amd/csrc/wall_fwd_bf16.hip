@@ -26,20 +26,24 @@
 //       column per lane, so all softmax state stays in-lane;
 //   softmax online in the log2 domain, fp32; the running max is raised only
 //       when a sub-block exceeds it by more than RESCALE (rare after the
-//       diagonal tile) and that test follows the exps, so it does not split
-//       the MFMA/VALU interleave;
+//       diagonal tile); O is then rescaled in a branch of its own, after the
+//       P formed with the old max has been accumulated;
 //   O^T += v^T p^T on the same MFMA, p as bf16.
 //
-// Interior tiles overlap the two units across sub-blocks: the QK of sub-block
-// b and then the PV of sub-block b+1 are issued before the softmax of b, so
-// the matrix cores run that PV while the vector ALUs take the softmax.
+// Interior tiles are software-pipelined over their four 32-key sub-blocks:
+// the exps of sub-block b share one basic block with the QK MFMAs of b-1 and
+// the PV MFMAs of b+1, so a single wave keeps the matrix cores and the vector
+// ALUs busy together.
 // Diagonal and window-boundary tiles take a plain masked loop.
 //
 // The key rows fed to the S^T MFMA are permuted (bits 2 and 3 of the row
 // index swapped) so each lane's output registers come out as runs of 8
 // consecutive keys: exactly the k-slots the PV MFMA needs from that lane.
-// LDS rows keep their 16-byte chunks XOR-swizzled by the row index, which
-// makes every MFMA fragment read free of bank conflicts.
+// LDS tiles are stored as 1 KB blocks padded to 1040 bytes, with the rows of
+// a tile interleaved across blocks (row j in block j % NBLK): one wave's
+// direct load fills exactly one block, the 16 rows an MFMA fragment read
+// touches lie in 16 different blocks (distinct bank groups), and every
+// fragment address is one per-lane base plus an immediate.
 #include <float.h>
 
 #include "wall_common.h"
@@ -64,12 +68,34 @@ __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 // Key row (within a 32-row block) that MFMA A-row m reads: bits 2 and 3 swapped.
 __device__ inline int key_perm(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
 
-__device__ inline float xor32(float x) { return __shfl_xor(x, 32, 64); }
+// Combine a value with the one held by lane ^ 32 (the other half of the wave
+// holds the same query's other keys): after v_permlane32_swap each lane holds
+// both halves' values, one in each result.
+__device__ inline float pair_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float pair_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// One tile as 1 KB blocks of whole rows (ROWB bytes each), row j stored in
+// block j % NBLK at slot j / NBLK; blocks are BLK_PITCH bytes apart.
+constexpr int BLK_PITCH = 1040;
+template <int NROWS, int ROWB>
+struct TileLayout {
+    static constexpr int NBLK = NROWS * ROWB / 1024;
+    static constexpr int BYTES = NBLK * BLK_PITCH;
+    static __device__ inline int byte(int row) { return (row % NBLK) * BLK_PITCH + (row / NBLK) * ROWB; }
+};
 
 template <int K, int V>
 struct Smem {
-    __bf16 k[2][TILE * K];      // rescaled keys, row = key, 16-byte chunks swizzled
-    __bf16 v[2][V * TILE];      // values transposed, row = value channel, swizzled
+    using KL = TileLayout<TILE, 2 * K>;  // rescaled keys, row = key
+    using VL = TileLayout<V, 2 * TILE>;  // values transposed, row = value channel
+    __attribute__((aligned(16))) char k[2][KL::BYTES];
+    __attribute__((aligned(16))) char v[2][VL::BYTES];
     uint32_t dsh[2][K / 2];     // per buffer: 128*(Rc - Rc+1) per channel pair, as two u16
     int32_t grow[2];            // some channel has Rc < Rc+1 (its prefix grows over the tile)
     float gk[2][TILE];          // G (log2) of the tile's keys; 0 beyond the sequence
@@ -141,36 +167,43 @@ __device__ inline void shift_qop(const Smem<K, V> &sm, int buf, int hl, QOp<K> &
     }
 }
 
-// S^T for sub-block b (32 keys) against both n-blocks.
+// Key fragments of sub-block b (A operands of the S^T MFMAs): lane (col, hl)
+// reads key row 32b + perm(col), channels 16*s8 + 8*hl .. +7.
 template <int K, int V>
-__device__ inline void qk(const Smem<K, V> &sm, int buf, int b, int col, int hl, const QOp<K> &qop,
-                          f32x16 (&S)[NB]) {
-    constexpr int KS = K / 16, CPR = K / 8;
-    const int row = SB * b + key_perm(col);
-    const __bf16 *base = sm.k[buf] + row * K;
+__device__ inline void load_kfrag(const Smem<K, V> &sm, int buf, int b, int kbase,
+                                  bf16x8 (&kf)[K / 16]) {
+    using KL = typename Smem<K, V>::KL;
+    // key 32b + perm(col): same block as key perm(col), (32 / NBLK) * b slots further
+    const char *base = sm.k[buf] + kbase + b * (SB / KL::NBLK) * (2 * K);
 #pragma unroll
-    for (int s8 = 0; s8 < KS; ++s8) {
-        const int ch = (2 * s8 + hl) ^ (row % CPR);
-        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(base + ch * 8);
+    for (int s8 = 0; s8 < K / 16; ++s8) kf[s8] = *reinterpret_cast<const bf16x8 *>(base + 32 * s8);
+}
+
+// S^T for one sub-block (32 keys) against the wave's n-blocks.
+template <int K>
+__device__ inline void qk(const bf16x8 (&kf)[K / 16], const QOp<K> &qop, f32x16 (&S)[NB]) {
+#pragma unroll
+    for (int s8 = 0; s8 < K / 16; ++s8)
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
-            S[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[nb][s8], s8 ? S[nb] : f32x16{}, 0, 0, 0);
-    }
+            S[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s8], qop[nb][s8], s8 ? S[nb] : f32x16{}, 0, 0, 0);
 }
 
 // O^T += v^T p^T for sub-block b (two 16-key MFMA k-steps).
 template <int K, int V>
-__device__ inline void pv(const Smem<K, V> &sm, int buf, int b, int col, int hl,
-                          const bf16x8 (&P)[NB][2], Acc<V> &acc) {
+__device__ inline void pv(const Smem<K, V> &sm, int buf, int b, int vbase, const bf16x8 (&P)[NB][2],
+                          Acc<V> &acc) {
     constexpr int VT = V / 32;
+    using VL = typename Smem<K, V>::VL;
+    const char *base = sm.v[buf] + vbase;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
         const int ks = 2 * b + t;
 #pragma unroll
         for (int vt = 0; vt < VT; ++vt) {
-            const int row = 32 * vt + col;
-            const int ch = (2 * ks + hl) ^ (row % 16);
-            const bf16x8 a = *reinterpret_cast<const bf16x8 *>(sm.v[buf] + row * TILE + ch * 8);
+            // lane (col, hl): value row 32*vt + col, keys 16*ks + 8*hl .. +7
+            const bf16x8 a = *reinterpret_cast<const bf16x8 *>(
+                base + vt * (32 / VL::NBLK) * (2 * TILE) + 32 * ks);
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb)
                 acc.O[nb][vt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, P[nb][t], acc.O[nb][vt], 0, 0, 0);
@@ -178,18 +211,20 @@ __device__ inline void pv(const Smem<K, V> &sm, int buf, int b, int col, int hl,
     }
 }
 
-// Online softmax of one sub-block's scores into bf16 p, one n-block at a
-// time.  MASKED applies causality, the window and the sequence end; HAS_G
-// subtracts the keys' scalar-gate prefix (the query's own G_i is added back
-// in the epilogue).
+// Online softmax of one sub-block, first half: masked scores into x and the
+// running max.  The max is raised only when the sub-block exceeds it by more
+// than RESCALE; then l is rescaled here and alpha (1 otherwise) is returned
+// for O, which the caller rescales with rescale_o once every P formed with
+// the old max has been accumulated.  MASKED applies causality, the window
+// and the sequence end; HAS_G subtracts the keys' scalar-gate prefix (the
+// query's own G_i is added back in the epilogue).
 template <int K, int V, bool MASKED, bool HAS_G>
-__device__ inline void softmax(const Smem<K, V> &sm, int buf, int b, int hl, const f32x16 (&S)[NB],
-                               Acc<V> &acc, bf16x8 (&P)[NB][2], int key0, const int (&qrow)[NB],
-                               int len, int window) {
-    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+__device__ inline void softmax_max(const Smem<K, V> &sm, int buf, int b, int hl,
+                                   const f32x16 (&S)[NB], Acc<V> &acc, float (&x)[NB][16],
+                                   float (&alpha)[NB], int key0, const int (&qrow)[NB], int len,
+                                   int window) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-        float x[16], p[16];
         float mx = -INFINITY;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -202,31 +237,47 @@ __device__ inline void softmax(const Smem<K, V> &sm, int buf, int b, int hl, con
                 if (window > 0) vis = vis && (qrow[nb] - key < window);
                 y = vis ? y : -INFINITY;
             }
-            x[r] = y;
+            x[nb][r] = y;
             mx = fmaxf(mx, y);
         }
-        const float mt = fmaxf(mx, xor32(mx));
+        const float mt = pair_max(mx);
+        const float m_new = mt > acc.m[nb] + RESCALE ? mt : acc.m[nb];
+        alpha[nb] = fast_exp2(acc.m[nb] - m_new);
+        acc.l[nb] *= alpha[nb];
+        acc.m[nb] = m_new;
+    }
+}
+
+// O *= alpha when some lane raised its max (rare after the first tiles).
+template <int V>
+__device__ inline void rescale_o(Acc<V> &acc, const float (&alpha)[NB]) {
+    bool any = false;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) p[r] = fast_exp2(x[r] - acc.m[nb]);
-        if (__any(mt > acc.m[nb] + RESCALE)) {  // rare after the first tiles: raise the max, redo
-            const float m_new = fmaxf(acc.m[nb], mt);
-            const float alpha = fast_exp2(acc.m[nb] - m_new);
+    for (int nb = 0; nb < NB; ++nb) any = any || alpha[nb] != 1.0f;
+    if (__any(any)) {
 #pragma unroll
-            for (int vt = 0; vt < V / 32; ++vt) acc.O[nb][vt] *= alpha;
-            acc.l[nb] *= alpha;
-            acc.m[nb] = m_new;
+        for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) p[r] = fast_exp2(x[r] - m_new);
-        }
+            for (int vt = 0; vt < V / 32; ++vt) acc.O[nb][vt] *= alpha[nb];
+    }
+}
+
+// Second half: p = exp2(x - m) as bf16 (the PV operand) and the row sum of
+// the rounded p, as the PV product sees it.
+template <int V>
+__device__ inline void softmax_exp(const float (&x)[NB][16], Acc<V> &acc, bf16x8 (&P)[NB][2]) {
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
         float sum = acc.l[nb];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             f32x8 pv8;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) pv8[e] = p[8 * t + e];
+            for (int e = 0; e < 8; ++e) pv8[e] = fast_exp2(x[nb][8 * t + e] - acc.m[nb]);
             P[nb][t] = __builtin_convertvector(pv8, bf16x8);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {  // row sum of the rounded p, as the PV product sees it
+            for (int e = 0; e < 4; ++e) {
                 const bf16x2 pr = {P[nb][t][2 * e], P[nb][t][2 * e + 1]};
                 sum = __builtin_amdgcn_fdot2_f32_bf16(pr, one, sum, false);
             }
@@ -236,27 +287,30 @@ __device__ inline void softmax(const Smem<K, V> &sm, int buf, int b, int hl, con
 }
 
 // Direct global->LDS copy of one key tile (k~) and one value tile (v^T) into
-// buffer `buf`.  Each wave instruction writes 1 KB of LDS lane-linearly; the
-// source address of each lane realises the XOR chunk swizzle.
+// buffer `buf`: one wave instruction per 1 KB block, written lane-linearly;
+// lane l fetches 16 bytes of the block's row l / (ROWB/16).
 template <int K, int V>
 __device__ inline void load_tile(Smem<K, V> &sm, int buf, const __bf16 *kt, const __bf16 *vt,
                                  int w, int lane) {
-    constexpr int CPR = K / 8;
+    using KL = typename Smem<K, V>::KL;
+    using VL = typename Smem<K, V>::VL;
+    constexpr int KCPR = K / 8, VCPR = TILE / 8;  // 16-byte chunks per row
+    static_assert(KL::NBLK % NW == 0 && VL::NBLK % NW == 0, "blocks split evenly over waves");
 #pragma unroll
-    for (int i = 0; i < K / (4 * NW); ++i) {
-        const int x = (i * NW + w) * 64 + lane;
-        const int row = x / CPR, pch = x % CPR;
-        const __bf16 *src = kt + row * K + ((pch ^ (row % CPR)) * 8);
-        __bf16 *dst = sm.k[buf] + (i * NW + w) * 512;
-        __builtin_amdgcn_global_load_lds((glb_cvoid *)src, (lds_void *)dst, 16, 0, 0);
+    for (int i = 0; i < KL::NBLK / NW; ++i) {
+        const int blk = i * NW + w;
+        const int row = (lane / KCPR) * KL::NBLK + blk;
+        const __bf16 *src = kt + row * K + (lane % KCPR) * 8;
+        __builtin_amdgcn_global_load_lds((glb_cvoid *)src, (lds_void *)(sm.k[buf] + blk * BLK_PITCH),
+                                         16, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < V / (4 * NW); ++i) {
-        const int x = (i * NW + w) * 64 + lane;
-        const int row = x / 16, pch = x % 16;
-        const __bf16 *src = vt + row * TILE + ((pch ^ (row % 16)) * 8);
-        __bf16 *dst = sm.v[buf] + (i * NW + w) * 512;
-        __builtin_amdgcn_global_load_lds((glb_cvoid *)src, (lds_void *)dst, 16, 0, 0);
+    for (int i = 0; i < VL::NBLK / NW; ++i) {
+        const int blk = i * NW + w;
+        const int row = (lane / VCPR) * VL::NBLK + blk;
+        const __bf16 *src = vt + row * TILE + (lane % VCPR) * 8;
+        __builtin_amdgcn_global_load_lds((glb_cvoid *)src, (lds_void *)(sm.v[buf] + blk * BLK_PITCH),
+                                         16, 0, 0);
     }
 }
 
@@ -283,6 +337,9 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const int col = lane & 31, hl = lane >> 5;
     const int var = w / (NW / 2);  // which of the block's two anchor tiles is this wave's diagonal
+    // per-lane byte offsets of the MFMA fragments in a tile buffer
+    const int kbase = Smem<K, V>::KL::byte(key_perm(col)) + 16 * hl;
+    const int vbase = Smem<K, V>::VL::byte(col) + 16 * hl;
     const int h = hq / (a.HQ / a.H);
     const __bf16 *qg = static_cast<const __bf16 *>(a.q);
     const __bf16 *ktg = static_cast<const __bf16 *>(a.kt);
@@ -382,24 +439,27 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
                 if (diag || sm.grow[buf]) load_qop<K>(a, sg, hq, c, qrow, hl, qop);
                 else shift_qop<K, V>(sm, buf, hl, qop);
                 if (!diag && !wtile) {
-                    // interior tile: per sub-block, QK(b) is issued, then PV(b+1) -- which
-                    // does not depend on it -- so the matrix cores run PV(b+1) while the
-                    // vector ALUs take the softmax of sub-block b
-                    bf16x8 Pn[NB][2];
+                    // interior tile, software-pipelined over its four sub-blocks: the
+                    // exps of sub-block b share a basic block with the QK MFMAs of b-1
+                    // and the PV MFMAs of b+1, so one wave keeps both units busy
+                    f32x16 S[NSB][NB];
+                    bf16x8 P[NSB][NB][2];
+                    bf16x8 kf[K / 16];
+                    load_kfrag<K, V>(sm, buf, NSB - 1, kbase, kf);
+                    qk<K>(kf, qop, S[NSB - 1]);
+                    load_kfrag<K, V>(sm, buf, NSB - 2, kbase, kf);
 #pragma unroll
                     for (int b = NSB - 1; b >= 0; --b) {
-                        f32x16 S[NB];
-                        bf16x8 P[NB][2];
-                        qk<K, V>(sm, buf, b, col, hl, qop, S);
-                        if (b < NSB - 1) pv<K, V>(sm, buf, b + 1, col, hl, Pn, acc);
-                        softmax<K, V, false, HAS_G>(sm, buf, b, hl, S, acc, P, key0, qrow, sg.len, 0);
-#pragma unroll
-                        for (int nb = 0; nb < NB; ++nb) {
-                            Pn[nb][0] = P[nb][0];
-                            Pn[nb][1] = P[nb][1];
-                        }
+                        float x[NB][16], alpha[NB];
+                        softmax_max<K, V, false, HAS_G>(sm, buf, b, hl, S[b], acc, x, alpha, key0,
+                                                        qrow, sg.len, 0);
+                        if (b > 0) qk<K>(kf, qop, S[b - 1]);
+                        if (b > 1) load_kfrag<K, V>(sm, buf, b - 2, kbase, kf);
+                        if (b < NSB - 1) pv<K, V>(sm, buf, b + 1, vbase, P[b + 1], acc);
+                        softmax_exp<V>(x, acc, P[b]);
+                        rescale_o<V>(acc, alpha);  // O = (O + P(b+1) V) * alpha
                     }
-                    pv<K, V>(sm, buf, 0, col, hl, Pn, acc);
+                    pv<K, V>(sm, buf, 0, vbase, P[0], acc);
                 } else {
                     // diagonal / window-boundary tile: masked, sub-blocks wholly in the
                     // future of all this wave's queries skipped
@@ -407,10 +467,15 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
                     for (int b = b_hi; b >= 0; --b) {
                         f32x16 S[NB];
                         bf16x8 P[NB][2];
-                        qk<K, V>(sm, buf, b, col, hl, qop, S);
-                        softmax<K, V, true, HAS_G>(sm, buf, b, hl, S, acc, P, key0, qrow, sg.len,
-                                                   a.window);
-                        pv<K, V>(sm, buf, b, col, hl, P, acc);
+                        bf16x8 kf[K / 16];
+                        load_kfrag<K, V>(sm, buf, b, kbase, kf);
+                        qk<K>(kf, qop, S);
+                        float x[NB][16], alpha[NB];
+                        softmax_max<K, V, true, HAS_G>(sm, buf, b, hl, S, acc, x, alpha, key0, qrow,
+                                                       sg.len, a.window);
+                        rescale_o<V>(acc, alpha);
+                        softmax_exp<V>(x, acc, P);
+                        pv<K, V>(sm, buf, b, vbase, P, acc);
                     }
                 }
             }
@@ -428,7 +493,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
         if (wave_on) {
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
-                const float l_tot = acc.l[nb] + xor32(acc.l[nb]);
+                const float l_tot = pair_sum(acc.l[nb]);
                 const float m_true = acc.m[nb] + g_i[nb];
                 float m_fin = m_true, l_fin = l_tot;
                 if (a.sink) {

@@ -163,6 +163,22 @@ def test_strong_uniform_decay():
     assert_parity(o, lse, o_ref, lse_ref, "bfloat16", what="uniform g=-1")
 
 
+@pytest.mark.parametrize("kv", [(64, 64), (64, 128), (128, 64), (128, 128)])
+def test_running_max_raised_in_interior_tiles(kv):
+    """A positive scalar gate (g_scalar = +0.04 per token) makes every older key
+    score higher through the additive fp32 bias G_i - G_j, by ~7 log2 units per
+    128-key tile, so the running max keeps being raised long after the
+    diagonal tile: the rescale of O must stay consistent with the software
+    pipeline.  The bias is exact in fp32, so the bf16 error stays that of
+    ordinary logits."""
+    K, V = kv
+    inp = make_inputs("gqa_bf16", B=1, T=700, HQ=2, H=1, K=K, V=V)
+    inp.g_scalar = torch.full((1, 700, 2), 0.04).to(inp.q.dtype)
+    o, lse = run_gpu(inp, f"raised max K={K} V={V}")
+    o_ref, lse_ref = run_oracle(inp)
+    assert_parity(o, lse, o_ref, lse_ref, "bfloat16", what=f"raised max K={K} V={V}")
+
+
 # --------------------------------------------------------------------------- full sizes, sampled rows
 
 
