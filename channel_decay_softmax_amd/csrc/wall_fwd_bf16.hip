@@ -46,6 +46,8 @@
 // fragment address is one per-lane base plus an immediate.
 #include <float.h>
 
+#include <type_traits>
+
 #include "wall_common.h"
 
 namespace wall {
@@ -91,11 +93,14 @@ struct TileLayout {
 };
 
 template <int K, int V>
-struct Smem {
+struct Layouts {
     using KL = TileLayout<TILE, 2 * K>;  // rescaled keys, row = key
     using VL = TileLayout<V, 2 * TILE>;  // values transposed, row = value channel
-    __attribute__((aligned(16))) char k[2][KL::BYTES];
-    __attribute__((aligned(16))) char v[2][VL::BYTES];
+};
+
+// Small per-tile rows, double-buffered like the tiles.
+template <int K>
+struct TileRows {
     uint32_t dsh[2][K / 2];     // per buffer: 128*(Rc - Rc+1) per channel pair, as two u16
     int32_t grow[2];            // some channel has Rc < Rc+1 (its prefix grows over the tile)
     float gk[2][TILE];          // G (log2) of the tile's keys; 0 beyond the sequence
@@ -144,12 +149,12 @@ __device__ inline void load_qop(const FwdArgs &a, const SegInfo &sg, int hq, int
 // by 128*(Rc - Rc+1) with unsigned saturation on the magnitude, keeping the
 // sign.  Exact while the result is a normal number; a value pushed out of
 // range becomes 0 (or a bf16 denormal).
-template <int K, int V>
-__device__ inline void shift_qop(const Smem<K, V> &sm, int buf, int hl, QOp<K> &qop) {
+template <int K>
+__device__ inline void shift_qop(const TileRows<K> &rows, int buf, int hl, QOp<K> &qop) {
     constexpr int KS = K / 16;
 #pragma unroll
     for (int s8 = 0; s8 < KS; ++s8) {
-        const uint4 d = *reinterpret_cast<const uint4 *>(&sm.dsh[buf][8 * s8 + 4 * hl]);
+        const uint4 d = *reinterpret_cast<const uint4 *>(&rows.dsh[buf][8 * s8 + 4 * hl]);
         const uint32_t dv[4] = {d.x, d.y, d.z, d.w};
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
@@ -169,12 +174,11 @@ __device__ inline void shift_qop(const Smem<K, V> &sm, int buf, int hl, QOp<K> &
 
 // Key fragments of sub-block b (A operands of the S^T MFMAs): lane (col, hl)
 // reads key row 32b + perm(col), channels 16*s8 + 8*hl .. +7.
-template <int K, int V>
-__device__ inline void load_kfrag(const Smem<K, V> &sm, int buf, int b, int kbase,
-                                  bf16x8 (&kf)[K / 16]) {
-    using KL = typename Smem<K, V>::KL;
+template <int K>
+__device__ inline void load_kfrag(const char *kb, int b, int kbase, bf16x8 (&kf)[K / 16]) {
+    using KL = typename Layouts<K, K>::KL;
     // key 32b + perm(col): same block as key perm(col), (32 / NBLK) * b slots further
-    const char *base = sm.k[buf] + kbase + b * (SB / KL::NBLK) * (2 * K);
+    const char *base = kb + kbase + b * (SB / KL::NBLK) * (2 * K);
 #pragma unroll
     for (int s8 = 0; s8 < K / 16; ++s8) kf[s8] = *reinterpret_cast<const bf16x8 *>(base + 32 * s8);
 }
@@ -191,11 +195,10 @@ __device__ inline void qk(const bf16x8 (&kf)[K / 16], const QOp<K> &qop, f32x16 
 
 // O^T += v^T p^T for sub-block b (two 16-key MFMA k-steps).
 template <int K, int V>
-__device__ inline void pv(const Smem<K, V> &sm, int buf, int b, int vbase, const bf16x8 (&P)[NB][2],
-                          Acc<V> &acc) {
+__device__ inline void pv(const char *vb, int b, int vbase, const bf16x8 (&P)[NB][2], Acc<V> &acc) {
     constexpr int VT = V / 32;
-    using VL = typename Smem<K, V>::VL;
-    const char *base = sm.v[buf] + vbase;
+    using VL = typename Layouts<K, V>::VL;
+    const char *base = vb + vbase;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
         const int ks = 2 * b + t;
@@ -219,7 +222,7 @@ __device__ inline void pv(const Smem<K, V> &sm, int buf, int b, int vbase, const
 // and the sequence end; HAS_G subtracts the keys' scalar-gate prefix (the
 // query's own G_i is added back in the epilogue).
 template <int K, int V, bool MASKED, bool HAS_G>
-__device__ inline void softmax_max(const Smem<K, V> &sm, int buf, int b, int hl,
+__device__ inline void softmax_max(const TileRows<K> &rows, int buf, int b, int hl,
                                    const f32x16 (&S)[NB], Acc<V> &acc, float (&x)[NB][16],
                                    float (&alpha)[NB], int key0, const int (&qrow)[NB], int len,
                                    int window) {
@@ -230,7 +233,7 @@ __device__ inline void softmax_max(const Smem<K, V> &sm, int buf, int b, int hl,
         for (int r = 0; r < 16; ++r) {
             const int kin = SB * b + 16 * (r / 8) + 8 * hl + (r % 8);  // key within the tile
             float y = S[nb][r];
-            if (HAS_G) y -= sm.gk[buf][kin];
+            if (HAS_G) y -= rows.gk[buf][kin];
             if (MASKED) {
                 const int key = key0 + kin;
                 bool vis = key <= qrow[nb] && key < len;
@@ -290,10 +293,10 @@ __device__ inline void softmax_exp(const float (&x)[NB][16], Acc<V> &acc, bf16x8
 // buffer `buf`: one wave instruction per 1 KB block, written lane-linearly;
 // lane l fetches 16 bytes of the block's row l / (ROWB/16).
 template <int K, int V>
-__device__ inline void load_tile(Smem<K, V> &sm, int buf, const __bf16 *kt, const __bf16 *vt,
-                                 int w, int lane) {
-    using KL = typename Smem<K, V>::KL;
-    using VL = typename Smem<K, V>::VL;
+__device__ inline void load_tile(char *kd, char *vd, const __bf16 *kt, const __bf16 *vt, int w,
+                                 int lane) {
+    using KL = typename Layouts<K, V>::KL;
+    using VL = typename Layouts<K, V>::VL;
     constexpr int KCPR = K / 8, VCPR = TILE / 8;  // 16-byte chunks per row
     static_assert(KL::NBLK % NW == 0 && VL::NBLK % NW == 0, "blocks split evenly over waves");
 #pragma unroll
@@ -301,7 +304,7 @@ __device__ inline void load_tile(Smem<K, V> &sm, int buf, const __bf16 *kt, cons
         const int blk = i * NW + w;
         const int row = (lane / KCPR) * KL::NBLK + blk;
         const __bf16 *src = kt + row * K + (lane % KCPR) * 8;
-        __builtin_amdgcn_global_load_lds((glb_cvoid *)src, (lds_void *)(sm.k[buf] + blk * BLK_PITCH),
+        __builtin_amdgcn_global_load_lds((glb_cvoid *)src, (lds_void *)(kd + blk * BLK_PITCH),
                                          16, 0, 0);
     }
 #pragma unroll
@@ -309,7 +312,7 @@ __device__ inline void load_tile(Smem<K, V> &sm, int buf, const __bf16 *kt, cons
         const int blk = i * NW + w;
         const int row = (lane / VCPR) * VL::NBLK + blk;
         const __bf16 *src = vt + row * TILE + (lane % VCPR) * 8;
-        __builtin_amdgcn_global_load_lds((glb_cvoid *)src, (lds_void *)(sm.v[buf] + blk * BLK_PITCH),
+        __builtin_amdgcn_global_load_lds((glb_cvoid *)src, (lds_void *)(vd + blk * BLK_PITCH),
                                          16, 0, 0);
     }
 }
@@ -317,7 +320,16 @@ __device__ inline void load_tile(Smem<K, V> &sm, int buf, const __bf16 *kt, cons
 template <int K, int V, bool HAS_G>
 __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
     constexpr int KS = K / 16, VT = V / 32;
-    __shared__ __attribute__((aligned(16))) Smem<K, V> sm;
+    using KL = typename Layouts<K, V>::KL;
+    using VL = typename Layouts<K, V>::VL;
+    // Each tile buffer is an LDS variable of its own: the compiler then knows
+    // that reading one buffer does not depend on the direct loads still
+    // filling the other, and does not wait for them.
+    __shared__ __attribute__((aligned(16))) char k0[KL::BYTES];
+    __shared__ __attribute__((aligned(16))) char k1[KL::BYTES];
+    __shared__ __attribute__((aligned(16))) char v0[VL::BYTES];
+    __shared__ __attribute__((aligned(16))) char v1[VL::BYTES];
+    __shared__ TileRows<K> rows;
 
     const int nblocks_max = (a.max_tiles + 1) / 2;  // 256-row blocks of the longest sequence
     const int npairs = (nblocks_max + 1) / 2;
@@ -338,8 +350,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
     const int col = lane & 31, hl = lane >> 5;
     const int var = w / (NW / 2);  // which of the block's two anchor tiles is this wave's diagonal
     // per-lane byte offsets of the MFMA fragments in a tile buffer
-    const int kbase = Smem<K, V>::KL::byte(key_perm(col)) + 16 * hl;
-    const int vbase = Smem<K, V>::VL::byte(col) + 16 * hl;
+    const int kbase = KL::byte(key_perm(col)) + 16 * hl;
+    const int vbase = VL::byte(col) + 16 * hl;
     const int h = hq / (a.HQ / a.H);
     const __bf16 *qg = static_cast<const __bf16 *>(a.q);
     const __bf16 *ktg = static_cast<const __bf16 *>(a.kt);
@@ -407,12 +419,12 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
                     up = d0 < 0.f || d1 < 0.f;
                     const uint32_t s0 = (uint32_t)fminf(fmaxf(d0, 0.f), 255.f) * 128u;
                     const uint32_t s1 = (uint32_t)fminf(fmaxf(d1, 0.f), 255.f) * 128u;
-                    sm.dsh[bb][pv_j] = s0 | (s1 << 16);
+                    rows.dsh[bb][pv_j] = s0 | (s1 << 16);
                 }
                 const bool any_up = __any(up);
-                if (tid == 0) sm.grow[bb] = any_up;
+                if (tid == 0) rows.grow[bb] = any_up;
             }
-            if (HAS_G && tid < TILE) sm.gk[bb][tid] = gval;
+            if (HAS_G && tid < TILE) rows.gk[bb][tid] = gval;
             rp0 = rc0;
             rp1 = rc1;
         };
@@ -420,24 +432,29 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
         auto vt_tile = [&](int c) { return vtg + ((int64_t)(sg.tile_base + c) * a.H + h) * V * TILE; };
 
         // ---- prologue: tile c_hi into buffer 0
-        int buf = 0;
         __syncthreads();  // the previous block's last reads of both buffers are done
         fetch_rows(c_hi);
-        load_tile<K, V>(sm, 0, kt_tile(c_hi), vt_tile(c_hi), w, lane);
+        load_tile<K, V>(k0, v0, kt_tile(c_hi), vt_tile(c_hi), w, lane);
         write_rows(0, true);
         if (c_hi - 1 >= c_lo) fetch_rows(c_hi - 1);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
 
-        for (int c = c_hi; c >= c_lo; --c) {
-            if (c - 1 >= c_lo) load_tile<K, V>(sm, buf ^ 1, kt_tile(c - 1), vt_tile(c - 1), w, lane);
+        // One key tile c held in buffer PB (tile c_hi in buffer 0, then alternating);
+        // the buffer is a compile-time choice so every LDS access names its variable.
+        auto tile_step = [&](int c, auto pb_tag) {
+            constexpr int PB = decltype(pb_tag)::value;
+            const char *kb = PB ? k1 : k0;
+            const char *vb = PB ? v1 : v0;
+            if (c - 1 >= c_lo)
+                load_tile<K, V>(PB ? k0 : k1, PB ? v0 : v1, kt_tile(c - 1), vt_tile(c - 1), w, lane);
 
             if (wave_on && c <= qt_w) {
                 const bool diag = c == qt_w;
                 const bool wtile = a.window > 0 && q0w + WQ - 1 - TILE * c >= a.window;
                 const int key0 = TILE * c;
-                if (diag || sm.grow[buf]) load_qop<K>(a, sg, hq, c, qrow, hl, qop);
-                else shift_qop<K, V>(sm, buf, hl, qop);
+                if (diag || rows.grow[PB]) load_qop<K>(a, sg, hq, c, qrow, hl, qop);
+                else shift_qop<K>(rows, PB, hl, qop);
                 if (!diag && !wtile) {
                     // interior tile, software-pipelined over its four sub-blocks: the
                     // exps of sub-block b share a basic block with the QK MFMAs of b-1
@@ -445,21 +462,21 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
                     f32x16 S[NSB][NB];
                     bf16x8 P[NSB][NB][2];
                     bf16x8 kf[K / 16];
-                    load_kfrag<K, V>(sm, buf, NSB - 1, kbase, kf);
+                    load_kfrag<K>(kb, NSB - 1, kbase, kf);
                     qk<K>(kf, qop, S[NSB - 1]);
-                    load_kfrag<K, V>(sm, buf, NSB - 2, kbase, kf);
+                    load_kfrag<K>(kb, NSB - 2, kbase, kf);
 #pragma unroll
                     for (int b = NSB - 1; b >= 0; --b) {
                         float x[NB][16], alpha[NB];
-                        softmax_max<K, V, false, HAS_G>(sm, buf, b, hl, S[b], acc, x, alpha, key0,
+                        softmax_max<K, V, false, HAS_G>(rows, PB, b, hl, S[b], acc, x, alpha, key0,
                                                         qrow, sg.len, 0);
                         if (b > 0) qk<K>(kf, qop, S[b - 1]);
-                        if (b > 1) load_kfrag<K, V>(sm, buf, b - 2, kbase, kf);
-                        if (b < NSB - 1) pv<K, V>(sm, buf, b + 1, vbase, P[b + 1], acc);
+                        if (b > 1) load_kfrag<K>(kb, b - 2, kbase, kf);
+                        if (b < NSB - 1) pv<K, V>(vb, b + 1, vbase, P[b + 1], acc);
                         softmax_exp<V>(x, acc, P[b]);
                         rescale_o<V>(acc, alpha);  // O = (O + P(b+1) V) * alpha
                     }
-                    pv<K, V>(sm, buf, 0, vbase, P[0], acc);
+                    pv<K, V>(vb, 0, vbase, P[0], acc);
                 } else {
                     // diagonal / window-boundary tile: masked, sub-blocks wholly in the
                     // future of all this wave's queries skipped
@@ -468,25 +485,28 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
                         f32x16 S[NB];
                         bf16x8 P[NB][2];
                         bf16x8 kf[K / 16];
-                        load_kfrag<K, V>(sm, buf, b, kbase, kf);
+                        load_kfrag<K>(kb, b, kbase, kf);
                         qk<K>(kf, qop, S);
                         float x[NB][16], alpha[NB];
-                        softmax_max<K, V, true, HAS_G>(sm, buf, b, hl, S, acc, x, alpha, key0, qrow,
+                        softmax_max<K, V, true, HAS_G>(rows, PB, b, hl, S, acc, x, alpha, key0, qrow,
                                                        sg.len, a.window);
                         rescale_o<V>(acc, alpha);
                         softmax_exp<V>(x, acc, P);
-                        pv<K, V>(sm, buf, b, vbase, P, acc);
+                        pv<K, V>(vb, b, vbase, P, acc);
                     }
                 }
             }
 
             __builtin_amdgcn_s_waitcnt(0);  // tile c-1 has landed in LDS, its rows in registers
             if (c - 1 >= c_lo) {
-                write_rows(buf ^ 1, false);
+                write_rows(PB ^ 1, false);
                 if (c - 2 >= c_lo) fetch_rows(c - 2);
             }
             __syncthreads();
-            buf ^= 1;
+        };
+        for (int c = c_hi; c >= c_lo; c -= 2) {
+            tile_step(c, std::integral_constant<int, 0>{});
+            if (c - 1 >= c_lo) tile_step(c - 1, std::integral_constant<int, 1>{});
         }
 
         // ---- epilogue: sink, normalisation, o and lse
