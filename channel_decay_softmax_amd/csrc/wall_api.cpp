@@ -100,8 +100,9 @@ wall_status_t enqueue_prepare(const void *k, const void *v, wall_dtype_t dtype, 
     char *ws = static_cast<char *>(workspace);
     SegInfo *seg = reinterpret_cast<SegInfo *>(ws + L.off_seg);
     if (launch_seg_table(seg, cu, L.nseg, s.B, s.T, stream) != hipSuccess) return WALL_ERR_LAUNCH;
-    PrepArgs pa{k, v, P, seg, reinterpret_cast<float *>(ws + L.off_anchor), ws + L.off_kt,
-                ws + L.off_vt, L.nseg, L.tiles, s.HQ, s.H, s.K, s.V};
+    PrepArgs pa{k, v, P, seg, reinterpret_cast<float *>(ws + L.off_anchor),
+                reinterpret_cast<uint32_t *>(ws + L.off_rec), ws + L.off_kt, ws + L.off_vt,
+                L.nseg, L.tiles, s.HQ, s.H, s.K, s.V};
     return launched(launch_prep(pa, dtype == WALL_BF16, stream));
 }
 
@@ -119,6 +120,7 @@ wall_status_t enqueue_run(const void *q, wall_dtype_t dtype, const float *P, con
     fa.kt = ws + L.off_kt;
     fa.vt = ws + L.off_vt;
     fa.anchor = reinterpret_cast<const float *>(ws + L.off_anchor);
+    fa.rec = reinterpret_cast<const uint32_t *>(ws + L.off_rec);
     fa.seg = reinterpret_cast<const SegInfo *>(ws + L.off_seg);
     fa.o = o;
     fa.lse = lse;

@@ -58,11 +58,20 @@ inline __host__ __device__ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 
 inline __host__ __device__ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // ----------------------------------------------------------------- workspace layouts
-// Forward workspace: segment table | anchors | rescaled key tiles | transposed value tiles.
+// Per (tile, query head) carry record, 1 KB: words 0..K/2-1 hold, per channel
+// pair, 128*(R[t-1] - R[t]) clamped to [0, 255*128] as two u16 (the bf16
+// exponent-field decrement that moves a query anchored at tile t to tile t-1);
+// word REC_GROW is 1 when some channel has R[t-1] < R[t] (a prefix that grows
+// over the boundary), else 0.  All zero for a sequence's first tile.
+constexpr int REC_WORDS = 256;
+constexpr int REC_GROW = 128;
+
+// Forward workspace: segment table | anchors | carry records | rescaled key
+// tiles | transposed value tiles.
 struct FwdLayout {
     int64_t nseg;        // sequences (num_seqs with packing, else B)
     int64_t tiles;       // upper bound on sum_s ceil(len_s / TILE)
-    size_t off_seg, off_anchor, off_kt, off_vt, total;
+    size_t off_seg, off_anchor, off_rec, off_kt, off_vt, total;
 };
 
 inline FwdLayout fwd_layout(int64_t esize, int64_t B, int64_t T, int64_t HQ, int64_t H,
@@ -75,6 +84,8 @@ inline FwdLayout fwd_layout(int64_t esize, int64_t B, int64_t T, int64_t HQ, int
     o = align_up(o + sizeof(SegInfo) * (size_t)L.nseg, 256);
     L.off_anchor = o;
     o = align_up(o + sizeof(float) * (size_t)(L.tiles * HQ * K), 256);
+    L.off_rec = o;
+    o = align_up(o + sizeof(uint32_t) * (size_t)(L.tiles * HQ * REC_WORDS), 256);
     L.off_kt = o;
     o = align_up(o + (size_t)esize * (size_t)(L.tiles * HQ * TILE * K), 256);
     L.off_vt = o;
@@ -117,6 +128,7 @@ struct PrepArgs {
     const float *P;    // [rows, HQ, K]
     const SegInfo *seg;
     float *anchor;     // [tiles, HQ, K]
+    uint32_t *rec;     // [tiles, HQ, REC_WORDS]
     void *kt;          // [tiles, HQ, TILE, K]
     void *vt;          // [tiles, H, V, TILE]
     int64_t nseg, tiles, HQ, H, K, V;
@@ -131,6 +143,7 @@ struct FwdArgs {
     const void *kt;         // [tiles, HQ, TILE, K]
     const void *vt;         // [tiles, H, V, TILE]
     const float *anchor;    // [tiles, HQ, K]
+    const uint32_t *rec;    // [tiles, HQ, REC_WORDS]
     const SegInfo *seg;     // [nseg]
     void *o;                // [rows, HQ, V]
     float *lse;             // [rows, HQ] or null

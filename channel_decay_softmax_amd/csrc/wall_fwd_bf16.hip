@@ -1,40 +1,52 @@
 // wall_fwd_bf16.hip -- fused causal Wall Attention forward, bf16 inputs, gfx950.
 //
-// Work decomposition.  A workgroup (4 waves) owns one (sequence, query head)
+// Work decomposition.  A workgroup (8 waves) owns one (sequence, query head)
 // and two 256-row query blocks, u and n-1-u, so every workgroup of a causal
-// launch does the same number of tile pairs.  Wave w owns query rows
-// 256u + 64w .. +63 as two 32-column MFMA n-blocks; its diagonal 128-row
-// anchor tile is 2u + w/2.  Workgroup ids are remapped so each XCD receives a
-// contiguous range of heads (their key caches then share that XCD's L2).
+// launch does about the same number of tiles.  Wave w owns the 32 query rows
+// 256u + 32w .. +31 (one MFMA n-block); waves 0-3 sit in the block's first
+// 128-row anchor tile 2u, waves 4-7 in the second, 2u+1.  Workgroup ids are
+// remapped so each XCD receives a contiguous range of heads (their key
+// caches then share that XCD's L2).
 //
-// Per key tile c (the block's last tile first, then older tiles down to the
-// first tile the window reaches), with the tile's rescaled keys k~ and
-// transposed values double-buffered in LDS by direct global->LDS loads (the
-// next tile streams in while this one is computed):
+// Per wave, keys are walked from the block's last tile down to the first
+// tile the window reaches, one 32-key sub-block (one MFMA m-tile) per step:
 //
-//   q~  the wave's bf16 queries anchored at tile c, q * scale*log2e *
+//   q~  the wave's bf16 queries anchored at the key tile c, q * scale*log2e *
 //       exp2(P_i - Rc).  Built from q and P at the wave's diagonal tile, then
-//       carried from tile c+1 to tile c by lowering each bf16 exponent field
-//       by the integer Rc - Rc+1 (>= 0 while the prefix does not grow) with a
-//       saturating packed subtract: exact, and a value that would leave the
-//       bf16 range becomes 0 and, the decay only growing further back, stays
-//       negligible.  A tile where some channel's prefix grows rebuilds q~ from
-//       q and P.  These are the per-tile anchors of the blog's "Fast training
-//       and inference" section, with the key-side factor exp2(Rc - P_j)
-//       already folded into k~;
-//   S^T = k~ q~^T on v_mfma_f32_32x32x16_bf16 per 32-key sub-block, one query
-//       column per lane, so all softmax state stays in-lane;
+//       carried from tile c to tile c-1 by lowering each bf16 exponent field
+//       by the integer R[c-1] - R[c] (>= 0 while the prefix does not grow)
+//       with a saturating packed subtract: exact, and a value that would leave
+//       the bf16 range becomes 0 and, the decay only growing further back,
+//       stays negligible.  A tile where some channel's prefix grows rebuilds
+//       q~ from q and P.  These are the per-tile anchors of the blog's "Fast
+//       training and inference" section, with the key-side factor
+//       exp2(Rc - P_j) already folded into k~;
+//   S^T = k~ q~^T - m on v_mfma_f32_32x32x16_bf16: the accumulator starts at
+//       -m (the running max), so scores come back already relative to it,
+//       one query column per lane, all softmax state in-lane;
 //   softmax online in the log2 domain, fp32; the running max is raised only
 //       when a sub-block exceeds it by more than RESCALE (rare after the
-//       diagonal tile); O is then rescaled in a branch of its own, after the
-//       P formed with the old max has been accumulated;
+//       diagonal), and O is then rescaled in a branch of its own;
 //   O^T += v^T p^T on the same MFMA, p as bf16.
 //
-// Interior tiles are software-pipelined over their four 32-key sub-blocks:
-// the exps of sub-block b share one basic block with the QK MFMAs of b-1 and
-// the PV MFMAs of b+1, so a single wave keeps the matrix cores and the vector
-// ALUs busy together.
-// Diagonal and window-boundary tiles take a plain masked loop.
+// Software pipeline.  Step b of tile c runs the softmax of sub-block b, the QK
+// products of the next sub-block (b-1, or sub-block 3 of tile c-1) and the PV
+// products of the previous one (b+1, or sub-block 0 of tile c+1), as one
+// instruction stream whose order is fixed at compile time (TilePlan) and
+// pinned with scheduling barriers: every LDS operand read is issued NPF reads
+// ahead of its MFMA, and the VALU work of the softmax sits between the
+// MFMAs.  Both waves of a SIMD run such streams, so each fills the other's
+// gaps on the matrix core and the vector ALU.
+//
+// Tiles stream into LDS by direct buffer->LDS loads, double-buffered, with
+// two workgroup barriers per tile: the values of tile c must be in place
+// before step 2 of tile c (barrier V), the keys of tile c-1 before the first
+// products of tile c-1 start in step 0 of tile c (barrier K).  Each barrier
+// waits for its own earlier load batch only and then issues the next batch
+// into the buffer just released; each buffer is an LDS variable of its own
+// so the compiler does not wait on the loads either.  A key buffer also
+// carries the tile's carry record (from the preparation step) and its keys'
+// scalar-gate prefix.
 //
 // The key rows fed to the S^T MFMA are permuted (bits 2 and 3 of the row
 // index swapped) so each lane's output registers come out as runs of 8
@@ -45,8 +57,11 @@
 // touches lie in 16 different blocks (distinct bank groups), and every
 // fragment address is one per-lane base plus an immediate.
 #include <float.h>
+#include <limits.h>
 
+#include <array>
 #include <type_traits>
+#include <utility>
 
 #include "wall_common.h"
 
@@ -55,31 +70,45 @@ namespace {
 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) const void glb_cvoid;
 
-constexpr int NB = 1;          // 32-column MFMA n-blocks (query groups) per wave
-constexpr int WQ = 32 * NB;    // query rows per wave
-constexpr int BQ = 2 * TILE;   // query rows per block: two anchor tiles
-constexpr int NW = BQ / WQ;    // waves per workgroup
-constexpr int SB = 32;         // keys per sub-block (one MFMA m-tile)
-constexpr int NSB = TILE / SB; // sub-blocks per tile
+constexpr int WQ = 32;          // query rows per wave (one MFMA n-block)
+constexpr int BQ = 2 * TILE;    // query rows per block: two anchor tiles
+constexpr int NW = BQ / WQ;     // waves per workgroup
+constexpr int SB = 32;          // keys per sub-block (one MFMA m-tile)
+constexpr int NSB = TILE / SB;  // sub-blocks per tile (pipeline steps per tile)
 constexpr float RESCALE = 10.0f;  // log2 headroom before the running max is raised
 
-__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Key row (within a 32-row block) that MFMA A-row m reads: bits 2 and 3 swapped.
-__device__ inline int key_perm(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
+__device__ __forceinline__ int key_perm(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
 
 // Combine a value with the one held by lane ^ 32 (the other half of the wave
 // holds the same query's other keys): after v_permlane32_swap each lane holds
 // both halves' values, one in each result.
-__device__ inline float pair_max(float x) {
+__device__ __forceinline__ float pair_max(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-__device__ inline float pair_sum(float x) {
+__device__ __forceinline__ float pair_sum(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Workgroup barrier that leaves direct-to-LDS loads in flight: the wave's own
+// LDS reads and writes complete first, vector memory is not waited for.  The
+// scheduling fences keep the surrounding stream on its side of the barrier.
+__device__ __forceinline__ void tile_barrier() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
 // One tile as 1 KB blocks of whole rows (ROWB bytes each), row j stored in
@@ -89,247 +118,556 @@ template <int NROWS, int ROWB>
 struct TileLayout {
     static constexpr int NBLK = NROWS * ROWB / 1024;
     static constexpr int BYTES = NBLK * BLK_PITCH;
-    static __device__ inline int byte(int row) { return (row % NBLK) * BLK_PITCH + (row / NBLK) * ROWB; }
+    static constexpr int ROW_BYTES = ROWB;
+    static __device__ __forceinline__ int byte(int row) { return (row % NBLK) * BLK_PITCH + (row / NBLK) * ROWB; }
 };
 
+// A key buffer holds the tile's rescaled keys, then its carry record (1 KB),
+// then the scalar-gate prefix G of its 128 keys (0 beyond the sequence).
 template <int K, int V>
 struct Layouts {
     using KL = TileLayout<TILE, 2 * K>;  // rescaled keys, row = key
     using VL = TileLayout<V, 2 * TILE>;  // values transposed, row = value channel
-};
-
-// Small per-tile rows, double-buffered like the tiles.
-template <int K>
-struct TileRows {
-    uint32_t dsh[2][K / 2];     // per buffer: 128*(Rc - Rc+1) per channel pair, as two u16
-    int32_t grow[2];            // some channel has Rc < Rc+1 (its prefix grows over the tile)
-    float gk[2][TILE];          // G (log2) of the tile's keys; 0 beyond the sequence
-};
-
-// One lane's accumulators and softmax state for its two query columns.
-template <int V>
-struct Acc {
-    f32x16 O[NB][V / 32];
-    float m[NB], l[NB];
+    static constexpr int REC_OFF = KL::BYTES;
+    static constexpr int GK_OFF = REC_OFF + REC_WORDS * 4;
+    static constexpr int KBUF = GK_OFF + TILE * 4;
 };
 
 template <int K>
-using QOp = bf16x8[NB][K / 16];  // [n-block][k-step]: 8 channels 16*s8 + 8*hl + e of one query
+using QOp = bf16x8[K / 16];  // [k-step]: 8 channels 16*s8 + 8*hl + e of one query
 
 // q~ at tile c straight from q and P: bf16(q * scale*log2e * exp2(P_i - Rc)).
-template <int K>
-__device__ inline void load_qop(const FwdArgs &a, const SegInfo &sg, int hq, int c, const int (&qrow)[NB],
-                                int hl, QOp<K> &qop) {
+// LEAN fences the scheduler between channel groups so the loads of one group
+// are in flight at a time (for use while the accumulators are live).
+template <int K, bool LEAN>
+__device__ __forceinline__ void load_qop(const FwdArgs &a, const SegInfo &sg, int hq, int c, int qrow, int hl,
+                                QOp<K> &qop) {
     constexpr int KS = K / 16;
     const int64_t HQ = a.HQ;
     const __bf16 *qg = static_cast<const __bf16 *>(a.q);
     const float *Rc = a.anchor + ((int64_t)(sg.tile_base + c) * HQ + hq) * K;
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-        const bool valid = qrow[nb] < sg.len;
-        const int64_t tok = (int64_t)sg.start + (valid ? qrow[nb] : 0);
-#pragma unroll
-        for (int s8 = 0; s8 < KS; ++s8) {
-            const int ch0 = 16 * s8 + 8 * hl;
-            const bf16x8 qv = *reinterpret_cast<const bf16x8 *>(qg + (tok * HQ + hq) * K + ch0);
-            const f32x8 pv8 = *reinterpret_cast<const f32x8 *>(a.P + (tok * HQ + hq) * K + ch0);
-            const f32x8 rv = *reinterpret_cast<const f32x8 *>(Rc + ch0);
-            f32x8 qh;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float xe = fminf(fmaxf(pv8[e] - rv[e], EXP2_LO), EXP2_HI);
-                qh[e] = valid ? (float)qv[e] * a.qscale * exp2f(xe) : 0.f;
-            }
-            qop[nb][s8] = __builtin_convertvector(qh, bf16x8);
-        }
-    }
-}
-
-// Carry q~ from tile c+1's anchor to tile c's: lower each bf16 exponent field
-// by 128*(Rc - Rc+1) with unsigned saturation on the magnitude, keeping the
-// sign.  Exact while the result is a normal number; a value pushed out of
-// range becomes 0 (or a bf16 denormal).
-template <int K>
-__device__ inline void shift_qop(const TileRows<K> &rows, int buf, int hl, QOp<K> &qop) {
-    constexpr int KS = K / 16;
+    if (LEAN) asm volatile("" : "+v"(qrow));  // keep the address arithmetic here, not hoisted
+    const bool valid = qrow < sg.len;
+    const int64_t tok = (int64_t)sg.start + (valid ? qrow : 0);
 #pragma unroll
     for (int s8 = 0; s8 < KS; ++s8) {
-        const uint4 d = *reinterpret_cast<const uint4 *>(&rows.dsh[buf][8 * s8 + 4 * hl]);
-        const uint32_t dv[4] = {d.x, d.y, d.z, d.w};
+        const int ch0 = 16 * s8 + 8 * hl;
+        const bf16x8 qv = *reinterpret_cast<const bf16x8 *>(qg + (tok * HQ + hq) * K + ch0);
+        const f32x8 pv8 = *reinterpret_cast<const f32x8 *>(a.P + (tok * HQ + hq) * K + ch0);
+        const f32x8 rv = *reinterpret_cast<const f32x8 *>(Rc + ch0);
+        f32x8 qh;
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            const uint4 x4 = __builtin_bit_cast(uint4, qop[nb][s8]);
-            const uint32_t xv[4] = {x4.x, x4.y, x4.z, x4.w};
-            uint32_t out[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const u16x2 mag = __builtin_bit_cast(u16x2, xv[e] & 0x7fff7fffu);
-                const u16x2 r = __builtin_elementwise_sub_sat(mag, __builtin_bit_cast(u16x2, dv[e]));
-                out[e] = (xv[e] & 0x80008000u) | __builtin_bit_cast(uint32_t, r);
-            }
-            qop[nb][s8] = __builtin_bit_cast(bf16x8, uint4{out[0], out[1], out[2], out[3]});
+        for (int e = 0; e < 8; ++e) {
+            const float xe = fminf(fmaxf(pv8[e] - rv[e], EXP2_LO), EXP2_HI);
+            qh[e] = valid ? (float)qv[e] * a.qscale * exp2f(xe) : 0.f;
         }
+        qop[s8] = __builtin_convertvector(qh, bf16x8);
+        if (LEAN) __builtin_amdgcn_sched_barrier(0);
     }
 }
 
-// Key fragments of sub-block b (A operands of the S^T MFMAs): lane (col, hl)
-// reads key row 32b + perm(col), channels 16*s8 + 8*hl .. +7.
-template <int K>
-__device__ inline void load_kfrag(const char *kb, int b, int kbase, bf16x8 (&kf)[K / 16]) {
-    using KL = typename Layouts<K, K>::KL;
-    // key 32b + perm(col): same block as key perm(col), (32 / NBLK) * b slots further
-    const char *base = kb + kbase + b * (SB / KL::NBLK) * (2 * K);
-#pragma unroll
-    for (int s8 = 0; s8 < K / 16; ++s8) kf[s8] = *reinterpret_cast<const bf16x8 *>(base + 32 * s8);
+// ---------------------------------------------------------------- loads
+// Direct buffer->LDS copies.  Each lane fetches BYTES from base + voff (a
+// buffer resource of nbytes over base, so fetches past its end read zeros)
+// and the wave writes them lane-linearly at LDS address `dst`.  They are
+// written as assembly so that the compiler does not track them: it cannot
+// tell the LDS buffers of copies in flight apart once control flow merges,
+// and would then wait for every copy before any LDS read.  Every read of
+// copied data here follows an explicit wait for the copies and a barrier.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+template <int BYTES>
+__device__ __forceinline__ void dma(const void *dst, const void *base, uint32_t nbytes, uint32_t voff,
+                                    uint32_t soff) {
+    static_assert(BYTES == 16 || BYTES == 4, "copy width");
+#if defined(__HIP_DEVICE_COMPILE__)
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    // base, stride 0, size in bytes, raw-buffer format word
+    const u32x4 rs = {(uint32_t)b, (uint32_t)(b >> 32) & 0xffffu, nbytes, 0x00020000u};
+    const uint32_t m0 = (uint32_t)(uintptr_t)(lds_void *)dst;
+    if constexpr (BYTES == 16)
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                     :
+                     : "s"(m0), "v"(voff), "s"(rs), "s"(soff)
+                     : "memory", "m0");
+    else
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+                     :
+                     : "s"(m0), "v"(voff), "s"(rs), "s"(soff)
+                     : "memory", "m0");
+#endif
 }
 
-// S^T for one sub-block (32 keys) against the wave's n-blocks.
-template <int K>
-__device__ inline void qk(const bf16x8 (&kf)[K / 16], const QOp<K> &qop, f32x16 (&S)[NB]) {
-#pragma unroll
-    for (int s8 = 0; s8 < K / 16; ++s8)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-            S[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s8], qop[nb][s8], s8 ? S[nb] : f32x16{}, 0, 0, 0);
+// One tile laid out as L: one wave instruction per 1 KB block, written
+// lane-linearly; lane l fetches 16 bytes of the block's row l / (ROW_BYTES/16).
+// The blocks are spread over the workgroup's waves.
+template <class L>
+__device__ __forceinline__ uint32_t tile_lane_offset(int lane) {
+    constexpr int CPR = L::ROW_BYTES / 16;  // 16-byte chunks per row
+    return (uint32_t)((lane / CPR) * L::NBLK * L::ROW_BYTES + (lane % CPR) * 16);
 }
-
-// O^T += v^T p^T for sub-block b (two 16-key MFMA k-steps).
-template <int K, int V>
-__device__ inline void pv(const char *vb, int b, int vbase, const bf16x8 (&P)[NB][2], Acc<V> &acc) {
-    constexpr int VT = V / 32;
-    using VL = typename Layouts<K, V>::VL;
-    const char *base = vb + vbase;
+template <class L>
+__device__ __forceinline__ void load_tile(char *dst, const void *src, uint32_t lane_off, int w) {
+    static_assert(L::NBLK % NW == 0, "blocks split evenly over waves");
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        const int ks = 2 * b + t;
-#pragma unroll
-        for (int vt = 0; vt < VT; ++vt) {
-            // lane (col, hl): value row 32*vt + col, keys 16*ks + 8*hl .. +7
-            const bf16x8 a = *reinterpret_cast<const bf16x8 *>(
-                base + vt * (32 / VL::NBLK) * (2 * TILE) + 32 * ks);
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
-                acc.O[nb][vt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, P[nb][t], acc.O[nb][vt], 0, 0, 0);
-        }
-    }
-}
-
-// Online softmax of one sub-block, first half: masked scores into x and the
-// running max.  The max is raised only when the sub-block exceeds it by more
-// than RESCALE; then l is rescaled here and alpha (1 otherwise) is returned
-// for O, which the caller rescales with rescale_o once every P formed with
-// the old max has been accumulated.  MASKED applies causality, the window
-// and the sequence end; HAS_G subtracts the keys' scalar-gate prefix (the
-// query's own G_i is added back in the epilogue).
-template <int K, int V, bool MASKED, bool HAS_G>
-__device__ inline void softmax_max(const TileRows<K> &rows, int buf, int b, int hl,
-                                   const f32x16 (&S)[NB], Acc<V> &acc, float (&x)[NB][16],
-                                   float (&alpha)[NB], int key0, const int (&qrow)[NB], int len,
-                                   int window) {
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int kin = SB * b + 16 * (r / 8) + 8 * hl + (r % 8);  // key within the tile
-            float y = S[nb][r];
-            if (HAS_G) y -= rows.gk[buf][kin];
-            if (MASKED) {
-                const int key = key0 + kin;
-                bool vis = key <= qrow[nb] && key < len;
-                if (window > 0) vis = vis && (qrow[nb] - key < window);
-                y = vis ? y : -INFINITY;
-            }
-            x[nb][r] = y;
-            mx = fmaxf(mx, y);
-        }
-        const float mt = pair_max(mx);
-        const float m_new = mt > acc.m[nb] + RESCALE ? mt : acc.m[nb];
-        alpha[nb] = fast_exp2(acc.m[nb] - m_new);
-        acc.l[nb] *= alpha[nb];
-        acc.m[nb] = m_new;
-    }
-}
-
-// O *= alpha when some lane raised its max (rare after the first tiles).
-template <int V>
-__device__ inline void rescale_o(Acc<V> &acc, const float (&alpha)[NB]) {
-    bool any = false;
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) any = any || alpha[nb] != 1.0f;
-    if (__any(any)) {
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-            for (int vt = 0; vt < V / 32; ++vt) acc.O[nb][vt] *= alpha[nb];
-    }
-}
-
-// Second half: p = exp2(x - m) as bf16 (the PV operand) and the row sum of
-// the rounded p, as the PV product sees it.
-template <int V>
-__device__ inline void softmax_exp(const float (&x)[NB][16], Acc<V> &acc, bf16x8 (&P)[NB][2]) {
-    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-        float sum = acc.l[nb];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            f32x8 pv8;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) pv8[e] = fast_exp2(x[nb][8 * t + e] - acc.m[nb]);
-            P[nb][t] = __builtin_convertvector(pv8, bf16x8);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const bf16x2 pr = {P[nb][t][2 * e], P[nb][t][2 * e + 1]};
-                sum = __builtin_amdgcn_fdot2_f32_bf16(pr, one, sum, false);
-            }
-        }
-        acc.l[nb] = sum;
-    }
-}
-
-// Direct global->LDS copy of one key tile (k~) and one value tile (v^T) into
-// buffer `buf`: one wave instruction per 1 KB block, written lane-linearly;
-// lane l fetches 16 bytes of the block's row l / (ROWB/16).
-template <int K, int V>
-__device__ inline void load_tile(char *kd, char *vd, const __bf16 *kt, const __bf16 *vt, int w,
-                                 int lane) {
-    using KL = typename Layouts<K, V>::KL;
-    using VL = typename Layouts<K, V>::VL;
-    constexpr int KCPR = K / 8, VCPR = TILE / 8;  // 16-byte chunks per row
-    static_assert(KL::NBLK % NW == 0 && VL::NBLK % NW == 0, "blocks split evenly over waves");
-#pragma unroll
-    for (int i = 0; i < KL::NBLK / NW; ++i) {
+    for (int i = 0; i < L::NBLK / NW; ++i) {
         const int blk = i * NW + w;
-        const int row = (lane / KCPR) * KL::NBLK + blk;
-        const __bf16 *src = kt + row * K + (lane % KCPR) * 8;
-        __builtin_amdgcn_global_load_lds((glb_cvoid *)src, (lds_void *)(kd + blk * BLK_PITCH),
-                                         16, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < VL::NBLK / NW; ++i) {
-        const int blk = i * NW + w;
-        const int row = (lane / VCPR) * VL::NBLK + blk;
-        const __bf16 *src = vt + row * TILE + (lane % VCPR) * 8;
-        __builtin_amdgcn_global_load_lds((glb_cvoid *)src, (lds_void *)(vd + blk * BLK_PITCH),
-                                         16, 0, 0);
+        dma<16>(dst + blk * BLK_PITCH, src, L::NBLK * 1024, lane_off, blk * L::ROW_BYTES);
     }
 }
+// Wave w's eighth of a tile's 1 KB carry record (8 lanes of 16 bytes).
+__device__ __forceinline__ void load_rec(char *dst, const uint32_t *rec, int w, int lane) {
+    if (lane < 8) dma<16>(dst + 128 * w, rec, REC_WORDS * 4, (uint32_t)(128 * w + 16 * lane), 0);
+}
+// Wave w's 16 keys of a tile's G values, gathered 4 bytes per lane from g0 =
+// G of the tile's first key; keys at or beyond `nkeys` read 0.  The whole
+// offset is in the lane offset, which the bounds check covers.
+__device__ __forceinline__ void load_gk(char *dst, const float *g0, int64_t HQ, int nkeys, int w, int lane) {
+    const uint32_t nbytes = nkeys > 0 ? (uint32_t)((int64_t)(nkeys - 1) * HQ * 4 + 4) : 0u;
+    if (lane < 16) dma<4>(dst + 64 * w, g0, nbytes, (uint32_t)((16 * w + lane) * HQ * 4), 0);
+}
+
+// ---------------------------------------------------------------- tile plan
+// The instruction stream of one tile, fixed at compile time.  Per step b
+// (3, 2, 1, 0): softmax stages SMA (mask, gate, first max level), SMB (max),
+// SMC (raise test), SMD0..7 (exps, packing and row sums of two keys each),
+// SME; PV products (index t*VT + vt) and QK products (index s8); CARRY of one
+// channel step of q~ to the next tile (first half in step 1 after its last
+// use, second half in step 0); the barriers BARV (start of step 2) and BARK
+// (in step 0, after the carries); RESC (an owed rescale of O) ends each step.
+// QK products only start after SMC, which may move m and with it the
+// accumulator start -m.
+enum OpKind : int { O_PV, O_QK, O_CARRY, O_SMA, O_SMB, O_SMC, O_SMD, O_SME, O_BARV, O_BARK, O_RESC };
+struct TOp {
+    int kind, step, idx;
+};
+constexpr bool is_read(int kind) { return kind == O_PV || kind == O_QK || kind == O_CARRY; }
+
+template <int K, int V>
+struct TilePlan {
+    static constexpr int VT = V / 32, KS = K / 16;
+    static constexpr int NPV = 2 * VT, NQK = KS, NSMD = 8, NC1 = KS / 2;
+    static constexpr int MAXOPS = NSB * (NPV + NQK + KS + 13) + 4;
+    using OpArr = std::array<TOp, MAXOPS>;
+
+    static constexpr int build(OpArr &a) {
+        int n = 0;
+        for (int b = NSB - 1; b >= 0; --b) {
+            int pv = 0, qk = 0, smd = 0;
+            if (b == 2) {
+                a[n++] = TOp{O_BARV, b, 0};
+                a[n++] = TOp{O_SMA, b, 0};
+                a[n++] = TOp{O_SMB, b, 0};
+                a[n++] = TOp{O_SMC, b, 0};
+            } else {
+                a[n++] = TOp{O_PV, b, pv++};
+                a[n++] = TOp{O_SMA, b, 0};
+                a[n++] = TOp{O_PV, b, pv++};
+                a[n++] = TOp{O_SMB, b, 0};
+                a[n++] = TOp{O_PV, b, pv++};
+                a[n++] = TOp{O_SMC, b, 0};
+                if (b == 0) {
+                    for (int s8 = NC1; s8 < KS; ++s8) {
+                        a[n++] = TOp{O_CARRY, b, s8};
+                        if (pv < NPV - 1) a[n++] = TOp{O_PV, b, pv++};
+                    }
+                    a[n++] = TOp{O_BARK, b, 0};
+                }
+            }
+            while (pv < NPV || qk < NQK) {
+                if (qk < NQK) {
+                    a[n++] = TOp{O_QK, b, qk};
+                    if (b == 1 && qk < NC1) a[n++] = TOp{O_CARRY, b, qk};
+                    ++qk;
+                    if (smd < NSMD) a[n++] = TOp{O_SMD, b, smd++};
+                }
+                if (pv < NPV) {
+                    a[n++] = TOp{O_PV, b, pv++};
+                    if (smd < NSMD) a[n++] = TOp{O_SMD, b, smd++};
+                }
+            }
+            while (smd < NSMD) a[n++] = TOp{O_SMD, b, smd++};
+            a[n++] = TOp{O_SME, b, 0};
+            a[n++] = TOp{O_RESC, b, 0};
+        }
+        return n;
+    }
+    static constexpr OpArr make_ops() {
+        OpArr a{};
+        build(a);
+        return a;
+    }
+    static constexpr int make_n() {
+        OpArr a{};
+        return build(a);
+    }
+    static constexpr OpArr OPS = make_ops();
+    static constexpr int N = make_n();
+
+    static constexpr int make_nr() {
+        int r = 0;
+        for (int i = 0; i < N; ++i) r += is_read(OPS[i].kind) ? 1 : 0;
+        return r;
+    }
+    static constexpr int NR = make_nr();  // LDS operand reads per tile
+    // Reads kept in flight: the largest of 7..4 that divides NR, so a read has
+    // the same ring slot in every tile.
+    static constexpr int NPF = NR % 7 == 0 ? 7 : NR % 6 == 0 ? 6 : NR % 5 == 0 ? 5 : 4;
+    static_assert(NR % NPF == 0, "reads per tile must fill whole rings");
+
+    static constexpr int pos_of(int kind) {
+        for (int i = 0; i < N; ++i)
+            if (OPS[i].kind == kind) return i;
+        return -1;
+    }
+    static constexpr int POS_BARV = pos_of(O_BARV), POS_BARK = pos_of(O_BARK);
+
+    using ReadArr = std::array<int, MAXOPS>;
+    static constexpr ReadArr make_cons() {  // position of the op consuming read r
+        ReadArr c{};
+        int k = 0;
+        for (int i = 0; i < N; ++i)
+            if (is_read(OPS[i].kind)) c[k++] = i;
+        return c;
+    }
+    static constexpr ReadArr CONS = make_cons();
+    static constexpr int consumer(int r) { return CONS[r % NR] + (r / NR) * N; }  // r >= NR: next tile
+    static constexpr TOp read_op(int r) { return OPS[CONS[r % NR]]; }
+    static constexpr ReadArr make_read_of() {  // read index consumed by the op at a position, else -1
+        ReadArr ro{};
+        int k = 0;
+        for (int i = 0; i < MAXOPS; ++i) ro[i] = -1;
+        for (int i = 0; i < N; ++i)
+            if (is_read(OPS[i].kind)) ro[i] = k++;
+        return ro;
+    }
+    static constexpr ReadArr READ_OF = make_read_of();
+    // The position after which read r (NPF <= r < NR + NPF) is issued: once
+    // its ring slot is free (read r - NPF consumed) and the data it reads is
+    // in place (after the barrier that publishes it, for the values and keys
+    // that arrive during this tile).
+    static constexpr int guard(int r) {
+        const TOp o = read_op(r);
+        if (r < NR) {
+            if (o.kind == O_PV && o.step <= 2) return POS_BARV;  // this tile's values
+            if (o.kind == O_QK && o.step == 0) return POS_BARK;  // the next tile's keys
+            return -1;
+        }
+        return o.kind == O_QK ? POS_BARK : -1;  // next tile's first reads: its keys
+    }
+    static constexpr int issue_pos(int r) {
+        const int nat = consumer(r - NPF);
+        const int g = guard(r);
+        return nat > g ? nat : g;
+    }
+    static constexpr bool check() {
+        for (int r = 0; r < NPF; ++r)
+            if (read_op(r).step != NSB - 1) return false;  // the prefetched reads belong to step 3
+        for (int r = NPF; r < NR + NPF; ++r)
+            if (!(issue_pos(r) < consumer(r) && issue_pos(r) < N)) return false;
+        return true;
+    }
+    static_assert(check(), "every read is issued before its use and within the tile");
+};
+
+// ---------------------------------------------------------------- per-wave pipeline
+template <int K, int V, bool HAS_G>
+struct Wave {
+    using LY = Layouts<K, V>;
+    using KL = typename LY::KL;
+    using VL = typename LY::VL;
+    using Plan = TilePlan<K, V>;
+    static constexpr int VT = V / 32, KS = K / 16, NPF = Plan::NPF;
+
+    // per-lane constants
+    int kbase, vbase, hl, qrow;
+    // accumulators and softmax state for the lane's query column: m is the
+    // running max (log2 units) the scores are taken relative to; negm holds -m
+    // in all 16 accumulator slots and starts every QK product.  Until a lane
+    // has seen a visible key m is 0 and not yet valid.
+    f32x16 O[VT];
+    f32x16 negm;
+    float m, l;
+    float alpha;  // rescale O still owes for the current step (1 if none)
+    bool valid, owe;
+    QOp<K> qop;
+    f32x16 S[2];           // S[b & 1]: scores of the sub-block softmaxed in step b
+    uint32_t Pw[2][2][4];  // Pw[b & 1][t]: packed bf16 p of that sub-block, keys 16t + 8hl + e
+    bf16x8 ring[NPF];      // LDS operand reads in flight
+    float red[5];          // partial maxima of the current step
+    float mt;              // the step's max, relative to m
+    float part[2];         // partial row sums of the current step
+
+    // buffers: keys of this tile and the next (older) one, values of this tile
+    // and of the previous (newer) one
+    const char *kcur, *knext, *vcur, *vprev;
+
+    // per-tile facts (wave-uniform)
+    int key_tile0;   // first key of the current tile (sequence-relative)
+    bool mask_tile;      // the tile needs causal / sequence-end masks for this wave
+    bool carry_on;       // carry q~ on to the next tile by the record's shifts
+    bool carry_on_grow;  // ... by rebuilding it there (some channel's prefix grows)
+    int window, len, q0w;
+
+    __device__ static __forceinline__ bf16x8 as_bf16(const uint32_t (&w)[4]) {
+        return __builtin_bit_cast(bf16x8, uint4{w[0], w[1], w[2], w[3]});
+    }
+
+    // ---- operand address of read r (NEXT: a read of the next tile's step 3)
+    template <int R>
+    __device__ __forceinline__ const bf16x8 *src() const {
+        constexpr bool NEXT = R >= Plan::NR;
+        constexpr TOp o = Plan::read_op(R);
+        if constexpr (o.kind == O_PV) {
+            constexpr int vt = o.idx % VT, t = o.idx / VT;
+            constexpr int sub = o.step == NSB - 1 ? 0 : o.step + 1;  // the previous sub-block
+            constexpr int off = vt * (32 / VL::NBLK) * (2 * TILE) + 32 * (2 * sub + t);
+            const char *vb = o.step == NSB - 1 ? (NEXT ? vcur : vprev) : vcur;
+            return reinterpret_cast<const bf16x8 *>(vb + vbase + off);
+        } else if constexpr (o.kind == O_QK) {
+            constexpr int sub = o.step == 0 ? NSB - 1 : o.step - 1;  // the next sub-block
+            constexpr int off = sub * (SB / KL::NBLK) * (2 * K) + 32 * o.idx;
+            const char *kb = (o.step == 0 || NEXT) ? knext : kcur;
+            return reinterpret_cast<const bf16x8 *>(kb + kbase + off);
+        } else {
+            // carry record words 8*s8 + 4*hl .. +3 of the current tile
+            return reinterpret_cast<const bf16x8 *>(kcur + LY::REC_OFF + 32 * o.idx + 16 * hl);
+        }
+    }
+    template <int R>
+    __device__ __forceinline__ void read() {
+        ring[R % NPF] = *src<R>();
+    }
+    template <int... Rs>
+    __device__ __forceinline__ void read_first(std::integer_sequence<int, Rs...>) {
+        (read<Rs>(), ...);
+    }
+
+    // ---- softmax stages of step B on S[B & 1]
+    template <int B>
+    __device__ __forceinline__ void sma() {
+        f32x16 &s = S[B & 1];
+        if (mask_tile || (window > 0 && q0w + WQ - 1 - (key_tile0 + SB * B) >= window)) {
+            // visible keys of this lane's query, as offsets from its first key in the sub-block:
+            // min with +inf inside [klo, khi], with -inf outside, where the sign of
+            // (off - klo) | (khi - off) marks outside (no compares)
+            const int kb0 = key_tile0 + SB * B + 8 * hl;
+            const int khi = min(qrow, len - 1) - kb0;
+            const int klo = window > 0 ? qrow - window + 1 - kb0 : -(1 << 30);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int off = 16 * (r / 8) + (r % 8);
+                const int out = (off - klo) | (khi - off);
+                s[r] = fminf(s[r], __int_as_float(0x7f800000 | (out & INT_MIN)));
+            }
+        }
+        if (HAS_G) {
+            const float *gk = reinterpret_cast<const float *>(kcur + LY::GK_OFF) + SB * B + 8 * hl;
+            const f32x8 g0 = *reinterpret_cast<const f32x8 *>(gk);
+            const f32x8 g1 = *reinterpret_cast<const f32x8 *>(gk + 16);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                s[e] -= g0[e];
+                s[8 + e] -= g1[e];
+            }
+        }
+        red[0] = fmaxf(fmaxf(s[0], s[1]), s[2]);
+        red[1] = fmaxf(fmaxf(s[3], s[4]), s[5]);
+        red[2] = fmaxf(fmaxf(s[6], s[7]), s[8]);
+        red[3] = fmaxf(fmaxf(s[9], s[10]), s[11]);
+        red[4] = fmaxf(fmaxf(s[12], s[13]), s[14]);
+    }
+    template <int B>
+    __device__ __forceinline__ void smb() {
+        const f32x16 &s = S[B & 1];
+        const float a = fmaxf(fmaxf(red[0], red[1]), red[2]);
+        const float b = fmaxf(fmaxf(red[3], red[4]), s[15]);
+        mt = pair_max(fmaxf(a, b));
+    }
+    template <int B>
+    __device__ __forceinline__ void smc() {
+        const bool raise = valid ? mt > RESCALE : mt > -FLT_MAX;
+        if (__any(raise)) {
+            const float delta = raise ? mt : 0.f;
+            const float al = fast_exp2(-delta);
+            m += delta;
+            l *= al;
+            alpha *= al;
+            owe = owe || raise;
+            valid = valid || raise;
+            negm -= delta;
+            S[B & 1] -= delta;
+        }
+    }
+    template <int B, int KK>
+    __device__ __forceinline__ void smd() {
+        const f32x16 &s = S[B & 1];
+        const float e0 = fast_exp2(s[2 * KK]), e1 = fast_exp2(s[2 * KK + 1]);
+        const bf16x2 p = {(__bf16)e0, (__bf16)e1};
+        const uint32_t w = __builtin_bit_cast(uint32_t, p);
+        Pw[B & 1][KK / 4][KK % 4] = w;
+        const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+        // row sum of the rounded p, two independent chains
+        part[KK & 1] = __builtin_amdgcn_fdot2_f32_bf16(p, one, KK < 2 ? 0.f : part[KK & 1], false);
+    }
+    __device__ __forceinline__ void sme() { l += part[0] + part[1]; }
+    __device__ __forceinline__ void resc() {
+        if (__any(owe)) {
+#pragma unroll
+            for (int vt = 0; vt < VT; ++vt) O[vt] *= alpha;
+        }
+        alpha = 1.f;
+        owe = false;
+    }
+};
+
+// ---------------------------------------------------------------- the kernel
+template <int K, int V, bool HAS_G>
+struct Kernel {
+    using W = Wave<K, V, HAS_G>;
+    using LY = Layouts<K, V>;
+    using KL = typename LY::KL;
+    using VL = typename LY::VL;
+    using Plan = TilePlan<K, V>;
+    static constexpr int VT = V / 32, KS = K / 16, NPF = Plan::NPF, NR = Plan::NR, N = Plan::N;
+    // buffer loads per wave per tile: the tile's blocks, then a slice of the
+    // carry record (and of G) for the keys
+    static constexpr int KLOADS = KL::NBLK / NW + 1 + (HAS_G ? 1 : 0), VLOADS = VL::NBLK / NW;
+
+    const FwdArgs &a;
+    W wv;
+    char *k0, *k1, *v0, *v1;
+    SegInfo sg;
+    int hq, h, w, lane, qt_w, c_lo;
+    uint32_t klane, vlane;
+    bool wave_on;
+
+    // per-tile facts of tile c whose keys (and carry record) are in kcur
+    __device__ __forceinline__ void tile_facts(int c, const char *kcur) {
+        wv.key_tile0 = TILE * c;
+        wv.mask_tile = c >= qt_w;
+        const bool grow = reinterpret_cast<const uint32_t *>(kcur + LY::REC_OFF)[REC_GROW] != 0u;
+        const bool go_on = wave_on && c <= qt_w && c - 1 >= c_lo;
+        wv.carry_on = go_on && !grow;
+        wv.carry_on_grow = go_on && grow;
+    }
+
+    __device__ __forceinline__ const __bf16 *kt_tile(int c) const {
+        return static_cast<const __bf16 *>(a.kt) + ((int64_t)(sg.tile_base + c) * a.HQ + hq) * TILE * K;
+    }
+    __device__ __forceinline__ const __bf16 *vt_tile(int c) const {
+        return static_cast<const __bf16 *>(a.vt) + ((int64_t)(sg.tile_base + c) * a.H + h) * V * TILE;
+    }
+    // keys of tile c (its carry record and G first) into key buffer kd
+    __device__ __forceinline__ void issue_k(char *kd, int c) const {
+        load_tile<KL>(kd, kt_tile(c), klane, w);
+        load_rec(kd + LY::REC_OFF, a.rec + ((int64_t)(sg.tile_base + c) * a.HQ + hq) * REC_WORDS, w, lane);
+        if (HAS_G)
+            load_gk(kd + LY::GK_OFF, a.G + ((int64_t)sg.start + (int64_t)c * TILE) * a.HQ + hq, a.HQ,
+                    sg.len - c * TILE, w, lane);
+    }
+    __device__ __forceinline__ void issue_v(char *vd, int c) const { load_tile<VL>(vd, vt_tile(c), vlane, w); }
+
+    // ---- one op of the plan at position P for tile c held in buffers of parity PB
+    template <int PB, int P>
+    __device__ __forceinline__ void op(int c) {
+        constexpr TOp o = Plan::OPS[P];
+        constexpr int B = o.step;
+        if constexpr (o.kind == O_PV) {
+            constexpr int vt = o.idx % VT, t = o.idx / VT;
+            const bf16x8 x = wv.ring[Plan::READ_OF[P] % NPF];
+            wv.O[vt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, W::as_bf16(wv.Pw[(B + 1) & 1][t]), wv.O[vt], 0,
+                                                               0, 0);
+        } else if constexpr (o.kind == O_QK) {
+            const bf16x8 x = wv.ring[Plan::READ_OF[P] % NPF];
+            f32x16 &sn = wv.S[(B + 1) & 1];
+            sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, wv.qop[o.idx], o.idx == 0 ? wv.negm : sn, 0, 0, 0);
+        } else if constexpr (o.kind == O_CARRY) {
+            const bf16x8 x = wv.ring[Plan::READ_OF[P] % NPF];
+            if (wv.carry_on) {
+                // lower each bf16 exponent field by the shift, saturating on the magnitude
+                const uint4 d = __builtin_bit_cast(uint4, x);
+                const uint32_t dv[4] = {d.x, d.y, d.z, d.w};
+                const uint4 x4 = __builtin_bit_cast(uint4, wv.qop[o.idx]);
+                const uint32_t xv[4] = {x4.x, x4.y, x4.z, x4.w};
+                uint32_t out[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const u16x2 mag = __builtin_bit_cast(u16x2, xv[e] & 0x7fff7fffu);
+                    const u16x2 r = __builtin_elementwise_sub_sat(mag, __builtin_bit_cast(u16x2, dv[e]));
+                    out[e] = (xv[e] & 0x80008000u) | __builtin_bit_cast(uint32_t, r);
+                }
+                wv.qop[o.idx] = __builtin_bit_cast(bf16x8, uint4{out[0], out[1], out[2], out[3]});
+            }
+        } else if constexpr (o.kind == O_SMA) {
+            wv.template sma<B>();
+        } else if constexpr (o.kind == O_SMB) {
+            wv.template smb<B>();
+        } else if constexpr (o.kind == O_SMC) {
+            wv.template smc<B>();
+        } else if constexpr (o.kind == O_SMD) {
+            wv.template smd<B, o.idx>();
+        } else if constexpr (o.kind == O_SME) {
+            wv.sme();
+        } else if constexpr (o.kind == O_RESC) {
+            wv.resc();
+        } else if constexpr (o.kind == O_BARV) {
+            // the values of tile c are in place once the key batch issued after them
+            // is the only one left in flight
+            // (every tile issues the same loads, past the last one those of tile
+            // c_lo again into a buffer no longer read, so that the counts are fixed)
+            wait_vm<KLOADS>();
+            tile_barrier();
+            issue_v(PB ? v0 : v1, max(c - 1, c_lo));
+        } else if constexpr (o.kind == O_BARK) {
+            wait_vm<VLOADS>();
+            tile_barrier();
+            if (wv.carry_on_grow) {
+                // some channel's prefix grows into tile c-1: rebuild q~ there instead
+                // (before the key loads are issued, so that waiting for these
+                // global loads never waits for them)
+                load_qop<K, true>(a, sg, hq, c - 1, wv.qrow, wv.hl, wv.qop);
+            }
+            issue_k(PB ? k1 : k0, max(c - 2, c_lo));
+        }
+    }
+    // reads issued after the op at position P
+    template <int P, int R>
+    __device__ __forceinline__ void maybe_read() {
+        if constexpr (Plan::issue_pos(R) == P) wv.template read<R>();
+    }
+    template <int P, int... Rs>
+    __device__ __forceinline__ void reads_after(std::integer_sequence<int, Rs...>) {
+        (maybe_read<P, Rs + NPF>(), ...);
+    }
+    template <int PB, int P>
+    __device__ __forceinline__ void step(int c) {
+        __builtin_amdgcn_sched_barrier(0);
+        op<PB, P>(c);
+        reads_after<P>(std::make_integer_sequence<int, NR>{});
+    }
+    template <int PB, int... Ps>
+    __device__ __forceinline__ void run_tile(int c, std::integer_sequence<int, Ps...>) {
+        (step<PB, Ps>(c), ...);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+};
 
 template <int K, int V, bool HAS_G>
 __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
-    constexpr int KS = K / 16, VT = V / 32;
-    using KL = typename Layouts<K, V>::KL;
-    using VL = typename Layouts<K, V>::VL;
+    using KR = Kernel<K, V, HAS_G>;
+    using W = Wave<K, V, HAS_G>;
+    using LY = Layouts<K, V>;
+    using KL = typename LY::KL;
+    using VL = typename LY::VL;
+    using Plan = TilePlan<K, V>;
+    constexpr int VT = V / 32, KS = K / 16, NPF = Plan::NPF;
     // Each tile buffer is an LDS variable of its own: the compiler then knows
     // that reading one buffer does not depend on the direct loads still
-    // filling the other, and does not wait for them.
-    __shared__ __attribute__((aligned(16))) char k0[KL::BYTES];
-    __shared__ __attribute__((aligned(16))) char k1[KL::BYTES];
+    // filling another, and does not wait for them.
+    __shared__ __attribute__((aligned(16))) char k0[LY::KBUF];
+    __shared__ __attribute__((aligned(16))) char k1[LY::KBUF];
     __shared__ __attribute__((aligned(16))) char v0[VL::BYTES];
     __shared__ __attribute__((aligned(16))) char v1[VL::BYTES];
-    __shared__ TileRows<K> rows;
 
     const int nblocks_max = (a.max_tiles + 1) / 2;  // 256-row blocks of the longest sequence
     const int npairs = (nblocks_max + 1) / 2;
@@ -346,198 +684,137 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
     const int nblk = (sg.len + BQ - 1) / BQ;
     if (p >= (nblk + 1) / 2) return;
 
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar registers and branches
     const int col = lane & 31, hl = lane >> 5;
-    const int var = w / (NW / 2);  // which of the block's two anchor tiles is this wave's diagonal
-    // per-lane byte offsets of the MFMA fragments in a tile buffer
-    const int kbase = KL::byte(key_perm(col)) + 16 * hl;
-    const int vbase = VL::byte(col) + 16 * hl;
-    const int h = hq / (a.HQ / a.H);
-    const __bf16 *qg = static_cast<const __bf16 *>(a.q);
-    const __bf16 *ktg = static_cast<const __bf16 *>(a.kt);
-    const __bf16 *vtg = static_cast<const __bf16 *>(a.vt);
-    __bf16 *og = static_cast<__bf16 *>(a.o);
     const int64_t HQ = a.HQ;
-    // threads 0..63 prepare a channel pair of each tile's shift row, threads 0..127 one key's G
-    const int pv_j = tid;
-    const bool pv_pair = tid < 64 && 2 * pv_j < K;
+
+    // Values are multiplied by p = 0 before their first use in a block: give the
+    // second value buffer finite contents once.
+    for (int i = tid; i < VL::BYTES / 16; i += NW * 64) reinterpret_cast<uint4 *>(v1)[i] = uint4{0, 0, 0, 0};
+
+    KR kr{a, {}, k0, k1, v0, v1, sg, hq, hq / (a.HQ / a.H), w, lane, 0, 0,
+          tile_lane_offset<KL>(lane), tile_lane_offset<VL>(lane), false};
+    W &wv = kr.wv;
+    wv.kbase = KL::byte(key_perm(col)) + 16 * hl;
+    wv.vbase = VL::byte(col) + 16 * hl;
+    wv.hl = hl;
 
     for (int pass = 0; pass < 2; ++pass) {
         const int u = pass == 0 ? p : nblk - 1 - p;
         if (pass == 1 && u == p) break;
-        const int qt_w = 2 * u + var;
+        const int qt_w = 2 * u + w / (NW / 2);
         const int q0w = BQ * u + WQ * w;
         const bool wave_on = q0w < sg.len;
-        int qrow[NB];
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) qrow[nb] = q0w + 32 * nb + col;
+        const int qrow = q0w + col;
         const int c_hi = min(2 * u + 1, ntiles - 1);
         int c_lo = 0;
         if (a.window > 0) {
             const int kmin = BQ * u - a.window + 1;
             c_lo = kmin > 0 ? kmin / TILE : 0;
         }
+        kr.qt_w = qt_w;
+        kr.c_lo = c_lo;
+        wv.qrow = qrow;
+        wv.window = a.window;
+        wv.len = sg.len;
+        wv.q0w = q0w;
 
-        float g_i[NB];
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) g_i[nb] = 0.f;
-        if (HAS_G && wave_on) {
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
-                if (qrow[nb] < sg.len) g_i[nb] = a.G[((int64_t)sg.start + qrow[nb]) * HQ + hq];
-        }
-        QOp<K> qop;
+        float g_i = 0.f;
+        if (HAS_G && wave_on && qrow < sg.len) g_i = a.G[((int64_t)sg.start + qrow) * HQ + hq];
 
-        Acc<V> acc;
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
+        for (int vt = 0; vt < VT; ++vt) wv.O[vt] = f32x16{};
+        wv.negm = f32x16{};
+        wv.m = 0.f;
+        wv.l = 0.f;
+        wv.alpha = 1.f;
+        wv.valid = false;
+        wv.owe = false;
 #pragma unroll
-            for (int vt = 0; vt < VT; ++vt) acc.O[nb][vt] = f32x16{};
-            acc.m[nb] = -FLT_MAX;
-            acc.l[nb] = 0.f;
-        }
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) wv.Pw[0][t][e] = 0u;
 
-        // per-tile rows prepared by threads 0..127: the anchor pair of the tile being
-        // prepared (rc) and of the tile after it (rp), and one key's G
-        float rc0 = 0.f, rc1 = 0.f, rp0 = 0.f, rp1 = 0.f, gval = 0.f;
-        auto fetch_rows = [&](int c) {
-            if (pv_pair) {
-                const float *R = a.anchor + ((int64_t)(sg.tile_base + c) * HQ + hq) * K;
-                rc0 = R[2 * pv_j];
-                rc1 = R[2 * pv_j + 1];
-            }
-            if (HAS_G && tid < TILE) {
-                const int j = c * TILE + tid;
-                gval = j < sg.len ? a.G[((int64_t)sg.start + j) * HQ + hq] : 0.f;
-            }
-        };
-        auto write_rows = [&](int bb, bool first) {
-            if (tid < 64) {
-                bool up = false;
-                if (pv_pair) {
-                    const float d0 = first ? 0.f : rc0 - rp0, d1 = first ? 0.f : rc1 - rp1;  // Rc - Rc+1
-                    up = d0 < 0.f || d1 < 0.f;
-                    const uint32_t s0 = (uint32_t)fminf(fmaxf(d0, 0.f), 255.f) * 128u;
-                    const uint32_t s1 = (uint32_t)fminf(fmaxf(d1, 0.f), 255.f) * 128u;
-                    rows.dsh[bb][pv_j] = s0 | (s1 << 16);
-                }
-                const bool any_up = __any(up);
-                if (tid == 0) rows.grow[bb] = any_up;
-            }
-            if (HAS_G && tid < TILE) rows.gk[bb][tid] = gval;
-            rp0 = rc0;
-            rp1 = rc1;
-        };
-        auto kt_tile = [&](int c) { return ktg + ((int64_t)(sg.tile_base + c) * HQ + hq) * TILE * K; };
-        auto vt_tile = [&](int c) { return vtg + ((int64_t)(sg.tile_base + c) * a.H + h) * V * TILE; };
-
-        // ---- prologue: tile c_hi into buffer 0
-        __syncthreads();  // the previous block's last reads of both buffers are done
-        fetch_rows(c_hi);
-        load_tile<K, V>(k0, v0, kt_tile(c_hi), vt_tile(c_hi), w, lane);
-        write_rows(0, true);
-        if (c_hi - 1 >= c_lo) fetch_rows(c_hi - 1);
+        // ---- prologue: q~ at the diagonal tile; tile c_hi into buffers 0, the keys of
+        // tile c_hi - 1 into key buffer 1
+        __syncthreads();  // the previous block's last reads of every buffer are done
+        if (wave_on) load_qop<K, false>(a, sg, hq, qt_w, qrow, hl, wv.qop);
+        kr.issue_k(k0, c_hi);
+        kr.issue_v(v0, c_hi);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-
-        // One key tile c held in buffer PB (tile c_hi in buffer 0, then alternating);
-        // the buffer is a compile-time choice so every LDS access names its variable.
-        auto tile_step = [&](int c, auto pb_tag) {
-            constexpr int PB = decltype(pb_tag)::value;
-            const char *kb = PB ? k1 : k0;
-            const char *vb = PB ? v1 : v0;
-            if (c - 1 >= c_lo)
-                load_tile<K, V>(PB ? k0 : k1, PB ? v0 : v1, kt_tile(c - 1), vt_tile(c - 1), w, lane);
-
-            if (wave_on && c <= qt_w) {
-                const bool diag = c == qt_w;
-                const bool wtile = a.window > 0 && q0w + WQ - 1 - TILE * c >= a.window;
-                const int key0 = TILE * c;
-                if (diag || rows.grow[PB]) load_qop<K>(a, sg, hq, c, qrow, hl, qop);
-                else shift_qop<K>(rows, PB, hl, qop);
-                if (!diag && !wtile) {
-                    // interior tile, software-pipelined over its four sub-blocks: the
-                    // exps of sub-block b share a basic block with the QK MFMAs of b-1
-                    // and the PV MFMAs of b+1, so one wave keeps both units busy
-                    f32x16 S[NSB][NB];
-                    bf16x8 P[NSB][NB][2];
-                    bf16x8 kf[K / 16];
-                    load_kfrag<K>(kb, NSB - 1, kbase, kf);
-                    qk<K>(kf, qop, S[NSB - 1]);
-                    load_kfrag<K>(kb, NSB - 2, kbase, kf);
+        kr.issue_k(k1, max(c_hi - 1, c_lo));
+        // the scores of the first sub-block (3 of tile c_hi), S[1]
+        {
+            const char *kb = k0 + wv.kbase + (NSB - 1) * (SB / KL::NBLK) * (2 * K);
 #pragma unroll
-                    for (int b = NSB - 1; b >= 0; --b) {
-                        float x[NB][16], alpha[NB];
-                        softmax_max<K, V, false, HAS_G>(rows, PB, b, hl, S[b], acc, x, alpha, key0,
-                                                        qrow, sg.len, 0);
-                        if (b > 0) qk<K>(kf, qop, S[b - 1]);
-                        if (b > 1) load_kfrag<K>(kb, b - 2, kbase, kf);
-                        if (b < NSB - 1) pv<K, V>(vb, b + 1, vbase, P[b + 1], acc);
-                        softmax_exp<V>(x, acc, P[b]);
-                        rescale_o<V>(acc, alpha);  // O = (O + P(b+1) V) * alpha
-                    }
-                    pv<K, V>(vb, 0, vbase, P[0], acc);
-                } else {
-                    // diagonal / window-boundary tile: masked, sub-blocks wholly in the
-                    // future of all this wave's queries skipped
-                    const int b_hi = diag ? min(3, (q0w + WQ - 1 - key0) / SB) : 3;
-                    for (int b = b_hi; b >= 0; --b) {
-                        f32x16 S[NB];
-                        bf16x8 P[NB][2];
-                        bf16x8 kf[K / 16];
-                        load_kfrag<K>(kb, b, kbase, kf);
-                        qk<K>(kf, qop, S);
-                        float x[NB][16], alpha[NB];
-                        softmax_max<K, V, true, HAS_G>(rows, PB, b, hl, S, acc, x, alpha, key0, qrow,
-                                                       sg.len, a.window);
-                        rescale_o<V>(acc, alpha);
-                        softmax_exp<V>(x, acc, P);
-                        pv<K, V>(vb, b, vbase, P, acc);
-                    }
-                }
+            for (int s8 = 0; s8 < KS; ++s8) {
+                const bf16x8 x = *reinterpret_cast<const bf16x8 *>(kb + 32 * s8);
+                wv.S[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, wv.qop[s8], s8 ? wv.S[1] : wv.negm, 0, 0, 0);
             }
+        }
 
-            __builtin_amdgcn_s_waitcnt(0);  // tile c-1 has landed in LDS, its rows in registers
-            if (c - 1 >= c_lo) {
-                write_rows(PB ^ 1, false);
-                if (c - 2 >= c_lo) fetch_rows(c - 2);
-            }
-            __syncthreads();
-        };
-        for (int c = c_hi; c >= c_lo; c -= 2) {
-            tile_step(c, std::integral_constant<int, 0>{});
-            if (c - 1 >= c_lo) tile_step(c - 1, std::integral_constant<int, 1>{});
+        kr.wave_on = wave_on;
+        // prefetch the first reads of tile c_hi (parity 0)
+        wv.kcur = k0;
+        wv.knext = k1;
+        wv.vcur = v0;
+        wv.vprev = v1;
+        wv.read_first(std::make_integer_sequence<int, NPF>{});
+
+        int c = c_hi;
+        for (;;) {
+            wv.kcur = k0; wv.knext = k1; wv.vcur = v0; wv.vprev = v1;
+            kr.tile_facts(c, k0);
+            kr.template run_tile<0>(c, std::make_integer_sequence<int, Plan::N>{});
+            if (--c < c_lo) break;
+            wv.kcur = k1; wv.knext = k0; wv.vcur = v1; wv.vprev = v0;
+            kr.tile_facts(c, k1);
+            kr.template run_tile<1>(c, std::make_integer_sequence<int, Plan::N>{});
+            if (--c < c_lo) break;
+        }
+        // the loads issued past tile c_lo land before the buffers are reused
+        // (or the workgroup ends)
+        wait_vm<0>();
+        // the last sub-block's PV products (sub-block 0 of tile c_lo, p in Pw[0])
+        {
+            const char *vb = ((c_hi - c_lo) & 1 ? v1 : v0) + wv.vbase;
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int vt = 0; vt < VT; ++vt) {
+                    const bf16x8 x = *reinterpret_cast<const bf16x8 *>(vb + vt * (32 / VL::NBLK) * (2 * TILE) + 32 * t);
+                    wv.O[vt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, W::as_bf16(wv.Pw[0][t]), wv.O[vt], 0, 0, 0);
+                }
         }
 
         // ---- epilogue: sink, normalisation, o and lse
         if (wave_on) {
+            const float l_tot = pair_sum(wv.l);
+            const float m_true = wv.m + g_i;
+            float m_fin = m_true, l_fin = l_tot;
+            if (a.sink) {
+                const float sb = a.sink[hq] * LOG2E;
+                m_fin = fmaxf(m_true, sb);
+                l_fin = l_tot * exp2f(m_true - m_fin) + exp2f(sb - m_fin);
+            }
+            const float fac = exp2f(m_true - m_fin) / l_fin;
+            if (qrow < sg.len) {
+                const int64_t tok = (int64_t)sg.start + qrow;
+                __bf16 *orow = static_cast<__bf16 *>(a.o) + (tok * HQ + hq) * V;
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                const float l_tot = pair_sum(acc.l[nb]);
-                const float m_true = acc.m[nb] + g_i[nb];
-                float m_fin = m_true, l_fin = l_tot;
-                if (a.sink) {
-                    const float sb = a.sink[hq] * LOG2E;
-                    m_fin = fmaxf(m_true, sb);
-                    l_fin = l_tot * exp2f(m_true - m_fin) + exp2f(sb - m_fin);
-                }
-                const float fac = exp2f(m_true - m_fin) / l_fin;
-                if (qrow[nb] < sg.len) {
-                    const int64_t tok = (int64_t)sg.start + qrow[nb];
-                    __bf16 *orow = og + (tok * HQ + hq) * V;
+                for (int vt = 0; vt < VT; ++vt) {
 #pragma unroll
-                    for (int vt = 0; vt < VT; ++vt) {
+                    for (int r4 = 0; r4 < 4; ++r4) {
+                        f32x4 y;
 #pragma unroll
-                        for (int r4 = 0; r4 < 4; ++r4) {
-                            f32x4 y;
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) y[e] = acc.O[nb][vt][4 * r4 + e] * fac;
-                            *reinterpret_cast<bf16x4 *>(orow + 32 * vt + 8 * r4 + 4 * hl) =
-                                __builtin_convertvector(y, bf16x4);
-                        }
+                        for (int e = 0; e < 4; ++e) y[e] = wv.O[vt][4 * r4 + e] * fac;
+                        *reinterpret_cast<bf16x4 *>(orow + 32 * vt + 8 * r4 + 4 * hl) =
+                            __builtin_convertvector(y, bf16x4);
                     }
-                    if (a.lse && hl == 0) a.lse[tok * HQ + hq] = (m_fin + log2f(l_fin)) * LN2;
                 }
+                if (a.lse && hl == 0) a.lse[tok * HQ + hq] = (m_fin + log2f(l_fin)) * LN2;
             }
         }
     }

@@ -4,7 +4,8 @@
 //    first 128-row tile in the tiled workspace).  Tiles never straddle two
 //    sequences, so a tile's rows always share one prefix P.
 // 2. key cache: per (tile, query head) the anchors R[n] = floor(P[a][n]) at the
-//    tile's middle row a, and the decay-rescaled keys
+//    tile's middle row a, the carry record that moves a query from this
+//    tile's anchors to the previous tile's, and the decay-rescaled keys
 //        k~[j][n] = k[j][n] * exp2(R[n] - P[j][n]),
 //    zero-padded to 128 rows.  This is the blog's per-tile anchor split
 //    ("Fast training and inference", per-tile anchors:
@@ -96,6 +97,24 @@ __global__ __launch_bounds__(256) void key_cache_kernel(PrepArgs a) {
     if (r0 == 0) {
         float *ap = a.anchor + ((int64_t)tile * a.HQ + hq) * K + c8 * 8;
         *reinterpret_cast<f32x8 *>(ap) = R;
+        // carry record: the shift from this tile's anchors to the previous tile's
+        bool up = false;
+        uint32_t *rec = a.rec + ((int64_t)tile * a.HQ + hq) * REC_WORDS;
+        for (int e = 0; e < 8; e += 2) {
+            uint32_t w = 0;
+            if (c > 0) {
+                const int prow = (c - 1) * TILE + ANCHOR_ROW;  // anchor row of tile c-1 (< len)
+                const float *Pp = a.P + ((int64_t)(sg.start + prow) * a.HQ + hq) * K + c8 * 8;
+                const float d0 = floorf(Pp[e]) - R[e], d1 = floorf(Pp[e + 1]) - R[e + 1];
+                up = up || d0 < 0.f || d1 < 0.f;
+                const uint32_t s0 = (uint32_t)fminf(fmaxf(d0, 0.f), 255.f) * 128u;
+                const uint32_t s1 = (uint32_t)fminf(fmaxf(d1, 0.f), 255.f) * 128u;
+                w = s0 | (s1 << 16);
+            }
+            rec[(c8 * 8 + e) / 2] = w;
+        }
+        const bool any_up = __any(up);  // the r0 == 0 threads are lanes 0..K/8-1 of wave 0
+        if (threadIdx.x == 0) rec[REC_GROW] = any_up ? 1u : 0u;
     }
     const T *kin = static_cast<const T *>(a.k);
     T *kout = static_cast<T *>(a.kt) + ((int64_t)tile * a.HQ + hq) * TILE * K;
