@@ -80,15 +80,21 @@ constexpr float RESCALE = 10.0f;  // log2 headroom before the running max is rai
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+
 // Key row (within a 32-row block) that MFMA A-row m reads: bits 2 and 3 swapped.
 __device__ __forceinline__ int key_perm(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
 
 // Combine a value with the one held by lane ^ 32 (the other half of the wave
 // holds the same query's other keys): after v_permlane32_swap each lane holds
 // both halves' values, one in each result.
+// Scores are never NaN, so the NaN-propagating maximum serves; unlike fmaxf
+// it needs no quieting of its inputs.
+__device__ __forceinline__ float max3(float a, float b, float c) {
+    return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
+}
 __device__ __forceinline__ float pair_max(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    return __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float pair_sum(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -246,49 +252,108 @@ template <int K, int V>
 struct TilePlan {
     static constexpr int VT = V / 32, KS = K / 16;
     static constexpr int NPV = 2 * VT, NQK = KS, NSMD = 8, NC1 = KS / 2;
-    static constexpr int MAXOPS = NSB * (NPV + NQK + KS + 13) + 4;
+    static constexpr int MAXOPS = NSB * (NPV + NQK + KS + 16) + 4;
     using OpArr = std::array<TOp, MAXOPS>;
+    // vector instructions per op (the common path), used to spread them evenly
+    // over the step's matrix products
+    static constexpr int cost(int kind) {
+        return kind == O_SMA ? 5 : kind == O_SMB ? 5 : kind == O_SMC ? 5 : kind == O_SMD ? 4 : kind == O_SME ? 5
+             : kind == O_CARRY ? 12 : 0;
+    }
 
-    static constexpr int build(OpArr &a) {
-        int n = 0;
-        for (int b = NSB - 1; b >= 0; --b) {
-            int pv = 0, qk = 0, smd = 0;
-            if (b == 2) {
-                a[n++] = TOp{O_BARV, b, 0};
-                a[n++] = TOp{O_SMA, b, 0};
-                a[n++] = TOp{O_SMB, b, 0};
-                a[n++] = TOp{O_SMC, b, 0};
-            } else {
-                a[n++] = TOp{O_PV, b, pv++};
-                a[n++] = TOp{O_SMA, b, 0};
-                a[n++] = TOp{O_PV, b, pv++};
-                a[n++] = TOp{O_SMB, b, 0};
-                a[n++] = TOp{O_PV, b, pv++};
-                a[n++] = TOp{O_SMC, b, 0};
-                if (b == 0) {
-                    for (int s8 = NC1; s8 < KS; ++s8) {
-                        a[n++] = TOp{O_CARRY, b, s8};
-                        if (pv < NPV - 1) a[n++] = TOp{O_PV, b, pv++};
-                    }
-                    a[n++] = TOp{O_BARK, b, 0};
-                }
-            }
+    // One step b: its matrix products in order (three value products first,
+    // in step 0 all but two, then BARK; then score and value products
+    // alternating), and after each product as many
+    // vector ops as keep their running total in proportion.  The softmax ops
+    // form a chain (SMA, SMB, SMC, SMD0..7, SME; at most one of the first
+    // three per slot, and SMD0 not in SMC's slot); score products wait for
+    // SMC.  Carries are one queue over steps 1 and 0: a carry waits for the
+    // last score product (in step 1) of its channel step, and all precede
+    // BARK; each of the two steps budgets half of them.
+    static constexpr int build_step(OpArr &a, int n, int b, int &car) {
+        TOp mf[NPV + NQK + 1]{};
+        int nm = 0, nmfma = 0;
+        if (b == 0) {
+            int pv = 0, qk = 0;
+            for (; pv < NPV - 2; ++pv) mf[nm++] = TOp{O_PV, b, pv};
+            mf[nm++] = TOp{O_BARK, b, 0};
             while (pv < NPV || qk < NQK) {
-                if (qk < NQK) {
-                    a[n++] = TOp{O_QK, b, qk};
-                    if (b == 1 && qk < NC1) a[n++] = TOp{O_CARRY, b, qk};
-                    ++qk;
-                    if (smd < NSMD) a[n++] = TOp{O_SMD, b, smd++};
+                if (qk < NQK) mf[nm++] = TOp{O_QK, b, qk++};
+                if (pv < NPV) mf[nm++] = TOp{O_PV, b, pv++};
+            }
+        } else {
+            int pv = 0, qk = 0;
+            for (; pv < 3; ++pv) mf[nm++] = TOp{O_PV, b, pv};
+            while (pv < NPV || qk < NQK) {
+                if (qk < NQK) mf[nm++] = TOp{O_QK, b, qk++};
+                if (pv < NPV) mf[nm++] = TOp{O_PV, b, pv++};
+            }
+        }
+        nmfma = NPV + NQK;
+        TOp chain[3 + NSMD + 1]{};
+        int nc = 0;
+        chain[nc++] = TOp{O_SMA, b, 0};
+        chain[nc++] = TOp{O_SMB, b, 0};
+        chain[nc++] = TOp{O_SMC, b, 0};
+        for (int k = 0; k < NSMD; ++k) chain[nc++] = TOp{O_SMD, b, k};
+        chain[nc++] = TOp{O_SME, b, 0};
+        const int c_hi = b <= 1 ? KS : 0;  // carries allowed in this step
+        int ch_total = 0;
+        for (int i = 0; i < nc; ++i) ch_total += cost(chain[i].kind);
+        // the carries' budget and the products they are spread over
+        const int car_total = b == 1 ? NC1 * cost(O_CARRY) : b == 0 ? (KS - car) * cost(O_CARRY) : 0;
+        const int car_slots = b == 0 ? NPV - 2 : nmfma;
+        int ci = 0, ch_placed = 0, car_placed = 0, done = 0, smc_slot = -1, slot = 0;
+        bool qk_done[KS]{};
+        if (b == 2) a[n++] = TOp{O_BARV, b, 0};
+        for (int e = 0; e < nm; ++e) {
+            const TOp m = mf[e];
+            if (m.kind == O_BARK) {
+                while (car < c_hi) a[n++] = TOp{O_CARRY, b, car++};
+                a[n++] = m;
+                continue;
+            }
+            if (m.kind == O_QK) {
+                while (ci < 3) { a[n++] = chain[ci++]; ch_placed += cost(O_SMA); smc_slot = slot; }
+            }
+            a[n++] = m;
+            ++done;
+            ++slot;
+            if (m.kind == O_QK) qk_done[m.idx] = true;
+            const int ch_t = ch_total * done / nmfma;
+            const int car_t = car_total * (done < car_slots ? done : car_slots) / car_slots;
+            bool stage = false;
+            for (;;) {
+                if (ci < 3) {  // SMA, SMB, SMC: one per product, as early as possible
+                    if (stage) break;
+                    a[n++] = chain[ci++];
+                    ch_placed += cost(O_SMA);
+                    stage = true;
+                    if (ci == 3) smc_slot = slot;
+                    continue;
                 }
-                if (pv < NPV) {
-                    a[n++] = TOp{O_PV, b, pv++};
-                    if (smd < NSMD) a[n++] = TOp{O_SMD, b, smd++};
+                const bool car_ok = car < c_hi && (b == 0 || qk_done[car]);
+                const bool ch_ok = ci < nc && !(ci == 3 && smc_slot == slot);
+                if (car_ok && car_placed + cost(O_CARRY) / 2 <= car_t) {
+                    a[n++] = TOp{O_CARRY, b, car++};
+                    car_placed += cost(O_CARRY);
+                } else if (ch_ok && ch_placed + cost(chain[ci].kind) / 2 <= ch_t) {
+                    ch_placed += cost(chain[ci].kind);
+                    a[n++] = chain[ci++];
+                } else {
+                    break;
                 }
             }
-            while (smd < NSMD) a[n++] = TOp{O_SMD, b, smd++};
-            a[n++] = TOp{O_SME, b, 0};
-            a[n++] = TOp{O_RESC, b, 0};
         }
+        if (b == 0)
+            while (car < c_hi) a[n++] = TOp{O_CARRY, b, car++};
+        while (ci < nc) a[n++] = chain[ci++];
+        a[n++] = TOp{O_RESC, b, 0};
+        return n;
+    }
+    static constexpr int build(OpArr &a) {
+        int n = 0, car = 0;
+        for (int b = NSB - 1; b >= 0; --b) n = build_step(a, n, b, car);
         return n;
     }
     static constexpr OpArr make_ops() {
@@ -383,18 +448,19 @@ struct Wave {
     // accumulators and softmax state for the lane's query column: m is the
     // running max (log2 units) the scores are taken relative to; negm holds -m
     // in all 16 accumulator slots and starts every QK product.  Until a lane
-    // has seen a visible key m is 0 and not yet valid.
+    // has seen a visible key m is 0 and any score raises it (thr).
     f32x16 O[VT];
     f32x16 negm;
     float m, l;
     float alpha;  // rescale O still owes for the current step (1 if none)
-    bool valid, owe;
+    float thr;    // a step max above m + thr raises m: -FLT_MAX at first, then RESCALE
     QOp<K> qop;
     f32x16 S[2];           // S[b & 1]: scores of the sub-block softmaxed in step b
     uint32_t Pw[2][2][4];  // Pw[b & 1][t]: packed bf16 p of that sub-block, keys 16t + 8hl + e
     bf16x8 ring[NPF];      // LDS operand reads in flight
     float red[5];          // partial maxima of the current step
     float mt;              // the step's max, relative to m
+    float ex[2][2];        // exps of the last two key pairs, packed one op later
     float part[2];         // partial row sums of the current step
 
     // buffers: keys of this tile and the next (older) one, values of this tile
@@ -447,17 +513,23 @@ struct Wave {
     __device__ __forceinline__ void sma() {
         f32x16 &s = S[B & 1];
         if (mask_tile || (window > 0 && q0w + WQ - 1 - (key_tile0 + SB * B) >= window)) {
-            // visible keys of this lane's query, as offsets from its first key in the sub-block:
-            // min with +inf inside [klo, khi], with -inf outside, where the sign of
-            // (off - klo) | (khi - off) marks outside (no compares)
+            // visible keys of this lane's query, as offsets from its first key in
+            // the sub-block: at most khi (causal, sequence end), at least klo (window)
             const int kb0 = key_tile0 + SB * B + 8 * hl;
             const int khi = min(qrow, len - 1) - kb0;
-            const int klo = window > 0 ? qrow - window + 1 - kb0 : -(1 << 30);
+            if (window > 0) {
+                const int klo = qrow - window + 1 - kb0;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int off = 16 * (r / 8) + (r % 8);
-                const int out = (off - klo) | (khi - off);
-                s[r] = fminf(s[r], __int_as_float(0x7f800000 | (out & INT_MIN)));
+                for (int r = 0; r < 16; ++r) {
+                    const int off = 16 * (r / 8) + (r % 8);
+                    s[r] = (off <= khi && off >= klo) ? s[r] : -__builtin_inff();
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int off = 16 * (r / 8) + (r % 8);
+                    s[r] = off <= khi ? s[r] : -__builtin_inff();
+                }
             }
         }
         if (HAS_G) {
@@ -470,53 +542,69 @@ struct Wave {
                 s[8 + e] -= g1[e];
             }
         }
-        red[0] = fmaxf(fmaxf(s[0], s[1]), s[2]);
-        red[1] = fmaxf(fmaxf(s[3], s[4]), s[5]);
-        red[2] = fmaxf(fmaxf(s[6], s[7]), s[8]);
-        red[3] = fmaxf(fmaxf(s[9], s[10]), s[11]);
-        red[4] = fmaxf(fmaxf(s[12], s[13]), s[14]);
+        red[0] = max3(s[0], s[1], s[2]);
+        red[1] = max3(s[3], s[4], s[5]);
+        red[2] = max3(s[6], s[7], s[8]);
+        red[3] = max3(s[9], s[10], s[11]);
+        red[4] = max3(s[12], s[13], s[14]);
     }
     template <int B>
     __device__ __forceinline__ void smb() {
         const f32x16 &s = S[B & 1];
-        const float a = fmaxf(fmaxf(red[0], red[1]), red[2]);
-        const float b = fmaxf(fmaxf(red[3], red[4]), s[15]);
-        mt = pair_max(fmaxf(a, b));
+        const float a = max3(red[0], red[1], red[2]);
+        const float b = max3(red[3], red[4], s[15]);
+        mt = pair_max(__builtin_elementwise_maximum(a, b));
     }
     template <int B>
     __device__ __forceinline__ void smc() {
-        const bool raise = valid ? mt > RESCALE : mt > -FLT_MAX;
+        const bool raise = mt > thr;
         if (__any(raise)) {
             const float delta = raise ? mt : 0.f;
             const float al = fast_exp2(-delta);
             m += delta;
             l *= al;
             alpha *= al;
-            owe = owe || raise;
-            valid = valid || raise;
+            thr = raise ? RESCALE : thr;
             negm -= delta;
             S[B & 1] -= delta;
         }
     }
+    // SMD KK: the exps of key pair KK.  The pair before it is rounded and
+    // packed, and the one before that summed, in the same op, so that no op
+    // waits for a result of its own.
     template <int B, int KK>
     __device__ __forceinline__ void smd() {
         const f32x16 &s = S[B & 1];
-        const float e0 = fast_exp2(s[2 * KK]), e1 = fast_exp2(s[2 * KK + 1]);
-        const bf16x2 p = {(__bf16)e0, (__bf16)e1};
-        const uint32_t w = __builtin_bit_cast(uint32_t, p);
-        Pw[B & 1][KK / 4][KK % 4] = w;
+        if constexpr (KK > 0) pack<B, KK - 1>();
+        if constexpr (KK > 1) rowsum<B, KK - 2>();
+        ex[KK & 1][0] = fast_exp2(s[2 * KK]);
+        ex[KK & 1][1] = fast_exp2(s[2 * KK + 1]);
+    }
+    template <int B, int KK>
+    __device__ __forceinline__ void pack() {
+        const bf16x2 p = {(__bf16)ex[KK & 1][0], (__bf16)ex[KK & 1][1]};
+        Pw[B & 1][KK / 4][KK % 4] = __builtin_bit_cast(uint32_t, p);
+    }
+    // row sum of the rounded p, two independent chains
+    template <int B, int KK>
+    __device__ __forceinline__ void rowsum() {
+        const bf16x2 p = __builtin_bit_cast(bf16x2, Pw[B & 1][KK / 4][KK % 4]);
         const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-        // row sum of the rounded p, two independent chains
         part[KK & 1] = __builtin_amdgcn_fdot2_f32_bf16(p, one, KK < 2 ? 0.f : part[KK & 1], false);
     }
-    __device__ __forceinline__ void sme() { l += part[0] + part[1]; }
+    template <int B>
+    __device__ __forceinline__ void sme() {
+        pack<B, 7>();
+        rowsum<B, 6>();
+        rowsum<B, 7>();
+        l += part[0] + part[1];
+    }
     __device__ __forceinline__ void resc() {
-        if (__any(owe)) {
+        if (__any(alpha != 1.f)) {
 #pragma unroll
             for (int vt = 0; vt < VT; ++vt) O[vt] *= alpha;
+            alpha = 1.f;
         }
-        alpha = 1.f;
-        owe = false;
     }
 };
 
@@ -568,11 +656,15 @@ struct Kernel {
     __device__ __forceinline__ void issue_v(char *vd, int c) const { load_tile<VL>(vd, vt_tile(c), vlane, w); }
 
     // ---- one op of the plan at position P for tile c held in buffers of parity PB
-    template <int PB, int P>
+    // DEAD: a tile wholly after the wave's queries.  Its p are all 0, so only
+    // the barriers and the score products of the next tile (step 0) remain.
+    template <int PB, int P, bool DEAD>
     __device__ __forceinline__ void op(int c) {
         constexpr TOp o = Plan::OPS[P];
         constexpr int B = o.step;
-        if constexpr (o.kind == O_PV) {
+        if constexpr (DEAD && o.kind != O_BARV && o.kind != O_BARK && !(o.kind == O_QK && o.step == 0)) {
+            return;
+        } else if constexpr (o.kind == O_PV) {
             constexpr int vt = o.idx % VT, t = o.idx / VT;
             const bf16x8 x = wv.ring[Plan::READ_OF[P] % NPF];
             wv.O[vt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, W::as_bf16(wv.Pw[(B + 1) & 1][t]), wv.O[vt], 0,
@@ -607,7 +699,7 @@ struct Kernel {
         } else if constexpr (o.kind == O_SMD) {
             wv.template smd<B, o.idx>();
         } else if constexpr (o.kind == O_SME) {
-            wv.sme();
+            wv.template sme<B>();
         } else if constexpr (o.kind == O_RESC) {
             wv.resc();
         } else if constexpr (o.kind == O_BARV) {
@@ -639,15 +731,15 @@ struct Kernel {
     __device__ __forceinline__ void reads_after(std::integer_sequence<int, Rs...>) {
         (maybe_read<P, Rs + NPF>(), ...);
     }
-    template <int PB, int P>
+    template <int PB, int P, bool DEAD>
     __device__ __forceinline__ void step(int c) {
         __builtin_amdgcn_sched_barrier(0);
-        op<PB, P>(c);
+        op<PB, P, DEAD>(c);
         reads_after<P>(std::make_integer_sequence<int, NR>{});
     }
-    template <int PB, int... Ps>
+    template <int PB, bool DEAD, int... Ps>
     __device__ __forceinline__ void run_tile(int c, std::integer_sequence<int, Ps...>) {
-        (step<PB, Ps>(c), ...);
+        (step<PB, Ps, DEAD>(c), ...);
         __builtin_amdgcn_sched_barrier(0);
     }
 };
@@ -729,8 +821,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
         wv.m = 0.f;
         wv.l = 0.f;
         wv.alpha = 1.f;
-        wv.valid = false;
-        wv.owe = false;
+        wv.thr = -FLT_MAX;
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -767,11 +858,11 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
         for (;;) {
             wv.kcur = k0; wv.knext = k1; wv.vcur = v0; wv.vprev = v1;
             kr.tile_facts(c, k0);
-            kr.template run_tile<0>(c, std::make_integer_sequence<int, Plan::N>{});
+            kr.template run_tile<0, false>(c, std::make_integer_sequence<int, Plan::N>{});
             if (--c < c_lo) break;
             wv.kcur = k1; wv.knext = k0; wv.vcur = v1; wv.vprev = v0;
             kr.tile_facts(c, k1);
-            kr.template run_tile<1>(c, std::make_integer_sequence<int, Plan::N>{});
+            kr.template run_tile<1, false>(c, std::make_integer_sequence<int, Plan::N>{});
             if (--c < c_lo) break;
         }
         // the loads issued past tile c_lo land before the buffers are reused
