@@ -87,6 +87,14 @@ __device__ __forceinline__ int key_perm(int m) { return (m & ~12) | ((m & 4) << 
 // Combine a value with the one held by lane ^ 32 (the other half of the wave
 // holds the same query's other keys): after v_permlane32_swap each lane holds
 // both halves' values, one in each result.
+// Keep the computation of x where it is written: the result is marked as
+// used there, so the compiler cannot sink it past the branches of later ops
+// (which would undo the interleaving the tile plan lays out).
+template <class T>
+__device__ __forceinline__ void pin(T &x) {
+    asm volatile("" : "+v"(x));
+}
+
 // Scores are never NaN, so the NaN-propagating maximum serves; unlike fmaxf
 // it needs no quieting of its inputs.
 __device__ __forceinline__ float max3(float a, float b, float c) {
@@ -547,6 +555,8 @@ struct Wave {
         red[2] = max3(s[6], s[7], s[8]);
         red[3] = max3(s[9], s[10], s[11]);
         red[4] = max3(s[12], s[13], s[14]);
+#pragma unroll
+        for (int i = 0; i < 5; ++i) pin(red[i]);
     }
     template <int B>
     __device__ __forceinline__ void smb() {
@@ -554,6 +564,7 @@ struct Wave {
         const float a = max3(red[0], red[1], red[2]);
         const float b = max3(red[3], red[4], s[15]);
         mt = pair_max(__builtin_elementwise_maximum(a, b));
+        pin(mt);
     }
     template <int B>
     __device__ __forceinline__ void smc() {
@@ -579,11 +590,14 @@ struct Wave {
         if constexpr (KK > 1) rowsum<B, KK - 2>();
         ex[KK & 1][0] = fast_exp2(s[2 * KK]);
         ex[KK & 1][1] = fast_exp2(s[2 * KK + 1]);
+        pin(ex[KK & 1][0]);
+        pin(ex[KK & 1][1]);
     }
     template <int B, int KK>
     __device__ __forceinline__ void pack() {
         const bf16x2 p = {(__bf16)ex[KK & 1][0], (__bf16)ex[KK & 1][1]};
         Pw[B & 1][KK / 4][KK % 4] = __builtin_bit_cast(uint32_t, p);
+        pin(Pw[B & 1][KK / 4][KK % 4]);
     }
     // row sum of the rounded p, two independent chains
     template <int B, int KK>
@@ -591,6 +605,7 @@ struct Wave {
         const bf16x2 p = __builtin_bit_cast(bf16x2, Pw[B & 1][KK / 4][KK % 4]);
         const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
         part[KK & 1] = __builtin_amdgcn_fdot2_f32_bf16(p, one, KK < 2 ? 0.f : part[KK & 1], false);
+        pin(part[KK & 1]);
     }
     template <int B>
     __device__ __forceinline__ void sme() {
@@ -598,6 +613,7 @@ struct Wave {
         rowsum<B, 6>();
         rowsum<B, 7>();
         l += part[0] + part[1];
+        pin(l);
     }
     __device__ __forceinline__ void resc() {
         if (__any(alpha != 1.f)) {
@@ -689,6 +705,7 @@ struct Kernel {
                     out[e] = (xv[e] & 0x80008000u) | __builtin_bit_cast(uint32_t, r);
                 }
                 wv.qop[o.idx] = __builtin_bit_cast(bf16x8, uint4{out[0], out[1], out[2], out[3]});
+                pin(wv.qop[o.idx]);
             }
         } else if constexpr (o.kind == O_SMA) {
             wv.template sma<B>();
