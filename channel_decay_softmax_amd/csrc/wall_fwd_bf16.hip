@@ -477,8 +477,8 @@ struct Wave {
 
     // per-tile facts (wave-uniform)
     int key_tile0;   // first key of the current tile (sequence-relative)
-    bool mask_tile;      // the tile needs causal / sequence-end masks for this wave
-    bool carry_on;       // carry q~ on to the next tile by the record's shifts
+    int mask_bits;   // bit B: step B's scores need causal / window / sequence-end masks
+    const char *recp;  // the tile's carry record, or zeros (no carry) for this wave
     bool carry_on_grow;  // ... by rebuilding it there (some channel's prefix grows)
     int window, len, q0w;
 
@@ -504,7 +504,7 @@ struct Wave {
             return reinterpret_cast<const bf16x8 *>(kb + kbase + off);
         } else {
             // carry record words 8*s8 + 4*hl .. +3 of the current tile
-            return reinterpret_cast<const bf16x8 *>(kcur + LY::REC_OFF + 32 * o.idx + 16 * hl);
+            return reinterpret_cast<const bf16x8 *>(recp + 32 * o.idx + 16 * hl);
         }
     }
     template <int R>
@@ -520,7 +520,7 @@ struct Wave {
     template <int B>
     __device__ __forceinline__ void sma() {
         f32x16 &s = S[B & 1];
-        if (mask_tile || (window > 0 && q0w + WQ - 1 - (key_tile0 + SB * B) >= window)) {
+        if (mask_bits & (1 << B)) {
             // visible keys of this lane's query, as offsets from its first key in
             // the sub-block: at most khi (causal, sequence end), at least klo (window)
             const int kb0 = key_tile0 + SB * B + 8 * hl;
@@ -644,14 +644,24 @@ struct Kernel {
     int hq, h, w, lane, qt_w, c_lo;
     uint32_t klane, vlane;
     bool wave_on;
+    const char *zrec = nullptr;  // zeros in LDS: the shifts of no carry
 
     // per-tile facts of tile c whose keys (and carry record) are in kcur
     __device__ __forceinline__ void tile_facts(int c, const char *kcur) {
         wv.key_tile0 = TILE * c;
-        wv.mask_tile = c >= qt_w;
+        // the diagonal tile (and the sequence end) masks every step; a window
+        // masks the steps whose first key is at or below lim
+        int mb = c >= qt_w ? (1 << NSB) - 1 : 0;
+        if (wv.window > 0) {
+            const int lim = wv.q0w + WQ - 1 - wv.window - TILE * c;
+            if (lim >= 0) mb |= (2 << min(lim / SB, NSB - 1)) - 1;
+        }
+        wv.mask_bits = mb;
         const bool grow = reinterpret_cast<const uint32_t *>(kcur + LY::REC_OFF)[REC_GROW] != 0u;
         const bool go_on = wave_on && c <= qt_w && c - 1 >= c_lo;
-        wv.carry_on = go_on && !grow;
+        // Without a carry the shifts are read from zeros.  A tile where some
+        // channel's prefix grows rebuilds q~ at BARK, after all carries.
+        wv.recp = go_on ? kcur + LY::REC_OFF : zrec;
         wv.carry_on_grow = go_on && grow;
     }
 
@@ -691,22 +701,22 @@ struct Kernel {
             sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, wv.qop[o.idx], o.idx == 0 ? wv.negm : sn, 0, 0, 0);
         } else if constexpr (o.kind == O_CARRY) {
             const bf16x8 x = wv.ring[Plan::READ_OF[P] % NPF];
-            if (wv.carry_on) {
-                // lower each bf16 exponent field by the shift, saturating on the magnitude
-                const uint4 d = __builtin_bit_cast(uint4, x);
-                const uint32_t dv[4] = {d.x, d.y, d.z, d.w};
-                const uint4 x4 = __builtin_bit_cast(uint4, wv.qop[o.idx]);
-                const uint32_t xv[4] = {x4.x, x4.y, x4.z, x4.w};
-                uint32_t out[4];
+            // lower each bf16 exponent field by the shift, saturating on the
+            // magnitude (the four words interleaved: no op waits on the one before)
+            const uint4 d = __builtin_bit_cast(uint4, x);
+            const uint32_t dv[4] = {d.x, d.y, d.z, d.w};
+            const uint4 x4 = __builtin_bit_cast(uint4, wv.qop[o.idx]);
+            const uint32_t xv[4] = {x4.x, x4.y, x4.z, x4.w};
+            u16x2 mag[4], r[4];
+            uint32_t out[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const u16x2 mag = __builtin_bit_cast(u16x2, xv[e] & 0x7fff7fffu);
-                    const u16x2 r = __builtin_elementwise_sub_sat(mag, __builtin_bit_cast(u16x2, dv[e]));
-                    out[e] = (xv[e] & 0x80008000u) | __builtin_bit_cast(uint32_t, r);
-                }
-                wv.qop[o.idx] = __builtin_bit_cast(bf16x8, uint4{out[0], out[1], out[2], out[3]});
-                pin(wv.qop[o.idx]);
-            }
+            for (int e = 0; e < 4; ++e) mag[e] = __builtin_bit_cast(u16x2, xv[e] & 0x7fff7fffu);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) r[e] = __builtin_elementwise_sub_sat(mag[e], __builtin_bit_cast(u16x2, dv[e]));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) out[e] = (xv[e] & 0x80008000u) | __builtin_bit_cast(uint32_t, r[e]);
+            wv.qop[o.idx] = __builtin_bit_cast(bf16x8, uint4{out[0], out[1], out[2], out[3]});
+            pin(wv.qop[o.idx]);
         } else if constexpr (o.kind == O_SMA) {
             wv.template sma<B>();
         } else if constexpr (o.kind == O_SMB) {
@@ -777,6 +787,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
     __shared__ __attribute__((aligned(16))) char k1[LY::KBUF];
     __shared__ __attribute__((aligned(16))) char v0[VL::BYTES];
     __shared__ __attribute__((aligned(16))) char v1[VL::BYTES];
+    __shared__ __attribute__((aligned(16))) char zrec[32 * KS];
 
     const int nblocks_max = (a.max_tiles + 1) / 2;  // 256-row blocks of the longest sequence
     const int npairs = (nblocks_max + 1) / 2;
@@ -801,10 +812,12 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
     // Values are multiplied by p = 0 before their first use in a block: give the
     // second value buffer finite contents once.
     for (int i = tid; i < VL::BYTES / 16; i += NW * 64) reinterpret_cast<uint4 *>(v1)[i] = uint4{0, 0, 0, 0};
+    if (tid < 2 * KS) reinterpret_cast<uint4 *>(zrec)[tid] = uint4{0, 0, 0, 0};
 
     KR kr{a, {}, k0, k1, v0, v1, sg, hq, hq / (a.HQ / a.H), w, lane, 0, 0,
           tile_lane_offset<KL>(lane), tile_lane_offset<VL>(lane), false};
     W &wv = kr.wv;
+    kr.zrec = zrec;
     wv.kbase = KL::byte(key_perm(col)) + 16 * hl;
     wv.vbase = VL::byte(col) + 16 * hl;
     wv.hl = hl;
