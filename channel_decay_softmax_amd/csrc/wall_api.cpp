@@ -99,10 +99,9 @@ wall_status_t enqueue_prepare(const void *k, const void *v, wall_dtype_t dtype, 
     const FwdLayout L = fwd_layout(esize_of(dtype), s.B, s.T, s.HQ, s.H, s.K, s.V, s.nseq);
     char *ws = static_cast<char *>(workspace);
     SegInfo *seg = reinterpret_cast<SegInfo *>(ws + L.off_seg);
-    if (launch_seg_table(seg, cu, L.nseg, s.B, s.T, stream) != hipSuccess) return WALL_ERR_LAUNCH;
-    PrepArgs pa{k, v, P, seg, reinterpret_cast<float *>(ws + L.off_anchor),
+    PrepArgs pa{k, v, P, seg, cu, reinterpret_cast<float *>(ws + L.off_anchor),
                 reinterpret_cast<uint32_t *>(ws + L.off_rec), ws + L.off_kt, ws + L.off_vt,
-                L.nseg, L.tiles, s.HQ, s.H, s.K, s.V};
+                L.nseg, L.tiles, s.HQ, s.H, s.K, s.V, s.T};
     return launched(launch_prep(pa, dtype == WALL_BF16, stream));
 }
 

@@ -116,8 +116,7 @@ inline ScanLayout scan_layout(int64_t B, int64_t T, int64_t C) {
 
 // ----------------------------------------------------------------- launchers (internal)
 // Each returns hipSuccess or the launch error; arguments were validated by the C API.
-hipError_t launch_seg_table(SegInfo *seg, const int32_t *cu, int64_t nseg, int64_t B, int64_t T,
-                            hipStream_t st);
+
 
 hipError_t launch_scan(const void *x, bool x_bf16, float *out, int64_t B, int64_t T, int64_t C,
                        const int32_t *cu, int64_t nseq, float scale, void *ws, hipStream_t st);
@@ -126,12 +125,13 @@ struct PrepArgs {
     const void *k;     // [rows, H, K]
     const void *v;     // [rows, H, V]
     const float *P;    // [rows, HQ, K]
-    const SegInfo *seg;
+    SegInfo *seg;      // [nseg], written here
+    const int32_t *cu; // [nseg + 1] sequence starts, or null for B sequences of T rows
     float *anchor;     // [tiles, HQ, K]
     uint32_t *rec;     // [tiles, HQ, REC_WORDS]
     void *kt;          // [tiles, HQ, TILE, K]
     void *vt;          // [tiles, H, V, TILE]
-    int64_t nseg, tiles, HQ, H, K, V;
+    int64_t nseg, tiles, HQ, H, K, V, T;
 };
 hipError_t launch_prep(const PrepArgs &a, bool bf16, hipStream_t st);
 

@@ -1,9 +1,12 @@
-// wall_prep.hip -- per-call preparation for the fused forward.
+// wall_prep.hip -- per-call preparation for the fused forward, one launch.
 //
-// 1. seg_table: one SegInfo per sequence (start row, length, index of its
-//    first 128-row tile in the tiled workspace).  Tiles never straddle two
-//    sequences, so a tile's rows always share one prefix P.
-// 2. key cache: per (tile, query head) the anchors R[n] = floor(P[a][n]) at the
+// Each block takes one 128-row tile of one sequence and either one query
+// head (keys) or one kv head (values):
+// 1. segments: the block finds the sequence its tile belongs to (one SegInfo
+//    per sequence: start row, length, index of its first 128-row tile in the
+//    tiled workspace; tiles never straddle two sequences, so a tile's rows
+//    always share one prefix P); block (0, 0) also stores the table.
+// 2. keys, per (tile, query head): the anchors R[n] = floor(P[a][n]) at the
 //    tile's middle row a, the carry record that moves a query from this
 //    tile's anchors to the previous tile's, and the decay-rescaled keys
 //        k~[j][n] = k[j][n] * exp2(R[n] - P[j][n]),
@@ -13,53 +16,60 @@
 //    side once per (tile, head) instead of once per (query tile, key tile);
 //    it is the same fold the README's decode cache performs with
 //    k_tilde[j] = k[j] * exp2(R_c - P[j]).
-// 3. value tiles: v copied per (tile, kv head), transposed to [V][128] for
-//    the bf16 MFMA kernel (its PV operand reads keys contiguously) and kept
-//    as [128][V] for the float32 kernel; zero-padded.
+// 3. values, per (tile, kv head): v transposed to [V][128] for the bf16 MFMA
+//    kernel (its PV operand reads keys contiguously, each thread transposing
+//    an 8 x 8 block in registers) and kept as [128][V] for the float32
+//    kernel; zero-padded.
 #include "wall_common.h"
 
 namespace wall {
 namespace {
 
-__global__ __launch_bounds__(256) void seg_table_kernel(SegInfo *seg, const int32_t *cu, int nseg,
-                                                        int T) {
-    __shared__ int part[256];
-    const int tid = threadIdx.x;
-    const int per = (nseg + 255) / 256;
-    const int s0 = tid * per, s1 = min(nseg, s0 + per);
-    int local = 0;
-    for (int s = s0; s < s1; ++s) {
-        const int len = cu ? cu[s + 1] - cu[s] : T;
-        local += (len + TILE - 1) / TILE;
+// The sequence that holds tile `tile` (false past the last tile); block
+// (0, 0) also stores the whole table.  Wave 0 scans the per-sequence tile
+// counts 64 sequences at a time.
+__device__ inline bool block_segment(const PrepArgs &a, int tile, bool write_table, SegInfo &out) {
+    const int nseg = (int)a.nseg;
+    if (!a.cu) {  // B sequences of T rows
+        const int T = (int)a.T, tps = (T + TILE - 1) / TILE;
+        if (write_table)
+            for (int i = threadIdx.x; i < nseg; i += blockDim.x) a.seg[i] = SegInfo{i * T, T, i * tps, 0};
+        const int s = tile / tps;
+        out = SegInfo{s * T, T, s * tps, 0};
+        return s < nseg;
     }
-    part[tid] = local;
-    __syncthreads();
-    if (tid == 0) {  // exclusive scan of 256 partial tile counts
+    __shared__ int found[4];
+    if (threadIdx.x < 64) {
+        const int lane = threadIdx.x;
+        if (lane == 0) found[3] = 0;
         int run = 0;
-        for (int i = 0; i < 256; ++i) {
-            const int x = part[i];
-            part[i] = run;
-            run += x;
+        for (int g0 = 0; g0 < nseg; g0 += 64) {
+            const int s = g0 + lane;
+            const int start = s < nseg ? a.cu[s] : 0;
+            const int len = s < nseg ? a.cu[s + 1] - start : 0;
+            const int cnt = (len + TILE - 1) / TILE;
+            int incl = cnt;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const int v = __shfl_up(incl, off);
+                if (lane >= off) incl += v;
+            }
+            const int base = run + incl - cnt;
+            if (s < nseg) {
+                if (write_table) a.seg[s] = SegInfo{start, len, base, 0};
+                if (tile >= base && tile < base + cnt) {
+                    found[0] = start;
+                    found[1] = len;
+                    found[2] = base;
+                    found[3] = 1;
+                }
+            }
+            run += __shfl(incl, 63);
         }
     }
     __syncthreads();
-    int base = part[tid];
-    for (int s = s0; s < s1; ++s) {
-        const int start = cu ? cu[s] : s * T;
-        const int len = cu ? cu[s + 1] - cu[s] : T;
-        seg[s] = SegInfo{start, len, base, 0};
-        base += (len + TILE - 1) / TILE;
-    }
-}
-
-// The sequence whose tiles hold tile id `tile` (last s with tile_base <= tile).
-__device__ inline int find_seg(const SegInfo *seg, int nseg, int tile) {
-    int lo = 0, hi = nseg - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (seg[mid].tile_base <= tile) lo = mid; else hi = mid - 1;
-    }
-    return lo;
+    out = SegInfo{found[0], found[1], found[2], 0};
+    return found[3] != 0;
 }
 
 template <typename T>
@@ -80,14 +90,11 @@ struct Vec8<float> {
 };
 
 template <typename T, int K>
-__global__ __launch_bounds__(256) void key_cache_kernel(PrepArgs a) {
+__device__ inline void key_tile(const PrepArgs &a, int tile, int hq, const SegInfo &sg) {
     constexpr int CPR = K / 8;          // 8-channel chunks per row
     constexpr int RPP = 256 / CPR;      // rows per pass
-    const int tile = blockIdx.x, hq = blockIdx.y;
-    const int s = find_seg(a.seg, (int)a.nseg, tile);
-    const SegInfo sg = a.seg[s];
+    constexpr int NPASS = TILE / RPP;
     const int c = tile - sg.tile_base;
-    if (c < 0 || c * TILE >= sg.len) return;  // beyond the last used tile
     const int h = hq / (int)(a.HQ / a.H);
     const int c8 = threadIdx.x % CPR, r0 = threadIdx.x / CPR;
     const int arow = min(c * TILE + ANCHOR_ROW, sg.len - 1);
@@ -118,63 +125,74 @@ __global__ __launch_bounds__(256) void key_cache_kernel(PrepArgs a) {
     }
     const T *kin = static_cast<const T *>(a.k);
     T *kout = static_cast<T *>(a.kt) + ((int64_t)tile * a.HQ + hq) * TILE * K;
-    for (int r = r0; r < TILE; r += RPP) {
-        const int j = c * TILE + r;
-        f32x8 out = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    // all of the thread's rows in flight before any is used
+    f32x8 kv[NPASS], pv[NPASS];
+#pragma unroll
+    for (int p = 0; p < NPASS; ++p) {
+        const int j = c * TILE + r0 + p * RPP;
+        kv[p] = f32x8{};
+        pv[p] = f32x8{};
         if (j < sg.len) {
             const int64_t tok = sg.start + j;
-            const f32x8 kv = Vec8<T>::load(kin + (tok * a.H + h) * K + c8 * 8);
-            const f32x8 pv = *reinterpret_cast<const f32x8 *>(a.P + (tok * a.HQ + hq) * K + c8 * 8);
-            for (int e = 0; e < 8; ++e)
-                out[e] = kv[e] * exp2f(fminf(fmaxf(R[e] - pv[e], EXP2_LO), EXP2_HI));
+            kv[p] = Vec8<T>::load(kin + (tok * a.H + h) * K + c8 * 8);
+            pv[p] = *reinterpret_cast<const f32x8 *>(a.P + (tok * a.HQ + hq) * K + c8 * 8);
         }
-        Vec8<T>::store(kout + r * K + c8 * 8, out);
+    }
+#pragma unroll
+    for (int p = 0; p < NPASS; ++p) {
+        f32x8 out;
+        for (int e = 0; e < 8; ++e) out[e] = kv[p][e] * exp2f(fminf(fmaxf(R[e] - pv[p][e], EXP2_LO), EXP2_HI));
+        Vec8<T>::store(kout + (r0 + p * RPP) * K + c8 * 8, out);
     }
 }
 
 // Value tile of (tile, kv head): transposed [V][TILE] (TRANSPOSE) or [TILE][V].
+// Thread (kb, db) moves the 8 x 8 block of keys 8kb.. and values 8db..
 template <typename T, int V, bool TRANSPOSE>
-__global__ __launch_bounds__(256) void value_tile_kernel(PrepArgs a) {
-    constexpr int CPR = V / 8;
-    constexpr int RPP = 256 / CPR;
-    constexpr int PITCH = V + 1;  // odd float pitch: conflict-free column reads
-    __shared__ float sv[TILE * PITCH];
-    const int tile = blockIdx.x, h = blockIdx.y;
-    const int s = find_seg(a.seg, (int)a.nseg, tile);
-    const SegInfo sg = a.seg[s];
+__device__ inline void value_tile(const PrepArgs &a, int tile, int h, const SegInfo &sg) {
+    constexpr int DB = V / 8, KB = TILE / 8;
     const int c = tile - sg.tile_base;
-    if (c < 0 || c * TILE >= sg.len) return;
     const T *vin = static_cast<const T *>(a.v);
     T *vout = static_cast<T *>(a.vt) + ((int64_t)tile * a.H + h) * V * TILE;
-    const int c8 = threadIdx.x % CPR, r0 = threadIdx.x / CPR;
-    for (int r = r0; r < TILE; r += RPP) {
-        const int j = c * TILE + r;
-        f32x8 x = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        if (j < sg.len) x = Vec8<T>::load(vin + ((int64_t)(sg.start + j) * a.H + h) * V + c8 * 8);
+    for (int t = threadIdx.x; t < DB * KB; t += blockDim.x) {
+        const int db = t % DB, kb = t / DB;
+        f32x8 x[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int j = c * TILE + kb * 8 + i;
+            x[i] = j < sg.len ? Vec8<T>::load(vin + ((int64_t)(sg.start + j) * a.H + h) * V + db * 8) : f32x8{};
+        }
         if (TRANSPOSE) {
-            for (int e = 0; e < 8; ++e) sv[r * PITCH + c8 * 8 + e] = x[e];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                f32x8 col;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) col[i] = x[i][e];
+                Vec8<T>::store(vout + (db * 8 + e) * TILE + kb * 8, col);
+            }
         } else {
-            Vec8<T>::store(vout + r * V + c8 * 8, x);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) Vec8<T>::store(vout + (kb * 8 + i) * V + db * 8, x[i]);
         }
     }
-    if (!TRANSPOSE) return;
-    __syncthreads();
-    // write [V][TILE]: 16 threads cover one value row of 128 keys, 8 keys each
-    const int k8 = threadIdx.x % (TILE / 8), d0 = threadIdx.x / (TILE / 8);
-    for (int d = d0; d < V; d += 256 / (TILE / 8)) {
-        f32x8 x;
-        for (int e = 0; e < 8; ++e) x[e] = sv[(k8 * 8 + e) * PITCH + d];
-        Vec8<T>::store(vout + d * TILE + k8 * 8, x);
-    }
+}
+
+// blockIdx.y < HQ: keys of query head y; else values of kv head y - HQ.
+template <typename T, int K, int V, bool TRANSPOSE>
+__global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
+    const int tile = blockIdx.x, y = blockIdx.y;
+    SegInfo sg;
+    if (!block_segment(a, tile, tile == 0 && y == 0, sg)) return;  // beyond the last used tile
+    if ((tile - sg.tile_base) * TILE >= sg.len) return;
+    if (y < a.HQ)
+        key_tile<T, K>(a, tile, y, sg);
+    else
+        value_tile<T, V, TRANSPOSE>(a, tile, y - (int)a.HQ, sg);
 }
 
 template <typename T, int K, int V, bool TRANSPOSE>
 hipError_t run_prep(const PrepArgs &a, hipStream_t st) {
-    hipLaunchKernelGGL((key_cache_kernel<T, K>), dim3((unsigned)a.tiles, (unsigned)a.HQ),
-                       dim3(256), 0, st, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((value_tile_kernel<T, V, TRANSPOSE>), dim3((unsigned)a.tiles, (unsigned)a.H),
+    hipLaunchKernelGGL((prep_kernel<T, K, V, TRANSPOSE>), dim3((unsigned)a.tiles, (unsigned)(a.HQ + a.H)),
                        dim3(256), 0, st, a);
     return hipGetLastError();
 }
@@ -188,13 +206,6 @@ hipError_t dispatch_prep(const PrepArgs &a, hipStream_t st) {
 }
 
 }  // namespace
-
-hipError_t launch_seg_table(SegInfo *seg, const int32_t *cu, int64_t nseg, int64_t B, int64_t T,
-                            hipStream_t st) {
-    (void)B;
-    hipLaunchKernelGGL(seg_table_kernel, dim3(1), dim3(256), 0, st, seg, cu, (int)nseg, (int)T);
-    return hipGetLastError();
-}
 
 hipError_t launch_prep(const PrepArgs &a, bool bf16, hipStream_t st) {
     return bf16 ? dispatch_prep<__bf16, true>(a, st) : dispatch_prep<float, false>(a, st);
