@@ -24,9 +24,11 @@
 //   S^T = k~ q~^T - m on v_mfma_f32_32x32x16_bf16: the accumulator starts at
 //       -m (the running max), so scores come back already relative to it,
 //       one query column per lane, all softmax state in-lane;
-//   softmax online in the log2 domain, fp32; the running max is raised only
-//       when a sub-block exceeds it by more than RESCALE (rare after the
-//       diagonal), and O is then rescaled in a branch of its own;
+//   softmax online in the log2 domain, fp32, with a lazy running max: the
+//       exps of a sub-block are taken against the current m, and only when
+//       a query's sum of them exceeds PSUM_LIM (or the lane has not seen a
+//       visible key yet) does a branch of its own raise m to the sub-block's
+//       max, move the scores, owe O a rescale and redo the exps;
 //   O^T += v^T p^T on the same MFMA, p as bf16.
 //
 // Software pipeline.  Step b of tile c runs the softmax of sub-block b, the QK
@@ -76,7 +78,9 @@ constexpr int BQ = 2 * TILE;    // query rows per block: two anchor tiles
 constexpr int NW = BQ / WQ;     // waves per workgroup
 constexpr int SB = 32;          // keys per sub-block (one MFMA m-tile)
 constexpr int NSB = TILE / SB;  // sub-blocks per tile (pipeline steps per tile)
-constexpr float RESCALE = 10.0f;  // log2 headroom before the running max is raised
+// a query's sum of the 32 p of one sub-block above this raises m (so every p
+// stays at most 2^12 before it is rounded to bf16 and summed in fp32)
+constexpr float PSUM_LIM = 4096.0f;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -242,15 +246,14 @@ __device__ __forceinline__ void load_gk(char *dst, const float *g0, int64_t HQ, 
 
 // ---------------------------------------------------------------- tile plan
 // The instruction stream of one tile, fixed at compile time.  Per step b
-// (3, 2, 1, 0): softmax stages SMA (mask, gate, first max level), SMB (max),
-// SMC (raise test), SMD0..7 (exps, packing and row sums of two keys each),
-// SME; PV products (index t*VT + vt) and QK products (index s8); CARRY of one
-// channel step of q~ to the next tile (first half in step 1 after its last
-// use, second half in step 0); the barriers BARV (start of step 2) and BARK
-// (in step 0, after the carries); RESC (an owed rescale of O) ends each step.
-// QK products only start after SMC, which may move m and with it the
-// accumulator start -m.
-enum OpKind : int { O_PV, O_QK, O_CARRY, O_SMA, O_SMB, O_SMC, O_SMD, O_SME, O_BARV, O_BARK, O_RESC };
+// (3, 2, 1, 0): softmax stages SMA (masks, gate), SMD0..7 (exps, packing and
+// row sums of two keys each), SME (the last pair, the raise test and its
+// rare branch); PV products (index t*VT + vt) and QK products (index s8);
+// CARRY of one channel step of q~ to the next tile (after its last use in
+// step 1, before BARK in step 0); the barriers BARV (start of step 2) and
+// BARK (in step 0, after the carries); RESC (an owed rescale of O) ends each
+// step.
+enum OpKind : int { O_PV, O_QK, O_CARRY, O_SMA, O_SMD, O_SME, O_BARV, O_BARK, O_RESC };
 struct TOp {
     int kind, step, idx;
 };
@@ -265,8 +268,7 @@ struct TilePlan {
     // vector instructions per op (the common path), used to spread them evenly
     // over the step's matrix products
     static constexpr int cost(int kind) {
-        return kind == O_SMA ? 5 : kind == O_SMB ? 5 : kind == O_SMC ? 5 : kind == O_SMD ? 4 : kind == O_SME ? 5
-             : kind == O_CARRY ? 12 : 0;
+        return kind == O_SMA ? 2 : kind == O_SMD ? 4 : kind == O_SME ? 8 : kind == O_CARRY ? 12 : 0;
     }
 
     // One step b: its matrix products in order (three value products first,
@@ -281,39 +283,41 @@ struct TilePlan {
     static constexpr int build_step(OpArr &a, int n, int b, int &car) {
         TOp mf[NPV + NQK + 1]{};
         int nm = 0, nmfma = 0;
-        if (b == 0) {
+        {
+            // A barrier publishes data the products right after it would read
+            // at once: let two products that read older data follow it first.
             int pv = 0, qk = 0;
-            for (; pv < NPV - 2; ++pv) mf[nm++] = TOp{O_PV, b, pv};
-            mf[nm++] = TOp{O_BARK, b, 0};
-            while (pv < NPV || qk < NQK) {
-                if (qk < NQK) mf[nm++] = TOp{O_QK, b, qk++};
-                if (pv < NPV) mf[nm++] = TOp{O_PV, b, pv++};
+            if (b == 0) {  // the carries go between these value products, before BARK
+                for (; pv < NPV - 2; ++pv) mf[nm++] = TOp{O_PV, b, pv};
+                mf[nm++] = TOp{O_BARK, b, 0};
+                mf[nm++] = TOp{O_PV, b, pv++};
+                mf[nm++] = TOp{O_PV, b, pv++};
+            } else if (b == 2) {  // the values of this tile arrive at BARV
+                mf[nm++] = TOp{O_QK, b, qk++};
+                mf[nm++] = TOp{O_BARV, b, 0};
+                mf[nm++] = TOp{O_QK, b, qk++};
+                mf[nm++] = TOp{O_QK, b, qk++};
+            } else {
+                mf[nm++] = TOp{O_PV, b, pv++};
             }
-        } else {
-            int pv = 0, qk = 0;
-            for (; pv < 3; ++pv) mf[nm++] = TOp{O_PV, b, pv};
             while (pv < NPV || qk < NQK) {
                 if (qk < NQK) mf[nm++] = TOp{O_QK, b, qk++};
                 if (pv < NPV) mf[nm++] = TOp{O_PV, b, pv++};
             }
         }
         nmfma = NPV + NQK;
-        TOp chain[3 + NSMD + 1]{};
+        TOp chain[1 + NSMD]{};
         int nc = 0;
         chain[nc++] = TOp{O_SMA, b, 0};
-        chain[nc++] = TOp{O_SMB, b, 0};
-        chain[nc++] = TOp{O_SMC, b, 0};
         for (int k = 0; k < NSMD; ++k) chain[nc++] = TOp{O_SMD, b, k};
-        chain[nc++] = TOp{O_SME, b, 0};
         const int c_hi = b <= 1 ? KS : 0;  // carries allowed in this step
         int ch_total = 0;
         for (int i = 0; i < nc; ++i) ch_total += cost(chain[i].kind);
         // the carries' budget and the products they are spread over
         const int car_total = b == 1 ? NC1 * cost(O_CARRY) : b == 0 ? (KS - car) * cost(O_CARRY) : 0;
         const int car_slots = b == 0 ? NPV - 2 : nmfma;
-        int ci = 0, ch_placed = 0, car_placed = 0, done = 0, smc_slot = -1, slot = 0;
+        int ci = 0, ch_placed = 0, car_placed = 0, done = 0, sma_slot = -1;
         bool qk_done[KS]{};
-        if (b == 2) a[n++] = TOp{O_BARV, b, 0};
         for (int e = 0; e < nm; ++e) {
             const TOp m = mf[e];
             if (m.kind == O_BARK) {
@@ -321,27 +325,23 @@ struct TilePlan {
                 a[n++] = m;
                 continue;
             }
-            if (m.kind == O_QK) {
-                while (ci < 3) { a[n++] = chain[ci++]; ch_placed += cost(O_SMA); smc_slot = slot; }
+            if (m.kind == O_BARV) {
+                a[n++] = m;
+                continue;
             }
             a[n++] = m;
             ++done;
-            ++slot;
             if (m.kind == O_QK) qk_done[m.idx] = true;
+            if (ci == 0) {  // SMA right after the first product (it reads what the last step's products wrote)
+                a[n++] = chain[ci++];
+                ch_placed += cost(O_SMA);
+                sma_slot = done;
+            }
             const int ch_t = ch_total * done / nmfma;
             const int car_t = car_total * (done < car_slots ? done : car_slots) / car_slots;
-            bool stage = false;
             for (;;) {
-                if (ci < 3) {  // SMA, SMB, SMC: one per product, as early as possible
-                    if (stage) break;
-                    a[n++] = chain[ci++];
-                    ch_placed += cost(O_SMA);
-                    stage = true;
-                    if (ci == 3) smc_slot = slot;
-                    continue;
-                }
                 const bool car_ok = car < c_hi && (b == 0 || qk_done[car]);
-                const bool ch_ok = ci < nc && !(ci == 3 && smc_slot == slot);
+                const bool ch_ok = ci < nc && !(ci == 1 && sma_slot == done);
                 if (car_ok && car_placed + cost(O_CARRY) / 2 <= car_t) {
                     a[n++] = TOp{O_CARRY, b, car++};
                     car_placed += cost(O_CARRY);
@@ -356,6 +356,9 @@ struct TilePlan {
         if (b == 0)
             while (car < c_hi) a[n++] = TOp{O_CARRY, b, car++};
         while (ci < nc) a[n++] = chain[ci++];
+        // after every product of the step: SME may move m, and with it the
+        // scores the step's products just wrote
+        a[n++] = TOp{O_SME, b, 0};
         a[n++] = TOp{O_RESC, b, 0};
         return n;
     }
@@ -456,18 +459,16 @@ struct Wave {
     // accumulators and softmax state for the lane's query column: m is the
     // running max (log2 units) the scores are taken relative to; negm holds -m
     // in all 16 accumulator slots and starts every QK product.  Until a lane
-    // has seen a visible key m is 0 and any score raises it (thr).
+    // has seen a visible key m is 0 and any score raises it (lim < 0).
     f32x16 O[VT];
     f32x16 negm;
     float m, l;
     float alpha;  // rescale O still owes for the current step (1 if none)
-    float thr;    // a step max above m + thr raises m: -FLT_MAX at first, then RESCALE
+    float lim;    // a step's sum of p above this raises m: -1 until the first visible key, then PSUM_LIM
     QOp<K> qop;
     f32x16 S[2];           // S[b & 1]: scores of the sub-block softmaxed in step b
     uint32_t Pw[2][2][4];  // Pw[b & 1][t]: packed bf16 p of that sub-block, keys 16t + 8hl + e
     bf16x8 ring[NPF];      // LDS operand reads in flight
-    float red[5];          // partial maxima of the current step
-    float mt;              // the step's max, relative to m
     float ex[2][2];        // exps of the last two key pairs, packed one op later
     float part[2];         // partial row sums of the current step
 
@@ -550,35 +551,6 @@ struct Wave {
                 s[8 + e] -= g1[e];
             }
         }
-        red[0] = max3(s[0], s[1], s[2]);
-        red[1] = max3(s[3], s[4], s[5]);
-        red[2] = max3(s[6], s[7], s[8]);
-        red[3] = max3(s[9], s[10], s[11]);
-        red[4] = max3(s[12], s[13], s[14]);
-#pragma unroll
-        for (int i = 0; i < 5; ++i) pin(red[i]);
-    }
-    template <int B>
-    __device__ __forceinline__ void smb() {
-        const f32x16 &s = S[B & 1];
-        const float a = max3(red[0], red[1], red[2]);
-        const float b = max3(red[3], red[4], s[15]);
-        mt = pair_max(__builtin_elementwise_maximum(a, b));
-        pin(mt);
-    }
-    template <int B>
-    __device__ __forceinline__ void smc() {
-        const bool raise = mt > thr;
-        if (__any(raise)) {
-            const float delta = raise ? mt : 0.f;
-            const float al = fast_exp2(-delta);
-            m += delta;
-            l *= al;
-            alpha *= al;
-            thr = raise ? RESCALE : thr;
-            negm -= delta;
-            S[B & 1] -= delta;
-        }
     }
     // SMD KK: the exps of key pair KK.  The pair before it is rounded and
     // packed, and the one before that summed, in the same op, so that no op
@@ -607,12 +579,45 @@ struct Wave {
         part[KK & 1] = __builtin_amdgcn_fdot2_f32_bf16(p, one, KK < 2 ? 0.f : part[KK & 1], false);
         pin(part[KK & 1]);
     }
+    template <int B, int... KKs>
+    __device__ __forceinline__ void redo(std::integer_sequence<int, KKs...>) {
+        (smd<B, KKs>(), ...);
+        pack<B, 7>();
+        rowsum<B, 6>();
+        rowsum<B, 7>();
+    }
+    // The step's last pair, then the raise test on the lane's sum of p.  The
+    // branch (first visible keys, or p grown past PSUM_LIM) raises m to the
+    // step's max, moves this step's scores and the next sub-block's (already
+    // started from the old -m), owes O the factor, and redoes the exps.
     template <int B>
     __device__ __forceinline__ void sme() {
         pack<B, 7>();
         rowsum<B, 6>();
         rowsum<B, 7>();
-        l += part[0] + part[1];
+        float ps = part[0] + part[1];
+        const float pq = pair_sum(ps);  // the query's sum over the sub-block's 32 keys
+        if (__any(pq > lim)) {
+            f32x16 &s = S[B & 1];
+            const float a = max3(max3(s[0], s[1], s[2]), max3(s[3], s[4], s[5]), max3(s[6], s[7], s[8]));
+            const float b = max3(max3(s[9], s[10], s[11]), max3(s[12], s[13], s[14]), s[15]);
+            const float mt = pair_max(__builtin_elementwise_maximum(a, b));
+            const bool raise = lim < 0.f ? mt > -FLT_MAX : pq > lim;
+            if (__any(raise)) {
+                const float delta = raise ? mt : 0.f;
+                const float al = fast_exp2(-delta);
+                m += delta;
+                l *= al;
+                alpha *= al;
+                lim = raise ? PSUM_LIM : lim;
+                negm -= delta;
+                s -= delta;
+                S[(B + 1) & 1] -= delta;
+                redo<B>(std::make_integer_sequence<int, Plan::NSMD>{});
+                ps = part[0] + part[1];
+            }
+        }
+        l += ps;
         pin(l);
     }
     __device__ __forceinline__ void resc() {
@@ -719,10 +724,7 @@ struct Kernel {
             pin(wv.qop[o.idx]);
         } else if constexpr (o.kind == O_SMA) {
             wv.template sma<B>();
-        } else if constexpr (o.kind == O_SMB) {
-            wv.template smb<B>();
-        } else if constexpr (o.kind == O_SMC) {
-            wv.template smc<B>();
+
         } else if constexpr (o.kind == O_SMD) {
             wv.template smd<B, o.idx>();
         } else if constexpr (o.kind == O_SME) {
@@ -851,7 +853,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
         wv.m = 0.f;
         wv.l = 0.f;
         wv.alpha = 1.f;
-        wv.thr = -FLT_MAX;
+        wv.lim = wave_on ? -1.f : __builtin_inff();  // a wave with no rows never raises
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -860,12 +862,14 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
         // ---- prologue: q~ at the diagonal tile; tile c_hi into buffers 0, the keys of
         // tile c_hi - 1 into key buffer 1
         __syncthreads();  // the previous block's last reads of every buffer are done
-        if (wave_on) load_qop<K, false>(a, sg, hq, qt_w, qrow, hl, wv.qop);
+        // the first two key tiles and the first value tile are copied while q~
+        // is built
         kr.issue_k(k0, c_hi);
         kr.issue_v(v0, c_hi);
+        kr.issue_k(k1, max(c_hi - 1, c_lo));
+        if (wave_on) load_qop<K, false>(a, sg, hq, qt_w, qrow, hl, wv.qop);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        kr.issue_k(k1, max(c_hi - 1, c_lo));
         // the scores of the first sub-block (3 of tile c_hi), S[1]
         {
             const char *kb = k0 + wv.kbase + (NSB - 1) * (SB / KL::NBLK) * (2 * K);
@@ -910,7 +914,10 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
                 }
         }
 
-        // ---- epilogue: sink, normalisation, o and lse
+        // ---- epilogue: sink, normalisation, o and lse.  Every wave is past its
+        // last LDS read (and every copy has landed) before o is staged in the
+        // tile buffers.
+        __syncthreads();
         if (wave_on) {
             const float l_tot = pair_sum(wv.l);
             const float m_true = wv.m + g_i;
@@ -921,22 +928,35 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
                 l_fin = l_tot * exp2f(m_true - m_fin) + exp2f(sb - m_fin);
             }
             const float fac = exp2f(m_true - m_fin) / l_fin;
-            if (qrow < sg.len) {
-                const int64_t tok = (int64_t)sg.start + qrow;
-                __bf16 *orow = static_cast<__bf16 *>(a.o) + (tok * HQ + hq) * V;
+            // o through LDS (the wave's own rows, OPITCH bytes apart so that the
+            // 32 rows' writes spread over the banks, in one of the tile
+            // buffers) so that each global store writes whole rows
+            constexpr int OPITCH = 2 * V + 16;
+            static_assert(2 * WQ * OPITCH <= LY::KBUF && 2 * WQ * OPITCH <= VL::BYTES, "staging fits");
+            char *ob = ((w >> 1) == 0 ? k0 : (w >> 1) == 1 ? k1 : (w >> 1) == 2 ? v0 : v1) + (w & 1) * (WQ * OPITCH);
 #pragma unroll
-                for (int vt = 0; vt < VT; ++vt) {
+            for (int vt = 0; vt < VT; ++vt) {
 #pragma unroll
-                    for (int r4 = 0; r4 < 4; ++r4) {
-                        f32x4 y;
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    f32x4 y;
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) y[e] = wv.O[vt][4 * r4 + e] * fac;
-                        *reinterpret_cast<bf16x4 *>(orow + 32 * vt + 8 * r4 + 4 * hl) =
-                            __builtin_convertvector(y, bf16x4);
-                    }
+                    for (int e = 0; e < 4; ++e) y[e] = wv.O[vt][4 * r4 + e] * fac;
+                    *reinterpret_cast<bf16x4 *>(ob + col * OPITCH + 2 * (32 * vt + 8 * r4 + 4 * hl)) =
+                        __builtin_convertvector(y, bf16x4);
                 }
-                if (a.lse && hl == 0) a.lse[tok * HQ + hq] = (m_fin + log2f(l_fin)) * LN2;
             }
+            constexpr int CPR = V * 2 / 16;  // 16-byte chunks per row
+#pragma unroll
+            for (int i = 0; i < WQ * CPR / 64; ++i) {
+                const int r = (64 * i + lane) / CPR, ch = (64 * i + lane) % CPR;
+                const uint4 x = *reinterpret_cast<const uint4 *>(ob + r * OPITCH + 16 * ch);
+                if (q0w + r < sg.len) {
+                    const int64_t tok = (int64_t)sg.start + q0w + r;
+                    *reinterpret_cast<uint4 *>(static_cast<char *>(a.o) + ((tok * HQ + hq) * V) * 2 + 16 * ch) = x;
+                }
+            }
+            if (qrow < sg.len && a.lse && hl == 0)
+                a.lse[((int64_t)sg.start + qrow) * HQ + hq] = (m_fin + log2f(l_fin)) * LN2;
         }
     }
 }

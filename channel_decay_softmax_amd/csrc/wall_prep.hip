@@ -177,10 +177,13 @@ __device__ inline void value_tile(const PrepArgs &a, int tile, int h, const SegI
     }
 }
 
-// blockIdx.y < HQ: keys of query head y; else values of kv head y - HQ.
+// Block id = tile * (HQ + H) + y; y < HQ: keys of query head y, else values
+// of kv head y - HQ.  The heads of one tile are neighbours in launch order, so
+// the query heads that share a kv head read its key rows from L2.
 template <typename T, int K, int V, bool TRANSPOSE>
 __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
-    const int tile = blockIdx.x, y = blockIdx.y;
+    const int nh = (int)(a.HQ + a.H);
+    const int tile = blockIdx.x / nh, y = blockIdx.x % nh;
     SegInfo sg;
     if (!block_segment(a, tile, tile == 0 && y == 0, sg)) return;  // beyond the last used tile
     if ((tile - sg.tile_base) * TILE >= sg.len) return;
@@ -192,8 +195,8 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
 
 template <typename T, int K, int V, bool TRANSPOSE>
 hipError_t run_prep(const PrepArgs &a, hipStream_t st) {
-    hipLaunchKernelGGL((prep_kernel<T, K, V, TRANSPOSE>), dim3((unsigned)a.tiles, (unsigned)(a.HQ + a.H)),
-                       dim3(256), 0, st, a);
+    hipLaunchKernelGGL((prep_kernel<T, K, V, TRANSPOSE>), dim3((unsigned)((a.HQ + a.H) * a.tiles)), dim3(256), 0,
+                       st, a);
     return hipGetLastError();
 }
 
