@@ -79,6 +79,10 @@ def assert_parity(o, lse, o_ref, lse_ref, dtype, rows=None, what=""):
     dict(shape=(1, 1500, 3, 5), dtype=torch.float32, cu=[0, 1, 130, 130, 600, 1500]),
     dict(shape=(1, 777, 7), dtype=torch.bfloat16, cu=[0, 256, 257, 777]),
     dict(shape=(3, 129, 1), dtype=torch.float32, cu=None),
+    # longer inputs: sequence starts on, next to and between 128- and 1024-row boundaries
+    dict(shape=(1, 5000, 3, 8), dtype=torch.float32, cu=[0, 1, 1024, 1025, 3000, 3000, 5000]),
+    dict(shape=(2, 3000, 2, 64), dtype=torch.bfloat16, cu=None),
+    dict(shape=(1, 4500, 5), dtype=torch.bfloat16, cu=[0, 4500]),
 ])
 def test_prefix_scan_parity(case):
     rng = np.random.default_rng(7)
@@ -95,6 +99,21 @@ def test_prefix_scan_parity(case):
     inc = np.diff(Pg, axis=1)
     inc_ref = np.diff(ref, axis=1)
     assert np.abs(inc - inc_ref).max() <= 4e-6 * np.maximum(1.0, np.abs(ref).max())
+
+
+@pytest.mark.parametrize("case", [
+    dict(shape=(1, 5000, 3, 8), dtype=torch.float32, cu=[0, 1, 1024, 1025, 3000, 3000, 5000]),
+    dict(shape=(2, 3000, 2, 64), dtype=torch.bfloat16, cu=None),
+])
+def test_prefix_scan_repeats_bit_for_bit(case):
+    rng = np.random.default_rng(11)
+    x = torch.from_numpy(-np.abs(rng.standard_normal(case["shape"]))).to(case["dtype"]).to(DEV)
+    cu = None if case["cu"] is None else torch.tensor(case["cu"], dtype=torch.int32, device=DEV)
+    say(f"prefix_scan repeat {case['shape']} {case['dtype']} cu={case['cu']}")
+    P1 = wall.wall_prefix_scan(x, cu)
+    P2 = wall.wall_prefix_scan(x, cu)
+    torch.cuda.synchronize()
+    assert torch.equal(P1, P2)
 
 
 def test_prefix_scan_long_bimodal_gate():
