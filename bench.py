@@ -10,7 +10,9 @@ H=4, K=V=128, bf16, bimodal gate), on which the headline metric is quoted.
 
 Prints one JSON line.  ``value`` is whole-step throughput in counted TFLOP/s
 (4*K per visible query/key pair and query head: 2K for QK^T and 2V for PV,
-K = V), timed over K back-to-back steps; ``roofline`` prices the fused
+K = V), timed over K back-to-back steps after W untimed ones (the defaults
+keep the timed steps in the steady state of the part's clocks, which the
+first ~40 ms of work after idle do not reach); ``roofline`` prices the fused
 forward kernel alone, timed with HIP events on the stream it is launched on
 over a second pass of the same K steps (an event record leaves a gap on the
 stream, so none sits in the timed region), against the dense bf16 MFMA peak;
@@ -138,8 +140,11 @@ def cpu_baseline(inp, flop_per_pair, target_s):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=int(os.environ.get("WORLD_SIZE", "1")))
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    # the part's clocks settle after about 40 ms of back-to-back steps (the
+    # first steps after idle run up to 20% slower): the defaults warm up for
+    # about 60 ms and time about 60 ms of steady state
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="long_bf16")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
