@@ -7,8 +7,8 @@ no code.
 
 ``wall_oracle.c`` holds the arithmetic (the product form of the Wall Attention
 blog's "Definition: Wall Attention" section, with the README's optional
-arguments); this module only builds it with gcc, loads it with ctypes and
-converts arrays.  Every function here takes and returns float64 numpy arrays.
+arguments, and the README's decode cache and cached decode); this module only
+builds it with gcc, loads it with ctypes and converts arrays.  Every function here takes and returns float64 numpy arrays.
 """
 
 from __future__ import annotations
@@ -25,7 +25,8 @@ _SRC = os.path.join(_HERE, "wall_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
-__all__ = ["build", "wall_attn_oracle", "prefix_scan_oracle", "num_threads"]
+__all__ = ["build", "wall_attn_oracle", "prefix_scan_oracle", "kv_cache_oracle", "decode_oracle",
+           "num_threads"]
 
 
 def build(force: bool = True) -> str:
@@ -49,6 +50,10 @@ def _bind(path: str):
     lib.wall_oracle_fwd.restype = ctypes.c_int
     lib.wall_oracle_prefix_scan.argtypes = [P, P, I, I, I, P, I, ctypes.c_double]
     lib.wall_oracle_prefix_scan.restype = ctypes.c_int
+    lib.wall_oracle_kv_cache.argtypes = [P, P, P, P, I, I, I, I, I, I]
+    lib.wall_oracle_kv_cache.restype = ctypes.c_int
+    lib.wall_oracle_decode.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, ctypes.c_double]
+    lib.wall_oracle_decode.restype = ctypes.c_int
     lib.wall_oracle_num_threads.argtypes = []
     lib.wall_oracle_num_threads.restype = ctypes.c_int
     return lib
@@ -140,3 +145,47 @@ def prefix_scan_oracle(x, cu_seqlens=None, scale: float = 1.0 / np.log(2.0)):
     if rc != 0:
         raise ValueError(f"wall_oracle_prefix_scan rejected its arguments (code {rc})")
     return out
+
+
+def kv_cache_oracle(k, P, chunk_size: int = 64):
+    """The README's decode cache in fp64: ``k_tilde [B,T,HQ,K]`` (keys with the
+    decay folded in against per-chunk anchors) and ``r_cache [B,ceil(T/C),HQ,K]``
+    (the anchors, floor of P at each chunk's first row).  k is [B,T,H,K], P the
+    log2 prefix [B,T,HQ,K]."""
+    k, P = _f64(k), _f64(P)
+    B, T, H, K = k.shape
+    HQ = P.shape[2]
+    assert P.shape == (B, T, HQ, K)
+    C = int(chunk_size)
+    NC = (T + C - 1) // C
+    kt = np.empty((B, T, HQ, K))
+    r = np.empty((B, NC, HQ, K))
+    rc = _load().wall_oracle_kv_cache(_ptr(k), _ptr(P), _ptr(kt), _ptr(r), B, T, HQ, H, K, C)
+    if rc != 0:
+        raise ValueError(f"wall_oracle_kv_cache rejected its arguments (code {rc})")
+    return kt, r
+
+
+def decode_oracle(q, v, p_curr, k_tilde, r_cache, chunk_size: int = 64, sink_bias=None,
+                  scale: Optional[float] = None):
+    """The README's cached decode in fp64: q and p_curr [B,1,HQ,K] (the current
+    query and its log2 prefix), v [B,T,H,V], the cache of kv_cache_oracle.
+    Returns ``(o [B,1,HQ,V], lse [B,1,HQ])``."""
+    q, v, pc = _f64(q), _f64(v), _f64(p_curr)
+    kt, r, sk = _f64(k_tilde), _f64(r_cache), _f64(sink_bias)
+    B, _, HQ, K = q.shape
+    T, H, V = v.shape[1], v.shape[2], v.shape[3]
+    C = int(chunk_size)
+    assert q.shape == (B, 1, HQ, K) and pc.shape == (B, 1, HQ, K)
+    assert kt.shape == (B, T, HQ, K) and r.shape == (B, (T + C - 1) // C, HQ, K)
+    if sk is not None:
+        assert sk.shape == (HQ,)
+    if scale is None:
+        scale = K ** -0.5
+    o = np.empty((B, 1, HQ, V))
+    lse = np.empty((B, 1, HQ))
+    rc = _load().wall_oracle_decode(_ptr(q), _ptr(v), _ptr(pc), _ptr(kt), _ptr(r), _ptr(sk), _ptr(o),
+                                    _ptr(lse), B, T, HQ, H, K, V, C, float(scale))
+    if rc != 0:
+        raise ValueError(f"wall_oracle_decode rejected its arguments (code {rc})")
+    return o, lse

@@ -175,6 +175,108 @@ int wall_oracle_prefix_scan(const double *x, double *out, int64_t B, int64_t T, 
     return 0;
 }
 
+/* Decode cache, wall-attention-release README ("Decode (cached generation)"):
+ * the keys with the decay folded in, per chunk of C rows,
+ *     k_tilde[b,j,hq,n] = k[b,j,h,n] * exp2(R[b,c,hq,n] - P[b,j,hq,n]),  c = j / C,
+ * with the chunk anchor R read as the floor of P at the chunk's first row
+ * (the README names a per-chunk anchor and its role, not the row; the first
+ * row is the one an append-as-you-go cache knows when the chunk opens).
+ * P is the log2 prefix [B,T,HQ,K] (prefix scan of g with scale 1/ln 2);
+ * h = hq / (HQ/H).  r_cache is [B, ceil(T/C), HQ, K]. */
+int wall_oracle_kv_cache(const double *k,  /* [B,T,H,K] */
+                         const double *P,  /* [B,T,HQ,K] */
+                         double *k_tilde,  /* [B,T,HQ,K] */
+                         double *r_cache,  /* [B,NC,HQ,K] */
+                         int64_t B, int64_t T, int64_t HQ, int64_t H, int64_t K, int64_t C)
+{
+    if (!k || !P || !k_tilde || !r_cache) return -1;
+    if (B < 1 || T < 1 || HQ < 1 || H < 1 || K < 1 || C < 1) return -2;
+    if (HQ % H != 0) return -3;
+    const int64_t group = HQ / H, NC = (T + C - 1) / C;
+#pragma omp parallel for collapse(3)
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t c = 0; c < NC; ++c)
+            for (int64_t hq = 0; hq < HQ; ++hq) {
+                const int64_t kvh = hq / group;
+                const int64_t j0 = c * C;
+                const double *Pa = P + ((b * T + j0) * HQ + hq) * K;
+                double *R = r_cache + ((b * NC + c) * HQ + hq) * K;
+                for (int64_t n = 0; n < K; ++n) R[n] = floor(Pa[n]);
+                for (int64_t j = j0; j < j0 + C && j < T; ++j) {
+                    const double *kj = k + ((b * T + j) * H + kvh) * K;
+                    const double *Pj = P + ((b * T + j) * HQ + hq) * K;
+                    double *kt = k_tilde + ((b * T + j) * HQ + hq) * K;
+                    for (int64_t n = 0; n < K; ++n) kt[n] = kj[n] * exp2(R[n] - Pj[n]);
+                }
+            }
+    return 0;
+}
+
+/* Decode, wall-attention-release README (wall_attn_decode): one query per
+ * (b, hq), at the row whose log2 prefix is p_curr, against every cached key
+ * j = 0 .. T-1 of sequence b:
+ *     logit_j = scale * sum_n q_n * exp2(p_curr_n - R[j / C, n]) * k_tilde[j, n],
+ * which is the forward's logit scale * sum_n exp2(p_curr_n - P_j,n) q_n k_j,n
+ * (the blog's factored form, "Definition: Wall Attention") with the anchor
+ * cancelling.  The optional sink adds one logit with a zero value; lse is
+ * the natural-log normaliser, sink included.  q, p_curr [B,HQ,K];
+ * v [B,T,H,V]; o [B,HQ,V]; lse [B,HQ] or NULL. */
+int wall_oracle_decode(const double *q, const double *v, const double *p_curr,
+                       const double *k_tilde, const double *r_cache, const double *sink,
+                       double *o, double *lse,
+                       int64_t B, int64_t T, int64_t HQ, int64_t H, int64_t K, int64_t V,
+                       int64_t C, double scale)
+{
+    if (!q || !v || !p_curr || !k_tilde || !r_cache || !o) return -1;
+    if (B < 1 || T < 1 || HQ < 1 || H < 1 || K < 1 || V < 1 || C < 1) return -2;
+    if (HQ % H != 0) return -3;
+    const int64_t group = HQ / H, NC = (T + C - 1) / C;
+    int fail = 0;
+#pragma omp parallel
+    {
+        double *logit = (double *)malloc(sizeof(double) * (size_t)T);
+        double *acc = (double *)malloc(sizeof(double) * (size_t)V);
+        if (!logit || !acc) {
+#pragma omp atomic write
+            fail = 1;
+        } else {
+#pragma omp for collapse(2)
+            for (int64_t b = 0; b < B; ++b)
+                for (int64_t hq = 0; hq < HQ; ++hq) {
+                    const int64_t kvh = hq / group;
+                    const double *qi = q + (b * HQ + hq) * K;
+                    const double *pc = p_curr + (b * HQ + hq) * K;
+                    for (int64_t j = 0; j < T; ++j) {
+                        const int64_t c = j / C;
+                        const double *R = r_cache + ((b * NC + c) * HQ + hq) * K;
+                        const double *kt = k_tilde + ((b * T + j) * HQ + hq) * K;
+                        double dot = 0.0;
+                        for (int64_t n = 0; n < K; ++n) dot += qi[n] * exp2(pc[n] - R[n]) * kt[n];
+                        logit[j] = scale * dot;
+                    }
+                    double m = -INFINITY;
+                    for (int64_t j = 0; j < T; ++j) m = logit[j] > m ? logit[j] : m;
+                    if (sink && sink[hq] > m) m = sink[hq];
+                    double Z = 0.0;
+                    for (int64_t d = 0; d < V; ++d) acc[d] = 0.0;
+                    for (int64_t j = 0; j < T; ++j) {
+                        const double p = exp(logit[j] - m);
+                        Z += p;
+                        const double *vj = v + ((b * T + j) * H + kvh) * V;
+                        for (int64_t d = 0; d < V; ++d) acc[d] += p * vj[d];
+                    }
+                    if (sink != NULL) Z += exp(sink[hq] - m);
+                    double *oi = o + (b * HQ + hq) * V;
+                    for (int64_t d = 0; d < V; ++d) oi[d] = acc[d] / Z;
+                    if (lse) lse[b * HQ + hq] = m + log(Z);
+                }
+        }
+        free(logit);
+        free(acc);
+    }
+    return fail ? -7 : 0;
+}
+
 int wall_oracle_num_threads(void)
 {
 #ifdef _OPENMP

@@ -43,6 +43,16 @@ MUTANTS = {
     "scan_scale_dropped": ("out[(b * T + t) * C + c] = scale * run;",
                            "out[(b * T + t) * C + c] = run;"),
     "scan_no_reset_at_sequence_start": ("if (t == cu_seqlens[s]) run = 0.0;", ";"),
+    "cache_factor_sign": ("kt[n] = kj[n] * exp2(R[n] - Pj[n]);", "kt[n] = kj[n] * exp2(Pj[n] - R[n]);"),
+    "cache_key_head_of_query": ("const double *kj = k + ((b * T + j) * H + kvh) * K;",
+                                "const double *kj = k + ((b * T + j) * H + hq % H) * K;"),
+    "decode_query_factor_sign": ("dot += qi[n] * exp2(pc[n] - R[n]) * kt[n];",
+                                 "dot += qi[n] * exp2(R[n] - pc[n]) * kt[n];"),
+    "decode_anchor_of_next_chunk": ("const int64_t c = j / C;", "const int64_t c = (j + 1 < T ? j + 1 : j) / C;"),
+    "decode_sink_dropped": ("if (sink != NULL) Z += exp(sink[hq] - m);", ";"),
+    "decode_scale_dropped": ("logit[j] = scale * dot;", "logit[j] = dot;"),
+    "decode_value_head": ("const double *vj = v + ((b * T + j) * H + kvh) * V;",
+                          "const double *vj = v + ((b * T + j) * H + 0) * V;"),
 }
 
 

@@ -325,3 +325,57 @@ def test_prefix_scan_matches_numpy_cumsum(oracle_mod):
     x = rnd(rng, 2, 77, 3, 5)
     P = oracle_mod.prefix_scan_oracle(x, scale=1.0 / math.log(2.0))
     np.testing.assert_allclose(P, np.cumsum(x, axis=1) / math.log(2.0), rtol=1e-13, atol=1e-13)
+
+
+# --------------------------------------------------------------------------- decode cache and decode
+
+
+@pytest.mark.parametrize("case", [
+    # strong decay, sink, GQA, a partial last chunk
+    dict(B=2, T=150, HQ=4, H=2, K=8, V=6, C=64, g=-0.3, sink=True, scale=0.35),
+    # gates of both signs, one row per chunk
+    dict(B=1, T=40, HQ=2, H=1, K=5, V=3, C=1, g=0.05, sink=False, scale=0.8),
+    # one chunk longer than the sequence, odd chunk size
+    dict(B=1, T=23, HQ=3, H=3, K=4, V=4, C=7, g=-1.0, sink=True, scale=0.5),
+    dict(B=3, T=23, HQ=2, H=1, K=4, V=2, C=64, g=-0.1, sink=False, scale=0.5),
+    # a single cached token
+    dict(B=2, T=1, HQ=2, H=2, K=3, V=5, C=64, g=-0.5, sink=True, scale=0.9),
+])
+def test_decode_equals_forward_last_row(oracle_mod, case):
+    """README: the decode kernel reproduces the training forward token for
+    token.  The cached decode (anchored keys, query factor exp2(p - R)) must
+    give the product-form forward's last row, for any anchors."""
+    rng = np.random.default_rng(31)
+    B, T, HQ, H, K, V, C = (case[x] for x in ("B", "T", "HQ", "H", "K", "V", "C"))
+    q, k, v = rnd(rng, B, T, HQ, K), rnd(rng, B, T, H, K), rnd(rng, B, T, H, V)
+    if case["g"] < 0:
+        g = case["g"] * np.abs(rnd(rng, B, T, HQ, K))
+    else:
+        g = case["g"] * rnd(rng, B, T, HQ, K)
+    sink = rnd(rng, HQ) if case["sink"] else None
+    P = oracle_mod.prefix_scan_oracle(g)
+    kt, r = oracle_mod.kv_cache_oracle(k, P, C)
+    assert r.shape == (B, -(-T // C), HQ, K)
+    assert np.array_equal(r, np.round(r))  # integer anchors: exact powers of two
+    o, l = oracle_mod.decode_oracle(q[:, -1:], v, P[:, -1:], kt, r, C, sink_bias=sink, scale=case["scale"])
+    of, lf = oracle_mod.wall_attn_oracle(q, k, v, g, scale=case["scale"], sink_bias=sink)
+    np.testing.assert_allclose(o[:, 0], of[:, -1], rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(l[:, 0], lf[:, -1], rtol=1e-12, atol=1e-12)
+
+
+def test_kv_cache_zero_gate_and_reconstruction(oracle_mod):
+    """g = 0: every anchor is 0 and k_tilde is k repeated over the query
+    heads of its group.  Any gate: the anchored keys carry exactly the
+    factor exp2(R - P_j), so k_tilde * exp2(P_j - R) gives k back."""
+    rng = np.random.default_rng(37)
+    B, T, HQ, H, K, C = 2, 70, 4, 2, 6, 16
+    k = rnd(rng, B, T, H, K)
+    kt, r = oracle_mod.kv_cache_oracle(k, np.zeros((B, T, HQ, K)), C)
+    assert not r.any()
+    np.testing.assert_array_equal(kt, np.repeat(k, HQ // H, axis=2))
+    P = oracle_mod.prefix_scan_oracle(-np.abs(rnd(rng, B, T, HQ, K)))
+    kt, r = oracle_mod.kv_cache_oracle(k, P, C)
+    Rj = np.repeat(r, C, axis=1)[:, :T]
+    np.testing.assert_allclose(kt * np.exp2(P - Rj), np.repeat(k, HQ // H, axis=2), rtol=1e-13, atol=1e-14)
+    # the factor stays within the chunk's decay: at most 1 below, never above the chunk start's prefix
+    assert (Rj - P > -1.0).all()
