@@ -17,15 +17,19 @@ from ._binding import (  # noqa: F401
     WALL_OK,
     WallError,
     attn_fwd_workspace_size,
+    build_wall_kv_cache,
     check_cu_seqlens,
+    decode_workspace_size,
     lib,
     prefix_scan_workspace_size,
     status_string,
     wall_attn,
+    wall_attn_decode,
     wall_attn_fwd,
     wall_attn_fwd_prepare,
     wall_attn_fwd_run,
     wall_prefix_scan,
 )
 
-__all__ = ["wall_attn", "wall_attn_fwd", "wall_prefix_scan", "WallError", "lib"]
+__all__ = ["wall_attn", "wall_attn_fwd", "wall_prefix_scan", "build_wall_kv_cache", "wall_attn_decode",
+           "WallError", "lib"]

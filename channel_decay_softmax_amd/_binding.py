@@ -27,6 +27,7 @@ EXPORTS = (
     "wall_prefix_scan_workspace_size", "wall_prefix_scan",
     "wall_attn_fwd_workspace_size", "wall_attn_fwd",
     "wall_attn_fwd_prepare", "wall_attn_fwd_run",
+    "wall_kv_cache_build", "wall_attn_decode_workspace_size", "wall_attn_decode",
 )
 
 _lib = None
@@ -66,6 +67,12 @@ def lib() -> ctypes.CDLL:
         L.wall_attn_fwd_run.argtypes = [P, E, P, P, P, P, P, I, I, I, I, I, I, F, I, P, I, I, P, S,
                                         P]
         L.wall_attn_fwd_run.restype = E
+        L.wall_kv_cache_build.argtypes = [P, E, P, P, P, I, I, I, I, I, I, I, I, P]
+        L.wall_kv_cache_build.restype = E
+        L.wall_attn_decode_workspace_size.argtypes = [I, I, I, I]
+        L.wall_attn_decode_workspace_size.restype = S
+        L.wall_attn_decode.argtypes = [P, P, E, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, P, S, P]
+        L.wall_attn_decode.restype = E
         _lib = L
     return _lib
 
@@ -256,3 +263,76 @@ def wall_attn_fwd_run(q: torch.Tensor, P: torch.Tensor, H: int, V: int, workspac
         K, V, float(K ** -0.5 if scale is None else scale), int(window_size or 0),
         _ptr(cu_seqlens), nseq, int(max_seqlen or 0), _ptr(workspace), workspace.numel(),
         _stream(dev)), "wall_attn_fwd_run")
+
+
+# --------------------------------------------------------------------------- decode
+
+
+def build_wall_kv_cache(k: torch.Tensor, P: torch.Tensor, chunk_size: int = 64,
+                        k_tilde: Optional[torch.Tensor] = None, r_cache: Optional[torch.Tensor] = None,
+                        t0: int = 0, t1: Optional[int] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """The README's build_wall_kv_cache: k [B,T_cap,H,K] (bfloat16/float32) and the
+    log2 prefix P [B,T_cap,HQ,K] -> k_tilde [B,T_cap,HQ,K] (decay folded in against
+    per-chunk anchors) and r_cache [B,ceil(T_cap/chunk_size),HQ,K] float32.
+    Rows t0 .. t1-1 are written (default all); pass the cache tensors to append."""
+    dev = _on_gpu(k, P, k_tilde, r_cache)
+    k, P = _dense(k), _dense(P)
+    B, T, H, K = k.shape
+    HQ = P.shape[2]
+    if P.shape != (B, T, HQ, K) or P.dtype != torch.float32:
+        raise ValueError("P must be float32 [B,T,HQ,K] matching k [B,T,H,K]")
+    NC = -(-T // int(chunk_size))
+    if k_tilde is None:
+        k_tilde = torch.empty((B, T, HQ, K), dtype=k.dtype, device=dev)
+    if r_cache is None:
+        r_cache = torch.empty((B, NC, HQ, K), dtype=torch.float32, device=dev)
+    if k_tilde.shape != (B, T, HQ, K) or r_cache.shape != (B, NC, HQ, K):
+        raise ValueError("k_tilde must be [B,T,HQ,K] and r_cache [B,ceil(T/C),HQ,K]")
+    if not (k_tilde.is_contiguous() and r_cache.is_contiguous()):
+        raise ValueError("k_tilde and r_cache must be contiguous")
+    t1 = T if t1 is None else int(t1)
+    _check(lib().wall_kv_cache_build(_ptr(k), _dtype(k), _ptr(P), _ptr(k_tilde), _ptr(r_cache), B, T,
+                                      HQ, H, K, int(chunk_size), int(t0), t1, _stream(dev)),
+           "wall_kv_cache_build")
+    return k_tilde, r_cache
+
+
+def decode_workspace_size(B: int, T: int, HQ: int, V: int) -> int:
+    return int(lib().wall_attn_decode_workspace_size(B, T, HQ, V))
+
+
+def wall_attn_decode(q: torch.Tensor, v: torch.Tensor, p_curr: torch.Tensor, k_tilde: torch.Tensor,
+                     r_cache: torch.Tensor, sink_bias: Optional[torch.Tensor] = None,
+                     scale: Optional[float] = None, cache_chunk_size: int = 64,
+                     seq_len: Optional[int] = None, out: Optional[torch.Tensor] = None,
+                     lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None
+                     ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """The README's wall_attn_decode: q and p_curr [B,1,HQ,K] (the newest token and
+    its log2 prefix), v [B,T_cap,H,V], the cache of build_wall_kv_cache; attends to
+    cached rows 0 .. seq_len-1 (default T_cap).  Returns (o [B,1,HQ,V], lse [B,1,HQ])."""
+    dev = _on_gpu(q, v, p_curr, k_tilde, r_cache, sink_bias, out, lse, workspace)
+    q, v, p_curr = _dense(q), _dense(v), _dense(p_curr)
+    B, _, HQ, K = q.shape
+    T_cap, H, V = v.shape[1], v.shape[2], v.shape[3]
+    T = T_cap if seq_len is None else int(seq_len)
+    if q.shape[1] != 1 or p_curr.shape != (B, 1, HQ, K) or p_curr.dtype != torch.float32:
+        raise ValueError("q and p_curr must be [B,1,HQ,K] (p_curr float32)")
+    if k_tilde.shape != (B, T_cap, HQ, K) or not k_tilde.is_contiguous() or not r_cache.is_contiguous():
+        raise ValueError("k_tilde must be a contiguous [B,T_cap,HQ,K] cache")
+    if not (q.dtype == v.dtype == k_tilde.dtype) or r_cache.dtype != torch.float32:
+        raise TypeError("q, v and k_tilde share one dtype; r_cache is float32")
+    if sink_bias is not None:
+        sink_bias = _dense(sink_bias.to(torch.float32))
+    if scale is None:
+        scale = K ** -0.5
+    if out is None:
+        out = torch.empty((B, 1, HQ, V), dtype=q.dtype, device=dev)
+    if lse is None:
+        lse = torch.empty((B, 1, HQ), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(decode_workspace_size(B, T, HQ, V), dtype=torch.uint8, device=dev)
+    _check(lib().wall_attn_decode(
+        _ptr(q), _ptr(v), _dtype(q), _ptr(p_curr), _ptr(k_tilde), _ptr(r_cache), _ptr(sink_bias),
+        _ptr(out), _ptr(lse), B, T, T_cap, HQ, H, K, V, int(cache_chunk_size), float(scale),
+        _ptr(workspace), workspace.numel(), _stream(dev)), "wall_attn_decode")
+    return out, lse

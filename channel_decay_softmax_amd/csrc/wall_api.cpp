@@ -1,4 +1,4 @@
-// wall_api.cpp -- the extern "C" boundary of the Wall Attention forward library.
+// wall_api.cpp -- the extern "C" boundary of the Wall Attention library (forward and decode).
 //
 // Every argument check below runs before the first HIP call, so invalid
 // calls return their status without touching the device (and can be tested
@@ -186,6 +186,72 @@ wall_status_t wall_attn_fwd(const void *q, const void *k, const void *v, wall_dt
     const wall_status_t sp = enqueue_prepare(k, v, dtype, P, s, cu_seqlens, workspace, stream);
     if (sp != WALL_OK) return sp;
     return enqueue_run(q, dtype, P, G, sink_bias, o, lse, s, scale, window_size, workspace, stream);
+}
+
+wall_status_t wall_kv_cache_build(const void *k, wall_dtype_t dtype, const float *P, void *k_tilde,
+                                  float *r_cache, int64_t B, int64_t T_cap, int64_t HQ, int64_t H,
+                                  int64_t K, int64_t chunk_size, int64_t t0, int64_t t1,
+                                  hipStream_t stream) {
+    if (!k || !P || !k_tilde || !r_cache) return WALL_ERR_INVALID_ARG;
+    if (B < 1 || T_cap < 1 || HQ < 1 || H < 1 || K < 1 || chunk_size < 1) return WALL_ERR_INVALID_ARG;
+    if (HQ % H != 0) return WALL_ERR_INVALID_ARG;
+    if (t0 < 0 || t1 <= t0 || t1 > T_cap) return WALL_ERR_INVALID_ARG;
+    if (B * T_cap > INT32_MAX / 2 || B * T_cap * HQ * K > ((int64_t)1 << 40)) return WALL_ERR_INVALID_ARG;
+    if (dtype != WALL_BF16 && dtype != WALL_F32) return WALL_ERR_UNSUPPORTED;
+    if ((K != 64 && K != 128) || chunk_size % 64 != 0) return WALL_ERR_UNSUPPORTED;
+    const void *ptrs[] = {k, P, k_tilde, r_cache};
+    for (const void *p : ptrs)
+        if (!aligned(p, 16)) return WALL_ERR_INVALID_ARG;
+    const CacheArgs a{k, P, k_tilde, r_cache, B, T_cap, HQ, H, K, chunk_size, t0, t1};
+    return launched(launch_kv_cache(a, dtype == WALL_BF16, stream));
+}
+
+size_t wall_attn_decode_workspace_size(int64_t B, int64_t T, int64_t HQ, int64_t V) {
+    if (B < 1 || T < 1 || HQ < 1 || V < 1) return 0;
+    return decode_layout(B, T, HQ, V).total;
+}
+
+wall_status_t wall_attn_decode(const void *q, const void *v, wall_dtype_t dtype, const float *p_curr,
+                               const void *k_tilde, const float *r_cache, const float *sink_bias,
+                               void *o, float *lse, int64_t B, int64_t T, int64_t T_cap, int64_t HQ,
+                               int64_t H, int64_t K, int64_t V, int64_t chunk_size, float scale,
+                               void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!q || !v || !p_curr || !k_tilde || !r_cache || !o || !workspace) return WALL_ERR_INVALID_ARG;
+    if (B < 1 || T < 1 || T_cap < 1 || HQ < 1 || H < 1 || K < 1 || V < 1 || chunk_size < 1)
+        return WALL_ERR_INVALID_ARG;
+    if (HQ % H != 0 || T > T_cap || B * HQ > 65535) return WALL_ERR_INVALID_ARG;
+    if (B * T_cap > INT32_MAX / 2 || B * T_cap * HQ * (K > V ? K : V) > ((int64_t)1 << 40))
+        return WALL_ERR_INVALID_ARG;
+    if (dtype != WALL_BF16 && dtype != WALL_F32) return WALL_ERR_UNSUPPORTED;
+    if ((K != 64 && K != 128) || (V != 64 && V != 128) || chunk_size % 64 != 0) return WALL_ERR_UNSUPPORTED;
+    const void *ptrs[] = {q, v, p_curr, k_tilde, r_cache, sink_bias, o, lse};
+    for (const void *p : ptrs)
+        if (p && !aligned(p, 16)) return WALL_ERR_INVALID_ARG;
+    if (!aligned(workspace, 256)) return WALL_ERR_INVALID_ARG;
+    const DecodeLayout L = decode_layout(B, T, HQ, V);
+    if (workspace_bytes < L.total) return WALL_ERR_INVALID_ARG;
+    DecodeArgs a{};
+    a.q = q;
+    a.v = v;
+    a.pc = p_curr;
+    a.kt = k_tilde;
+    a.r = r_cache;
+    a.sink = sink_bias;
+    a.o = o;
+    a.lse = lse;
+    a.part = static_cast<float *>(workspace);
+    a.B = (int32_t)B;
+    a.T = (int32_t)T;
+    a.Tcap = (int32_t)T_cap;
+    a.HQ = (int32_t)HQ;
+    a.H = (int32_t)H;
+    a.K = (int32_t)K;
+    a.V = (int32_t)V;
+    a.C = (int32_t)chunk_size;
+    a.nsplit = (int32_t)L.nsplit;
+    a.S = (int32_t)L.S;
+    a.qscale = scale * LOG2E;
+    return launched(launch_decode(a, dtype == WALL_BF16, stream));
 }
 
 }  // extern "C"

@@ -154,4 +154,47 @@ struct FwdArgs {
 hipError_t launch_fwd_bf16(const FwdArgs &a, hipStream_t st);
 hipError_t launch_fwd_f32(const FwdArgs &a, hipStream_t st);
 
+// ----------------------------------------------------------------- decode
+struct CacheArgs {
+    const void *k;      // [B, Tcap, H, K]
+    const float *P;     // [B, Tcap, HQ, K]
+    void *kt;           // [B, Tcap, HQ, K]
+    float *r;           // [B, ceil(Tcap / C), HQ, K]
+    int64_t B, Tcap, HQ, H, K, C, t0, t1;  // rows t0 .. t1-1 are written
+};
+hipError_t launch_kv_cache(const CacheArgs &a, bool bf16, hipStream_t st);
+
+struct DecodeArgs {
+    const void *q;      // [B, HQ, K]
+    const void *v;      // [B, Tcap, H, V]
+    const float *pc;    // [B, HQ, K]
+    const void *kt;     // [B, Tcap, HQ, K]
+    const float *r;     // [B, ceil(Tcap / C), HQ, K]
+    const float *sink;  // [HQ] or null
+    void *o;            // [B, HQ, V]
+    float *lse;         // [B, HQ] or null
+    float *part;        // [nsplit][B * HQ][V + 2]: o not normalised, m, l (log2 units)
+    int32_t B, T, Tcap, HQ, H, K, V, C, nsplit, S;
+    float qscale;       // scale * log2(e)
+};
+hipError_t launch_decode(const DecodeArgs &a, bool bf16, hipStream_t st);
+
+// Decode splits: about 2048 one-wave blocks when the keys allow, S keys each
+// (a multiple of 64), every split non-empty.
+struct DecodeLayout {
+    int64_t nsplit, S;
+    size_t total;
+};
+inline DecodeLayout decode_layout(int64_t B, int64_t T, int64_t HQ, int64_t V) {
+    const int64_t rounds = cdiv(T, 64);
+    int64_t want = cdiv(2048, B * HQ);
+    if (want > rounds) want = rounds;
+    if (want < 1) want = 1;
+    DecodeLayout L;
+    L.S = 64 * cdiv(rounds, want);
+    L.nsplit = cdiv(T, L.S);
+    L.total = align_up(sizeof(float) * (size_t)(L.nsplit * B * HQ * (V + 2)), 256);
+    return L;
+}
+
 }  // namespace wall

@@ -186,6 +186,82 @@ wall_status_t wall_attn_fwd_run(const void *q, wall_dtype_t dtype,
                                 const void *workspace, size_t workspace_bytes,
                                 hipStream_t stream);
 
+/* ------------------------------------------------------------------ decode cache
+ *
+ * The README's build_wall_kv_cache (section "Decode (cached generation)"):
+ * the decay folded into the keys against per-chunk anchors, so that a
+ * decode step never re-accumulates the prefix.  For chunk c of chunk_size
+ * rows, query head hq and channel n:
+ *
+ *   r_cache[b, c, hq, n]  = floor(P[b, c*chunk_size, hq, n])   (the chunk's first row)
+ *   k_tilde[b, j, hq, n]  = k[b, j, hq / (HQ/H), n] * exp2(r_cache[b, j/chunk_size, hq, n] - P[b, j, hq, n])
+ *
+ * (the README names a per-chunk anchor without fixing its row; the first
+ * row is the one known when a chunk opens, so appending never moves an
+ * anchor).  Only rows t0 .. t1-1 of every sequence are written: a call with
+ * t0 = 0, t1 = T builds the cache of a prefill, a call with t1 = t0 + 1
+ * appends one token.  A chunk whose first row lies in [t0, t1) gets its
+ * anchor from P and stores it; a chunk opened by an earlier call (on the same
+ * stream, or otherwise completed) reads the stored anchor.  The exponent is
+ * clamped to [-160, 126].
+ *
+ *   k           [B, T_cap, H, K]  dtype; rows t0 .. t1-1 are read
+ *   P           [B, T_cap, HQ, K] float32 log2 prefix (wall_prefix_scan of g
+ *               with scale 1/ln 2); rows t0 .. t1-1 and the first rows of the
+ *               chunks they open are read
+ *   k_tilde     [B, T_cap, HQ, K] dtype (rows t0 .. t1-1 written)
+ *   r_cache     [B, ceil(T_cap / chunk_size), HQ, K] float32 (anchors of the
+ *               chunks opened in [t0, t1) written, earlier ones read)
+ *   T_cap       rows allocated per sequence in k, P, k_tilde (and v below)
+ * All pointers are caller-owned device memory, 16-byte aligned.
+ * Errors: INVALID_ARG for a null pointer, a size < 1, HQ % H != 0, not
+ * 0 <= t0 < t1 <= T_cap, misalignment, sizes past 2^40 elements;
+ * UNSUPPORTED for K not in {64, 128}, chunk_size not a positive multiple of
+ * 64, or another dtype; LAUNCH on a failed launch. */
+wall_status_t wall_kv_cache_build(const void *k, wall_dtype_t dtype, const float *P,
+                                  void *k_tilde, float *r_cache,
+                                  int64_t B, int64_t T_cap, int64_t HQ, int64_t H, int64_t K,
+                                  int64_t chunk_size, int64_t t0, int64_t t1,
+                                  hipStream_t stream);
+
+/* ------------------------------------------------------------------ decode
+ *
+ * The README's wall_attn_decode: one query per (b, hq) -- the newest token,
+ * whose log2 prefix is p_curr -- against the cached keys j = 0 .. T-1 of
+ * its sequence (the newest token included, so every key is visible):
+ *
+ *   logit_j (log2 units) = scale*log2(e) * sum_n q_n * exp2(p_curr_n - r_cache[j/C, n]) * k_tilde[j, n]
+ *   o  = sum_j 2^(logit_j - M) v_j / Z,  lse = ln 2 * (M + log2 Z)
+ *
+ * with the sink as in wall_attn_fwd.  This is the forward's last row: the
+ * anchors cancel (blog, "Definition: Wall Attention", factored form).
+ *
+ *   q           [B, HQ, K] dtype (the README's [B, 1, HQ, K])
+ *   v           [B, T_cap, H, V] dtype, rows 0 .. T-1 read
+ *   p_curr      [B, HQ, K] float32, P at the query's row
+ *   k_tilde, r_cache   a cache built by wall_kv_cache_build with this
+ *               chunk_size and T_cap, rows 0 .. T-1 complete
+ *   sink_bias   NULL or [HQ] float32
+ *   o           [B, HQ, V] dtype (written); lse NULL or [B, HQ] float32 (written)
+ *   workspace   device scratch of at least
+ *               wall_attn_decode_workspace_size(B, T, HQ, V) bytes, 256-byte
+ *               aligned, contents on entry ignored (split-KV partials)
+ * Numerics: q~ = q * scale*log2(e) * exp2(p_curr - R) is rounded to the cache
+ * dtype once per chunk; dot products and the softmax are float32.
+ * Errors: INVALID_ARG for a null required pointer, a size < 1, HQ % H != 0,
+ * T > T_cap, B*HQ > 65535, misalignment, a short workspace; UNSUPPORTED for K
+ * or V not in {64, 128}, chunk_size not a positive multiple of 64, or another
+ * dtype; LAUNCH on a failed launch. */
+size_t wall_attn_decode_workspace_size(int64_t B, int64_t T, int64_t HQ, int64_t V);
+
+wall_status_t wall_attn_decode(const void *q, const void *v, wall_dtype_t dtype,
+                               const float *p_curr, const void *k_tilde, const float *r_cache,
+                               const float *sink_bias, void *o, float *lse,
+                               int64_t B, int64_t T, int64_t T_cap, int64_t HQ, int64_t H,
+                               int64_t K, int64_t V, int64_t chunk_size, float scale,
+                               void *workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -95,6 +95,50 @@ def test_fwd_rejects_unsupported_shapes(kw):
     assert fwd(**kw) == UNSUPPORTED
 
 
+def cache(k=FAKE, dtype=B.WALL_BF16, Pp=FAKE, kt=FAKE, r=FAKE, b=2, tcap=300, hq=4, h=2, kk=128, c=64,
+          t0=0, t1=300):
+    return wall.lib().wall_kv_cache_build(P(k), dtype, P(Pp), P(kt), P(r), b, tcap, hq, h, kk, c, t0, t1,
+                                          None)
+
+
+def decode(q=FAKE, v=FAKE, dtype=B.WALL_BF16, pc=FAKE, kt=FAKE, r=FAKE, sink=None, o=FAKE, lse=None,
+           b=2, t=300, tcap=512, hq=4, h=2, kk=128, vv=128, c=64, ws=FAKE, wsb=None):
+    L = wall.lib()
+    if wsb is None:
+        wsb = L.wall_attn_decode_workspace_size(b, t, hq, vv)
+    return L.wall_attn_decode(P(q), P(v), dtype, P(pc), P(kt), P(r), P(sink), P(o), P(lse), b, t, tcap,
+                              hq, h, kk, vv, c, 0.088, P(ws), wsb, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(k=None), dict(Pp=None), dict(kt=None), dict(r=None), dict(b=0), dict(tcap=0), dict(hq=0),
+    dict(h=0), dict(hq=6, h=4), dict(c=0), dict(t0=-1), dict(t0=300), dict(t0=10, t1=10),
+    dict(t1=301), dict(k=FAKE + 2), dict(Pp=FAKE + 4), dict(kt=FAKE + 8), dict(r=FAKE + 12),
+])
+def test_kv_cache_rejects_invalid_arguments(kw):
+    assert cache(**kw) == INVALID
+
+
+@pytest.mark.parametrize("kw", [dict(kk=96), dict(c=32), dict(c=100), dict(dtype=5)])
+def test_kv_cache_rejects_unsupported_shapes(kw):
+    assert cache(**kw) == UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw", [
+    dict(q=None), dict(v=None), dict(pc=None), dict(kt=None), dict(r=None), dict(o=None), dict(ws=None),
+    dict(b=0), dict(t=0), dict(tcap=0), dict(hq=0), dict(h=0), dict(hq=6, h=4), dict(t=513),
+    dict(b=8192, hq=16, h=4), dict(q=FAKE + 2), dict(sink=FAKE + 4), dict(lse=FAKE + 8),
+    dict(ws=FAKE + 16), dict(wsb=64),
+])
+def test_decode_rejects_invalid_arguments(kw):
+    assert decode(**kw) == INVALID
+
+
+@pytest.mark.parametrize("kw", [dict(kk=96), dict(vv=32), dict(c=32), dict(c=0 + 96), dict(dtype=5)])
+def test_decode_rejects_unsupported_shapes(kw):
+    assert decode(**kw) == UNSUPPORTED
+
+
 def test_workspace_sizes():
     L = wall.lib()
     assert L.wall_prefix_scan_workspace_size(0, 10, 10) == 0

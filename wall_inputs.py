@@ -32,7 +32,8 @@ from typing import Optional
 import numpy as np
 import torch
 
-__all__ = ["WORKLOADS", "Workload", "WallInputs", "make_inputs", "workload"]
+__all__ = ["WORKLOADS", "DECODE_WORKLOADS", "Workload", "WallInputs", "DecodeInputs", "make_inputs",
+           "make_decode_inputs", "workload"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -67,9 +68,21 @@ WORKLOADS = {
 }
 
 
+# Decode: one new token per sequence against a cache of T rows (the newest
+# token's row included), the README's decode example at the long-context
+# shapes with a batch of 16 sequences.
+DECODE_WORKLOADS = {
+    w.name: w
+    for w in [
+        Workload("decode_bf16", 6, 16, 8192, 16, 4, 128, 128, "bfloat16", "bimodal"),
+    ]
+}
+
+
 def workload(name: str, **overrides) -> Workload:
     """The named workload, optionally with some fields replaced (e.g. a shorter T)."""
-    return dataclasses.replace(WORKLOADS[name], **overrides)
+    table = DECODE_WORKLOADS if name in DECODE_WORKLOADS else WORKLOADS
+    return dataclasses.replace(table[name], **overrides)
 
 
 @dataclasses.dataclass
@@ -151,3 +164,56 @@ def make_inputs(spec: Workload | str, **overrides) -> WallInputs:
         g_scalar=None if gs is None else cast(gs),
         sink_bias=sink, cu_seqlens=cu, window_size=spec.window,
         scale=float(K) ** -0.5, spec=spec)
+
+
+@dataclasses.dataclass
+class DecodeInputs:
+    q: torch.Tensor  # [B, 1, HQ, K] the newest token of each sequence
+    k: torch.Tensor  # [B, T, H, K]
+    v: torch.Tensor  # [B, T, H, V]
+    g: torch.Tensor  # [B, T, HQ, K] natural-log gate
+    sink_bias: Optional[torch.Tensor]  # [HQ] float32
+    scale: float
+    chunk_size: int
+    spec: Workload
+
+    def to(self, device) -> "DecodeInputs":
+        mv = lambda t: None if t is None else t.to(device)
+        return dataclasses.replace(self, q=mv(self.q), k=mv(self.k), v=mv(self.v), g=mv(self.g),
+                                   sink_bias=mv(self.sink_bias))
+
+
+def make_decode_inputs(spec: Workload | str, chunk_size: int = 64, **overrides) -> DecodeInputs:
+    """Draw the inputs of one decode workload on the CPU: the same recipe as
+    make_inputs, drawn one sequence at a time (q of the newest token, then k,
+    v, x_g of all T rows) so that host memory stays bounded, then the sink."""
+    if isinstance(spec, str):
+        spec = workload(spec, **overrides)
+    elif overrides:
+        spec = dataclasses.replace(spec, **overrides)
+    rng = np.random.default_rng(spec.seed)
+    B, T, HQ, H, K, V = spec.B, spec.T, spec.HQ, spec.H, spec.K, spec.V
+    dt = {"float32": torch.float32, "bfloat16": torch.bfloat16}[spec.dtype]
+    cast = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dt)
+    q = torch.empty((B, 1, HQ, K), dtype=dt)
+    k = torch.empty((B, T, H, K), dtype=dt)
+    v = torch.empty((B, T, H, V), dtype=dt)
+    g = torch.empty((B, T, HQ, K), dtype=dt)
+    for b in range(B):
+        q[b] = cast(rng.standard_normal(size=(1, HQ, K)))
+        k[b] = cast(rng.standard_normal(size=(T, H, K)))
+        v[b] = cast(rng.standard_normal(size=(T, H, V)))
+        x_g = rng.standard_normal(size=(T, HQ, K))
+        if spec.gate == "small":
+            gb = 0.02 * x_g
+        elif spec.gate == "bimodal":
+            x_g[..., : K // 2] += 4.0
+            gb = _logsigmoid(x_g)
+        elif spec.gate == "logsig4":
+            gb = _logsigmoid(x_g + 4.0)
+        else:
+            raise ValueError(spec.gate)
+        g[b] = cast(gb)
+    sink = torch.from_numpy(rng.standard_normal(size=(HQ,))).to(torch.float32) if spec.sink else None
+    return DecodeInputs(q=q, k=k, v=v, g=g, sink_bias=sink, scale=float(K) ** -0.5,
+                        chunk_size=int(chunk_size), spec=spec)
