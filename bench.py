@@ -40,6 +40,10 @@ PEAK_HBM_GBS = 8000.0
 FWD_KERNEL_SOURCES = ["channel_decay_softmax_amd/csrc/wall_fwd_bf16.hip",
                       "channel_decay_softmax_amd/csrc/wall_common.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_bf16_long_bf16_traffic.json")
+DECODE_METRIC = "wall_attn_decode step HBM GB/s (append one token + split-KV decode), B=16 T=8192 HQ=16 K=128"
+DECODE_KERNEL_SOURCES = ["channel_decay_softmax_amd/csrc/wall_decode.hip",
+                         "channel_decay_softmax_amd/csrc/wall_common.h"]
+DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_decode_bf16_traffic.json")
 
 
 def visible_pairs(lens, W):
@@ -69,14 +73,14 @@ def source_hash(paths):
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload):
-    """Per-launch HBM bytes of the fused kernel, measured with rocprofv3 counters
+def load_traffic(workload, path=TRAFFIC_FILE, sources=FWD_KERNEL_SOURCES):
+    """Per-launch HBM bytes of the timed kernel, measured with rocprofv3 counters
     (see profiles/), or None when absent or taken on an older kernel source."""
-    if not os.path.exists(TRAFFIC_FILE):
+    if not os.path.exists(path):
         return None
-    with open(TRAFFIC_FILE) as f:
+    with open(path) as f:
         rec = json.load(f)
-    if rec.get("workload") != workload or rec.get("source_hash") != source_hash(FWD_KERNEL_SOURCES):
+    if rec.get("workload") != workload or rec.get("source_hash") != source_hash(sources):
         return None
     return rec.get("bytes_per_launch")
 
@@ -137,14 +141,145 @@ def cpu_baseline(inp, flop_per_pair, target_s):
     }
 
 
+def decode_bytes(B, T, HQ, H, K, V, C, es):
+    """Algorithmic HBM bytes of one decode call and of one one-row cache append."""
+    nc = -(-T // C)
+    dec = (B * T * HQ * K * es + B * T * H * V * es + B * nc * HQ * K * 4   # k_tilde, v, anchors
+           + B * HQ * K * es + B * HQ * K * 4 + B * HQ * V * es + B * HQ * 4)  # q, p_curr, o, lse
+    opens = (T - 1) % C == 0
+    app = B * H * K * es + B * HQ * K * 4 + B * HQ * K * es + B * HQ * K * 4  # k, P, k_tilde row; anchor
+    return dec, app, opens
+
+
+def decode_cpu_baseline(inp, nseq, es):
+    """Time the fp64 decode oracle (as it stands) on the first nseq sequences;
+    the oracle's cache is built beforehand, outside the timing."""
+    import numpy as np
+
+    import oracle
+
+    oracle.build(force=False)
+    B, T, HQ, K = inp.q.shape[0], inp.k.shape[1], inp.q.shape[2], inp.q.shape[3]
+    H, V, C = inp.k.shape[2], inp.v.shape[3], inp.chunk_size
+    sel = slice(0, nseq)
+    g = inp.g[sel].double().numpy()
+    P = oracle.prefix_scan_oracle(g)
+    kt, r = oracle.kv_cache_oracle(inp.k[sel], P, C)
+    q, v = inp.q[sel].double().numpy(), inp.v[sel].double().numpy()
+    pc = np.ascontiguousarray(P[:, T - 1:T])
+    t0 = time.perf_counter()
+    oracle.decode_oracle(q, v, pc, kt, r, C, sink_bias=inp.sink_bias, scale=inp.scale)
+    t = time.perf_counter() - t0
+    dec, _, _ = decode_bytes(nseq, T, HQ, H, K, V, C, es)
+    return {
+        "value": dec / t / 1e9,
+        "unit": "GB/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"{nseq} of {B} sequences (all {HQ} heads, {T} cached rows), {t:.2f} s fp64 cached decode",
+        "seconds": t,
+    }
+
+
+def bench_decode(args):
+    """One decode step of a serving loop: append the newest token's row to the
+    anchored key cache, then the split-KV decode of every sequence's newest query."""
+    import torch
+
+    import channel_decay_softmax_amd as wall
+    from wall_inputs import make_decode_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda", 0)
+    inp = make_decode_inputs(args.workload)
+    d = inp.to(dev)
+    B, _, HQ, K = d.q.shape
+    T, H, V, C = d.k.shape[1], d.k.shape[2], d.v.shape[3], inp.chunk_size
+    es = 2 if d.q.dtype == torch.bfloat16 else 4
+    # the prefill state: the log2 prefix and the cache of the first T-1 rows
+    P = wall.wall_prefix_scan(d.g)
+    kt = torch.empty((B, T, HQ, K), dtype=d.q.dtype, device=dev)
+    r = torch.empty((B, -(-T // C), HQ, K), dtype=torch.float32, device=dev)
+    wall.build_wall_kv_cache(d.k, P, C, k_tilde=kt, r_cache=r, t0=0, t1=T - 1)
+    pc = P[:, T - 1:T].contiguous()
+    o = torch.empty((B, 1, HQ, V), dtype=d.q.dtype, device=dev)
+    lse = torch.empty((B, 1, HQ), dtype=torch.float32, device=dev)
+    ws = torch.empty(wall.decode_workspace_size(B, T, HQ, V), dtype=torch.uint8, device=dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+
+    def step(marks=None):
+        if marks:
+            marks[0].record()
+        wall.build_wall_kv_cache(d.k, P, C, k_tilde=kt, r_cache=r, t0=T - 1, t1=T)
+        if marks:
+            marks[1].record()
+        wall.wall_attn_decode(d.q, d.v, pc, kt, r, sink_bias=d.sink_bias, scale=inp.scale,
+                              cache_chunk_size=C, out=o, lse=lse, workspace=ws)
+        if marks:
+            marks[2].record()
+
+    dec, app, _ = decode_bytes(B, T, HQ, H, K, V, C, es)
+    print(f"[bench] {args.workload}: B={B} T={T} HQ={HQ} H={H} K={K} V={V} C={C} {d.q.dtype} "
+          f"decode bytes={dec} append bytes={app}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    for i in range(args.steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    app_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    dec_ms = [e[1].elapsed_time(e[2]) for e in ev]
+    dec_avg = statistics.fmean(dec_ms)
+    achieved = dec / (dec_avg * 1e-3) / 1e9
+    value = (dec + app) / (ms_step * 1e-3) / 1e9
+    print(f"[bench] step {ms_step * 1e3:.1f} us: append {statistics.fmean(app_ms) * 1e3:.1f} us, "
+          f"decode {dec_avg * 1e3:.1f} us -> decode {achieved:.0f} GB/s", file=sys.stderr, flush=True)
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the fp64 decode oracle on the host", file=sys.stderr, flush=True)
+        cpu = decode_cpu_baseline(inp, B, es)
+    rec = {
+        "metric": DECODE_METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {torch.bfloat16: "bf16", torch.float32: "f32"}[d.q.dtype],
+        "data": "synthetic",
+        "config": {"workload": args.workload, "B": B, "T": T, "HQ": HQ, "H": H, "K": K, "V": V,
+                   "chunk_size": C, "sink": inp.sink_bias is not None, "decode_bytes": dec,
+                   "append_bytes": app},
+        "tokens_per_s": round(B / (ms_step * 1e-3), 1),
+        "stages_us": {"append": round(statistics.fmean(app_ms) * 1e3, 2), "decode": round(dec_avg * 1e3, 2)},
+        "roofline": {"kernel": "decode_split + decode_merge", "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": load_traffic(args.workload, DECODE_TRAFFIC_FILE, DECODE_KERNEL_SOURCES)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=int(os.environ.get("WORLD_SIZE", "1")))
     # the part's clocks settle after about 40 ms of back-to-back steps (the
     # first steps after idle run up to 20% slower): the defaults warm up for
     # about 60 ms and time about 60 ms of steady state
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=200)
+    # (the decode step is about a third as long: it defaults to 600 and 600)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="long_bf16")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -158,6 +293,14 @@ def main():
               "is built and measured for a single GPU; see DESIGN.md for how it would shard.",
               file=sys.stderr)
         sys.exit(2)
+    from wall_inputs import DECODE_WORKLOADS
+    decode = args.workload in DECODE_WORKLOADS
+    if args.steps is None:
+        args.steps = 600 if decode else 200
+    if args.warmup is None:
+        args.warmup = 600 if decode else 200
+    if decode:
+        return bench_decode(args)
 
     import torch
 

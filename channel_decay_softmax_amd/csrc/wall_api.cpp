@@ -250,6 +250,13 @@ wall_status_t wall_attn_decode(const void *q, const void *v, wall_dtype_t dtype,
     a.C = (int32_t)chunk_size;
     a.nsplit = (int32_t)L.nsplit;
     a.S = (int32_t)L.S;
+    // the query heads of one kv head share a block (the largest divisor of HQ/H up to 4)
+    a.nwg = 1;
+    for (int32_t d = 4; d >= 1; --d)
+        if ((HQ / H) % d == 0) {
+            a.nwg = d;
+            break;
+        }
     a.qscale = scale * LOG2E;
     return launched(launch_decode(a, dtype == WALL_BF16, stream));
 }

@@ -175,6 +175,7 @@ struct DecodeArgs {
     float *lse;         // [B, HQ] or null
     float *part;        // [nsplit][B * HQ][V + 2]: o not normalised, m, l (log2 units)
     int32_t B, T, Tcap, HQ, H, K, V, C, nsplit, S;
+    int32_t nwg;        // waves (query heads of one kv head) per block, divides HQ / H, <= 4
     float qscale;       // scale * log2(e)
 };
 hipError_t launch_decode(const DecodeArgs &a, bool bf16, hipStream_t st);

@@ -11,20 +11,25 @@
 // Attention") with the anchor cancelling; the inner loop carries no gate
 // arithmetic beyond one exp2 per channel per chunk.
 //
-// The decode is split over the keys (split-KV): each block takes one (b, hq)
-// and S keys, one wave, 64 keys per round:
-//   - q~ of the round's chunk (K exps, once per chunk) goes to LDS in the
-//     cache's element type;
-//   - lane j takes key j of the round: its k_tilde row (K elements, 16-byte
-//     loads) against q~ read from LDS by broadcast, bf16 pairs through the
-//     packed dot product, in log2 units;
-//   - the online softmax over the round (wave max / sum);
-//   - p goes to LDS and the value rows are read row-contiguously (lane =
-//     8 channels x one of 64/(V/8) key slots), accumulated in fp32.
+// The decode is split over the keys (split-KV): each block takes S keys of
+// up to four query heads of one kv head, one wave per head, 32 keys per round:
+//   - q~ of the round's chunk (one exp2 per channel), each lane keeping the 8
+//     channels it multiplies, in the cache's element type;
+//   - a group of K/8 lanes reads one k_tilde row (whole rows per load), bf16
+//     pairs through the packed dot product, summed over the group;
+//   - the online softmax over the round, in log2 units;
+//   - a group of V/8 lanes reads one value row and accumulates p * v in fp32.
+//     The waves of a block read the same value rows (one kv head), so all but
+//     the first read of each row hit the CU's L1.
+// Small rounds keep each wave near 128 registers, so four waves share a SIMD:
+// occupancy, rather than loads issued further ahead, is what covers the
+// latency of HBM here.
 // A second kernel merges the splits with the sink.  The kernels are bound
 // by HBM: each step reads the cached keys of every query head, the values of
 // every kv head and the anchors once.
 #include "wall_common.h"
+
+#include <type_traits>
 
 namespace wall {
 namespace {
@@ -46,17 +51,6 @@ struct Vec8<float> {
     static __device__ inline f32x8 load(const float *p) { return *reinterpret_cast<const f32x8 *>(p); }
     static __device__ inline void store(float *p, f32x8 v) { *reinterpret_cast<f32x8 *>(p) = v; }
 };
-
-__device__ inline float wave_max(float x) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
-    return x;
-}
-__device__ inline float wave_sum(float x) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
-    return x;
-}
 
 // ---------------------------------------------------------------- cache
 // Thread = 8 channels of one (b, row j, hq), rows t0 .. t1-1.  A chunk that
@@ -96,92 +90,146 @@ __global__ __launch_bounds__(256) void kv_cache_kernel(CacheArgs a) {
 }
 
 // ---------------------------------------------------------------- decode
-// Dot product of 8 channels of a cached key with 8 channels of q~.
-__device__ inline float dot8(const __bf16 *k, const __bf16 *q, float acc) {
+// Dot product of 8 channels of a cached key with the lane's 8 channels of q~.
+__device__ inline float dot8(const bf16x8 &kk, const bf16x8 &qq) {
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    const bf16x8 kk = *reinterpret_cast<const bf16x8 *>(k);
-    const bf16x8 qq = *reinterpret_cast<const bf16x8 *>(q);
+    float acc = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; e += 2)
         acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{kk[e], kk[e + 1]}, bf16x2{qq[e], qq[e + 1]}, acc, false);
     return acc;
 }
-__device__ inline float dot8(const float *k, const float *q, float acc) {
-    const f32x8 kk = *reinterpret_cast<const f32x8 *>(k);
-    const f32x8 qq = *reinterpret_cast<const f32x8 *>(q);
+__device__ inline float dot8(const f32x8 &kk, const f32x8 &qq) {
+    float acc = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc = fmaf(kk[e], qq[e], acc);
     return acc;
 }
+template <typename T>
+using Vec = typename std::conditional<std::is_same<T, __bf16>::value, bf16x8, f32x8>::type;
 
+// x summed over aligned groups of W lanes (W = 8 or 16), every lane of a
+// group receiving the group's sum: quad swaps, then half-row and row mirrors.
+template <int CTRL>
+__device__ inline float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+template <int W>
+__device__ inline float group_sum(float x) {
+    x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]
+    x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]
+    x += dpp<0x141>(x);  // row_half_mirror
+    if constexpr (W == 16) x += dpp<0x140>(x);  // row_mirror
+    return x;
+}
+
+// One round = RK keys.  QK: a group of K/8 lanes reads one key row (16 bytes
+// a lane, whole rows per load), each lane against its own 8 channels of q~
+// (registers), then the group's sum; 64/(K/8) keys per load.  PV: a group
+// of V/8 lanes reads one value row the same way and accumulates p * v for
+// its 8 channels; the groups are summed at the end.  With K == V the two
+// mappings coincide and p stays in registers, else it goes through LDS.
+// Wave w of the block is query head blockIdx.y * nwg + w (flattened with b).
 template <typename T, int K, int V>
-__global__ __launch_bounds__(64) void decode_split(DecodeArgs a) {
-    __shared__ __attribute__((aligned(32))) T qs[K];
-    __shared__ float ps[64];
-    constexpr int CG = V / 8, KSL = 64 / CG;  // value loads: 8 channels x KSL keys
-    const int lane = threadIdx.x;
-    const int split = blockIdx.x, bh = blockIdx.y;
+__global__ __launch_bounds__(256) void decode_split(DecodeArgs a) {
+    constexpr int RK = 32;  // keys per round
+    constexpr int GK = K / 8, NKQ = 64 / GK, NQ = RK / NKQ;  // QK: lanes per key, keys per load, loads
+    constexpr int GV = V / 8, NKV = 64 / GV, NVL = RK / NKV;  // PV: the same for values
+    __shared__ float ps[4][64];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int split = blockIdx.x, bh = blockIdx.y * a.nwg + w;
     const int64_t b = bh / a.HQ, hq = bh % a.HQ, h = hq / (a.HQ / a.H);
     const int s0 = split * a.S, s1 = min(a.T, s0 + a.S);
-    const int cg = lane % CG, kg = lane / CG;
+    const int gq = lane / GK, cq = lane % GK;
+    const int gv = lane / GV, cv = lane % GV;
     const int64_t NC = cdiv(a.Tcap, a.C);
-    const T *kt = static_cast<const T *>(a.kt) + (b * a.Tcap * a.HQ + hq) * K;
-    const T *vb = static_cast<const T *>(a.v) + (b * a.Tcap * a.H + h) * V + cg * 8;
-    const T *qg = static_cast<const T *>(a.q) + bh * K;
-    const float *pg = a.pc + bh * K;
+    const T *kt = static_cast<const T *>(a.kt) + (b * a.Tcap * a.HQ + hq) * K + cq * 8;
+    const T *vb = static_cast<const T *>(a.v) + (b * a.Tcap * a.H + h) * V + cv * 8;
+    const int64_t kstride = a.HQ * K, vstride = a.H * V;
 
     float m = -__builtin_inff(), l = 0.f;
     f32x8 o8 = {};
-    int64_t cprev = -1;
-    for (int j0 = s0; j0 < s1; j0 += 64) {
-        const int64_t c = j0 / a.C;  // C is a multiple of 64: one chunk per round
-        if (c != cprev) {
-            const float *R = a.r + ((b * NC + c) * a.HQ + hq) * K;
-            for (int n = lane; n < K; n += 64)
-                qs[n] = (T)((float)qg[n] * a.qscale * exp2f(fminf(fmaxf(pg[n] - R[n], EXP2_LO), EXP2_HI)));
-            cprev = c;
-            __syncthreads();
-        }
-        const int j = j0 + lane;
-        float s = -__builtin_inff();
-        if (j < s1) {
-            const T *kr = kt + (int64_t)j * a.HQ * K;
-            float acc0 = 0.f, acc1 = 0.f;
+    // q and its prefix, once; the anchors of each round's chunk one round ahead
+    const f32x8 qv = Vec8<T>::load(static_cast<const T *>(a.q) + bh * K + cq * 8);
+    const f32x8 pv = *reinterpret_cast<const f32x8 *>(a.pc + bh * K + cq * 8);
+    const float *rb = a.r + (b * NC * a.HQ + hq) * K + cq * 8;
+    const int64_t rstride = a.HQ * K;
+    f32x8 rv = *reinterpret_cast<const f32x8 *>(rb + (s0 / a.C) * rstride);
+    for (int j0 = s0; j0 < s1; j0 += RK) {
+        // the round's key and value rows, all in flight
+        Vec<T> kk[NQ];
 #pragma unroll
-            for (int n = 0; n < K; n += 16) {
-                acc0 = dot8(kr + n, qs + n, acc0);
-                acc1 = dot8(kr + n + 8, qs + n + 8, acc1);
-            }
-            s = acc0 + acc1;
+        for (int i = 0; i < NQ; ++i) {
+            const int j = j0 + NKQ * i + gq;
+            if (j < s1) kk[i] = *reinterpret_cast<const Vec<T> *>(kt + (int64_t)j * kstride);
+            else kk[i] = Vec<T>{};
         }
-        // online softmax over the round (log2 units); at least key j0 is visible
-        const float mn = fmaxf(m, wave_max(s));
+        Vec<T> vv[NVL];
+#pragma unroll
+        for (int i = 0; i < NVL; ++i) {
+            const int j = j0 + NKV * i + gv;
+            if (j < s1) vv[i] = *reinterpret_cast<const Vec<T> *>(vb + (int64_t)j * vstride);
+            else vv[i] = Vec<T>{};
+        }
+        // the lane's 8 channels of q~ = q * scale*log2e * exp2(p - R_c) for the
+        // round's chunk (C is a multiple of 64: one chunk per round), in the cache dtype
+        Vec<T> q8;
+        {
+            f32x8 qt;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                qt[e] = qv[e] * a.qscale * exp2f(fminf(fmaxf(pv[e] - rv[e], EXP2_LO), EXP2_HI));
+            if constexpr (std::is_same<T, __bf16>::value) q8 = __builtin_convertvector(qt, bf16x8);
+            else q8 = qt;
+        }
+        if (j0 + RK < s1) rv = *reinterpret_cast<const f32x8 *>(rb + ((j0 + RK) / a.C) * rstride);
+        float sc[NQ];
+        float mt = -__builtin_inff();
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) {
+            sc[i] = group_sum<GK>(dot8(kk[i], q8));
+            sc[i] = j0 + NKQ * i + gq < s1 ? sc[i] : -__builtin_inff();
+            mt = fmaxf(mt, sc[i]);
+        }
+        // the round's max over the NKQ groups (each lane of a group holds the same values)
+#pragma unroll
+        for (int off = GK; off < 64; off <<= 1) mt = fmaxf(mt, __shfl_xor(mt, off));
+        const float mn = fmaxf(m, mt);  // finite: key j0 is visible
         const float al = exp2f(m - mn);
-        const float p = j < s1 ? exp2f(s - mn) : 0.f;
-        l = l * al + wave_sum(p);
+        float ls = 0.f;
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) {
+            sc[i] = exp2f(sc[i] - mn);
+            ls += sc[i];
+        }
+#pragma unroll
+        for (int off = GK; off < 64; off <<= 1) ls += __shfl_xor(ls, off);
+        l = l * al + ls;
         o8 *= al;
         m = mn;
-        ps[lane] = p;
-        __syncthreads();
-#pragma unroll 4
-        for (int it = 0; it < 64 / KSL; ++it) {
-            const int jj = it * KSL + kg;
-            if (j0 + jj < s1) {
-                const f32x8 vv = Vec8<T>::load(vb + (int64_t)(j0 + jj) * a.H * V);
-                o8 += ps[jj] * vv;
-            }
+        if constexpr (GK != GV) {
+            if (cq < NQ) ps[w][NKQ * cq + gq] = sc[cq];  // lane (gq, cq) holds key NKQ*cq + gq once
+            __syncthreads();
         }
-        __syncthreads();  // q~ and p are rewritten next round
-    }
-    // the KSL key slots of each channel group
 #pragma unroll
-    for (int off = CG; off < 64; off <<= 1)
+        for (int i = 0; i < NVL; ++i) {
+            const float p = GK == GV ? sc[i] : ps[w][NKV * i + gv];
+            f32x8 x;
+            if constexpr (std::is_same<T, __bf16>::value) x = __builtin_convertvector(vv[i], f32x8);
+            else x = vv[i];
+            o8 += p * x;
+        }
+        if constexpr (GK != GV) __syncthreads();  // p is rewritten next round
+    }
+    // the NKV key groups of each channel block
+#pragma unroll
+    for (int off = GV; off < 64; off <<= 1)
 #pragma unroll
         for (int e = 0; e < 8; ++e) o8[e] += __shfl_xor(o8[e], off);
     float *pp = a.part + ((int64_t)split * a.B * a.HQ + bh) * (V + 2);
-    if (kg == 0) {
-        reinterpret_cast<f32x4 *>(pp + cg * 8)[0] = f32x4{o8[0], o8[1], o8[2], o8[3]};
-        reinterpret_cast<f32x4 *>(pp + cg * 8)[1] = f32x4{o8[4], o8[5], o8[6], o8[7]};
+    if (gv == 0) {
+        reinterpret_cast<f32x4 *>(pp + cv * 8)[0] = f32x4{o8[0], o8[1], o8[2], o8[3]};
+        reinterpret_cast<f32x4 *>(pp + cv * 8)[1] = f32x4{o8[4], o8[5], o8[6], o8[7]};
     }
     if (lane == 0) {
         pp[V] = m;
@@ -220,8 +268,8 @@ hipError_t run_cache(const CacheArgs &a, hipStream_t st) {
 
 template <typename T, int K, int V>
 hipError_t run_decode(const DecodeArgs &a, hipStream_t st) {
-    hipLaunchKernelGGL((decode_split<T, K, V>), dim3((unsigned)a.nsplit, (unsigned)(a.B * a.HQ)), dim3(64), 0, st,
-                       a);
+    hipLaunchKernelGGL((decode_split<T, K, V>), dim3((unsigned)a.nsplit, (unsigned)(a.B * a.HQ / a.nwg)),
+                       dim3(64 * a.nwg), 0, st, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((decode_merge<T, V>), dim3((unsigned)(a.B * a.HQ)), dim3(V), 0, st, a);
