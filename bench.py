@@ -220,6 +220,13 @@ def bench_decode(args):
         if marks:
             marks[2].record()
 
+    if args.copy_mb:
+        n = args.copy_mb * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.mul(src, 1.0, out=dst)  # reads and writes copy_mb MiB each
+        torch.cuda.synchronize()
+        del src, dst
     dec, app, _ = decode_bytes(B, T, HQ, H, K, V, C, es)
     print(f"[bench] {args.workload}: B={B} T={T} HQ={HQ} H={H} K={K} V={V} C={C} {d.q.dtype} "
           f"decode bytes={dec} append bytes={app}", file=sys.stderr, flush=True)
