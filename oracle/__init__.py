@@ -25,8 +25,8 @@ _SRC = os.path.join(_HERE, "wall_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
-__all__ = ["build", "wall_attn_oracle", "prefix_scan_oracle", "kv_cache_oracle", "decode_oracle",
-           "num_threads"]
+__all__ = ["build", "wall_attn_oracle", "wall_attn_bwd_oracle", "prefix_scan_oracle", "kv_cache_oracle",
+           "decode_oracle", "num_threads"]
 
 
 def build(force: bool = True) -> str:
@@ -50,6 +50,9 @@ def _bind(path: str):
     lib.wall_oracle_fwd.restype = ctypes.c_int
     lib.wall_oracle_prefix_scan.argtypes = [P, P, I, I, I, P, I, ctypes.c_double]
     lib.wall_oracle_prefix_scan.restype = ctypes.c_int
+    lib.wall_oracle_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I,
+                                    ctypes.c_double, I, P, I]
+    lib.wall_oracle_bwd.restype = ctypes.c_int
     lib.wall_oracle_kv_cache.argtypes = [P, P, P, P, I, I, I, I, I, I]
     lib.wall_oracle_kv_cache.restype = ctypes.c_int
     lib.wall_oracle_decode.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, ctypes.c_double]
@@ -126,6 +129,37 @@ def wall_attn_oracle(q, k, v, g, scale: Optional[float] = None, g_scalar=None,
     if rc != 0:
         raise ValueError(f"wall_oracle_fwd rejected its arguments (code {rc})")
     return o, lse
+
+
+def wall_attn_bwd_oracle(q, k, v, g, do, scale: Optional[float] = None, g_scalar=None, sink_bias=None,
+                         window_size: Optional[int] = None, cu_seqlens=None):
+    """Gradients of the product-form forward in fp64 for an upstream gradient
+    ``do`` [B,T,HQ,V] of o.  Returns ``(dq, dk, dv, dg, dg_scalar, dsink)``;
+    the last two are None when g_scalar / sink_bias is."""
+    q, k, v, g, do = _f64(q), _f64(k), _f64(v), _f64(g), _f64(do)
+    gs, sk = _f64(g_scalar), _f64(sink_bias)
+    B, T, HQ, K = q.shape
+    H, V = k.shape[2], v.shape[3]
+    assert k.shape == (B, T, H, K) and v.shape == (B, T, H, V) and g.shape == (B, T, HQ, K)
+    assert do.shape == (B, T, HQ, V)
+    if scale is None:
+        scale = K ** -0.5
+    cu = None
+    nseq = 0
+    if cu_seqlens is not None:
+        if hasattr(cu_seqlens, "detach"):
+            cu_seqlens = cu_seqlens.detach().cpu().numpy()
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+        nseq = cu.shape[0] - 1
+    dq, dk, dv, dg = np.empty_like(q), np.empty_like(k), np.empty_like(v), np.empty_like(g)
+    dgs = None if gs is None else np.empty_like(gs)
+    dsk = None if sk is None else np.empty_like(sk)
+    rc = _load().wall_oracle_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(gs), _ptr(sk), _ptr(do), _ptr(dq),
+                                 _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dgs), _ptr(dsk), B, T, HQ, H, K, V,
+                                 float(scale), int(window_size or 0), _ptr(cu), nseq)
+    if rc != 0:
+        raise ValueError(f"wall_oracle_bwd rejected its arguments (code {rc})")
+    return dq, dk, dv, dg, dgs, dsk
 
 
 def prefix_scan_oracle(x, cu_seqlens=None, scale: float = 1.0 / np.log(2.0)):

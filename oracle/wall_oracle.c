@@ -175,6 +175,192 @@ int wall_oracle_prefix_scan(const double *x, double *out, int64_t B, int64_t T, 
     return 0;
 }
 
+/* Backward of the forward above (README: "exact analytic gradients" for q,
+ * k, v, g and g_scalar), written from the product form.  With the logits
+ * s_ij = scale * sum_n F_ij,n q_in k_jn + (Gs_i - Gs_j) (Gs the running sum
+ * of g_scalar), A_ij = exp(s_ij - lse_i) and D_i = sum_v do_iv o_iv:
+ *     dS_ij = A_ij (do_i . v_j - D_i)
+ *     dv_j  = sum_i A_ij do_i                     (over the query heads of j's kv head)
+ *     dq_in = scale sum_j dS_ij F_ij,n k_jn
+ *     dk_jn = scale sum_i dS_ij F_ij,n q_in       (per query head, then summed)
+ *     dsink = -sum_i exp(sink - lse_i) D_i
+ * F_ij,n = prod_{r=j+1..i} exp(g_rn) depends on g_un for j < u <= i, so
+ *     dg_un = sum_{i >= u > j} scale dS_ij F_ij,n q_in k_jn
+ *           = sum_{t >= u, same sequence} (q_tn dq_tn - k_tn dk^(hq)_tn)
+ * (the pairs with i >= u, minus those with j >= u, which also have i >= u),
+ * and likewise dg_scalar_u = sum_{t >= u} (sum_j dS_tj - sum_i dS_it).
+ * o and lse are recomputed here in fp64.  Outputs are overwritten; any of
+ * dg_scalar / dsink may be NULL when g_scalar / sink is. */
+int wall_oracle_bwd(const double *q, const double *k, const double *v, const double *g,
+                    const double *g_scalar, const double *sink, const double *dout,
+                    double *dq, double *dk, double *dv, double *dg, double *dgs, double *dsink,
+                    int64_t B, int64_t T, int64_t HQ, int64_t H, int64_t K, int64_t V,
+                    double scale, int64_t window, const int64_t *cu_seqlens, int64_t nseq)
+{
+    if (!q || !k || !v || !g || !dout || !dq || !dk || !dv || !dg) return -1;
+    if (B < 1 || T < 1 || HQ < 1 || H < 1 || K < 1 || V < 1) return -2;
+    if (HQ % H != 0) return -3;
+    if (cu_seqlens && (B != 1 || nseq < 1)) return -4;
+    const int64_t group = HQ / H;
+    /* per query head: dk contributions and the two per-token sums whose
+     * suffix sums give dg and dg_scalar */
+    double *dkh = (double *)calloc((size_t)(B * T * HQ * K), sizeof(double));
+    double *dvh = (double *)calloc((size_t)(B * T * HQ * V), sizeof(double));
+    double *grow = (double *)calloc((size_t)(B * T * HQ), sizeof(double));
+    double *gcol = (double *)calloc((size_t)(B * T * HQ), sizeof(double));
+    double *sk = (double *)calloc((size_t)(B * HQ), sizeof(double));
+    if (!dkh || !dvh || !grow || !gcol || !sk) {
+        free(dkh); free(dvh); free(grow); free(gcol); free(sk);
+        return -7;
+    }
+    int fail = 0;
+#pragma omp parallel
+    {
+        double *F = (double *)malloc(sizeof(double) * (size_t)(K * T));
+        double *logit = (double *)malloc(sizeof(double) * (size_t)T);
+        double *o = (double *)malloc(sizeof(double) * (size_t)V);
+        if (!F || !logit || !o) {
+#pragma omp atomic write
+            fail = 1;
+        } else {
+            /* one (b, hq) per task: its dk/dv/g sums are private to it */
+#pragma omp for collapse(2) schedule(dynamic, 1)
+            for (int64_t b = 0; b < B; ++b)
+                for (int64_t hq = 0; hq < HQ; ++hq) {
+                    const int64_t hk = hq / group;
+                    for (int64_t i = 0; i < T; ++i) {
+                        int64_t s0 = 0;
+                        if (cu_seqlens)
+                            for (int64_t s = 0; s < nseq; ++s)
+                                if (i >= cu_seqlens[s] && i < cu_seqlens[s + 1]) s0 = cu_seqlens[s];
+                        int64_t lo = s0;
+                        if (window > 0 && lo < i + 1 - window) lo = i + 1 - window;
+                        const double *qi = q + ((b * T + i) * HQ + hq) * K;
+                        const double *doi = dout + ((b * T + i) * HQ + hq) * V;
+                        /* logits of row i, keeping F for every visible key (F[(i-j)*K + n]) */
+                        double fox = 0.0;
+                        for (int64_t j = i; j >= lo; --j) {
+                            double *Fj = F + (i - j) * K;
+                            if (j == i) {
+                                for (int64_t n = 0; n < K; ++n) Fj[n] = 1.0;
+                            } else {
+                                const double *gj1 = g + ((b * T + j + 1) * HQ + hq) * K;
+                                for (int64_t n = 0; n < K; ++n) Fj[n] = Fj[n - K] * exp(gj1[n]);
+                                if (g_scalar) fox = fox + g_scalar[(b * T + j + 1) * HQ + hq];
+                            }
+                            const double *kj = k + ((b * T + j) * H + hk) * K;
+                            double dot = 0.0;
+                            for (int64_t n = 0; n < K; ++n) dot += Fj[n] * qi[n] * kj[n];
+                            logit[i - j] = scale * dot + fox;
+                        }
+                        const int64_t cnt = i - lo + 1;
+                        double m = -INFINITY;
+                        for (int64_t c = 0; c < cnt; ++c) m = logit[c] > m ? logit[c] : m;
+                        if (sink && sink[hq] > m) m = sink[hq];
+                        double Z = 0.0;
+                        for (int64_t c = 0; c < cnt; ++c) Z += exp(logit[c] - m);
+                        if (sink) Z = Z + exp(sink[hq] - m);
+                        const double lse = m + log(Z);
+                        for (int64_t d = 0; d < V; ++d) o[d] = 0.0;
+                        for (int64_t c = 0; c < cnt; ++c) {
+                            const double *vj = v + ((b * T + (i - c)) * H + hk) * V;
+                            const double a = exp(logit[c] - lse);
+                            for (int64_t d = 0; d < V; ++d) o[d] += a * vj[d];
+                        }
+                        double Di = 0.0;
+                        for (int64_t d = 0; d < V; ++d) Di += doi[d] * o[d];
+                        if (sink) sk[b * HQ + hq] -= exp(sink[hq] - lse) * Di;
+                        double *dqi = dq + ((b * T + i) * HQ + hq) * K;
+                        for (int64_t n = 0; n < K; ++n) dqi[n] = 0.0;
+                        for (int64_t c = 0; c < cnt; ++c) {
+                            const int64_t j = i - c;
+                            const double *vj = v + ((b * T + j) * H + hk) * V;
+                            const double *kj = k + ((b * T + j) * H + hk) * K;
+                            const double a = exp(logit[c] - lse);
+                            double dpv = 0.0;
+                            for (int64_t d = 0; d < V; ++d) dpv += doi[d] * vj[d];
+                            const double dS = a * (dpv - Di);
+                            const double *Fj = F + c * K;
+                            double *dkj = dkh + ((b * T + j) * HQ + hq) * K;
+                            double *dvj = dvh + ((b * T + j) * HQ + hq) * V;
+                            for (int64_t n = 0; n < K; ++n) {
+                                dqi[n] += scale * dS * Fj[n] * kj[n];
+                                dkj[n] += scale * dS * Fj[n] * qi[n];
+                            }
+                            for (int64_t d = 0; d < V; ++d) dvj[d] += a * doi[d];
+                            grow[(b * T + i) * HQ + hq] += dS;
+                            gcol[(b * T + j) * HQ + hq] += dS;
+                        }
+                    }
+                }
+        }
+        free(F);
+        free(logit);
+        free(o);
+    }
+    if (!fail) {
+        /* dk, dv: sums over the query heads of each kv head */
+        for (int64_t t = 0; t < B * T; ++t)
+            for (int64_t h = 0; h < H; ++h) {
+                double *dkt = dk + (t * H + h) * K;
+                double *dvt = dv + (t * H + h) * V;
+                for (int64_t n = 0; n < K; ++n) dkt[n] = 0.0;
+                for (int64_t d = 0; d < V; ++d) dvt[d] = 0.0;
+                for (int64_t hq = h * group; hq < (h + 1) * group; ++hq) {
+                    for (int64_t n = 0; n < K; ++n) dkt[n] += dkh[(t * HQ + hq) * K + n];
+                    for (int64_t d = 0; d < V; ++d) dvt[d] += dvh[(t * HQ + hq) * V + d];
+                }
+            }
+        /* dg, dg_scalar: suffix sums within each sequence */
+        for (int64_t b = 0; b < B; ++b)
+            for (int64_t hq = 0; hq < HQ; ++hq) {
+                const int64_t hk = hq / group;
+                for (int64_t n = 0; n < K; ++n) {
+                    double run = 0.0;
+                    int64_t s = nseq - 1;
+                    for (int64_t t = T - 1; t >= 0; --t) {
+                        if (cu_seqlens) {
+                            while (s > 0 && t < cu_seqlens[s]) --s;
+                            if (t == cu_seqlens[s + 1] - 1) run = 0.0;
+                        } else if (t == T - 1) {
+                            run = 0.0;
+                        }
+                        const int64_t tk = (b * T + t) * HQ + hq;
+                        run += q[tk * K + n] * dq[tk * K + n] - k[((b * T + t) * H + hk) * K + n] * dkh[tk * K + n];
+                        dg[tk * K + n] = run;
+                    }
+                }
+                if (dgs) {
+                    double run = 0.0;
+                    int64_t s = nseq - 1;
+                    for (int64_t t = T - 1; t >= 0; --t) {
+                        if (cu_seqlens) {
+                            while (s > 0 && t < cu_seqlens[s]) --s;
+                            if (t == cu_seqlens[s + 1] - 1) run = 0.0;
+                        } else if (t == T - 1) {
+                            run = 0.0;
+                        }
+                        const int64_t tk = (b * T + t) * HQ + hq;
+                        run += grow[tk] - gcol[tk];
+                        dgs[tk] = run;
+                    }
+                }
+            }
+        if (dsink)
+            for (int64_t hq = 0; hq < HQ; ++hq) {
+                double acc = 0.0;
+                for (int64_t b = 0; b < B; ++b) acc += sk[b * HQ + hq];
+                dsink[hq] = sink ? acc : 0.0;
+            }
+    }
+    free(dkh);
+    free(dvh);
+    free(grow);
+    free(gcol);
+    free(sk);
+    return fail ? -7 : 0;
+}
+
 /* Decode cache, wall-attention-release README ("Decode (cached generation)"):
  * the keys with the decay folded in, per chunk of C rows,
  *     k_tilde[b,j,hq,n] = k[b,j,h,n] * exp2(R[b,c,hq,n] - P[b,j,hq,n]),  c = j / C,

@@ -53,6 +53,15 @@ MUTANTS = {
     "decode_scale_dropped": ("logit[j] = scale * dot;", "logit[j] = dot;"),
     "decode_value_head": ("const double *vj = v + ((b * T + j) * H + kvh) * V;",
                           "const double *vj = v + ((b * T + j) * H + 0) * V;"),
+    "bwd_dS_without_D": ("const double dS = a * (dpv - Di);", "const double dS = a * dpv;"),
+    "bwd_dk_decay_dropped": ("dkj[n] += scale * dS * Fj[n] * qi[n];", "dkj[n] += scale * dS * qi[n];"),
+    "bwd_dv_unweighted": ("for (int64_t d = 0; d < V; ++d) dvj[d] += a * doi[d];",
+                          "for (int64_t d = 0; d < V; ++d) dvj[d] += doi[d];"),
+    "bwd_dg_key_term_sign": ("run += q[tk * K + n] * dq[tk * K + n] - k[((b * T + t) * H + hk) * K + n] * dkh[tk * K + n];",
+                             "run += q[tk * K + n] * dq[tk * K + n] + k[((b * T + t) * H + hk) * K + n] * dkh[tk * K + n];"),
+    "bwd_dgs_row_sums_only": ("run += grow[tk] - gcol[tk];", "run += grow[tk];"),
+    "bwd_dsink_sign": ("if (sink) sk[b * HQ + hq] -= exp(sink[hq] - lse) * Di;",
+                       "if (sink) sk[b * HQ + hq] += exp(sink[hq] - lse) * Di;"),
 }
 
 

@@ -379,3 +379,77 @@ def test_kv_cache_zero_gate_and_reconstruction(oracle_mod):
     np.testing.assert_allclose(kt * np.exp2(P - Rj), np.repeat(k, HQ // H, axis=2), rtol=1e-13, atol=1e-14)
     # the factor stays within the chunk's decay: at most 1 below, never above the chunk start's prefix
     assert (Rj - P > -1.0).all()
+
+
+# --------------------------------------------------------------------------- backward
+
+
+def _fd_check(oracle_mod, args, kw, grads, rng, eps=1e-6, rtol=1e-6):
+    """Central differences of sum(o * do) in a random direction per input."""
+    q, k, v, g, gs, sink, do = args
+
+    def loss(q, k, v, g, gs, sink):
+        o, _ = oracle_mod.wall_attn_oracle(q, k, v, g, g_scalar=gs, sink_bias=sink, **kw)
+        return float((o * do).sum())
+
+    base = [q, k, v, g, gs, sink]
+    for idx, name in enumerate(["q", "k", "v", "g", "g_scalar", "sink"]):
+        if base[idx] is None:
+            assert grads[idx] is None
+            continue
+        d = rng.standard_normal(base[idx].shape)
+        up, dn = list(base), list(base)
+        up[idx] = base[idx] + eps * d
+        dn[idx] = base[idx] - eps * d
+        fd = (loss(*up) - loss(*dn)) / (2 * eps)
+        an = float((grads[idx] * d).sum())
+        assert abs(fd - an) <= rtol * max(1.0, abs(fd)), (name, fd, an)
+
+
+@pytest.mark.parametrize("case", ["plain", "gqa_window_fox_sink", "varlen", "positive_gate", "single_token"])
+def test_backward_matches_central_differences(oracle_mod, case):
+    """README: the g / g_scalar gradients are verified against central finite
+    differences; every gradient of the oracle's backward is held to that."""
+    rng = np.random.default_rng(41)
+    B, T, HQ, H, K, V = 2, 29, 4, 2, 5, 3
+    kw = dict(scale=0.45)
+    gs = sink = None
+    cu = None
+    if case == "single_token":
+        T = 1
+    if case == "varlen":
+        B, cu = 1, [0, 7, 7, 8, 29]
+        kw["cu_seqlens"] = cu
+    q, k, v = rnd(rng, B, T, HQ, K), rnd(rng, B, T, H, K), rnd(rng, B, T, H, V)
+    g = (0.2 if case == "positive_gate" else -0.3) * np.abs(rnd(rng, B, T, HQ, K))
+    if case == "gqa_window_fox_sink":
+        gs = -0.2 * np.abs(rnd(rng, B, T, HQ))
+        sink = rnd(rng, HQ)
+        kw["window_size"] = 11
+    do = rnd(rng, B, T, HQ, V)
+    grads = oracle_mod.wall_attn_bwd_oracle(q, k, v, g, do, g_scalar=gs, sink_bias=sink, **kw)
+    _fd_check(oracle_mod, (q, k, v, g, gs, sink, do), kw, grads, rng)
+    # a decay-gate entry at a sequence's first token moves nothing: its gradient is 0
+    starts = [0] if cu is None else sorted(set(x for x in cu[:-1] if x < T))
+    for s in starts:
+        np.testing.assert_allclose(grads[3][:, s], 0.0, atol=1e-10)
+        if gs is not None:
+            np.testing.assert_allclose(grads[4][:, s], 0.0, atol=1e-10)
+
+
+def test_backward_g_zero_is_sdpa_autograd(oracle_mod):
+    """g = 0: dq, dk, dv are softmax attention's, from torch autograd of
+    scaled_dot_product_attention in fp64 (GQA by explicit repetition)."""
+    rng = np.random.default_rng(43)
+    B, T, HQ, H, K, V = 2, 33, 4, 2, 6, 5
+    q, k, v, do = rnd(rng, B, T, HQ, K), rnd(rng, B, T, H, K), rnd(rng, B, T, H, V), rnd(rng, B, T, HQ, V)
+    dq, dk, dv, _, _, _ = oracle_mod.wall_attn_bwd_oracle(q, k, v, np.zeros((B, T, HQ, K)), do, scale=0.3)
+    qt = torch.tensor(q).transpose(1, 2).requires_grad_()
+    kt = torch.tensor(k).transpose(1, 2).requires_grad_()
+    vt = torch.tensor(v).transpose(1, 2).requires_grad_()
+    o = F.scaled_dot_product_attention(qt, kt.repeat_interleave(HQ // H, 1), vt.repeat_interleave(HQ // H, 1),
+                                       is_causal=True, scale=0.3)
+    o.backward(torch.tensor(do).transpose(1, 2))
+    np.testing.assert_allclose(dq, qt.grad.transpose(1, 2).numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dk, kt.grad.transpose(1, 2).numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dv, vt.grad.transpose(1, 2).numpy(), rtol=1e-10, atol=1e-12)
