@@ -24,6 +24,7 @@ from ._binding import (  # noqa: F401
     prefix_scan_workspace_size,
     status_string,
     wall_attn,
+    wall_attn_bwd,
     wall_attn_decode,
     wall_attn_fwd,
     wall_attn_fwd_prepare,
@@ -31,5 +32,5 @@ from ._binding import (  # noqa: F401
     wall_prefix_scan,
 )
 
-__all__ = ["wall_attn", "wall_attn_fwd", "wall_prefix_scan", "build_wall_kv_cache", "wall_attn_decode",
+__all__ = ["wall_attn", "wall_attn_fwd", "wall_attn_bwd", "wall_prefix_scan", "build_wall_kv_cache", "wall_attn_decode",
            "WallError", "lib"]

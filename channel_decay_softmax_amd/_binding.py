@@ -27,6 +27,7 @@ EXPORTS = (
     "wall_prefix_scan_workspace_size", "wall_prefix_scan",
     "wall_attn_fwd_workspace_size", "wall_attn_fwd",
     "wall_attn_fwd_prepare", "wall_attn_fwd_run",
+    "wall_attn_bwd_workspace_size", "wall_attn_bwd",
     "wall_kv_cache_build", "wall_attn_decode_workspace_size", "wall_attn_decode",
 )
 
@@ -67,6 +68,11 @@ def lib() -> ctypes.CDLL:
         L.wall_attn_fwd_run.argtypes = [P, E, P, P, P, P, P, I, I, I, I, I, I, F, I, P, I, I, P, S,
                                         P]
         L.wall_attn_fwd_run.restype = E
+        L.wall_attn_bwd_workspace_size.argtypes = [I, I, I, I, I]
+        L.wall_attn_bwd_workspace_size.restype = S
+        L.wall_attn_bwd.argtypes = [P, P, P, E, P, P, P, P, P, P, P, P, P, P, P, E, P, I, I, I, I, I, I, F, I,
+                                    P, I, I, P, S, P]
+        L.wall_attn_bwd.restype = E
         L.wall_kv_cache_build.argtypes = [P, E, P, P, P, I, I, I, I, I, I, I, I, P]
         L.wall_kv_cache_build.restype = E
         L.wall_attn_decode_workspace_size.argtypes = [I, I, I, I]
@@ -212,6 +218,73 @@ def check_cu_seqlens(cu_seqlens: torch.Tensor, B: int, T: int) -> int:
     return int((cu[1:] - cu[:-1]).max())
 
 
+def wall_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, P: torch.Tensor, o: torch.Tensor,
+                  lse: torch.Tensor, dout: torch.Tensor, G: Optional[torch.Tensor] = None,
+                  sink_bias: Optional[torch.Tensor] = None, scale: Optional[float] = None,
+                  window_size: Optional[int] = None, cu_seqlens: Optional[torch.Tensor] = None,
+                  max_seqlen: Optional[int] = None, g_dtype: Optional[torch.dtype] = None,
+                  workspace: Optional[torch.Tensor] = None):
+    """Gradients of wall_attn_fwd for the upstream gradient ``dout`` of o.
+    Returns (dq, dk, dv, dg, dg_scalar, dsink); dg / dg_scalar are the gradients
+    of the natural-log gates in ``g_dtype`` (default: q's dtype), dg_scalar is
+    None without G and dsink (float32) None without sink_bias."""
+    dev = _on_gpu(q, k, v, P, o, lse, dout, G, sink_bias, cu_seqlens, workspace)
+    q, k, v, P, o, lse, dout, G = (_dense(t) for t in (q, k, v, P, o, lse, dout, G))
+    B, T, HQ, K = q.shape
+    H, V = k.shape[2], v.shape[3]
+    if dout.shape != (B, T, HQ, V) or dout.dtype != q.dtype or o.shape != (B, T, HQ, V):
+        raise ValueError("o and dout must be [B,T,HQ,V] in q's dtype")
+    if sink_bias is not None:
+        sink_bias = _dense(sink_bias.to(torch.float32))
+    if scale is None:
+        scale = K ** -0.5
+    gd = q.dtype if g_dtype is None else g_dtype
+    cu = None if cu_seqlens is None else _dense(cu_seqlens.to(torch.int32))
+    nseq = 0 if cu is None else cu.numel() - 1
+    if cu is not None and max_seqlen is None:
+        max_seqlen = int((cu[1:] - cu[:-1]).max().item())
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dg = torch.empty((B, T, HQ, K), dtype=gd, device=dev)
+    dgs = None if G is None else torch.empty((B, T, HQ), dtype=gd, device=dev)
+    dsink = None if sink_bias is None else torch.empty((HQ,), dtype=torch.float32, device=dev)
+    nbytes = int(lib().wall_attn_bwd_workspace_size(B, T, HQ, K, nseq))
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    _check(lib().wall_attn_bwd(
+        _ptr(q), _ptr(k), _ptr(v), _dtype(q), _ptr(P), _ptr(G), _ptr(sink_bias), _ptr(o), _ptr(lse), _ptr(dout),
+        _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dgs), WALL_BF16 if gd == torch.bfloat16 else WALL_F32,
+        _ptr(dsink), B, T, HQ, H, K, V, float(scale), int(window_size or 0), _ptr(cu), nseq,
+        int(max_seqlen or 0), _ptr(workspace), workspace.numel(), _stream(dev)), "wall_attn_bwd")
+    return dq, dk, dv, dg, dgs, dsink
+
+
+class _WallAttn(torch.autograd.Function):
+    """wall_attn with its gradients (q, k, v, g, g_scalar, sink_bias)."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, g, g_scalar, sink_bias, scale, window_size, cu_seqlens, max_seqlen):
+        P = wall_prefix_scan(g, cu_seqlens)
+        G = None if g_scalar is None else wall_prefix_scan(g_scalar, cu_seqlens)
+        o, lse = wall_attn_fwd(q, k, v, P, G, sink_bias, scale, window_size, cu_seqlens, max_seqlen,
+                               return_lse=True)
+        ctx.save_for_backward(q, k, v, P, G, sink_bias, o, lse, cu_seqlens)
+        ctx.set_materialize_grads(False)  # an unused lse gets no gradient tensor
+        ctx.opts = (scale, window_size, max_seqlen, g.dtype, g_scalar is not None, sink_bias is not None)
+        return o, lse
+
+    @staticmethod
+    def backward(ctx, do, dlse):
+        q, k, v, P, G, sink_bias, o, lse, cu_seqlens = ctx.saved_tensors
+        scale, window_size, max_seqlen, gdt, has_gs, has_sink = ctx.opts
+        if dlse is not None:
+            raise NotImplementedError("wall_attn: a gradient through lse is not supported")
+        if do is None:
+            do = torch.zeros_like(o)
+        dq, dk, dv, dg, dgs, dsink = wall_attn_bwd(q, k, v, P, o, lse, do.contiguous(), G, sink_bias, scale,
+                                                   window_size, cu_seqlens, max_seqlen, g_dtype=gdt)
+        return dq, dk, dv, dg, dgs, dsink, None, None, None, None
+
+
 def wall_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
               scale: Optional[float] = None, g_scalar: Optional[torch.Tensor] = None,
               sink_bias: Optional[torch.Tensor] = None, window_size: Optional[int] = None,
@@ -221,16 +294,18 @@ def wall_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
     natural-log decay (g = 0 is softmax attention), scale default K**-0.5;
     optional g_scalar [B,T,HQ], sink_bias [HQ], window_size, cu_seqlens (B == 1).
     Runs wall_prefix_scan (g -> P, g_scalar -> G) and wall_attn_fwd on the
-    current stream.  Returns o [B,T,HQ,V] (and lse [B,T,HQ] if asked)."""
+    current stream; when an input requires grad, o.backward() runs
+    wall_attn_bwd.  Returns o [B,T,HQ,V] (and lse [B,T,HQ] if asked)."""
     _on_gpu(q, k, v, g, g_scalar, sink_bias, cu_seqlens)
     B, T = q.shape[:2]
     max_seqlen = None
     if cu_seqlens is not None:
         max_seqlen = check_cu_seqlens(cu_seqlens, B, T)
-    P = wall_prefix_scan(g, cu_seqlens)
-    G = None if g_scalar is None else wall_prefix_scan(g_scalar, cu_seqlens)
-    o, lse = wall_attn_fwd(q, k, v, P, G, sink_bias, scale, window_size, cu_seqlens, max_seqlen,
-                           return_lse=return_lse)
+    if scale is None:
+        scale = q.shape[3] ** -0.5
+    if sink_bias is not None and sink_bias.dtype != torch.float32:
+        sink_bias = sink_bias.float()
+    o, lse = _WallAttn.apply(q, k, v, g, g_scalar, sink_bias, scale, window_size, cu_seqlens, max_seqlen)
     return (o, lse) if return_lse else o
 
 

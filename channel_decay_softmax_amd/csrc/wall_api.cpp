@@ -188,6 +188,82 @@ wall_status_t wall_attn_fwd(const void *q, const void *k, const void *v, wall_dt
     return enqueue_run(q, dtype, P, G, sink_bias, o, lse, s, scale, window_size, workspace, stream);
 }
 
+size_t wall_attn_bwd_workspace_size(int64_t B, int64_t T, int64_t HQ, int64_t K, int64_t num_seqs) {
+    if (B < 1 || T < 1 || HQ < 1 || K < 1) return 0;
+    return bwd_layout(B, T, HQ, K, num_seqs > 0 ? num_seqs : B).total;
+}
+
+wall_status_t wall_attn_bwd(const void *q, const void *k, const void *v, wall_dtype_t dtype, const float *P,
+                            const float *G, const float *sink_bias, const void *o, const float *lse,
+                            const void *dout, void *dq, void *dk, void *dv, void *dg, void *dg_scalar,
+                            wall_dtype_t g_dtype, float *dsink, int64_t B, int64_t T, int64_t HQ, int64_t H,
+                            int64_t K, int64_t V, float scale, int64_t window_size, const int32_t *cu_seqlens,
+                            int64_t num_seqs, int64_t max_seqlen, void *workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+    if (!q || !k || !v || !P || !o || !lse || !dout || !dq || !dk || !dv || !dg || !workspace)
+        return WALL_ERR_INVALID_ARG;
+    if (G && !dg_scalar) return WALL_ERR_INVALID_ARG;
+    if (sink_bias && !dsink) return WALL_ERR_INVALID_ARG;
+    if (B < 1 || T < 1 || HQ < 1 || H < 1 || K < 1 || V < 1) return WALL_ERR_INVALID_ARG;
+    if (HQ % H != 0) return WALL_ERR_INVALID_ARG;
+    if (B * T > INT32_MAX / 2 || B * T * HQ * (K > V ? K : V) > ((int64_t)1 << 40)) return WALL_ERR_INVALID_ARG;
+    if (cu_seqlens && (B != 1 || num_seqs < 1 || num_seqs > T || max_seqlen < 1 || max_seqlen > T))
+        return WALL_ERR_INVALID_ARG;
+    if (dtype != WALL_BF16 && dtype != WALL_F32) return WALL_ERR_UNSUPPORTED;
+    if (g_dtype != WALL_BF16 && g_dtype != WALL_F32) return WALL_ERR_UNSUPPORTED;
+    if ((K != 64 && K != 128) || (V != 64 && V != 128)) return WALL_ERR_UNSUPPORTED;
+    const void *ptrs[] = {q, k, v, P, G, sink_bias, o, lse, dout, dq, dk, dv, dg, dg_scalar, dsink, cu_seqlens};
+    for (const void *p : ptrs)
+        if (p && !aligned(p, 16)) return WALL_ERR_INVALID_ARG;
+    if (!aligned(workspace, 256)) return WALL_ERR_INVALID_ARG;
+    const int64_t nseg = cu_seqlens ? num_seqs : B;
+    const BwdLayout L = bwd_layout(B, T, HQ, K, nseg);
+    if (workspace_bytes < L.total) return WALL_ERR_INVALID_ARG;
+    char *ws = static_cast<char *>(workspace);
+    SegInfo *seg = reinterpret_cast<SegInfo *>(ws + L.off_seg);
+    wall_status_t st = launched(launch_bwd_seg(seg, cu_seqlens, nseg, T, stream));
+    if (st != WALL_OK) return st;
+    BwdArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.dout = dout;
+    a.P = P;
+    a.G = G;
+    a.sink = sink_bias;
+    a.lse = lse;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.dsink = sink_bias ? dsink : nullptr;
+    a.D = reinterpret_cast<float *>(ws + L.off_D);
+    a.X = reinterpret_cast<float *>(ws + L.off_X);
+    a.Y = reinterpret_cast<float *>(ws + L.off_Y);
+    a.Z = reinterpret_cast<float *>(ws + L.off_Z);
+    a.seg = seg;
+    a.nseg = (int32_t)nseg;
+    a.max_seqlen = (int32_t)(cu_seqlens ? max_seqlen : T);
+    a.rows = (int32_t)(B * T);
+    a.HQ = (int32_t)HQ;
+    a.H = (int32_t)H;
+    a.K = (int32_t)K;
+    a.V = (int32_t)V;
+    a.window = window_size > 0 ? (int32_t)(window_size > T ? T : window_size) : 0;
+    a.scale = scale;
+    a.qscale = scale * LOG2E;
+    st = launched(launch_bwd(a, dtype == WALL_BF16, stream));
+    if (st != WALL_OK) return st;
+    // dg = -(exclusive prefix of X), dg_scalar = -(exclusive prefix of Y), per sequence
+    void *sws = ws + L.off_scan;
+    const int64_t ns = cu_seqlens ? num_seqs : 0;
+    st = launched(launch_scan_excl(a.X, dg, g_dtype == WALL_BF16, B, T, HQ * K, cu_seqlens, ns, -1.0f, sws,
+                                   stream));
+    if (st != WALL_OK || !G) return st;
+    return launched(launch_scan_excl(a.Y, dg_scalar, g_dtype == WALL_BF16, B, T, HQ, cu_seqlens, ns, -1.0f, sws,
+                                     stream));
+}
+
 wall_status_t wall_kv_cache_build(const void *k, wall_dtype_t dtype, const float *P, void *k_tilde,
                                   float *r_cache, int64_t B, int64_t T_cap, int64_t HQ, int64_t H,
                                   int64_t K, int64_t chunk_size, int64_t t0, int64_t t1,

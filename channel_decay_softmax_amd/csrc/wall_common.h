@@ -120,6 +120,10 @@ inline ScanLayout scan_layout(int64_t B, int64_t T, int64_t C) {
 
 hipError_t launch_scan(const void *x, bool x_bf16, float *out, int64_t B, int64_t T, int64_t C,
                        const int32_t *cu, int64_t nseq, float scale, void *ws, hipStream_t st);
+// The exclusive form (scale * the sum of the earlier rows of the sequence) of
+// a float32 input, written as float32 or bf16.
+hipError_t launch_scan_excl(const float *x, void *out, bool out_bf16, int64_t B, int64_t T, int64_t C,
+                            const int32_t *cu, int64_t nseq, float scale, void *ws, hipStream_t st);
 
 struct PrepArgs {
     const void *k;     // [rows, H, K]
@@ -153,6 +157,43 @@ struct FwdArgs {
 };
 hipError_t launch_fwd_bf16(const FwdArgs &a, hipStream_t st);
 hipError_t launch_fwd_f32(const FwdArgs &a, hipStream_t st);
+
+// ----------------------------------------------------------------- backward
+struct BwdArgs {
+    const void *q, *k, *v, *o, *dout;  // [rows, HQ or H, K / V] in dtype
+    const float *P, *G, *sink, *lse;   // P [rows, HQ, K]; G [rows, HQ] or null; sink [HQ] or null
+    void *dq, *dk, *dv;                // in dtype
+    float *dsink;                      // [HQ] or null
+    float *D, *X, *Y, *Z;              // workspace: do.o; q.dq - k.dk per head; dS row - column sums; sink terms
+    const SegInfo *seg;
+    int32_t nseg, max_seqlen, rows, HQ, H, K, V, window;
+    float scale, qscale;               // scale, scale * log2(e)
+};
+hipError_t launch_bwd_seg(SegInfo *seg, const int32_t *cu, int64_t nseg, int64_t T, hipStream_t st);
+hipError_t launch_bwd(const BwdArgs &a, bool bf16, hipStream_t st);
+
+struct BwdLayout {
+    size_t off_seg, off_D, off_X, off_Y, off_Z, off_scan, total;
+};
+inline BwdLayout bwd_layout(int64_t B, int64_t T, int64_t HQ, int64_t K, int64_t nseg) {
+    BwdLayout L;
+    const size_t rows = (size_t)(B * T);
+    size_t o = 0;
+    L.off_seg = o;
+    o = align_up(o + sizeof(SegInfo) * (size_t)nseg, 256);
+    L.off_D = o;
+    o = align_up(o + sizeof(float) * rows * HQ, 256);
+    L.off_X = o;
+    o = align_up(o + sizeof(float) * rows * HQ * K, 256);
+    L.off_Y = o;
+    o = align_up(o + sizeof(float) * rows * HQ, 256);
+    L.off_Z = o;
+    o = align_up(o + sizeof(float) * rows * HQ, 256);
+    L.off_scan = o;
+    o = align_up(o + scan_layout(B, T, HQ * K).total, 256);
+    L.total = o;
+    return L;
+}
 
 // ----------------------------------------------------------------- decode
 struct CacheArgs {

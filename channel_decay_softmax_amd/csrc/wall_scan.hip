@@ -60,6 +60,11 @@ struct Row<float, 1> {
     static __device__ inline fvec<1> val(Raw u) { return fvec<1>{u}; }
 };
 template <int VEC>
+__device__ inline void store_row(__bf16 *p, fvec<VEC> v) {
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) p[e] = (__bf16)v[e];
+}
+template <int VEC>
 __device__ inline void store_row(float *p, fvec<VEC> v) {
     if constexpr (VEC == 8) {
         reinterpret_cast<f32x4 *>(p)[0] = f32x4{v[0], v[1], v[2], v[3]};
@@ -195,10 +200,12 @@ __global__ __launch_bounds__(CV * CARRY_GROUPS) void scan_chunk_carry(const floa
     }
 }
 
-template <typename Tin, int VEC>
+// EXCL: out = scale * the sum of the rows before r in its sequence (0 at a
+// start) instead of up to and including r.  Tout: float32 or bf16 output.
+template <typename Tin, int VEC, typename Tout, bool EXCL>
 __global__ __launch_bounds__(256) void scan_finish(const Tin *__restrict__ x,
                                                    const float *__restrict__ carry,
-                                                   float *__restrict__ out, int64_t rows, int64_t C,
+                                                   Tout *__restrict__ out, int64_t rows, int64_t C,
                                                    const int32_t *cu, int nseq, int T, float scale) {
     using R = Row<Tin, VEC>;
     __shared__ uint32_t smask[GROUPS];
@@ -234,13 +241,14 @@ __global__ __launch_bounds__(256) void scan_finish(const Tin *__restrict__ x,
 #pragma unroll
     for (int i = 0; i < ROWS_PER_GROUP; ++i) {
         if ((mask >> i) & 1u) run = fvec<VEC>{};
+        if (EXCL && i < nr) store_row<VEC>(out + (r0 + i) * C + ch, run * scale);
         run += R::val(raw[i]);
-        if (i < nr) store_row<VEC>(out + (r0 + i) * C + ch, run * scale);
+        if (!EXCL && i < nr) store_row<VEC>(out + (r0 + i) * C + ch, run * scale);
     }
 }
 
-template <typename Tin, int VEC>
-hipError_t run_scan(const Tin *x, float *out, int64_t B, int64_t T, int64_t C, const int32_t *cu,
+template <typename Tin, int VEC, typename Tout = float, bool EXCL = false>
+hipError_t run_scan(const Tin *x, Tout *out, int64_t B, int64_t T, int64_t C, const int32_t *cu,
                     int64_t nseq, float scale, void *ws, hipStream_t st) {
     const ScanLayout L = scan_layout(B, T, C);
     char *w = static_cast<char *>(ws);
@@ -257,12 +265,25 @@ hipError_t run_scan(const Tin *x, float *out, int64_t B, int64_t T, int64_t C, c
                        st, csum, cflag, carry, L.nchunk, C);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((scan_finish<Tin, VEC>), grid, dim3(256), 0, st, x, carry, out, rows, C, cu,
+    hipLaunchKernelGGL((scan_finish<Tin, VEC, Tout, EXCL>), grid, dim3(256), 0, st, x, carry, out, rows, C, cu,
                        (int)nseq, (int)T, scale);
     return hipGetLastError();
 }
 
 }  // namespace
+
+hipError_t launch_scan_excl(const float *x, void *out, bool out_bf16, int64_t B, int64_t T, int64_t C,
+                            const int32_t *cu, int64_t nseq, float scale, void *ws, hipStream_t st) {
+    const bool vec = (C % 4) == 0;
+    if (out_bf16) {
+        __bf16 *o = static_cast<__bf16 *>(out);
+        return vec ? run_scan<float, 4, __bf16, true>(x, o, B, T, C, cu, nseq, scale, ws, st)
+                   : run_scan<float, 1, __bf16, true>(x, o, B, T, C, cu, nseq, scale, ws, st);
+    }
+    float *o = static_cast<float *>(out);
+    return vec ? run_scan<float, 4, float, true>(x, o, B, T, C, cu, nseq, scale, ws, st)
+               : run_scan<float, 1, float, true>(x, o, B, T, C, cu, nseq, scale, ws, st);
+}
 
 hipError_t launch_scan(const void *x, bool x_bf16, float *out, int64_t B, int64_t T, int64_t C,
                        const int32_t *cu, int64_t nseq, float scale, void *ws, hipStream_t st) {

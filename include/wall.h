@@ -186,6 +186,56 @@ wall_status_t wall_attn_fwd_run(const void *q, wall_dtype_t dtype,
                                 const void *workspace, size_t workspace_bytes,
                                 hipStream_t stream);
 
+/* ------------------------------------------------------------------ backward
+ *
+ * Gradients of wall_attn_fwd (the README's training path: "exact analytic
+ * gradients" for q, k, v, the decay gate g and the scalar gate g_scalar,
+ * and the sink).  With s_ij the natural-log logit of wall_attn_fwd,
+ * A_ij = exp(s_ij - lse_i) and D_i = dout_i . o_i:
+ *   dS_ij = A_ij (dout_i . v_j - D_i)
+ *   dv_j  = sum_i A_ij dout_i                       (summed over the query heads of j's kv head)
+ *   dq_in = scale sum_j dS_ij exp2(P_in - P_jn) k_jn
+ *   dk_jn = scale sum_i dS_ij exp2(P_in - P_jn) q_in (summed likewise)
+ *   dg_un = sum_{t >= u in u's sequence} (q_tn dq_tn - k_tn dk^(hq)_tn)
+ *   dg_scalar_u = sum_{t >= u} (sum_j dS_tj - sum_i dS_it)
+ *   dsink = -sum_i exp(sink - lse_i) D_i
+ * (dk^(hq): the query head's own part of dk; the decay between j and i is
+ * the product of the gates g_u, j < u <= i, of the blog's "Definition: Wall
+ * Attention", so dg collects every pair that straddles u).
+ *
+ *   q, k, v, P, G, sink_bias, cu_seqlens, max_seqlen, scale, window_size
+ *               as passed to wall_attn_fwd
+ *   o, lse      that call's outputs (lse required)
+ *   dout        [B, T, HQ, V] dtype, the gradient of o
+ *   dq [B,T,HQ,K], dk [B,T,H,K], dv [B,T,H,V]  dtype (written)
+ *   dg          [B, T, HQ, K] in g_dtype (written), the gradient of the
+ *               natural-log gate g (not of P)
+ *   dg_scalar   [B, T, HQ] in g_dtype (written; required when G is given)
+ *   dsink       [HQ] float32 (written; required when sink_bias is given)
+ *   workspace   device scratch of at least wall_attn_bwd_workspace_size(...)
+ *               bytes, 256-byte aligned, contents on entry ignored
+ * Every product is float32 on the vector ALUs (bf16 inputs are widened), with
+ * the forward's anchoring: exp2(P_i - P_j) split at an integer anchor inside
+ * the 64-row block at hand.  Over one sequence the summands of dg (and of
+ * dg_scalar) add up to zero, so the suffix sums are taken as minus the
+ * exclusive prefix sums.
+ * Errors: INVALID_ARG for a null required pointer, G without dg_scalar, a
+ * sink without dsink, a size < 1, HQ % H != 0, bad cu_seqlens arguments,
+ * misalignment, a short workspace; UNSUPPORTED for K or V not in {64, 128}
+ * or another dtype; LAUNCH on a failed launch. */
+size_t wall_attn_bwd_workspace_size(int64_t B, int64_t T, int64_t HQ, int64_t K, int64_t num_seqs);
+
+wall_status_t wall_attn_bwd(const void *q, const void *k, const void *v, wall_dtype_t dtype,
+                            const float *P, const float *G, const float *sink_bias,
+                            const void *o, const float *lse, const void *dout,
+                            void *dq, void *dk, void *dv, void *dg, void *dg_scalar,
+                            wall_dtype_t g_dtype, float *dsink,
+                            int64_t B, int64_t T, int64_t HQ, int64_t H, int64_t K, int64_t V,
+                            float scale, int64_t window_size,
+                            const int32_t *cu_seqlens, int64_t num_seqs, int64_t max_seqlen,
+                            void *workspace, size_t workspace_bytes,
+                            hipStream_t stream);
+
 /* ------------------------------------------------------------------ decode cache
  *
  * The README's build_wall_kv_cache (section "Decode (cached generation)"):

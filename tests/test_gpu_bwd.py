@@ -1,0 +1,108 @@
+"""GPU parity of the backward (wall_attn_bwd through the C ABI, and the
+autograd path of wall_attn) against the fp64 oracle's backward.
+
+Each gradient is compared as a whole tensor, relative to its own size:
+max |d| <= tol_max * max|ref| and RMS(d) <= tol_rms * RMS(ref).  bf16 inputs
+are widened to float32 in the kernels; the gradients are rounded once to
+bf16 (relative 2^-9) and the products carry the forward's bf16-rounded o
+and the float32 lse, so bf16 is held to 3e-2 / 1e-2 and float32 to 1e-4 /
+1e-5.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import channel_decay_softmax_amd as wall
+import oracle
+from wall_inputs import make_inputs
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+TOL = {"bfloat16": (3e-2, 1e-2), "float32": (1e-4, 1e-5)}
+
+
+def say(msg):
+    print(f"[gpu] {msg}", flush=True)
+
+
+def f64(t):
+    return None if t is None else t.detach().float().cpu().double().numpy()
+
+
+CASES = [
+    dict(wl="long_bf16", T=300, HQ=4, H=2, K=128, V=128),
+    dict(wl="tiny_fp32", B=2, T=200, HQ=2, H=1, K=64, V=64),
+    dict(wl="options_bf16", B=2, T=257, HQ=4, H=2, K=128, V=64, window=50),
+    dict(wl="varlen_bf16", T=250, HQ=2, H=1, K=64, V=128, nseq=None, cu=[0, 100, 100, 101, 250]),
+    dict(wl="gqa_bf16", B=1, T=190, HQ=4, H=2, K=64, V=64, dtype="float32"),
+]
+
+
+def case_id(c):
+    return "-".join(f"{k}{v}" for k, v in c.items() if k != "cu")
+
+
+@pytest.mark.parametrize("c", CASES, ids=case_id)
+def test_backward_parity(c):
+    over = {k: v for k, v in c.items() if k not in ("wl", "cu")}
+    inp = make_inputs(c["wl"], **over)
+    if c.get("cu") is not None:
+        inp.cu_seqlens = torch.tensor(c["cu"], dtype=torch.int32)
+    B, T, HQ, K = inp.q.shape
+    V = inp.v.shape[3]
+    say(f"backward {case_id(c)} {inp.q.dtype} W={inp.window_size} gs={inp.g_scalar is not None} "
+        f"sink={inp.sink_bias is not None} varlen={inp.cu_seqlens is not None}")
+    rng = np.random.default_rng(17)
+    do = torch.from_numpy(rng.standard_normal((B, T, HQ, V))).to(inp.q.dtype)
+    d = inp.to(DEV)
+    cu = d.cu_seqlens
+    maxlen = None if cu is None else int((cu[1:] - cu[:-1]).max().item())
+    P = wall.wall_prefix_scan(d.g, cu)
+    G = None if d.g_scalar is None else wall.wall_prefix_scan(d.g_scalar, cu)
+    o, lse = wall.wall_attn_fwd(d.q, d.k, d.v, P, G, d.sink_bias, d.scale, d.window_size, cu, maxlen)
+    grads = wall.wall_attn_bwd(d.q, d.k, d.v, P, o, lse, do.to(DEV), G, d.sink_bias, d.scale, d.window_size,
+                               cu, maxlen, g_dtype=d.g.dtype)
+    torch.cuda.synchronize()
+    ref = oracle.wall_attn_bwd_oracle(inp.q, inp.k, inp.v, inp.g, do, scale=inp.scale, g_scalar=inp.g_scalar,
+                                      sink_bias=inp.sink_bias, window_size=inp.window_size,
+                                      cu_seqlens=inp.cu_seqlens)
+    tmax, trms = TOL[str(inp.q.dtype).split(".")[1]]
+    for name, gg, rr in zip(["dq", "dk", "dv", "dg", "dg_scalar", "dsink"], grads, ref):
+        if rr is None:
+            assert gg is None
+            continue
+        x = f64(gg)
+        dd = np.abs(x - rr)
+        mx, rms = dd.max(), math.sqrt((dd ** 2).mean())
+        rmax, rrms = np.abs(rr).max(), math.sqrt((rr ** 2).mean())
+        say(f"  {name}: max|d|={mx:.3e} (ref max {rmax:.3e})  rms={rms:.3e} (ref rms {rrms:.3e})")
+        assert mx <= tmax * max(rmax, 1e-30) and rms <= trms * max(rrms, 1e-30), name
+    # a decay-gate entry at a sequence's first token has gradient 0
+    starts = [0] if inp.cu_seqlens is None else sorted(set(x for x in c["cu"][:-1] if x < T))
+    dg = f64(grads[3])
+    for s in starts:
+        assert not dg[:, s].any()
+
+
+def test_autograd_matches_direct_backward():
+    inp = make_inputs("options_bf16", B=1, T=160, HQ=4, H=2, K=64, V=64, window=40)
+    say("autograd wall_attn vs wall_attn_bwd")
+    d = inp.to(DEV)
+    leaves = [t.clone().requires_grad_() for t in (d.q, d.k, d.v, d.g, d.g_scalar, d.sink_bias)]
+    q, k, v, g, gs, sk = leaves
+    o = wall.wall_attn(q, k, v, g, scale=d.scale, g_scalar=gs, sink_bias=sk, window_size=d.window_size)
+    rng = np.random.default_rng(3)
+    do = torch.from_numpy(rng.standard_normal(o.shape)).to(o.dtype).to(DEV)
+    o.backward(do)
+    P = wall.wall_prefix_scan(d.g)
+    G = wall.wall_prefix_scan(d.g_scalar)
+    o2, lse2 = wall.wall_attn_fwd(d.q, d.k, d.v, P, G, d.sink_bias, d.scale, d.window_size)
+    direct = wall.wall_attn_bwd(d.q, d.k, d.v, P, o2, lse2, do, G, d.sink_bias, d.scale, d.window_size,
+                                g_dtype=d.g.dtype)
+    torch.cuda.synchronize()
+    assert torch.equal(o.detach(), o2)
+    for leaf, gd in zip(leaves, direct):
+        assert torch.equal(leaf.grad, gd)
