@@ -139,6 +139,32 @@ def test_decode_rejects_unsupported_shapes(kw):
     assert decode(**kw) == UNSUPPORTED
 
 
+def bwd(q=FAKE, k=FAKE, v=FAKE, dtype=B.WALL_BF16, Pp=FAKE, G=None, sink=None, o=FAKE, lse=FAKE, do=FAKE,
+        dq=FAKE, dk=FAKE, dv=FAKE, dg=FAKE, dgs=None, gdt=B.WALL_BF16, dsink=None, b=1, t=256, hq=4, h=2,
+        kk=128, vv=128, window=0, cu=None, nseq=0, maxlen=0, ws=FAKE, wsb=None):
+    L = wall.lib()
+    if wsb is None:
+        wsb = L.wall_attn_bwd_workspace_size(b, t, hq, kk, nseq)
+    return L.wall_attn_bwd(P(q), P(k), P(v), dtype, P(Pp), P(G), P(sink), P(o), P(lse), P(do), P(dq), P(dk),
+                           P(dv), P(dg), P(dgs), gdt, P(dsink), b, t, hq, h, kk, vv, 0.088, window, P(cu), nseq,
+                           maxlen, P(ws), wsb, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(q=None), dict(k=None), dict(v=None), dict(Pp=None), dict(o=None), dict(lse=None), dict(do=None),
+    dict(dq=None), dict(dk=None), dict(dv=None), dict(dg=None), dict(ws=None), dict(G=FAKE),
+    dict(sink=FAKE), dict(b=0), dict(t=0), dict(hq=6, h=4), dict(cu=FAKE, nseq=2, b=2, maxlen=128),
+    dict(cu=FAKE, nseq=2, maxlen=0), dict(q=FAKE + 2), dict(dg=FAKE + 4), dict(ws=FAKE + 16), dict(wsb=1024),
+])
+def test_bwd_rejects_invalid_arguments(kw):
+    assert bwd(**kw) == INVALID
+
+
+@pytest.mark.parametrize("kw", [dict(kk=96), dict(vv=32), dict(dtype=5), dict(gdt=3)])
+def test_bwd_rejects_unsupported_shapes(kw):
+    assert bwd(**kw) == UNSUPPORTED
+
+
 def test_workspace_sizes():
     L = wall.lib()
     assert L.wall_prefix_scan_workspace_size(0, 10, 10) == 0
