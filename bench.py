@@ -36,10 +36,12 @@ sys.path.insert(0, ROOT)
 
 METRIC = "wall_attn_fwd causal TFLOP/s and % of bf16 MFMA peak, T=8192 HQ=16 K=128"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+PEAK_F32_VALU_TFLOPS = 157.3  # MI355X vector fp32, published
 PEAK_HBM_GBS = 8000.0
 FWD_KERNEL_SOURCES = ["channel_decay_softmax_amd/csrc/wall_fwd_bf16.hip",
                       "channel_decay_softmax_amd/csrc/wall_common.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_bf16_long_bf16_traffic.json")
+BWD_METRIC = "wall_attn_bwd causal TFLOP/s (dq, dk, dv, dg), T=8192 HQ=16 K=128"
 DECODE_METRIC = "wall_attn_decode step HBM GB/s (append one token + split-KV decode), B=16 T=8192 HQ=16 K=128"
 DECODE_KERNEL_SOURCES = ["channel_decay_softmax_amd/csrc/wall_decode.hip",
                          "channel_decay_softmax_amd/csrc/wall_common.h"]
@@ -278,6 +280,111 @@ def bench_decode(args):
     print(json.dumps(rec), flush=True)
 
 
+def bwd_cpu_baseline(inp, rows, flop_per_pair):
+    """Time the fp64 backward oracle (as it stands) on the first ``rows`` tokens of
+    the workload taken as sequences of their own (every head)."""
+    import numpy as np
+
+    import oracle
+
+    oracle.build(force=False)
+    sl = slice(0, rows)
+    rng = np.random.default_rng(5)
+    do = rng.standard_normal((inp.q.shape[0], rows, inp.q.shape[2], inp.v.shape[3]))
+    t0 = time.perf_counter()
+    oracle.wall_attn_bwd_oracle(inp.q[:, sl], inp.k[:, sl], inp.v[:, sl], inp.g[:, sl], do, scale=inp.scale)
+    t = time.perf_counter() - t0
+    pairs = inp.q.shape[0] * inp.q.shape[2] * rows * (rows + 1) // 2
+    return {
+        "value": pairs * flop_per_pair / t / 1e12,
+        "unit": "TFLOP/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"the first {rows} of {inp.q.shape[1]} rows as a sequence of their own (all "
+                  f"{inp.q.shape[2]} heads), {pairs} visible pairs, {t:.1f} s fp64 backward",
+        "seconds": t,
+    }
+
+
+def bench_backward(args):
+    """The backward of the fused forward on the workload: given q, k, v, the
+    prefixes, o and lse, one step computes dq, dk, dv, dg (and dg_scalar, dsink)."""
+    import torch
+
+    import channel_decay_softmax_amd as wall
+    from wall_inputs import make_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda", 0)
+    inp = make_inputs(args.workload)
+    d = inp.to(dev)
+    B, T, HQ, K = d.q.shape
+    H, V = d.k.shape[2], d.v.shape[3]
+    lens = seq_lengths(inp)
+    pairs = visible_pairs(lens, inp.window_size) * HQ
+    flop_per_pair = 6 * K + 4 * V  # QK^T again, dO V^T, dS K, dS^T Q, P^T dO
+    flop = pairs * flop_per_pair
+    cu = d.cu_seqlens
+    maxlen = max(lens)
+    P = wall.wall_prefix_scan(d.g, cu)
+    G = None if d.g_scalar is None else wall.wall_prefix_scan(d.g_scalar, cu)
+    o, lse = wall.wall_attn_fwd(d.q, d.k, d.v, P, G, d.sink_bias, d.scale, inp.window_size, cu, maxlen)
+    rng = __import__("numpy").random.default_rng(9)
+    do = torch.from_numpy(rng.standard_normal((B, T, HQ, V))).to(d.q.dtype).to(dev)
+    nseq = 0 if cu is None else cu.numel() - 1
+    ws = torch.empty(wall.lib().wall_attn_bwd_workspace_size(B, T, HQ, K, nseq), dtype=torch.uint8, device=dev)
+
+    def step():
+        wall.wall_attn_bwd(d.q, d.k, d.v, P, o, lse, do, G, d.sink_bias, d.scale, inp.window_size, cu, maxlen,
+                           g_dtype=d.g.dtype, workspace=ws)
+
+    print(f"[bench] backward {args.workload}: B={B} T={T} HQ={HQ} H={H} K={K} V={V} {d.q.dtype} "
+          f"pairs={pairs} flop={flop:.4e}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    value = flop / (ms_step * 1e-3) / 1e12
+    print(f"[bench] backward step {ms_step:.3f} ms -> {value:.1f} TFLOP/s", file=sys.stderr, flush=True)
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the fp64 backward oracle on the host", file=sys.stderr, flush=True)
+        cpu = bwd_cpu_baseline(inp, 2048, flop_per_pair)
+    # bf16 inputs run the products on bf16 MFMA (float32 accumulation), float32
+    # inputs on the float32 vector ALUs
+    if d.q.dtype == torch.bfloat16:
+        dt, bound, peak = "bf16", "mfma", PEAK_BF16_TFLOPS
+    else:
+        dt, bound, peak = "f32", "alu", PEAK_F32_VALU_TFLOPS
+    rec = {
+        "metric": BWD_METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dt,
+        "data": "synthetic",
+        "config": {"workload": args.workload, "B": B, "T": T, "HQ": HQ, "H": H, "K": K, "V": V,
+                   "visible_pairs": pairs, "counted_flop": flop},
+        "roofline": {"kernel": "the whole backward step (dq and dk/dv products, group sum, D, scans)",
+                     "bound": bound, "achieved": round(value, 3), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(value / peak, 4), "traffic": None},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=int(os.environ.get("WORLD_SIZE", "1")))
@@ -290,6 +397,8 @@ def main():
     ap.add_argument("--workload", default="long_bf16")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward (wall_attn_bwd) of the workload instead of the forward hot path")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="run a plain device copy of this many MiB (read + write) before the "
                          "timed region, as the reference kernel for HBM byte counters")
@@ -302,6 +411,10 @@ def main():
         sys.exit(2)
     from wall_inputs import DECODE_WORKLOADS
     decode = args.workload in DECODE_WORKLOADS
+    if args.backward and not decode:
+        args.steps = 50 if args.steps is None else args.steps
+        args.warmup = 30 if args.warmup is None else args.warmup
+        return bench_backward(args)
     if args.steps is None:
         args.steps = 600 if decode else 200
     if args.warmup is None:

@@ -35,6 +35,8 @@
 // R is at most 2 and the other at most 2^(change of P over 64 rows).
 #include <float.h>
 
+#include <type_traits>
+
 #include "wall_common.h"
 
 namespace wall {
@@ -346,11 +348,31 @@ __global__ __launch_bounds__(NT) void dsink_kernel(const float *Z, float *dsink,
 }
 
 template <typename T, int K, int V>
+hipError_t run_valu(const BwdArgs &a, hipStream_t st);
+
+template <typename T, int K, int V>
 hipError_t run_bwd(const BwdArgs &a, hipStream_t st) {
     const int64_t nrows = (int64_t)a.rows * a.HQ;
     hipLaunchKernelGGL((bwd_pre_kernel<T, V>), dim3((unsigned)cdiv(nrows, NT / 16)), dim3(NT), 0, st, a, nrows);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if constexpr (std::is_same<T, __bf16>::value) {
+        e = launch_bwd_mfma(a, st);
+    } else {
+        e = run_valu<T, K, V>(a, st);
+    }
+    if (e != hipSuccess) return e;
+    if (a.dsink) {
+        hipLaunchKernelGGL(dsink_kernel, dim3((unsigned)a.HQ), dim3(NT), 0, st, a.Z, a.dsink, (int64_t)a.rows,
+                           (int)a.HQ);
+        e = hipGetLastError();
+    }
+    return e;
+}
+
+template <typename T, int K, int V>
+hipError_t run_valu(const BwdArgs &a, hipStream_t st) {
+    hipError_t e;
     const int nblk = (int)cdiv(a.max_seqlen, BB);
     constexpr size_t smem_q =
         sizeof(float) * (BB * (K + 1) + BB * (V + 1) + BS * (K + 1) + BS * (V + 1) + BB * (BS + 1) + BS + K);
@@ -368,14 +390,7 @@ hipError_t run_bwd(const BwdArgs &a, hipStream_t st) {
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_dkdv_kernel<T, K, V>), dim3((unsigned)((int64_t)a.H * a.nseg * nblk)), dim3(NT), smem_k,
                        st, a, nblk);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    if (a.dsink) {
-        hipLaunchKernelGGL(dsink_kernel, dim3((unsigned)a.HQ), dim3(NT), 0, st, a.Z, a.dsink, (int64_t)a.rows,
-                           (int)a.HQ);
-        e = hipGetLastError();
-    }
-    return e;
+    return hipGetLastError();
 }
 
 template <typename T>

@@ -1,0 +1,541 @@
+// wall_bwd_mfma.hip -- backward of the causal Wall Attention forward for bf16
+// inputs on the gfx950 matrix cores (v_mfma_f32_32x32x16_bf16, fp32
+// accumulation).  Same gradients as the float32 kernels of wall_bwd.hip:
+//     dS_ij = A_ij (do_i . v_j - D_i),  dv_j = sum_i A_ij do_i,
+//     dq_i  = scale 2^(P_i - R) sum_j dS_ij k~_j,
+//     dk_j  = ln2 2^(R - P_j) sum_i dS_ij q~_i            (per query head),
+// with q~ = q scale log2e 2^(P - R) and k~ = k 2^(R - P) rounded to bf16, A and
+// dS rounded to bf16 as MFMA operands, everything else in float32.
+//
+// Work decomposition.  A block owns 128 rows of one (query head, sequence):
+// keys in the dk/dv kernel, queries in the dq kernel; its 4 waves own 32 rows
+// each (one MFMA block).  The block anchors every channel at the floored
+// prefix of its middle row (row 64, or the last row of a shorter tail), as
+// the forward anchors its 128-row tiles, so both exp2 factors of a pair stay
+// within 2^(+-change of P over 64 rows).  The other side streams through LDS
+// 32 rows at a time, each tile both row-major (the MFMA's first operand) and
+// transposed (the second operand of the product that contracts over the
+// streamed rows); the next tile's global loads are issued before the current
+// tile's products.  The block's own rows stay in registers as second
+// operands.
+//
+// dk/dv (per key block, queries from the block's first key on):
+//   S  = q~ k~^T,  dP = do v^T   (32 streamed queries x the wave's 32 keys);
+//   A, dS in-lane;  dv += A^T do,  dk += dS^T q~.
+// dq (per query block, keys up to the block's last query):
+//   S^T = k~ q~^T, dP^T = v do^T (32 streamed keys x the wave's 32 queries);
+//   dq += dS k~.
+// The streamed rows of the first products are fed in the order that swaps
+// bits 2 and 3 of the row index, so each lane's 16 accumulator registers hold
+// two runs of 8 consecutive streamed rows: exactly the k-slots the lane
+// supplies to the second product, with no data exchange between lanes.
+//
+// X.  The gate gradient is a suffix sum of X_t = q_t (.) dq_t - k_t (.) dk_t^(hq),
+// whose terms cancel pair by pair: the pair (i, j) adds dS_ij q~_i k~_j to X_i
+// and takes it from X_j.  The kernels therefore form both sides from the
+// same bf16 q~ and k~ the products use, ln2 q~_i (.) sum_j dS_ij k~_j and
+// ln2 k~_j (.) sum_i dS_ij q~_i (the anchors of the two kernels differ by
+// integers, which moves q~ and k~ by exact powers of two), so the rounding of
+// the operands cancels in the sums as the exact terms do.  Built from the
+// unrounded q and k instead, each pair would leave a residue of the operand
+// rounding (2^-9 relative), and over a long sequence these residues add up
+// to several times the error of dq and dk themselves.
+//
+// A block handles a single query head, so dk and dv leave as float32 per
+// query head partials, summed over the heads of a kv group by
+// bwd_reduce_kernel.  The dk/dv kernel also subtracts k (.) dk^(hq) and the
+// column sums of dS from the X and Y rows the dq kernel wrote (it runs after
+// it on the same stream).
+#include <float.h>
+
+#include "wall_common.h"
+
+namespace wall {
+namespace {
+
+constexpr int BR = 128;      // rows per block
+constexpr int BT = 32;       // streamed rows per tile
+constexpr int NW = 4;        // waves per block
+constexpr int NTH = NW * 64;
+constexpr int TP = BT + 8;   // transposed tile row pitch (elements): 80 bytes
+
+__device__ inline float clamp2(float e) { return exp2f(fminf(fmaxf(e, EXP2_LO), EXP2_HI)); }
+__device__ inline int swap23(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
+
+__device__ inline f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ inline bf16x8 lds8(const __bf16 *p) { return *reinterpret_cast<const bf16x8 *>(p); }
+
+__device__ inline f32x8 to_f32(uint4 raw) {
+    return __builtin_convertvector(__builtin_bit_cast(bf16x8, raw), f32x8);
+}
+
+// Block index -> (query head, sequence, row block).  The row block is the
+// slowest index and runs from the heaviest end (most partner rows) down, so
+// the longest blocks start first; consecutive ids are consecutive (head,
+// sequence) pairs, which with HQ * nseg a multiple of 8 keeps each pair on one
+// XCD.
+struct BlockPos {
+    int hq, seg, rb;
+};
+__device__ inline BlockPos block_pos(const BwdArgs &a, int nblk, bool heavy_first_low) {
+    const int hs_n = a.HQ * a.nseg;
+    const int rank = blockIdx.x / hs_n, hs = blockIdx.x % hs_n;
+    BlockPos p;
+    p.hq = hs % a.HQ;
+    p.seg = hs / a.HQ;
+    p.rb = heavy_first_low ? rank : nblk - 1 - rank;
+    return p;
+}
+
+// ---------------------------------------------------------------- dk, dv
+template <int K, int V, bool HAS_G>
+__global__ __launch_bounds__(NTH) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
+    constexpr int RPK = K + 8, RPV = V + 8;
+    constexpr int CK = BT * K / 8, CV = BT * V / 8;  // 8-element chunks per tile
+    constexpr int UK = CK / NTH, UV = CV / NTH;
+    static_assert(CK % NTH == 0 && CV % NTH == 0, "tile chunks");
+    __shared__ __attribute__((aligned(16))) __bf16 sQ[BT * RPK];   // q~ rows
+    __shared__ __attribute__((aligned(16))) __bf16 sQT[K * TP];    // q~ transposed
+    __shared__ __attribute__((aligned(16))) __bf16 sO[BT * RPV];   // do rows
+    __shared__ __attribute__((aligned(16))) __bf16 sOT[V * TP];    // do transposed
+    __shared__ __attribute__((aligned(16))) float sL[BT];
+    __shared__ __attribute__((aligned(16))) float sD[BT];
+    __shared__ __attribute__((aligned(16))) float sGq[BT];
+    __shared__ float sR[K];
+
+    const BlockPos bp = block_pos(a, nblk, true);
+    const SegInfo sg = a.seg[bp.seg];
+    const int hq = bp.hq, j0 = bp.rb * BR;
+    if (j0 >= sg.len) return;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, hl = lane >> 5;
+    const int64_t HQ = a.HQ;
+    const int h = hq / (a.HQ / a.H);
+    const int len = sg.len, jn = min(BR, len - j0);
+    const int64_t s0 = sg.start;
+    const __bf16 *qg = static_cast<const __bf16 *>(a.q);
+    const __bf16 *kg = static_cast<const __bf16 *>(a.k);
+    const __bf16 *vg = static_cast<const __bf16 *>(a.v);
+    const __bf16 *dog = static_cast<const __bf16 *>(a.dout);
+
+    if (tid < K) sR[tid] = floorf(a.P[(s0 + j0 + min(ANCHOR_ROW, jn - 1)) * HQ * K + hq * K + tid]);
+    __syncthreads();
+
+    // the wave's keys as second operands: k~ and v rows of key jw + l32
+    const int jw = j0 + 32 * w, j = jw + l32;
+    const bool jok = j < len;
+    const int64_t tj = s0 + (jok ? j : 0);
+    bf16x8 kop[K / 16], vop[V / 16];
+#pragma unroll
+    for (int s = 0; s < K / 16; ++s) {
+        const int ch = 16 * s + 8 * hl;
+        f32x8 x = 0.f;
+        if (jok) {
+            const f32x8 kk = to_f32(*reinterpret_cast<const uint4 *>(kg + (tj * a.H + h) * K + ch));
+            const float *pp = a.P + (tj * HQ + hq) * K + ch;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = kk[e] * clamp2(sR[ch + e] - pp[e]);
+        }
+        kop[s] = __builtin_convertvector(x, bf16x8);
+    }
+#pragma unroll
+    for (int s = 0; s < V / 16; ++s) {
+        const int ch = 16 * s + 8 * hl;
+        uint4 raw = {0, 0, 0, 0};
+        if (jok) raw = *reinterpret_cast<const uint4 *>(vg + (tj * a.H + h) * V + ch);
+        vop[s] = __builtin_bit_cast(bf16x8, raw);
+    }
+    const float gj = (HAS_G && jok) ? a.G[tj * HQ + hq] : 0.f;
+
+    f32x16 dk[K / 32], dv[V / 32];
+#pragma unroll
+    for (int n = 0; n < K / 32; ++n) dk[n] = 0.f;
+#pragma unroll
+    for (int n = 0; n < V / 32; ++n) dv[n] = 0.f;
+    float colsum = 0.f;
+
+    const int qend = a.window > 0 ? min(len, j0 + jn - 1 + a.window) : len;
+    const int wlast = min(jw + 31, len - 1);  // the wave's last valid key
+
+    // prefetch registers for one tile
+    uint4 qraw[UK], oraw[UV];
+    f32x8 praw[UK];
+    float il = 0.f, id = 0.f, ig = 0.f;
+    auto load_tile = [&](int q0) {
+#pragma unroll
+        for (int u = 0; u < UK; ++u) {
+            const int c = tid + NTH * u, r = c / (K / 8), ch = 8 * (c % (K / 8)), i = q0 + r;
+            qraw[u] = {0, 0, 0, 0};
+            praw[u] = 0.f;
+            if (i < len) {
+                const int64_t t = (s0 + i) * HQ + hq;
+                qraw[u] = *reinterpret_cast<const uint4 *>(qg + t * K + ch);
+                const f32x4 *pp = reinterpret_cast<const f32x4 *>(a.P + t * K + ch);
+                const f32x4 p0 = pp[0], p1 = pp[1];
+                praw[u] = f32x8{p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < UV; ++u) {
+            const int c = tid + NTH * u, r = c / (V / 8), ch = 8 * (c % (V / 8)), i = q0 + r;
+            oraw[u] = {0, 0, 0, 0};
+            if (i < len) oraw[u] = *reinterpret_cast<const uint4 *>(dog + ((s0 + i) * HQ + hq) * V + ch);
+        }
+        if (tid < BT) {
+            const int i = q0 + tid;
+            il = id = ig = 0.f;
+            if (i < len) {
+                const int64_t t = (s0 + i) * HQ + hq;
+                il = a.lse[t] * LOG2E;
+                id = a.D[t];
+                if (HAS_G) ig = a.G[t];
+            }
+        }
+    };
+    auto store_tile = [&]() {
+#pragma unroll
+        for (int u = 0; u < UK; ++u) {
+            const int c = tid + NTH * u, r = c / (K / 8), ch = 8 * (c % (K / 8));
+            const f32x8 qq = to_f32(qraw[u]);
+            f32x8 x;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = qq[e] * a.qscale * clamp2(praw[u][e] - sR[ch + e]);
+            const bf16x8 b = __builtin_convertvector(x, bf16x8);
+            *reinterpret_cast<bf16x8 *>(sQ + r * RPK + ch) = b;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sQT[(ch + e) * TP + r] = b[e];
+        }
+#pragma unroll
+        for (int u = 0; u < UV; ++u) {
+            const int c = tid + NTH * u, r = c / (V / 8), ch = 8 * (c % (V / 8));
+            const bf16x8 b = __builtin_bit_cast(bf16x8, oraw[u]);
+            *reinterpret_cast<bf16x8 *>(sO + r * RPV + ch) = b;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sOT[(ch + e) * TP + r] = b[e];
+        }
+        if (tid < BT) {
+            sL[tid] = il;
+            sD[tid] = id;
+            sGq[tid] = ig;
+        }
+    };
+
+    load_tile(j0);
+    for (int q0 = j0; q0 < qend; q0 += BT) {
+        __syncthreads();  // every wave is done with the previous tile
+        store_tile();
+        __syncthreads();
+        if (q0 + BT < qend) load_tile(q0 + BT);
+        // does the tile hold a visible pair for this wave's keys?
+        bool act = jw < len && q0 + BT - 1 >= jw;
+        if (a.window > 0) act = act && q0 <= wlast + a.window - 1;
+        if (!act) continue;
+
+        f32x16 S = 0.f, dP = 0.f;
+        const int qrow = swap23(l32);
+#pragma unroll
+        for (int s = 0; s < K / 16; ++s) S = mfma(lds8(sQ + qrow * RPK + 16 * s + 8 * hl), kop[s], S);
+#pragma unroll
+        for (int s = 0; s < V / 16; ++s) dP = mfma(lds8(sO + qrow * RPV + 16 * s + 8 * hl), vop[s], dP);
+
+        bf16x8 pb[2], db[2];
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const int qi0 = 16 * c + 8 * hl;
+            const f32x4 *L4 = reinterpret_cast<const f32x4 *>(sL + qi0);
+            const f32x4 *D4 = reinterpret_cast<const f32x4 *>(sD + qi0);
+            const f32x4 *G4 = reinterpret_cast<const f32x4 *>(sGq + qi0);
+            f32x8 pv, dv8;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int i = q0 + qi0 + e;
+                const float lse2 = L4[e / 4][e % 4], Di = D4[e / 4][e % 4];
+                const float Gi = HAS_G ? G4[e / 4][e % 4] : 0.f;
+                bool vis = jok && i >= j && i < len;
+                if (a.window > 0) vis = vis && i - j < a.window;
+                const float p = vis ? exp2f(S[8 * c + e] + Gi - gj - lse2) : 0.f;
+                const float ds = p * (dP[8 * c + e] - Di);
+                colsum += ds;
+                pv[e] = p;
+                dv8[e] = ds;
+            }
+            pb[c] = __builtin_convertvector(pv, bf16x8);
+            db[c] = __builtin_convertvector(dv8, bf16x8);
+        }
+#pragma unroll
+        for (int n = 0; n < V / 32; ++n)
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+                dv[n] = mfma(pb[c], lds8(sOT + (32 * n + l32) * TP + 16 * c + 8 * hl), dv[n]);
+#pragma unroll
+        for (int n = 0; n < K / 32; ++n)
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+                dk[n] = mfma(db[c], lds8(sQT + (32 * n + l32) * TP + 16 * c + 8 * hl), dk[n]);
+    }
+
+    if (jw >= len) return;
+    colsum += __shfl_xor(colsum, 32);
+    if (hl == 0 && jok) a.Y[tj * HQ + hq] -= colsum;
+    // accumulator register r of lane (l32, hl): key jw + 8(r/4) + 4hl + r%4, channel 32n + l32
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int jr = jw + 8 * (r / 4) + 4 * hl + (r % 4);
+        if (jr >= len) continue;
+        const int64_t t = s0 + jr;
+#pragma unroll
+        for (int n = 0; n < K / 32; ++n) {
+            const int ch = 32 * n + l32;
+            const int64_t ix = (t * HQ + hq) * K + ch;
+            const float f = clamp2(sR[ch] - a.P[ix]);
+            a.dkp[ix] = LN2 * f * dk[n][r];
+            // k (.) dk^(hq) from the bf16 k~ the dq products used (see the X note above)
+            const float kt = (float)(__bf16)((float)kg[(t * a.H + h) * K + ch] * f);
+            a.X[ix] -= LN2 * kt * dk[n][r];
+        }
+#pragma unroll
+        for (int n = 0; n < V / 32; ++n) a.dvp[(t * HQ + hq) * V + 32 * n + l32] = dv[n][r];
+    }
+}
+
+// ---------------------------------------------------------------- dq
+template <int K, int V, bool HAS_G>
+__global__ __launch_bounds__(NTH) void bwd_dq_mfma(BwdArgs a, int nblk) {
+    constexpr int RPK = K + 8, RPV = V + 8;
+    constexpr int CK = BT * K / 8, CV = BT * V / 8;
+    constexpr int UK = CK / NTH, UV = CV / NTH;
+    static_assert(CK % NTH == 0 && CV % NTH == 0, "tile chunks");
+    __shared__ __attribute__((aligned(16))) __bf16 sK[BT * RPK];   // k~ rows
+    __shared__ __attribute__((aligned(16))) __bf16 sKT[K * TP];    // k~ transposed
+    __shared__ __attribute__((aligned(16))) __bf16 sV[BT * RPV];   // v rows
+    __shared__ __attribute__((aligned(16))) float sGk[BT];
+    __shared__ float sR[K];
+
+    const BlockPos bp = block_pos(a, nblk, false);
+    const SegInfo sg = a.seg[bp.seg];
+    const int hq = bp.hq, i0 = bp.rb * BR;
+    if (i0 >= sg.len) return;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, hl = lane >> 5;
+    const int64_t HQ = a.HQ;
+    const int h = hq / (a.HQ / a.H);
+    const int len = sg.len, in_ = min(BR, len - i0);
+    const int64_t s0 = sg.start;
+    const __bf16 *qg = static_cast<const __bf16 *>(a.q);
+    const __bf16 *kg = static_cast<const __bf16 *>(a.k);
+    const __bf16 *vg = static_cast<const __bf16 *>(a.v);
+    const __bf16 *dog = static_cast<const __bf16 *>(a.dout);
+
+    if (tid < K) sR[tid] = floorf(a.P[(s0 + i0 + min(ANCHOR_ROW, in_ - 1)) * HQ * K + hq * K + tid]);
+    __syncthreads();
+
+    // the wave's queries as second operands
+    const int iw = i0 + 32 * w, i = iw + l32;
+    const bool iok = i < len;
+    const int64_t ti = s0 + (iok ? i : 0);
+    bf16x8 qop[K / 16], oop[V / 16];
+#pragma unroll
+    for (int s = 0; s < K / 16; ++s) {
+        const int ch = 16 * s + 8 * hl;
+        f32x8 x = 0.f;
+        if (iok) {
+            const f32x8 qq = to_f32(*reinterpret_cast<const uint4 *>(qg + (ti * HQ + hq) * K + ch));
+            const float *pp = a.P + (ti * HQ + hq) * K + ch;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = qq[e] * a.qscale * clamp2(pp[e] - sR[ch + e]);
+        }
+        qop[s] = __builtin_convertvector(x, bf16x8);
+    }
+#pragma unroll
+    for (int s = 0; s < V / 16; ++s) {
+        const int ch = 16 * s + 8 * hl;
+        uint4 raw = {0, 0, 0, 0};
+        if (iok) raw = *reinterpret_cast<const uint4 *>(dog + (ti * HQ + hq) * V + ch);
+        oop[s] = __builtin_bit_cast(bf16x8, raw);
+    }
+    const float lse2 = iok ? a.lse[ti * HQ + hq] * LOG2E : 0.f;
+    const float Di = iok ? a.D[ti * HQ + hq] : 0.f;
+    const float Gi = (HAS_G && iok) ? a.G[ti * HQ + hq] : 0.f;
+
+    f32x16 dq[K / 32];
+#pragma unroll
+    for (int n = 0; n < K / 32; ++n) dq[n] = 0.f;
+    float rowsum = 0.f;
+
+    const int ilast = i0 + in_ - 1;
+    const int klo = a.window > 0 ? max(0, i0 - a.window + 1) / BT * BT : 0;
+    const int wlast = min(iw + 31, len - 1);
+
+    uint4 kraw[UK], vraw[UV];
+    f32x8 praw[UK];
+    float kgv = 0.f;
+    auto load_tile = [&](int k0) {
+#pragma unroll
+        for (int u = 0; u < UK; ++u) {
+            const int c = tid + NTH * u, r = c / (K / 8), ch = 8 * (c % (K / 8)), jj = k0 + r;
+            kraw[u] = {0, 0, 0, 0};
+            praw[u] = 0.f;
+            if (jj < len) {
+                const int64_t t = s0 + jj;
+                kraw[u] = *reinterpret_cast<const uint4 *>(kg + (t * a.H + h) * K + ch);
+                const f32x4 *pp = reinterpret_cast<const f32x4 *>(a.P + (t * HQ + hq) * K + ch);
+                const f32x4 p0 = pp[0], p1 = pp[1];
+                praw[u] = f32x8{p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < UV; ++u) {
+            const int c = tid + NTH * u, r = c / (V / 8), ch = 8 * (c % (V / 8)), jj = k0 + r;
+            vraw[u] = {0, 0, 0, 0};
+            if (jj < len) vraw[u] = *reinterpret_cast<const uint4 *>(vg + ((s0 + jj) * a.H + h) * V + ch);
+        }
+        if (HAS_G && tid < BT) {
+            const int jj = k0 + tid;
+            kgv = jj < len ? a.G[(s0 + jj) * HQ + hq] : 0.f;
+        }
+    };
+    auto store_tile = [&]() {
+#pragma unroll
+        for (int u = 0; u < UK; ++u) {
+            const int c = tid + NTH * u, r = c / (K / 8), ch = 8 * (c % (K / 8));
+            const f32x8 kk = to_f32(kraw[u]);
+            f32x8 x;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = kk[e] * clamp2(sR[ch + e] - praw[u][e]);
+            const bf16x8 b = __builtin_convertvector(x, bf16x8);
+            *reinterpret_cast<bf16x8 *>(sK + r * RPK + ch) = b;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sKT[(ch + e) * TP + r] = b[e];
+        }
+#pragma unroll
+        for (int u = 0; u < UV; ++u) {
+            const int c = tid + NTH * u, r = c / (V / 8), ch = 8 * (c % (V / 8));
+            *reinterpret_cast<uint4 *>(sV + r * RPV + ch) = vraw[u];
+        }
+        if (HAS_G && tid < BT) sGk[tid] = kgv;
+    };
+
+    load_tile(klo);
+    for (int k0 = klo; k0 <= ilast; k0 += BT) {
+        __syncthreads();
+        store_tile();
+        __syncthreads();
+        if (k0 + BT <= ilast) load_tile(k0 + BT);
+        bool act = iw < len && k0 <= wlast;
+        if (a.window > 0) act = act && k0 + BT - 1 >= iw - a.window + 1;
+        if (!act) continue;
+
+        f32x16 S = 0.f, dP = 0.f;
+        const int krow = swap23(l32);
+#pragma unroll
+        for (int s = 0; s < K / 16; ++s) S = mfma(lds8(sK + krow * RPK + 16 * s + 8 * hl), qop[s], S);
+#pragma unroll
+        for (int s = 0; s < V / 16; ++s) dP = mfma(lds8(sV + krow * RPV + 16 * s + 8 * hl), oop[s], dP);
+
+        bf16x8 db[2];
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const int kj0 = 16 * c + 8 * hl;
+            const f32x4 *G4 = reinterpret_cast<const f32x4 *>(sGk + kj0);
+            f32x8 d8;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int jj = k0 + kj0 + e;
+                const float Gj = HAS_G ? G4[e / 4][e % 4] : 0.f;
+                bool vis = iok && jj <= i;
+                if (a.window > 0) vis = vis && i - jj < a.window;
+                const float p = vis ? exp2f(S[8 * c + e] + Gi - Gj - lse2) : 0.f;
+                const float ds = p * (dP[8 * c + e] - Di);
+                rowsum += ds;
+                d8[e] = ds;
+            }
+            db[c] = __builtin_convertvector(d8, bf16x8);
+        }
+#pragma unroll
+        for (int n = 0; n < K / 32; ++n)
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+                dq[n] = mfma(db[c], lds8(sKT + (32 * n + l32) * TP + 16 * c + 8 * hl), dq[n]);
+    }
+
+    if (iw >= len) return;
+    rowsum += __shfl_xor(rowsum, 32);
+    if (hl == 0 && iok) {
+        a.Y[ti * HQ + hq] = rowsum;
+        a.Z[ti * HQ + hq] = a.sink ? -exp2f(a.sink[hq] * LOG2E - lse2) * Di : 0.f;
+    }
+    __bf16 *dqg = static_cast<__bf16 *>(a.dq);
+    // accumulator register r of lane (l32, hl): query iw + 8(r/4) + 4hl + r%4, channel 32n + l32
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int ir = iw + 8 * (r / 4) + 4 * hl + (r % 4);
+        if (ir >= len) continue;
+        const int64_t t = s0 + ir;
+#pragma unroll
+        for (int n = 0; n < K / 32; ++n) {
+            const int ch = 32 * n + l32;
+            const int64_t ix = (t * HQ + hq) * K + ch;
+            const float f = clamp2(a.P[ix] - sR[ch]);
+            dqg[ix] = (__bf16)(a.scale * f * dq[n][r]);
+            const float qt = (float)(__bf16)((float)qg[ix] * a.qscale * f);
+            a.X[ix] = LN2 * qt * dq[n][r];
+        }
+    }
+}
+
+// ---------------------------------------------------------------- dk, dv: sum over the kv group
+template <int K, int V>
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdArgs a, int64_t nrow_h) {
+    // one (row, kv head) per 32 lanes; K/32 and V/32 channels per lane
+    const int64_t rh = (int64_t)blockIdx.x * 8 + threadIdx.x / 32;
+    if (rh >= nrow_h) return;
+    const int l = threadIdx.x % 32;
+    const int64_t t = rh / a.H;
+    const int h = (int)(rh % a.H), grp = a.HQ / a.H;
+    __bf16 *dkg = static_cast<__bf16 *>(a.dk) + rh * K;
+    __bf16 *dvg = static_cast<__bf16 *>(a.dv) + rh * V;
+#pragma unroll
+    for (int n = l; n < K; n += 32) {
+        float s = 0.f;
+        for (int g = 0; g < grp; ++g) s += a.dkp[(t * a.HQ + h * grp + g) * K + n];
+        dkg[n] = (__bf16)s;
+    }
+#pragma unroll
+    for (int n = l; n < V; n += 32) {
+        float s = 0.f;
+        for (int g = 0; g < grp; ++g) s += a.dvp[(t * a.HQ + h * grp + g) * V + n];
+        dvg[n] = (__bf16)s;
+    }
+}
+
+template <int K, int V, bool HAS_G>
+hipError_t run(const BwdArgs &a, hipStream_t st) {
+    const int nblk = (int)cdiv(a.max_seqlen, BR);
+    const unsigned nb = (unsigned)((int64_t)a.HQ * a.nseg * nblk);
+    hipLaunchKernelGGL((bwd_dq_mfma<K, V, HAS_G>), dim3(nb), dim3(NTH), 0, st, a, nblk);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_dkdv_mfma<K, V, HAS_G>), dim3(nb), dim3(NTH), 0, st, a, nblk);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t nrow_h = (int64_t)a.rows * a.H;
+    hipLaunchKernelGGL((bwd_reduce_kernel<K, V>), dim3((unsigned)cdiv(nrow_h, 8)), dim3(256), 0, st, a, nrow_h);
+    return hipGetLastError();
+}
+
+template <int K, int V>
+hipError_t run_g(const BwdArgs &a, hipStream_t st) {
+    return a.G ? run<K, V, true>(a, st) : run<K, V, false>(a, st);
+}
+
+}  // namespace
+
+hipError_t launch_bwd_mfma(const BwdArgs &a, hipStream_t st) {
+    if (a.K == 64 && a.V == 64) return run_g<64, 64>(a, st);
+    if (a.K == 64 && a.V == 128) return run_g<64, 128>(a, st);
+    if (a.K == 128 && a.V == 64) return run_g<128, 64>(a, st);
+    return run_g<128, 128>(a, st);
+}
+
+}  // namespace wall

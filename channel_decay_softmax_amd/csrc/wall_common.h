@@ -165,15 +165,19 @@ struct BwdArgs {
     void *dq, *dk, *dv;                // in dtype
     float *dsink;                      // [HQ] or null
     float *D, *X, *Y, *Z;              // workspace: do.o; q.dq - k.dk per head; dS row - column sums; sink terms
+    float *dkp, *dvp;                  // workspace: per query head dk [rows, HQ, K] and dv [rows, HQ, V] (bf16 path)
     const SegInfo *seg;
     int32_t nseg, max_seqlen, rows, HQ, H, K, V, window;
     float scale, qscale;               // scale, scale * log2(e)
 };
 hipError_t launch_bwd_seg(SegInfo *seg, const int32_t *cu, int64_t nseg, int64_t T, hipStream_t st);
 hipError_t launch_bwd(const BwdArgs &a, bool bf16, hipStream_t st);
+hipError_t launch_bwd_mfma(const BwdArgs &a, hipStream_t st);  // the dq, dk/dv and group-sum kernels, bf16
+// Largest value channel count the backward takes (sizes the dv partials).
+constexpr int64_t BWD_MAX_V = 128;
 
 struct BwdLayout {
-    size_t off_seg, off_D, off_X, off_Y, off_Z, off_scan, total;
+    size_t off_seg, off_D, off_X, off_Y, off_Z, off_part, off_scan, total;
 };
 inline BwdLayout bwd_layout(int64_t B, int64_t T, int64_t HQ, int64_t K, int64_t nseg) {
     BwdLayout L;
@@ -189,6 +193,8 @@ inline BwdLayout bwd_layout(int64_t B, int64_t T, int64_t HQ, int64_t K, int64_t
     o = align_up(o + sizeof(float) * rows * HQ, 256);
     L.off_Z = o;
     o = align_up(o + sizeof(float) * rows * HQ, 256);
+    L.off_part = o;
+    o = align_up(o + sizeof(float) * rows * HQ * (K + BWD_MAX_V), 256);
     L.off_scan = o;
     o = align_up(o + scan_layout(B, T, HQ * K).total, 256);
     L.total = o;
