@@ -42,7 +42,7 @@ FWD_KERNEL_SOURCES = ["channel_decay_softmax_amd/csrc/wall_fwd_bf16.hip",
                       "channel_decay_softmax_amd/csrc/wall_common.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_bf16_long_bf16_traffic.json")
 BWD_METRIC = "wall_attn_bwd causal TFLOP/s (dq, dk, dv, dg), T=8192 HQ=16 K=128"
-DECODE_METRIC = "wall_attn_decode step HBM GB/s (append one token + split-KV decode), B=16 T=8192 HQ=16 K=128"
+DECODE_METRIC = "wall_attn_decode streaming step HBM GB/s (prefix and cache append of one token, split-KV decode), B=16 T=8192 HQ=16 K=128"
 DECODE_KERNEL_SOURCES = ["channel_decay_softmax_amd/csrc/wall_decode.hip",
                          "channel_decay_softmax_amd/csrc/wall_common.h"]
 DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_decode_bf16_traffic.json")
@@ -144,12 +144,14 @@ def cpu_baseline(inp, flop_per_pair, target_s):
 
 
 def decode_bytes(B, T, HQ, H, K, V, C, es):
-    """Algorithmic HBM bytes of one decode call and of one one-row cache append."""
+    """Algorithmic HBM bytes of one decode call and of one row's append (prefix
+    row and cache row)."""
     nc = -(-T // C)
     dec = (B * T * HQ * K * es + B * T * H * V * es + B * nc * HQ * K * 4   # k_tilde, v, anchors
            + B * HQ * K * es + B * HQ * K * 4 + B * HQ * V * es + B * HQ * 4)  # q, p_curr, o, lse
     opens = (T - 1) % C == 0
     app = B * H * K * es + B * HQ * K * 4 + B * HQ * K * es + B * HQ * K * 4  # k, P, k_tilde row; anchor
+    app += B * HQ * K * es + 2 * B * HQ * K * 4  # the prefix row: g, the previous P row, the new P row
     return dec, app, opens
 
 
@@ -184,8 +186,9 @@ def decode_cpu_baseline(inp, nseq, es):
 
 
 def bench_decode(args):
-    """One decode step of a serving loop: append the newest token's row to the
-    anchored key cache, then the split-KV decode of every sequence's newest query."""
+    """One step of the streaming decode loop: the newest token's log2 prefix from
+    the previous row's, its row of the anchored key cache, then the split-KV
+    decode of every sequence's newest query."""
     import torch
 
     import channel_decay_softmax_amd as wall
@@ -201,11 +204,12 @@ def bench_decode(args):
     T, H, V, C = d.k.shape[1], d.k.shape[2], d.v.shape[3], inp.chunk_size
     es = 2 if d.q.dtype == torch.bfloat16 else 4
     # the prefill state: the log2 prefix and the cache of the first T-1 rows
-    P = wall.wall_prefix_scan(d.g)
+    P = torch.empty((B, T, HQ, K), dtype=torch.float32, device=dev)
+    P[:, :T - 1] = wall.wall_prefix_scan(d.g[:, :T - 1].contiguous())
     kt = torch.empty((B, T, HQ, K), dtype=d.q.dtype, device=dev)
     r = torch.empty((B, -(-T // C), HQ, K), dtype=torch.float32, device=dev)
     wall.build_wall_kv_cache(d.k, P, C, k_tilde=kt, r_cache=r, t0=0, t1=T - 1)
-    pc = P[:, T - 1:T].contiguous()
+    g_new, p_prev, pc = d.g[:, T - 1:T], P[:, T - 2], P[:, T - 1:T]
     o = torch.empty((B, 1, HQ, V), dtype=d.q.dtype, device=dev)
     lse = torch.empty((B, 1, HQ), dtype=torch.float32, device=dev)
     ws = torch.empty(wall.decode_workspace_size(B, T, HQ, V), dtype=torch.uint8, device=dev)
@@ -214,6 +218,7 @@ def bench_decode(args):
     def step(marks=None):
         if marks:
             marks[0].record()
+        wall.wall_prefix_append(g_new, prev=p_prev, out=pc)
         wall.build_wall_kv_cache(d.k, P, C, k_tilde=kt, r_cache=r, t0=T - 1, t1=T)
         if marks:
             marks[1].record()

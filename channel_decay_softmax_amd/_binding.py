@@ -24,7 +24,7 @@ WALL_OK, WALL_ERR_INVALID_ARG, WALL_ERR_UNSUPPORTED, WALL_ERR_LAUNCH = 0, 1, 2, 
 #: every symbol include/wall.h declares
 EXPORTS = (
     "wall_status_string", "wall_version",
-    "wall_prefix_scan_workspace_size", "wall_prefix_scan",
+    "wall_prefix_scan_workspace_size", "wall_prefix_scan", "wall_prefix_append",
     "wall_attn_fwd_workspace_size", "wall_attn_fwd",
     "wall_attn_fwd_prepare", "wall_attn_fwd_run",
     "wall_attn_bwd_workspace_size", "wall_attn_bwd",
@@ -57,6 +57,7 @@ def lib() -> ctypes.CDLL:
         L.wall_prefix_scan_workspace_size.argtypes = [I, I, I]
         L.wall_prefix_scan_workspace_size.restype = S
         L.wall_prefix_scan.argtypes = [P, E, P, I, I, I, P, I, F, P, S, P]
+        L.wall_prefix_append.argtypes = [P, E, I, P, I, P, I, I, I, I, F, P]
         L.wall_prefix_scan.restype = E
         L.wall_attn_fwd_workspace_size.argtypes = [E, I, I, I, I, I, I, I]
         L.wall_attn_fwd_workspace_size.restype = S
@@ -77,7 +78,7 @@ def lib() -> ctypes.CDLL:
         L.wall_kv_cache_build.restype = E
         L.wall_attn_decode_workspace_size.argtypes = [I, I, I, I]
         L.wall_attn_decode_workspace_size.restype = S
-        L.wall_attn_decode.argtypes = [P, P, E, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, P, S, P]
+        L.wall_attn_decode.argtypes = [P, P, E, P, I, P, P, P, P, P, I, I, I, I, I, I, I, I, F, P, S, P]
         L.wall_attn_decode.restype = E
         _lib = L
     return _lib
@@ -160,6 +161,46 @@ def wall_prefix_scan(x: torch.Tensor, cu_seqlens: Optional[torch.Tensor] = None,
     _check(lib().wall_prefix_scan(_ptr(x), _dtype(x), _ptr(out), B, T, C, _ptr(cu), nseq,
                                   float(scale), _ptr(workspace), workspace.numel(), _stream(dev)),
            "wall_prefix_scan")
+    return out
+
+
+def _rows(t: torch.Tensor, n: int, C: int, what: str) -> int:
+    """Batch stride (elements) of a [B, n, ...] tensor whose rows of C values are
+    contiguous and consecutive within a batch row."""
+    if t.dim() < 2 or t.shape[1] != n or t.numel() != t.shape[0] * n * C:
+        raise ValueError(f"{what}: expected [B, {n}, ...] with {C} values per row")
+    inner = t[0, 0] if t.dim() > 2 else None
+    if t.dim() > 2 and not inner.is_contiguous():
+        raise ValueError(f"{what}: each row must be contiguous")
+    if n > 1 and t.stride(1) != C:
+        raise ValueError(f"{what}: rows must be consecutive")
+    return t.stride(0) if t.shape[0] > 1 else n * C
+
+
+def wall_prefix_append(x: torch.Tensor, prev: Optional[torch.Tensor] = None,
+                       scale: float = 1.0 / math.log(2.0), out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """out[b,t] = prev[b] + scale * (x[b,0] + ... + x[b,t]) (float32): the log2 prefix
+    of rows appended to a sequence whose last prefix row is ``prev`` (None starts
+    one).  x is [B, n, ...]; prev [B, ...] (e.g. P[:, t0-1]) and out [B, n, ...]
+    (e.g. P[:, t0:t0+n]) may be row slices of a larger prefix buffer."""
+    dev = _on_gpu(x, prev, out)
+    B, n = x.shape[0], x.shape[1]
+    C = x.numel() // (B * n)
+    x_bs = _rows(x, n, C, "x")
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.float32, device=dev)
+    if out.dtype != torch.float32 or out.shape != x.shape:
+        raise ValueError("out must be float32 with x's shape")
+    out_bs = _rows(out, n, C, "out")
+    prev_bs = 0
+    if prev is not None:
+        if prev.dtype != torch.float32 or prev.numel() != B * C or prev.shape[0] != B:
+            raise ValueError("prev must be float32 [B, ...] with one row of x's width")
+        if prev.dim() > 1 and not prev[0].is_contiguous():
+            raise ValueError("prev: each row must be contiguous")
+        prev_bs = prev.stride(0) if B > 1 else C
+    _check(lib().wall_prefix_append(_ptr(x), _dtype(x), x_bs, _ptr(prev), prev_bs, _ptr(out), out_bs, B, n, C,
+                                    float(scale), _stream(dev)), "wall_prefix_append")
     return out
 
 
@@ -384,9 +425,13 @@ def wall_attn_decode(q: torch.Tensor, v: torch.Tensor, p_curr: torch.Tensor, k_t
                      ) -> Tuple[torch.Tensor, torch.Tensor]:
     """The README's wall_attn_decode: q and p_curr [B,1,HQ,K] (the newest token and
     its log2 prefix), v [B,T_cap,H,V], the cache of build_wall_kv_cache; attends to
-    cached rows 0 .. seq_len-1 (default T_cap).  Returns (o [B,1,HQ,V], lse [B,1,HQ])."""
+    cached rows 0 .. seq_len-1 (default T_cap).  p_curr may be a row of a larger
+    prefix buffer (P[:, t:t+1]).  Returns (o [B,1,HQ,V], lse [B,1,HQ])."""
     dev = _on_gpu(q, v, p_curr, k_tilde, r_cache, sink_bias, out, lse, workspace)
-    q, v, p_curr = _dense(q), _dense(v), _dense(p_curr)
+    q, v = _dense(q), _dense(v)
+    if not (p_curr.dim() == 4 and p_curr[0, 0].is_contiguous() and p_curr.stride(0) % 4 == 0):
+        p_curr = _dense(p_curr)
+    pc_bs = p_curr.stride(0) if p_curr.shape[0] > 1 else 0
     B, _, HQ, K = q.shape
     T_cap, H, V = v.shape[1], v.shape[2], v.shape[3]
     T = T_cap if seq_len is None else int(seq_len)
@@ -407,7 +452,7 @@ def wall_attn_decode(q: torch.Tensor, v: torch.Tensor, p_curr: torch.Tensor, k_t
     if workspace is None:
         workspace = torch.empty(decode_workspace_size(B, T, HQ, V), dtype=torch.uint8, device=dev)
     _check(lib().wall_attn_decode(
-        _ptr(q), _ptr(v), _dtype(q), _ptr(p_curr), _ptr(k_tilde), _ptr(r_cache), _ptr(sink_bias),
+        _ptr(q), _ptr(v), _dtype(q), _ptr(p_curr), pc_bs, _ptr(k_tilde), _ptr(r_cache), _ptr(sink_bias),
         _ptr(out), _ptr(lse), B, T, T_cap, HQ, H, K, V, int(cache_chunk_size), float(scale),
         _ptr(workspace), workspace.numel(), _stream(dev)), "wall_attn_decode")
     return out, lse

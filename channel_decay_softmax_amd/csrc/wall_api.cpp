@@ -60,6 +60,27 @@ wall_status_t wall_prefix_scan(const void *x, wall_dtype_t x_dtype, float *out, 
                                 cu_seqlens, cu_seqlens ? num_seqs : 0, scale, workspace, stream));
 }
 
+wall_status_t wall_prefix_append(const void *x, wall_dtype_t x_dtype, int64_t x_batch_stride,
+                                 const float *prev, int64_t prev_batch_stride, float *out,
+                                 int64_t out_batch_stride, int64_t B, int64_t n, int64_t C, float scale,
+                                 hipStream_t stream) {
+    if (!x || !out) return WALL_ERR_INVALID_ARG;
+    if (B < 1 || n < 1 || C < 1 || B * n * C > (int64_t)1 << 40) return WALL_ERR_INVALID_ARG;
+    if (x_batch_stride < n * C || out_batch_stride < n * C || (prev && prev_batch_stride < C))
+        return WALL_ERR_INVALID_ARG;
+    if (x_dtype != WALL_BF16 && x_dtype != WALL_F32) return WALL_ERR_UNSUPPORTED;
+    if (!aligned(x, x_dtype == WALL_BF16 ? 2 : 4) || !aligned(out, 4) || (prev && !aligned(prev, 4)))
+        return WALL_ERR_INVALID_ARG;
+    // out may not overlap x; it may start right after prev (a running buffer)
+    const char *o0 = reinterpret_cast<const char *>(out);
+    const char *o1 = o0 + sizeof(float) * ((B - 1) * out_batch_stride + n * C);
+    const char *x0 = static_cast<const char *>(x);
+    const char *x1 = x0 + esize_of(x_dtype) * ((B - 1) * x_batch_stride + n * C);
+    if (o0 < x1 && x0 < o1) return WALL_ERR_INVALID_ARG;
+    return launched(launch_prefix_append(x, x_dtype == WALL_BF16, x_batch_stride, prev, prev_batch_stride, out,
+                                         out_batch_stride, B, n, C, scale, stream));
+}
+
 size_t wall_attn_fwd_workspace_size(wall_dtype_t dtype, int64_t B, int64_t T, int64_t HQ,
                                     int64_t H, int64_t K, int64_t V, int64_t num_seqs) {
     const int64_t es = esize_of(dtype);
@@ -290,7 +311,7 @@ size_t wall_attn_decode_workspace_size(int64_t B, int64_t T, int64_t HQ, int64_t
 }
 
 wall_status_t wall_attn_decode(const void *q, const void *v, wall_dtype_t dtype, const float *p_curr,
-                               const void *k_tilde, const float *r_cache, const float *sink_bias,
+                               int64_t p_curr_batch_stride, const void *k_tilde, const float *r_cache, const float *sink_bias,
                                void *o, float *lse, int64_t B, int64_t T, int64_t T_cap, int64_t HQ,
                                int64_t H, int64_t K, int64_t V, int64_t chunk_size, float scale,
                                void *workspace, size_t workspace_bytes, hipStream_t stream) {
@@ -298,6 +319,8 @@ wall_status_t wall_attn_decode(const void *q, const void *v, wall_dtype_t dtype,
     if (B < 1 || T < 1 || T_cap < 1 || HQ < 1 || H < 1 || K < 1 || V < 1 || chunk_size < 1)
         return WALL_ERR_INVALID_ARG;
     if (HQ % H != 0 || T > T_cap || B * HQ > 65535) return WALL_ERR_INVALID_ARG;
+    if (p_curr_batch_stride != 0 && (p_curr_batch_stride < HQ * K || p_curr_batch_stride % 4 != 0))
+        return WALL_ERR_INVALID_ARG;
     if (B * T_cap > INT32_MAX / 2 || B * T_cap * HQ * (K > V ? K : V) > ((int64_t)1 << 40))
         return WALL_ERR_INVALID_ARG;
     if (dtype != WALL_BF16 && dtype != WALL_F32) return WALL_ERR_UNSUPPORTED;
@@ -312,6 +335,7 @@ wall_status_t wall_attn_decode(const void *q, const void *v, wall_dtype_t dtype,
     a.q = q;
     a.v = v;
     a.pc = p_curr;
+    a.pc_bs = p_curr_batch_stride ? p_curr_batch_stride : HQ * K;
     a.kt = k_tilde;
     a.r = r_cache;
     a.sink = sink_bias;

@@ -120,6 +120,11 @@ inline ScanLayout scan_layout(int64_t B, int64_t T, int64_t C) {
 
 hipError_t launch_scan(const void *x, bool x_bf16, float *out, int64_t B, int64_t T, int64_t C,
                        const int32_t *cu, int64_t nseq, float scale, void *ws, hipStream_t st);
+// out[b, t] = prev[b] (or 0) + scale * (x[b, 0] + ... + x[b, t]) for t < n;
+// batch strides in elements, rows of C contiguous.
+hipError_t launch_prefix_append(const void *x, bool x_bf16, int64_t x_bs, const float *prev, int64_t prev_bs,
+                                float *out, int64_t out_bs, int64_t B, int64_t n, int64_t C, float scale,
+                                hipStream_t st);
 // The exclusive form (scale * the sum of the earlier rows of the sequence) of
 // a float32 input, written as float32 or bf16.
 hipError_t launch_scan_excl(const float *x, void *out, bool out_bf16, int64_t B, int64_t T, int64_t C,
@@ -214,7 +219,8 @@ hipError_t launch_kv_cache(const CacheArgs &a, bool bf16, hipStream_t st);
 struct DecodeArgs {
     const void *q;      // [B, HQ, K]
     const void *v;      // [B, Tcap, H, V]
-    const float *pc;    // [B, HQ, K]
+    const float *pc;    // [B, HQ, K], batch rows pc_bs floats apart
+    int64_t pc_bs;
     const void *kt;     // [B, Tcap, HQ, K]
     const float *r;     // [B, ceil(Tcap / C), HQ, K]
     const float *sink;  // [HQ] or null

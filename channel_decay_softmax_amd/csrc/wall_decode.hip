@@ -151,7 +151,7 @@ __global__ __launch_bounds__(256) void decode_split(DecodeArgs a) {
     f32x8 o8 = {};
     // q and its prefix, once; the anchors of each round's chunk one round ahead
     const f32x8 qv = Vec8<T>::load(static_cast<const T *>(a.q) + bh * K + cq * 8);
-    const f32x8 pv = *reinterpret_cast<const f32x8 *>(a.pc + bh * K + cq * 8);
+    const f32x8 pv = *reinterpret_cast<const f32x8 *>(a.pc + b * a.pc_bs + hq * K + cq * 8);
     const float *rb = a.r + (b * NC * a.HQ + hq) * K + cq * 8;
     const int64_t rstride = a.HQ * K;
     f32x8 rv = *reinterpret_cast<const f32x8 *>(rb + (s0 / a.C) * rstride);

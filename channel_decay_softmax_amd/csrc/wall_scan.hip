@@ -272,6 +272,45 @@ hipError_t run_scan(const Tin *x, Tout *out, int64_t B, int64_t T, int64_t C, co
 
 }  // namespace
 
+namespace {
+
+// ---------------------------------------------------------------- append
+// Rows appended to a running prefix: one thread per (batch, channel), the n
+// new rows in order, s += x_t, out_t = prev + scale * s.  Coalesced across
+// channels; meant for the few rows of a decode step.
+template <typename Tin>
+__global__ __launch_bounds__(256) void prefix_append_kernel(const Tin *__restrict__ x, int64_t x_bs,
+                                                            const float *__restrict__ prev, int64_t prev_bs,
+                                                            float *__restrict__ out, int64_t out_bs,
+                                                            int64_t B, int64_t n, int64_t C, float scale) {
+    const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (id >= B * C) return;
+    const int64_t b = id / C, c = id % C;
+    const float p = prev ? prev[b * prev_bs + c] : 0.f;
+    const Tin *xr = x + b * x_bs + c;
+    float *orow = out + b * out_bs + c;
+    float s = 0.f;
+    for (int64_t t = 0; t < n; ++t) {
+        s += (float)xr[t * C];
+        orow[t * C] = p + scale * s;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_prefix_append(const void *x, bool x_bf16, int64_t x_bs, const float *prev, int64_t prev_bs,
+                                float *out, int64_t out_bs, int64_t B, int64_t n, int64_t C, float scale,
+                                hipStream_t st) {
+    const dim3 grid((unsigned)cdiv(B * C, 256));
+    if (x_bf16)
+        hipLaunchKernelGGL(prefix_append_kernel<__bf16>, grid, dim3(256), 0, st, static_cast<const __bf16 *>(x),
+                           x_bs, prev, prev_bs, out, out_bs, B, n, C, scale);
+    else
+        hipLaunchKernelGGL(prefix_append_kernel<float>, grid, dim3(256), 0, st, static_cast<const float *>(x),
+                           x_bs, prev, prev_bs, out, out_bs, B, n, C, scale);
+    return hipGetLastError();
+}
+
 hipError_t launch_scan_excl(const float *x, void *out, bool out_bf16, int64_t B, int64_t T, int64_t C,
                             const int32_t *cu, int64_t nseq, float scale, void *ws, hipStream_t st) {
     const bool vec = (C % 4) == 0;

@@ -95,6 +95,32 @@ wall_status_t wall_prefix_scan(const void *x, wall_dtype_t x_dtype, float *out,
                                void *workspace, size_t workspace_bytes,
                                hipStream_t stream);
 
+/* ------------------------------------------------------------------ prefix append
+ *
+ * out[b, t, c] = prev[b, c] + scale * sum_{u = 0 .. t} x[b, u, c],  t < n
+ *
+ * The running prefix of an append-as-you-go sequence (the README's
+ * streaming decode loop: P of each new token from the previous token's P,
+ * the blog's "Fast training and inference" cache that a decoder extends one
+ * token at a time).  prev = NULL starts a sequence (prev = 0).  Rows of C
+ * values are contiguous; consecutive batch rows are *_batch_stride elements
+ * apart, so x, prev and out may be row slices of larger [B, T_cap, C]
+ * buffers (out at row t0 and prev at row t0-1 of the same P buffer).
+ *
+ *   x     [B, n, C] in x_dtype (WALL_BF16 or WALL_F32), row stride C
+ *   prev  NULL or [B, C] float32
+ *   out   [B, n, C] float32; must not overlap x (prev may lie in out's buffer)
+ * Accumulation: float32, s = x_0 + ... + x_t in order, then prev + scale*s,
+ * so a prefix built by appends matches wall_prefix_scan's up to float32
+ * rounding of |P| (not bit for bit).
+ * Errors: INVALID_ARG for a null x/out, B, n or C < 1, a batch stride
+ * below n*C (below C for prev), misalignment, out overlapping x;
+ * UNSUPPORTED for another dtype; LAUNCH on a failed launch. */
+wall_status_t wall_prefix_append(const void *x, wall_dtype_t x_dtype, int64_t x_batch_stride,
+                                 const float *prev, int64_t prev_batch_stride, float *out,
+                                 int64_t out_batch_stride, int64_t B, int64_t n, int64_t C,
+                                 float scale, hipStream_t stream);
+
 /* ------------------------------------------------------------------ fused forward
  *
  * The causal Wall Attention forward of the README's `wall_attn` (usage
@@ -288,7 +314,11 @@ wall_status_t wall_kv_cache_build(const void *k, wall_dtype_t dtype, const float
  *
  *   q           [B, HQ, K] dtype (the README's [B, 1, HQ, K])
  *   v           [B, T_cap, H, V] dtype, rows 0 .. T-1 read
- *   p_curr      [B, HQ, K] float32, P at the query's row
+ *   p_curr      [B, HQ, K] float32, P at the query's row; batch rows are
+ *               p_curr_batch_stride floats apart (0: HQ*K, dense), so p_curr
+ *               may be the newest row of a [B, T_cap, HQ, K] prefix buffer
+ *               (stride T_cap*HQ*K); a nonzero stride is a multiple of 4,
+ *               at least HQ*K
  *   k_tilde, r_cache   a cache built by wall_kv_cache_build with this
  *               chunk_size and T_cap, rows 0 .. T-1 complete
  *   sink_bias   NULL or [HQ] float32
@@ -299,13 +329,15 @@ wall_status_t wall_kv_cache_build(const void *k, wall_dtype_t dtype, const float
  * Numerics: q~ = q * scale*log2(e) * exp2(p_curr - R) is rounded to the cache
  * dtype once per chunk; dot products and the softmax are float32.
  * Errors: INVALID_ARG for a null required pointer, a size < 1, HQ % H != 0,
- * T > T_cap, B*HQ > 65535, misalignment, a short workspace; UNSUPPORTED for K
+ * T > T_cap, B*HQ > 65535, a bad p_curr stride, misalignment, a short
+ * workspace; UNSUPPORTED for K
  * or V not in {64, 128}, chunk_size not a positive multiple of 64, or another
  * dtype; LAUNCH on a failed launch. */
 size_t wall_attn_decode_workspace_size(int64_t B, int64_t T, int64_t HQ, int64_t V);
 
 wall_status_t wall_attn_decode(const void *q, const void *v, wall_dtype_t dtype,
-                               const float *p_curr, const void *k_tilde, const float *r_cache,
+                               const float *p_curr, int64_t p_curr_batch_stride,
+                               const void *k_tilde, const float *r_cache,
                                const float *sink_bias, void *o, float *lse,
                                int64_t B, int64_t T, int64_t T_cap, int64_t HQ, int64_t H,
                                int64_t K, int64_t V, int64_t chunk_size, float scale,

@@ -54,6 +54,26 @@ def scan(x=FAKE, dtype=B.WALL_BF16, out=FAKE * 2, b=1, t=64, c=8, cu=None, nseq=
                               P(ws), wsb, None)
 
 
+def append(x=FAKE, dtype=B.WALL_BF16, xbs=None, prev=None, pbs=0, out=FAKE * 2, obs=None, b=2, n=3, c=8):
+    xbs = n * c if xbs is None else xbs
+    obs = n * c if obs is None else obs
+    return wall.lib().wall_prefix_append(P(x), dtype, xbs, P(prev), pbs, P(out), obs, b, n, c,
+                                         1.4426950408889634, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(x=None), dict(out=None), dict(b=0), dict(n=0), dict(c=0), dict(xbs=23), dict(obs=23),
+    dict(prev=FAKE * 3, pbs=7), dict(x=FAKE + 1), dict(dtype=B.WALL_F32, x=FAKE + 2),
+    dict(out=FAKE * 2 + 2), dict(prev=FAKE * 3 + 2, pbs=8), dict(out=FAKE + 8),
+])
+def test_prefix_append_rejects_invalid_arguments(kw):
+    assert append(**kw) == INVALID
+
+
+def test_prefix_append_rejects_unsupported_dtype():
+    assert append(dtype=7) == UNSUPPORTED
+
+
 def fwd(q=FAKE, k=FAKE, v=FAKE, dtype=B.WALL_BF16, Pp=FAKE, G=None, sink=None, o=FAKE, lse=None,
         b=1, t=256, hq=4, h=2, kk=128, vv=128, window=0, cu=None, nseq=0, maxlen=0, ws=FAKE,
         wsb=None):
@@ -101,12 +121,12 @@ def cache(k=FAKE, dtype=B.WALL_BF16, Pp=FAKE, kt=FAKE, r=FAKE, b=2, tcap=300, hq
                                           None)
 
 
-def decode(q=FAKE, v=FAKE, dtype=B.WALL_BF16, pc=FAKE, kt=FAKE, r=FAKE, sink=None, o=FAKE, lse=None,
+def decode(q=FAKE, v=FAKE, dtype=B.WALL_BF16, pc=FAKE, pcs=0, kt=FAKE, r=FAKE, sink=None, o=FAKE, lse=None,
            b=2, t=300, tcap=512, hq=4, h=2, kk=128, vv=128, c=64, ws=FAKE, wsb=None):
     L = wall.lib()
     if wsb is None:
         wsb = L.wall_attn_decode_workspace_size(b, t, hq, vv)
-    return L.wall_attn_decode(P(q), P(v), dtype, P(pc), P(kt), P(r), P(sink), P(o), P(lse), b, t, tcap,
+    return L.wall_attn_decode(P(q), P(v), dtype, P(pc), pcs, P(kt), P(r), P(sink), P(o), P(lse), b, t, tcap,
                               hq, h, kk, vv, c, 0.088, P(ws), wsb, None)
 
 
@@ -128,7 +148,7 @@ def test_kv_cache_rejects_unsupported_shapes(kw):
     dict(q=None), dict(v=None), dict(pc=None), dict(kt=None), dict(r=None), dict(o=None), dict(ws=None),
     dict(b=0), dict(t=0), dict(tcap=0), dict(hq=0), dict(h=0), dict(hq=6, h=4), dict(t=513),
     dict(b=8192, hq=16, h=4), dict(q=FAKE + 2), dict(sink=FAKE + 4), dict(lse=FAKE + 8),
-    dict(ws=FAKE + 16), dict(wsb=64),
+    dict(ws=FAKE + 16), dict(wsb=64), dict(pcs=100), dict(pcs=514),
 ])
 def test_decode_rejects_invalid_arguments(kw):
     assert decode(**kw) == INVALID
@@ -183,6 +203,8 @@ def test_python_wrappers_refuse_cpu_tensors():
     x = torch.zeros(1, 8, 2, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="GPU only"):
         wall.wall_prefix_scan(x)
+    with pytest.raises(ValueError, match="GPU only"):
+        wall.wall_prefix_append(x)
     with pytest.raises(ValueError, match="GPU only"):
         wall.wall_attn(x, x[:, :, :1], x[:, :, :1], x)
 

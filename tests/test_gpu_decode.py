@@ -157,3 +157,71 @@ def test_decode_full_size_sampled():
                                         scale=inp.scale)
     check_o(f64(o[sel])[:, 0], f64(lse[sel])[:, 0], o_ref[:, 0], l_ref[:, 0], "bfloat16",
             "full-size decode vs cached-decode oracle (3 sequences)")
+
+
+@pytest.mark.parametrize("dtype", ["bfloat16", "float32"])
+def test_prefix_append_matches_full_prefix(dtype):
+    """P built by appends of 1..100 rows (the first without a previous row)
+    equals the fp64 prefix of g / ln 2 within the float32 bound of a
+    sequential sum, (rows + 2) * 2^-24 * sum |g| / ln 2, and the scan's P
+    within twice that."""
+    B, T, HQ, K = 3, 300, 2, 64
+    say(f"prefix append {dtype} B={B} T={T} C={HQ * K}")
+    inp = make_decode_inputs("decode_bf16", B=B, T=T, HQ=HQ, H=1, K=K, V=64, dtype=dtype)
+    d = inp.to(DEV)
+    P = torch.full((B, T, HQ, K), float("nan"), dtype=torch.float32, device=DEV)
+    cuts = [0, 1, 2, 9, 64, 65, 164, 165, 299, 300]
+    for t0, t1 in zip(cuts[:-1], cuts[1:]):
+        wall.wall_prefix_append(d.g[:, t0:t1], prev=None if t0 == 0 else P[:, t0 - 1], out=P[:, t0:t1])
+    Ps = wall.wall_prefix_scan(d.g)
+    torch.cuda.synchronize()
+    g = f64(inp.g)
+    ref = oracle.prefix_scan_oracle(inp.g)
+    bound = (np.arange(T)[None, :, None, None] + 2) * 2.0 ** -24 * np.cumsum(np.abs(g), axis=1) / math.log(2.0)
+    got = f64(P)
+    assert np.isfinite(got).all()
+    assert (np.abs(got - ref) <= bound + 1e-30).all(), f"max excess {(np.abs(got - ref) - bound).max():.3e}"
+    assert (np.abs(got - f64(Ps)) <= 2 * bound + 1e-30).all()
+
+
+def test_streaming_loop_with_incremental_prefix():
+    """The README's streaming loop end to end on the GPU: a prefill of the
+    first rows (prefix by append, cache build), then per token the prefix
+    append, the cache append and the decode.  Every decoded row matches the
+    product-form forward oracle's row; each chunk's anchor is set when the
+    chunk opens and never moves (its first row's floored P); the last chunk is
+    partial (200 rows, C = 64)."""
+    B, Tcap, HQ, H, K, V, C = 2, 200, 4, 2, 128, 128, 64
+    t_first = 60
+    say(f"streaming loop B={B} rows {t_first}..{Tcap - 1} HQ={HQ} H={H} K={K} V={V} C={C}")
+    inp = make_decode_inputs("decode_bf16", chunk_size=C, B=B, T=Tcap, HQ=HQ, H=H, K=K, V=V, sink=True)
+    rng = np.random.default_rng(12)
+    qall = torch.from_numpy(rng.standard_normal((B, Tcap, HQ, K))).to(torch.bfloat16)
+    d = inp.to(DEV)
+    P = torch.empty((B, Tcap, HQ, K), dtype=torch.float32, device=DEV)
+    kt = torch.empty((B, Tcap, HQ, K), dtype=torch.bfloat16, device=DEV)
+    r = torch.empty((B, -(-Tcap // C), HQ, K), dtype=torch.float32, device=DEV)
+    wall.wall_prefix_append(d.g[:, :t_first], out=P[:, :t_first])
+    wall.build_wall_kv_cache(d.k, P, C, k_tilde=kt, r_cache=r, t0=0, t1=t_first)
+    outs, anchors = [], {}
+    for t in range(t_first, Tcap):
+        wall.wall_prefix_append(d.g[:, t:t + 1], prev=P[:, t - 1], out=P[:, t:t + 1])
+        wall.build_wall_kv_cache(d.k, P, C, k_tilde=kt, r_cache=r, t0=t, t1=t + 1)
+        if t % C == 0:
+            anchors[t // C] = r[:, t // C].clone()
+        o, lse = wall.wall_attn_decode(qall[:, t:t + 1].to(DEV), d.v, P[:, t:t + 1], kt, r,
+                                       sink_bias=d.sink_bias, scale=inp.scale, cache_chunk_size=C,
+                                       seq_len=t + 1)
+        outs.append((f64(o)[:, 0], f64(lse)[:, 0]))
+    torch.cuda.synchronize()
+    Pg = f64(P)
+    for c in range(-(-Tcap // C)):
+        assert np.array_equal(f64(r[:, c]), np.floor(Pg[:, c * C])), f"anchor of chunk {c}"
+        if c in anchors:
+            assert torch.equal(anchors[c], r[:, c]), f"anchor of chunk {c} moved"
+    rows = [b * Tcap + t for b in range(B) for t in range(t_first, Tcap)]
+    o_f, l_f = oracle.wall_attn_oracle(qall, inp.k, inp.v, inp.g, scale=inp.scale, sink_bias=inp.sink_bias,
+                                       rows=rows)
+    og = np.stack([x[0] for x in outs], axis=1)
+    lg = np.stack([x[1] for x in outs], axis=1)
+    check_o(og, lg, o_f[:, t_first:], l_f[:, t_first:], "bfloat16", "streaming loop vs forward rows")
