@@ -16,8 +16,10 @@
 // 32 rows at a time, each tile both row-major (the MFMA's first operand) and
 // transposed (the second operand of the product that contracts over the
 // streamed rows); the next tile's global loads are issued before the current
-// tile's products.  The block's own rows stay in registers as second
-// operands.
+// tile's products, and the tiles are double-buffered in LDS (one barrier
+// per tile).  Staging lanes take consecutive rows of one 8-channel chunk, so
+// the transposed copy is written as runs of consecutive bf16.  The block's
+// own rows stay in registers as second operands.
 //
 // dk/dv (per key block, queries from the block's first key on):
 //   S  = q~ k~^T,  dP = do v^T   (32 streamed queries x the wave's 32 keys);
@@ -68,6 +70,17 @@ __device__ inline f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
 
 __device__ inline bf16x8 lds8(const __bf16 *p) { return *reinterpret_cast<const bf16x8 *>(p); }
 
+// Row-major tiles: 16-byte chunk c of row r sits at chunk c ^ 4 when bit 3
+// of r is set (else at c), rows PITCH elements apart.  With a pitch of 4
+// dwords modulo the 32 banks, the 8 rows one 8-lane phase of a first-operand
+// read touches ({0..3, 8..11} + 16k + 4m, the bits-2-and-3 order) and the 8
+// consecutive rows of a staging write then fall on 8 different 4-bank
+// groups.
+template <int PITCH>
+__device__ inline int roff(int r, int chunk) { return r * PITCH + 8 * (chunk ^ (((r >> 3) & 1) << 2)); }
+template <int PITCH>
+constexpr int rows_size() { return BT * PITCH; }
+
 __device__ inline f32x8 to_f32(uint4 raw) {
     return __builtin_convertvector(__builtin_bit_cast(bf16x8, raw), f32x8);
 }
@@ -97,13 +110,14 @@ __global__ __launch_bounds__(NTH) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
     constexpr int CK = BT * K / 8, CV = BT * V / 8;  // 8-element chunks per tile
     constexpr int UK = CK / NTH, UV = CV / NTH;
     static_assert(CK % NTH == 0 && CV % NTH == 0, "tile chunks");
-    __shared__ __attribute__((aligned(16))) __bf16 sQ[BT * RPK];   // q~ rows
-    __shared__ __attribute__((aligned(16))) __bf16 sQT[K * TP];    // q~ transposed
-    __shared__ __attribute__((aligned(16))) __bf16 sO[BT * RPV];   // do rows
-    __shared__ __attribute__((aligned(16))) __bf16 sOT[V * TP];    // do transposed
-    __shared__ __attribute__((aligned(16))) float sL[BT];
-    __shared__ __attribute__((aligned(16))) float sD[BT];
-    __shared__ __attribute__((aligned(16))) float sGq[BT];
+    // two buffers of each streamed tile: one read while the other is filled
+    __shared__ __attribute__((aligned(16))) __bf16 sQ[2][rows_size<RPK>()];  // q~ rows
+    __shared__ __attribute__((aligned(16))) __bf16 sQT[2][K * TP];           // q~ transposed
+    __shared__ __attribute__((aligned(16))) __bf16 sO[2][rows_size<RPV>()];  // do rows
+    __shared__ __attribute__((aligned(16))) __bf16 sOT[2][V * TP];           // do transposed
+    __shared__ __attribute__((aligned(16))) float sL[2][BT];
+    __shared__ __attribute__((aligned(16))) float sD[2][BT];
+    __shared__ __attribute__((aligned(16))) float sGq[2][BT];
     __shared__ float sR[K];
 
     const BlockPos bp = block_pos(a, nblk, true);
@@ -166,7 +180,7 @@ __global__ __launch_bounds__(NTH) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
     auto load_tile = [&](int q0) {
 #pragma unroll
         for (int u = 0; u < UK; ++u) {
-            const int c = tid + NTH * u, r = c / (K / 8), ch = 8 * (c % (K / 8)), i = q0 + r;
+            const int c = tid + NTH * u, r = c % BT, ch = 8 * (c / BT), i = q0 + r;
             qraw[u] = {0, 0, 0, 0};
             praw[u] = 0.f;
             if (i < len) {
@@ -179,7 +193,7 @@ __global__ __launch_bounds__(NTH) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
         }
 #pragma unroll
         for (int u = 0; u < UV; ++u) {
-            const int c = tid + NTH * u, r = c / (V / 8), ch = 8 * (c % (V / 8)), i = q0 + r;
+            const int c = tid + NTH * u, r = c % BT, ch = 8 * (c / BT), i = q0 + r;
             oraw[u] = {0, 0, 0, 0};
             if (i < len) oraw[u] = *reinterpret_cast<const uint4 *>(dog + ((s0 + i) * HQ + hq) * V + ch);
         }
@@ -194,68 +208,84 @@ __global__ __launch_bounds__(NTH) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
             }
         }
     };
-    auto store_tile = [&]() {
+    auto store_tile = [&](int buf) {
 #pragma unroll
         for (int u = 0; u < UK; ++u) {
-            const int c = tid + NTH * u, r = c / (K / 8), ch = 8 * (c % (K / 8));
+            const int c = tid + NTH * u, r = c % BT, ch = 8 * (c / BT);
             const f32x8 qq = to_f32(qraw[u]);
             f32x8 x;
 #pragma unroll
             for (int e = 0; e < 8; ++e) x[e] = qq[e] * a.qscale * clamp2(praw[u][e] - sR[ch + e]);
             const bf16x8 b = __builtin_convertvector(x, bf16x8);
-            *reinterpret_cast<bf16x8 *>(sQ + r * RPK + ch) = b;
+            *reinterpret_cast<bf16x8 *>(&sQ[buf][roff<RPK>(r, ch / 8)]) = b;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) sQT[(ch + e) * TP + r] = b[e];
+            for (int e = 0; e < 8; ++e) sQT[buf][(ch + e) * TP + r] = b[e];
         }
 #pragma unroll
         for (int u = 0; u < UV; ++u) {
-            const int c = tid + NTH * u, r = c / (V / 8), ch = 8 * (c % (V / 8));
+            const int c = tid + NTH * u, r = c % BT, ch = 8 * (c / BT);
             const bf16x8 b = __builtin_bit_cast(bf16x8, oraw[u]);
-            *reinterpret_cast<bf16x8 *>(sO + r * RPV + ch) = b;
+            *reinterpret_cast<bf16x8 *>(&sO[buf][roff<RPV>(r, ch / 8)]) = b;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) sOT[(ch + e) * TP + r] = b[e];
+            for (int e = 0; e < 8; ++e) sOT[buf][(ch + e) * TP + r] = b[e];
         }
         if (tid < BT) {
-            sL[tid] = il;
-            sD[tid] = id;
-            sGq[tid] = ig;
+            sL[buf][tid] = il;
+            sD[buf][tid] = id;
+            sGq[buf][tid] = ig;
         }
     };
 
+    // Tile it lives in buffer it & 1.  Iteration it computes on it, then
+    // stores tile it+1 (loaded during iteration it-1) into the other buffer,
+    // which every wave finished reading before the previous barrier; one
+    // barrier per tile.
     load_tile(j0);
-    for (int q0 = j0; q0 < qend; q0 += BT) {
-        __syncthreads();  // every wave is done with the previous tile
-        store_tile();
-        __syncthreads();
-        if (q0 + BT < qend) load_tile(q0 + BT);
+    store_tile(0);
+    __syncthreads();
+    if (j0 + BT < qend) load_tile(j0 + BT);
+    for (int q0 = j0, it = 0; q0 < qend; q0 += BT, ++it) {
+        const int cur = it & 1;
         // does the tile hold a visible pair for this wave's keys?
         bool act = jw < len && q0 + BT - 1 >= jw;
         if (a.window > 0) act = act && q0 <= wlast + a.window - 1;
-        if (!act) continue;
+        if (act) {
 
         f32x16 S = 0.f, dP = 0.f;
         const int qrow = swap23(l32);
 #pragma unroll
-        for (int s = 0; s < K / 16; ++s) S = mfma(lds8(sQ + qrow * RPK + 16 * s + 8 * hl), kop[s], S);
+        for (int s = 0; s < K / 16; ++s) S = mfma(lds8(&sQ[cur][roff<RPK>(qrow, 2 * s + hl)]), kop[s], S);
 #pragma unroll
-        for (int s = 0; s < V / 16; ++s) dP = mfma(lds8(sO + qrow * RPV + 16 * s + 8 * hl), vop[s], dP);
+        for (int s = 0; s < V / 16; ++s) dP = mfma(lds8(&sO[cur][roff<RPV>(qrow, 2 * s + hl)]), vop[s], dP);
 
+        // the tile's per-query values, read before any use so the reads
+        // overlap; the exps are taken unconditionally and masked by a select
+        f32x4 L4[2][2], D4[2][2], G4[2][2];
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int x = 0; x < 2; ++x) {
+                const int qi = 16 * c + 8 * hl + 4 * x;
+                L4[c][x] = *reinterpret_cast<const f32x4 *>(&sL[cur][qi]);
+                D4[c][x] = *reinterpret_cast<const f32x4 *>(&sD[cur][qi]);
+                if (HAS_G) G4[c][x] = *reinterpret_cast<const f32x4 *>(&sGq[cur][qi]);
+            }
+        // every pair of the tile visible: no mask
+        const bool full = jw + 31 < len && q0 >= jw + 31 && q0 + BT <= len &&
+                          (a.window <= 0 || q0 + BT - 1 - jw < a.window);
         bf16x8 pb[2], db[2];
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
             const int qi0 = 16 * c + 8 * hl;
-            const f32x4 *L4 = reinterpret_cast<const f32x4 *>(sL + qi0);
-            const f32x4 *D4 = reinterpret_cast<const f32x4 *>(sD + qi0);
-            const f32x4 *G4 = reinterpret_cast<const f32x4 *>(sGq + qi0);
             f32x8 pv, dv8;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int i = q0 + qi0 + e;
-                const float lse2 = L4[e / 4][e % 4], Di = D4[e / 4][e % 4];
-                const float Gi = HAS_G ? G4[e / 4][e % 4] : 0.f;
-                bool vis = jok && i >= j && i < len;
-                if (a.window > 0) vis = vis && i - j < a.window;
-                const float p = vis ? exp2f(S[8 * c + e] + Gi - gj - lse2) : 0.f;
+                const float lse2 = L4[c][e / 4][e % 4], Di = D4[c][e / 4][e % 4];
+                const float Gi = HAS_G ? G4[c][e / 4][e % 4] : 0.f;
+                bool vis = full || (jok && i >= j && i < len && (a.window <= 0 || i - j < a.window));
+                const float ex = exp2f(S[8 * c + e] + Gi - gj - lse2);
+                const float p = vis ? ex : 0.f;
                 const float ds = p * (dP[8 * c + e] - Di);
                 colsum += ds;
                 pv[e] = p;
@@ -268,12 +298,16 @@ __global__ __launch_bounds__(NTH) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
         for (int n = 0; n < V / 32; ++n)
 #pragma unroll
             for (int c = 0; c < 2; ++c)
-                dv[n] = mfma(pb[c], lds8(sOT + (32 * n + l32) * TP + 16 * c + 8 * hl), dv[n]);
+                dv[n] = mfma(pb[c], lds8(&sOT[cur][(32 * n + l32) * TP + 16 * c + 8 * hl]), dv[n]);
 #pragma unroll
         for (int n = 0; n < K / 32; ++n)
 #pragma unroll
             for (int c = 0; c < 2; ++c)
-                dk[n] = mfma(db[c], lds8(sQT + (32 * n + l32) * TP + 16 * c + 8 * hl), dk[n]);
+                dk[n] = mfma(db[c], lds8(&sQT[cur][(32 * n + l32) * TP + 16 * c + 8 * hl]), dk[n]);
+        }
+        if (q0 + BT < qend) store_tile(cur ^ 1);
+        __syncthreads();
+        if (q0 + 2 * BT < qend) load_tile(q0 + 2 * BT);
     }
 
     if (jw >= len) return;
@@ -307,10 +341,10 @@ __global__ __launch_bounds__(NTH) void bwd_dq_mfma(BwdArgs a, int nblk) {
     constexpr int CK = BT * K / 8, CV = BT * V / 8;
     constexpr int UK = CK / NTH, UV = CV / NTH;
     static_assert(CK % NTH == 0 && CV % NTH == 0, "tile chunks");
-    __shared__ __attribute__((aligned(16))) __bf16 sK[BT * RPK];   // k~ rows
-    __shared__ __attribute__((aligned(16))) __bf16 sKT[K * TP];    // k~ transposed
-    __shared__ __attribute__((aligned(16))) __bf16 sV[BT * RPV];   // v rows
-    __shared__ __attribute__((aligned(16))) float sGk[BT];
+    __shared__ __attribute__((aligned(16))) __bf16 sK[2][rows_size<RPK>()];  // k~ rows
+    __shared__ __attribute__((aligned(16))) __bf16 sKT[2][K * TP];           // k~ transposed
+    __shared__ __attribute__((aligned(16))) __bf16 sV[2][rows_size<RPV>()];  // v rows
+    __shared__ __attribute__((aligned(16))) float sGk[2][BT];
     __shared__ float sR[K];
 
     const BlockPos bp = block_pos(a, nblk, false);
@@ -373,7 +407,7 @@ __global__ __launch_bounds__(NTH) void bwd_dq_mfma(BwdArgs a, int nblk) {
     auto load_tile = [&](int k0) {
 #pragma unroll
         for (int u = 0; u < UK; ++u) {
-            const int c = tid + NTH * u, r = c / (K / 8), ch = 8 * (c % (K / 8)), jj = k0 + r;
+            const int c = tid + NTH * u, r = c % BT, ch = 8 * (c / BT), jj = k0 + r;
             kraw[u] = {0, 0, 0, 0};
             praw[u] = 0.f;
             if (jj < len) {
@@ -386,7 +420,7 @@ __global__ __launch_bounds__(NTH) void bwd_dq_mfma(BwdArgs a, int nblk) {
         }
 #pragma unroll
         for (int u = 0; u < UV; ++u) {
-            const int c = tid + NTH * u, r = c / (V / 8), ch = 8 * (c % (V / 8)), jj = k0 + r;
+            const int c = tid + NTH * u, r = c % BT, ch = 8 * (c / BT), jj = k0 + r;
             vraw[u] = {0, 0, 0, 0};
             if (jj < len) vraw[u] = *reinterpret_cast<const uint4 *>(vg + ((s0 + jj) * a.H + h) * V + ch);
         }
@@ -395,57 +429,67 @@ __global__ __launch_bounds__(NTH) void bwd_dq_mfma(BwdArgs a, int nblk) {
             kgv = jj < len ? a.G[(s0 + jj) * HQ + hq] : 0.f;
         }
     };
-    auto store_tile = [&]() {
+    auto store_tile = [&](int buf) {
 #pragma unroll
         for (int u = 0; u < UK; ++u) {
-            const int c = tid + NTH * u, r = c / (K / 8), ch = 8 * (c % (K / 8));
+            const int c = tid + NTH * u, r = c % BT, ch = 8 * (c / BT);
             const f32x8 kk = to_f32(kraw[u]);
             f32x8 x;
 #pragma unroll
             for (int e = 0; e < 8; ++e) x[e] = kk[e] * clamp2(sR[ch + e] - praw[u][e]);
             const bf16x8 b = __builtin_convertvector(x, bf16x8);
-            *reinterpret_cast<bf16x8 *>(sK + r * RPK + ch) = b;
+            *reinterpret_cast<bf16x8 *>(&sK[buf][roff<RPK>(r, ch / 8)]) = b;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) sKT[(ch + e) * TP + r] = b[e];
+            for (int e = 0; e < 8; ++e) sKT[buf][(ch + e) * TP + r] = b[e];
         }
 #pragma unroll
         for (int u = 0; u < UV; ++u) {
-            const int c = tid + NTH * u, r = c / (V / 8), ch = 8 * (c % (V / 8));
-            *reinterpret_cast<uint4 *>(sV + r * RPV + ch) = vraw[u];
+            const int c = tid + NTH * u, r = c % BT, ch = 8 * (c / BT);
+            *reinterpret_cast<uint4 *>(&sV[buf][roff<RPV>(r, ch / 8)]) = vraw[u];
         }
-        if (HAS_G && tid < BT) sGk[tid] = kgv;
+        if (HAS_G && tid < BT) sGk[buf][tid] = kgv;
     };
 
+    // double-buffered as in the dk/dv kernel
     load_tile(klo);
-    for (int k0 = klo; k0 <= ilast; k0 += BT) {
-        __syncthreads();
-        store_tile();
-        __syncthreads();
-        if (k0 + BT <= ilast) load_tile(k0 + BT);
+    store_tile(0);
+    __syncthreads();
+    if (klo + BT <= ilast) load_tile(klo + BT);
+    for (int k0 = klo, it = 0; k0 <= ilast; k0 += BT, ++it) {
+        const int cur = it & 1;
         bool act = iw < len && k0 <= wlast;
         if (a.window > 0) act = act && k0 + BT - 1 >= iw - a.window + 1;
-        if (!act) continue;
-
+        if (act) {
         f32x16 S = 0.f, dP = 0.f;
         const int krow = swap23(l32);
 #pragma unroll
-        for (int s = 0; s < K / 16; ++s) S = mfma(lds8(sK + krow * RPK + 16 * s + 8 * hl), qop[s], S);
+        for (int s = 0; s < K / 16; ++s) S = mfma(lds8(&sK[cur][roff<RPK>(krow, 2 * s + hl)]), qop[s], S);
 #pragma unroll
-        for (int s = 0; s < V / 16; ++s) dP = mfma(lds8(sV + krow * RPV + 16 * s + 8 * hl), oop[s], dP);
+        for (int s = 0; s < V / 16; ++s) dP = mfma(lds8(&sV[cur][roff<RPV>(krow, 2 * s + hl)]), oop[s], dP);
 
+        f32x4 G4[2][2];
+        if (HAS_G) {
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int x = 0; x < 2; ++x)
+                    G4[c][x] = *reinterpret_cast<const f32x4 *>(&sGk[cur][16 * c + 8 * hl + 4 * x]);
+        }
+        // every pair of the tile visible: no mask
+        const bool full = iw + 31 < len && k0 + BT - 1 <= iw &&
+                          (a.window <= 0 || iw + 31 - k0 < a.window);
         bf16x8 db[2];
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
             const int kj0 = 16 * c + 8 * hl;
-            const f32x4 *G4 = reinterpret_cast<const f32x4 *>(sGk + kj0);
             f32x8 d8;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int jj = k0 + kj0 + e;
-                const float Gj = HAS_G ? G4[e / 4][e % 4] : 0.f;
-                bool vis = iok && jj <= i;
-                if (a.window > 0) vis = vis && i - jj < a.window;
-                const float p = vis ? exp2f(S[8 * c + e] + Gi - Gj - lse2) : 0.f;
+                const float Gj = HAS_G ? G4[c][e / 4][e % 4] : 0.f;
+                bool vis = full || (iok && jj <= i && (a.window <= 0 || i - jj < a.window));
+                const float ex = exp2f(S[8 * c + e] + Gi - Gj - lse2);
+                const float p = vis ? ex : 0.f;
                 const float ds = p * (dP[8 * c + e] - Di);
                 rowsum += ds;
                 d8[e] = ds;
@@ -456,7 +500,11 @@ __global__ __launch_bounds__(NTH) void bwd_dq_mfma(BwdArgs a, int nblk) {
         for (int n = 0; n < K / 32; ++n)
 #pragma unroll
             for (int c = 0; c < 2; ++c)
-                dq[n] = mfma(db[c], lds8(sKT + (32 * n + l32) * TP + 16 * c + 8 * hl), dq[n]);
+                dq[n] = mfma(db[c], lds8(&sKT[cur][(32 * n + l32) * TP + 16 * c + 8 * hl]), dq[n]);
+        }
+        if (k0 + BT <= ilast) store_tile(cur ^ 1);
+        __syncthreads();
+        if (k0 + 2 * BT <= ilast) load_tile(k0 + 2 * BT);
     }
 
     if (iw >= len) return;
