@@ -50,6 +50,8 @@
 // it on the same stream).
 #include <float.h>
 
+#include <type_traits>
+
 #include "wall_common.h"
 
 namespace wall {
@@ -61,7 +63,11 @@ constexpr int NW = 4;        // waves per block
 constexpr int NTH = NW * 64;
 constexpr int TP = BT + 8;   // transposed tile row pitch (elements): 80 bytes
 
-__device__ inline float clamp2(float e) { return exp2f(fminf(fmaxf(e, EXP2_LO), EXP2_HI)); }
+// exp2 of a clamped anchored exponent on v_exp_f32 itself: results below
+// the float32 normal range may come back as 0, which only drops terms below
+// 2^-126 of the largest.  Every anchored factor of this file goes through it,
+// so the staged operands and the epilogue's recomputed ones agree bit for bit.
+__device__ inline float clamp2(float e) { return __builtin_amdgcn_exp2f(fminf(fmaxf(e, EXP2_LO), EXP2_HI)); }
 __device__ inline int swap23(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
 __device__ inline f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -171,7 +177,6 @@ __global__ __launch_bounds__(NTH) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
     float colsum = 0.f;
 
     const int qend = a.window > 0 ? min(len, j0 + jn - 1 + a.window) : len;
-    const int wlast = min(jw + 31, len - 1);  // the wave's last valid key
 
     // prefetch registers for one tile
     uint4 qraw[UK], oraw[UV];
@@ -179,23 +184,19 @@ __global__ __launch_bounds__(NTH) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
     float il = 0.f, id = 0.f, ig = 0.f;
     auto load_tile = [&](int q0) {
 #pragma unroll
+        // rows past the sequence load its last row (in bounds) and are zeroed when stored
         for (int u = 0; u < UK; ++u) {
-            const int c = tid + NTH * u, r = c % BT, ch = 8 * (c / BT), i = q0 + r;
-            qraw[u] = {0, 0, 0, 0};
-            praw[u] = 0.f;
-            if (i < len) {
-                const int64_t t = (s0 + i) * HQ + hq;
-                qraw[u] = *reinterpret_cast<const uint4 *>(qg + t * K + ch);
-                const f32x4 *pp = reinterpret_cast<const f32x4 *>(a.P + t * K + ch);
-                const f32x4 p0 = pp[0], p1 = pp[1];
-                praw[u] = f32x8{p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
-            }
+            const int c = tid + NTH * u, r = c % BT, ch = 8 * (c / BT), i = min(q0 + r, len - 1);
+            const int64_t t = (s0 + i) * HQ + hq;
+            qraw[u] = *reinterpret_cast<const uint4 *>(qg + t * K + ch);
+            const f32x4 *pp = reinterpret_cast<const f32x4 *>(a.P + t * K + ch);
+            const f32x4 p0 = pp[0], p1 = pp[1];
+            praw[u] = f32x8{p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
         }
 #pragma unroll
         for (int u = 0; u < UV; ++u) {
-            const int c = tid + NTH * u, r = c % BT, ch = 8 * (c / BT), i = q0 + r;
-            oraw[u] = {0, 0, 0, 0};
-            if (i < len) oraw[u] = *reinterpret_cast<const uint4 *>(dog + ((s0 + i) * HQ + hq) * V + ch);
+            const int c = tid + NTH * u, r = c % BT, ch = 8 * (c / BT), i = min(q0 + r, len - 1);
+            oraw[u] = *reinterpret_cast<const uint4 *>(dog + ((s0 + i) * HQ + hq) * V + ch);
         }
         if (tid < BT) {
             const int i = q0 + tid;
@@ -208,7 +209,7 @@ __global__ __launch_bounds__(NTH) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
             }
         }
     };
-    auto store_tile = [&](int buf) {
+    auto store_tile = [&](int buf, int q0) {
 #pragma unroll
         for (int u = 0; u < UK; ++u) {
             const int c = tid + NTH * u, r = c % BT, ch = 8 * (c / BT);
@@ -216,6 +217,7 @@ __global__ __launch_bounds__(NTH) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
             f32x8 x;
 #pragma unroll
             for (int e = 0; e < 8; ++e) x[e] = qq[e] * a.qscale * clamp2(praw[u][e] - sR[ch + e]);
+            if (q0 + r >= len) x = 0.f;
             const bf16x8 b = __builtin_convertvector(x, bf16x8);
             *reinterpret_cast<bf16x8 *>(&sQ[buf][roff<RPK>(r, ch / 8)]) = b;
 #pragma unroll
@@ -224,7 +226,8 @@ __global__ __launch_bounds__(NTH) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
 #pragma unroll
         for (int u = 0; u < UV; ++u) {
             const int c = tid + NTH * u, r = c % BT, ch = 8 * (c / BT);
-            const bf16x8 b = __builtin_bit_cast(bf16x8, oraw[u]);
+            const uint4 z = {0, 0, 0, 0};
+            const bf16x8 b = __builtin_bit_cast(bf16x8, q0 + r < len ? oraw[u] : z);
             *reinterpret_cast<bf16x8 *>(&sO[buf][roff<RPV>(r, ch / 8)]) = b;
 #pragma unroll
             for (int e = 0; e < 8; ++e) sOT[buf][(ch + e) * TP + r] = b[e];
@@ -241,15 +244,16 @@ __global__ __launch_bounds__(NTH) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
     // which every wave finished reading before the previous barrier; one
     // barrier per tile.
     load_tile(j0);
-    store_tile(0);
+    store_tile(0, j0);
     __syncthreads();
     if (j0 + BT < qend) load_tile(j0 + BT);
     for (int q0 = j0, it = 0; q0 < qend; q0 += BT, ++it) {
         const int cur = it & 1;
-        // does the tile hold a visible pair for this wave's keys?
-        bool act = jw < len && q0 + BT - 1 >= jw;
-        if (a.window > 0) act = act && q0 <= wlast + a.window - 1;
-        if (act) {
+        // Every wave runs every tile: a tile with no visible pair for its keys
+        // (at most the first three, or three past the window) is masked to
+        // zero, and the accumulators stay on one straight path through the
+        // loop.
+        {
 
         f32x16 S = 0.f, dP = 0.f;
         const int qrow = swap23(l32);
@@ -274,26 +278,36 @@ __global__ __launch_bounds__(NTH) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
         const bool full = jw + 31 < len && q0 >= jw + 31 && q0 + BT <= len &&
                           (a.window <= 0 || q0 + BT - 1 - jw < a.window);
         bf16x8 pb[2], db[2];
+        // two copies of the softmax step: without the mask for a full tile,
+        // with it for the diagonal, the window edge and a sequence's end
+        auto softmax = [&](auto masked) {
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            const int qi0 = 16 * c + 8 * hl;
-            f32x8 pv, dv8;
+            for (int c = 0; c < 2; ++c) {
+                const int qi0 = 16 * c + 8 * hl;
+                f32x8 pv, dv8;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int i = q0 + qi0 + e;
-                const float lse2 = L4[c][e / 4][e % 4], Di = D4[c][e / 4][e % 4];
-                const float Gi = HAS_G ? G4[c][e / 4][e % 4] : 0.f;
-                bool vis = full || (jok && i >= j && i < len && (a.window <= 0 || i - j < a.window));
-                const float ex = exp2f(S[8 * c + e] + Gi - gj - lse2);
-                const float p = vis ? ex : 0.f;
-                const float ds = p * (dP[8 * c + e] - Di);
-                colsum += ds;
-                pv[e] = p;
-                dv8[e] = ds;
+                for (int e = 0; e < 8; ++e) {
+                    const float lse2 = L4[c][e / 4][e % 4], Di = D4[c][e / 4][e % 4];
+                    const float Gi = HAS_G ? G4[c][e / 4][e % 4] : 0.f;
+                    float p = __builtin_amdgcn_exp2f(S[8 * c + e] + Gi - gj - lse2);
+                    if constexpr (decltype(masked)::value) {
+                        const int i = q0 + qi0 + e;
+                        const bool vis = jok && i >= j && i < len && (a.window <= 0 || i - j < a.window);
+                        p = vis ? p : 0.f;
+                    }
+                    const float ds = p * (dP[8 * c + e] - Di);
+                    colsum += ds;
+                    pv[e] = p;
+                    dv8[e] = ds;
+                }
+                pb[c] = __builtin_convertvector(pv, bf16x8);
+                db[c] = __builtin_convertvector(dv8, bf16x8);
             }
-            pb[c] = __builtin_convertvector(pv, bf16x8);
-            db[c] = __builtin_convertvector(dv8, bf16x8);
-        }
+        };
+        if (full)
+            softmax(std::false_type{});
+        else
+            softmax(std::true_type{});
 #pragma unroll
         for (int n = 0; n < V / 32; ++n)
 #pragma unroll
@@ -305,7 +319,7 @@ __global__ __launch_bounds__(NTH) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
             for (int c = 0; c < 2; ++c)
                 dk[n] = mfma(db[c], lds8(&sQT[cur][(32 * n + l32) * TP + 16 * c + 8 * hl]), dk[n]);
         }
-        if (q0 + BT < qend) store_tile(cur ^ 1);
+        if (q0 + BT < qend) store_tile(cur ^ 1, q0 + BT);
         __syncthreads();
         if (q0 + 2 * BT < qend) load_tile(q0 + 2 * BT);
     }
@@ -399,37 +413,32 @@ __global__ __launch_bounds__(NTH) void bwd_dq_mfma(BwdArgs a, int nblk) {
 
     const int ilast = i0 + in_ - 1;
     const int klo = a.window > 0 ? max(0, i0 - a.window + 1) / BT * BT : 0;
-    const int wlast = min(iw + 31, len - 1);
 
     uint4 kraw[UK], vraw[UV];
     f32x8 praw[UK];
     float kgv = 0.f;
     auto load_tile = [&](int k0) {
 #pragma unroll
+        // rows past the sequence load its last row (in bounds) and are zeroed when stored
         for (int u = 0; u < UK; ++u) {
-            const int c = tid + NTH * u, r = c % BT, ch = 8 * (c / BT), jj = k0 + r;
-            kraw[u] = {0, 0, 0, 0};
-            praw[u] = 0.f;
-            if (jj < len) {
-                const int64_t t = s0 + jj;
-                kraw[u] = *reinterpret_cast<const uint4 *>(kg + (t * a.H + h) * K + ch);
-                const f32x4 *pp = reinterpret_cast<const f32x4 *>(a.P + (t * HQ + hq) * K + ch);
-                const f32x4 p0 = pp[0], p1 = pp[1];
-                praw[u] = f32x8{p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
-            }
+            const int c = tid + NTH * u, r = c % BT, ch = 8 * (c / BT);
+            const int64_t t = s0 + min(k0 + r, len - 1);
+            kraw[u] = *reinterpret_cast<const uint4 *>(kg + (t * a.H + h) * K + ch);
+            const f32x4 *pp = reinterpret_cast<const f32x4 *>(a.P + (t * HQ + hq) * K + ch);
+            const f32x4 p0 = pp[0], p1 = pp[1];
+            praw[u] = f32x8{p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
         }
 #pragma unroll
         for (int u = 0; u < UV; ++u) {
-            const int c = tid + NTH * u, r = c % BT, ch = 8 * (c / BT), jj = k0 + r;
-            vraw[u] = {0, 0, 0, 0};
-            if (jj < len) vraw[u] = *reinterpret_cast<const uint4 *>(vg + ((s0 + jj) * a.H + h) * V + ch);
+            const int c = tid + NTH * u, r = c % BT, ch = 8 * (c / BT);
+            vraw[u] = *reinterpret_cast<const uint4 *>(vg + ((s0 + min(k0 + r, len - 1)) * a.H + h) * V + ch);
         }
         if (HAS_G && tid < BT) {
             const int jj = k0 + tid;
             kgv = jj < len ? a.G[(s0 + jj) * HQ + hq] : 0.f;
         }
     };
-    auto store_tile = [&](int buf) {
+    auto store_tile = [&](int buf, int k0) {
 #pragma unroll
         for (int u = 0; u < UK; ++u) {
             const int c = tid + NTH * u, r = c % BT, ch = 8 * (c / BT);
@@ -437,6 +446,7 @@ __global__ __launch_bounds__(NTH) void bwd_dq_mfma(BwdArgs a, int nblk) {
             f32x8 x;
 #pragma unroll
             for (int e = 0; e < 8; ++e) x[e] = kk[e] * clamp2(sR[ch + e] - praw[u][e]);
+            if (k0 + r >= len) x = 0.f;
             const bf16x8 b = __builtin_convertvector(x, bf16x8);
             *reinterpret_cast<bf16x8 *>(&sK[buf][roff<RPK>(r, ch / 8)]) = b;
 #pragma unroll
@@ -445,21 +455,21 @@ __global__ __launch_bounds__(NTH) void bwd_dq_mfma(BwdArgs a, int nblk) {
 #pragma unroll
         for (int u = 0; u < UV; ++u) {
             const int c = tid + NTH * u, r = c % BT, ch = 8 * (c / BT);
-            *reinterpret_cast<uint4 *>(&sV[buf][roff<RPV>(r, ch / 8)]) = vraw[u];
+            const uint4 z = {0, 0, 0, 0};
+            *reinterpret_cast<uint4 *>(&sV[buf][roff<RPV>(r, ch / 8)]) = k0 + r < len ? vraw[u] : z;
         }
         if (HAS_G && tid < BT) sGk[buf][tid] = kgv;
     };
 
     // double-buffered as in the dk/dv kernel
     load_tile(klo);
-    store_tile(0);
+    store_tile(0, klo);
     __syncthreads();
     if (klo + BT <= ilast) load_tile(klo + BT);
     for (int k0 = klo, it = 0; k0 <= ilast; k0 += BT, ++it) {
         const int cur = it & 1;
-        bool act = iw < len && k0 <= wlast;
-        if (a.window > 0) act = act && k0 + BT - 1 >= iw - a.window + 1;
-        if (act) {
+        // every wave runs every tile, as in the dk/dv kernel
+        {
         f32x16 S = 0.f, dP = 0.f;
         const int krow = swap23(l32);
 #pragma unroll
@@ -479,30 +489,38 @@ __global__ __launch_bounds__(NTH) void bwd_dq_mfma(BwdArgs a, int nblk) {
         const bool full = iw + 31 < len && k0 + BT - 1 <= iw &&
                           (a.window <= 0 || iw + 31 - k0 < a.window);
         bf16x8 db[2];
+        auto softmax = [&](auto masked) {
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            const int kj0 = 16 * c + 8 * hl;
-            f32x8 d8;
+            for (int c = 0; c < 2; ++c) {
+                const int kj0 = 16 * c + 8 * hl;
+                f32x8 d8;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int jj = k0 + kj0 + e;
-                const float Gj = HAS_G ? G4[c][e / 4][e % 4] : 0.f;
-                bool vis = full || (iok && jj <= i && (a.window <= 0 || i - jj < a.window));
-                const float ex = exp2f(S[8 * c + e] + Gi - Gj - lse2);
-                const float p = vis ? ex : 0.f;
-                const float ds = p * (dP[8 * c + e] - Di);
-                rowsum += ds;
-                d8[e] = ds;
+                for (int e = 0; e < 8; ++e) {
+                    const float Gj = HAS_G ? G4[c][e / 4][e % 4] : 0.f;
+                    float p = __builtin_amdgcn_exp2f(S[8 * c + e] + Gi - Gj - lse2);
+                    if constexpr (decltype(masked)::value) {
+                        const int jj = k0 + kj0 + e;
+                        const bool vis = iok && jj <= i && (a.window <= 0 || i - jj < a.window);
+                        p = vis ? p : 0.f;
+                    }
+                    const float ds = p * (dP[8 * c + e] - Di);
+                    rowsum += ds;
+                    d8[e] = ds;
+                }
+                db[c] = __builtin_convertvector(d8, bf16x8);
             }
-            db[c] = __builtin_convertvector(d8, bf16x8);
-        }
+        };
+        if (full)
+            softmax(std::false_type{});
+        else
+            softmax(std::true_type{});
 #pragma unroll
         for (int n = 0; n < K / 32; ++n)
 #pragma unroll
             for (int c = 0; c < 2; ++c)
                 dq[n] = mfma(db[c], lds8(&sKT[cur][(32 * n + l32) * TP + 16 * c + 8 * hl]), dq[n]);
         }
-        if (k0 + BT <= ilast) store_tile(cur ^ 1);
+        if (k0 + BT <= ilast) store_tile(cur ^ 1, k0 + BT);
         __syncthreads();
         if (k0 + 2 * BT <= ilast) load_tile(k0 + 2 * BT);
     }
