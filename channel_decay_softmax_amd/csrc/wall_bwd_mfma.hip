@@ -24,6 +24,10 @@
 // dk/dv (per key block, queries from the block's first key on):
 //   S  = q~ k~^T,  dP = do v^T   (32 streamed queries x the wave's 32 keys);
 //   A, dS in-lane;  dv += A^T do,  dk += dS^T q~.
+// The dq kernel fits two waves per SIMD (its own rows' q~ and do operands,
+// the dq accumulators and one tile of prefetch registers); the dk/dv kernel,
+// with both the dk and dv accumulators, runs one.
+//
 // dq (per query block, keys up to the block's last query):
 //   S^T = k~ q~^T, dP^T = v do^T (32 streamed keys x the wave's 32 queries);
 //   dq += dS k~.
@@ -350,7 +354,7 @@ __global__ __launch_bounds__(NTH) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
 
 // ---------------------------------------------------------------- dq
 template <int K, int V, bool HAS_G>
-__global__ __launch_bounds__(NTH) void bwd_dq_mfma(BwdArgs a, int nblk) {
+__global__ __launch_bounds__(NTH, 2) void bwd_dq_mfma(BwdArgs a, int nblk) {
     constexpr int RPK = K + 8, RPV = V + 8;
     constexpr int CK = BT * K / 8, CV = BT * V / 8;
     constexpr int UK = CK / NTH, UV = CV / NTH;
