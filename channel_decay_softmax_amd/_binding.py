@@ -153,6 +153,9 @@ def wall_prefix_scan(x: torch.Tensor, cu_seqlens: Optional[torch.Tensor] = None,
     C = x.numel() // (B * T)
     if out is None:
         out = torch.empty(x.shape, dtype=torch.float32, device=dev)
+    if out.dtype != torch.float32 or out.shape != x.shape or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 tensor of x's shape (wall_prefix_append "
+                         "writes into row slices)")
     nbytes = prefix_scan_workspace_size(B, T, C)
     if workspace is None:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
@@ -162,6 +165,15 @@ def wall_prefix_scan(x: torch.Tensor, cu_seqlens: Optional[torch.Tensor] = None,
                                   float(scale), _ptr(workspace), workspace.numel(), _stream(dev)),
            "wall_prefix_scan")
     return out
+
+
+def _out(t: Optional[torch.Tensor], shape, dtype: torch.dtype, dev: torch.device, what: str) -> torch.Tensor:
+    """A caller-provided output (checked: shape, dtype, dense) or a new one."""
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=dev)
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous():
+        raise ValueError(f"{what} must be a contiguous {dtype} tensor of shape {tuple(shape)}")
+    return t
 
 
 def _rows(t: torch.Tensor, n: int, C: int, what: str) -> int:
@@ -232,10 +244,9 @@ def wall_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, P: torch.Te
     nseq = 0 if cu is None else cu.numel() - 1
     if cu is not None and max_seqlen is None:
         max_seqlen = int((cu[1:] - cu[:-1]).max().item())
-    if out is None:
-        out = torch.empty((B, T, HQ, V), dtype=q.dtype, device=dev)
-    if lse is None and return_lse:
-        lse = torch.empty((B, T, HQ), dtype=torch.float32, device=dev)
+    out = _out(out, (B, T, HQ, V), q.dtype, dev, "out")
+    if lse is not None or return_lse:
+        lse = _out(lse, (B, T, HQ), torch.float32, dev, "lse")
     nbytes = attn_fwd_workspace_size(q.dtype, B, T, HQ, H, K, V, nseq)
     if workspace is None:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
@@ -406,6 +417,8 @@ def build_wall_kv_cache(k: torch.Tensor, P: torch.Tensor, chunk_size: int = 64,
         raise ValueError("k_tilde must be [B,T,HQ,K] and r_cache [B,ceil(T/C),HQ,K]")
     if not (k_tilde.is_contiguous() and r_cache.is_contiguous()):
         raise ValueError("k_tilde and r_cache must be contiguous")
+    if k_tilde.dtype != k.dtype or r_cache.dtype != torch.float32:
+        raise TypeError("k_tilde has k's dtype and r_cache is float32")
     t1 = T if t1 is None else int(t1)
     _check(lib().wall_kv_cache_build(_ptr(k), _dtype(k), _ptr(P), _ptr(k_tilde), _ptr(r_cache), B, T,
                                       HQ, H, K, int(chunk_size), int(t0), t1, _stream(dev)),
@@ -445,10 +458,8 @@ def wall_attn_decode(q: torch.Tensor, v: torch.Tensor, p_curr: torch.Tensor, k_t
         sink_bias = _dense(sink_bias.to(torch.float32))
     if scale is None:
         scale = K ** -0.5
-    if out is None:
-        out = torch.empty((B, 1, HQ, V), dtype=q.dtype, device=dev)
-    if lse is None:
-        lse = torch.empty((B, 1, HQ), dtype=torch.float32, device=dev)
+    out = _out(out, (B, 1, HQ, V), q.dtype, dev, "out")
+    lse = _out(lse, (B, 1, HQ), torch.float32, dev, "lse")
     if workspace is None:
         workspace = torch.empty(decode_workspace_size(B, T, HQ, V), dtype=torch.uint8, device=dev)
     _check(lib().wall_attn_decode(
