@@ -164,3 +164,43 @@ def test_backward_full_size_sampled():
         mx, rms = dd.max(), math.sqrt((dd ** 2).mean())
         say(f"  {name}: max|d|={mx:.3e} (ref max {rmax:.3e})  rms={rms:.3e} (ref rms {rrms:.3e})")
         assert mx <= tmax * rmax and rms <= trms * rrms, name
+
+
+def test_backward_options_full_size_sampled():
+    """options_bf16 at its full size (B=4, T=4096, HQ=32, H=8, window 1024,
+    g_scalar, sink), upstream gradient zero after row R0 = 1536 (past the
+    window, so it takes effect).  Batch element 0 is checked against the
+    oracle's backward of its first R0 rows; the other elements only for
+    their zero tails."""
+    R0 = 1536
+    inp = make_inputs("options_bf16")
+    B, T, HQ, K = inp.q.shape
+    V = inp.v.shape[3]
+    say(f"backward options full size B={B} T={T} HQ={HQ} W={inp.window_size}, upstream gradient on rows < {R0}")
+    rng = np.random.default_rng(23)
+    do = torch.zeros((B, T, HQ, V), dtype=inp.q.dtype)
+    do[:, :R0] = torch.from_numpy(rng.standard_normal((B, R0, HQ, V))).to(inp.q.dtype)
+    d = inp.to(DEV)
+    P = wall.wall_prefix_scan(d.g)
+    G = wall.wall_prefix_scan(d.g_scalar)
+    o, lse = wall.wall_attn_fwd(d.q, d.k, d.v, P, G, d.sink_bias, d.scale, d.window_size)
+    grads = wall.wall_attn_bwd(d.q, d.k, d.v, P, o, lse, do.to(DEV), G, d.sink_bias, d.scale, d.window_size,
+                               g_dtype=d.g.dtype)
+    torch.cuda.synchronize()
+    s = (slice(0, 1), slice(0, R0))
+    ref = oracle.wall_attn_bwd_oracle(inp.q[s], inp.k[s], inp.v[s], inp.g[s], do[s], scale=inp.scale,
+                                      g_scalar=inp.g_scalar[s], sink_bias=inp.sink_bias,
+                                      window_size=inp.window_size)
+    tmax, trms = TOL["bfloat16"]
+    for name, gg, rr in zip(["dq", "dk", "dv", "dg", "dg_scalar"], grads[:5], ref[:5]):
+        x = f64(gg)
+        rmax = np.abs(rr).max()
+        if name in ("dg", "dg_scalar"):
+            assert np.abs(x[:, R0:]).max() <= tmax * rmax, f"{name} after the last row with a gradient"
+        else:
+            assert not x[:, R0:].any(), f"{name}: nonzero gradient after row {R0}"
+        dd = np.abs(x[:1, :R0] - rr)
+        mx, rms = dd.max(), math.sqrt((dd ** 2).mean())
+        rrms = math.sqrt((rr ** 2).mean())
+        say(f"  {name}: max|d|={mx:.3e} (ref max {rmax:.3e})  rms={rms:.3e} (ref rms {rrms:.3e})")
+        assert mx <= tmax * rmax and rms <= trms * rrms, name
