@@ -23,10 +23,11 @@
 //
 // dk/dv (per key block, queries from the block's first key on):
 //   S  = q~ k~^T,  dP = do v^T   (32 streamed queries x the wave's 32 keys);
-//   A, dS in-lane;  dv += A^T do,  dk += dS^T q~.
-// The dq kernel fits two waves per SIMD (its own rows' q~ and do operands,
-// the dq accumulators and one tile of prefetch registers); the dk/dv kernel,
-// with both the dk and dv accumulators, runs one.
+//   A, dS in-lane;  dv += A^T do (dv waves),  dk += dS^T q~ (dk waves).
+// Both kernels run two waves per SIMD: the dq kernel holds its own rows' q~
+// and do operands, the dq accumulators and one tile of prefetch registers;
+// the dk/dv kernel splits its eight waves into a dk role and a dv role over
+// the same staged tiles, so no wave holds both accumulator sets.
 //
 // dq (per query block, keys up to the block's last query):
 //   S^T = k~ q~^T, dP^T = v do^T (32 streamed keys x the wave's 32 queries);
@@ -114,12 +115,17 @@ __device__ inline BlockPos block_pos(const BwdArgs &a, int nblk, bool heavy_firs
 }
 
 // ---------------------------------------------------------------- dk, dv
+// Eight waves in two roles over the same staged tiles: waves 0-3 own 32 keys
+// each for dk (S, dP, dS, dk += dS^T q~, and the X and Y updates), waves 4-7
+// the same keys for dv (S, A, dv += A^T do).  Each role holds one accumulator
+// set, so both fit two waves per SIMD; S is formed by both roles.
+constexpr int NTH_KV = 2 * NTH;
+
 template <int K, int V, bool HAS_G>
-__global__ __launch_bounds__(NTH) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
+__global__ __launch_bounds__(NTH_KV) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
     constexpr int RPK = K + 8, RPV = V + 8;
     constexpr int CK = BT * K / 8, CV = BT * V / 8;  // 8-element chunks per tile
-    constexpr int UK = CK / NTH, UV = CV / NTH;
-    static_assert(CK % NTH == 0 && CV % NTH == 0, "tile chunks");
+    constexpr int UK = (CK + NTH_KV - 1) / NTH_KV, UV = (CV + NTH_KV - 1) / NTH_KV;
     // two buffers of each streamed tile: one read while the other is filled
     __shared__ __attribute__((aligned(16))) __bf16 sQ[2][rows_size<RPK>()];  // q~ rows
     __shared__ __attribute__((aligned(16))) __bf16 sQT[2][K * TP];           // q~ transposed
@@ -147,39 +153,6 @@ __global__ __launch_bounds__(NTH) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
     if (tid < K) sR[tid] = floorf(a.P[(s0 + j0 + min(ANCHOR_ROW, jn - 1)) * HQ * K + hq * K + tid]);
     __syncthreads();
 
-    // the wave's keys as second operands: k~ and v rows of key jw + l32
-    const int jw = j0 + 32 * w, j = jw + l32;
-    const bool jok = j < len;
-    const int64_t tj = s0 + (jok ? j : 0);
-    bf16x8 kop[K / 16], vop[V / 16];
-#pragma unroll
-    for (int s = 0; s < K / 16; ++s) {
-        const int ch = 16 * s + 8 * hl;
-        f32x8 x = 0.f;
-        if (jok) {
-            const f32x8 kk = to_f32(*reinterpret_cast<const uint4 *>(kg + (tj * a.H + h) * K + ch));
-            const float *pp = a.P + (tj * HQ + hq) * K + ch;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = kk[e] * clamp2(sR[ch + e] - pp[e]);
-        }
-        kop[s] = __builtin_convertvector(x, bf16x8);
-    }
-#pragma unroll
-    for (int s = 0; s < V / 16; ++s) {
-        const int ch = 16 * s + 8 * hl;
-        uint4 raw = {0, 0, 0, 0};
-        if (jok) raw = *reinterpret_cast<const uint4 *>(vg + (tj * a.H + h) * V + ch);
-        vop[s] = __builtin_bit_cast(bf16x8, raw);
-    }
-    const float gj = (HAS_G && jok) ? a.G[tj * HQ + hq] : 0.f;
-
-    f32x16 dk[K / 32], dv[V / 32];
-#pragma unroll
-    for (int n = 0; n < K / 32; ++n) dk[n] = 0.f;
-#pragma unroll
-    for (int n = 0; n < V / 32; ++n) dv[n] = 0.f;
-    float colsum = 0.f;
-
     const int qend = a.window > 0 ? min(len, j0 + jn - 1 + a.window) : len;
 
     // prefetch registers for one tile
@@ -187,20 +160,23 @@ __global__ __launch_bounds__(NTH) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
     f32x8 praw[UK];
     float il = 0.f, id = 0.f, ig = 0.f;
     auto load_tile = [&](int q0) {
-#pragma unroll
         // rows past the sequence load its last row (in bounds) and are zeroed when stored
+#pragma unroll
         for (int u = 0; u < UK; ++u) {
-            const int c = tid + NTH * u, r = c % BT, ch = 8 * (c / BT), i = min(q0 + r, len - 1);
-            const int64_t t = (s0 + i) * HQ + hq;
-            qraw[u] = *reinterpret_cast<const uint4 *>(qg + t * K + ch);
-            const f32x4 *pp = reinterpret_cast<const f32x4 *>(a.P + t * K + ch);
-            const f32x4 p0 = pp[0], p1 = pp[1];
-            praw[u] = f32x8{p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+            const int c = tid + NTH_KV * u, r = c % BT, ch = 8 * (c / BT), i = min(q0 + r, len - 1);
+            if (CK % NTH_KV == 0 || c < CK) {
+                const int64_t t = (s0 + i) * HQ + hq;
+                qraw[u] = *reinterpret_cast<const uint4 *>(qg + t * K + ch);
+                const f32x4 *pp = reinterpret_cast<const f32x4 *>(a.P + t * K + ch);
+                const f32x4 p0 = pp[0], p1 = pp[1];
+                praw[u] = f32x8{p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+            }
         }
 #pragma unroll
         for (int u = 0; u < UV; ++u) {
-            const int c = tid + NTH * u, r = c % BT, ch = 8 * (c / BT), i = min(q0 + r, len - 1);
-            oraw[u] = *reinterpret_cast<const uint4 *>(dog + ((s0 + i) * HQ + hq) * V + ch);
+            const int c = tid + NTH_KV * u, r = c % BT, ch = 8 * (c / BT), i = min(q0 + r, len - 1);
+            if (CV % NTH_KV == 0 || c < CV)
+                oraw[u] = *reinterpret_cast<const uint4 *>(dog + ((s0 + i) * HQ + hq) * V + ch);
         }
         if (tid < BT) {
             const int i = q0 + tid;
@@ -216,25 +192,29 @@ __global__ __launch_bounds__(NTH) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
     auto store_tile = [&](int buf, int q0) {
 #pragma unroll
         for (int u = 0; u < UK; ++u) {
-            const int c = tid + NTH * u, r = c % BT, ch = 8 * (c / BT);
-            const f32x8 qq = to_f32(qraw[u]);
-            f32x8 x;
+            const int c = tid + NTH_KV * u, r = c % BT, ch = 8 * (c / BT);
+            if (CK % NTH_KV == 0 || c < CK) {
+                const f32x8 qq = to_f32(qraw[u]);
+                f32x8 x;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = qq[e] * a.qscale * clamp2(praw[u][e] - sR[ch + e]);
-            if (q0 + r >= len) x = 0.f;
-            const bf16x8 b = __builtin_convertvector(x, bf16x8);
-            *reinterpret_cast<bf16x8 *>(&sQ[buf][roff<RPK>(r, ch / 8)]) = b;
+                for (int e = 0; e < 8; ++e) x[e] = qq[e] * a.qscale * clamp2(praw[u][e] - sR[ch + e]);
+                if (q0 + r >= len) x = 0.f;
+                const bf16x8 b = __builtin_convertvector(x, bf16x8);
+                *reinterpret_cast<bf16x8 *>(&sQ[buf][roff<RPK>(r, ch / 8)]) = b;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) sQT[buf][(ch + e) * TP + r] = b[e];
+                for (int e = 0; e < 8; ++e) sQT[buf][(ch + e) * TP + r] = b[e];
+            }
         }
 #pragma unroll
         for (int u = 0; u < UV; ++u) {
-            const int c = tid + NTH * u, r = c % BT, ch = 8 * (c / BT);
-            const uint4 z = {0, 0, 0, 0};
-            const bf16x8 b = __builtin_bit_cast(bf16x8, q0 + r < len ? oraw[u] : z);
-            *reinterpret_cast<bf16x8 *>(&sO[buf][roff<RPV>(r, ch / 8)]) = b;
+            const int c = tid + NTH_KV * u, r = c % BT, ch = 8 * (c / BT);
+            if (CV % NTH_KV == 0 || c < CV) {
+                const uint4 z = {0, 0, 0, 0};
+                const bf16x8 b = __builtin_bit_cast(bf16x8, q0 + r < len ? oraw[u] : z);
+                *reinterpret_cast<bf16x8 *>(&sO[buf][roff<RPV>(r, ch / 8)]) = b;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) sOT[buf][(ch + e) * TP + r] = b[e];
+                for (int e = 0; e < 8; ++e) sOT[buf][(ch + e) * TP + r] = b[e];
+            }
         }
         if (tid < BT) {
             sL[buf][tid] = il;
@@ -251,105 +231,146 @@ __global__ __launch_bounds__(NTH) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
     store_tile(0, j0);
     __syncthreads();
     if (j0 + BT < qend) load_tile(j0 + BT);
-    for (int q0 = j0, it = 0; q0 < qend; q0 += BT, ++it) {
-        const int cur = it & 1;
-        // Every wave runs every tile: a tile with no visible pair for its keys
-        // (at most the first three, or three past the window) is masked to
-        // zero, and the accumulators stay on one straight path through the
-        // loop.
-        {
 
-        f32x16 S = 0.f, dP = 0.f;
-        const int qrow = swap23(l32);
+    // One role's whole walk over the query tiles; the two instantiations keep
+    // their accumulators apart.  Every wave runs every tile: a tile with no
+    // visible pair for its keys (at most the first three, or three past the
+    // window) is masked to zero, and the accumulators stay on one straight
+    // path through the loop.
+    auto walk = [&](auto dk_role) {
+        constexpr bool DK = decltype(dk_role)::value;
+        constexpr int NA = DK ? K / 32 : V / 32;
+        const int jw = j0 + 32 * (w % NW), j = jw + l32;
+        const bool jok = j < len;
+        const int64_t tj = s0 + (jok ? j : 0);
+        // the wave's keys as second operands: k~ (and v for dP) rows of key j
+        bf16x8 kop[K / 16], vop[DK ? V / 16 : 1];
 #pragma unroll
-        for (int s = 0; s < K / 16; ++s) S = mfma(lds8(&sQ[cur][roff<RPK>(qrow, 2 * s + hl)]), kop[s], S);
+        for (int s = 0; s < K / 16; ++s) {
+            const int ch = 16 * s + 8 * hl;
+            f32x8 x = 0.f;
+            if (jok) {
+                const f32x8 kk = to_f32(*reinterpret_cast<const uint4 *>(kg + (tj * a.H + h) * K + ch));
+                const float *pp = a.P + (tj * HQ + hq) * K + ch;
 #pragma unroll
-        for (int s = 0; s < V / 16; ++s) dP = mfma(lds8(&sO[cur][roff<RPV>(qrow, 2 * s + hl)]), vop[s], dP);
-
-        // the tile's per-query values, read before any use so the reads
-        // overlap; the exps are taken unconditionally and masked by a select
-        f32x4 L4[2][2], D4[2][2], G4[2][2];
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-#pragma unroll
-            for (int x = 0; x < 2; ++x) {
-                const int qi = 16 * c + 8 * hl + 4 * x;
-                L4[c][x] = *reinterpret_cast<const f32x4 *>(&sL[cur][qi]);
-                D4[c][x] = *reinterpret_cast<const f32x4 *>(&sD[cur][qi]);
-                if (HAS_G) G4[c][x] = *reinterpret_cast<const f32x4 *>(&sGq[cur][qi]);
+                for (int e = 0; e < 8; ++e) x[e] = kk[e] * clamp2(sR[ch + e] - pp[e]);
             }
-        // every pair of the tile visible: no mask
-        const bool full = jw + 31 < len && q0 >= jw + 31 && q0 + BT <= len &&
-                          (a.window <= 0 || q0 + BT - 1 - jw < a.window);
-        bf16x8 pb[2], db[2];
-        // two copies of the softmax step: without the mask for a full tile,
-        // with it for the diagonal, the window edge and a sequence's end
-        auto softmax = [&](auto masked) {
+            kop[s] = __builtin_convertvector(x, bf16x8);
+        }
+        if constexpr (DK) {
 #pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                const int qi0 = 16 * c + 8 * hl;
-                f32x8 pv, dv8;
+            for (int s = 0; s < V / 16; ++s) {
+                const int ch = 16 * s + 8 * hl;
+                uint4 raw = {0, 0, 0, 0};
+                if (jok) raw = *reinterpret_cast<const uint4 *>(vg + (tj * a.H + h) * V + ch);
+                vop[s] = __builtin_bit_cast(bf16x8, raw);
+            }
+        }
+        const float gj = (HAS_G && jok) ? a.G[tj * HQ + hq] : 0.f;
+        f32x16 acc[NA];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float lse2 = L4[c][e / 4][e % 4], Di = D4[c][e / 4][e % 4];
-                    const float Gi = HAS_G ? G4[c][e / 4][e % 4] : 0.f;
-                    float p = __builtin_amdgcn_exp2f(S[8 * c + e] + Gi - gj - lse2);
-                    if constexpr (decltype(masked)::value) {
-                        const int i = q0 + qi0 + e;
-                        const bool vis = jok && i >= j && i < len && (a.window <= 0 || i - j < a.window);
-                        p = vis ? p : 0.f;
+        for (int n = 0; n < NA; ++n) acc[n] = 0.f;
+        float colsum = 0.f;
+
+        for (int q0 = j0, it = 0; q0 < qend; q0 += BT, ++it) {
+            const int cur = it & 1;
+            const int qrow = swap23(l32);
+            f32x16 S = 0.f, dP = 0.f;
+#pragma unroll
+            for (int s = 0; s < K / 16; ++s) S = mfma(lds8(&sQ[cur][roff<RPK>(qrow, 2 * s + hl)]), kop[s], S);
+            if constexpr (DK) {
+#pragma unroll
+                for (int s = 0; s < V / 16; ++s)
+                    dP = mfma(lds8(&sO[cur][roff<RPV>(qrow, 2 * s + hl)]), vop[s], dP);
+            }
+            // every pair of the tile visible: no mask
+            const bool full = jw + 31 < len && q0 >= jw + 31 && q0 + BT <= len &&
+                              (a.window <= 0 || q0 + BT - 1 - jw < a.window);
+            bf16x8 ob[2];  // A (dv role) or dS (dk role), the first operand of the last product
+            // two copies of the softmax step: without the mask for a full tile,
+            // with it for the diagonal, the window edge and a sequence's end
+            auto softmax = [&](auto masked) {
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    const int qi0 = 16 * c + 8 * hl;
+                    // the 8 rows' values, read unconditionally ahead of their use
+                    f32x4 L4[2], D4[2], G4[2];
+#pragma unroll
+                    for (int x = 0; x < 2; ++x) {
+                        L4[x] = *reinterpret_cast<const f32x4 *>(&sL[cur][qi0 + 4 * x]);
+                        if (DK) D4[x] = *reinterpret_cast<const f32x4 *>(&sD[cur][qi0 + 4 * x]);
+                        if (HAS_G) G4[x] = *reinterpret_cast<const f32x4 *>(&sGq[cur][qi0 + 4 * x]);
                     }
-                    const float ds = p * (dP[8 * c + e] - Di);
-                    colsum += ds;
-                    pv[e] = p;
-                    dv8[e] = ds;
+                    f32x8 o8;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float lse2 = L4[e / 4][e % 4];
+                        const float Gi = HAS_G ? G4[e / 4][e % 4] : 0.f;
+                        float p = __builtin_amdgcn_exp2f(S[8 * c + e] + Gi - gj - lse2);
+                        if constexpr (decltype(masked)::value) {
+                            const int i = q0 + qi0 + e;
+                            const bool vis = jok && i >= j && i < len && (a.window <= 0 || i - j < a.window);
+                            p = vis ? p : 0.f;
+                        }
+                        if constexpr (DK) {
+                            const float ds = p * (dP[8 * c + e] - D4[e / 4][e % 4]);
+                            colsum += ds;
+                            o8[e] = ds;
+                        } else {
+                            o8[e] = p;
+                        }
+                    }
+                    ob[c] = __builtin_convertvector(o8, bf16x8);
                 }
-                pb[c] = __builtin_convertvector(pv, bf16x8);
-                db[c] = __builtin_convertvector(dv8, bf16x8);
-            }
-        };
-        if (full)
-            softmax(std::false_type{});
-        else
-            softmax(std::true_type{});
+            };
+            if (full)
+                softmax(std::false_type{});
+            else
+                softmax(std::true_type{});
 #pragma unroll
-        for (int n = 0; n < V / 32; ++n)
+            for (int n = 0; n < NA; ++n)
 #pragma unroll
-            for (int c = 0; c < 2; ++c)
-                dv[n] = mfma(pb[c], lds8(&sOT[cur][(32 * n + l32) * TP + 16 * c + 8 * hl]), dv[n]);
-#pragma unroll
-        for (int n = 0; n < K / 32; ++n)
-#pragma unroll
-            for (int c = 0; c < 2; ++c)
-                dk[n] = mfma(db[c], lds8(&sQT[cur][(32 * n + l32) * TP + 16 * c + 8 * hl]), dk[n]);
+                for (int c = 0; c < 2; ++c) {
+                    const __bf16 *src = DK ? &sQT[cur][(32 * n + l32) * TP + 16 * c + 8 * hl]
+                                           : &sOT[cur][(32 * n + l32) * TP + 16 * c + 8 * hl];
+                    acc[n] = mfma(ob[c], lds8(src), acc[n]);
+                }
+            if (q0 + BT < qend) store_tile(cur ^ 1, q0 + BT);
+            __syncthreads();
+            if (q0 + 2 * BT < qend) load_tile(q0 + 2 * BT);
         }
-        if (q0 + BT < qend) store_tile(cur ^ 1, q0 + BT);
-        __syncthreads();
-        if (q0 + 2 * BT < qend) load_tile(q0 + 2 * BT);
-    }
 
-    if (jw >= len) return;
-    colsum += __shfl_xor(colsum, 32);
-    if (hl == 0 && jok) a.Y[tj * HQ + hq] -= colsum;
-    // accumulator register r of lane (l32, hl): key jw + 8(r/4) + 4hl + r%4, channel 32n + l32
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int jr = jw + 8 * (r / 4) + 4 * hl + (r % 4);
-        if (jr >= len) continue;
-        const int64_t t = s0 + jr;
-#pragma unroll
-        for (int n = 0; n < K / 32; ++n) {
-            const int ch = 32 * n + l32;
-            const int64_t ix = (t * HQ + hq) * K + ch;
-            const float f = clamp2(sR[ch] - a.P[ix]);
-            a.dkp[ix] = LN2 * f * dk[n][r];
-            // k (.) dk^(hq) from the bf16 k~ the dq products used (see the X note above)
-            const float kt = (float)(__bf16)((float)kg[(t * a.H + h) * K + ch] * f);
-            a.X[ix] -= LN2 * kt * dk[n][r];
+        if (jw >= len) return;
+        if constexpr (DK) {
+            colsum += __shfl_xor(colsum, 32);
+            if (hl == 0 && jok) a.Y[tj * HQ + hq] -= colsum;
         }
+        // accumulator register r of lane (l32, hl): key jw + 8(r/4) + 4hl + r%4, channel 32n + l32
 #pragma unroll
-        for (int n = 0; n < V / 32; ++n) a.dvp[(t * HQ + hq) * V + 32 * n + l32] = dv[n][r];
-    }
+        for (int r = 0; r < 16; ++r) {
+            const int jr = jw + 8 * (r / 4) + 4 * hl + (r % 4);
+            if (jr >= len) continue;
+            const int64_t t = s0 + jr;
+#pragma unroll
+            for (int n = 0; n < NA; ++n) {
+                const int ch = 32 * n + l32;
+                if constexpr (DK) {
+                    const int64_t ix = (t * HQ + hq) * K + ch;
+                    const float f = clamp2(sR[ch] - a.P[ix]);
+                    a.dkp[ix] = LN2 * f * acc[n][r];
+                    // k (.) dk^(hq) from the bf16 k~ the dq products used (see the X note above)
+                    const float kt = (float)(__bf16)((float)kg[(t * a.H + h) * K + ch] * f);
+                    a.X[ix] -= LN2 * kt * acc[n][r];
+                } else {
+                    a.dvp[(t * HQ + hq) * V + ch] = acc[n][r];
+                }
+            }
+        }
+    };
+    if (w < NW)
+        walk(std::true_type{});
+    else
+        walk(std::false_type{});
 }
 
 // ---------------------------------------------------------------- dq
@@ -481,14 +502,6 @@ __global__ __launch_bounds__(NTH, 2) void bwd_dq_mfma(BwdArgs a, int nblk) {
 #pragma unroll
         for (int s = 0; s < V / 16; ++s) dP = mfma(lds8(&sV[cur][roff<RPV>(krow, 2 * s + hl)]), oop[s], dP);
 
-        f32x4 G4[2][2];
-        if (HAS_G) {
-#pragma unroll
-            for (int c = 0; c < 2; ++c)
-#pragma unroll
-                for (int x = 0; x < 2; ++x)
-                    G4[c][x] = *reinterpret_cast<const f32x4 *>(&sGk[cur][16 * c + 8 * hl + 4 * x]);
-        }
         // every pair of the tile visible: no mask
         const bool full = iw + 31 < len && k0 + BT - 1 <= iw &&
                           (a.window <= 0 || iw + 31 - k0 < a.window);
@@ -497,10 +510,15 @@ __global__ __launch_bounds__(NTH, 2) void bwd_dq_mfma(BwdArgs a, int nblk) {
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
                 const int kj0 = 16 * c + 8 * hl;
+                f32x4 G4[2];
+                if (HAS_G) {
+#pragma unroll
+                    for (int x = 0; x < 2; ++x) G4[x] = *reinterpret_cast<const f32x4 *>(&sGk[cur][kj0 + 4 * x]);
+                }
                 f32x8 d8;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const float Gj = HAS_G ? G4[c][e / 4][e % 4] : 0.f;
+                    const float Gj = HAS_G ? G4[e / 4][e % 4] : 0.f;
                     float p = __builtin_amdgcn_exp2f(S[8 * c + e] + Gi - Gj - lse2);
                     if constexpr (decltype(masked)::value) {
                         const int jj = k0 + kj0 + e;
@@ -586,7 +604,7 @@ hipError_t run(const BwdArgs &a, hipStream_t st) {
     hipLaunchKernelGGL((bwd_dq_mfma<K, V, HAS_G>), dim3(nb), dim3(NTH), 0, st, a, nblk);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_dkdv_mfma<K, V, HAS_G>), dim3(nb), dim3(NTH), 0, st, a, nblk);
+    hipLaunchKernelGGL((bwd_dkdv_mfma<K, V, HAS_G>), dim3(nb), dim3(NTH_KV), 0, st, a, nblk);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t nrow_h = (int64_t)a.rows * a.H;
