@@ -264,6 +264,9 @@ wall_status_t wall_attn_bwd(const void *q, const void *k, const void *v, wall_dt
     a.Z = reinterpret_cast<float *>(ws + L.off_Z);
     a.dkp = reinterpret_cast<float *>(ws + L.off_part);
     a.dvp = a.dkp + B * T * HQ * K;
+    a.qh = ws + L.off_qh;
+    a.kh = ws + L.off_kh;
+    a.Rt = reinterpret_cast<float *>(ws + L.off_rt);
     a.seg = seg;
     a.nseg = (int32_t)nseg;
     a.max_seqlen = (int32_t)(cu_seqlens ? max_seqlen : T);

@@ -54,10 +54,31 @@ __device__ inline void st(T *p, float x) { *p = (T)x; }
 __device__ inline float clamp2(float e) { return exp2f(fminf(fmaxf(e, EXP2_LO), EXP2_HI)); }
 
 // ---------------------------------------------------------------- sequence table
+// One block of 256: per sequence its start, length and the index of its
+// first 128-row tile (an inclusive scan of the tile counts, 256 at a time).
 __global__ void bwd_seg_kernel(SegInfo *seg, const int32_t *cu, int nseg, int T) {
-    for (int s = threadIdx.x; s < nseg; s += blockDim.x) {
-        if (cu) seg[s] = SegInfo{cu[s], cu[s + 1] - cu[s], 0, 0};
-        else seg[s] = SegInfo{s * T, T, 0, 0};
+    __shared__ int part[256];
+    const int tid = threadIdx.x;
+    int base = 0;
+    for (int s0 = 0; s0 < nseg; s0 += 256) {
+        const int s = s0 + tid;
+        int start = 0, len = 0;
+        if (s < nseg) {
+            start = cu ? cu[s] : s * T;
+            len = cu ? cu[s + 1] - cu[s] : T;
+        }
+        const int cnt = (len + TILE - 1) / TILE;
+        part[tid] = cnt;
+        __syncthreads();
+        for (int off = 1; off < 256; off <<= 1) {
+            const int v = tid >= off ? part[tid - off] : 0;
+            __syncthreads();
+            part[tid] += v;
+            __syncthreads();
+        }
+        if (s < nseg) seg[s] = SegInfo{start, len, base + part[tid] - cnt, 0};
+        base += part[255];
+        __syncthreads();
     }
 }
 

@@ -114,6 +114,57 @@ __device__ inline BlockPos block_pos(const BwdArgs &a, int nblk, bool heavy_firs
     return p;
 }
 
+// ---------------------------------------------------------------- tile anchors, q~ and k~
+// Per (128-row tile, query head): R = floor(P) at the tile's middle row, and
+// every row's q~ = q scale log2e 2^(P - R) and k~ = k 2^(R - P) in bf16.  The
+// dq and dk/dv kernels use their own tile's rows as they are and move a
+// streamed tile to their block's anchor by the integer difference of the two
+// anchors: an exact power of two, applied with v_ldexp_f32 instead of an
+// exp2 per element.
+template <int K>
+__global__ __launch_bounds__(256) void bwd_anchor_kernel(BwdArgs a) {
+    __shared__ float sR[K];
+    const int tile = blockIdx.x, hq = blockIdx.y % a.HQ;
+    const SegInfo sg = a.seg[blockIdx.y / a.HQ];
+    const int r0 = tile * BR;
+    if (r0 >= sg.len) return;
+    const int n = min(BR, sg.len - r0), tid = threadIdx.x;
+    const int64_t HQ = a.HQ, s0 = sg.start;
+    const int h = hq / (a.HQ / a.H);
+    if (tid < K) {
+        const float R = floorf(a.P[(s0 + r0 + min(ANCHOR_ROW, n - 1)) * HQ * K + hq * K + tid]);
+        sR[tid] = R;
+        a.Rt[((int64_t)(sg.tile_base + tile) * HQ + hq) * K + tid] = R;
+    }
+    __syncthreads();
+    const __bf16 *qg = static_cast<const __bf16 *>(a.q);
+    const __bf16 *kg = static_cast<const __bf16 *>(a.k);
+    __bf16 *qh = static_cast<__bf16 *>(a.qh);
+    __bf16 *kh = static_cast<__bf16 *>(a.kh);
+    for (int c = tid; c < n * (K / 8); c += 256) {
+        const int r = c / (K / 8), ch = 8 * (c % (K / 8));
+        const int64_t t = s0 + r0 + r, ix = (t * HQ + hq) * K + ch;
+        const f32x8 qq = to_f32(*reinterpret_cast<const uint4 *>(qg + ix));
+        const f32x8 kk = to_f32(*reinterpret_cast<const uint4 *>(kg + (t * a.H + h) * K + ch));
+        const f32x4 *pp = reinterpret_cast<const f32x4 *>(a.P + ix);
+        const f32x4 p0 = pp[0], p1 = pp[1];
+        f32x8 xq, xk;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float pv = e < 4 ? p0[e] : p1[e - 4];
+            xq[e] = qq[e] * a.qscale * clamp2(pv - sR[ch + e]);
+            xk[e] = kk[e] * clamp2(sR[ch + e] - pv);
+        }
+        *reinterpret_cast<bf16x8 *>(qh + ix) = __builtin_convertvector(xq, bf16x8);
+        *reinterpret_cast<bf16x8 *>(kh + ix) = __builtin_convertvector(xk, bf16x8);
+    }
+}
+
+// 2^(to - from) applied to an anchored value: from, to are integer anchors
+__device__ inline float shift_anchor(float x, float to, float from) {
+    return ldexpf(x, (int)fminf(fmaxf(to - from, -1000.0f), 1000.0f));
+}
+
 // ---------------------------------------------------------------- dk, dv
 // Eight waves in two roles over the same staged tiles: waves 0-3 own 32 keys
 // each for dk (S, dP, dS, dk += dS^T q~, and the X and Y updates), waves 4-7
@@ -145,8 +196,6 @@ __global__ __launch_bounds__(NTH_KV) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
     const int h = hq / (a.HQ / a.H);
     const int len = sg.len, jn = min(BR, len - j0);
     const int64_t s0 = sg.start;
-    const __bf16 *qg = static_cast<const __bf16 *>(a.q);
-    const __bf16 *kg = static_cast<const __bf16 *>(a.k);
     const __bf16 *vg = static_cast<const __bf16 *>(a.v);
     const __bf16 *dog = static_cast<const __bf16 *>(a.dout);
 
@@ -155,21 +204,23 @@ __global__ __launch_bounds__(NTH_KV) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
 
     const int qend = a.window > 0 ? min(len, j0 + jn - 1 + a.window) : len;
 
-    // prefetch registers for one tile
+    const __bf16 *qhg = static_cast<const __bf16 *>(a.qh);
+    const __bf16 *khg = static_cast<const __bf16 *>(a.kh);
+    // prefetch registers for one tile: q~ at its own tile's anchor and that anchor
     uint4 qraw[UK], oraw[UV];
-    f32x8 praw[UK];
+    f32x8 araw[UK];
     float il = 0.f, id = 0.f, ig = 0.f;
     auto load_tile = [&](int q0) {
         // rows past the sequence load its last row (in bounds) and are zeroed when stored
+        const float *rt = a.Rt + ((int64_t)(sg.tile_base + q0 / BR) * HQ + hq) * K;
 #pragma unroll
         for (int u = 0; u < UK; ++u) {
             const int c = tid + NTH_KV * u, r = c % BT, ch = 8 * (c / BT), i = min(q0 + r, len - 1);
             if (CK % NTH_KV == 0 || c < CK) {
-                const int64_t t = (s0 + i) * HQ + hq;
-                qraw[u] = *reinterpret_cast<const uint4 *>(qg + t * K + ch);
-                const f32x4 *pp = reinterpret_cast<const f32x4 *>(a.P + t * K + ch);
+                qraw[u] = *reinterpret_cast<const uint4 *>(qhg + ((s0 + i) * HQ + hq) * K + ch);
+                const f32x4 *pp = reinterpret_cast<const f32x4 *>(rt + ch);
                 const f32x4 p0 = pp[0], p1 = pp[1];
-                praw[u] = f32x8{p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+                araw[u] = f32x8{p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
             }
         }
 #pragma unroll
@@ -197,7 +248,7 @@ __global__ __launch_bounds__(NTH_KV) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
                 const f32x8 qq = to_f32(qraw[u]);
                 f32x8 x;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) x[e] = qq[e] * a.qscale * clamp2(praw[u][e] - sR[ch + e]);
+                for (int e = 0; e < 8; ++e) x[e] = shift_anchor(qq[e], araw[u][e], sR[ch + e]);
                 if (q0 + r >= len) x = 0.f;
                 const bf16x8 b = __builtin_convertvector(x, bf16x8);
                 *reinterpret_cast<bf16x8 *>(&sQ[buf][roff<RPK>(r, ch / 8)]) = b;
@@ -243,19 +294,15 @@ __global__ __launch_bounds__(NTH_KV) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
         const int jw = j0 + 32 * (w % NW), j = jw + l32;
         const bool jok = j < len;
         const int64_t tj = s0 + (jok ? j : 0);
-        // the wave's keys as second operands: k~ (and v for dP) rows of key j
+        // the wave's keys as second operands: k~ (its own tile's anchor is the
+        // block's) and, for dP, v rows of key j
         bf16x8 kop[K / 16], vop[DK ? V / 16 : 1];
 #pragma unroll
         for (int s = 0; s < K / 16; ++s) {
             const int ch = 16 * s + 8 * hl;
-            f32x8 x = 0.f;
-            if (jok) {
-                const f32x8 kk = to_f32(*reinterpret_cast<const uint4 *>(kg + (tj * a.H + h) * K + ch));
-                const float *pp = a.P + (tj * HQ + hq) * K + ch;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) x[e] = kk[e] * clamp2(sR[ch + e] - pp[e]);
-            }
-            kop[s] = __builtin_convertvector(x, bf16x8);
+            uint4 raw = {0, 0, 0, 0};
+            if (jok) raw = *reinterpret_cast<const uint4 *>(khg + (tj * HQ + hq) * K + ch);
+            kop[s] = __builtin_bit_cast(bf16x8, raw);
         }
         if constexpr (DK) {
 #pragma unroll
@@ -356,11 +403,9 @@ __global__ __launch_bounds__(NTH_KV) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
                 const int ch = 32 * n + l32;
                 if constexpr (DK) {
                     const int64_t ix = (t * HQ + hq) * K + ch;
-                    const float f = clamp2(sR[ch] - a.P[ix]);
-                    a.dkp[ix] = LN2 * f * acc[n][r];
+                    a.dkp[ix] = LN2 * clamp2(sR[ch] - a.P[ix]) * acc[n][r];
                     // k (.) dk^(hq) from the bf16 k~ the dq products used (see the X note above)
-                    const float kt = (float)(__bf16)((float)kg[(t * a.H + h) * K + ch] * f);
-                    a.X[ix] -= LN2 * kt * acc[n][r];
+                    a.X[ix] -= LN2 * (float)khg[ix] * acc[n][r];
                 } else {
                     a.dvp[(t * HQ + hq) * V + ch] = acc[n][r];
                 }
@@ -395,8 +440,6 @@ __global__ __launch_bounds__(NTH, 2) void bwd_dq_mfma(BwdArgs a, int nblk) {
     const int h = hq / (a.HQ / a.H);
     const int len = sg.len, in_ = min(BR, len - i0);
     const int64_t s0 = sg.start;
-    const __bf16 *qg = static_cast<const __bf16 *>(a.q);
-    const __bf16 *kg = static_cast<const __bf16 *>(a.k);
     const __bf16 *vg = static_cast<const __bf16 *>(a.v);
     const __bf16 *dog = static_cast<const __bf16 *>(a.dout);
 
@@ -407,18 +450,16 @@ __global__ __launch_bounds__(NTH, 2) void bwd_dq_mfma(BwdArgs a, int nblk) {
     const int iw = i0 + 32 * w, i = iw + l32;
     const bool iok = i < len;
     const int64_t ti = s0 + (iok ? i : 0);
+    const __bf16 *qhg = static_cast<const __bf16 *>(a.qh);
+    const __bf16 *khg = static_cast<const __bf16 *>(a.kh);
+    // the block is one tile: its rows' q~ are at the block's anchor already
     bf16x8 qop[K / 16], oop[V / 16];
 #pragma unroll
     for (int s = 0; s < K / 16; ++s) {
         const int ch = 16 * s + 8 * hl;
-        f32x8 x = 0.f;
-        if (iok) {
-            const f32x8 qq = to_f32(*reinterpret_cast<const uint4 *>(qg + (ti * HQ + hq) * K + ch));
-            const float *pp = a.P + (ti * HQ + hq) * K + ch;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = qq[e] * a.qscale * clamp2(pp[e] - sR[ch + e]);
-        }
-        qop[s] = __builtin_convertvector(x, bf16x8);
+        uint4 raw = {0, 0, 0, 0};
+        if (iok) raw = *reinterpret_cast<const uint4 *>(qhg + (ti * HQ + hq) * K + ch);
+        qop[s] = __builtin_bit_cast(bf16x8, raw);
     }
 #pragma unroll
     for (int s = 0; s < V / 16; ++s) {
@@ -439,19 +480,21 @@ __global__ __launch_bounds__(NTH, 2) void bwd_dq_mfma(BwdArgs a, int nblk) {
     const int ilast = i0 + in_ - 1;
     const int klo = a.window > 0 ? max(0, i0 - a.window + 1) / BT * BT : 0;
 
+    // prefetch registers for one tile: k~ at its own tile's anchor and that anchor
     uint4 kraw[UK], vraw[UV];
-    f32x8 praw[UK];
+    f32x8 araw[UK];
     float kgv = 0.f;
     auto load_tile = [&](int k0) {
-#pragma unroll
         // rows past the sequence load its last row (in bounds) and are zeroed when stored
+        const float *rt = a.Rt + ((int64_t)(sg.tile_base + k0 / BR) * HQ + hq) * K;
+#pragma unroll
         for (int u = 0; u < UK; ++u) {
             const int c = tid + NTH * u, r = c % BT, ch = 8 * (c / BT);
             const int64_t t = s0 + min(k0 + r, len - 1);
-            kraw[u] = *reinterpret_cast<const uint4 *>(kg + (t * a.H + h) * K + ch);
-            const f32x4 *pp = reinterpret_cast<const f32x4 *>(a.P + (t * HQ + hq) * K + ch);
+            kraw[u] = *reinterpret_cast<const uint4 *>(khg + (t * HQ + hq) * K + ch);
+            const f32x4 *pp = reinterpret_cast<const f32x4 *>(rt + ch);
             const f32x4 p0 = pp[0], p1 = pp[1];
-            praw[u] = f32x8{p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+            araw[u] = f32x8{p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
         }
 #pragma unroll
         for (int u = 0; u < UV; ++u) {
@@ -470,7 +513,7 @@ __global__ __launch_bounds__(NTH, 2) void bwd_dq_mfma(BwdArgs a, int nblk) {
             const f32x8 kk = to_f32(kraw[u]);
             f32x8 x;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = kk[e] * clamp2(sR[ch + e] - praw[u][e]);
+            for (int e = 0; e < 8; ++e) x[e] = shift_anchor(kk[e], sR[ch + e], araw[u][e]);
             if (k0 + r >= len) x = 0.f;
             const bf16x8 b = __builtin_convertvector(x, bf16x8);
             *reinterpret_cast<bf16x8 *>(&sK[buf][roff<RPK>(r, ch / 8)]) = b;
@@ -564,10 +607,8 @@ __global__ __launch_bounds__(NTH, 2) void bwd_dq_mfma(BwdArgs a, int nblk) {
         for (int n = 0; n < K / 32; ++n) {
             const int ch = 32 * n + l32;
             const int64_t ix = (t * HQ + hq) * K + ch;
-            const float f = clamp2(a.P[ix] - sR[ch]);
-            dqg[ix] = (__bf16)(a.scale * f * dq[n][r]);
-            const float qt = (float)(__bf16)((float)qg[ix] * a.qscale * f);
-            a.X[ix] = LN2 * qt * dq[n][r];
+            dqg[ix] = (__bf16)(a.scale * clamp2(a.P[ix] - sR[ch]) * dq[n][r]);
+            a.X[ix] = LN2 * (float)qhg[ix] * dq[n][r];
         }
     }
 }
@@ -601,8 +642,11 @@ template <int K, int V, bool HAS_G>
 hipError_t run(const BwdArgs &a, hipStream_t st) {
     const int nblk = (int)cdiv(a.max_seqlen, BR);
     const unsigned nb = (unsigned)((int64_t)a.HQ * a.nseg * nblk);
-    hipLaunchKernelGGL((bwd_dq_mfma<K, V, HAS_G>), dim3(nb), dim3(NTH), 0, st, a, nblk);
+    hipLaunchKernelGGL((bwd_anchor_kernel<K>), dim3((unsigned)nblk, (unsigned)(a.HQ * a.nseg)), dim3(256), 0, st, a);
     hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_dq_mfma<K, V, HAS_G>), dim3(nb), dim3(NTH), 0, st, a, nblk);
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_dkdv_mfma<K, V, HAS_G>), dim3(nb), dim3(NTH_KV), 0, st, a, nblk);
     e = hipGetLastError();

@@ -171,6 +171,8 @@ struct BwdArgs {
     float *dsink;                      // [HQ] or null
     float *D, *X, *Y, *Z;              // workspace: do.o; q.dq - k.dk per head; dS row - column sums; sink terms
     float *dkp, *dvp;                  // workspace: per query head dk [rows, HQ, K] and dv [rows, HQ, V] (bf16 path)
+    void *qh, *kh;                     // workspace (bf16 path): q~ and k~ [rows, HQ, K] bf16 at their own tile's anchor
+    float *Rt;                         // workspace (bf16 path): anchors [tiles, HQ, K], tile = seg.tile_base + row / 128
     const SegInfo *seg;
     int32_t nseg, max_seqlen, rows, HQ, H, K, V, window;
     float scale, qscale;               // scale, scale * log2(e)
@@ -182,7 +184,7 @@ hipError_t launch_bwd_mfma(const BwdArgs &a, hipStream_t st);  // the dq, dk/dv 
 constexpr int64_t BWD_MAX_V = 128;
 
 struct BwdLayout {
-    size_t off_seg, off_D, off_X, off_Y, off_Z, off_part, off_scan, total;
+    size_t off_seg, off_D, off_X, off_Y, off_Z, off_part, off_qh, off_kh, off_rt, off_scan, total;
 };
 inline BwdLayout bwd_layout(int64_t B, int64_t T, int64_t HQ, int64_t K, int64_t nseg) {
     BwdLayout L;
@@ -200,6 +202,12 @@ inline BwdLayout bwd_layout(int64_t B, int64_t T, int64_t HQ, int64_t K, int64_t
     o = align_up(o + sizeof(float) * rows * HQ, 256);
     L.off_part = o;
     o = align_up(o + sizeof(float) * rows * HQ * (K + BWD_MAX_V), 256);
+    L.off_qh = o;
+    o = align_up(o + 2 * rows * HQ * K, 256);
+    L.off_kh = o;
+    o = align_up(o + 2 * rows * HQ * K, 256);
+    L.off_rt = o;
+    o = align_up(o + sizeof(float) * (size_t)(cdiv((int64_t)rows, TILE) + nseg) * HQ * K, 256);
     L.off_scan = o;
     o = align_up(o + scan_layout(B, T, HQ * K).total, 256);
     L.total = o;
