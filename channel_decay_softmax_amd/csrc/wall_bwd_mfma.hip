@@ -167,9 +167,12 @@ __device__ inline float shift_anchor(float x, float to, float from) {
 
 // ---------------------------------------------------------------- dk, dv
 // Eight waves in two roles over the same staged tiles: waves 0-3 own 32 keys
-// each for dk (S, dP, dS, dk += dS^T q~, and the X and Y updates), waves 4-7
-// the same keys for dv (S, A, dv += A^T do).  Each role holds one accumulator
-// set, so both fit two waves per SIMD; S is formed by both roles.
+// each for dk (S, dP, A, dS, dk += dS^T q~, and the X and Y updates), waves
+// 4-7 the same keys for dv (dv += A^T do).  A dk wave leaves its bf16 A in
+// LDS in the lane order of the dv product's first operand, and the dv wave
+// of the same keys consumes it one tile later (after the tile's barrier), so
+// no barrier is added; do^T keeps three buffers for that lag.  Each role
+// holds one accumulator set, so both fit two waves per SIMD.
 constexpr int NTH_KV = 2 * NTH;
 
 template <int K, int V, bool HAS_G>
@@ -181,7 +184,8 @@ __global__ __launch_bounds__(NTH_KV) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
     __shared__ __attribute__((aligned(16))) __bf16 sQ[2][rows_size<RPK>()];  // q~ rows
     __shared__ __attribute__((aligned(16))) __bf16 sQT[2][K * TP];           // q~ transposed
     __shared__ __attribute__((aligned(16))) __bf16 sO[2][rows_size<RPV>()];  // do rows
-    __shared__ __attribute__((aligned(16))) __bf16 sOT[2][V * TP];           // do transposed
+    __shared__ __attribute__((aligned(16))) __bf16 sOT[3][V * TP];           // do transposed
+    __shared__ __attribute__((aligned(16))) __bf16 sP[2][NW][2][64 * 8];     // A from the dk waves
     __shared__ __attribute__((aligned(16))) float sL[2][BT];
     __shared__ __attribute__((aligned(16))) float sD[2][BT];
     __shared__ __attribute__((aligned(16))) float sGq[2][BT];
@@ -240,7 +244,7 @@ __global__ __launch_bounds__(NTH_KV) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
             }
         }
     };
-    auto store_tile = [&](int buf, int q0) {
+    auto store_tile = [&](int buf, int q0, int tix) {
 #pragma unroll
         for (int u = 0; u < UK; ++u) {
             const int c = tid + NTH_KV * u, r = c % BT, ch = 8 * (c / BT);
@@ -264,7 +268,7 @@ __global__ __launch_bounds__(NTH_KV) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
                 const bf16x8 b = __builtin_bit_cast(bf16x8, q0 + r < len ? oraw[u] : z);
                 *reinterpret_cast<bf16x8 *>(&sO[buf][roff<RPV>(r, ch / 8)]) = b;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) sOT[buf][(ch + e) * TP + r] = b[e];
+                for (int e = 0; e < 8; ++e) sOT[tix % 3][(ch + e) * TP + r] = b[e];
             }
         }
         if (tid < BT) {
@@ -279,7 +283,7 @@ __global__ __launch_bounds__(NTH_KV) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
     // which every wave finished reading before the previous barrier; one
     // barrier per tile.
     load_tile(j0);
-    store_tile(0, j0);
+    store_tile(0, j0, 0);
     __syncthreads();
     if (j0 + BT < qend) load_tile(j0 + BT);
 
@@ -291,20 +295,37 @@ __global__ __launch_bounds__(NTH_KV) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
     auto walk = [&](auto dk_role) {
         constexpr bool DK = decltype(dk_role)::value;
         constexpr int NA = DK ? K / 32 : V / 32;
-        const int jw = j0 + 32 * (w % NW), j = jw + l32;
+        const int wr = w % NW;
+        const int jw = j0 + 32 * wr, j = jw + l32;
         const bool jok = j < len;
         const int64_t tj = s0 + (jok ? j : 0);
-        // the wave's keys as second operands: k~ (its own tile's anchor is the
-        // block's) and, for dP, v rows of key j
-        bf16x8 kop[K / 16], vop[DK ? V / 16 : 1];
+        f32x16 acc[NA];
 #pragma unroll
-        for (int s = 0; s < K / 16; ++s) {
-            const int ch = 16 * s + 8 * hl;
-            uint4 raw = {0, 0, 0, 0};
-            if (jok) raw = *reinterpret_cast<const uint4 *>(khg + (tj * HQ + hq) * K + ch);
-            kop[s] = __builtin_bit_cast(bf16x8, raw);
-        }
+        for (int n = 0; n < NA; ++n) acc[n] = 0.f;
+        // dv += A^T do for tile tix, A left in LDS by the dk wave of these keys
+        auto dv_step = [&](int tix) {
+            bf16x8 pb[2];
+#pragma unroll
+            for (int c = 0; c < 2; ++c) pb[c] = lds8(&sP[tix & 1][wr][c][lane * 8]);
+#pragma unroll
+            for (int n = 0; n < NA; ++n)
+#pragma unroll
+                for (int c = 0; c < 2; ++c)
+                    acc[n] = mfma(pb[c], lds8(&sOT[tix % 3][(32 * n + l32) * TP + 16 * c + 8 * hl]), acc[n]);
+        };
+        float colsum = 0.f;
+        int it = 0;
         if constexpr (DK) {
+            // the wave's keys as second operands: k~ (its own tile's anchor is the
+            // block's) and v rows of key j
+            bf16x8 kop[K / 16], vop[V / 16];
+#pragma unroll
+            for (int s = 0; s < K / 16; ++s) {
+                const int ch = 16 * s + 8 * hl;
+                uint4 raw = {0, 0, 0, 0};
+                if (jok) raw = *reinterpret_cast<const uint4 *>(khg + (tj * HQ + hq) * K + ch);
+                kop[s] = __builtin_bit_cast(bf16x8, raw);
+            }
 #pragma unroll
             for (int s = 0; s < V / 16; ++s) {
                 const int ch = 16 * s + 8 * hl;
@@ -312,79 +333,77 @@ __global__ __launch_bounds__(NTH_KV) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
                 if (jok) raw = *reinterpret_cast<const uint4 *>(vg + (tj * a.H + h) * V + ch);
                 vop[s] = __builtin_bit_cast(bf16x8, raw);
             }
-        }
-        const float gj = (HAS_G && jok) ? a.G[tj * HQ + hq] : 0.f;
-        f32x16 acc[NA];
+            const float gj = (HAS_G && jok) ? a.G[tj * HQ + hq] : 0.f;
+            for (int q0 = j0; q0 < qend; q0 += BT, ++it) {
+                const int cur = it & 1;
+                const int qrow = swap23(l32);
+                f32x16 S = 0.f, dP = 0.f;
 #pragma unroll
-        for (int n = 0; n < NA; ++n) acc[n] = 0.f;
-        float colsum = 0.f;
-
-        for (int q0 = j0, it = 0; q0 < qend; q0 += BT, ++it) {
-            const int cur = it & 1;
-            const int qrow = swap23(l32);
-            f32x16 S = 0.f, dP = 0.f;
-#pragma unroll
-            for (int s = 0; s < K / 16; ++s) S = mfma(lds8(&sQ[cur][roff<RPK>(qrow, 2 * s + hl)]), kop[s], S);
-            if constexpr (DK) {
+                for (int s = 0; s < K / 16; ++s)
+                    S = mfma(lds8(&sQ[cur][roff<RPK>(qrow, 2 * s + hl)]), kop[s], S);
 #pragma unroll
                 for (int s = 0; s < V / 16; ++s)
                     dP = mfma(lds8(&sO[cur][roff<RPV>(qrow, 2 * s + hl)]), vop[s], dP);
-            }
-            // every pair of the tile visible: no mask
-            const bool full = jw + 31 < len && q0 >= jw + 31 && q0 + BT <= len &&
-                              (a.window <= 0 || q0 + BT - 1 - jw < a.window);
-            bf16x8 ob[2];  // A (dv role) or dS (dk role), the first operand of the last product
-            // two copies of the softmax step: without the mask for a full tile,
-            // with it for the diagonal, the window edge and a sequence's end
-            auto softmax = [&](auto masked) {
+                // every pair of the tile visible: no mask
+                const bool full = jw + 31 < len && q0 >= jw + 31 && q0 + BT <= len &&
+                                  (a.window <= 0 || q0 + BT - 1 - jw < a.window);
+                bf16x8 db[2];
+                // two copies of the softmax step: without the mask for a full tile,
+                // with it for the diagonal, the window edge and a sequence's end
+                auto softmax = [&](auto masked) {
 #pragma unroll
-                for (int c = 0; c < 2; ++c) {
-                    const int qi0 = 16 * c + 8 * hl;
-                    // the 8 rows' values, read unconditionally ahead of their use
-                    f32x4 L4[2], D4[2], G4[2];
+                    for (int c = 0; c < 2; ++c) {
+                        const int qi0 = 16 * c + 8 * hl;
+                        // the 8 rows' values, read unconditionally ahead of their use
+                        f32x4 L4[2], D4[2], G4[2];
 #pragma unroll
-                    for (int x = 0; x < 2; ++x) {
-                        L4[x] = *reinterpret_cast<const f32x4 *>(&sL[cur][qi0 + 4 * x]);
-                        if (DK) D4[x] = *reinterpret_cast<const f32x4 *>(&sD[cur][qi0 + 4 * x]);
-                        if (HAS_G) G4[x] = *reinterpret_cast<const f32x4 *>(&sGq[cur][qi0 + 4 * x]);
-                    }
-                    f32x8 o8;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const float lse2 = L4[e / 4][e % 4];
-                        const float Gi = HAS_G ? G4[e / 4][e % 4] : 0.f;
-                        float p = __builtin_amdgcn_exp2f(S[8 * c + e] + Gi - gj - lse2);
-                        if constexpr (decltype(masked)::value) {
-                            const int i = q0 + qi0 + e;
-                            const bool vis = jok && i >= j && i < len && (a.window <= 0 || i - j < a.window);
-                            p = vis ? p : 0.f;
+                        for (int x = 0; x < 2; ++x) {
+                            L4[x] = *reinterpret_cast<const f32x4 *>(&sL[cur][qi0 + 4 * x]);
+                            D4[x] = *reinterpret_cast<const f32x4 *>(&sD[cur][qi0 + 4 * x]);
+                            if (HAS_G) G4[x] = *reinterpret_cast<const f32x4 *>(&sGq[cur][qi0 + 4 * x]);
                         }
-                        if constexpr (DK) {
+                        f32x8 p8, d8;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const float Gi = HAS_G ? G4[e / 4][e % 4] : 0.f;
+                            float p = __builtin_amdgcn_exp2f(S[8 * c + e] + Gi - gj - L4[e / 4][e % 4]);
+                            if constexpr (decltype(masked)::value) {
+                                const int i = q0 + qi0 + e;
+                                const bool vis = jok && i >= j && i < len && (a.window <= 0 || i - j < a.window);
+                                p = vis ? p : 0.f;
+                            }
                             const float ds = p * (dP[8 * c + e] - D4[e / 4][e % 4]);
                             colsum += ds;
-                            o8[e] = ds;
-                        } else {
-                            o8[e] = p;
+                            p8[e] = p;
+                            d8[e] = ds;
                         }
+                        // A goes straight to LDS for the dv wave of these keys
+                        *reinterpret_cast<bf16x8 *>(&sP[cur][wr][c][lane * 8]) = __builtin_convertvector(p8, bf16x8);
+                        db[c] = __builtin_convertvector(d8, bf16x8);
                     }
-                    ob[c] = __builtin_convertvector(o8, bf16x8);
-                }
-            };
-            if (full)
-                softmax(std::false_type{});
-            else
-                softmax(std::true_type{});
+                };
+                if (full)
+                    softmax(std::false_type{});
+                else
+                    softmax(std::true_type{});
 #pragma unroll
-            for (int n = 0; n < NA; ++n)
+                for (int n = 0; n < NA; ++n)
 #pragma unroll
-                for (int c = 0; c < 2; ++c) {
-                    const __bf16 *src = DK ? &sQT[cur][(32 * n + l32) * TP + 16 * c + 8 * hl]
-                                           : &sOT[cur][(32 * n + l32) * TP + 16 * c + 8 * hl];
-                    acc[n] = mfma(ob[c], lds8(src), acc[n]);
-                }
-            if (q0 + BT < qend) store_tile(cur ^ 1, q0 + BT);
-            __syncthreads();
-            if (q0 + 2 * BT < qend) load_tile(q0 + 2 * BT);
+                    for (int c = 0; c < 2; ++c)
+                        acc[n] = mfma(db[c], lds8(&sQT[cur][(32 * n + l32) * TP + 16 * c + 8 * hl]), acc[n]);
+                if (q0 + BT < qend) store_tile(cur ^ 1, q0 + BT, it + 1);
+                __syncthreads();
+                if (q0 + 2 * BT < qend) load_tile(q0 + 2 * BT);
+            }
+        } else {
+            // one tile behind the dk waves
+            for (int q0 = j0; q0 < qend; q0 += BT, ++it) {
+                if (it > 0) dv_step(it - 1);
+                if (q0 + BT < qend) store_tile((it & 1) ^ 1, q0 + BT, it + 1);
+                __syncthreads();
+                if (q0 + 2 * BT < qend) load_tile(q0 + 2 * BT);
+            }
+            if (it > 0) dv_step(it - 1);
         }
 
         if (jw >= len) return;
