@@ -171,15 +171,18 @@ __device__ inline float shift_anchor(float x, float to, float from) {
 // 4-7 the same keys for dv (dv += A^T do).  A dk wave leaves its bf16 A in
 // LDS in the lane order of the dv product's first operand, and the dv wave
 // of the same keys consumes it one tile later (after the tile's barrier), so
-// no barrier is added; do^T keeps three buffers for that lag.  Each role
-// holds one accumulator set, so both fit two waves per SIMD.
+// no barrier is added; do^T keeps three buffers for that lag.  The dv waves
+// also stage every tile, so the dk waves' chain holds only their products and
+// the softmax.  Each role holds one accumulator set, so both fit two waves
+// per SIMD.
 constexpr int NTH_KV = 2 * NTH;
 
 template <int K, int V, bool HAS_G>
 __global__ __launch_bounds__(NTH_KV) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
     constexpr int RPK = K + 8, RPV = V + 8;
     constexpr int CK = BT * K / 8, CV = BT * V / 8;  // 8-element chunks per tile
-    constexpr int UK = (CK + NTH_KV - 1) / NTH_KV, UV = (CV + NTH_KV - 1) / NTH_KV;
+    // the four dv waves stage the tiles (NTH threads)
+    constexpr int UK = (CK + NTH - 1) / NTH, UV = (CV + NTH - 1) / NTH;
     // two buffers of each streamed tile: one read while the other is filled
     __shared__ __attribute__((aligned(16))) __bf16 sQ[2][rows_size<RPK>()];  // q~ rows
     __shared__ __attribute__((aligned(16))) __bf16 sQT[2][K * TP];           // q~ transposed
@@ -214,13 +217,14 @@ __global__ __launch_bounds__(NTH_KV) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
     uint4 qraw[UK], oraw[UV];
     f32x8 araw[UK];
     float il = 0.f, id = 0.f, ig = 0.f;
+    const int sid = tid - NTH;  // staging thread index (dv waves)
     auto load_tile = [&](int q0) {
         // rows past the sequence load its last row (in bounds) and are zeroed when stored
         const float *rt = a.Rt + ((int64_t)(sg.tile_base + q0 / BR) * HQ + hq) * K;
 #pragma unroll
         for (int u = 0; u < UK; ++u) {
-            const int c = tid + NTH_KV * u, r = c % BT, ch = 8 * (c / BT), i = min(q0 + r, len - 1);
-            if (CK % NTH_KV == 0 || c < CK) {
+            const int c = sid + NTH * u, r = c % BT, ch = 8 * (c / BT), i = min(q0 + r, len - 1);
+            if (CK % NTH == 0 || c < CK) {
                 qraw[u] = *reinterpret_cast<const uint4 *>(qhg + ((s0 + i) * HQ + hq) * K + ch);
                 const f32x4 *pp = reinterpret_cast<const f32x4 *>(rt + ch);
                 const f32x4 p0 = pp[0], p1 = pp[1];
@@ -229,12 +233,12 @@ __global__ __launch_bounds__(NTH_KV) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
         }
 #pragma unroll
         for (int u = 0; u < UV; ++u) {
-            const int c = tid + NTH_KV * u, r = c % BT, ch = 8 * (c / BT), i = min(q0 + r, len - 1);
-            if (CV % NTH_KV == 0 || c < CV)
+            const int c = sid + NTH * u, r = c % BT, ch = 8 * (c / BT), i = min(q0 + r, len - 1);
+            if (CV % NTH == 0 || c < CV)
                 oraw[u] = *reinterpret_cast<const uint4 *>(dog + ((s0 + i) * HQ + hq) * V + ch);
         }
-        if (tid < BT) {
-            const int i = q0 + tid;
+        if (sid < BT) {
+            const int i = q0 + sid;
             il = id = ig = 0.f;
             if (i < len) {
                 const int64_t t = (s0 + i) * HQ + hq;
@@ -247,8 +251,8 @@ __global__ __launch_bounds__(NTH_KV) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
     auto store_tile = [&](int buf, int q0, int tix) {
 #pragma unroll
         for (int u = 0; u < UK; ++u) {
-            const int c = tid + NTH_KV * u, r = c % BT, ch = 8 * (c / BT);
-            if (CK % NTH_KV == 0 || c < CK) {
+            const int c = sid + NTH * u, r = c % BT, ch = 8 * (c / BT);
+            if (CK % NTH == 0 || c < CK) {
                 const f32x8 qq = to_f32(qraw[u]);
                 f32x8 x;
 #pragma unroll
@@ -262,8 +266,8 @@ __global__ __launch_bounds__(NTH_KV) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
         }
 #pragma unroll
         for (int u = 0; u < UV; ++u) {
-            const int c = tid + NTH_KV * u, r = c % BT, ch = 8 * (c / BT);
-            if (CV % NTH_KV == 0 || c < CV) {
+            const int c = sid + NTH * u, r = c % BT, ch = 8 * (c / BT);
+            if (CV % NTH == 0 || c < CV) {
                 const uint4 z = {0, 0, 0, 0};
                 const bf16x8 b = __builtin_bit_cast(bf16x8, q0 + r < len ? oraw[u] : z);
                 *reinterpret_cast<bf16x8 *>(&sO[buf][roff<RPV>(r, ch / 8)]) = b;
@@ -271,10 +275,10 @@ __global__ __launch_bounds__(NTH_KV) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
                 for (int e = 0; e < 8; ++e) sOT[tix % 3][(ch + e) * TP + r] = b[e];
             }
         }
-        if (tid < BT) {
-            sL[buf][tid] = il;
-            sD[buf][tid] = id;
-            sGq[buf][tid] = ig;
+        if (sid < BT) {
+            sL[buf][sid] = il;
+            sD[buf][sid] = id;
+            sGq[buf][sid] = ig;
         }
     };
 
@@ -282,10 +286,13 @@ __global__ __launch_bounds__(NTH_KV) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
     // stores tile it+1 (loaded during iteration it-1) into the other buffer,
     // which every wave finished reading before the previous barrier; one
     // barrier per tile.
-    load_tile(j0);
-    store_tile(0, j0, 0);
+    const bool stager = w >= NW;
+    if (stager) {
+        load_tile(j0);
+        store_tile(0, j0, 0);
+    }
     __syncthreads();
-    if (j0 + BT < qend) load_tile(j0 + BT);
+    if (stager && j0 + BT < qend) load_tile(j0 + BT);
 
     // One role's whole walk over the query tiles; the two instantiations keep
     // their accumulators apart.  Every wave runs every tile: a tile with no
@@ -391,12 +398,10 @@ __global__ __launch_bounds__(NTH_KV) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
 #pragma unroll
                     for (int c = 0; c < 2; ++c)
                         acc[n] = mfma(db[c], lds8(&sQT[cur][(32 * n + l32) * TP + 16 * c + 8 * hl]), acc[n]);
-                if (q0 + BT < qend) store_tile(cur ^ 1, q0 + BT, it + 1);
                 __syncthreads();
-                if (q0 + 2 * BT < qend) load_tile(q0 + 2 * BT);
             }
         } else {
-            // one tile behind the dk waves
+            // one tile behind the dk waves; these waves also stage every tile
             for (int q0 = j0; q0 < qend; q0 += BT, ++it) {
                 if (it > 0) dv_step(it - 1);
                 if (q0 + BT < qend) store_tile((it & 1) ^ 1, q0 + BT, it + 1);
