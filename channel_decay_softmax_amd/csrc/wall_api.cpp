@@ -238,6 +238,8 @@ wall_status_t wall_attn_bwd(const void *q, const void *k, const void *v, wall_dt
         if (p && !aligned(p, 16)) return WALL_ERR_INVALID_ARG;
     if (!aligned(workspace, 256)) return WALL_ERR_INVALID_ARG;
     const int64_t nseg = cu_seqlens ? num_seqs : B;
+    // the backward launches one block per (query head, sequence, 128-row block of the longest sequence)
+    if (HQ * nseg * cdiv(cu_seqlens ? max_seqlen : T, TILE) > INT32_MAX) return WALL_ERR_UNSUPPORTED;
     const BwdLayout L = bwd_layout(B, T, HQ, K, nseg);
     if (workspace_bytes < L.total) return WALL_ERR_INVALID_ARG;
     char *ws = static_cast<char *>(workspace);

@@ -122,10 +122,11 @@ __device__ inline BlockPos block_pos(const BwdArgs &a, int nblk, bool heavy_firs
 // anchors: an exact power of two, applied with v_ldexp_f32 instead of an
 // exp2 per element.
 template <int K>
-__global__ __launch_bounds__(256) void bwd_anchor_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256) void bwd_anchor_kernel(BwdArgs a, int nblk) {
     __shared__ float sR[K];
-    const int tile = blockIdx.x, hq = blockIdx.y % a.HQ;
-    const SegInfo sg = a.seg[blockIdx.y / a.HQ];
+    // one block per (tile of a sequence, query head), tiles fastest
+    const int tile = blockIdx.x % nblk, hs = blockIdx.x / nblk, hq = hs % a.HQ;
+    const SegInfo sg = a.seg[hs / a.HQ];
     const int r0 = tile * BR;
     if (r0 >= sg.len) return;
     const int n = min(BR, sg.len - r0), tid = threadIdx.x;
@@ -666,7 +667,7 @@ template <int K, int V, bool HAS_G>
 hipError_t run(const BwdArgs &a, hipStream_t st) {
     const int nblk = (int)cdiv(a.max_seqlen, BR);
     const unsigned nb = (unsigned)((int64_t)a.HQ * a.nseg * nblk);
-    hipLaunchKernelGGL((bwd_anchor_kernel<K>), dim3((unsigned)nblk, (unsigned)(a.HQ * a.nseg)), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((bwd_anchor_kernel<K>), dim3(nb), dim3(256), 0, st, a, nblk);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_dq_mfma<K, V, HAS_G>), dim3(nb), dim3(NTH), 0, st, a, nblk);

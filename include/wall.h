@@ -240,15 +240,21 @@ wall_status_t wall_attn_fwd_run(const void *q, wall_dtype_t dtype,
  *   dsink       [HQ] float32 (written; required when sink_bias is given)
  *   workspace   device scratch of at least wall_attn_bwd_workspace_size(...)
  *               bytes, 256-byte aligned, contents on entry ignored
- * Every product is float32 on the vector ALUs (bf16 inputs are widened), with
- * the forward's anchoring: exp2(P_i - P_j) split at an integer anchor inside
- * the 64-row block at hand.  Over one sequence the summands of dg (and of
- * dg_scalar) add up to zero, so the suffix sums are taken as minus the
- * exclusive prefix sums.
+ * Numerics: exp2(P_i - P_j) is split at integer anchors, one per 128-row
+ * tile and channel at the tile's middle row, as in the forward.  bf16 inputs:
+ * the five products run on bf16 matrix cores with float32 accumulation (q~,
+ * k~, the probabilities and dS rounded to bf16; softmax, scaling and the
+ * gate sums in float32); the q-side and k-side terms of dg are formed from
+ * the same rounded q~ and k~, so their rounding cancels in dg's sums.
+ * float32 inputs: every product in float32 on the vector ALUs.  Over one
+ * sequence the summands of dg (and of dg_scalar) add up to zero, so the
+ * suffix sums are taken as minus the exclusive prefix sums.  Deterministic
+ * (no atomics).
  * Errors: INVALID_ARG for a null required pointer, G without dg_scalar, a
  * sink without dsink, a size < 1, HQ % H != 0, bad cu_seqlens arguments,
- * misalignment, a short workspace; UNSUPPORTED for K or V not in {64, 128}
- * or another dtype; LAUNCH on a failed launch. */
+ * misalignment, a short workspace; UNSUPPORTED for K or V not in {64, 128},
+ * another dtype, or HQ * sequences * ceil(longest sequence / 128) above
+ * INT32_MAX (one block each); LAUNCH on a failed launch. */
 size_t wall_attn_bwd_workspace_size(int64_t B, int64_t T, int64_t HQ, int64_t K, int64_t num_seqs);
 
 wall_status_t wall_attn_bwd(const void *q, const void *k, const void *v, wall_dtype_t dtype,

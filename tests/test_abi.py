@@ -180,7 +180,9 @@ def test_bwd_rejects_invalid_arguments(kw):
     assert bwd(**kw) == INVALID
 
 
-@pytest.mark.parametrize("kw", [dict(kk=96), dict(vv=32), dict(dtype=5), dict(gdt=3)])
+@pytest.mark.parametrize("kw", [dict(kk=96), dict(vv=32), dict(dtype=5), dict(gdt=3),
+                                # 64 heads x 2^19 sequences x ceil(2^19 / 128) blocks: past a 32-bit grid
+                                dict(t=1 << 20, hq=64, h=64, cu=FAKE, nseq=1 << 19, maxlen=1 << 19)])
 def test_bwd_rejects_unsupported_shapes(kw):
     assert bwd(**kw) == UNSUPPORTED
 
