@@ -411,7 +411,8 @@ def main():
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for {args.gpus}): the Wall Attention forward "
-              "is built and measured for a single GPU; see DESIGN.md for how it would shard.",
+              "is built and measured for a single GPU.  Across GPUs it would shard by key/value-head "
+              "group (each GPU runs the same kernels on its heads, with no communication).",
               file=sys.stderr)
         sys.exit(2)
     from wall_inputs import DECODE_WORKLOADS
