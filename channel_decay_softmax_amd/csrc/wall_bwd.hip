@@ -16,7 +16,9 @@
 // changes no logit), so the suffix sums equal minus the exclusive prefix
 // sums, which the prefix scan computes.
 //
-// The kernels run in float32 on the vector ALUs for either input dtype:
+// bwd_pre_kernel and dsink_kernel serve both input dtypes; bf16 inputs take
+// the matrix-core kernels of wall_bwd_mfma.hip for the rest.  For float32
+// inputs the kernels below run everything in float32 on the vector ALUs:
 //   bwd_pre_kernel   D_i
 //   bwd_dq_kernel    one block per (query head, sequence, 64 query rows): keys
 //                    staged 32 at a time in LDS; writes dq, X = q (.) dq, the
@@ -85,14 +87,23 @@ __global__ void bwd_seg_kernel(SegInfo *seg, const int32_t *cu, int nseg, int T)
 // ---------------------------------------------------------------- D = do . o
 template <typename T, int V>
 __global__ __launch_bounds__(NT) void bwd_pre_kernel(BwdArgs a, int64_t nrows) {
-    // one row (token, head) per 16 lanes: V/16 channels each
+    // one row (token, head) per 16 lanes: V/16 consecutive channels each, so
+    // each lane's share is one or two 16-byte loads per operand
+    constexpr int VL = V / 16;
     const int64_t r = (int64_t)blockIdx.x * (NT / 16) + threadIdx.x / 16;
     const int l = threadIdx.x % 16;
     float acc = 0.f;
     if (r < nrows) {
-        const T *o = static_cast<const T *>(a.o) + r * V;
-        const T *d = static_cast<const T *>(a.dout) + r * V;
-        for (int c = l; c < V; c += 16) acc = fmaf(ld(o + c), ld(d + c), acc);
+        const T *o = static_cast<const T *>(a.o) + r * V + l * VL;
+        const T *d = static_cast<const T *>(a.dout) + r * V + l * VL;
+        T ov[VL], dv[VL];
+#pragma unroll
+        for (int c = 0; c < VL; ++c) {
+            ov[c] = o[c];
+            dv[c] = d[c];
+        }
+#pragma unroll
+        for (int c = 0; c < VL; ++c) acc = fmaf((float)ov[c], (float)dv[c], acc);
     }
 #pragma unroll
     for (int off = 8; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 16);

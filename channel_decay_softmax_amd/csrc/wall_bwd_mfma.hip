@@ -641,26 +641,29 @@ __global__ __launch_bounds__(NTH, 2) void bwd_dq_mfma(BwdArgs a, int nblk) {
 // ---------------------------------------------------------------- dk, dv: sum over the kv group
 template <int K, int V>
 __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdArgs a, int64_t nrow_h) {
-    // one (row, kv head) per 32 lanes; K/32 and V/32 channels per lane
+    // one (row, kv head) per 32 lanes; K/32 and V/32 consecutive channels per
+    // lane, read as one vector per query head of the group
+    constexpr int KL = K / 32, VL = V / 32;
     const int64_t rh = (int64_t)blockIdx.x * 8 + threadIdx.x / 32;
     if (rh >= nrow_h) return;
     const int l = threadIdx.x % 32;
     const int64_t t = rh / a.H;
     const int h = (int)(rh % a.H), grp = a.HQ / a.H;
-    __bf16 *dkg = static_cast<__bf16 *>(a.dk) + rh * K;
-    __bf16 *dvg = static_cast<__bf16 *>(a.dv) + rh * V;
+    float sk[KL] = {}, sv[VL] = {};
+    for (int g = 0; g < grp; ++g) {
+        const float *pk = a.dkp + (t * a.HQ + h * grp + g) * K + l * KL;
+        const float *pv = a.dvp + (t * a.HQ + h * grp + g) * V + l * VL;
 #pragma unroll
-    for (int n = l; n < K; n += 32) {
-        float s = 0.f;
-        for (int g = 0; g < grp; ++g) s += a.dkp[(t * a.HQ + h * grp + g) * K + n];
-        dkg[n] = (__bf16)s;
-    }
+        for (int e = 0; e < KL; ++e) sk[e] += pk[e];
 #pragma unroll
-    for (int n = l; n < V; n += 32) {
-        float s = 0.f;
-        for (int g = 0; g < grp; ++g) s += a.dvp[(t * a.HQ + h * grp + g) * V + n];
-        dvg[n] = (__bf16)s;
+        for (int e = 0; e < VL; ++e) sv[e] += pv[e];
     }
+    __bf16 *dkg = static_cast<__bf16 *>(a.dk) + rh * K + l * KL;
+    __bf16 *dvg = static_cast<__bf16 *>(a.dv) + rh * V + l * VL;
+#pragma unroll
+    for (int e = 0; e < KL; ++e) dkg[e] = (__bf16)sk[e];
+#pragma unroll
+    for (int e = 0; e < VL; ++e) dvg[e] = (__bf16)sv[e];
 }
 
 template <int K, int V, bool HAS_G>
