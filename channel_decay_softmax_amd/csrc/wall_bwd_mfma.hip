@@ -7,31 +7,32 @@
 // with q~ = q scale log2e 2^(P - R) and k~ = k 2^(R - P) rounded to bf16, A and
 // dS rounded to bf16 as MFMA operands, everything else in float32.
 //
-// Work decomposition.  A block owns 128 rows of one (query head, sequence):
-// keys in the dk/dv kernel, queries in the dq kernel; its 4 waves own 32 rows
-// each (one MFMA block).  The block anchors every channel at the floored
-// prefix of its middle row (row 64, or the last row of a shorter tail), as
-// the forward anchors its 128-row tiles, so both exp2 factors of a pair stay
-// within 2^(+-change of P over 64 rows).  The other side streams through LDS
-// 32 rows at a time, each tile both row-major (the MFMA's first operand) and
-// transposed (the second operand of the product that contracts over the
-// streamed rows); the next tile's global loads are issued before the current
-// tile's products, and the tiles are double-buffered in LDS (one barrier
-// per tile).  Staging lanes take consecutive rows of one 8-channel chunk, so
-// the transposed copy is written as runs of consecutive bf16.  The block's
-// own rows stay in registers as second operands.
+// Work decomposition.  A block owns one 128-row tile of one (query head,
+// sequence): keys in the dk/dv kernel, queries in the dq kernel; its waves own
+// 32 rows each (one MFMA block).  Every tile is anchored per channel at the
+// floored prefix of its middle row (row 64, or the last row of a shorter
+// tail), as the forward anchors its tiles, so both exp2 factors of a pair
+// stay within 2^(+-change of P over 64 rows); bwd_anchor_kernel writes every
+// row's q~ and k~ at its own tile's anchor once.  The other side streams
+// through LDS 32 rows at a time, each tile both row-major (the MFMA's first
+// operand) and transposed (the second operand of the product that contracts
+// over the streamed rows), moved to the block's anchor by an exact power of
+// two as it is staged; the next tile's global loads are issued before the
+// current tile's products, and the tiles are double-buffered in LDS (one
+// barrier per tile).  Staging lanes take consecutive rows of one 8-channel
+// chunk, so the transposed copy is written as runs of consecutive bf16.  The
+// block's own rows stay in registers as second operands.
 //
-// dk/dv (per key block, queries from the block's first key on):
-//   S  = q~ k~^T,  dP = do v^T   (32 streamed queries x the wave's 32 keys);
-//   A, dS in-lane;  dv += A^T do (dv waves),  dk += dS^T q~ (dk waves).
-// Both kernels run two waves per SIMD: the dq kernel holds its own rows' q~
-// and do operands, the dq accumulators and one tile of prefetch registers;
-// the dk/dv kernel splits its eight waves into a dk role and a dv role over
-// the same staged tiles, so no wave holds both accumulator sets.
-//
-// dq (per query block, keys up to the block's last query):
+// dk/dv (per key block, queries from the block's first key on; 8 waves):
+//   dk waves  S = q~ k~^T, dP = do v^T (32 streamed queries x the wave's 32
+//             keys), A and dS in-lane, dk += dS^T q~; A to LDS;
+//   dv waves  stage the tiles; one tile behind, dv += A^T do.
+// dq (per query block, keys up to the block's last query; 4 waves):
 //   S^T = k~ q~^T, dP^T = v do^T (32 streamed keys x the wave's 32 queries);
-//   dq += dS k~.
+//   dq += dS k~; the waves stage the tiles together.
+// Both kernels run two waves per SIMD: no wave of the dk/dv kernel holds both
+// accumulator sets, and two 4-wave dq blocks share a CU.
+//
 // The streamed rows of the first products are fed in the order that swaps
 // bits 2 and 3 of the row index, so each lane's 16 accumulator registers hold
 // two runs of 8 consecutive streamed rows: exactly the k-slots the lane
