@@ -41,6 +41,9 @@ CASES = [
     dict(wl="gqa_bf16", B=2, T=333, HQ=8, H=4, K=64, V=64),
     dict(wl="long_bf16", B=1, T=700, HQ=2, H=1, K=128, V=128),
     dict(wl="options_bf16", B=1, T=520, HQ=2, H=2, K=64, V=64, window=130),
+    dict(wl="options_bf16", B=3, T=97, HQ=4, H=1, K=128, V=128, window=40),
+    dict(wl="varlen_bf16", T=400, HQ=4, H=2, K=128, V=64, nseq=None, cu=[0, 1, 33, 160, 161, 300, 400]),
+    dict(wl="long_bf16", B=2, T=130, HQ=2, H=1, K=128, V=128),
 ]
 
 
