@@ -145,13 +145,14 @@ def cpu_baseline(inp, flop_per_pair, target_s):
 
 def decode_bytes(B, T, HQ, H, K, V, C, es):
     """Algorithmic HBM bytes of one decode call and of one row's append (prefix
-    row and cache row)."""
+    row and cache row in one pass)."""
     nc = -(-T // C)
     dec = (B * T * HQ * K * es + B * T * H * V * es + B * nc * HQ * K * 4   # k_tilde, v, anchors
            + B * HQ * K * es + B * HQ * K * 4 + B * HQ * V * es + B * HQ * 4)  # q, p_curr, o, lse
     opens = (T - 1) % C == 0
-    app = B * H * K * es + B * HQ * K * 4 + B * HQ * K * es + B * HQ * K * 4  # k, P, k_tilde row; anchor
-    app += B * HQ * K * es + 2 * B * HQ * K * 4  # the prefix row: g, the previous P row, the new P row
+    # one row through wall_stream_append: g and the previous P row in, the new P
+    # row out; k in, the k_tilde row out; the chunk anchor read (or written)
+    app = B * HQ * K * es + 2 * B * HQ * K * 4 + B * H * K * es + B * HQ * K * es + B * HQ * K * 4
     return dec, app, opens
 
 
@@ -187,8 +188,8 @@ def decode_cpu_baseline(inp, nseq, es):
 
 def bench_decode(args):
     """One step of the streaming decode loop: the newest token's log2 prefix from
-    the previous row's, its row of the anchored key cache, then the split-KV
-    decode of every sequence's newest query."""
+    the previous row's and its row of the anchored key cache (one pass), then the
+    split-KV decode of every sequence's newest query."""
     import torch
 
     import channel_decay_softmax_amd as wall
@@ -209,7 +210,7 @@ def bench_decode(args):
     kt = torch.empty((B, T, HQ, K), dtype=d.q.dtype, device=dev)
     r = torch.empty((B, -(-T // C), HQ, K), dtype=torch.float32, device=dev)
     wall.build_wall_kv_cache(d.k, P, C, k_tilde=kt, r_cache=r, t0=0, t1=T - 1)
-    g_new, p_prev, pc = d.g[:, T - 1:T], P[:, T - 2], P[:, T - 1:T]
+    pc = P[:, T - 1:T]
     o = torch.empty((B, 1, HQ, V), dtype=d.q.dtype, device=dev)
     lse = torch.empty((B, 1, HQ), dtype=torch.float32, device=dev)
     ws = torch.empty(wall.decode_workspace_size(B, T, HQ, V), dtype=torch.uint8, device=dev)
@@ -218,8 +219,7 @@ def bench_decode(args):
     def step(marks=None):
         if marks:
             marks[0].record()
-        wall.wall_prefix_append(g_new, prev=p_prev, out=pc)
-        wall.build_wall_kv_cache(d.k, P, C, k_tilde=kt, r_cache=r, t0=T - 1, t1=T)
+        wall.wall_stream_append(d.g, d.k, P, kt, r, C, T - 1, T)
         if marks:
             marks[1].record()
         wall.wall_attn_decode(d.q, d.v, pc, kt, r, sink_bias=d.sink_bias, scale=inp.scale,

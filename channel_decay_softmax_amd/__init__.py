@@ -31,6 +31,7 @@ from ._binding import (  # noqa: F401
     wall_attn_fwd_run,
     wall_prefix_scan,
     wall_prefix_append,
+    wall_stream_append,
 )
 
 __all__ = ["wall_attn", "wall_attn_fwd", "wall_attn_bwd", "wall_prefix_scan", "build_wall_kv_cache", "wall_attn_decode",

@@ -24,7 +24,7 @@ WALL_OK, WALL_ERR_INVALID_ARG, WALL_ERR_UNSUPPORTED, WALL_ERR_LAUNCH = 0, 1, 2, 
 #: every symbol include/wall.h declares
 EXPORTS = (
     "wall_status_string", "wall_version",
-    "wall_prefix_scan_workspace_size", "wall_prefix_scan", "wall_prefix_append",
+    "wall_prefix_scan_workspace_size", "wall_prefix_scan", "wall_prefix_append", "wall_stream_append",
     "wall_attn_fwd_workspace_size", "wall_attn_fwd",
     "wall_attn_fwd_prepare", "wall_attn_fwd_run",
     "wall_attn_bwd_workspace_size", "wall_attn_bwd",
@@ -58,6 +58,7 @@ def lib() -> ctypes.CDLL:
         L.wall_prefix_scan_workspace_size.restype = S
         L.wall_prefix_scan.argtypes = [P, E, P, I, I, I, P, I, F, P, S, P]
         L.wall_prefix_append.argtypes = [P, E, I, P, I, P, I, I, I, I, F, P]
+        L.wall_stream_append.argtypes = [P, E, P, E, P, P, P, I, I, I, I, I, I, I, I, F, P]
         L.wall_prefix_scan.restype = E
         L.wall_attn_fwd_workspace_size.argtypes = [E, I, I, I, I, I, I, I]
         L.wall_attn_fwd_workspace_size.restype = S
@@ -214,6 +215,31 @@ def wall_prefix_append(x: torch.Tensor, prev: Optional[torch.Tensor] = None,
     _check(lib().wall_prefix_append(_ptr(x), _dtype(x), x_bs, _ptr(prev), prev_bs, _ptr(out), out_bs, B, n, C,
                                     float(scale), _stream(dev)), "wall_prefix_append")
     return out
+
+
+def wall_stream_append(g: torch.Tensor, k: torch.Tensor, P: torch.Tensor, k_tilde: torch.Tensor,
+                       r_cache: torch.Tensor, chunk_size: int = 64, t0: int = 0, t1: Optional[int] = None,
+                       scale: float = 1.0 / math.log(2.0)) -> None:
+    """One turn of the streaming loop for rows t0 .. t1-1: P of the new rows from
+    row t0-1 (in place, as wall_prefix_append) and their cache rows and chunk
+    anchors (as build_wall_kv_cache), in one pass.  g, P, k_tilde are
+    [B, T_cap, HQ, K] buffers, k [B, T_cap, H, K], r_cache [B, ceil(T_cap/C), HQ, K]."""
+    _on_gpu(g, k, P, k_tilde, r_cache)
+    B, T_cap, H, K = k.shape
+    HQ = g.shape[2]
+    NC = -(-T_cap // int(chunk_size))
+    for t, shape, what in ((g, (B, T_cap, HQ, K), "g"), (P, (B, T_cap, HQ, K), "P"),
+                           (k_tilde, (B, T_cap, HQ, K), "k_tilde"), (r_cache, (B, NC, HQ, K), "r_cache")):
+        if tuple(t.shape) != shape or not t.is_contiguous():
+            raise ValueError(f"{what} must be a contiguous tensor of shape {shape}")
+    if not k.is_contiguous() or P.dtype != torch.float32 or r_cache.dtype != torch.float32:
+        raise ValueError("k must be contiguous; P and r_cache are float32")
+    if k_tilde.dtype != k.dtype:
+        raise TypeError("k_tilde has k's dtype")
+    t1 = T_cap if t1 is None else int(t1)
+    _check(lib().wall_stream_append(_ptr(g), _dtype(g), _ptr(k), _dtype(k), _ptr(P), _ptr(k_tilde),
+                                    _ptr(r_cache), B, T_cap, HQ, H, K, int(chunk_size), int(t0), t1,
+                                    float(scale), _stream(g.device)), "wall_stream_append")
 
 
 def wall_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, P: torch.Tensor,

@@ -19,7 +19,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libwall.so")
-SOURCES = ["wall_api.cpp", "wall_scan.hip", "wall_prep.hip", "wall_fwd_bf16.hip", "wall_fwd_f32.hip", "wall_decode.hip", "wall_bwd.hip", "wall_bwd_mfma.hip"]
+SOURCES = ["wall_api.cpp", "wall_scan.hip", "wall_prep.hip", "wall_fwd_bf16.hip", "wall_fwd_f32.hip", "wall_decode.hip", "wall_bwd.hip", "wall_bwd_mfma.hip", "wall_stream.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

@@ -7,6 +7,7 @@
 #include "wall.h"
 
 #include "wall_common.h"
+#include "wall_stream.h"
 
 using namespace wall;
 
@@ -308,6 +309,25 @@ wall_status_t wall_kv_cache_build(const void *k, wall_dtype_t dtype, const float
         if (!aligned(p, 16)) return WALL_ERR_INVALID_ARG;
     const CacheArgs a{k, P, k_tilde, r_cache, B, T_cap, HQ, H, K, chunk_size, t0, t1};
     return launched(launch_kv_cache(a, dtype == WALL_BF16, stream));
+}
+
+wall_status_t wall_stream_append(const void *g, wall_dtype_t g_dtype, const void *k, wall_dtype_t dtype,
+                                 float *P, void *k_tilde, float *r_cache, int64_t B, int64_t T_cap,
+                                 int64_t HQ, int64_t H, int64_t K, int64_t chunk_size, int64_t t0,
+                                 int64_t t1, float scale, hipStream_t stream) {
+    if (!g || !k || !P || !k_tilde || !r_cache) return WALL_ERR_INVALID_ARG;
+    if (B < 1 || T_cap < 1 || HQ < 1 || H < 1 || K < 1 || chunk_size < 1) return WALL_ERR_INVALID_ARG;
+    if (HQ % H != 0) return WALL_ERR_INVALID_ARG;
+    if (t0 < 0 || t1 <= t0 || t1 > T_cap) return WALL_ERR_INVALID_ARG;
+    if (B * T_cap > INT32_MAX / 2 || B * T_cap * HQ * K > ((int64_t)1 << 40)) return WALL_ERR_INVALID_ARG;
+    if ((dtype != WALL_BF16 && dtype != WALL_F32) || (g_dtype != WALL_BF16 && g_dtype != WALL_F32))
+        return WALL_ERR_UNSUPPORTED;
+    if ((K != 64 && K != 128) || chunk_size % 64 != 0) return WALL_ERR_UNSUPPORTED;
+    const void *ptrs[] = {g, k, P, k_tilde, r_cache};
+    for (const void *p : ptrs)
+        if (!aligned(p, 16)) return WALL_ERR_INVALID_ARG;
+    const StreamArgs a{g, k, P, k_tilde, r_cache, B, T_cap, HQ, H, K, chunk_size, t0, t1, scale};
+    return launched(launch_stream_append(a, g_dtype == WALL_BF16, dtype == WALL_BF16, stream));
 }
 
 size_t wall_attn_decode_workspace_size(int64_t B, int64_t T, int64_t HQ, int64_t V) {

@@ -306,6 +306,33 @@ wall_status_t wall_kv_cache_build(const void *k, wall_dtype_t dtype, const float
                                   int64_t chunk_size, int64_t t0, int64_t t1,
                                   hipStream_t stream);
 
+/* ------------------------------------------------------------------ streaming append
+ *
+ * One turn of the README's append-as-you-go decode loop for new rows
+ * t0 .. t1-1 of every sequence, in one pass: the log2 prefix of the new rows
+ * from the previous row's, exactly as wall_prefix_append computes it
+ * (prev = P[b, t0-1], or 0 when t0 = 0; s = g_t0 + ... + g_t in float32;
+ * P[b, t] = prev + scale * s), then the cache rows and chunk anchors exactly
+ * as wall_kv_cache_build computes them from that P.  The results equal those
+ * two calls bit for bit; the saving is one launch and one pass over P.
+ *
+ *   g           [B, T_cap, HQ, K] in g_dtype (WALL_BF16 or WALL_F32), rows t0 .. t1-1 read
+ *   k           [B, T_cap, H, K] in dtype, rows t0 .. t1-1 read
+ *   P           [B, T_cap, HQ, K] float32: row t0-1 read (t0 > 0), rows t0 .. t1-1 written
+ *   k_tilde     [B, T_cap, HQ, K] in dtype, rows t0 .. t1-1 written
+ *   r_cache     [B, ceil(T_cap / chunk_size), HQ, K] float32: the anchor of a
+ *               chunk opened before t0 is read, the anchor of a chunk opening
+ *               at a row in t0 .. t1-1 is written
+ *   scale       1 / ln 2 for the natural-log gate of the README
+ * Errors: INVALID_ARG for a null pointer, a size < 1, HQ % H != 0, t0 < 0,
+ * t1 <= t0 or t1 > T_cap, misalignment; UNSUPPORTED for K not in {64, 128},
+ * chunk_size not a positive multiple of 64, or another dtype; LAUNCH on a
+ * failed launch. */
+wall_status_t wall_stream_append(const void *g, wall_dtype_t g_dtype, const void *k, wall_dtype_t dtype,
+                                 float *P, void *k_tilde, float *r_cache, int64_t B, int64_t T_cap,
+                                 int64_t HQ, int64_t H, int64_t K, int64_t chunk_size, int64_t t0,
+                                 int64_t t1, float scale, hipStream_t stream);
+
 /* ------------------------------------------------------------------ decode
  *
  * The README's wall_attn_decode: one query per (b, hq) -- the newest token,

@@ -74,6 +74,25 @@ def test_prefix_append_rejects_unsupported_dtype():
     assert append(dtype=7) == UNSUPPORTED
 
 
+def stream(g=FAKE, gdt=B.WALL_BF16, k=FAKE, dtype=B.WALL_BF16, Pp=FAKE, kt=FAKE, r=FAKE, b=2, tcap=256, hq=4,
+           h=2, kk=128, c=64, t0=10, t1=11):
+    return wall.lib().wall_stream_append(P(g), gdt, P(k), dtype, P(Pp), P(kt), P(r), b, tcap, hq, h, kk, c, t0, t1,
+                                         1.4426950408889634, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(g=None), dict(k=None), dict(Pp=None), dict(kt=None), dict(r=None), dict(b=0), dict(tcap=0), dict(hq=0),
+    dict(hq=6, h=4), dict(t0=-1), dict(t1=10), dict(t1=257), dict(g=FAKE + 2), dict(r=FAKE + 4),
+])
+def test_stream_append_rejects_invalid_arguments(kw):
+    assert stream(**kw) == INVALID
+
+
+@pytest.mark.parametrize("kw", [dict(kk=96), dict(c=32), dict(dtype=5), dict(gdt=3)])
+def test_stream_append_rejects_unsupported_shapes(kw):
+    assert stream(**kw) == UNSUPPORTED
+
+
 def fwd(q=FAKE, k=FAKE, v=FAKE, dtype=B.WALL_BF16, Pp=FAKE, G=None, sink=None, o=FAKE, lse=None,
         b=1, t=256, hq=4, h=2, kk=128, vv=128, window=0, cu=None, nseq=0, maxlen=0, ws=FAKE,
         wsb=None):

@@ -225,3 +225,31 @@ def test_streaming_loop_with_incremental_prefix():
     og = np.stack([x[0] for x in outs], axis=1)
     lg = np.stack([x[1] for x in outs], axis=1)
     check_o(og, lg, o_f[:, t_first:], l_f[:, t_first:], "bfloat16", "streaming loop vs forward rows")
+
+
+@pytest.mark.parametrize("dtype", ["bfloat16", "float32"])
+def test_stream_append_equals_separate_calls(dtype):
+    """wall_stream_append gives the bits of wall_prefix_append followed by
+    build_wall_kv_cache, for a prefill, single rows and a multi-row append
+    that opens a chunk, with a partial last chunk."""
+    B, Tcap, HQ, H, K, C = 2, 200, 4, 2, 64, 64
+    say(f"stream append vs separate calls {dtype} B={B} T_cap={Tcap} HQ={HQ} H={H} K={K} C={C}")
+    inp = make_decode_inputs("decode_bf16", chunk_size=C, B=B, T=Tcap, HQ=HQ, H=H, K=K, V=64, dtype=dtype)
+    d = inp.to(DEV)
+    NC = -(-Tcap // C)
+
+    def bufs():
+        return (torch.full((B, Tcap, HQ, K), float("nan"), dtype=torch.float32, device=DEV),
+                torch.zeros((B, Tcap, HQ, K), dtype=d.k.dtype, device=DEV),
+                torch.full((B, NC, HQ, K), float("nan"), dtype=torch.float32, device=DEV))
+
+    Pa, kta, ra = bufs()
+    Pb, ktb, rb = bufs()
+    for t0, t1 in [(0, 60), (60, 61), (61, 62), (62, 140), (140, 141), (141, 199), (199, 200)]:
+        wall.wall_prefix_append(d.g[:, t0:t1], prev=None if t0 == 0 else Pa[:, t0 - 1], out=Pa[:, t0:t1])
+        wall.build_wall_kv_cache(d.k, Pa, C, k_tilde=kta, r_cache=ra, t0=t0, t1=t1)
+        wall.wall_stream_append(d.g, d.k, Pb, ktb, rb, C, t0, t1)
+    torch.cuda.synchronize()
+    assert torch.equal(Pa, Pb), "P differs"
+    assert torch.equal(kta, ktb), "k_tilde differs"
+    assert torch.equal(ra, rb), "anchors differ"
