@@ -46,6 +46,9 @@ DECODE_METRIC = "wall_attn_decode streaming step HBM GB/s (prefix and cache appe
 DECODE_KERNEL_SOURCES = ["channel_decay_softmax_amd/csrc/wall_decode.hip",
                          "channel_decay_softmax_amd/csrc/wall_common.h"]
 DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_decode_bf16_traffic.json")
+BWD_KERNEL_SOURCES = ["channel_decay_softmax_amd/csrc/wall_bwd_mfma.hip", "channel_decay_softmax_amd/csrc/wall_bwd.hip",
+                      "channel_decay_softmax_amd/csrc/wall_scan.hip", "channel_decay_softmax_amd/csrc/wall_common.h"]
+BWD_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_long_bf16_traffic.json")
 
 
 def visible_pairs(lens, W):
@@ -345,6 +348,13 @@ def bench_backward(args):
         wall.wall_attn_bwd(d.q, d.k, d.v, P, o, lse, do, G, d.sink_bias, d.scale, inp.window_size, cu, maxlen,
                            g_dtype=d.g.dtype, workspace=ws)
 
+    if args.copy_mb:
+        n = args.copy_mb * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.mul(src, 1.0, out=dst)  # reads and writes copy_mb MiB each
+        torch.cuda.synchronize()
+        del src, dst
     print(f"[bench] backward {args.workload}: B={B} T={T} HQ={HQ} H={H} K={K} V={V} {d.q.dtype} "
           f"pairs={pairs} flop={flop:.4e}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -384,7 +394,9 @@ def bench_backward(args):
                    "visible_pairs": pairs, "counted_flop": flop},
         "roofline": {"kernel": "the whole backward step (dq and dk/dv products, group sum, D, scans)",
                      "bound": bound, "achieved": round(value, 3), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(value / peak, 4), "traffic": None},
+                     "frac": round(value / peak, 4),
+                     "traffic": (load_traffic(args.workload, BWD_TRAFFIC_FILE, BWD_KERNEL_SOURCES)
+                                 if d.q.dtype == torch.bfloat16 else None)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
