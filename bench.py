@@ -482,7 +482,7 @@ def main():
         wall.wall_attn_fwd_prepare(d.k, d.v, P, HQ, ws_fwd, cu)
         if marks:
             marks[2].record()
-        wall.wall_attn_fwd_run(d.q, P, H, V, ws_fwd, o, lse, G=G, sink_bias=d.sink_bias,
+        wall.wall_attn_fwd_run(d.q, d.k, d.v, P, ws_fwd, o, lse, G=G, sink_bias=d.sink_bias,
                                scale=d.scale, window_size=inp.window_size, cu_seqlens=cu,
                                max_seqlen=max_seqlen)
         if marks:

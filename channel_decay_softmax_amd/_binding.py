@@ -67,8 +67,8 @@ def lib() -> ctypes.CDLL:
         L.wall_attn_fwd.restype = E
         L.wall_attn_fwd_prepare.argtypes = [P, P, E, P, I, I, I, I, I, I, P, I, P, S, P]
         L.wall_attn_fwd_prepare.restype = E
-        L.wall_attn_fwd_run.argtypes = [P, E, P, P, P, P, P, I, I, I, I, I, I, F, I, P, I, I, P, S,
-                                        P]
+        L.wall_attn_fwd_run.argtypes = [P, P, P, E, P, P, P, P, P, I, I, I, I, I, I, F, I, P, I, I,
+                                        P, S, P]
         L.wall_attn_fwd_run.restype = E
         L.wall_attn_bwd_workspace_size.argtypes = [I, I, I, I, I]
         L.wall_attn_bwd_workspace_size.restype = S
@@ -400,20 +400,22 @@ def wall_attn_fwd_prepare(k: torch.Tensor, v: torch.Tensor, P: torch.Tensor, HQ:
                                        _stream(dev)), "wall_attn_fwd_prepare")
 
 
-def wall_attn_fwd_run(q: torch.Tensor, P: torch.Tensor, H: int, V: int, workspace: torch.Tensor,
-                      out: torch.Tensor, lse: Optional[torch.Tensor] = None,
+def wall_attn_fwd_run(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, P: torch.Tensor,
+                      workspace: torch.Tensor, out: torch.Tensor, lse: Optional[torch.Tensor] = None,
                       G: Optional[torch.Tensor] = None, sink_bias: Optional[torch.Tensor] = None,
                       scale: Optional[float] = None, window_size: Optional[int] = None,
                       cu_seqlens: Optional[torch.Tensor] = None,
                       max_seqlen: Optional[int] = None) -> None:
-    """Stage 2 of wall_attn_fwd: the fused kernel, reading the prepared ``workspace``.
-    All tensors must already be dense and on one device (no copies are made here)."""
-    dev = _on_gpu(q, P, workspace, out, lse, G, sink_bias, cu_seqlens)
+    """Stage 2 of wall_attn_fwd: the fused kernel, reading the prepared ``workspace``
+    and the raw k, v of the prepare call.  All tensors must already be dense and on
+    one device (no copies are made here)."""
+    dev = _on_gpu(q, k, v, P, workspace, out, lse, G, sink_bias, cu_seqlens)
     B, T, HQ, K = q.shape
+    H, V = k.shape[2], v.shape[3]
     nseq = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
     _check(lib().wall_attn_fwd_run(
-        _ptr(q), _dtype(q), _ptr(P), _ptr(G), _ptr(sink_bias), _ptr(out), _ptr(lse), B, T, HQ, H,
-        K, V, float(K ** -0.5 if scale is None else scale), int(window_size or 0),
+        _ptr(q), _ptr(k), _ptr(v), _dtype(q), _ptr(P), _ptr(G), _ptr(sink_bias), _ptr(out), _ptr(lse),
+        B, T, HQ, H, K, V, float(K ** -0.5 if scale is None else scale), int(window_size or 0),
         _ptr(cu_seqlens), nseq, int(max_seqlen or 0), _ptr(workspace), workspace.numel(),
         _stream(dev)), "wall_attn_fwd_run")
 

@@ -127,14 +127,16 @@ wall_status_t enqueue_prepare(const void *k, const void *v, wall_dtype_t dtype, 
     return launched(launch_prep(pa, dtype == WALL_BF16, stream));
 }
 
-wall_status_t enqueue_run(const void *q, wall_dtype_t dtype, const float *P, const float *G,
-                          const float *sink_bias, void *o, float *lse, const FwdShape &s,
-                          float scale, int64_t window_size, const void *workspace,
+wall_status_t enqueue_run(const void *q, const void *k, const void *v, wall_dtype_t dtype,
+                          const float *P, const float *G, const float *sink_bias, void *o, float *lse,
+                          const FwdShape &s, float scale, int64_t window_size, const void *workspace,
                           hipStream_t stream) {
     const FwdLayout L = fwd_layout(esize_of(dtype), s.B, s.T, s.HQ, s.H, s.K, s.V, s.nseq);
     const char *ws = static_cast<const char *>(workspace);
     FwdArgs fa{};
     fa.q = q;
+    fa.k = k;
+    fa.v = v;
     fa.P = P;
     fa.G = G;
     fa.sink = sink_bias;
@@ -174,21 +176,21 @@ wall_status_t wall_attn_fwd_prepare(const void *k, const void *v, wall_dtype_t d
     return enqueue_prepare(k, v, dtype, P, s, cu_seqlens, workspace, stream);
 }
 
-wall_status_t wall_attn_fwd_run(const void *q, wall_dtype_t dtype, const float *P, const float *G,
-                                const float *sink_bias, void *o, float *lse, int64_t B, int64_t T,
-                                int64_t HQ, int64_t H, int64_t K, int64_t V, float scale,
-                                int64_t window_size, const int32_t *cu_seqlens, int64_t num_seqs,
-                                int64_t max_seqlen, const void *workspace, size_t workspace_bytes,
-                                hipStream_t stream) {
-    if (!q || !P || !o) return WALL_ERR_INVALID_ARG;
+wall_status_t wall_attn_fwd_run(const void *q, const void *k, const void *v, wall_dtype_t dtype,
+                                const float *P, const float *G, const float *sink_bias, void *o, float *lse,
+                                int64_t B, int64_t T, int64_t HQ, int64_t H, int64_t K, int64_t V,
+                                float scale, int64_t window_size, const int32_t *cu_seqlens,
+                                int64_t num_seqs, int64_t max_seqlen, const void *workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+    if (!q || !k || !v || !P || !o) return WALL_ERR_INVALID_ARG;
     const FwdShape s{B, T, HQ, H, K, V, cu_seqlens ? num_seqs : 0, cu_seqlens ? max_seqlen : T};
     const wall_status_t st =
         check_fwd(dtype, s, cu_seqlens, num_seqs, max_seqlen, workspace, workspace_bytes);
     if (st != WALL_OK) return st;
-    const void *ptrs[] = {q, P, o, G, sink_bias, lse};
+    const void *ptrs[] = {q, k, v, P, o, G, sink_bias, lse};
     for (const void *p : ptrs)
         if (p && !aligned(p, 16)) return WALL_ERR_INVALID_ARG;
-    return enqueue_run(q, dtype, P, G, sink_bias, o, lse, s, scale, window_size, workspace, stream);
+    return enqueue_run(q, k, v, dtype, P, G, sink_bias, o, lse, s, scale, window_size, workspace, stream);
 }
 
 wall_status_t wall_attn_fwd(const void *q, const void *k, const void *v, wall_dtype_t dtype,
@@ -207,7 +209,7 @@ wall_status_t wall_attn_fwd(const void *q, const void *k, const void *v, wall_dt
         if (p && !aligned(p, 16)) return WALL_ERR_INVALID_ARG;
     const wall_status_t sp = enqueue_prepare(k, v, dtype, P, s, cu_seqlens, workspace, stream);
     if (sp != WALL_OK) return sp;
-    return enqueue_run(q, dtype, P, G, sink_bias, o, lse, s, scale, window_size, workspace, stream);
+    return enqueue_run(q, k, v, dtype, P, G, sink_bias, o, lse, s, scale, window_size, workspace, stream);
 }
 
 size_t wall_attn_bwd_workspace_size(int64_t B, int64_t T, int64_t HQ, int64_t K, int64_t num_seqs) {

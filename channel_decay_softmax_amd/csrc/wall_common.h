@@ -18,12 +18,11 @@ typedef __attribute__((ext_vector_type(8))) float f32x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 
 // ----------------------------------------------------------------- geometry
-// Rows of one key / query tile.  Anchors are chosen per TILE rows, per query
-// head and per channel, so this is also the anchor granularity.
+// Rows of one key / query tile.  The forward anchors the keys of a tile per
+// query head and per channel at the floored prefix of the tile's last row
+// (for the queries of later tiles); the backward anchors its 128-row blocks
+// at their middle row (ANCHOR_ROW).
 constexpr int TILE = 128;
-// Row of the tile whose floored prefix is the anchor: the middle row keeps
-// both exp2 factors of every pair inside the tile within half the tile's
-// prefix range.
 constexpr int ANCHOR_ROW = 64;
 // Rows per chunk of the two-level prefix scan.
 constexpr int SCAN_CHUNK = 128;
@@ -36,15 +35,6 @@ constexpr float LN2 = 0.6931471805599453f;
 // the smallest denormal), and 126 keeps every factor finite.
 constexpr float EXP2_LO = -160.0f;
 constexpr float EXP2_HI = 126.0f;
-
-// Integer exponent that moves a value anchored at one tile to another tile's
-// anchor (the difference of two integer anchors).  It is applied with ldexp
-// to the anchored value itself, never materialised as a factor 2^d: such a
-// factor is often below the float32 normal range (a fast channel's anchors
-// are ~150 apart per tile) while the product it would form is a normal
-// number, and a denormal factor is not reliably kept.  Capped at +127, which
-// only a prefix that grows (gates above 1) by more than that can reach.
-__device__ inline int anchor_shift(float d) { return (int)fminf(fmaxf(d, -1024.0f), 127.0f); }
 
 // One packed sequence (or one batch row).
 struct SegInfo {
@@ -60,14 +50,15 @@ inline __host__ __device__ size_t align_up(size_t x, size_t a) { return (x + a -
 // ----------------------------------------------------------------- workspace layouts
 // Per (tile, query head) carry record, 1 KB: words 0..K/2-1 hold, per channel
 // pair, 128*(R[t-1] - R[t]) clamped to [0, 255*128] as two u16 (the bf16
-// exponent-field decrement that moves a query anchored at tile t to tile t-1);
-// word REC_GROW is 1 when some channel has R[t-1] < R[t] (a prefix that grows
-// over the boundary), else 0.  All zero for a sequence's first tile.
+// exponent-field decrement that moves a query anchored at tile t to tile t-1;
+// R[t] is the floored prefix of tile t's last row); word REC_GROW is 1 when
+// some channel has R[t-1] < R[t] (a prefix that grows over the tile), else 0.
+// All zero for a sequence's first tile.
 constexpr int REC_WORDS = 256;
 constexpr int REC_GROW = 128;
 
 // Forward workspace: segment table | anchors | carry records | rescaled key
-// tiles | transposed value tiles.
+// tiles | transposed value tiles (the last four for bf16 inputs only).
 struct FwdLayout {
     int64_t nseg;        // sequences (num_seqs with packing, else B)
     int64_t tiles;       // upper bound on sum_s ceil(len_s / TILE)
@@ -78,7 +69,8 @@ inline FwdLayout fwd_layout(int64_t esize, int64_t B, int64_t T, int64_t HQ, int
                             int64_t K, int64_t V, int64_t num_seqs) {
     FwdLayout L;
     L.nseg = num_seqs > 0 ? num_seqs : B;
-    L.tiles = cdiv(B * T, TILE) + L.nseg;
+    // the float32 path reads the raw tensors: no tiles
+    L.tiles = esize == 2 ? cdiv(B * T, TILE) + L.nseg : 0;
     size_t o = 0;
     L.off_seg = o;
     o = align_up(o + sizeof(SegInfo) * (size_t)L.nseg, 256);
@@ -136,22 +128,26 @@ struct PrepArgs {
     const float *P;    // [rows, HQ, K]
     SegInfo *seg;      // [nseg], written here
     const int32_t *cu; // [nseg + 1] sequence starts, or null for B sequences of T rows
-    float *anchor;     // [tiles, HQ, K]
+    float *anchor;     // [tiles, HQ, K] floored prefix of each tile's last row
     uint32_t *rec;     // [tiles, HQ, REC_WORDS]
-    void *kt;          // [tiles, HQ, TILE, K]
-    void *vt;          // [tiles, H, V, TILE]
+    void *kt;          // [tiles, HQ, TILE, K] bf16
+    void *vt;          // [tiles, H, V, TILE] bf16
     int64_t nseg, tiles, HQ, H, K, V, T;
 };
+// bf16: the sequence table, anchors, carry records, key and value tiles;
+// float32: the sequence table only.
 hipError_t launch_prep(const PrepArgs &a, bool bf16, hipStream_t st);
 
 struct FwdArgs {
     const void *q;          // [rows, HQ, K]
+    const void *k;          // [rows, H, K] raw keys (the query's own tile, float32 path)
+    const void *v;          // [rows, H, V] raw values (float32 path)
     const float *P;         // [rows, HQ, K]
     const float *G;         // [rows, HQ] or null
     const float *sink;      // [HQ] or null
-    const void *kt;         // [tiles, HQ, TILE, K]
-    const void *vt;         // [tiles, H, V, TILE]
-    const float *anchor;    // [tiles, HQ, K]
+    const void *kt;         // [tiles, HQ, TILE, K] (bf16 path)
+    const void *vt;         // [tiles, H, V, TILE] (bf16 path)
+    const float *anchor;    // [tiles, HQ, K] (bf16 path)
     const uint32_t *rec;    // [tiles, HQ, REC_WORDS]
     const SegInfo *seg;     // [nseg]
     void *o;                // [rows, HQ, V]

@@ -4,23 +4,48 @@
 // and two 256-row query blocks, u and n-1-u, so every workgroup of a causal
 // launch does about the same number of tiles.  Wave w owns the 32 query rows
 // 256u + 32w .. +31 (one MFMA n-block); waves 0-3 sit in the block's first
-// 128-row anchor tile 2u, waves 4-7 in the second, 2u+1.  Workgroup ids are
+// 128-row tile 2u, waves 4-7 in the second, 2u+1.  Workgroup ids are
 // remapped so each XCD receives a contiguous range of heads (their key
 // caches then share that XCD's L2).
 //
-// Per wave, keys are walked from the block's last tile down to the first
-// tile the window reaches, one 32-key sub-block (one MFMA m-tile) per step:
+// Anchors.  exp2(P_i - P_j) is split as exp2(P_i - R) * exp2(R - P_j) at
+// integer per-channel anchors R (the per-tile anchors of the blog's "Fast
+// training and inference" section), chosen so that no factor of a term that
+// matters leaves the float range, at any gate strength:
+//   * keys of the tiles before the wave's own tile are read from the
+//     prepared key cache, anchored at each tile's last row.  That row lies
+//     between the key and the query, so for a prefix that falls both factors
+//     are at most about 1, and a factor that underflows belongs to a term
+//     that is itself below 2^-125;
+//   * keys of the wave's own tile (the diagonal phase, below) are read from
+//     the raw keys at anchors the wave chooses for its own 32 rows.
 //
-//   q~  the wave's bf16 queries anchored at the key tile c, q * scale*log2e *
-//       exp2(P_i - Rc).  Built from q and P at the wave's diagonal tile, then
-//       carried from tile c to tile c-1 by lowering each bf16 exponent field
-//       by the integer R[c-1] - R[c] (>= 0 while the prefix does not grow)
-//       with a saturating packed subtract: exact, and a value that would leave
-//       the bf16 range becomes 0 and, the decay only growing further back,
-//       stays negligible.  A tile where some channel's prefix grows rebuilds
-//       q~ from q and P.  These are the per-tile anchors of the blog's "Fast
-//       training and inference" section, with the key-side factor
-//       exp2(Rc - P_j) already folded into k~;
+// Diagonal phase (per wave, no LDS, no barriers).  The keys of the wave's
+// tile up to its last query, 32 at a time, against the floored prefix M of
+// the middle of the wave's rows: q~ and k~ are formed from q, k and P with
+// one exp2 per element, S^T = k~ q~^T on the matrix cores, then an online
+// softmax and O^T += v^T p^T (values from the prepared transposed tiles).
+// While every row of the wave lies within 100 log2 units of M, every factor
+// stays within 2^+-100 and the lost terms are below 2^-26.  Beyond that the
+// keys before the wave's rows are read at the floored prefix of the row just
+// before the wave (between every such pair), and the 32 x 32 block of the
+// wave's own rows is formed pair by pair in float32 without any anchor,
+// scale * sum_n q_in k_jn exp2(P_in - P_jn).
+//
+// Pipeline (the tiles before the wave's own).  Per wave, keys are walked from
+// tile 2u (2u - 1 when the block has a single tile) down to the first tile
+// the window reaches, one 32-key sub-block (one MFMA m-tile) per step; a
+// tile at or after a wave's own tile is masked whole for that wave:
+//
+//   q~  the wave's bf16 queries anchored at key tile c, q * scale*log2e *
+//       exp2(P_i - Rc).  Built from q and P at the tile before the wave's
+//       own, then carried from tile c to tile c-1 by lowering each bf16
+//       exponent field by the integer R[c-1] - R[c] (>= 0 while the prefix
+//       does not grow) with a saturating packed subtract: exact, and a value
+//       that would leave the bf16 range becomes 0 and, the decay only
+//       growing further back, stays negligible.  A tile where some channel's
+//       prefix grows rebuilds q~ from q and P.  The key-side factor
+//       exp2(Rc - P_j) is already folded into k~;
 //   S^T = k~ q~^T - m on v_mfma_f32_32x32x16_bf16: the accumulator starts at
 //       -m (the running max), so scores come back already relative to it,
 //       one query column per lane, all softmax state in-lane;
@@ -48,7 +73,8 @@
 // into the buffer just released; each buffer is an LDS variable of its own
 // so the compiler does not wait on the loads either.  A key buffer also
 // carries the tile's carry record (from the preparation step) and its keys'
-// scalar-gate prefix.
+// scalar-gate prefix.  The first tiles' copies are issued before the
+// diagonal phase and land while it runs.
 //
 // The key rows fed to the S^T MFMA are permuted (bits 2 and 3 of the row
 // index swapped) so each lane's output registers come out as runs of 8
@@ -81,6 +107,11 @@ constexpr int NSB = TILE / SB;  // sub-blocks per tile (pipeline steps per tile)
 // a query's sum of the 32 p of one sub-block above this raises m (so every p
 // stays at most 2^12 before it is rounded to bf16 and summed in fp32)
 constexpr float PSUM_LIM = 4096.0f;
+// Largest distance (log2 units) of a wave's rows' prefix from the diagonal
+// phase's middle-row anchor: within it every factor stays inside 2^+-100 and
+// a term lost to an underflowing factor is below 2^(100 - 126).  Beyond it
+// the wave's own 32 x 32 block is formed pair by pair.
+constexpr float DIAG_SPREAD = 100.0f;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -478,7 +509,8 @@ struct Wave {
 
     // per-tile facts (wave-uniform)
     int key_tile0;   // first key of the current tile (sequence-relative)
-    int mask_bits;   // bit B: step B's scores need causal / window / sequence-end masks
+    int mask_bits;   // bit B: step B's scores need window masks (all bits: a dead tile)
+    bool dead;       // the tile is the wave's own tile or later: every key masked
     const char *recp;  // the tile's carry record, or zeros (no carry) for this wave
     bool carry_on_grow;  // ... by rebuilding it there (some channel's prefix grows)
     int window, len, q0w;
@@ -523,9 +555,9 @@ struct Wave {
         f32x16 &s = S[B & 1];
         if (mask_bits & (1 << B)) {
             // visible keys of this lane's query, as offsets from its first key in
-            // the sub-block: at most khi (causal, sequence end), at least klo (window)
+            // the sub-block: at most khi (none on a dead tile), at least klo (window)
             const int kb0 = key_tile0 + SB * B + 8 * hl;
-            const int khi = min(qrow, len - 1) - kb0;
+            const int khi = dead ? -1 : min(qrow, len - 1) - kb0;
             if (window > 0) {
                 const int klo = qrow - window + 1 - kb0;
 #pragma unroll
@@ -654,16 +686,19 @@ struct Kernel {
     // per-tile facts of tile c whose keys (and carry record) are in kcur
     __device__ __forceinline__ void tile_facts(int c, const char *kcur) {
         wv.key_tile0 = TILE * c;
-        // the diagonal tile (and the sequence end) masks every step; a window
-        // masks the steps whose first key is at or below lim
-        int mb = c >= qt_w ? (1 << NSB) - 1 : 0;
-        if (wv.window > 0) {
+        // the wave's own tile (its keys were read in the diagonal phase) masks
+        // every step; a window masks the steps whose first key is at or below lim
+        const bool dead = c >= qt_w;
+        int mb = dead ? (1 << NSB) - 1 : 0;
+        if (!dead && wv.window > 0) {
             const int lim = wv.q0w + WQ - 1 - wv.window - TILE * c;
             if (lim >= 0) mb |= (2 << min(lim / SB, NSB - 1)) - 1;
         }
         wv.mask_bits = mb;
+        wv.dead = dead;
         const bool grow = reinterpret_cast<const uint32_t *>(kcur + LY::REC_OFF)[REC_GROW] != 0u;
-        const bool go_on = wave_on && c <= qt_w && c - 1 >= c_lo;
+        // q~ sits at tile c's anchors only for a tile before the wave's own
+        const bool go_on = wave_on && c < qt_w && c - 1 >= c_lo;
         // Without a carry the shifts are read from zeros.  A tile where some
         // channel's prefix grows rebuilds q~ at BARK, after all carries.
         wv.recp = go_on ? kcur + LY::REC_OFF : zrec;
@@ -751,6 +786,175 @@ struct Kernel {
             issue_k(PB ? k1 : k0, max(c - 2, c_lo));
         }
     }
+    // ---- the diagonal phase: keys of the wave's own tile up to its last query
+    // q~ of the lane's query at the anchors floor(P[Pa row]) (0 for a row past
+    // the sequence); dev: the largest |P_i - R| over the lane's channels.
+    __device__ __forceinline__ void diag_q(const float *Pa, QOp<K> &qo, float &dev) const {
+        const bool qv = wv.qrow < sg.len;
+        const int64_t tok = (int64_t)sg.start + (qv ? wv.qrow : 0);
+        const __bf16 *qg = static_cast<const __bf16 *>(a.q) + (tok * a.HQ + hq) * K;
+        const float *pg = a.P + (tok * a.HQ + hq) * K;
+        float d = 0.f;
+#pragma unroll
+        for (int s8 = 0; s8 < KS; ++s8) {
+            const int ch0 = 16 * s8 + 8 * wv.hl;
+            const f32x8 qv8 = __builtin_convertvector(*reinterpret_cast<const bf16x8 *>(qg + ch0), f32x8);
+            const f32x8 pv8 = *reinterpret_cast<const f32x8 *>(pg + ch0);
+            const f32x8 rv = *reinterpret_cast<const f32x8 *>(Pa + ch0);
+            f32x8 qh;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float x = pv8[e] - floorf(rv[e]);
+                d = fmaxf(d, fabsf(x));
+                qh[e] = qv ? qv8[e] * a.qscale * exp2f(fminf(fmaxf(x, EXP2_LO), EXP2_HI)) : 0.f;
+            }
+            qo[s8] = __builtin_convertvector(qh, bf16x8);
+            __builtin_amdgcn_sched_barrier(0);  // one channel step's loads in flight at a time
+        }
+        dev = qv ? d : 0.f;
+    }
+    // S^T of the 32 keys from kb against qa, both anchored at floor(P[Pa row]):
+    // the lane forms k~ of key row kb + key_perm(lane) (rows past the sequence
+    // read its last row; they are masked later).
+    __device__ __forceinline__ f32x16 diag_scores(int kb, const float *Pa, const QOp<K> &qa) const {
+        const int kr = min(kb + key_perm(lane & 31), sg.len - 1);
+        const int64_t tok = (int64_t)sg.start + kr;
+        const __bf16 *kg = static_cast<const __bf16 *>(a.k) + (tok * a.H + h) * K;
+        const float *pg = a.P + (tok * a.HQ + hq) * K;
+        f32x16 S = {};
+#pragma unroll
+        for (int s8 = 0; s8 < KS; ++s8) {
+            const int ch0 = 16 * s8 + 8 * wv.hl;
+            const f32x8 kv8 = __builtin_convertvector(*reinterpret_cast<const bf16x8 *>(kg + ch0), f32x8);
+            const f32x8 pv8 = *reinterpret_cast<const f32x8 *>(pg + ch0);
+            const f32x8 rv = *reinterpret_cast<const f32x8 *>(Pa + ch0);
+            f32x8 kh;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) kh[e] = kv8[e] * exp2f(fminf(fmaxf(floorf(rv[e]) - pv8[e], EXP2_LO), EXP2_HI));
+            S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_convertvector(kh, bf16x8), qa[s8], S, 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);  // one channel step's loads in flight at a time
+        }
+        return S;
+    }
+    // The 32 x 32 block of the wave's own rows (keys from kb = the wave's first
+    // row), pair by pair in float32: scale*log2e * sum_n q_in k_jn exp2(P_in - P_jn).
+    // One key at a time, so that few registers are live (a rare path).
+    __device__ f32x16 exact_scores(int kb) const {
+        const int qrow = wv.qrow;
+        const bool qv = qrow < sg.len;
+        const int64_t qtok = (int64_t)sg.start + (qv ? qrow : 0);
+        const __bf16 *qg = static_cast<const __bf16 *>(a.q) + (qtok * a.HQ + hq) * K;
+        const float *pq = a.P + (qtok * a.HQ + hq) * K;
+        const int kb0 = kb + 8 * wv.hl;
+        f32x16 S = {};
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int j = kb0 + 16 * (r / 8) + (r % 8);
+            float acc = 0.f;
+            if (qv && j <= qrow) {
+                const int64_t jt = (int64_t)sg.start + j;
+                const __bf16 *kg = static_cast<const __bf16 *>(a.k) + (jt * a.H + h) * K;
+                const float *pk = a.P + (jt * a.HQ + hq) * K;
+#pragma unroll 1
+                for (int c8 = 0; c8 < K / 8; ++c8) {
+                    const f32x8 qq = __builtin_convertvector(*reinterpret_cast<const bf16x8 *>(qg + 8 * c8), f32x8);
+                    const f32x8 pi = *reinterpret_cast<const f32x8 *>(pq + 8 * c8);
+                    const f32x8 kk = __builtin_convertvector(*reinterpret_cast<const bf16x8 *>(kg + 8 * c8), f32x8);
+                    const f32x8 pj = *reinterpret_cast<const f32x8 *>(pk + 8 * c8);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        acc = fmaf(qq[e] * kk[e], exp2f(fminf(fmaxf(pi[e] - pj[e], EXP2_LO), EXP2_HI)), acc);
+                }
+            }
+            S[r] = acc * a.qscale;
+        }
+        return S;
+    }
+    // Masks, the online softmax of the 32 keys from kb (scores not relative to
+    // m) and O^T += v^T p^T with the values of the wave's tile (vtile, keys
+    // from kt0).
+    __device__ __forceinline__ void diag_block(f32x16 S, int kb, const __bf16 *vtile, int kt0) {
+        const int qrow = wv.qrow, len = sg.len;
+        const bool qv = qrow < len;
+        const int kb0 = kb + 8 * wv.hl;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int j = kb0 + 16 * (r / 8) + (r % 8);
+            bool vis = qv && j <= qrow;
+            if (a.window > 0) vis = vis && qrow - j < a.window;
+            float x = S[r];
+            if (HAS_G) x -= a.G[((int64_t)sg.start + min(j, len - 1)) * a.HQ + hq];
+            S[r] = vis ? x : -__builtin_inff();
+        }
+        const float m1 = max3(max3(S[0], S[1], S[2]), max3(S[3], S[4], S[5]), max3(S[6], S[7], S[8]));
+        const float m2 = max3(max3(S[9], S[10], S[11]), max3(S[12], S[13], S[14]), S[15]);
+        const float mn = fmaxf(wv.m, pair_max(__builtin_elementwise_maximum(m1, m2)));
+        const float al = fast_exp2(wv.m - mn);
+        uint32_t pw[2][4];
+        float ps = 0.f;
+        const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const bf16x2 pp = {(__bf16)fast_exp2(S[8 * t + 2 * e] - mn), (__bf16)fast_exp2(S[8 * t + 2 * e + 1] - mn)};
+                pw[t][e] = __builtin_bit_cast(uint32_t, pp);
+                ps = __builtin_amdgcn_fdot2_f32_bf16(pp, one, ps, false);
+            }
+        wv.l = wv.l * al + ps;
+        wv.m = mn;
+        const int col = lane & 31;
+#pragma unroll
+        for (int vt = 0; vt < VT; ++vt) {
+            wv.O[vt] *= al;
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const bf16x8 x = *reinterpret_cast<const bf16x8 *>(vtile + (32 * vt + col) * TILE + (kb - kt0) + 16 * t +
+                                                                    8 * wv.hl);
+                wv.O[vt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, W::as_bf16(pw[t]), wv.O[vt], 0, 0, 0);
+            }
+        }
+    }
+    // The whole diagonal phase of the wave (queries q0w.., tile qt): leaves O,
+    // m (from -FLT_MAX; the lane's own key is always visible) and l.
+    __device__ void diag_phase(int qt, int q0w) {
+        const int wq = (q0w - TILE * qt) / WQ;  // the wave's 32-row block within its tile
+        const int kt0 = TILE * qt;
+        const int last = min(q0w + WQ - 1, sg.len - 1);
+        const float *Pm = a.P + ((int64_t)(sg.start + ((q0w + last) >> 1)) * a.HQ + hq) * K;
+        const __bf16 *vtile = static_cast<const __bf16 *>(vt_tile(qt));
+        // the lowest 32-key block any query of the wave sees
+        int b_lo = 0;
+        if (a.window > 0) {
+            const int kmin = q0w - a.window + 1;
+            if (kmin > kt0) b_lo = (kmin - kt0) / SB;
+        }
+#pragma unroll
+        for (int vt = 0; vt < VT; ++vt) wv.O[vt] = f32x16{};
+        wv.m = -FLT_MAX;
+        wv.l = 0.f;
+        QOp<K> qa;
+        float dev;
+        diag_q(Pm, qa, dev);
+        if (!__any(dev > DIAG_SPREAD)) {
+            for (int b = wq; b >= b_lo; --b) {
+                const int kb = kt0 + SB * b;
+                diag_block(diag_scores(kb, Pm, qa), kb, vtile, kt0);
+            }
+        } else {
+            diag_block(exact_scores(q0w), q0w, vtile, kt0);
+            if (wq - 1 >= b_lo) {
+                // the keys before the wave's rows, at the row just before them
+                const float *Pb = a.P + ((int64_t)(sg.start + q0w - 1) * a.HQ + hq) * K;
+                diag_q(Pb, qa, dev);
+                for (int b = wq - 1; b >= b_lo; --b) {
+                    const int kb = kt0 + SB * b;
+                    diag_block(diag_scores(kb, Pb, qa), kb, vtile, kt0);
+                }
+            }
+        }
+    }
+
     // reads issued after the op at position P
     template <int P, int R>
     __device__ __forceinline__ void maybe_read() {
@@ -831,12 +1035,16 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
         const int q0w = BQ * u + WQ * w;
         const bool wave_on = q0w < sg.len;
         const int qrow = q0w + col;
-        const int c_hi = min(2 * u + 1, ntiles - 1);
+        // the pipeline's tiles: from the block's first tile (2u; its keys are the
+        // second tile's earlier keys) or, when the block has a single tile, the
+        // one before it, down to the first tile the window reaches
+        const int c_hi = 2 * u + 1 < ntiles ? 2 * u : 2 * u - 1;
         int c_lo = 0;
         if (a.window > 0) {
             const int kmin = BQ * u - a.window + 1;
             c_lo = kmin > 0 ? kmin / TILE : 0;
         }
+        const bool run_pipe = c_hi >= c_lo;  // uniform over the workgroup
         kr.qt_w = qt_w;
         kr.c_lo = c_lo;
         wv.qrow = qrow;
@@ -847,71 +1055,92 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
         float g_i = 0.f;
         if (HAS_G && wave_on && qrow < sg.len) g_i = a.G[((int64_t)sg.start + qrow) * HQ + hq];
 
+        // ---- prologue: tile c_hi into buffers 0 and the keys of tile c_hi - 1
+        // into key buffer 1, copied while each wave works through its own tile
+        __syncthreads();  // the previous block's last reads of every buffer are done
+        if (run_pipe) {
+            kr.issue_k(k0, c_hi);
+            kr.issue_v(v0, c_hi);
+            kr.issue_k(k1, max(c_hi - 1, c_lo));
+        }
+        if (wave_on) {
+            kr.diag_phase(qt_w, q0w);
+            // q~ for the pipeline at the anchors of the tile before the wave's own
+            if (qt_w > 0 && run_pipe) load_qop<K, true>(a, sg, hq, qt_w - 1, qrow, hl, wv.qop);
+        } else {
 #pragma unroll
-        for (int vt = 0; vt < VT; ++vt) wv.O[vt] = f32x16{};
-        wv.negm = f32x16{};
-        wv.m = 0.f;
-        wv.l = 0.f;
+            for (int vt = 0; vt < VT; ++vt) wv.O[vt] = f32x16{};
+            wv.m = 0.f;
+            wv.l = 0.f;
+        }
+        if (!wave_on || qt_w == 0 || !run_pipe) {
+#pragma unroll
+            for (int s8 = 0; s8 < KS; ++s8) wv.qop[s8] = bf16x8{};
+        }
+        {
+            // a lane whose row lies past the sequence restarts at m = 0 and raises
+            // m at its first visible key (its output is never stored); a wave
+            // with no rows never raises
+            const bool qv = wave_on && qrow < sg.len;
+            wv.m = qv ? wv.m : 0.f;
+            wv.lim = !wave_on ? __builtin_inff() : qv ? PSUM_LIM : -1.f;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) wv.negm[r] = -wv.m;
         wv.alpha = 1.f;
-        wv.lim = wave_on ? -1.f : __builtin_inff();  // a wave with no rows never raises
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int e = 0; e < 4; ++e) wv.Pw[0][t][e] = 0u;
-
-        // ---- prologue: q~ at the diagonal tile; tile c_hi into buffers 0, the keys of
-        // tile c_hi - 1 into key buffer 1
-        __syncthreads();  // the previous block's last reads of every buffer are done
-        // the first two key tiles and the first value tile are copied while q~
-        // is built
-        kr.issue_k(k0, c_hi);
-        kr.issue_v(v0, c_hi);
-        kr.issue_k(k1, max(c_hi - 1, c_lo));
-        if (wave_on) load_qop<K, false>(a, sg, hq, qt_w, qrow, hl, wv.qop);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        // the scores of the first sub-block (3 of tile c_hi), S[1]
-        {
-            const char *kb = k0 + wv.kbase + (NSB - 1) * (SB / KL::NBLK) * (2 * K);
-#pragma unroll
-            for (int s8 = 0; s8 < KS; ++s8) {
-                const bf16x8 x = *reinterpret_cast<const bf16x8 *>(kb + 32 * s8);
-                wv.S[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, wv.qop[s8], s8 ? wv.S[1] : wv.negm, 0, 0, 0);
-            }
-        }
 
-        kr.wave_on = wave_on;
-        // prefetch the first reads of tile c_hi (parity 0)
-        wv.kcur = k0;
-        wv.knext = k1;
-        wv.vcur = v0;
-        wv.vprev = v1;
-        wv.read_first(std::make_integer_sequence<int, NPF>{});
-
-        int c = c_hi;
-        for (;;) {
-            wv.kcur = k0; wv.knext = k1; wv.vcur = v0; wv.vprev = v1;
-            kr.tile_facts(c, k0);
-            kr.template run_tile<0, false>(c, std::make_integer_sequence<int, Plan::N>{});
-            if (--c < c_lo) break;
-            wv.kcur = k1; wv.knext = k0; wv.vcur = v1; wv.vprev = v0;
-            kr.tile_facts(c, k1);
-            kr.template run_tile<1, false>(c, std::make_integer_sequence<int, Plan::N>{});
-            if (--c < c_lo) break;
-        }
-        // the loads issued past tile c_lo land before the buffers are reused
-        // (or the workgroup ends)
-        wait_vm<0>();
-        // the last sub-block's PV products (sub-block 0 of tile c_lo, p in Pw[0])
-        {
-            const char *vb = ((c_hi - c_lo) & 1 ? v1 : v0) + wv.vbase;
+        if (run_pipe) {
+            // the scores of the first sub-block (3 of tile c_hi), S[1]
+            {
+                const char *kb = k0 + wv.kbase + (NSB - 1) * (SB / KL::NBLK) * (2 * K);
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int vt = 0; vt < VT; ++vt) {
-                    const bf16x8 x = *reinterpret_cast<const bf16x8 *>(vb + vt * (32 / VL::NBLK) * (2 * TILE) + 32 * t);
-                    wv.O[vt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, W::as_bf16(wv.Pw[0][t]), wv.O[vt], 0, 0, 0);
+                for (int s8 = 0; s8 < KS; ++s8) {
+                    const bf16x8 x = *reinterpret_cast<const bf16x8 *>(kb + 32 * s8);
+                    wv.S[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, wv.qop[s8], s8 ? wv.S[1] : wv.negm, 0, 0, 0);
                 }
+            }
+
+            kr.wave_on = wave_on;
+            // prefetch the first reads of tile c_hi (parity 0)
+            wv.kcur = k0;
+            wv.knext = k1;
+            wv.vcur = v0;
+            wv.vprev = v1;
+            wv.read_first(std::make_integer_sequence<int, NPF>{});
+
+            int c = c_hi;
+            for (;;) {
+                wv.kcur = k0; wv.knext = k1; wv.vcur = v0; wv.vprev = v1;
+                kr.tile_facts(c, k0);
+                kr.template run_tile<0, false>(c, std::make_integer_sequence<int, Plan::N>{});
+                if (--c < c_lo) break;
+                wv.kcur = k1; wv.knext = k0; wv.vcur = v1; wv.vprev = v0;
+                kr.tile_facts(c, k1);
+                kr.template run_tile<1, false>(c, std::make_integer_sequence<int, Plan::N>{});
+                if (--c < c_lo) break;
+            }
+            // the loads issued past tile c_lo land before the buffers are reused
+            // (or the workgroup ends)
+            wait_vm<0>();
+            // the last sub-block's PV products (sub-block 0 of tile c_lo, p in Pw[0])
+            {
+                const char *vb = ((c_hi - c_lo) & 1 ? v1 : v0) + wv.vbase;
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int vt = 0; vt < VT; ++vt) {
+                        const bf16x8 x =
+                            *reinterpret_cast<const bf16x8 *>(vb + vt * (32 / VL::NBLK) * (2 * TILE) + 32 * t);
+                        wv.O[vt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, W::as_bf16(wv.Pw[0][t]), wv.O[vt], 0, 0, 0);
+                    }
+            }
+            // a raise owed by the last step was applied by its RESC
         }
 
         // ---- epilogue: sink, normalisation, o and lse.  Every wave is past its

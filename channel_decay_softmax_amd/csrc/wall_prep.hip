@@ -7,19 +7,25 @@
 //    tiled workspace; tiles never straddle two sequences, so a tile's rows
 //    always share one prefix P); block (0, 0) also stores the table.
 // 2. keys, per (tile, query head): the anchors R[n] = floor(P[a][n]) at the
-//    tile's middle row a, the carry record that moves a query from this
-//    tile's anchors to the previous tile's, and the decay-rescaled keys
+//    tile's last row a, the carry record that moves a query from this tile's
+//    anchors to the previous tile's, and the decay-rescaled keys
 //        k~[j][n] = k[j][n] * exp2(R[n] - P[j][n]),
 //    zero-padded to 128 rows.  This is the blog's per-tile anchor split
 //    ("Fast training and inference", per-tile anchors:
 //    exp2(P_i - P_j) = exp2(P_i - R) * exp2(R - P_j)) applied on the key
 //    side once per (tile, head) instead of once per (query tile, key tile);
 //    it is the same fold the README's decode cache performs with
-//    k_tilde[j] = k[j] * exp2(R_c - P[j]).
+//    k_tilde[j] = k[j] * exp2(R_c - P[j]).  The fused kernel reads these
+//    keys only from queries after the tile, and the last row lies between
+//    every such pair: for a prefix that falls, both factors are at most
+//    about 1, so a factor that underflows belongs to a negligible term, at
+//    any gate strength.  (Keys of a query's own tile are handled inside the
+//    fused kernel from the raw keys.)
 // 3. values, per (tile, kv head): v transposed to [V][128] for the bf16 MFMA
 //    kernel (its PV operand reads keys contiguously, each thread transposing
-//    an 8 x 8 block in registers) and kept as [128][V] for the float32
-//    kernel; zero-padded.
+//    an 8 x 8 block in registers); zero-padded.
+// The float32 forward reads the raw tensors; for it only the sequence table
+// is written (one block).
 #include "wall_common.h"
 
 namespace wall {
@@ -83,11 +89,6 @@ struct Vec8<__bf16> {
         *reinterpret_cast<bf16x8 *>(p) = __builtin_convertvector(v, bf16x8);
     }
 };
-template <>
-struct Vec8<float> {
-    static __device__ inline f32x8 load(const float *p) { return *reinterpret_cast<const f32x8 *>(p); }
-    static __device__ inline void store(float *p, f32x8 v) { *reinterpret_cast<f32x8 *>(p) = v; }
-};
 
 template <typename T, int K>
 __device__ inline void key_tile(const PrepArgs &a, int tile, int hq, const SegInfo &sg) {
@@ -97,7 +98,7 @@ __device__ inline void key_tile(const PrepArgs &a, int tile, int hq, const SegIn
     const int c = tile - sg.tile_base;
     const int h = hq / (int)(a.HQ / a.H);
     const int c8 = threadIdx.x % CPR, r0 = threadIdx.x / CPR;
-    const int arow = min(c * TILE + ANCHOR_ROW, sg.len - 1);
+    const int arow = min(c * TILE + TILE - 1, sg.len - 1);
     const float *Pa = a.P + ((int64_t)(sg.start + arow) * a.HQ + hq) * K + c8 * 8;
     f32x8 R;
     for (int e = 0; e < 8; ++e) R[e] = floorf(Pa[e]);
@@ -110,7 +111,7 @@ __device__ inline void key_tile(const PrepArgs &a, int tile, int hq, const SegIn
         for (int e = 0; e < 8; e += 2) {
             uint32_t w = 0;
             if (c > 0) {
-                const int prow = (c - 1) * TILE + ANCHOR_ROW;  // anchor row of tile c-1 (< len)
+                const int prow = c * TILE - 1;  // anchor row of tile c-1: its last row
                 const float *Pp = a.P + ((int64_t)(sg.start + prow) * a.HQ + hq) * K + c8 * 8;
                 const float d0 = floorf(Pp[e]) - R[e], d1 = floorf(Pp[e + 1]) - R[e + 1];
                 up = up || d0 < 0.f || d1 < 0.f;
@@ -146,9 +147,9 @@ __device__ inline void key_tile(const PrepArgs &a, int tile, int hq, const SegIn
     }
 }
 
-// Value tile of (tile, kv head): transposed [V][TILE] (TRANSPOSE) or [TILE][V].
-// Thread (kb, db) moves the 8 x 8 block of keys 8kb.. and values 8db..
-template <typename T, int V, bool TRANSPOSE>
+// Value tile of (tile, kv head), transposed [V][TILE].  Thread (kb, db)
+// moves the 8 x 8 block of keys 8kb.. and values 8db..
+template <typename T, int V>
 __device__ inline void value_tile(const PrepArgs &a, int tile, int h, const SegInfo &sg) {
     constexpr int DB = V / 8, KB = TILE / 8;
     const int c = tile - sg.tile_base;
@@ -162,17 +163,12 @@ __device__ inline void value_tile(const PrepArgs &a, int tile, int h, const SegI
             const int j = c * TILE + kb * 8 + i;
             x[i] = j < sg.len ? Vec8<T>::load(vin + ((int64_t)(sg.start + j) * a.H + h) * V + db * 8) : f32x8{};
         }
-        if (TRANSPOSE) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                f32x8 col;
+        for (int e = 0; e < 8; ++e) {
+            f32x8 col;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) col[i] = x[i][e];
-                Vec8<T>::store(vout + (db * 8 + e) * TILE + kb * 8, col);
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) Vec8<T>::store(vout + (kb * 8 + i) * V + db * 8, x[i]);
+            for (int i = 0; i < 8; ++i) col[i] = x[i][e];
+            Vec8<T>::store(vout + (db * 8 + e) * TILE + kb * 8, col);
         }
     }
 }
@@ -180,7 +176,7 @@ __device__ inline void value_tile(const PrepArgs &a, int tile, int h, const SegI
 // Block id = tile * (HQ + H) + y; y < HQ: keys of query head y, else values
 // of kv head y - HQ.  The heads of one tile are neighbours in launch order, so
 // the query heads that share a kv head read its key rows from L2.
-template <typename T, int K, int V, bool TRANSPOSE>
+template <int K, int V>
 __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
     const int nh = (int)(a.HQ + a.H);
     const int tile = blockIdx.x / nh, y = blockIdx.x % nh;
@@ -188,30 +184,34 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
     if (!block_segment(a, tile, tile == 0 && y == 0, sg)) return;  // beyond the last used tile
     if ((tile - sg.tile_base) * TILE >= sg.len) return;
     if (y < a.HQ)
-        key_tile<T, K>(a, tile, y, sg);
+        key_tile<__bf16, K>(a, tile, y, sg);
     else
-        value_tile<T, V, TRANSPOSE>(a, tile, y - (int)a.HQ, sg);
+        value_tile<__bf16, V>(a, tile, y - (int)a.HQ, sg);
 }
 
-template <typename T, int K, int V, bool TRANSPOSE>
+// The sequence table alone (the float32 forward reads the raw tensors).
+__global__ __launch_bounds__(256) void seg_table_kernel(PrepArgs a) {
+    SegInfo sg;
+    block_segment(a, 0, true, sg);
+}
+
+template <int K, int V>
 hipError_t run_prep(const PrepArgs &a, hipStream_t st) {
-    hipLaunchKernelGGL((prep_kernel<T, K, V, TRANSPOSE>), dim3((unsigned)((a.HQ + a.H) * a.tiles)), dim3(256), 0,
-                       st, a);
+    hipLaunchKernelGGL((prep_kernel<K, V>), dim3((unsigned)((a.HQ + a.H) * a.tiles)), dim3(256), 0, st, a);
     return hipGetLastError();
-}
-
-template <typename T, bool TRANSPOSE>
-hipError_t dispatch_prep(const PrepArgs &a, hipStream_t st) {
-    if (a.K == 64 && a.V == 64) return run_prep<T, 64, 64, TRANSPOSE>(a, st);
-    if (a.K == 64 && a.V == 128) return run_prep<T, 64, 128, TRANSPOSE>(a, st);
-    if (a.K == 128 && a.V == 64) return run_prep<T, 128, 64, TRANSPOSE>(a, st);
-    return run_prep<T, 128, 128, TRANSPOSE>(a, st);
 }
 
 }  // namespace
 
 hipError_t launch_prep(const PrepArgs &a, bool bf16, hipStream_t st) {
-    return bf16 ? dispatch_prep<__bf16, true>(a, st) : dispatch_prep<float, false>(a, st);
+    if (!bf16) {
+        hipLaunchKernelGGL(seg_table_kernel, dim3(1), dim3(256), 0, st, a);
+        return hipGetLastError();
+    }
+    if (a.K == 64 && a.V == 64) return run_prep<64, 64>(a, st);
+    if (a.K == 64 && a.V == 128) return run_prep<64, 128>(a, st);
+    if (a.K == 128 && a.V == 64) return run_prep<128, 64>(a, st);
+    return run_prep<128, 128>(a, st);
 }
 
 }  // namespace wall

@@ -154,13 +154,24 @@ wall_status_t wall_prefix_append(const void *x, wall_dtype_t x_dtype, int64_t x_
  *              bytes, 256-byte aligned; contents on entry are ignored.  It
  *              holds the decay-rescaled key cache, the transposed values and
  *              the per-tile anchors of this call.
- * Numerics: exp2(P_i - P_j) is split at an integer per-tile, per-channel
- * anchor R (the blog's "per-tile anchors", section "Fast training and
- * inference") as exp2(P_i - R) * exp2(R - P_j), so no factor leaves the
- * float range while the per-channel change of P within one 64-row half of a
- * 128-row key tile stays below about 120 (log2 units).  bf16 inputs use bf16
- * MFMA operands with float32 accumulation and a float32 online softmax;
- * float32 inputs are computed in float32 throughout.
+ * Numerics: exp2(P_i - P_j) is split at integer per-channel anchors R (the
+ * blog's per-tile anchors, section "Fast training and inference") as
+ * exp2(P_i - R) * exp2(R - P_j).  A key of a 128-row tile before its
+ * query's tile is read at the floored prefix of its own tile's last row, a
+ * row between the two, so for a prefix that falls (g <= 0) neither factor
+ * exceeds 2 and a factor that underflows belongs to a term below 2^-125 of
+ * the largest.  The keys of the query's own tile are read at anchors chosen
+ * by the query's group of 32 rows: the floored prefix at the middle of its
+ * rows; or, when some row of the group lies more than 100 log2 units from
+ * it, the row just before the group for the earlier keys and no anchor at
+ * all (the decay formed pair by pair in float32) for the keys among the
+ * group's rows.  The result therefore keeps its accuracy for every g <= 0,
+ * down to closed gates; for a prefix that grows (g > 0) while it grows by
+ * less than about 100 log2 units within any 128 rows and every factor
+ * exp2(P_i - P_j) stays below about 2^100.  bf16 inputs use bf16 MFMA
+ * operands with float32 accumulation and a float32 online softmax; float32
+ * inputs are computed in float32 throughout (one anchor for all keys
+ * before a 64-row query block, pair-by-pair decay inside it).
  * Errors: INVALID_ARG for a null required pointer, a size < 1, HQ % H != 0,
  * cu_seqlens with B != 1 or num_seqs < 1 or max_seqlen < 1, misalignment, a
  * short workspace; UNSUPPORTED for K or V not in {64, 128} or another dtype;
@@ -193,8 +204,10 @@ wall_status_t wall_attn_fwd(const void *q, const void *k, const void *v, wall_dt
  *
  * wall_attn_fwd_run reads that workspace (unchanged since a prepare call
  * with the same k, v, P, shapes and cu_seqlens, ordered before it on the
- * stream) together with q, P, G and sink_bias, and writes o and lse.
- * `workspace` is read only.
+ * stream) together with q, k, v, P, G and sink_bias, and writes o and lse.
+ * k and v are the prepare call's raw keys and values: the keys of each
+ * query's own tile (and, for float32 inputs, every key and value) are read
+ * from them.  `workspace` is read only.
  * Errors are those of wall_attn_fwd for the arguments each stage takes. */
 wall_status_t wall_attn_fwd_prepare(const void *k, const void *v, wall_dtype_t dtype,
                                     const float *P,
@@ -203,7 +216,7 @@ wall_status_t wall_attn_fwd_prepare(const void *k, const void *v, wall_dtype_t d
                                     void *workspace, size_t workspace_bytes,
                                     hipStream_t stream);
 
-wall_status_t wall_attn_fwd_run(const void *q, wall_dtype_t dtype,
+wall_status_t wall_attn_fwd_run(const void *q, const void *k, const void *v, wall_dtype_t dtype,
                                 const float *P, const float *G, const float *sink_bias,
                                 void *o, float *lse,
                                 int64_t B, int64_t T, int64_t HQ, int64_t H, int64_t K, int64_t V,

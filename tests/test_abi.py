@@ -129,6 +129,14 @@ def test_fwd_rejects_invalid_arguments(kw):
     assert fwd(**kw) == INVALID
 
 
+def test_fwd_run_needs_the_raw_keys_and_values():
+    L = wall.lib()
+    wsb = L.wall_attn_fwd_workspace_size(1, 1, 256, 4, 2, 128, 128, 0)
+    for k, v in ((None, FAKE), (FAKE, None), (FAKE + 2, FAKE), (FAKE, FAKE + 4)):
+        assert L.wall_attn_fwd_run(P(FAKE), P(k), P(v), 1, P(FAKE), None, None, P(FAKE), None, 1, 256, 4, 2,
+                                   128, 128, 0.088, 0, None, 0, 0, P(FAKE), wsb, None) == INVALID
+
+
 @pytest.mark.parametrize("kw", [dict(kk=96), dict(vv=32), dict(kk=256), dict(dtype=5)])
 def test_fwd_rejects_unsupported_shapes(kw):
     assert fwd(**kw) == UNSUPPORTED
@@ -214,8 +222,9 @@ def test_workspace_sizes():
     assert L.wall_attn_fwd_workspace_size(7, 1, 10, 1, 1, 64, 64, 0) == 0
     b16 = L.wall_attn_fwd_workspace_size(1, 1, 8192, 16, 4, 128, 128, 0)
     f32 = L.wall_attn_fwd_workspace_size(0, 1, 8192, 16, 4, 128, 128, 0)
-    # key cache per query head + value tiles per kv head, 65 tiles bound
-    assert b16 >= 65 * 128 * (16 * 128 + 4 * 128) * 2 and f32 > b16
+    # bf16: key cache per query head + value tiles per kv head, 65 tiles bound;
+    # float32 reads the raw tensors and keeps only the sequence table
+    assert b16 >= 65 * 128 * (16 * 128 + 4 * 128) * 2 and 0 < f32 <= 256
     assert L.wall_attn_fwd_workspace_size(1, 1, 1000, 2, 1, 64, 64, 9) > \
         L.wall_attn_fwd_workspace_size(1, 1, 1000, 2, 1, 64, 64, 1)
 

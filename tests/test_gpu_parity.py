@@ -182,6 +182,68 @@ def test_strong_uniform_decay():
     assert_parity(o, lse, o_ref, lse_ref, "bfloat16", what="uniform g=-1")
 
 
+def _strong(gate, dtype, K, T=420):
+    """A strong uniform gate on every channel, two query heads of one kv head,
+    and a packed sequence start inside the first tile."""
+    inp = make_inputs("long_bf16", dtype=dtype, B=1, T=T, HQ=2, H=1, K=K, V=K)
+    inp.g = torch.full_like(inp.g, gate)
+    inp.cu_seqlens = torch.tensor([0, 37, T], dtype=torch.int32)
+    return inp
+
+
+@pytest.mark.parametrize("K", [64, 128])
+@pytest.mark.parametrize("dtype", ["bfloat16", "float32"])
+@pytest.mark.parametrize("gate", [-1.5, -2.0, -5.0])
+def test_strong_uniform_decay_exact(gate, dtype, K):
+    """Gates past the reach of a middle-row tile anchor (the prefix falls 2.2 to
+    7.2 log2 units per token): last-row anchors for earlier tiles and the
+    diagonal phase's own anchors (pair by pair past 100 log2 units) keep
+    every term that matters."""
+    inp = _strong(gate, dtype, K)
+    what = f"uniform g={gate} {dtype} K=V={K}"
+    o, lse = run_gpu(inp, what)
+    o_ref, lse_ref = run_oracle(inp)
+    assert_parity(o, lse, o_ref, lse_ref, dtype, what=what)
+
+
+@pytest.mark.parametrize("dtype", ["bfloat16", "float32"])
+def test_all_gates_closed(dtype):
+    """g = -800 per token: every earlier key's decay is exactly 0, so its logit
+    is 0, while a token's own key keeps s_ii = scale q_i.k_i:
+    o_i = (sum_{j<i} v_j + e^{s_ii} v_i) / (n_i + e^{s_ii}), n_i the earlier
+    tokens of i's sequence (the closed form of the oracle pins)."""
+    inp = _strong(-800.0, dtype, 128, T=300)
+    o, lse = run_gpu(inp, f"g=-800 {dtype}")
+    q = inp.q.double().numpy()[0]
+    k = inp.k.double().numpy()[0]
+    v = inp.v.double().numpy()[0]
+    ref = np.zeros(o.shape[1:])
+    lref = np.zeros(lse.shape[1:])
+    for a, b in ((0, 37), (37, 300)):
+        csum = np.cumsum(v[a:b, 0], axis=0)
+        for i in range(a, b):
+            for hq in range(2):
+                s = inp.scale * float(q[i, hq] @ k[i, 0])
+                n = i - a
+                prev = csum[i - a - 1] if n > 0 else 0.0
+                ref[i, hq] = (prev + math.exp(s) * v[i, 0]) / (n + math.exp(s))
+                lref[i, hq] = math.log(n + math.exp(s))
+    assert_parity(o, lse, ref[None], lref[None], dtype, what=f"g=-800 closed form {dtype}")
+
+
+def test_strong_and_slow_channels():
+    """Half the channels forget at -3 nats per token, half at -0.01: the fast
+    channels trip the diagonal phase's pair-by-pair path while the slow ones
+    carry logits across many tiles."""
+    inp = make_inputs("long_bf16", B=1, T=700, HQ=4, H=2)
+    g = torch.full(inp.g.shape, -0.01, dtype=torch.float64)
+    g[..., 64:] = -3.0
+    inp.g = g.to(inp.g.dtype)
+    o, lse = run_gpu(inp, "channels at -3 and -0.01")
+    o_ref, lse_ref = run_oracle(inp)
+    assert_parity(o, lse, o_ref, lse_ref, "bfloat16", what="channels at -3 and -0.01")
+
+
 @pytest.mark.parametrize("kv", [(64, 64), (64, 128), (128, 64), (128, 128)])
 def test_running_max_raised_in_interior_tiles(kv):
     """A positive scalar gate (g_scalar = +0.04 per token) makes every older key
