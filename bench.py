@@ -479,7 +479,7 @@ def main():
             wall.wall_prefix_scan(d.g_scalar, cu, out=G, workspace=ws_scan)
         if marks:
             marks[1].record()
-        wall.wall_attn_fwd_prepare(d.k, d.v, P, HQ, ws_fwd, cu)
+        wall.wall_attn_fwd_prepare(d.q, d.k, d.v, P, ws_fwd, scale=d.scale, cu_seqlens=cu)
         if marks:
             marks[2].record()
         wall.wall_attn_fwd_run(d.q, d.k, d.v, P, ws_fwd, o, lse, G=G, sink_bias=d.sink_bias,

@@ -65,7 +65,7 @@ def lib() -> ctypes.CDLL:
         L.wall_attn_fwd.argtypes = [P, P, P, E, P, P, P, P, P, I, I, I, I, I, I, F, I, P, I, I,
                                     P, S, P]
         L.wall_attn_fwd.restype = E
-        L.wall_attn_fwd_prepare.argtypes = [P, P, E, P, I, I, I, I, I, I, P, I, P, S, P]
+        L.wall_attn_fwd_prepare.argtypes = [P, P, P, E, P, I, I, I, I, I, I, F, P, I, P, S, P]
         L.wall_attn_fwd_prepare.restype = E
         L.wall_attn_fwd_run.argtypes = [P, P, P, E, P, P, P, P, P, I, I, I, I, I, I, F, I, P, I, I,
                                         P, S, P]
@@ -387,17 +387,19 @@ def wall_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
     return (o, lse) if return_lse else o
 
 
-def wall_attn_fwd_prepare(k: torch.Tensor, v: torch.Tensor, P: torch.Tensor, HQ: int,
-                          workspace: torch.Tensor, cu_seqlens: Optional[torch.Tensor] = None) -> None:
-    """Stage 1 of wall_attn_fwd: build the anchored key cache and value tiles in ``workspace``.
-    All tensors must already be dense and on one device (no copies are made here)."""
-    dev = _on_gpu(k, v, P, workspace, cu_seqlens)
-    B, T, H, K = k.shape
-    V = v.shape[3]
+def wall_attn_fwd_prepare(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, P: torch.Tensor,
+                          workspace: torch.Tensor, scale: Optional[float] = None,
+                          cu_seqlens: Optional[torch.Tensor] = None) -> None:
+    """Stage 1 of wall_attn_fwd: build the anchored key and query tiles and the value
+    tiles in ``workspace``.  All tensors must already be dense and on one device (no
+    copies are made here)."""
+    dev = _on_gpu(q, k, v, P, workspace, cu_seqlens)
+    B, T, HQ, K = q.shape
+    H, V = k.shape[2], v.shape[3]
     nseq = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
-    _check(lib().wall_attn_fwd_prepare(_ptr(k), _ptr(v), _dtype(k), _ptr(P), B, T, HQ, H, K, V,
-                                       _ptr(cu_seqlens), nseq, _ptr(workspace), workspace.numel(),
-                                       _stream(dev)), "wall_attn_fwd_prepare")
+    _check(lib().wall_attn_fwd_prepare(_ptr(q), _ptr(k), _ptr(v), _dtype(k), _ptr(P), B, T, HQ, H, K, V,
+                                       float(K ** -0.5 if scale is None else scale), _ptr(cu_seqlens), nseq,
+                                       _ptr(workspace), workspace.numel(), _stream(dev)), "wall_attn_fwd_prepare")
 
 
 def wall_attn_fwd_run(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, P: torch.Tensor,

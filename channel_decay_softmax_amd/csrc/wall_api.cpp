@@ -115,14 +115,15 @@ wall_status_t check_fwd(wall_dtype_t dtype, const FwdShape &s, const int32_t *cu
     return WALL_OK;
 }
 
-wall_status_t enqueue_prepare(const void *k, const void *v, wall_dtype_t dtype, const float *P,
-                              const FwdShape &s, const int32_t *cu, void *workspace,
+wall_status_t enqueue_prepare(const void *q, const void *k, const void *v, wall_dtype_t dtype, const float *P,
+                              float scale, const FwdShape &s, const int32_t *cu, void *workspace,
                               hipStream_t stream) {
     const FwdLayout L = fwd_layout(esize_of(dtype), s.B, s.T, s.HQ, s.H, s.K, s.V, s.nseq);
     char *ws = static_cast<char *>(workspace);
     SegInfo *seg = reinterpret_cast<SegInfo *>(ws + L.off_seg);
-    PrepArgs pa{k, v, P, seg, cu, reinterpret_cast<float *>(ws + L.off_anchor),
-                reinterpret_cast<uint32_t *>(ws + L.off_rec), ws + L.off_kt, ws + L.off_vt,
+    PrepArgs pa{q, k, v, P, seg, cu, reinterpret_cast<float *>(ws + L.off_anchor),
+                reinterpret_cast<uint32_t *>(ws + L.off_rec), ws + L.off_kt, ws + L.off_vt, ws + L.off_kd,
+                ws + L.off_qd, reinterpret_cast<uint32_t *>(ws + L.off_drec), scale * LOG2E,
                 L.nseg, L.tiles, s.HQ, s.H, s.K, s.V, s.T};
     return launched(launch_prep(pa, dtype == WALL_BF16, stream));
 }
@@ -142,6 +143,9 @@ wall_status_t enqueue_run(const void *q, const void *k, const void *v, wall_dtyp
     fa.sink = sink_bias;
     fa.kt = ws + L.off_kt;
     fa.vt = ws + L.off_vt;
+    fa.kd = ws + L.off_kd;
+    fa.qd = ws + L.off_qd;
+    fa.drec = reinterpret_cast<const uint32_t *>(ws + L.off_drec);
     fa.anchor = reinterpret_cast<const float *>(ws + L.off_anchor);
     fa.rec = reinterpret_cast<const uint32_t *>(ws + L.off_rec);
     fa.seg = reinterpret_cast<const SegInfo *>(ws + L.off_seg);
@@ -160,20 +164,19 @@ wall_status_t enqueue_run(const void *q, const void *k, const void *v, wall_dtyp
 
 }  // namespace
 
-wall_status_t wall_attn_fwd_prepare(const void *k, const void *v, wall_dtype_t dtype,
-                                    const float *P, int64_t B, int64_t T, int64_t HQ, int64_t H,
-                                    int64_t K, int64_t V, const int32_t *cu_seqlens,
-                                    int64_t num_seqs, void *workspace, size_t workspace_bytes,
-                                    hipStream_t stream) {
-    if (!k || !v || !P) return WALL_ERR_INVALID_ARG;
+wall_status_t wall_attn_fwd_prepare(const void *q, const void *k, const void *v, wall_dtype_t dtype,
+                                    const float *P, int64_t B, int64_t T, int64_t HQ, int64_t H, int64_t K,
+                                    int64_t V, float scale, const int32_t *cu_seqlens, int64_t num_seqs,
+                                    void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!q || !k || !v || !P) return WALL_ERR_INVALID_ARG;
     const FwdShape s{B, T, HQ, H, K, V, cu_seqlens ? num_seqs : 0, T};
     // max_seqlen plays no part in the preparation: pass T to the shared checks
     const wall_status_t st = check_fwd(dtype, s, cu_seqlens, num_seqs, T, workspace, workspace_bytes);
     if (st != WALL_OK) return st;
-    const void *ptrs[] = {k, v, P};
+    const void *ptrs[] = {q, k, v, P};
     for (const void *p : ptrs)
         if (!aligned(p, 16)) return WALL_ERR_INVALID_ARG;
-    return enqueue_prepare(k, v, dtype, P, s, cu_seqlens, workspace, stream);
+    return enqueue_prepare(q, k, v, dtype, P, scale, s, cu_seqlens, workspace, stream);
 }
 
 wall_status_t wall_attn_fwd_run(const void *q, const void *k, const void *v, wall_dtype_t dtype,
@@ -207,7 +210,7 @@ wall_status_t wall_attn_fwd(const void *q, const void *k, const void *v, wall_dt
     const void *ptrs[] = {q, k, v, P, o, G, sink_bias, lse};
     for (const void *p : ptrs)
         if (p && !aligned(p, 16)) return WALL_ERR_INVALID_ARG;
-    const wall_status_t sp = enqueue_prepare(k, v, dtype, P, s, cu_seqlens, workspace, stream);
+    const wall_status_t sp = enqueue_prepare(q, k, v, dtype, P, scale, s, cu_seqlens, workspace, stream);
     if (sp != WALL_OK) return sp;
     return enqueue_run(q, k, v, dtype, P, G, sink_bias, o, lse, s, scale, window_size, workspace, stream);
 }

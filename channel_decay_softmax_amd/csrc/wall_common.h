@@ -56,13 +56,32 @@ inline __host__ __device__ size_t align_up(size_t x, size_t a) { return (x + a -
 // All zero for a sequence's first tile.
 constexpr int REC_WORDS = 256;
 constexpr int REC_GROW = 128;
+// Word REC_DIAG: bit b set when some row of the tile's 32-row block b lies more
+// than DIAG_SPREAD log2 units from the block's anchor (its last row's floored
+// prefix) on some channel: that block's own 32 x 32 pairs are then formed pair
+// by pair.  Within it every factor of the block's own pairs stays inside
+// 2^+-DIAG_SPREAD, and a term lost to an underflowing factor is below
+// 2^(DIAG_SPREAD - 126).
+constexpr int REC_DIAG = 129;
+constexpr float DIAG_SPREAD = 100.0f;
+// Rows of one diagonal-phase block (one MFMA n-block of queries).
+constexpr int DBLK = 32;
+// Per (tile, query head) diagonal-phase carry records, DREC_N records of
+// K/2 words in the tile record's format (u16 exponent decrements per channel,
+// 128 * shift clamped to [0, 255*128]): record b (b < TILE/DBLK) moves a query
+// from block b's anchor to the previous tile's anchor; record TILE/DBLK + b
+// moves it from block b+1's anchor to block b's.  Bit 8 + r of the tile
+// record's word REC_DIAG is set when some channel's shift of record r is
+// negative (a prefix that grows; the kernel then rebuilds q~ from q and P).
+constexpr int DREC_N = 2 * (TILE / DBLK);
 
 // Forward workspace: segment table | anchors | carry records | rescaled key
-// tiles | transposed value tiles (the last four for bf16 inputs only).
+// tiles | transposed value tiles | block-anchored key and query tiles | the
+// diagonal phase's carry records (all but the table for bf16 inputs only).
 struct FwdLayout {
     int64_t nseg;        // sequences (num_seqs with packing, else B)
     int64_t tiles;       // upper bound on sum_s ceil(len_s / TILE)
-    size_t off_seg, off_anchor, off_rec, off_kt, off_vt, total;
+    size_t off_seg, off_anchor, off_rec, off_kt, off_vt, off_kd, off_qd, off_drec, total;
 };
 
 inline FwdLayout fwd_layout(int64_t esize, int64_t B, int64_t T, int64_t HQ, int64_t H,
@@ -82,6 +101,12 @@ inline FwdLayout fwd_layout(int64_t esize, int64_t B, int64_t T, int64_t HQ, int
     o = align_up(o + (size_t)esize * (size_t)(L.tiles * HQ * TILE * K), 256);
     L.off_vt = o;
     o = align_up(o + (size_t)esize * (size_t)(L.tiles * H * V * TILE), 256);
+    L.off_kd = o;
+    o = align_up(o + (size_t)esize * (size_t)(L.tiles * HQ * TILE * K), 256);
+    L.off_qd = o;
+    o = align_up(o + (size_t)esize * (size_t)(L.tiles * HQ * TILE * K), 256);
+    L.off_drec = o;
+    o = align_up(o + sizeof(uint32_t) * (size_t)(L.tiles * HQ * DREC_N * (K / 2)), 256);
     L.total = o;
     return L;
 }
@@ -123,6 +148,7 @@ hipError_t launch_scan_excl(const float *x, void *out, bool out_bf16, int64_t B,
                             const int32_t *cu, int64_t nseq, float scale, void *ws, hipStream_t st);
 
 struct PrepArgs {
+    const void *q;     // [rows, HQ, K]
     const void *k;     // [rows, H, K]
     const void *v;     // [rows, H, V]
     const float *P;    // [rows, HQ, K]
@@ -130,8 +156,12 @@ struct PrepArgs {
     const int32_t *cu; // [nseg + 1] sequence starts, or null for B sequences of T rows
     float *anchor;     // [tiles, HQ, K] floored prefix of each tile's last row
     uint32_t *rec;     // [tiles, HQ, REC_WORDS]
-    void *kt;          // [tiles, HQ, TILE, K] bf16
+    void *kt;          // [tiles, HQ, TILE, K] bf16, keys at the tile's anchor
     void *vt;          // [tiles, H, V, TILE] bf16
+    void *kd;          // [tiles, HQ, TILE, K] bf16, keys at their 32-row block's anchor
+    void *qd;          // [tiles, HQ, TILE, K] bf16, queries (times qscale) at their block's anchor
+    uint32_t *drec;    // [tiles, HQ, DREC_N, K / 2] diagonal-phase carry records
+    float qscale;      // scale * log2(e)
     int64_t nseg, tiles, HQ, H, K, V, T;
 };
 // bf16: the sequence table, anchors, carry records, key and value tiles;
@@ -147,6 +177,9 @@ struct FwdArgs {
     const float *sink;      // [HQ] or null
     const void *kt;         // [tiles, HQ, TILE, K] (bf16 path)
     const void *vt;         // [tiles, H, V, TILE] (bf16 path)
+    const void *kd;         // [tiles, HQ, TILE, K] (bf16 path)
+    const void *qd;         // [tiles, HQ, TILE, K] (bf16 path)
+    const uint32_t *drec;   // [tiles, HQ, DREC_N, K / 2] (bf16 path)
     const float *anchor;    // [tiles, HQ, K] (bf16 path)
     const uint32_t *rec;    // [tiles, HQ, REC_WORDS]
     const SegInfo *seg;     // [nseg]

@@ -17,20 +17,25 @@
 //     between the key and the query, so for a prefix that falls both factors
 //     are at most about 1, and a factor that underflows belongs to a term
 //     that is itself below 2^-125;
-//   * keys of the wave's own tile (the diagonal phase, below) are read from
-//     the raw keys at anchors the wave chooses for its own 32 rows.
+//   * keys of the wave's own tile (the diagonal phase, below) are read at the
+//     anchors of 32-row blocks.
 //
-// Diagonal phase (per wave, no LDS, no barriers).  The keys of the wave's
-// tile up to its last query, 32 at a time, against the floored prefix M of
-// the middle of the wave's rows: q~ and k~ are formed from q, k and P with
-// one exp2 per element, S^T = k~ q~^T on the matrix cores, then an online
-// softmax and O^T += v^T p^T (values from the prepared transposed tiles).
-// While every row of the wave lies within 100 log2 units of M, every factor
-// stays within 2^+-100 and the lost terms are below 2^-26.  Beyond that the
-// keys before the wave's rows are read at the floored prefix of the row just
-// before the wave (between every such pair), and the 32 x 32 block of the
-// wave's own rows is formed pair by pair in float32 without any anchor,
-// scale * sum_n q_in k_jn exp2(P_in - P_jn).
+// Diagonal phase (after the pipeline, per wave over its own tile).  The
+// preparation step stores every tile again with each 32-row block anchored at
+// its own last row A_b: keys k * exp2(A_b - P) and queries q * scale*log2e *
+// exp2(P - A_b).  The block's keys are staged into the tile's key buffer; a
+// wave takes its own rows' q~ at its block's anchor, its own 32 x 32 block at
+// that anchor, then each earlier block b at A_b (a row between those keys and
+// its queries: exact at any gate strength), lowering q~'s exponents by
+// A_b - A_{b+1} from block to block; an online softmax continues the
+// pipeline's, and O^T += v^T p^T with the tile's values.  While every row of
+// the wave's block lies within DIAG_SPREAD = 100 log2 units of A_b, every
+// factor of its own pairs stays within 2^+-100 and a lost term is below 2^-26;
+// beyond that (flagged by the preparation step) the wave forms its own 32 x 32
+// block pair by pair in float32 without any anchor,
+// scale * sum_n q_in k_jn exp2(P_in - P_jn), and reads the earlier blocks with
+// q~ rebuilt at the row just before its own.  The same prepared q~, lowered
+// to the previous tile's anchors, starts the pipeline.
 //
 // Pipeline (the tiles before the wave's own).  Per wave, keys are walked from
 // tile 2u (2u - 1 when the block has a single tile) down to the first tile
@@ -38,8 +43,8 @@
 // tile at or after a wave's own tile is masked whole for that wave:
 //
 //   q~  the wave's bf16 queries anchored at key tile c, q * scale*log2e *
-//       exp2(P_i - Rc).  Built from q and P at the tile before the wave's
-//       own, then carried from tile c to tile c-1 by lowering each bf16
+//       exp2(P_i - Rc).  The prepared block-anchored q~ lowered to the tile
+//       before the wave's own, then carried from tile c to tile c-1 by lowering each bf16
 //       exponent field by the integer R[c-1] - R[c] (>= 0 while the prefix
 //       does not grow) with a saturating packed subtract: exact, and a value
 //       that would leave the bf16 range becomes 0 and, the decay only
@@ -73,8 +78,7 @@
 // into the buffer just released; each buffer is an LDS variable of its own
 // so the compiler does not wait on the loads either.  A key buffer also
 // carries the tile's carry record (from the preparation step) and its keys'
-// scalar-gate prefix.  The first tiles' copies are issued before the
-// diagonal phase and land while it runs.
+// scalar-gate prefix.
 //
 // The key rows fed to the S^T MFMA are permuted (bits 2 and 3 of the row
 // index swapped) so each lane's output registers come out as runs of 8
@@ -107,11 +111,7 @@ constexpr int NSB = TILE / SB;  // sub-blocks per tile (pipeline steps per tile)
 // a query's sum of the 32 p of one sub-block above this raises m (so every p
 // stays at most 2^12 before it is rounded to bf16 and summed in fp32)
 constexpr float PSUM_LIM = 4096.0f;
-// Largest distance (log2 units) of a wave's rows' prefix from the diagonal
-// phase's middle-row anchor: within it every factor stays inside 2^+-100 and
-// a term lost to an underflowing factor is below 2^(100 - 126).  Beyond it
-// the wave's own 32 x 32 block is formed pair by pair.
-constexpr float DIAG_SPREAD = 100.0f;
+
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -787,14 +787,37 @@ struct Kernel {
         }
     }
     // ---- the diagonal phase: keys of the wave's own tile up to its last query
-    // q~ of the lane's query at the anchors floor(P[Pa row]) (0 for a row past
-    // the sequence); dev: the largest |P_i - R| over the lane's channels.
-    __device__ __forceinline__ void diag_q(const float *Pa, QOp<K> &qo, float &dev) const {
+    //
+    // The preparation step stored every row of the tile again with each 32-row
+    // block anchored at its own last row: the keys (staged into the tile's key
+    // buffer) and the queries (times scale*log2e).  A wave reads its own rows'
+    // q~ at its block's anchor, its own block's keys at the same anchor, and
+    // each earlier block's keys at that block's anchor, between them and the
+    // wave's queries, carrying q~ from block to block.
+    __device__ __forceinline__ const __bf16 *kd_tile(int c) const {
+        return static_cast<const __bf16 *>(a.kd) + ((int64_t)(sg.tile_base + c) * a.HQ + hq) * TILE * K;
+    }
+    __device__ __forceinline__ const uint32_t *drec_tile(int c) const {
+        return a.drec + ((int64_t)(sg.tile_base + c) * a.HQ + hq) * DREC_N * (K / 2);
+    }
+    __device__ __forceinline__ uint32_t diag_flags(int c) const {
+        return a.rec[((int64_t)(sg.tile_base + c) * a.HQ + hq) * REC_WORDS + REC_DIAG];
+    }
+    // the prepared q~ of the lane's query (tile c), at its block's anchor
+    __device__ __forceinline__ void load_qd(int c, QOp<K> &qd) const {
+        const __bf16 *src = static_cast<const __bf16 *>(a.qd) +
+                            (((int64_t)(sg.tile_base + c) * a.HQ + hq) * TILE + (wv.qrow - TILE * c)) * K;
+#pragma unroll
+        for (int s8 = 0; s8 < KS; ++s8) qd[s8] = *reinterpret_cast<const bf16x8 *>(src + 16 * s8 + 8 * wv.hl);
+    }
+    // q~ of the lane's query at the anchors floor(P[Pa row]) from q and P (0 for
+    // a row past the sequence).  A rare path: one channel step in flight at a
+    // time, so that it adds no register pressure.
+    __device__ void diag_q(const float *Pa, QOp<K> &qo) const {
         const bool qv = wv.qrow < sg.len;
         const int64_t tok = (int64_t)sg.start + (qv ? wv.qrow : 0);
         const __bf16 *qg = static_cast<const __bf16 *>(a.q) + (tok * a.HQ + hq) * K;
         const float *pg = a.P + (tok * a.HQ + hq) * K;
-        float d = 0.f;
 #pragma unroll
         for (int s8 = 0; s8 < KS; ++s8) {
             const int ch0 = 16 * s8 + 8 * wv.hl;
@@ -803,37 +826,40 @@ struct Kernel {
             const f32x8 rv = *reinterpret_cast<const f32x8 *>(Pa + ch0);
             f32x8 qh;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float x = pv8[e] - floorf(rv[e]);
-                d = fmaxf(d, fabsf(x));
-                qh[e] = qv ? qv8[e] * a.qscale * exp2f(fminf(fmaxf(x, EXP2_LO), EXP2_HI)) : 0.f;
-            }
+            for (int e = 0; e < 8; ++e)
+                qh[e] = qv ? qv8[e] * a.qscale * exp2f(fminf(fmaxf(pv8[e] - floorf(rv[e]), EXP2_LO), EXP2_HI)) : 0.f;
             qo[s8] = __builtin_convertvector(qh, bf16x8);
-            __builtin_amdgcn_sched_barrier(0);  // one channel step's loads in flight at a time
+            __builtin_amdgcn_sched_barrier(0);
         }
-        dev = qv ? d : 0.f;
     }
-    // S^T of the 32 keys from kb against qa, both anchored at floor(P[Pa row]):
-    // the lane forms k~ of key row kb + key_perm(lane) (rows past the sequence
-    // read its last row; they are masked later).
-    __device__ __forceinline__ f32x16 diag_scores(int kb, const float *Pa, const QOp<K> &qa) const {
-        const int kr = min(kb + key_perm(lane & 31), sg.len - 1);
-        const int64_t tok = (int64_t)sg.start + kr;
-        const __bf16 *kg = static_cast<const __bf16 *>(a.k) + (tok * a.H + h) * K;
-        const float *pg = a.P + (tok * a.HQ + hq) * K;
-        f32x16 S = {};
+    // q~ lowered by a carry record (the u16 exponent decrements of the lane's
+    // channels, as the pipeline's tile records): exact, or 0 below the bf16 range.
+    __device__ __forceinline__ void carry_rec(QOp<K> &qd, const uint32_t *rec) const {
 #pragma unroll
         for (int s8 = 0; s8 < KS; ++s8) {
-            const int ch0 = 16 * s8 + 8 * wv.hl;
-            const f32x8 kv8 = __builtin_convertvector(*reinterpret_cast<const bf16x8 *>(kg + ch0), f32x8);
-            const f32x8 pv8 = *reinterpret_cast<const f32x8 *>(pg + ch0);
-            const f32x8 rv = *reinterpret_cast<const f32x8 *>(Pa + ch0);
-            f32x8 kh;
+            const uint4 d = *reinterpret_cast<const uint4 *>(rec + 8 * s8 + 4 * wv.hl);
+            const uint32_t dv[4] = {d.x, d.y, d.z, d.w};
+            const uint4 x4 = __builtin_bit_cast(uint4, qd[s8]);
+            const uint32_t xv[4] = {x4.x, x4.y, x4.z, x4.w};
+            uint32_t out[4];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) kh[e] = kv8[e] * exp2f(fminf(fmaxf(floorf(rv[e]) - pv8[e], EXP2_LO), EXP2_HI));
-            S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_convertvector(kh, bf16x8), qa[s8], S, 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);  // one channel step's loads in flight at a time
+            for (int e = 0; e < 4; ++e) {
+                const u16x2 mag = __builtin_bit_cast(u16x2, xv[e] & 0x7fff7fffu);
+                const u16x2 rr = __builtin_elementwise_sub_sat(mag, __builtin_bit_cast(u16x2, dv[e]));
+                out[e] = (xv[e] & 0x80008000u) | __builtin_bit_cast(uint32_t, rr);
+            }
+            qd[s8] = __builtin_bit_cast(bf16x8, uint4{out[0], out[1], out[2], out[3]});
         }
+    }
+    // S^T of the keys of 32-row block b of the tile in kd against q~ (LDS
+    // reads in the pipeline's operand order).
+    __device__ __forceinline__ f32x16 diag_scores(const char *kd, int b, const QOp<K> &qd) const {
+        const char *kb = kd + wv.kbase + b * (SB / KL::NBLK) * (2 * K);
+        f32x16 S = {};
+#pragma unroll
+        for (int s8 = 0; s8 < KS; ++s8)
+            S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8 *>(kb + 32 * s8), qd[s8], S, 0,
+                                                        0, 0);
         return S;
     }
     // The 32 x 32 block of the wave's own rows (keys from kb = the wave's first
@@ -870,20 +896,20 @@ struct Kernel {
         }
         return S;
     }
-    // Masks, the online softmax of the 32 keys from kb (scores not relative to
-    // m) and O^T += v^T p^T with the values of the wave's tile (vtile, keys
-    // from kt0).
-    __device__ __forceinline__ void diag_block(f32x16 S, int kb, const __bf16 *vtile, int kt0) {
+    // Masks, the online softmax of the 32 keys of block b (scores not relative
+    // to m) and O^T += v^T p^T with the values of the tile in vd; G of the
+    // tile's keys in kd.
+    __device__ __forceinline__ void diag_block(f32x16 S, int kt0, int b, const char *kd, const char *vd) {
         const int qrow = wv.qrow, len = sg.len;
         const bool qv = qrow < len;
-        const int kb0 = kb + 8 * wv.hl;
+        const int kb0 = kt0 + SB * b + 8 * wv.hl;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int j = kb0 + 16 * (r / 8) + (r % 8);
             bool vis = qv && j <= qrow;
             if (a.window > 0) vis = vis && qrow - j < a.window;
             float x = S[r];
-            if (HAS_G) x -= a.G[((int64_t)sg.start + min(j, len - 1)) * a.HQ + hq];
+            if (HAS_G) x -= reinterpret_cast<const float *>(kd + LY::GK_OFF)[j - kt0];
             S[r] = vis ? x : -__builtin_inff();
         }
         const float m1 = max3(max3(S[0], S[1], S[2]), max3(S[3], S[4], S[5]), max3(S[6], S[7], S[8]));
@@ -903,55 +929,56 @@ struct Kernel {
             }
         wv.l = wv.l * al + ps;
         wv.m = mn;
-        const int col = lane & 31;
+        const char *vb = vd + wv.vbase;
 #pragma unroll
         for (int vt = 0; vt < VT; ++vt) {
             wv.O[vt] *= al;
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                const bf16x8 x = *reinterpret_cast<const bf16x8 *>(vtile + (32 * vt + col) * TILE + (kb - kt0) + 16 * t +
-                                                                    8 * wv.hl);
+                const bf16x8 x =
+                    *reinterpret_cast<const bf16x8 *>(vb + vt * (32 / VL::NBLK) * (2 * TILE) + 32 * (2 * b + t));
                 wv.O[vt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, W::as_bf16(pw[t]), wv.O[vt], 0, 0, 0);
             }
         }
     }
-    // The whole diagonal phase of the wave (queries q0w.., tile qt): leaves O,
-    // m (from -FLT_MAX; the lane's own key is always visible) and l.
-    __device__ void diag_phase(int qt, int q0w) {
+    // The walk of the wave (queries q0w.., tile qt, the tile's block-anchored
+    // keys in kd and its values in vd, flags the tile's REC_DIAG word, qd the
+    // wave's prepared q~) over its own tile, continuing the online softmax of
+    // the pipeline (a lane that has seen no visible key yet restarts its max).
+    __device__ void diag_walk(int qt, int q0w, uint32_t flags, const char *kd, const char *vd, QOp<K> &qd) {
+        constexpr int NB = TILE / DBLK;
         const int wq = (q0w - TILE * qt) / WQ;  // the wave's 32-row block within its tile
         const int kt0 = TILE * qt;
-        const int last = min(q0w + WQ - 1, sg.len - 1);
-        const float *Pm = a.P + ((int64_t)(sg.start + ((q0w + last) >> 1)) * a.HQ + hq) * K;
-        const __bf16 *vtile = static_cast<const __bf16 *>(vt_tile(qt));
+        const bool flagged = (flags >> wq) & 1u;
+        const uint32_t *drec = drec_tile(qt);
         // the lowest 32-key block any query of the wave sees
         int b_lo = 0;
         if (a.window > 0) {
             const int kmin = q0w - a.window + 1;
             if (kmin > kt0) b_lo = (kmin - kt0) / SB;
         }
-#pragma unroll
-        for (int vt = 0; vt < VT; ++vt) wv.O[vt] = f32x16{};
-        wv.m = -FLT_MAX;
-        wv.l = 0.f;
-        QOp<K> qa;
-        float dev;
-        diag_q(Pm, qa, dev);
-        if (!__any(dev > DIAG_SPREAD)) {
-            for (int b = wq; b >= b_lo; --b) {
-                const int kb = kt0 + SB * b;
-                diag_block(diag_scores(kb, Pm, qa), kb, vtile, kt0);
-            }
+        if (wv.lim < 0.f) wv.m = -FLT_MAX;
+        if (!flagged) {
+            diag_block(diag_scores(kd, wq, qd), kt0, wq, kd, vd);
         } else {
-            diag_block(exact_scores(q0w), q0w, vtile, kt0);
-            if (wq - 1 >= b_lo) {
-                // the keys before the wave's rows, at the row just before them
-                const float *Pb = a.P + ((int64_t)(sg.start + q0w - 1) * a.HQ + hq) * K;
-                diag_q(Pb, qa, dev);
-                for (int b = wq - 1; b >= b_lo; --b) {
-                    const int kb = kt0 + SB * b;
-                    diag_block(diag_scores(kb, Pb, qa), kb, vtile, kt0);
-                }
+            // some row of the wave lies more than DIAG_SPREAD from its anchor: its
+            // own block pair by pair, and q~ for the earlier blocks at the anchor
+            // of the row just before the wave (block wq - 1's)
+            diag_block(exact_scores(q0w), kt0, wq, kd, vd);
+            if (wq > b_lo) diag_q(a.P + ((int64_t)(sg.start + q0w - 1) * a.HQ + hq) * K, qd);
+        }
+        // block b < wq is read with q~ at block b's anchor (its last row, between
+        // its keys and the wave's queries); `cur` is the block whose anchor q~ is at
+        int cur = flagged ? wq - 1 : wq;
+        for (int b = wq - 1; b >= b_lo; --b) {
+            if (b != cur) {
+                if ((flags >> (8 + NB + b)) & 1u)
+                    diag_q(a.P + ((int64_t)(sg.start + kt0 + SB * b + SB - 1) * a.HQ + hq) * K, qd);
+                else
+                    carry_rec(qd, drec + (NB + b) * (K / 2));
+                cur = b;
             }
+            diag_block(diag_scores(kd, b, qd), kt0, b, kd, vd);
         }
     }
 
@@ -1055,39 +1082,38 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
         float g_i = 0.f;
         if (HAS_G && wave_on && qrow < sg.len) g_i = a.G[((int64_t)sg.start + qrow) * HQ + hq];
 
-        // ---- prologue: tile c_hi into buffers 0 and the keys of tile c_hi - 1
-        // into key buffer 1, copied while each wave works through its own tile
+        // ---- the pipeline's prologue: q~ at the anchors of the tile before the
+        // wave's own; tile c_hi into buffers 0, the keys of tile c_hi - 1 into key
+        // buffer 1
         __syncthreads();  // the previous block's last reads of every buffer are done
         if (run_pipe) {
             kr.issue_k(k0, c_hi);
             kr.issue_v(v0, c_hi);
             kr.issue_k(k1, max(c_hi - 1, c_lo));
         }
-        if (wave_on) {
-            kr.diag_phase(qt_w, q0w);
-            // q~ for the pipeline at the anchors of the tile before the wave's own
-            if (qt_w > 0 && run_pipe) load_qop<K, true>(a, sg, hq, qt_w - 1, qrow, hl, wv.qop);
+        if (wave_on && qt_w > 0 && run_pipe) {
+            // the prepared q~ moved from the wave's block anchor to the previous
+            // tile's (an exact exponent decrement); from q and P when the block
+            // needs its pair-by-pair path or some channel's prefix grows
+            const int wq = (q0w - TILE * qt_w) / WQ;
+            const uint32_t fl = kr.diag_flags(qt_w);
+            if (((fl >> wq) | (fl >> (8 + wq))) & 1u) {
+                load_qop<K, false>(a, sg, hq, qt_w - 1, qrow, hl, wv.qop);
+            } else {
+                kr.load_qd(qt_w, wv.qop);
+                kr.carry_rec(wv.qop, kr.drec_tile(qt_w) + wq * (K / 2));
+            }
         } else {
-#pragma unroll
-            for (int vt = 0; vt < VT; ++vt) wv.O[vt] = f32x16{};
-            wv.m = 0.f;
-            wv.l = 0.f;
-        }
-        if (!wave_on || qt_w == 0 || !run_pipe) {
 #pragma unroll
             for (int s8 = 0; s8 < KS; ++s8) wv.qop[s8] = bf16x8{};
         }
-        {
-            // a lane whose row lies past the sequence restarts at m = 0 and raises
-            // m at its first visible key (its output is never stored); a wave
-            // with no rows never raises
-            const bool qv = wave_on && qrow < sg.len;
-            wv.m = qv ? wv.m : 0.f;
-            wv.lim = !wave_on ? __builtin_inff() : qv ? PSUM_LIM : -1.f;
-        }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) wv.negm[r] = -wv.m;
+        for (int vt = 0; vt < VT; ++vt) wv.O[vt] = f32x16{};
+        wv.negm = f32x16{};
+        wv.m = 0.f;
+        wv.l = 0.f;
         wv.alpha = 1.f;
+        wv.lim = wave_on ? -1.f : __builtin_inff();  // a wave with no rows never raises
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -1126,7 +1152,6 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
                 if (--c < c_lo) break;
             }
             // the loads issued past tile c_lo land before the buffers are reused
-            // (or the workgroup ends)
             wait_vm<0>();
             // the last sub-block's PV products (sub-block 0 of tile c_lo, p in Pw[0])
             {
@@ -1140,8 +1165,35 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
                         wv.O[vt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, W::as_bf16(wv.Pw[0][t]), wv.O[vt], 0, 0, 0);
                     }
             }
-            // a raise owed by the last step was applied by its RESC
         }
+
+        // ---- the diagonal phase: the block's two tiles, waves 0-3 in tile 2u
+        // (key buffer k0, values v0), waves 4-7 in tile 2u+1 (k1, v1)
+        __syncthreads();  // every wave is past the pipeline's buffers
+        const bool second = 2 * u + 1 < ntiles;
+        char *kd = w < NW / 2 ? k0 : k1;
+        char *vd = w < NW / 2 ? v0 : v1;
+        load_tile<KL>(k0, kr.kd_tile(2 * u), kr.klane, w);
+        kr.issue_v(v0, 2 * u);
+        if (second) {
+            load_tile<KL>(k1, kr.kd_tile(2 * u + 1), kr.klane, w);
+            kr.issue_v(v1, 2 * u + 1);
+        }
+        if (HAS_G) {
+            const int r0 = BQ * u;
+            load_gk(k0 + LY::GK_OFF, a.G + ((int64_t)sg.start + r0) * HQ + hq, HQ, sg.len - r0, w, lane);
+            if (second)
+                load_gk(k1 + LY::GK_OFF, a.G + ((int64_t)sg.start + r0 + TILE) * HQ + hq, HQ, sg.len - r0 - TILE, w,
+                        lane);
+        }
+        uint32_t dflags = 0u;
+        if (wave_on) {
+            kr.load_qd(qt_w, wv.qop);
+            dflags = kr.diag_flags(qt_w);
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (wave_on) kr.diag_walk(qt_w, q0w, dflags, kd, vd, wv.qop);
 
         // ---- epilogue: sink, normalisation, o and lse.  Every wave is past its
         // last LDS read (and every copy has landed) before o is staged in the

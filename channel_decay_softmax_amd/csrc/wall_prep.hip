@@ -6,9 +6,10 @@
 //    per sequence: start row, length, index of its first 128-row tile in the
 //    tiled workspace; tiles never straddle two sequences, so a tile's rows
 //    always share one prefix P); block (0, 0) also stores the table.
-// 2. keys, per (tile, query head): the anchors R[n] = floor(P[a][n]) at the
-//    tile's last row a, the carry record that moves a query from this tile's
-//    anchors to the previous tile's, and the decay-rescaled keys
+// 2. keys and queries, per (tile, query head): the anchors R[n] =
+//    floor(P[a][n]) at the tile's last row a, the carry record that moves a
+//    query from this tile's anchors to the previous tile's, and the
+//    decay-rescaled keys
 //        k~[j][n] = k[j][n] * exp2(R[n] - P[j][n]),
 //    zero-padded to 128 rows.  This is the blog's per-tile anchor split
 //    ("Fast training and inference", per-tile anchors:
@@ -19,8 +20,11 @@
 //    keys only from queries after the tile, and the last row lies between
 //    every such pair: for a prefix that falls, both factors are at most
 //    about 1, so a factor that underflows belongs to a negligible term, at
-//    any gate strength.  (Keys of a query's own tile are handled inside the
-//    fused kernel from the raw keys.)
+//    any gate strength.  For the fused kernel's diagonal phase (the keys of a
+//    query's own tile) the same rows again, each 32-row block anchored at its
+//    own last row A: k[j] * exp2(A - P[j]) and q[j] * scale*log2e *
+//    exp2(P[j] - A), the carry records between those anchors, and per tile a
+//    mask of the blocks whose rows lie more than DIAG_SPREAD from their anchor.
 // 3. values, per (tile, kv head): v transposed to [V][128] for the bf16 MFMA
 //    kernel (its PV operand reads keys contiguously, each thread transposing
 //    an 8 x 8 block in registers); zero-padded.
@@ -90,61 +94,124 @@ struct Vec8<__bf16> {
     }
 };
 
-template <typename T, int K>
+template <int K>
 __device__ inline void key_tile(const PrepArgs &a, int tile, int hq, const SegInfo &sg) {
     constexpr int CPR = K / 8;          // 8-channel chunks per row
     constexpr int RPP = 256 / CPR;      // rows per pass
     constexpr int NPASS = TILE / RPP;
+    constexpr int NB = TILE / DBLK;     // 32-row blocks per tile
+    __shared__ uint32_t sflag;
     const int c = tile - sg.tile_base;
     const int h = hq / (int)(a.HQ / a.H);
     const int c8 = threadIdx.x % CPR, r0 = threadIdx.x / CPR;
+    const int64_t HQ = a.HQ;
+    if (threadIdx.x == 0) sflag = 0u;
+    __syncthreads();
+    // anchors: the tile's last row (keys read from later tiles) and each
+    // 32-row block's last row (the fused kernel's diagonal phase)
     const int arow = min(c * TILE + TILE - 1, sg.len - 1);
-    const float *Pa = a.P + ((int64_t)(sg.start + arow) * a.HQ + hq) * K + c8 * 8;
-    f32x8 R;
+    const float *Pa = a.P + ((int64_t)(sg.start + arow) * HQ + hq) * K + c8 * 8;
+    f32x8 R, A[NB];
     for (int e = 0; e < 8; ++e) R[e] = floorf(Pa[e]);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        const int brow = min(c * TILE + DBLK * b + DBLK - 1, sg.len - 1);
+        const f32x8 pb = *reinterpret_cast<const f32x8 *>(a.P + ((int64_t)(sg.start + brow) * HQ + hq) * K + c8 * 8);
+        for (int e = 0; e < 8; ++e) A[b][e] = floorf(pb[e]);
+    }
     if (r0 == 0) {
-        float *ap = a.anchor + ((int64_t)tile * a.HQ + hq) * K + c8 * 8;
+        float *ap = a.anchor + ((int64_t)tile * HQ + hq) * K + c8 * 8;
         *reinterpret_cast<f32x8 *>(ap) = R;
-        // carry record: the shift from this tile's anchors to the previous tile's
+        // carry records: the shift from this tile's anchors to the previous
+        // tile's, and the diagonal phase's (each block's anchor to the previous
+        // tile's, block b+1's to block b's)
+        auto shift = [](float d) { return (uint32_t)fminf(fmaxf(d, 0.f), 255.f) * 128u; };
+        f32x8 Lp = R;  // the previous tile's anchors (none for a sequence's first tile)
+        if (c > 0) {
+            const float *Pp = a.P + ((int64_t)(sg.start + c * TILE - 1) * HQ + hq) * K + c8 * 8;
+            for (int e = 0; e < 8; ++e) Lp[e] = floorf(Pp[e]);
+        }
         bool up = false;
-        uint32_t *rec = a.rec + ((int64_t)tile * a.HQ + hq) * REC_WORDS;
+        uint32_t dgrow = 0;
+        uint32_t *rec = a.rec + ((int64_t)tile * HQ + hq) * REC_WORDS;
+        uint32_t *drec = a.drec + ((int64_t)tile * HQ + hq) * DREC_N * (K / 2);
         for (int e = 0; e < 8; e += 2) {
+            const int wd = (c8 * 8 + e) / 2;
             uint32_t w = 0;
             if (c > 0) {
-                const int prow = c * TILE - 1;  // anchor row of tile c-1: its last row
-                const float *Pp = a.P + ((int64_t)(sg.start + prow) * a.HQ + hq) * K + c8 * 8;
-                const float d0 = floorf(Pp[e]) - R[e], d1 = floorf(Pp[e + 1]) - R[e + 1];
+                const float d0 = Lp[e] - R[e], d1 = Lp[e + 1] - R[e + 1];
                 up = up || d0 < 0.f || d1 < 0.f;
-                const uint32_t s0 = (uint32_t)fminf(fmaxf(d0, 0.f), 255.f) * 128u;
-                const uint32_t s1 = (uint32_t)fminf(fmaxf(d1, 0.f), 255.f) * 128u;
-                w = s0 | (s1 << 16);
+                w = shift(d0) | (shift(d1) << 16);
             }
-            rec[(c8 * 8 + e) / 2] = w;
+            rec[wd] = w;
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                uint32_t x = 0;
+                if (c > 0) {
+                    const float d0 = Lp[e] - A[b][e], d1 = Lp[e + 1] - A[b][e + 1];
+                    if (d0 < 0.f || d1 < 0.f) dgrow |= 1u << b;
+                    x = shift(d0) | (shift(d1) << 16);
+                }
+                drec[b * (K / 2) + wd] = x;
+            }
+#pragma unroll
+            for (int b = 0; b + 1 < NB; ++b) {
+                const float d0 = A[b][e] - A[b + 1][e], d1 = A[b][e + 1] - A[b + 1][e + 1];
+                if (d0 < 0.f || d1 < 0.f) dgrow |= 1u << (NB + b);
+                drec[(NB + b) * (K / 2) + wd] = shift(d0) | (shift(d1) << 16);
+            }
         }
         const bool any_up = __any(up);  // the r0 == 0 threads are lanes 0..K/8-1 of wave 0
         if (threadIdx.x == 0) rec[REC_GROW] = any_up ? 1u : 0u;
+        if (dgrow) atomicOr(&sflag, dgrow << 8);
     }
-    const T *kin = static_cast<const T *>(a.k);
-    T *kout = static_cast<T *>(a.kt) + ((int64_t)tile * a.HQ + hq) * TILE * K;
-    // all of the thread's rows in flight before any is used
-    f32x8 kv[NPASS], pv[NPASS];
+    const __bf16 *qin = static_cast<const __bf16 *>(a.q);
+    const __bf16 *kin = static_cast<const __bf16 *>(a.k);
+    const int64_t o0 = ((int64_t)tile * HQ + hq) * TILE * K;
+    __bf16 *kout = static_cast<__bf16 *>(a.kt) + o0;
+    __bf16 *kdout = static_cast<__bf16 *>(a.kd) + o0;
+    __bf16 *qdout = static_cast<__bf16 *>(a.qd) + o0;
+    // the thread's rows in two batches, each batch's loads in flight before any is used
+    constexpr int NH = NPASS / 2;
+    uint32_t flags = 0;
 #pragma unroll
-    for (int p = 0; p < NPASS; ++p) {
-        const int j = c * TILE + r0 + p * RPP;
-        kv[p] = f32x8{};
-        pv[p] = f32x8{};
-        if (j < sg.len) {
-            const int64_t tok = sg.start + j;
-            kv[p] = Vec8<T>::load(kin + (tok * a.H + h) * K + c8 * 8);
-            pv[p] = *reinterpret_cast<const f32x8 *>(a.P + (tok * a.HQ + hq) * K + c8 * 8);
+    for (int half = 0; half < 2; ++half) {
+        f32x8 kv[NH], pv[NH], qv[NH];
+#pragma unroll
+        for (int i = 0; i < NH; ++i) {
+            const int j = c * TILE + r0 + (half * NH + i) * RPP;
+            kv[i] = f32x8{};
+            pv[i] = f32x8{};
+            qv[i] = f32x8{};
+            if (j < sg.len) {
+                const int64_t tok = sg.start + j;
+                kv[i] = Vec8<__bf16>::load(kin + (tok * a.H + h) * K + c8 * 8);
+                qv[i] = Vec8<__bf16>::load(qin + (tok * HQ + hq) * K + c8 * 8);
+                pv[i] = *reinterpret_cast<const f32x8 *>(a.P + (tok * HQ + hq) * K + c8 * 8);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NH; ++i) {
+            const int row = r0 + (half * NH + i) * RPP, b = row / DBLK;
+            const bool valid = c * TILE + row < sg.len;
+            f32x8 kl, kb, qb;
+            float dev = 0.f;
+            for (int e = 0; e < 8; ++e) {
+                kl[e] = kv[i][e] * exp2f(fminf(fmaxf(R[e] - pv[i][e], EXP2_LO), EXP2_HI));
+                const float x = pv[i][e] - A[b][e];
+                dev = fmaxf(dev, fabsf(x));
+                kb[e] = kv[i][e] * exp2f(fminf(fmaxf(-x, EXP2_LO), EXP2_HI));
+                qb[e] = qv[i][e] * a.qscale * exp2f(fminf(fmaxf(x, EXP2_LO), EXP2_HI));
+            }
+            if (valid && dev > DIAG_SPREAD) flags |= 1u << b;
+            Vec8<__bf16>::store(kout + row * K + c8 * 8, kl);
+            Vec8<__bf16>::store(kdout + row * K + c8 * 8, kb);
+            Vec8<__bf16>::store(qdout + row * K + c8 * 8, qb);
         }
     }
-#pragma unroll
-    for (int p = 0; p < NPASS; ++p) {
-        f32x8 out;
-        for (int e = 0; e < 8; ++e) out[e] = kv[p][e] * exp2f(fminf(fmaxf(R[e] - pv[p][e], EXP2_LO), EXP2_HI));
-        Vec8<T>::store(kout + (r0 + p * RPP) * K + c8 * 8, out);
-    }
+    if (flags) atomicOr(&sflag, flags);
+    __syncthreads();
+    if (threadIdx.x == 0) a.rec[((int64_t)tile * HQ + hq) * REC_WORDS + REC_DIAG] = sflag;
 }
 
 // Value tile of (tile, kv head), transposed [V][TILE].  Thread (kb, db)
@@ -184,7 +251,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
     if (!block_segment(a, tile, tile == 0 && y == 0, sg)) return;  // beyond the last used tile
     if ((tile - sg.tile_base) * TILE >= sg.len) return;
     if (y < a.HQ)
-        key_tile<__bf16, K>(a, tile, y, sg);
+        key_tile<K>(a, tile, y, sg);
     else
         value_tile<__bf16, V>(a, tile, y - (int)a.HQ, sg);
 }

@@ -198,21 +198,24 @@ wall_status_t wall_attn_fwd(const void *q, const void *k, const void *v, wall_dt
  * wall_attn_fwd_prepare folds the decay into the keys once per 128-row tile
  * and query head -- the prefill counterpart of the README's
  * build_wall_kv_cache (k_tilde[j] = k[j] * exp2(R_c - P[j]) with a per-chunk
- * anchor R_c) -- and stores, in `workspace`, the sequence table, the
- * anchors, the rescaled keys and the value tiles.  Arguments mean what they
- * mean for wall_attn_fwd (no q, G, sink, window or max_seqlen here).
+ * anchor R_c) -- and, for each tile's own queries, into the keys and the
+ * queries (times scale*log2(e)) of every 32-row block at that block's own
+ * anchor; it stores, in `workspace`, the sequence table, the anchors, these
+ * rescaled keys and queries and the value tiles.  Arguments mean what they
+ * mean for wall_attn_fwd (no G, sink, window or max_seqlen here).
  *
  * wall_attn_fwd_run reads that workspace (unchanged since a prepare call
- * with the same k, v, P, shapes and cu_seqlens, ordered before it on the
- * stream) together with q, k, v, P, G and sink_bias, and writes o and lse.
+ * with the same q, k, v, P, scale, shapes and cu_seqlens, ordered before it
+ * on the stream) together with q, k, v, P, G and sink_bias, and writes o and
+ * lse.
  * k and v are the prepare call's raw keys and values: the keys of each
  * query's own tile (and, for float32 inputs, every key and value) are read
  * from them.  `workspace` is read only.
  * Errors are those of wall_attn_fwd for the arguments each stage takes. */
-wall_status_t wall_attn_fwd_prepare(const void *k, const void *v, wall_dtype_t dtype,
+wall_status_t wall_attn_fwd_prepare(const void *q, const void *k, const void *v, wall_dtype_t dtype,
                                     const float *P,
                                     int64_t B, int64_t T, int64_t HQ, int64_t H, int64_t K, int64_t V,
-                                    const int32_t *cu_seqlens, int64_t num_seqs,
+                                    float scale, const int32_t *cu_seqlens, int64_t num_seqs,
                                     void *workspace, size_t workspace_bytes,
                                     hipStream_t stream);
 
