@@ -184,8 +184,9 @@ def prefix_scan_oracle(x, cu_seqlens=None, scale: float = 1.0 / np.log(2.0)):
 def kv_cache_oracle(k, P, chunk_size: int = 64):
     """The README's decode cache in fp64: ``k_tilde [B,T,HQ,K]`` (keys with the
     decay folded in against per-chunk anchors) and ``r_cache [B,ceil(T/C),HQ,K]``
-    (the anchors, floor of P at each chunk's first row).  k is [B,T,H,K], P the
-    log2 prefix [B,T,HQ,K]."""
+    (the anchors: floor of P at each chunk's first row, moved to a later row's
+    floored P whenever that row lies more than 64 log2 units below it).  k is
+    [B,T,H,K], P the log2 prefix [B,T,HQ,K]."""
     k, P = _f64(k), _f64(P)
     B, T, H, K = k.shape
     HQ = P.shape[2]

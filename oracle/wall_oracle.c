@@ -364,11 +364,17 @@ int wall_oracle_bwd(const double *q, const double *k, const double *v, const dou
 /* Decode cache, wall-attention-release README ("Decode (cached generation)"):
  * the keys with the decay folded in, per chunk of C rows,
  *     k_tilde[b,j,hq,n] = k[b,j,h,n] * exp2(R[b,c,hq,n] - P[b,j,hq,n]),  c = j / C,
- * with the chunk anchor R read as the floor of P at the chunk's first row
- * (the README names a per-chunk anchor and its role, not the row; the first
- * row is the one an append-as-you-go cache knows when the chunk opens).
+ * with one anchor R per chunk and channel.  The README names a per-chunk
+ * anchor and its role, not its row; the reading taken here is the one an
+ * append-as-you-go cache can keep while every cached factor stays in range:
+ * R starts as the floor of P at the chunk's first row, and whenever a later
+ * row t of the chunk has R - P[t] > CACHE_SPAN (its key factor would pass
+ * 2^CACHE_SPAN) the anchor moves to floor(P[t]).  The rows before t are
+ * then held against the new anchor too (k_tilde above always uses the final
+ * R of the chunk).  CACHE_SPAN is 64 log2 units.
  * P is the log2 prefix [B,T,HQ,K] (prefix scan of g with scale 1/ln 2);
  * h = hq / (HQ/H).  r_cache is [B, ceil(T/C), HQ, K]. */
+#define CACHE_SPAN 64.0
 int wall_oracle_kv_cache(const double *k,  /* [B,T,H,K] */
                          const double *P,  /* [B,T,HQ,K] */
                          double *k_tilde,  /* [B,T,HQ,K] */
@@ -385,10 +391,17 @@ int wall_oracle_kv_cache(const double *k,  /* [B,T,H,K] */
             for (int64_t hq = 0; hq < HQ; ++hq) {
                 const int64_t kvh = hq / group;
                 const int64_t j0 = c * C;
-                const double *Pa = P + ((b * T + j0) * HQ + hq) * K;
+                const int64_t j1 = j0 + C < T ? j0 + C : T;
                 double *R = r_cache + ((b * NC + c) * HQ + hq) * K;
-                for (int64_t n = 0; n < K; ++n) R[n] = floor(Pa[n]);
-                for (int64_t j = j0; j < j0 + C && j < T; ++j) {
+                for (int64_t n = 0; n < K; ++n) {
+                    double r = floor(P[((b * T + j0) * HQ + hq) * K + n]);
+                    for (int64_t j = j0 + 1; j < j1; ++j) {
+                        const double pj = P[((b * T + j) * HQ + hq) * K + n];
+                        if (r - pj > CACHE_SPAN) r = floor(pj);
+                    }
+                    R[n] = r;
+                }
+                for (int64_t j = j0; j < j1; ++j) {
                     const double *kj = k + ((b * T + j) * H + kvh) * K;
                     const double *Pj = P + ((b * T + j) * HQ + hq) * K;
                     double *kt = k_tilde + ((b * T + j) * HQ + hq) * K;

@@ -44,6 +44,9 @@ MUTANTS = {
                            "out[(b * T + t) * C + c] = run;"),
     "scan_no_reset_at_sequence_start": ("if (t == cu_seqlens[s]) run = 0.0;", ";"),
     "cache_factor_sign": ("kt[n] = kj[n] * exp2(R[n] - Pj[n]);", "kt[n] = kj[n] * exp2(Pj[n] - R[n]);"),
+    "cache_anchor_never_moves": ("if (r - pj > CACHE_SPAN) r = floor(pj);", ";"),
+    "cache_anchor_moves_to_unfloored_prefix": ("if (r - pj > CACHE_SPAN) r = floor(pj);",
+                                               "if (r - pj > CACHE_SPAN) r = pj;"),
     "cache_key_head_of_query": ("const double *kj = k + ((b * T + j) * H + kvh) * K;",
                                 "const double *kj = k + ((b * T + j) * H + hq % H) * K;"),
     "decode_query_factor_sign": ("dot += qi[n] * exp2(pc[n] - R[n]) * kt[n];",

@@ -340,6 +340,9 @@ def test_prefix_scan_matches_numpy_cumsum(oracle_mod):
     dict(B=3, T=23, HQ=2, H=1, K=4, V=2, C=64, g=-0.1, sink=False, scale=0.5),
     # a single cached token
     dict(B=2, T=1, HQ=2, H=2, K=3, V=5, C=64, g=-0.5, sink=True, scale=0.9),
+    # gates strong enough to move the chunk anchors many times
+    dict(B=2, T=140, HQ=2, H=1, K=6, V=4, C=64, g=-5.0, sink=True, scale=0.4),
+    dict(B=1, T=70, HQ=2, H=2, K=4, V=3, C=64, g=-800.0, sink=False, scale=0.6),
 ])
 def test_decode_equals_forward_last_row(oracle_mod, case):
     """README: the decode kernel reproduces the training forward token for
@@ -377,8 +380,25 @@ def test_kv_cache_zero_gate_and_reconstruction(oracle_mod):
     kt, r = oracle_mod.kv_cache_oracle(k, P, C)
     Rj = np.repeat(r, C, axis=1)[:, :T]
     np.testing.assert_allclose(kt * np.exp2(P - Rj), np.repeat(k, HQ // H, axis=2), rtol=1e-13, atol=1e-14)
-    # the factor stays within the chunk's decay: at most 1 below, never above the chunk start's prefix
-    assert (Rj - P > -1.0).all()
+    # every key factor exp2(R - P_j) of a chunk stays at most 2^64, and the
+    # anchor is the floored prefix of one of the chunk's own rows
+    assert (Rj - P <= 64.0).all()
+    for c in range(-(-T // C)):
+        rows = np.floor(P[:, c * C:(c + 1) * C])
+        assert np.all(np.any(rows == r[:, c:c + 1], axis=1))
+
+
+def test_kv_cache_anchor_moves_worked_example(oracle_mod):
+    """One chunk of four rows whose prefix falls 0, -10, -70.5, -100 (log2
+    units): the anchor starts at 0, stays while the rows lie at most 64 below
+    it, moves to floor(-70.5) = -71 at the third row, and stays (the fourth row
+    is 29 below).  Worked by hand."""
+    P = np.array([0.0, -10.0, -70.5, -100.0]).reshape(1, 4, 1, 1)
+    k = np.array([1.0, 2.0, 3.0, 4.0]).reshape(1, 4, 1, 1)
+    kt, r = oracle_mod.kv_cache_oracle(k, P, 4)
+    assert r.reshape(-1).tolist() == [-71.0]
+    np.testing.assert_allclose(kt.reshape(-1), [2.0 ** -71, 2.0 * 2.0 ** -61, 3.0 * 2.0 ** -0.5, 4.0 * 2.0 ** 29],
+                               rtol=1e-15)
 
 
 # --------------------------------------------------------------------------- backward
