@@ -2,14 +2,17 @@
 // ("Decode (cached generation)"): a cache of decay-folded keys built once
 // (and appended to as tokens arrive), then one query per head per step.
 //
-// Cache, per chunk c of C rows, query head hq and channel n:
-//     R[c][n]        = floor(P[c*C][n])                (anchor: the chunk's first row)
-//     k_tilde[j][n]  = k[j][n] * exp2(R[c][n] - P[j][n]),   c = j / C
-// Decode, query q at the row whose prefix is p:
+// Cache, per chunk c of C rows, query head hq and channel n (wall_cache.h):
+//     k_tilde[j][n]  = k[j][n] * exp2(R[c][n] - P[j][n]),   c = j / C,
+// with the anchor R[c][n] the floored prefix of the chunk's first row, moved
+// to a later row's floored prefix whenever that row lies more than 64 log2
+// units below it (the chunk's earlier rows lowered by the exact power of
+// two), so every cached factor stays at most 2^64.
+// Decode, query q at the row whose prefix is p (at or after every cached row):
 //     logit_j = scale * sum_n q_n * exp2(p_n - R[j/C][n]) * k_tilde[j][n]
 // which is the forward's logit (the blog's factored form, "Definition: Wall
-// Attention") with the anchor cancelling; the inner loop carries no gate
-// arithmetic beyond one exp2 per channel per chunk.
+// Attention") with the anchor cancelling; the query factor is at most 2.  The
+// inner loop carries no gate arithmetic beyond one exp2 per channel per chunk.
 //
 // The decode is split over the keys (split-KV): each block takes S keys of
 // up to four query heads of one kv head, one wave per head, 32 keys per round:
@@ -27,6 +30,7 @@
 // A second kernel merges the splits with the sink.  The kernels are bound
 // by HBM: each step reads the cached keys of every query head, the values of
 // every kv head and the anchors once.
+#include "wall_cache.h"
 #include "wall_common.h"
 
 #include <type_traits>
@@ -53,40 +57,26 @@ struct Vec8<float> {
 };
 
 // ---------------------------------------------------------------- cache
-// Thread = 8 channels of one (b, row j, hq), rows t0 .. t1-1.  A chunk that
-// opens inside the range takes its anchor from P (every thread of the chunk
-// reads the first row's prefix; the first row's threads store it); a chunk
-// opened by an earlier call reads the stored anchor.
+// Thread = 8 channels of one (b, chunk, hq) among the chunks that rows t0..t1-1
+// touch: its rows of the range in order (wall_cache.h).
 template <typename T, int K>
 __global__ __launch_bounds__(256) void kv_cache_kernel(CacheArgs a) {
     constexpr int CPR = K / 8;
-    const int64_t nrows = a.t1 - a.t0;
+    const int64_t c_first = a.t0 / a.C, nch = (a.t1 - 1) / a.C - c_first + 1;
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= a.B * nrows * a.HQ * CPR) return;
+    if (idx >= a.B * nch * a.HQ * CPR) return;
     const int c8 = (int)(idx % CPR);
     int64_t r = idx / CPR;
     const int64_t hq = r % a.HQ;
     r /= a.HQ;
-    const int64_t j = a.t0 + r % nrows, b = r / nrows;
+    const int64_t c = c_first + r % nch, b = r / nch;
     const int64_t h = hq / (a.HQ / a.H);
-    const int64_t c = j / a.C, j0 = c * a.C;
+    const int64_t j0 = c * a.C, ja = j0 > a.t0 ? j0 : a.t0, jb = j0 + a.C < a.t1 ? j0 + a.C : a.t1;
     const int64_t NC = cdiv(a.Tcap, a.C);
-    float *Rp = a.r + ((b * NC + c) * a.HQ + hq) * K + c8 * 8;
-    f32x8 R;
-    if (j0 >= a.t0) {
-        const f32x8 Pa = *reinterpret_cast<const f32x8 *>(a.P + ((b * a.Tcap + j0) * a.HQ + hq) * K + c8 * 8);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) R[e] = floorf(Pa[e]);
-        if (j == j0) *reinterpret_cast<f32x8 *>(Rp) = R;
-    } else {
-        R = *reinterpret_cast<const f32x8 *>(Rp);
-    }
-    const f32x8 kv = Vec8<T>::load(static_cast<const T *>(a.k) + ((b * a.Tcap + j) * a.H + h) * K + c8 * 8);
-    const f32x8 Pj = *reinterpret_cast<const f32x8 *>(a.P + ((b * a.Tcap + j) * a.HQ + hq) * K + c8 * 8);
-    f32x8 out;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) out[e] = kv[e] * exp2f(fminf(fmaxf(R[e] - Pj[e], EXP2_LO), EXP2_HI));
-    Vec8<T>::store(static_cast<T *>(a.kt) + ((b * a.Tcap + j) * a.HQ + hq) * K + c8 * 8, out);
+    cache_chunk<T>(static_cast<const T *>(a.k) + (b * a.Tcap * a.H + h) * K + c8 * 8,
+                   a.P + (b * a.Tcap * a.HQ + hq) * K + c8 * 8,
+                   static_cast<T *>(a.kt) + (b * a.Tcap * a.HQ + hq) * K + c8 * 8,
+                   a.r + ((b * NC + c) * a.HQ + hq) * K + c8 * 8, a.HQ * K, a.H * K, j0, ja, jb);
 }
 
 // ---------------------------------------------------------------- decode
@@ -261,7 +251,7 @@ __global__ __launch_bounds__(V) void decode_merge(DecodeArgs a) {
 
 template <typename T, int K>
 hipError_t run_cache(const CacheArgs &a, hipStream_t st) {
-    const int64_t n = a.B * (a.t1 - a.t0) * a.HQ * (K / 8);
+    const int64_t n = a.B * ((a.t1 - 1) / a.C - a.t0 / a.C + 1) * a.HQ * (K / 8);
     hipLaunchKernelGGL((kv_cache_kernel<T, K>), dim3((unsigned)cdiv(n, 256)), dim3(256), 0, st, a);
     return hipGetLastError();
 }

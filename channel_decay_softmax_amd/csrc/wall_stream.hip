@@ -1,9 +1,10 @@
 // wall_stream.hip -- one turn of the append-as-you-go decode loop in one pass
 // (the README's streaming decode): for new rows t0 .. t1-1 of each sequence,
 // the log2 prefix P from the previous row's (as wall_prefix_append computes
-// it) and the cache rows k~ = k 2^(R_c - P) with the chunk anchors R_c (as
-// wall_kv_cache_build computes them), with the same float32 operations in the
-// same order, so the results are those of the two separate calls bit for bit.
+// it) and the cache rows and chunk anchors (as wall_kv_cache_build computes
+// them, wall_cache.h), with the same float32 operations in the same order,
+// so the results are those of the two separate calls bit for bit.
+#include "wall_cache.h"
 #include "wall_common.h"
 #include "wall_stream.h"
 
@@ -20,18 +21,9 @@ template <>
 __device__ inline f32x8 load8<float>(const float *p) {
     return *reinterpret_cast<const f32x8 *>(p);
 }
-template <typename T>
-__device__ inline void store8(T *p, f32x8 v);
-template <>
-__device__ inline void store8<__bf16>(__bf16 *p, f32x8 v) {
-    *reinterpret_cast<bf16x8 *>(p) = __builtin_convertvector(v, bf16x8);
-}
-template <>
-__device__ inline void store8<float>(float *p, f32x8 v) {
-    *reinterpret_cast<f32x8 *>(p) = v;
-}
 
-// One thread per (sequence, query head, 8 channels); the new rows in order.
+// One thread per (sequence, query head, 8 channels); the new rows in order:
+// first their prefix, then their cache rows chunk by chunk.
 template <typename Tg, typename T, int K>
 __global__ __launch_bounds__(256) void stream_append_kernel(StreamArgs a) {
     constexpr int CPR = K / 8;
@@ -46,9 +38,7 @@ __global__ __launch_bounds__(256) void stream_append_kernel(StreamArgs a) {
     const int64_t kbase = (b * a.Tcap * a.H + h) * K + c8 * 8;        // [b, 0, h, ch] in k
     f32x8 prev = 0.f;
     if (a.t0 > 0) prev = *reinterpret_cast<const f32x8 *>(a.P + base + (a.t0 - 1) * rowP);
-    f32x8 s = 0.f, R = 0.f;
-    if (a.t0 % a.C != 0)  // the chunk of t0 opened before this call: its stored anchor
-        R = *reinterpret_cast<const f32x8 *>(a.r + ((b * NC + a.t0 / a.C) * a.HQ + hq) * K + c8 * 8);
+    f32x8 s = 0.f;
     for (int64_t t = a.t0; t < a.t1; ++t) {
         const f32x8 g8 = load8<Tg>(static_cast<const Tg *>(a.g) + base + t * rowP);
         f32x8 P;
@@ -58,16 +48,12 @@ __global__ __launch_bounds__(256) void stream_append_kernel(StreamArgs a) {
             P[e] = prev[e] + a.scale * s[e];
         }
         *reinterpret_cast<f32x8 *>(a.P + base + t * rowP) = P;
-        if (t % a.C == 0) {  // a chunk opens: its anchor is this row's floored prefix
-#pragma unroll
-            for (int e = 0; e < 8; ++e) R[e] = floorf(P[e]);
-            *reinterpret_cast<f32x8 *>(a.r + ((b * NC + t / a.C) * a.HQ + hq) * K + c8 * 8) = R;
-        }
-        const f32x8 kv = load8<T>(static_cast<const T *>(a.k) + kbase + t * rowK);
-        f32x8 out;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) out[e] = kv[e] * exp2f(fminf(fmaxf(R[e] - P[e], EXP2_LO), EXP2_HI));
-        store8<T>(static_cast<T *>(a.kt) + base + t * rowP, out);
+    }
+    for (int64_t ja = a.t0; ja < a.t1;) {
+        const int64_t c = ja / a.C, j0 = c * a.C, jb = j0 + a.C < a.t1 ? j0 + a.C : a.t1;
+        cache_chunk<T>(static_cast<const T *>(a.k) + kbase, a.P + base, static_cast<T *>(a.kt) + base,
+                       a.r + ((b * NC + c) * a.HQ + hq) * K + c8 * 8, rowP, rowK, j0, ja, jb);
+        ja = jb;
     }
 }
 

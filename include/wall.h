@@ -291,25 +291,32 @@ wall_status_t wall_attn_bwd(const void *q, const void *k, const void *v, wall_dt
  * decode step never re-accumulates the prefix.  For chunk c of chunk_size
  * rows, query head hq and channel n:
  *
- *   r_cache[b, c, hq, n]  = floor(P[b, c*chunk_size, hq, n])   (the chunk's first row)
  *   k_tilde[b, j, hq, n]  = k[b, j, hq / (HQ/H), n] * exp2(r_cache[b, j/chunk_size, hq, n] - P[b, j, hq, n])
  *
- * (the README names a per-chunk anchor without fixing its row; the first
- * row is the one known when a chunk opens, so appending never moves an
- * anchor).  Only rows t0 .. t1-1 of every sequence are written: a call with
- * t0 = 0, t1 = T builds the cache of a prefill, a call with t1 = t0 + 1
- * appends one token.  A chunk whose first row lies in [t0, t1) gets its
- * anchor from P and stores it; a chunk opened by an earlier call (on the same
- * stream, or otherwise completed) reads the stored anchor.  The exponent is
- * clamped to [-160, 126].
+ * The README names one anchor per chunk without fixing its row.  Here the
+ * anchor of a chunk is floor(P) of its first row until a later row t of the
+ * chunk lies more than 64 log2 units below it (r - P[t] > 64, its key
+ * factor would pass 2^64); the anchor then moves to floor(P[t]) and the rows
+ * of the chunk cached before t are lowered by the exact power of two
+ * 2^(new - old) (on the bit pattern: exponent lowered, 0 below the range).
+ * Every cached factor stays at most 2^64 and a decode query's factor at most
+ * 2, at any gate strength (down to closed gates); a row lowered out of range
+ * carries a term below 2^-60 of the largest.  Only rows t0 .. t1-1 of every
+ * sequence are written (and, when an anchor moves, the earlier rows of its
+ * chunk lowered): a call with t0 = 0, t1 = T builds the cache of a prefill,
+ * a call with t1 = t0 + 1 appends one token.  A chunk opened by an earlier
+ * call (on the same stream, or otherwise completed) continues from its
+ * stored anchor, so building in pieces gives the bits of one build.  The
+ * exponent is clamped to [-160, 126].
  *
  *   k           [B, T_cap, H, K]  dtype; rows t0 .. t1-1 are read
  *   P           [B, T_cap, HQ, K] float32 log2 prefix (wall_prefix_scan of g
- *               with scale 1/ln 2); rows t0 .. t1-1 and the first rows of the
- *               chunks they open are read
- *   k_tilde     [B, T_cap, HQ, K] dtype (rows t0 .. t1-1 written)
+ *               with scale 1/ln 2); rows t0 .. t1-1 are read
+ *   k_tilde     [B, T_cap, HQ, K] dtype (rows t0 .. t1-1 written; the rows of
+ *               their chunks before t0 rewritten when an anchor moves)
  *   r_cache     [B, ceil(T_cap / chunk_size), HQ, K] float32 (anchors of the
- *               chunks opened in [t0, t1) written, earlier ones read)
+ *               chunks that rows t0 .. t1-1 touch: read when the chunk opened
+ *               before t0, written)
  *   T_cap       rows allocated per sequence in k, P, k_tilde (and v below)
  * All pointers are caller-owned device memory, 16-byte aligned.
  * Errors: INVALID_ARG for a null pointer, a size < 1, HQ % H != 0, not
@@ -336,9 +343,9 @@ wall_status_t wall_kv_cache_build(const void *k, wall_dtype_t dtype, const float
  *   k           [B, T_cap, H, K] in dtype, rows t0 .. t1-1 read
  *   P           [B, T_cap, HQ, K] float32: row t0-1 read (t0 > 0), rows t0 .. t1-1 written
  *   k_tilde     [B, T_cap, HQ, K] in dtype, rows t0 .. t1-1 written
- *   r_cache     [B, ceil(T_cap / chunk_size), HQ, K] float32: the anchor of a
- *               chunk opened before t0 is read, the anchor of a chunk opening
- *               at a row in t0 .. t1-1 is written
+ *   k_tilde, r_cache   as for wall_kv_cache_build (the chunk of t0 continues
+ *               from its stored anchor; the anchors of every touched chunk
+ *               are written)
  *   scale       1 / ln 2 for the natural-log gate of the README
  * Errors: INVALID_ARG for a null pointer, a size < 1, HQ % H != 0, t0 < 0,
  * t1 <= t0 or t1 > T_cap, misalignment; UNSUPPORTED for K not in {64, 128},
@@ -369,14 +376,18 @@ wall_status_t wall_stream_append(const void *g, wall_dtype_t g_dtype, const void
  *               (stride T_cap*HQ*K); a nonzero stride is a multiple of 4,
  *               at least HQ*K
  *   k_tilde, r_cache   a cache built by wall_kv_cache_build with this
- *               chunk_size and T_cap, rows 0 .. T-1 complete
+ *               chunk_size and T_cap, rows 0 .. T-1 complete and no later
+ *               row built (a row after the query could have moved the last
+ *               chunk's anchor past it; rows are appended, never rolled back)
  *   sink_bias   NULL or [HQ] float32
  *   o           [B, HQ, V] dtype (written); lse NULL or [B, HQ] float32 (written)
  *   workspace   device scratch of at least
  *               wall_attn_decode_workspace_size(B, T, HQ, V) bytes, 256-byte
  *               aligned, contents on entry ignored (split-KV partials)
  * Numerics: q~ = q * scale*log2(e) * exp2(p_curr - R) is rounded to the cache
- * dtype once per chunk; dot products and the softmax are float32.
+ * dtype once per chunk (at most 2, since the query row is at or after every
+ * cached row and the anchor is the floor of one of them); dot products and
+ * the softmax are float32.
  * Errors: INVALID_ARG for a null required pointer, a size < 1, HQ % H != 0,
  * T > T_cap, B*HQ > 65535, a bad p_curr stride, misalignment, a short
  * workspace; UNSUPPORTED for K
