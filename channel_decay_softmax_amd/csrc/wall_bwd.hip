@@ -20,9 +20,11 @@
 // the matrix-core kernels of wall_bwd_mfma.hip for the rest.  For float32
 // inputs the kernels below run everything in float32 on the vector ALUs:
 //   bwd_pre_kernel   D_i
+//   (wall_bwd_diag.hip) the pairs inside every 32-row block, pair by pair:
+//                    dq, dk and dv parts, X and Y of those pairs
 //   bwd_dq_kernel    one block per (query head, sequence, 64 query rows): keys
-//                    staged 32 at a time in LDS; writes dq, X = q (.) dq, the
-//                    row sums of dS and the sink terms
+//                    staged 32 at a time in LDS; adds dq, q (.) dq, the row
+//                    sums of dS and writes the sink terms
 //   bwd_dkdv_kernel  one block per (kv head, sequence, 64 keys), looping over
 //                    the kv head's query heads and over the visible queries 32
 //                    at a time; writes dk, dv and subtracts k (.) dk^(hq) and
@@ -31,10 +33,14 @@
 //   dsink_kernel     the sink sums
 // and the exclusive prefix scans of X and Y give dg and dg_scalar.
 //
-// Anchors: the dq kernel writes 2^(P_i - P_j) = 2^(P_i - R) 2^(R - P_j) with
-// R = floor(P) at the block's last row, the dk/dv kernel with R = floor(P) at
-// the block's first key.  For a gate g <= 0 the factor on the side away from
-// R is at most 2 and the other at most 2^(change of P over 64 rows).
+// Anchors (the anchor identity of the Wall Attention blog, "Fast training
+// and inference"): every pair of rows in different 32-row blocks is read at
+// R = floor(P) of a row between them -- the row before the query block (dq
+// kernel) or the key block's last row (dk/dv kernel) for rows of other
+// 64-row blocks, the last row of the first half for the pairs across the two
+// halves -- so for a prefix that falls both factors 2^(P_i - R) and
+// 2^(R - P_j) are at most 2 at any gate strength.  The accumulators move from
+// one anchor to the next by exact powers of two.
 #include <float.h>
 
 #include <type_traits>
@@ -111,17 +117,24 @@ __global__ __launch_bounds__(NT) void bwd_pre_kernel(BwdArgs a, int64_t nrows) {
 }
 
 // ---------------------------------------------------------------- dq
+// One block per (query head, sequence, 64 query rows: halves h0 and h1).  The
+// keys before the block are read against A0 = floor(P) of the row before it;
+// then the keys of h0 against A1 = floor(P) of h0's last row for the queries
+// of h1, with the h1 accumulators moved from A0 to A1 (an exact power of two,
+// at most 1).  The pairs inside h0 and inside h1 come from the pair-by-pair
+// kernel (dqd, X, Y), which runs first.
 template <typename T, int K, int V>
 __global__ __launch_bounds__(NT) void bwd_dq_kernel(BwdArgs a, int nblk) {
     constexpr int QP = K + 1, VP = V + 1, SP = BS + 1, KQ = K / 4;
     extern __shared__ float smem[];
-    float *sQ = smem;                 // [BB][QP] q * scale*log2e * 2^(P - R)
+    float *sQ = smem;                 // [BB][QP] q * scale*log2e * 2^(P - anchor)
     float *sDO = sQ + BB * QP;        // [BB][VP]
-    float *sK = sDO + BB * VP;        // [BS][QP] k * 2^(R - P)
+    float *sK = sDO + BB * VP;        // [BS][QP] k * 2^(anchor - P)
     float *sV = sK + BS * QP;         // [BS][VP]
     float *sDS = sV + BS * VP;        // [BB][SP]
     float *sG = sDS + BB * SP;        // [BS] -G_j (log2 units)
-    float *sR = sG + BS;              // [K] anchors
+    float *sA0 = sG + BS;             // [K] A0
+    float *sA1 = sA0 + K;             // [K] A1
 
     const int bid = blockIdx.x;
     const int hq = bid / (a.nseg * nblk);
@@ -132,23 +145,32 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(BwdArgs a, int nblk) {
     const int tid = threadIdx.x, qi = tid / 4, sub = tid % 4;
     const int64_t HQ = a.HQ;
     const int h = hq / (a.HQ / a.H);
-    const int i0 = qb * BB, ilast = min(i0 + BB, sg.len) - 1;
+    const int i0 = qb * BB;
+    const bool has_h1 = i0 + BS < sg.len;
     const T *qg = static_cast<const T *>(a.q);
     const T *kg = static_cast<const T *>(a.k);
     const T *vg = static_cast<const T *>(a.v);
     const T *dog = static_cast<const T *>(a.dout);
+    const float *Pg = a.P + hq * K;
 
-    if (tid < K) sR[tid] = floorf(a.P[((int64_t)sg.start + ilast) * HQ * K + hq * K + tid]);
-    __syncthreads();
-    for (int x = tid; x < BB * K; x += NT) {
-        const int r = x / K, n = x % K, row = i0 + r;
-        float val = 0.f;
-        if (row < sg.len) {
-            const int64_t t = (int64_t)sg.start + row;
-            val = ld(qg + (t * HQ + hq) * K + n) * a.qscale * clamp2(a.P[(t * HQ + hq) * K + n] - sR[n]);
-        }
-        sQ[r * QP + n] = val;
+    if (tid < K) {
+        sA0[tid] = i0 > 0 ? floorf(Pg[((int64_t)sg.start + i0 - 1) * HQ * K + tid]) : 0.f;
+        sA1[tid] = has_h1 ? floorf(Pg[((int64_t)sg.start + i0 + BS - 1) * HQ * K + tid]) : 0.f;
     }
+    __syncthreads();
+    // q of rows first .. BB-1 of the block at anchor R
+    auto stage_q = [&](int first, const float *R) {
+        for (int x = tid; x < (BB - first) * K; x += NT) {
+            const int r = first + x / K, n = x % K, row = i0 + r;
+            float val = 0.f;
+            if (row < sg.len) {
+                const int64_t t = (int64_t)sg.start + row;
+                val = ld(qg + (t * HQ + hq) * K + n) * a.qscale * clamp2(Pg[t * HQ * K + n] - R[n]);
+            }
+            sQ[r * QP + n] = val;
+        }
+    };
+    stage_q(0, sA0);
     for (int x = tid; x < BB * V; x += NT) {
         const int r = x / V, c = x % V, row = i0 + r;
         sDO[r * VP + c] = row < sg.len ? ld(dog + (((int64_t)sg.start + row) * HQ + hq) * V + c) : 0.f;
@@ -166,14 +188,30 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(BwdArgs a, int nblk) {
     float grow = 0.f;
     int lo = 0;
     if (a.window > 0) lo = max(0, i0 - a.window + 1);
-    for (int key0 = lo / BS * BS; key0 <= ilast; key0 += BS) {
+    // stages: the keys before the block, then (for h1) the keys of h0
+    const int nst_off = i0 > lo / BS * BS ? (i0 - lo / BS * BS) / BS : 0;
+    const int nst = nst_off + (has_h1 ? 1 : 0);
+    for (int st_i = 0; st_i < nst; ++st_i) {
+        const bool own = st_i == nst_off;
+        const int key0 = own ? i0 : lo / BS * BS + BS * st_i;
+        const float *R = own ? sA1 : sA0;
         __syncthreads();
+        if (own) {
+            stage_q(BS, sA1);
+            if (qi >= BS) {
+#pragma unroll
+                for (int n = 0; n < KQ; ++n) {
+                    const int ch = sub * KQ + n;
+                    acc[n] *= exp2f(sA1[ch] - sA0[ch]);
+                }
+            }
+        }
         for (int x = tid; x < BS * K; x += NT) {
             const int r = x / K, n = x % K, j = key0 + r;
             float val = 0.f;
             if (j < sg.len) {
                 const int64_t t = (int64_t)sg.start + j;
-                val = ld(kg + (t * a.H + h) * K + n) * clamp2(sR[n] - a.P[(t * HQ + hq) * K + n]);
+                val = ld(kg + (t * a.H + h) * K + n) * clamp2(R[n] - Pg[t * HQ * K + n]);
             }
             sK[r * QP + n] = val;
         }
@@ -188,14 +226,17 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(BwdArgs a, int nblk) {
         __syncthreads();
         for (int kk = 0; kk < BS / 4; ++kk) {
             const int kr = sub * (BS / 4) + kk, key = key0 + kr;
-            float dot = 0.f;
-            for (int n = 0; n < K; ++n) dot = fmaf(sQ[qi * QP + n], sK[kr * QP + n], dot);
-            bool vis = qvalid && key <= qrow && key < sg.len;
+            bool vis = qvalid && key <= qrow && key < sg.len && (!own || qi >= BS);
             if (a.window > 0) vis = vis && qrow - key < a.window;
-            const float A = vis ? exp2f(dot + gi + sG[kr] - lse2) : 0.f;
-            float dp = 0.f;
-            for (int c = 0; c < V; ++c) dp = fmaf(sDO[qi * VP + c], sV[kr * VP + c], dp);
-            const float dS = A * (dp - Di);
+            float dS = 0.f;
+            if (vis) {
+                float dot = 0.f;
+                for (int n = 0; n < K; ++n) dot = fmaf(sQ[qi * QP + n], sK[kr * QP + n], dot);
+                const float A = exp2f(dot + gi + sG[kr] - lse2);
+                float dp = 0.f;
+                for (int c = 0; c < V; ++c) dp = fmaf(sDO[qi * VP + c], sV[kr * VP + c], dp);
+                dS = A * (dp - Di);
+            }
             sDS[qi * SP + kr] = dS;
             grow += dS;
         }
@@ -210,34 +251,43 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(BwdArgs a, int nblk) {
     grow += __shfl_xor(grow, 1, 64);
     grow += __shfl_xor(grow, 2, 64);
     if (!qvalid) return;
+    const float *R = qi >= BS ? sA1 : sA0;
     T *dqg = static_cast<T *>(a.dq) + (qt * HQ + hq) * K + sub * KQ;
-    float *X = a.X + (qt * HQ + hq) * K + sub * KQ;
+    const int64_t base = (qt * HQ + hq) * K + sub * KQ;
 #pragma unroll
     for (int n = 0; n < KQ; ++n) {
         const int ch = sub * KQ + n;
-        const float dq = a.scale * clamp2(a.P[(qt * HQ + hq) * K + ch] - sR[ch]) * acc[n];
-        st(dqg + n, dq);
-        X[n] = ld(qg + (qt * HQ + hq) * K + ch) * dq;
+        const float dq = a.scale * clamp2(a.P[base + n] - R[ch]) * acc[n];
+        st(dqg + n, dq + a.dqd[base + n]);
+        a.X[base + n] += ld(qg + base + n) * dq;
     }
     if (sub == 0) {
-        a.Y[qt * HQ + hq] = grow;
+        a.Y[qt * HQ + hq] += grow;
         a.Z[qt * HQ + hq] = a.sink ? -exp2f(a.sink[hq] * LOG2E - lse2) * Di : 0.f;
     }
 }
 
 // ---------------------------------------------------------------- dk, dv
+// One block per (kv head, sequence, 64 keys: halves k0 and k1), looping over
+// the kv head's query heads.  The queries after the block are read against
+// B = floor(P) of its last row; then the queries of k1 against A = floor(P) of
+// k0's last row for the keys of k0, whose accumulators move from B to A (an
+// exact power of two, at most 1).  The pairs inside k0 and inside k1 come from
+// the pair-by-pair kernel, whose per query head dk and dv parts (dkp, dvp) are
+// added here.
 template <typename T, int K, int V>
 __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a, int nblk) {
     constexpr int QP = K + 1, VP = V + 1, SP = BS + 1, KQ = K / 4, VQ = V / 4;
     extern __shared__ float smem[];
-    float *sK = smem;                 // [BB][QP] k * 2^(R - P) for the current query head
+    float *sK = smem;                 // [BB][QP] k * 2^(anchor - P) for the current query head
     float *sV = sK + BB * QP;         // [BB][VP]
-    float *sQ = sV + BB * VP;         // [BS][QP] q * scale*log2e * 2^(P - R)
+    float *sQ = sV + BB * VP;         // [BS][QP] q * scale*log2e * 2^(P - anchor)
     float *sDO = sQ + BS * QP;        // [BS][VP]
     float *sA = sDO + BS * VP;        // [BB][SP]
     float *sDS = sA + BB * SP;        // [BB][SP]
     float *sI = sDS + BB * SP;        // [BS][4]: lse2, D, G (log2), valid
-    float *sR = sI + BS * 4;          // [K]
+    float *sB = sI + BS * 4;          // [K] B
+    float *sAk = sB + K;              // [K] A
 
     const int bid = blockIdx.x;
     const int h = bid / (a.nseg * nblk);
@@ -268,33 +318,57 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a, int nblk) {
     for (int n = 0; n < KQ; ++n) dk[n] = 0.f;
     int ihi = sg.len - 1;
     if (a.window > 0) ihi = min(ihi, min(j0 + BB, sg.len) - 1 + a.window - 1);
+    // stages: the queries after the block, then (keys of k0) the queries of k1
+    const int nst_off = ihi >= j0 + BB ? (ihi - (j0 + BB)) / BS + 1 : 0;
+    const bool has_k1 = ihi >= j0 + BS;
+    const int nst = nst_off + (has_k1 ? 1 : 0);
 
     for (int hq = h * group; hq < (h + 1) * group; ++hq) {
+        const float *Pg = a.P + hq * K;
         __syncthreads();
-        if (tid < K) sR[tid] = floorf(a.P[((int64_t)sg.start + j0) * HQ * K + hq * K + tid]);
-        __syncthreads();
-        for (int x = tid; x < BB * K; x += NT) {
-            const int r = x / K, n = x % K, j = j0 + r;
-            float val = 0.f;
-            if (j < sg.len) {
-                const int64_t t = (int64_t)sg.start + j;
-                val = ld(kg + (t * a.H + h) * K + n) * clamp2(sR[n] - a.P[(t * HQ + hq) * K + n]);
-            }
-            sK[r * QP + n] = val;
+        if (tid < K) {
+            sB[tid] = j0 + BB - 1 < sg.len ? floorf(Pg[((int64_t)sg.start + j0 + BB - 1) * HQ * K + tid]) : 0.f;
+            sAk[tid] = j0 + BS - 1 < sg.len ? floorf(Pg[((int64_t)sg.start + j0 + BS - 1) * HQ * K + tid]) : 0.f;
         }
+        __syncthreads();
+        auto stage_k = [&](int rows, const float *R) {
+            for (int x = tid; x < rows * K; x += NT) {
+                const int r = x / K, n = x % K, j = j0 + r;
+                float val = 0.f;
+                if (j < sg.len) {
+                    const int64_t t = (int64_t)sg.start + j;
+                    val = ld(kg + (t * a.H + h) * K + n) * clamp2(R[n] - Pg[t * HQ * K + n]);
+                }
+                sK[r * QP + n] = val;
+            }
+        };
+        stage_k(BB, sB);
         const float gj = (a.G && kvalid) ? a.G[kt * HQ + hq] : 0.f;
         float dkh[KQ];
 #pragma unroll
         for (int n = 0; n < KQ; ++n) dkh[n] = 0.f;
         float gcol = 0.f;
-        for (int q0 = j0 / BS * BS; q0 <= ihi; q0 += BS) {
+        for (int st_i = 0; st_i < nst; ++st_i) {
+            const bool own = st_i == nst_off;
+            const int q0 = own ? j0 + BS : j0 + BB + BS * st_i;
+            const float *R = own ? sAk : sB;
             __syncthreads();
+            if (own) {
+                stage_k(BS, sAk);
+                if (kj < BS && nst_off > 0) {
+#pragma unroll
+                    for (int n = 0; n < KQ; ++n) {
+                        const int ch = sub * KQ + n;
+                        dkh[n] *= exp2f(sB[ch] - sAk[ch]);
+                    }
+                }
+            }
             for (int x = tid; x < BS * K; x += NT) {
                 const int r = x / K, n = x % K, i = q0 + r;
                 float val = 0.f;
                 if (i < sg.len) {
                     const int64_t t = (int64_t)sg.start + i;
-                    val = ld(qg + (t * HQ + hq) * K + n) * a.qscale * clamp2(a.P[(t * HQ + hq) * K + n] - sR[n]);
+                    val = ld(qg + (t * HQ + hq) * K + n) * a.qscale * clamp2(Pg[t * HQ * K + n] - R[n]);
                 }
                 sQ[r * QP + n] = val;
             }
@@ -314,14 +388,17 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a, int nblk) {
             __syncthreads();
             for (int ii = 0; ii < BS / 4; ++ii) {
                 const int ir = sub * (BS / 4) + ii, i = q0 + ir;
-                float dot = 0.f;
-                for (int n = 0; n < K; ++n) dot = fmaf(sQ[ir * QP + n], sK[kj * QP + n], dot);
-                bool vis = kvalid && sI[ir * 4 + 3] != 0.f && key <= i;
+                bool vis = kvalid && sI[ir * 4 + 3] != 0.f && key <= i && (!own || kj < BS);
                 if (a.window > 0) vis = vis && i - key < a.window;
-                const float A = vis ? exp2f(dot + sI[ir * 4 + 2] - gj - sI[ir * 4 + 0]) : 0.f;
-                float dp = 0.f;
-                for (int c = 0; c < V; ++c) dp = fmaf(sDO[ir * VP + c], sV[kj * VP + c], dp);
-                const float dS = A * (dp - sI[ir * 4 + 1]);
+                float A = 0.f, dS = 0.f;
+                if (vis) {
+                    float dot = 0.f;
+                    for (int n = 0; n < K; ++n) dot = fmaf(sQ[ir * QP + n], sK[kj * QP + n], dot);
+                    A = exp2f(dot + sI[ir * 4 + 2] - gj - sI[ir * 4 + 0]);
+                    float dp = 0.f;
+                    for (int c = 0; c < V; ++c) dp = fmaf(sDO[ir * VP + c], sV[kj * VP + c], dp);
+                    dS = A * (dp - sI[ir * 4 + 1]);
+                }
                 sA[kj * SP + ir] = A;
                 sDS[kj * SP + ir] = dS;
                 gcol += dS;
@@ -342,14 +419,19 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a, int nblk) {
         if (kvalid) {
             // this query head's part of dk: scale * 2^(R - P_j) * sum_i dS q 2^(P_i - R);
             // sQ carries scale*log2e, so the factor left is ln 2
-            float *X = a.X + (kt * HQ + hq) * K + sub * KQ;
+            const float *R = (kj < BS && has_k1) ? sAk : sB;
+            const int64_t base = (kt * HQ + hq) * K + sub * KQ;
+            float *X = a.X + base;
 #pragma unroll
             for (int n = 0; n < KQ; ++n) {
                 const int ch = sub * KQ + n;
-                const float d = LN2 * clamp2(sR[ch] - a.P[(kt * HQ + hq) * K + ch]) * dkh[n];
-                dk[n] += d;
+                const float d = LN2 * clamp2(R[ch] - a.P[base + n]) * dkh[n];
+                dk[n] += d + a.dkp[base + n];
                 X[n] -= ld(kg + (kt * a.H + h) * K + ch) * d;
             }
+            const float *dvd = a.dvp + (kt * HQ + hq) * V + sub * VQ;
+#pragma unroll
+            for (int c = 0; c < VQ; ++c) dv[c] += dvd[c];
             if (sub == 0) a.Y[kt * HQ + hq] -= gcol;
         }
     }
@@ -407,9 +489,13 @@ hipError_t run_valu(const BwdArgs &a, hipStream_t st) {
     hipError_t e;
     const int nblk = (int)cdiv(a.max_seqlen, BB);
     constexpr size_t smem_q =
-        sizeof(float) * (BB * (K + 1) + BB * (V + 1) + BS * (K + 1) + BS * (V + 1) + BB * (BS + 1) + BS + K);
+        sizeof(float) * (BB * (K + 1) + BB * (V + 1) + BS * (K + 1) + BS * (V + 1) + BB * (BS + 1) + BS + 2 * K);
     constexpr size_t smem_k = sizeof(float) * (BB * (K + 1) + BB * (V + 1) + BS * (K + 1) + BS * (V + 1) +
-                                               2 * BB * (BS + 1) + BS * 4 + K);
+                                               2 * BB * (BS + 1) + BS * 4 + 2 * K);
+    static_assert(smem_q <= 160 * 1024 && smem_k <= 160 * 1024, "LDS per workgroup");
+    // the pairs inside 32-row blocks first: the kernels below add its parts
+    e = launch_bwd_diag(a, std::is_same<T, __bf16>::value, true, st);
+    if (e != hipSuccess) return e;
     e = hipFuncSetAttribute(reinterpret_cast<const void *>(&bwd_dq_kernel<T, K, V>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem_q);
     if (e != hipSuccess) return e;

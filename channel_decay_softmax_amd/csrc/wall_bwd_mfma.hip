@@ -9,19 +9,39 @@
 //
 // Work decomposition.  A block owns one 128-row tile of one (query head,
 // sequence): keys in the dk/dv kernel, queries in the dq kernel; its waves own
-// 32 rows each (one MFMA block).  Every tile is anchored per channel at the
-// floored prefix of its middle row (row 64, or the last row of a shorter
-// tail), as the forward anchors its tiles, so both exp2 factors of a pair
-// stay within 2^(+-change of P over 64 rows); bwd_anchor_kernel writes every
-// row's q~ and k~ at its own tile's anchor once.  The other side streams
+// 32 rows each (one MFMA block, one anchor block).  The other side streams
 // through LDS 32 rows at a time, each tile both row-major (the MFMA's first
 // operand) and transposed (the second operand of the product that contracts
-// over the streamed rows), moved to the block's anchor by an exact power of
-// two as it is staged; the next tile's global loads are issued before the
+// over the streamed rows); the next tile's global loads are issued before the
 // current tile's products, and the tiles are double-buffered in LDS (one
 // barrier per tile).  Staging lanes take consecutive rows of one 8-channel
 // chunk, so the transposed copy is written as runs of consecutive bf16.  The
 // block's own rows stay in registers as second operands.
+//
+// Anchors (the anchor identity exp2(P_i - P_j) = exp2(P_i - R) exp2(R - P_j)
+// of the Wall Attention blog, "Fast training and inference"), per query head
+// and channel, with A_b = floor(P) of 32-row block b's last row:
+//   * bwd_anchor_kernel writes A_b, each row's q~ at A_(b-1) of the block
+//     before its own and k~ at its own block's A_b (both factors at most 2
+//     for a falling prefix), and flags a block whose rows lie more than
+//     BWD_SPREAD log2 units from A_b or A_(b-1);
+//   * a pair whose rows lie in different 128-row tiles is read at a tile
+//     boundary: floor(P) of the row before the query tile in the dq kernel,
+//     A of the key tile's last block in the dk/dv kernel; both lie between
+//     the two rows, so both factors stay at most 2;
+//   * a pair inside one tile is read at A of the key's block (dq kernel) or
+//     of the block before the query's (dk/dv kernel), again between the rows
+//     unless the two rows share a block: then one factor is at most
+//     2^(BWD_SPREAD + 1), and the pairs of a flagged block are left to the
+//     pair-by-pair kernel of wall_bwd_diag.hip, which runs first;
+//   * every move of q~ or k~ to another anchor is an exact power of two of the
+//     stored bf16 value, so each pair's product q~ k~ is the same in both
+//     kernels; the accumulators move between anchors the same way, only ever
+//     downwards (the dq kernel walks the key tiles upwards, the dk/dv kernel
+//     the query tiles after its tile first, then its own tile from the last
+//     block down).
+// A term lost to an underflowing factor is below 2^(BWD_SPREAD + 1 - 126) of
+// |dS q k| for the rows it belongs to.
 //
 // dk/dv (per key block, queries from the block's first key on; 8 waves):
 //   dk waves  S = q~ k~^T, dP = do v^T (32 streamed queries x the wave's 32
@@ -42,18 +62,20 @@
 // whose terms cancel pair by pair: the pair (i, j) adds dS_ij q~_i k~_j to X_i
 // and takes it from X_j.  The kernels therefore form both sides from the
 // same bf16 q~ and k~ the products use, ln2 q~_i (.) sum_j dS_ij k~_j and
-// ln2 k~_j (.) sum_i dS_ij q~_i (the anchors of the two kernels differ by
-// integers, which moves q~ and k~ by exact powers of two), so the rounding of
-// the operands cancels in the sums as the exact terms do.  Built from the
-// unrounded q and k instead, each pair would leave a residue of the operand
-// rounding (2^-9 relative), and over a long sequence these residues add up
-// to several times the error of dq and dk themselves.
+// ln2 k~_j (.) sum_i dS_ij q~_i at the accumulators' final anchors (all
+// anchors are integers, which moves q~ and k~ by exact powers of two), so the
+// rounding of the operands cancels in the sums as the exact terms do.  Built
+// from the unrounded q and k instead, each pair would leave a residue of the
+// operand rounding (2^-9 relative), and over a long sequence these residues
+// add up to several times the error of dq and dk themselves.
 //
 // A block handles a single query head, so dk and dv leave as float32 per
 // query head partials, summed over the heads of a kv group by
 // bwd_reduce_kernel.  The dk/dv kernel also subtracts k (.) dk^(hq) and the
 // column sums of dS from the X and Y rows the dq kernel wrote (it runs after
-// it on the same stream).
+// it on the same stream).  For the rows of a flagged block both kernels add
+// the pair-by-pair kernel's parts (dqd, dkp, dvp, X, Y) instead of
+// overwriting them.
 #include <float.h>
 
 #include <type_traits>
@@ -115,51 +137,83 @@ __device__ inline BlockPos block_pos(const BwdArgs &a, int nblk, bool heavy_firs
     return p;
 }
 
-// ---------------------------------------------------------------- tile anchors, q~ and k~
-// Per (128-row tile, query head): R = floor(P) at the tile's middle row, and
-// every row's q~ = q scale log2e 2^(P - R) and k~ = k 2^(R - P) in bf16.  The
-// dq and dk/dv kernels use their own tile's rows as they are and move a
-// streamed tile to their block's anchor by the integer difference of the two
-// anchors: an exact power of two, applied with v_ldexp_f32 instead of an
-// exp2 per element.
+// ---------------------------------------------------------------- block anchors, q~ and k~
+// Per (128-row tile, query head): the anchors A_b of its four 32-row blocks,
+// every row's q~ = q scale log2e 2^(P - A_(b-1)) and k~ = k 2^(A_b - P) in bf16,
+// and the spread flags (sequence + 1 for a flagged block, else 0).  The dq and
+// dk/dv kernels move these rows to other anchors by integer differences of
+// anchors: exact powers of two, applied with v_ldexp_f32.
 template <int K>
 __global__ __launch_bounds__(256) void bwd_anchor_kernel(BwdArgs a, int nblk) {
-    __shared__ float sR[K];
+    constexpr int NBK = BR / BWD_BLK;
+    __shared__ float sA[NBK + 1][K];  // A_(first - 1), A_first .. A_(first + 3)
+    __shared__ int sflag;
     // one block per (tile of a sequence, query head), tiles fastest
-    const int tile = blockIdx.x % nblk, hs = blockIdx.x / nblk, hq = hs % a.HQ;
-    const SegInfo sg = a.seg[hs / a.HQ];
+    const int tile = blockIdx.x % nblk, hs = blockIdx.x / nblk, hq = hs % a.HQ, sidx = hs / a.HQ;
+    const SegInfo sg = a.seg[sidx];
     const int r0 = tile * BR;
     if (r0 >= sg.len) return;
     const int n = min(BR, sg.len - r0), tid = threadIdx.x;
     const int64_t HQ = a.HQ, s0 = sg.start;
     const int h = hq / (a.HQ / a.H);
+    const int64_t gb0 = (int64_t)(sg.tile_base + tile) * NBK;
+    if (tid == 0) sflag = 0;
     if (tid < K) {
-        const float R = floorf(a.P[(s0 + r0 + min(ANCHOR_ROW, n - 1)) * HQ * K + hq * K + tid]);
-        sR[tid] = R;
-        a.Rt[((int64_t)(sg.tile_base + tile) * HQ + hq) * K + tid] = R;
+        const float *Pc = a.P + hq * K + tid;
+        sA[0][tid] = r0 > 0 ? floorf(Pc[(s0 + r0 - 1) * HQ * K]) : 0.f;
+#pragma unroll
+        for (int b = 0; b < NBK; ++b) {
+            if (BWD_BLK * b >= n) break;
+            const float A = floorf(Pc[(s0 + r0 + min(BWD_BLK * b + BWD_BLK - 1, n - 1)) * HQ * K]);
+            sA[b + 1][tid] = A;
+            a.Ab[((gb0 + b) * HQ + hq) * K + tid] = A;
+        }
     }
     __syncthreads();
     const __bf16 *qg = static_cast<const __bf16 *>(a.q);
     const __bf16 *kg = static_cast<const __bf16 *>(a.k);
     __bf16 *qh = static_cast<__bf16 *>(a.qh);
     __bf16 *kh = static_cast<__bf16 *>(a.kh);
+    int spread = 0;
     for (int c = tid; c < n * (K / 8); c += 256) {
-        const int r = c / (K / 8), ch = 8 * (c % (K / 8));
+        const int r = c / (K / 8), ch = 8 * (c % (K / 8)), b = r / BWD_BLK;
         const int64_t t = s0 + r0 + r, ix = (t * HQ + hq) * K + ch;
         const f32x8 qq = to_f32(*reinterpret_cast<const uint4 *>(qg + ix));
         const f32x8 kk = to_f32(*reinterpret_cast<const uint4 *>(kg + (t * a.H + h) * K + ch));
         const f32x4 *pp = reinterpret_cast<const f32x4 *>(a.P + ix);
         const f32x4 p0 = pp[0], p1 = pp[1];
         f32x8 xq, xk;
+        bool far = false;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const float pv = e < 4 ? p0[e] : p1[e - 4];
-            xq[e] = qq[e] * a.qscale * clamp2(pv - sR[ch + e]);
-            xk[e] = kk[e] * clamp2(sR[ch + e] - pv);
+            const float Ap = sA[b][ch + e], Ao = sA[b + 1][ch + e];
+            xq[e] = qq[e] * a.qscale * clamp2(pv - Ap);
+            xk[e] = kk[e] * clamp2(Ao - pv);
+            far = far || fabsf(pv - Ap) > BWD_SPREAD || fabsf(pv - Ao) > BWD_SPREAD;
         }
+        if (far) spread |= 1 << b;
         *reinterpret_cast<bf16x8 *>(qh + ix) = __builtin_convertvector(xq, bf16x8);
         *reinterpret_cast<bf16x8 *>(kh + ix) = __builtin_convertvector(xk, bf16x8);
     }
+    if (spread) atomicOr(&sflag, spread);
+    __syncthreads();
+    // all four entries of the tile, also those of blocks past a short tail (0)
+    if (tid < NBK) a.flag[(gb0 + tid) * HQ + hq] = (BWD_BLK * tid < n && ((sflag >> tid) & 1)) ? sidx + 1 : 0;
+}
+
+// x * 2^d per element for integer-valued d: an exact power of two of a bf16
+// value, rounded back to bf16 (exact unless it leaves the normal range)
+__device__ inline bf16x8 scale8(bf16x8 x, f32x8 d) {
+    const f32x8 f = __builtin_convertvector(x, f32x8);
+    f32x8 y;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = ldexpf(f[e], (int)fminf(fmaxf(d[e], -1000.0f), 1000.0f));
+    return __builtin_convertvector(y, bf16x8);
+}
+__device__ inline f32x8 lds_f8(const float *p) {
+    const f32x4 a = *reinterpret_cast<const f32x4 *>(p), b = *reinterpret_cast<const f32x4 *>(p + 4);
+    return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
 // 2^(to - from) applied to an anchored value: from, to are integer anchors
@@ -183,6 +237,7 @@ template <int K, int V, bool HAS_G>
 __global__ __launch_bounds__(NTH_KV) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
     constexpr int RPK = K + 8, RPV = V + 8;
     constexpr int CK = BT * K / 8, CV = BT * V / 8;  // 8-element chunks per tile
+    constexpr int NBK = BR / BWD_BLK;
     // the four dv waves stage the tiles (NTH threads)
     constexpr int UK = (CK + NTH - 1) / NTH, UV = (CV + NTH - 1) / NTH;
     // two buffers of each streamed tile: one read while the other is filled
@@ -194,7 +249,9 @@ __global__ __launch_bounds__(NTH_KV) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
     __shared__ __attribute__((aligned(16))) float sL[2][BT];
     __shared__ __attribute__((aligned(16))) float sD[2][BT];
     __shared__ __attribute__((aligned(16))) float sGq[2][BT];
-    __shared__ float sR[K];
+    // anchors: sA[0] = A of the block before the tile, sA[1 + b] = A of its block b
+    __shared__ __attribute__((aligned(16))) float sA[NBK + 1][K];
+    __shared__ int sFl[NBK];
 
     const BlockPos bp = block_pos(a, nblk, true);
     const SegInfo sg = a.seg[bp.seg];
@@ -205,32 +262,50 @@ __global__ __launch_bounds__(NTH_KV) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
     const int h = hq / (a.HQ / a.H);
     const int len = sg.len, jn = min(BR, len - j0);
     const int64_t s0 = sg.start;
+    const int64_t gb0 = (int64_t)(sg.tile_base + bp.rb) * NBK;
     const __bf16 *vg = static_cast<const __bf16 *>(a.v);
     const __bf16 *dog = static_cast<const __bf16 *>(a.dout);
 
-    if (tid < K) sR[tid] = floorf(a.P[(s0 + j0 + min(ANCHOR_ROW, jn - 1)) * HQ * K + hq * K + tid]);
+    if (tid < K) {
+        sA[0][tid] = j0 > 0 ? a.Ab[((gb0 - 1) * HQ + hq) * K + tid] : 0.f;
+#pragma unroll
+        for (int b = 0; b < NBK; ++b)
+            if (BWD_BLK * b < jn) sA[b + 1][tid] = a.Ab[((gb0 + b) * HQ + hq) * K + tid];
+    }
+    if (tid < NBK) sFl[tid] = BWD_BLK * tid < jn ? a.flag[(gb0 + tid) * HQ + hq] : 0;
     __syncthreads();
 
     const int qend = a.window > 0 ? min(len, j0 + jn - 1 + a.window) : len;
+    // Query tiles in the order the dk accumulators need: those after the key
+    // tile (read at A of its last block, sA[NBK]), then the tile's own blocks
+    // from the last down (own block bq read at the stored anchor of its q~).
+    const int n_off = qend > j0 + BR ? (qend - j0 - BR + BT - 1) / BT : 0;
+    const int n_dg = (min(qend, j0 + jn) - j0 + BT - 1) / BT;
+    const int ntl = n_off + n_dg;
+    auto tile_q0 = [&](int it) { return it < n_off ? j0 + BR + BT * it : j0 + BT * (ntl - 1 - it); };
 
     const __bf16 *qhg = static_cast<const __bf16 *>(a.qh);
     const __bf16 *khg = static_cast<const __bf16 *>(a.kh);
-    // prefetch registers for one tile: q~ at its own tile's anchor and that anchor
+    // prefetch registers for one tile: q~ at its stored anchor and that anchor
     uint4 qraw[UK], oraw[UV];
     f32x8 araw[UK];
     float il = 0.f, id = 0.f, ig = 0.f;
     const int sid = tid - NTH;  // staging thread index (dv waves)
-    auto load_tile = [&](int q0) {
+    auto load_tile = [&](int it) {
+        const int q0 = tile_q0(it);
+        // the anchor of the block before the tile's rows (a tile after the key tile only)
+        const float *ab = a.Ab + ((gb0 + q0 / BWD_BLK - bp.rb * NBK - 1) * HQ + hq) * K;
         // rows past the sequence load its last row (in bounds) and are zeroed when stored
-        const float *rt = a.Rt + ((int64_t)(sg.tile_base + q0 / BR) * HQ + hq) * K;
 #pragma unroll
         for (int u = 0; u < UK; ++u) {
             const int c = sid + NTH * u, r = c % BT, ch = 8 * (c / BT), i = min(q0 + r, len - 1);
             if (CK % NTH == 0 || c < CK) {
                 qraw[u] = *reinterpret_cast<const uint4 *>(qhg + ((s0 + i) * HQ + hq) * K + ch);
-                const f32x4 *pp = reinterpret_cast<const f32x4 *>(rt + ch);
-                const f32x4 p0 = pp[0], p1 = pp[1];
-                araw[u] = f32x8{p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+                if (it < n_off) {
+                    const f32x4 *pp = reinterpret_cast<const f32x4 *>(ab + ch);
+                    const f32x4 p0 = pp[0], p1 = pp[1];
+                    araw[u] = f32x8{p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+                }
             }
         }
 #pragma unroll
@@ -250,15 +325,17 @@ __global__ __launch_bounds__(NTH_KV) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
             }
         }
     };
-    auto store_tile = [&](int buf, int q0, int tix) {
+    auto store_tile = [&](int buf, int it, int tix) {
+        const int q0 = tile_q0(it);
 #pragma unroll
         for (int u = 0; u < UK; ++u) {
             const int c = sid + NTH * u, r = c % BT, ch = 8 * (c / BT);
             if (CK % NTH == 0 || c < CK) {
-                const f32x8 qq = to_f32(qraw[u]);
-                f32x8 x;
+                f32x8 x = to_f32(qraw[u]);
+                if (it < n_off) {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) x[e] = shift_anchor(qq[e], araw[u][e], sR[ch + e]);
+                    for (int e = 0; e < 8; ++e) x[e] = shift_anchor(x[e], araw[u][e], sA[NBK][ch + e]);
+                }
                 if (q0 + r >= len) x = 0.f;
                 const bf16x8 b = __builtin_convertvector(x, bf16x8);
                 *reinterpret_cast<bf16x8 *>(&sQ[buf][roff<RPK>(r, ch / 8)]) = b;
@@ -290,17 +367,17 @@ __global__ __launch_bounds__(NTH_KV) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
     // barrier per tile.
     const bool stager = w >= NW;
     if (stager) {
-        load_tile(j0);
-        store_tile(0, j0, 0);
+        load_tile(0);
+        store_tile(0, 0, 0);
     }
     __syncthreads();
-    if (stager && j0 + BT < qend) load_tile(j0 + BT);
+    if (stager && 1 < ntl) load_tile(1);
 
     // One role's whole walk over the query tiles; the two instantiations keep
-    // their accumulators apart.  Every wave runs every tile: a tile with no
-    // visible pair for its keys (at most the first three, or three past the
-    // window) is masked to zero, and the accumulators stay on one straight
-    // path through the loop.
+    // their accumulators apart.  Every wave runs every tile after the key
+    // tile (a tile with no visible pair for its keys, at most three past the
+    // window, is masked to zero) and, of its own tile, the blocks at or after
+    // its keys' block, except that block itself when it is flagged.
     auto walk = [&](auto dk_role) {
         constexpr bool DK = decltype(dk_role)::value;
         constexpr int NA = DK ? K / 32 : V / 32;
@@ -308,6 +385,13 @@ __global__ __launch_bounds__(NTH_KV) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
         const int jw = j0 + 32 * wr, j = jw + l32;
         const bool jok = j < len;
         const int64_t tj = s0 + (jok ? j : 0);
+        const bool flagged = sFl[wr] != 0;
+        // the own-tile block of tile it (or -1), and whether this wave computes it
+        auto own_block = [&](int it) { return it < n_off ? -1 : ntl - 1 - it; };
+        auto active = [&](int it) {
+            const int bq = own_block(it);
+            return bq < 0 || bq > wr || (bq == wr && !flagged);
+        };
         f32x16 acc[NA];
 #pragma unroll
         for (int n = 0; n < NA; ++n) acc[n] = 0.f;
@@ -323,18 +407,21 @@ __global__ __launch_bounds__(NTH_KV) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
                     acc[n] = mfma(pb[c], lds8(&sOT[tix % 3][(32 * n + l32) * TP + 16 * c + 8 * hl]), acc[n]);
         };
         float colsum = 0.f;
-        int it = 0;
+        // anchor index (into sA) of the dk accumulators, -1 before the first tile
+        int fa = -1;
         if constexpr (DK) {
-            // the wave's keys as second operands: k~ (its own tile's anchor is the
-            // block's) and v rows of key j
-            bf16x8 kop[K / 16], vop[V / 16];
+            // the wave's keys as second operands: k~ at its block's anchor (moved to
+            // the anchor of each tile) and v rows of key j
+            auto load_k = [&](bf16x8 *kv) {
 #pragma unroll
-            for (int s = 0; s < K / 16; ++s) {
-                const int ch = 16 * s + 8 * hl;
-                uint4 raw = {0, 0, 0, 0};
-                if (jok) raw = *reinterpret_cast<const uint4 *>(khg + (tj * HQ + hq) * K + ch);
-                kop[s] = __builtin_bit_cast(bf16x8, raw);
-            }
+                for (int s = 0; s < K / 16; ++s) {
+                    const int ch = 16 * s + 8 * hl;
+                    uint4 raw = {0, 0, 0, 0};
+                    if (jok) raw = *reinterpret_cast<const uint4 *>(khg + (tj * HQ + hq) * K + ch);
+                    kv[s] = __builtin_bit_cast(bf16x8, raw);
+                }
+            };
+            bf16x8 vop[V / 16];
 #pragma unroll
             for (int s = 0; s < V / 16; ++s) {
                 const int ch = 16 * s + 8 * hl;
@@ -342,17 +429,37 @@ __global__ __launch_bounds__(NTH_KV) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
                 if (jok) raw = *reinterpret_cast<const uint4 *>(vg + (tj * a.H + h) * V + ch);
                 vop[s] = __builtin_bit_cast(bf16x8, raw);
             }
+            // 8 channels at channel block s times 2^(sA[p] - sA[m])
+            auto move = [&](bf16x8 v8, int s, int p, int m) {
+                const int ch = 16 * s + 8 * hl;
+                return scale8(v8, lds_f8(&sA[p][ch]) - lds_f8(&sA[m][ch]));
+            };
+            // the accumulators at anchor sA[x]: acc(x) = acc(fa) 2^(sA[fa] - sA[x])
+            // (at most 1 for a falling prefix: x only rises)
+            auto acc_to = [&](int x) {
+                if (fa >= 0) {
+#pragma unroll
+                    for (int n = 0; n < NA; ++n) {
+                        const int d = (int)fminf(fmaxf(sA[fa][32 * n + l32] - sA[x][32 * n + l32], -1000.f), 1000.f);
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) acc[n][r] = ldexpf(acc[n][r], d);
+                    }
+                }
+                fa = x;
+            };
             const float gj = (HAS_G && jok) ? a.G[tj * HQ + hq] : 0.f;
-            for (int q0 = j0; q0 < qend; q0 += BT, ++it) {
+            // one query tile: S, dP, A, dS and dk += dS^T q~; S from the wave's k~
+            // operands kget and the staged q~ rows passed through qget
+            auto tile = [&](int it, auto kget, auto qget) {
                 const int cur = it & 1;
+                const int q0 = tile_q0(it);
                 const int qrow = swap23(l32);
                 f32x16 S = 0.f, dP = 0.f;
 #pragma unroll
                 for (int s = 0; s < K / 16; ++s)
-                    S = mfma(lds8(&sQ[cur][roff<RPK>(qrow, 2 * s + hl)]), kop[s], S);
+                    S = mfma(qget(lds8(&sQ[cur][roff<RPK>(qrow, 2 * s + hl)]), s), kget(s), S);
 #pragma unroll
-                for (int s = 0; s < V / 16; ++s)
-                    dP = mfma(lds8(&sO[cur][roff<RPV>(qrow, 2 * s + hl)]), vop[s], dP);
+                for (int s = 0; s < V / 16; ++s) dP = mfma(lds8(&sO[cur][roff<RPV>(qrow, 2 * s + hl)]), vop[s], dP);
                 // every pair of the tile visible: no mask
                 const bool full = jw + 31 < len && q0 >= jw + 31 && q0 + BT <= len &&
                                   (a.window <= 0 || q0 + BT - 1 - jw < a.window);
@@ -400,17 +507,46 @@ __global__ __launch_bounds__(NTH_KV) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
 #pragma unroll
                     for (int c = 0; c < 2; ++c)
                         acc[n] = mfma(db[c], lds8(&sQT[cur][(32 * n + l32) * TP + 16 * c + 8 * hl]), acc[n]);
-                __syncthreads();
+            };
+            // The query tiles after the key tile at sA[NBK], with k~ moved there
+            // once; then the own tile's blocks bq: S at the stored k~'s anchor
+            // sA[wr + 1], the staged q~ (at sA[bq]) moved there as it is read,
+            // and dk += dS^T q~ at sA[bq].  Each loop holds one set of k~ registers.
+            int it = 0;
+            if (n_off > 0) {
+                bf16x8 kop[K / 16];
+                load_k(kop);
+#pragma unroll
+                for (int s = 0; s < K / 16; ++s) kop[s] = move(kop[s], s, NBK, wr + 1);
+                acc_to(NBK);
+                for (; it < n_off; ++it) {
+                    tile(it, [&](int s) { return kop[s]; }, [&](bf16x8 x, int) { return x; });
+                    __syncthreads();
+                }
+            }
+            {
+                bf16x8 kst[K / 16];
+                load_k(kst);
+                for (; it < ntl; ++it) {
+                    if (active(it)) {
+                        const int x = own_block(it);
+                        acc_to(x);
+                        // q~ 2^(sA[x] - sA[wr + 1]): at most 1 for a later block
+                        tile(it, [&](int s) { return kst[s]; },
+                             [&](bf16x8 qv, int s) { return move(qv, s, x, wr + 1); });
+                    }
+                    __syncthreads();
+                }
             }
         } else {
             // one tile behind the dk waves; these waves also stage every tile
-            for (int q0 = j0; q0 < qend; q0 += BT, ++it) {
-                if (it > 0) dv_step(it - 1);
-                if (q0 + BT < qend) store_tile((it & 1) ^ 1, q0 + BT, it + 1);
+            for (int it = 0; it < ntl; ++it) {
+                if (it > 0 && active(it - 1)) dv_step(it - 1);
+                if (it + 1 < ntl) store_tile((it & 1) ^ 1, it + 1, it + 1);
                 __syncthreads();
-                if (q0 + 2 * BT < qend) load_tile(q0 + 2 * BT);
+                if (it + 2 < ntl) load_tile(it + 2);
             }
-            if (it > 0) dv_step(it - 1);
+            if (ntl > 0 && active(ntl - 1)) dv_step(ntl - 1);
         }
 
         if (jw >= len) return;
@@ -418,6 +554,8 @@ __global__ __launch_bounds__(NTH_KV) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
             colsum += __shfl_xor(colsum, 32);
             if (hl == 0 && jok) a.Y[tj * HQ + hq] -= colsum;
         }
+        // the dk accumulators' anchor (the key block's own with none)
+        const int fx = fa >= 0 ? fa : wr + 1;
         // accumulator register r of lane (l32, hl): key jw + 8(r/4) + 4hl + r%4, channel 32n + l32
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -429,11 +567,15 @@ __global__ __launch_bounds__(NTH_KV) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
                 const int ch = 32 * n + l32;
                 if constexpr (DK) {
                     const int64_t ix = (t * HQ + hq) * K + ch;
-                    a.dkp[ix] = LN2 * clamp2(sR[ch] - a.P[ix]) * acc[n][r];
+                    const float F = sA[fx][ch];
+                    float dk = LN2 * clamp2(F - a.P[ix]) * acc[n][r];
+                    if (flagged) dk += a.dkp[ix];
+                    a.dkp[ix] = dk;
                     // k (.) dk^(hq) from the bf16 k~ the dq products used (see the X note above)
-                    a.X[ix] -= LN2 * (float)khg[ix] * acc[n][r];
+                    a.X[ix] -= LN2 * shift_anchor((float)khg[ix], F, sA[wr + 1][ch]) * acc[n][r];
                 } else {
-                    a.dvp[(t * HQ + hq) * V + ch] = acc[n][r];
+                    const int64_t ix = (t * HQ + hq) * V + ch;
+                    a.dvp[ix] = flagged ? a.dvp[ix] + acc[n][r] : acc[n][r];
                 }
             }
         }
@@ -450,12 +592,15 @@ __global__ __launch_bounds__(NTH, 2) void bwd_dq_mfma(BwdArgs a, int nblk) {
     constexpr int RPK = K + 8, RPV = V + 8;
     constexpr int CK = BT * K / 8, CV = BT * V / 8;
     constexpr int UK = CK / NTH, UV = CV / NTH;
+    constexpr int NBK = BR / BWD_BLK;
     static_assert(CK % NTH == 0 && CV % NTH == 0, "tile chunks");
     __shared__ __attribute__((aligned(16))) __bf16 sK[2][rows_size<RPK>()];  // k~ rows
     __shared__ __attribute__((aligned(16))) __bf16 sKT[2][K * TP];           // k~ transposed
     __shared__ __attribute__((aligned(16))) __bf16 sV[2][rows_size<RPV>()];  // v rows
     __shared__ __attribute__((aligned(16))) float sGk[2][BT];
-    __shared__ float sR[K];
+    // anchors: sA[0] = A of the block before the tile, sA[1 + b] = A of its block b
+    __shared__ __attribute__((aligned(16))) float sA[NBK + 1][K];
+    __shared__ int sFl[NBK];
 
     const BlockPos bp = block_pos(a, nblk, false);
     const SegInfo sg = a.seg[bp.seg];
@@ -466,27 +611,37 @@ __global__ __launch_bounds__(NTH, 2) void bwd_dq_mfma(BwdArgs a, int nblk) {
     const int h = hq / (a.HQ / a.H);
     const int len = sg.len, in_ = min(BR, len - i0);
     const int64_t s0 = sg.start;
+    const int64_t gb0 = (int64_t)(sg.tile_base + bp.rb) * NBK;
     const __bf16 *vg = static_cast<const __bf16 *>(a.v);
     const __bf16 *dog = static_cast<const __bf16 *>(a.dout);
 
-    if (tid < K) sR[tid] = floorf(a.P[(s0 + i0 + min(ANCHOR_ROW, in_ - 1)) * HQ * K + hq * K + tid]);
+    if (tid < K) {
+        sA[0][tid] = i0 > 0 ? a.Ab[((gb0 - 1) * HQ + hq) * K + tid] : 0.f;
+#pragma unroll
+        for (int b = 0; b < NBK; ++b)
+            if (BWD_BLK * b < in_) sA[b + 1][tid] = a.Ab[((gb0 + b) * HQ + hq) * K + tid];
+    }
+    if (tid < NBK) sFl[tid] = BWD_BLK * tid < in_ ? a.flag[(gb0 + tid) * HQ + hq] : 0;
     __syncthreads();
 
     // the wave's queries as second operands
     const int iw = i0 + 32 * w, i = iw + l32;
     const bool iok = i < len;
     const int64_t ti = s0 + (iok ? i : 0);
+    const bool flagged = sFl[w] != 0;
     const __bf16 *qhg = static_cast<const __bf16 *>(a.qh);
     const __bf16 *khg = static_cast<const __bf16 *>(a.kh);
-    // the block is one tile: its rows' q~ are at the block's anchor already
-    bf16x8 qop[K / 16], oop[V / 16];
+    // q~ as stored (at sA[w], the anchor of the block before the wave's)
+    auto load_q = [&](bf16x8 *qv) {
 #pragma unroll
-    for (int s = 0; s < K / 16; ++s) {
-        const int ch = 16 * s + 8 * hl;
-        uint4 raw = {0, 0, 0, 0};
-        if (iok) raw = *reinterpret_cast<const uint4 *>(qhg + (ti * HQ + hq) * K + ch);
-        qop[s] = __builtin_bit_cast(bf16x8, raw);
-    }
+        for (int s = 0; s < K / 16; ++s) {
+            const int ch = 16 * s + 8 * hl;
+            uint4 raw = {0, 0, 0, 0};
+            if (iok) raw = *reinterpret_cast<const uint4 *>(qhg + (ti * HQ + hq) * K + ch);
+            qv[s] = __builtin_bit_cast(bf16x8, raw);
+        }
+    };
+    bf16x8 oop[V / 16];
 #pragma unroll
     for (int s = 0; s < V / 16; ++s) {
         const int ch = 16 * s + 8 * hl;
@@ -502,25 +657,48 @@ __global__ __launch_bounds__(NTH, 2) void bwd_dq_mfma(BwdArgs a, int nblk) {
 #pragma unroll
     for (int n = 0; n < K / 32; ++n) dq[n] = 0.f;
     float rowsum = 0.f;
+    // anchor index (into sA) of the accumulators, -1 before the first tile;
+    // acc(x) = acc(fa) 2^(sA[x] - sA[fa]) (at most 1 for a falling prefix: x only falls)
+    int fa = -1;
+    auto acc_to = [&](int x) {
+        if (fa >= 0) {
+#pragma unroll
+            for (int n = 0; n < K / 32; ++n) {
+                const int d = (int)fminf(fmaxf(sA[x][32 * n + l32] - sA[fa][32 * n + l32], -1000.f), 1000.f);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) dq[n][r] = ldexpf(dq[n][r], d);
+            }
+        }
+        fa = x;
+    };
+    // 8 channels of q~ (or k~) at anchor sA[to] from anchor sA[from]: x 2^(sA[from] - sA[to])
+    // for q~, x 2^(sA[to] - sA[from]) for k~
+    auto lower_q = [&](bf16x8 x, int s, int from, int to) {
+        const int ch = 16 * s + 8 * hl;
+        return scale8(x, lds_f8(&sA[from][ch]) - lds_f8(&sA[to][ch]));
+    };
 
     const int ilast = i0 + in_ - 1;
     const int klo = a.window > 0 ? max(0, i0 - a.window + 1) / BT * BT : 0;
 
-    // prefetch registers for one tile: k~ at its own tile's anchor and that anchor
+    // prefetch registers for one tile: k~ at its block's anchor and that anchor
     uint4 kraw[UK], vraw[UV];
     f32x8 araw[UK];
     float kgv = 0.f;
     auto load_tile = [&](int k0) {
+        // a tile before the query tile moves to sA[0]: the anchor of its block
+        const float *ab = a.Ab + ((gb0 - bp.rb * NBK + k0 / BWD_BLK) * HQ + hq) * K;
         // rows past the sequence load its last row (in bounds) and are zeroed when stored
-        const float *rt = a.Rt + ((int64_t)(sg.tile_base + k0 / BR) * HQ + hq) * K;
 #pragma unroll
         for (int u = 0; u < UK; ++u) {
             const int c = tid + NTH * u, r = c % BT, ch = 8 * (c / BT);
             const int64_t t = s0 + min(k0 + r, len - 1);
             kraw[u] = *reinterpret_cast<const uint4 *>(khg + (t * HQ + hq) * K + ch);
-            const f32x4 *pp = reinterpret_cast<const f32x4 *>(rt + ch);
-            const f32x4 p0 = pp[0], p1 = pp[1];
-            araw[u] = f32x8{p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+            if (k0 < i0) {
+                const f32x4 *pp = reinterpret_cast<const f32x4 *>(ab + ch);
+                const f32x4 p0 = pp[0], p1 = pp[1];
+                araw[u] = f32x8{p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+            }
         }
 #pragma unroll
         for (int u = 0; u < UV; ++u) {
@@ -536,10 +714,11 @@ __global__ __launch_bounds__(NTH, 2) void bwd_dq_mfma(BwdArgs a, int nblk) {
 #pragma unroll
         for (int u = 0; u < UK; ++u) {
             const int c = tid + NTH * u, r = c % BT, ch = 8 * (c / BT);
-            const f32x8 kk = to_f32(kraw[u]);
-            f32x8 x;
+            f32x8 x = to_f32(kraw[u]);
+            if (k0 < i0) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = shift_anchor(kk[e], sR[ch + e], araw[u][e]);
+                for (int e = 0; e < 8; ++e) x[e] = shift_anchor(x[e], sA[0][ch + e], araw[u][e]);
+            }
             if (k0 + r >= len) x = 0.f;
             const bf16x8 b = __builtin_convertvector(x, bf16x8);
             *reinterpret_cast<bf16x8 *>(&sK[buf][roff<RPK>(r, ch / 8)]) = b;
@@ -549,31 +728,31 @@ __global__ __launch_bounds__(NTH, 2) void bwd_dq_mfma(BwdArgs a, int nblk) {
 #pragma unroll
         for (int u = 0; u < UV; ++u) {
             const int c = tid + NTH * u, r = c % BT, ch = 8 * (c / BT);
-            const uint4 z = {0, 0, 0, 0};
-            *reinterpret_cast<uint4 *>(&sV[buf][roff<RPV>(r, ch / 8)]) = k0 + r < len ? vraw[u] : z;
+            // a row past the sequence stores zeros (selected per dword, in registers)
+            const bool ok = k0 + r < len;
+            uint4 vv = vraw[u];
+            vv.x = ok ? vv.x : 0u;
+            vv.y = ok ? vv.y : 0u;
+            vv.z = ok ? vv.z : 0u;
+            vv.w = ok ? vv.w : 0u;
+            *reinterpret_cast<uint4 *>(&sV[buf][roff<RPV>(r, ch / 8)]) = vv;
         }
         if (HAS_G && tid < BT) sGk[buf][tid] = kgv;
     };
 
-    // double-buffered as in the dk/dv kernel
-    load_tile(klo);
-    store_tile(0, klo);
-    __syncthreads();
-    if (klo + BT <= ilast) load_tile(klo + BT);
-    for (int k0 = klo, it = 0; k0 <= ilast; k0 += BT, ++it) {
-        const int cur = it & 1;
-        // every wave runs every tile, as in the dk/dv kernel
-        {
+    // one key tile: S, dP, dS and dq += dS k~; S from the wave's q~ operands
+    // qget and the staged k~ rows passed through kget
+    auto tile = [&](int k0, int cur, auto qget, auto kget) {
         f32x16 S = 0.f, dP = 0.f;
         const int krow = swap23(l32);
 #pragma unroll
-        for (int s = 0; s < K / 16; ++s) S = mfma(lds8(&sK[cur][roff<RPK>(krow, 2 * s + hl)]), qop[s], S);
+        for (int s = 0; s < K / 16; ++s)
+            S = mfma(kget(lds8(&sK[cur][roff<RPK>(krow, 2 * s + hl)]), s), qget(s), S);
 #pragma unroll
         for (int s = 0; s < V / 16; ++s) dP = mfma(lds8(&sV[cur][roff<RPV>(krow, 2 * s + hl)]), oop[s], dP);
 
         // every pair of the tile visible: no mask
-        const bool full = iw + 31 < len && k0 + BT - 1 <= iw &&
-                          (a.window <= 0 || iw + 31 - k0 < a.window);
+        const bool full = iw + 31 < len && k0 + BT - 1 <= iw && (a.window <= 0 || iw + 31 - k0 < a.window);
         bf16x8 db[2];
         auto softmax = [&](auto masked) {
 #pragma unroll
@@ -582,7 +761,7 @@ __global__ __launch_bounds__(NTH, 2) void bwd_dq_mfma(BwdArgs a, int nblk) {
                 f32x4 G4[2];
                 if (HAS_G) {
 #pragma unroll
-                    for (int x = 0; x < 2; ++x) G4[x] = *reinterpret_cast<const f32x4 *>(&sGk[cur][kj0 + 4 * x]);
+                    for (int x2 = 0; x2 < 2; ++x2) G4[x2] = *reinterpret_cast<const f32x4 *>(&sGk[cur][kj0 + 4 * x2]);
                 }
                 f32x8 d8;
 #pragma unroll
@@ -610,18 +789,59 @@ __global__ __launch_bounds__(NTH, 2) void bwd_dq_mfma(BwdArgs a, int nblk) {
 #pragma unroll
             for (int c = 0; c < 2; ++c)
                 dq[n] = mfma(db[c], lds8(&sKT[cur][(32 * n + l32) * TP + 16 * c + 8 * hl]), dq[n]);
-        }
+    };
+    auto advance = [&](int k0, int cur) {
         if (k0 + BT <= ilast) store_tile(cur ^ 1, k0 + BT);
         __syncthreads();
         if (k0 + 2 * BT <= ilast) load_tile(k0 + 2 * BT);
+    };
+
+    // double-buffered as in the dk/dv kernel.  The key tiles before the query
+    // tile at sA[0], with q~ moved there once; then the tile's own blocks b
+    // (for the waves at or after block b, the wave's own block only when it is
+    // not flagged): S at the stored q~'s anchor sA[w], the staged k~ moved
+    // there as it is read, and dq += dS k~ at the block's own anchor sA[1 + b].
+    // Each loop holds one set of q~ registers.
+    load_tile(klo);
+    store_tile(0, klo);
+    __syncthreads();
+    if (klo + BT <= ilast) load_tile(klo + BT);
+    int k0 = klo, it = 0;
+    if (k0 < i0) {
+        bf16x8 qop[K / 16];
+        load_q(qop);
+#pragma unroll
+        for (int s = 0; s < K / 16; ++s) qop[s] = lower_q(qop[s], s, w, 0);
+        acc_to(0);
+        for (; k0 < i0; k0 += BT, ++it) {
+            tile(k0, it & 1, [&](int s) { return qop[s]; }, [&](bf16x8 x, int) { return x; });
+            advance(k0, it & 1);
+        }
+    }
+    {
+        bf16x8 qst[K / 16];
+        load_q(qst);
+        for (; k0 <= ilast; k0 += BT, ++it) {
+            const int b = (k0 - i0) / BT;
+            if (b < w || (b == w && !flagged)) {
+                const int x = b + 1;
+                acc_to(x);
+                // k~ 2^(sA[w] - sA[x]): at most 1 for an earlier block
+                tile(k0, it & 1, [&](int s) { return qst[s]; },
+                     [&](bf16x8 kv, int s) { return lower_q(kv, s, w, x); });
+            }
+            advance(k0, it & 1);
+        }
     }
 
     if (iw >= len) return;
     rowsum += __shfl_xor(rowsum, 32);
     if (hl == 0 && iok) {
-        a.Y[ti * HQ + hq] = rowsum;
+        a.Y[ti * HQ + hq] = flagged ? a.Y[ti * HQ + hq] + rowsum : rowsum;
         a.Z[ti * HQ + hq] = a.sink ? -exp2f(a.sink[hq] * LOG2E - lse2) * Di : 0.f;
     }
+    // the accumulators' anchor (the stored q~'s with none)
+    const int fx = fa >= 0 ? fa : w;
     __bf16 *dqg = static_cast<__bf16 *>(a.dq);
     // accumulator register r of lane (l32, hl): query iw + 8(r/4) + 4hl + r%4, channel 32n + l32
 #pragma unroll
@@ -633,8 +853,15 @@ __global__ __launch_bounds__(NTH, 2) void bwd_dq_mfma(BwdArgs a, int nblk) {
         for (int n = 0; n < K / 32; ++n) {
             const int ch = 32 * n + l32;
             const int64_t ix = (t * HQ + hq) * K + ch;
-            dqg[ix] = (__bf16)(a.scale * clamp2(a.P[ix] - sR[ch]) * dq[n][r]);
-            a.X[ix] = LN2 * (float)qhg[ix] * dq[n][r];
+            const float F = sA[fx][ch];
+            float dqv = a.scale * clamp2(a.P[ix] - F) * dq[n][r];
+            float xv = LN2 * shift_anchor((float)qhg[ix], sA[w][ch], F) * dq[n][r];
+            if (flagged) {
+                dqv += a.dqd[ix];
+                xv += a.X[ix];
+            }
+            dqg[ix] = (__bf16)dqv;
+            a.X[ix] = xv;
         }
     }
 }
@@ -673,6 +900,9 @@ hipError_t run(const BwdArgs &a, hipStream_t st) {
     const unsigned nb = (unsigned)((int64_t)a.HQ * a.nseg * nblk);
     hipLaunchKernelGGL((bwd_anchor_kernel<K>), dim3(nb), dim3(256), 0, st, a, nblk);
     hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // the pairs inside flagged blocks, before the kernels that add them
+    e = launch_bwd_diag(a, true, false, st);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_dq_mfma<K, V, HAS_G>), dim3(nb), dim3(NTH), 0, st, a, nblk);
     e = hipGetLastError();

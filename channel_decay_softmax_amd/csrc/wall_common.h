@@ -20,10 +20,8 @@ typedef __attribute__((ext_vector_type(16))) float f32x16;
 // ----------------------------------------------------------------- geometry
 // Rows of one key / query tile.  The forward anchors the keys of a tile per
 // query head and per channel at the floored prefix of the tile's last row
-// (for the queries of later tiles); the backward anchors its 128-row blocks
-// at their middle row (ANCHOR_ROW).
+// (for the queries of later tiles).
 constexpr int TILE = 128;
-constexpr int ANCHOR_ROW = 64;
 // Rows per chunk of the two-level prefix scan.
 constexpr int SCAN_CHUNK = 128;
 
@@ -199,25 +197,43 @@ struct BwdArgs {
     void *dq, *dk, *dv;                // in dtype
     float *dsink;                      // [HQ] or null
     float *D, *X, *Y, *Z;              // workspace: do.o; q.dq - k.dk per head; dS row - column sums; sink terms
-    float *dkp, *dvp;                  // workspace: per query head dk [rows, HQ, K] and dv [rows, HQ, V] (bf16 path)
-    void *qh, *kh;                     // workspace (bf16 path): q~ and k~ [rows, HQ, K] bf16 at their own tile's anchor
-    float *Rt;                         // workspace (bf16 path): anchors [tiles, HQ, K], tile = seg.tile_base + row / 128
+    float *dkp, *dvp;                  // workspace: per query head dk [rows, HQ, K] and dv [rows, HQ, V]
+    float *dqd;                        // workspace: dq of the pairs inside one 32-row block [rows, HQ, K]
+    void *qh, *kh;                     // workspace (bf16 path): q~ and k~ [rows, HQ, K] bf16, see BWD_BLK
+    float *Ab;                         // workspace (bf16 path): block anchors [blocks, HQ, K]
+    int32_t *flag;                     // workspace (bf16 path): [blocks, HQ], sequence + 1 of a spread block, else 0
     const SegInfo *seg;
     int32_t nseg, max_seqlen, rows, HQ, H, K, V, window;
-    float scale, qscale;               // scale, scale * log2(e)
+    float scale, qscale;               // scale, scale * log2e
 };
+// The backward's anchor blocks: 32 rows, the block of row r of a sequence is
+// 4 * tile_base + r / 32.  Block b's anchor A_b is the floored prefix of its
+// last row (of the sequence's last row for a short tail block), A_(-1) = 0.
+// q~ of a row is stored at the anchor of the block before its own, k~ at its
+// own block's anchor, so either factor is at most 2 for a prefix that falls.
+// A block is spread when some channel of one of its rows lies more than
+// BWD_SPREAD log2 units from A_b or A_(b-1); pairs inside a spread block are
+// formed pair by pair, every other pair through anchors.
+constexpr int BWD_BLK = 32;
+constexpr float BWD_SPREAD = 64.0f;
 hipError_t launch_bwd_seg(SegInfo *seg, const int32_t *cu, int64_t nseg, int64_t T, hipStream_t st);
 hipError_t launch_bwd(const BwdArgs &a, bool bf16, hipStream_t st);
 hipError_t launch_bwd_mfma(const BwdArgs &a, hipStream_t st);  // the dq, dk/dv and group-sum kernels, bf16
+// pair-by-pair gradients of the pairs inside 32-row blocks: every block
+// (flags null) or the spread ones
+hipError_t launch_bwd_diag(const BwdArgs &a, bool bf16, bool all, hipStream_t st);
 // Largest value channel count the backward takes (sizes the dv partials).
 constexpr int64_t BWD_MAX_V = 128;
 
 struct BwdLayout {
-    size_t off_seg, off_D, off_X, off_Y, off_Z, off_part, off_qh, off_kh, off_rt, off_scan, total;
+    size_t off_seg, off_D, off_X, off_Y, off_Z, off_part, off_dqd, off_qh, off_kh, off_rt, off_flag, off_scan,
+        total;
 };
 inline BwdLayout bwd_layout(int64_t B, int64_t T, int64_t HQ, int64_t K, int64_t nseg) {
     BwdLayout L;
     const size_t rows = (size_t)(B * T);
+    // anchor blocks: 4 per 128-row tile, a partial tile per sequence at most
+    const size_t blocks = (size_t)(cdiv((int64_t)rows, TILE) + nseg) * (TILE / BWD_BLK);
     size_t o = 0;
     L.off_seg = o;
     o = align_up(o + sizeof(SegInfo) * (size_t)nseg, 256);
@@ -231,12 +247,16 @@ inline BwdLayout bwd_layout(int64_t B, int64_t T, int64_t HQ, int64_t K, int64_t
     o = align_up(o + sizeof(float) * rows * HQ, 256);
     L.off_part = o;
     o = align_up(o + sizeof(float) * rows * HQ * (K + BWD_MAX_V), 256);
+    L.off_dqd = o;
+    o = align_up(o + sizeof(float) * rows * HQ * K, 256);
     L.off_qh = o;
     o = align_up(o + 2 * rows * HQ * K, 256);
     L.off_kh = o;
     o = align_up(o + 2 * rows * HQ * K, 256);
     L.off_rt = o;
-    o = align_up(o + sizeof(float) * (size_t)(cdiv((int64_t)rows, TILE) + nseg) * HQ * K, 256);
+    o = align_up(o + sizeof(float) * blocks * HQ * K, 256);
+    L.off_flag = o;
+    o = align_up(o + sizeof(int32_t) * blocks * HQ, 256);
     L.off_scan = o;
     o = align_up(o + scan_layout(B, T, HQ * K).total, 256);
     L.total = o;

@@ -256,16 +256,25 @@ wall_status_t wall_attn_fwd_run(const void *q, const void *k, const void *v, wal
  *   dsink       [HQ] float32 (written; required when sink_bias is given)
  *   workspace   device scratch of at least wall_attn_bwd_workspace_size(...)
  *               bytes, 256-byte aligned, contents on entry ignored
- * Numerics: exp2(P_i - P_j) is split at integer anchors, one per 128-row
- * tile and channel at the tile's middle row, as in the forward.  bf16 inputs:
- * the five products run on bf16 matrix cores with float32 accumulation (q~,
- * k~, the probabilities and dS rounded to bf16; softmax, scaling and the
- * gate sums in float32); the q-side and k-side terms of dg are formed from
- * the same rounded q~ and k~, so their rounding cancels in dg's sums.
- * float32 inputs: every product in float32 on the vector ALUs.  Over one
- * sequence the summands of dg (and of dg_scalar) add up to zero, so the
- * suffix sums are taken as minus the exclusive prefix sums.  Deterministic
- * (no atomics).
+ * Numerics: every pair (i, j) of rows in different 32-row blocks uses the
+ * anchor identity exp2(P_i - P_j) = exp2(P_i - R) exp2(R - P_j) at an integer
+ * per-channel anchor R = floor(P) of a row between j and i (the last row of
+ * a block at or after j's and before i's), so for a prefix that falls both
+ * factors are at most 2 at any gate strength, and a factor that underflows
+ * belongs to a term below 2^-125 of |dS q k|.  The pairs inside one 32-row
+ * block use the block's own last-row anchor (one factor up to 2^65) when
+ * every row of the block lies within 64 log2 units of it and of the
+ * previous block's anchor, and are otherwise formed pair by pair in float32
+ * with one exp2 per pair and channel.  bf16 inputs: the five products run on
+ * bf16 matrix cores with float32 accumulation (q~, k~, the probabilities
+ * and dS rounded to bf16; softmax, scaling and the gate sums in float32);
+ * every move of q~, k~ or an accumulator between anchors is an exact power
+ * of two, and the q-side and k-side terms of dg are formed from the same
+ * rounded q~ and k~, so their rounding cancels in dg's sums.  float32
+ * inputs: every product in float32 on the vector ALUs, the pairs inside each
+ * 32-row block always pair by pair.  Over one sequence the summands of dg
+ * (and of dg_scalar) add up to zero, so the suffix sums are taken as minus
+ * the exclusive prefix sums.  Deterministic (no atomics on the results).
  * Errors: INVALID_ARG for a null required pointer, G without dg_scalar, a
  * sink without dsink, a size < 1, HQ % H != 0, bad cu_seqlens arguments,
  * misalignment, a short workspace; UNSUPPORTED for K or V not in {64, 128},

@@ -207,3 +207,156 @@ def test_backward_options_full_size_sampled():
         rrms = math.sqrt((rr ** 2).mean())
         say(f"  {name}: max|d|={mx:.3e} (ref max {rmax:.3e})  rms={rms:.3e} (ref rms {rrms:.3e})")
         assert mx <= tmax * rmax and rms <= trms * rrms, name
+
+
+# --------------------------------------------------------------------------- strong decay
+def _bwd_gpu(inp, do):
+    d = inp.to(DEV)
+    cu = d.cu_seqlens
+    maxlen = None if cu is None else int((cu[1:] - cu[:-1]).max().item())
+    P = wall.wall_prefix_scan(d.g, cu)
+    G = None if d.g_scalar is None else wall.wall_prefix_scan(d.g_scalar, cu)
+    o, lse = wall.wall_attn_fwd(d.q, d.k, d.v, P, G, d.sink_bias, d.scale, d.window_size, cu, maxlen)
+    grads = wall.wall_attn_bwd(d.q, d.k, d.v, P, o, lse, do.to(DEV), G, d.sink_bias, d.scale, d.window_size,
+                               cu, maxlen, g_dtype=d.g.dtype)
+    torch.cuda.synchronize()
+    return grads
+
+
+def _compare(grads, ref, dtype, names=("dq", "dk", "dv", "dg", "dg_scalar", "dsink"), q=None):
+    """Each gradient against the reference at the module's bars.  With q given,
+    dg is measured against the larger of its own size and that of the terms
+    q (.) dq it sums: under strong decay those terms cancel (dg shrinks with
+    the decay's derivative) while the rounding of their sum stays that of the
+    terms."""
+    tmax, trms = TOL[dtype]
+    for name, gg, rr in zip(names, grads, ref):
+        if rr is None:
+            assert gg is None
+            continue
+        x = f64(gg)
+        dd = np.abs(x - rr)
+        mx, rms = dd.max(), math.sqrt((dd ** 2).mean())
+        rmax, rrms = np.abs(rr).max(), math.sqrt((rr ** 2).mean())
+        if name == "dg" and q is not None:
+            terms = q * ref[0]
+            rmax, rrms = max(rmax, np.abs(terms).max()), max(rrms, math.sqrt((terms ** 2).mean()))
+        say(f"  {name}: max|d|={mx:.3e} (ref max {rmax:.3e})  rms={rms:.3e} (ref rms {rrms:.3e})")
+        assert mx <= tmax * max(rmax, 1e-30) and rms <= trms * max(rrms, 1e-30), name
+
+
+def _strong(gate, dtype, K, T=420, window=None):
+    """A strong uniform gate on every channel, two query heads of one kv head,
+    and a packed sequence start inside the first tile."""
+    inp = make_inputs("long_bf16", dtype=dtype, B=1, T=T, HQ=2, H=1, K=K, V=K)
+    inp.g = torch.full_like(inp.g, gate)
+    inp.cu_seqlens = torch.tensor([0, 37, T], dtype=torch.int32)
+    inp.window_size = window
+    return inp
+
+
+def _do(inp, seed):
+    B, T, HQ, _ = inp.q.shape
+    rng = np.random.default_rng(seed)
+    return torch.from_numpy(rng.standard_normal((B, T, HQ, inp.v.shape[3]))).to(inp.q.dtype)
+
+
+@pytest.mark.parametrize("K", [64, 128])
+@pytest.mark.parametrize("dtype", ["bfloat16", "float32"])
+@pytest.mark.parametrize("gate", [-1.5, -2.0, -5.0])
+def test_backward_strong_uniform_decay(gate, dtype, K):
+    """Gates past the reach of one anchor per 128-row tile (the prefix falls 2.2
+    to 7.2 log2 units per token, 69 to 231 per 32-row block): boundary anchors
+    for pairs in different blocks, the block's own anchor for unflagged
+    blocks, and the pair-by-pair kernel for spread ones keep every gradient
+    at the bar."""
+    inp = _strong(gate, dtype, K)
+    say(f"backward uniform g={gate} {dtype} K=V={K}")
+    do = _do(inp, 31)
+    grads = _bwd_gpu(inp, do)
+    ref = oracle.wall_attn_bwd_oracle(inp.q, inp.k, inp.v, inp.g, do, scale=inp.scale, cu_seqlens=inp.cu_seqlens)
+    _compare(grads, ref, dtype, q=f64(inp.q))
+
+
+@pytest.mark.parametrize("dtype", ["bfloat16", "float32"])
+def test_backward_strong_decay_window(dtype):
+    """g = -2 with a 50-token window and a packed start."""
+    inp = _strong(-2.0, dtype, 128, T=360, window=50)
+    say(f"backward uniform g=-2 window 50 {dtype}")
+    do = _do(inp, 33)
+    grads = _bwd_gpu(inp, do)
+    ref = oracle.wall_attn_bwd_oracle(inp.q, inp.k, inp.v, inp.g, do, scale=inp.scale, window_size=50,
+                                      cu_seqlens=inp.cu_seqlens)
+    _compare(grads, ref, dtype, q=f64(inp.q))
+
+
+def test_backward_strong_and_slow_channels():
+    """Half the channels forget at -3 nats per token, half at -0.01: every block
+    is spread, while the slow channels carry the gradients across tiles."""
+    inp = make_inputs("long_bf16", B=1, T=700, HQ=4, H=2)
+    g = torch.full(inp.g.shape, -0.01, dtype=torch.float64)
+    g[..., 64:] = -3.0
+    inp.g = g.to(inp.g.dtype)
+    say("backward channels at -3 and -0.01")
+    do = _do(inp, 35)
+    grads = _bwd_gpu(inp, do)
+    ref = oracle.wall_attn_bwd_oracle(inp.q, inp.k, inp.v, inp.g, do, scale=inp.scale)
+    _compare(grads, ref, "bfloat16", q=f64(inp.q))
+
+
+def test_backward_one_spread_block():
+    """Ordinary gates except one strong step inside a single 32-row block of one
+    query head's channels: only that block takes the pair-by-pair path, next to
+    anchored blocks in the same tile."""
+    inp = make_inputs("long_bf16", B=1, T=300, HQ=2, H=1)
+    g = inp.g.double().clone()
+    g[0, 150, 1, :] = -200.0
+    inp.g = g.to(inp.g.dtype)
+    say("backward one spread block")
+    do = _do(inp, 37)
+    grads = _bwd_gpu(inp, do)
+    ref = oracle.wall_attn_bwd_oracle(inp.q, inp.k, inp.v, inp.g, do, scale=inp.scale)
+    _compare(grads, ref, "bfloat16")
+
+
+@pytest.mark.parametrize("dtype", ["bfloat16", "float32"])
+def test_backward_all_gates_closed(dtype):
+    """g = -800 per token: every earlier key's decay and its derivative are 0,
+    so with s_ii = scale q_i.k_i, Z_i = n_i + e^{s_ii} (n_i earlier tokens of i's
+    sequence), A_ij = 1/Z_i (j < i) and e^{s_ii}/Z_i (j = i),
+    dS_ij = A_ij (do_i.v_j - do_i.o_i):
+        dq_i = scale dS_ii k_i,  dk_j = scale sum_hq dS_jj q_j,
+        dv_j = sum_hq sum_{i >= j} A_ij do_i,  dg = 0."""
+    inp = _strong(-800.0, dtype, 128, T=300)
+    say(f"backward g=-800 closed form {dtype}")
+    do = _do(inp, 39)
+    grads = _bwd_gpu(inp, do)
+    q = inp.q.double().numpy()[0]
+    k = inp.k.double().numpy()[0]
+    v = inp.v.double().numpy()[0]
+    dd = do.double().numpy()[0]
+    T, HQ = q.shape[0], q.shape[1]
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for a, b in ((0, 37), (37, T)):
+        for hq in range(HQ):
+            vs = v[a:b, 0]
+            s = inp.scale * np.einsum("ik,ik->i", q[a:b, hq], k[a:b, 0])
+            n = np.arange(b - a)
+            Z = n + np.exp(s)
+            A = np.tril(np.ones((b - a, b - a)), -1) / Z[:, None]
+            A[n, n] = np.exp(s) / Z
+            o = A @ vs
+            D = np.einsum("iv,iv->i", dd[a:b, hq], o)
+            dS = A * (dd[a:b, hq] @ vs.T - D[:, None])
+            diag = dS[n, n]
+            dq[a:b, hq] = inp.scale * diag[:, None] * k[a:b, 0]
+            dk[a:b, 0] += inp.scale * diag[:, None] * q[a:b, hq]
+            dv[a:b, 0] += A.T @ dd[a:b, hq]
+    _compare(grads[:3], [dq[None], dk[None], dv[None]], dtype, names=("dq", "dk", "dv"))
+    # dg: every X term cancels; what is left is rounding of the pairs i = j
+    dg = f64(grads[3])
+    bound = 1e-5 * np.abs(q * dq).sum(axis=0).max()
+    say(f"  dg: max|dg|={np.abs(dg).max():.3e} (bound {bound:.3e})")
+    assert np.abs(dg).max() <= bound
