@@ -11,7 +11,9 @@ from ._binding import (  # noqa: F401
     EXPORTS,
     WALL_BF16,
     WALL_ERR_INVALID_ARG,
+    WALL_DECODE_SCRATCH_BYTES,
     WALL_ERR_LAUNCH,
+    WALL_ERR_SCRATCH,
     WALL_ERR_UNSUPPORTED,
     WALL_F32,
     WALL_OK,

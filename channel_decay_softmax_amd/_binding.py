@@ -19,7 +19,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libwall.so")
 
 WALL_F32, WALL_BF16 = 0, 1
-WALL_OK, WALL_ERR_INVALID_ARG, WALL_ERR_UNSUPPORTED, WALL_ERR_LAUNCH = 0, 1, 2, 3
+WALL_OK, WALL_ERR_INVALID_ARG, WALL_ERR_UNSUPPORTED, WALL_ERR_LAUNCH, WALL_ERR_SCRATCH = 0, 1, 2, 3, 4
+# bytes of the fixed per-GPU scratch of wall_attn_decode_noalloc
+WALL_DECODE_SCRATCH_BYTES = 4 << 20
 
 #: every symbol include/wall.h declares
 EXPORTS = (
@@ -29,6 +31,7 @@ EXPORTS = (
     "wall_attn_fwd_prepare", "wall_attn_fwd_run",
     "wall_attn_bwd_workspace_size", "wall_attn_bwd",
     "wall_kv_cache_build", "wall_attn_decode_workspace_size", "wall_attn_decode",
+    "wall_attn_decode_noalloc",
 )
 
 _lib = None
@@ -81,6 +84,8 @@ def lib() -> ctypes.CDLL:
         L.wall_attn_decode_workspace_size.restype = S
         L.wall_attn_decode.argtypes = [P, P, E, P, I, P, P, P, P, P, I, I, I, I, I, I, I, I, F, P, S, P]
         L.wall_attn_decode.restype = E
+        L.wall_attn_decode_noalloc.argtypes = [P, P, E, P, I, P, P, P, P, P, I, I, I, I, I, I, I, I, F, P]
+        L.wall_attn_decode_noalloc.restype = E
         _lib = L
     return _lib
 
@@ -464,12 +469,15 @@ def wall_attn_decode(q: torch.Tensor, v: torch.Tensor, p_curr: torch.Tensor, k_t
                      r_cache: torch.Tensor, sink_bias: Optional[torch.Tensor] = None,
                      scale: Optional[float] = None, cache_chunk_size: int = 64,
                      seq_len: Optional[int] = None, out: Optional[torch.Tensor] = None,
-                     lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None
-                     ) -> Tuple[torch.Tensor, torch.Tensor]:
+                     lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                     no_alloc: bool = False) -> Tuple[torch.Tensor, torch.Tensor]:
     """The README's wall_attn_decode: q and p_curr [B,1,HQ,K] (the newest token and
     its log2 prefix), v [B,T_cap,H,V], the cache of build_wall_kv_cache; attends to
     cached rows 0 .. seq_len-1 (default T_cap).  p_curr may be a row of a larger
-    prefix buffer (P[:, t:t+1]).  Returns (o [B,1,HQ,V], lse [B,1,HQ])."""
+    prefix buffer (P[:, t:t+1]).  Returns (o [B,1,HQ,V], lse [B,1,HQ]).  With
+    no_alloc (and out and lse given) the call allocates nothing: it goes through
+    wall_attn_decode_noalloc, whose split partials live in the library's fixed
+    per-GPU scratch."""
     dev = _on_gpu(q, v, p_curr, k_tilde, r_cache, sink_bias, out, lse, workspace)
     q, v = _dense(q), _dense(v)
     if not (p_curr.dim() == 4 and p_curr[0, 0].is_contiguous() and p_curr.stride(0) % 4 == 0):
@@ -490,6 +498,14 @@ def wall_attn_decode(q: torch.Tensor, v: torch.Tensor, p_curr: torch.Tensor, k_t
         scale = K ** -0.5
     out = _out(out, (B, 1, HQ, V), q.dtype, dev, "out")
     lse = _out(lse, (B, 1, HQ), torch.float32, dev, "lse")
+    if no_alloc:
+        if workspace is not None:
+            raise ValueError("no_alloc takes no workspace")
+        _check(lib().wall_attn_decode_noalloc(
+            _ptr(q), _ptr(v), _dtype(q), _ptr(p_curr), pc_bs, _ptr(k_tilde), _ptr(r_cache), _ptr(sink_bias),
+            _ptr(out), _ptr(lse), B, T, T_cap, HQ, H, K, V, int(cache_chunk_size), float(scale), _stream(dev)),
+            "wall_attn_decode_noalloc")
+        return out, lse
     if workspace is None:
         workspace = torch.empty(decode_workspace_size(B, T, HQ, V), dtype=torch.uint8, device=dev)
     _check(lib().wall_attn_decode(

@@ -7,6 +7,7 @@
 #include "wall.h"
 
 #include "wall_common.h"
+#include "wall_entry.h"
 #include "wall_stream.h"
 
 using namespace wall;
@@ -24,6 +25,68 @@ int64_t esize_of(wall_dtype_t d) { return d == WALL_BF16 ? 2 : (d == WALL_F32 ? 
 
 }  // namespace
 
+namespace wall {
+
+wall_status_t decode_check(const void *q, const void *v, wall_dtype_t dtype, const float *p_curr,
+                           int64_t p_curr_batch_stride, const void *k_tilde, const float *r_cache,
+                           const float *sink_bias, const void *o, const float *lse, int64_t B, int64_t T,
+                           int64_t T_cap, int64_t HQ, int64_t H, int64_t K, int64_t V, int64_t chunk_size) {
+    if (!q || !v || !p_curr || !k_tilde || !r_cache || !o) return WALL_ERR_INVALID_ARG;
+    if (B < 1 || T < 1 || T_cap < 1 || HQ < 1 || H < 1 || K < 1 || V < 1 || chunk_size < 1)
+        return WALL_ERR_INVALID_ARG;
+    if (HQ % H != 0 || T > T_cap || B * HQ > 65535) return WALL_ERR_INVALID_ARG;
+    if (p_curr_batch_stride != 0 && (p_curr_batch_stride < HQ * K || p_curr_batch_stride % 4 != 0))
+        return WALL_ERR_INVALID_ARG;
+    if (B * T_cap > INT32_MAX / 2 || B * T_cap * HQ * (K > V ? K : V) > ((int64_t)1 << 40))
+        return WALL_ERR_INVALID_ARG;
+    if (dtype != WALL_BF16 && dtype != WALL_F32) return WALL_ERR_UNSUPPORTED;
+    if ((K != 64 && K != 128) || (V != 64 && V != 128) || chunk_size % 64 != 0) return WALL_ERR_UNSUPPORTED;
+    const void *ptrs[] = {q, v, p_curr, k_tilde, r_cache, sink_bias, o, lse};
+    for (const void *p : ptrs)
+        if (p && !aligned(p, 16)) return WALL_ERR_INVALID_ARG;
+    return WALL_OK;
+}
+
+wall_status_t decode_launch(const void *q, const void *v, wall_dtype_t dtype, const float *p_curr,
+                            int64_t p_curr_batch_stride, const void *k_tilde, const float *r_cache,
+                            const float *sink_bias, void *o, float *lse, int64_t B, int64_t T, int64_t T_cap,
+                            int64_t HQ, int64_t H, int64_t K, int64_t V, int64_t chunk_size, float scale,
+                            float *part, hipStream_t stream) {
+    const DecodeLayout L = decode_layout(B, T, HQ, V);
+    DecodeArgs a{};
+    a.q = q;
+    a.v = v;
+    a.pc = p_curr;
+    a.pc_bs = p_curr_batch_stride ? p_curr_batch_stride : HQ * K;
+    a.kt = k_tilde;
+    a.r = r_cache;
+    a.sink = sink_bias;
+    a.o = o;
+    a.lse = lse;
+    a.part = part;
+    a.B = (int32_t)B;
+    a.T = (int32_t)T;
+    a.Tcap = (int32_t)T_cap;
+    a.HQ = (int32_t)HQ;
+    a.H = (int32_t)H;
+    a.K = (int32_t)K;
+    a.V = (int32_t)V;
+    a.C = (int32_t)chunk_size;
+    a.nsplit = (int32_t)L.nsplit;
+    a.S = (int32_t)L.S;
+    // the query heads of one kv head share a block (the largest divisor of HQ/H up to 4)
+    a.nwg = 1;
+    for (int32_t d = 4; d >= 1; --d)
+        if ((HQ / H) % d == 0) {
+            a.nwg = d;
+            break;
+        }
+    a.qscale = scale * LOG2E;
+    return launched(launch_decode(a, dtype == WALL_BF16, stream));
+}
+
+}  // namespace wall
+
 extern "C" {
 
 const char *wall_status_string(wall_status_t s) {
@@ -32,6 +95,7 @@ const char *wall_status_string(wall_status_t s) {
         case WALL_ERR_INVALID_ARG: return "WALL_ERR_INVALID_ARG";
         case WALL_ERR_UNSUPPORTED: return "WALL_ERR_UNSUPPORTED";
         case WALL_ERR_LAUNCH: return "WALL_ERR_LAUNCH";
+        case WALL_ERR_SCRATCH: return "WALL_ERR_SCRATCH";
     }
     return "WALL_ERR_UNKNOWN";
 }
@@ -347,52 +411,14 @@ wall_status_t wall_attn_decode(const void *q, const void *v, wall_dtype_t dtype,
                                void *o, float *lse, int64_t B, int64_t T, int64_t T_cap, int64_t HQ,
                                int64_t H, int64_t K, int64_t V, int64_t chunk_size, float scale,
                                void *workspace, size_t workspace_bytes, hipStream_t stream) {
-    if (!q || !v || !p_curr || !k_tilde || !r_cache || !o || !workspace) return WALL_ERR_INVALID_ARG;
-    if (B < 1 || T < 1 || T_cap < 1 || HQ < 1 || H < 1 || K < 1 || V < 1 || chunk_size < 1)
-        return WALL_ERR_INVALID_ARG;
-    if (HQ % H != 0 || T > T_cap || B * HQ > 65535) return WALL_ERR_INVALID_ARG;
-    if (p_curr_batch_stride != 0 && (p_curr_batch_stride < HQ * K || p_curr_batch_stride % 4 != 0))
-        return WALL_ERR_INVALID_ARG;
-    if (B * T_cap > INT32_MAX / 2 || B * T_cap * HQ * (K > V ? K : V) > ((int64_t)1 << 40))
-        return WALL_ERR_INVALID_ARG;
-    if (dtype != WALL_BF16 && dtype != WALL_F32) return WALL_ERR_UNSUPPORTED;
-    if ((K != 64 && K != 128) || (V != 64 && V != 128) || chunk_size % 64 != 0) return WALL_ERR_UNSUPPORTED;
-    const void *ptrs[] = {q, v, p_curr, k_tilde, r_cache, sink_bias, o, lse};
-    for (const void *p : ptrs)
-        if (p && !aligned(p, 16)) return WALL_ERR_INVALID_ARG;
+    if (!workspace) return WALL_ERR_INVALID_ARG;
+    const wall_status_t st = wall::decode_check(q, v, dtype, p_curr, p_curr_batch_stride, k_tilde, r_cache,
+                                                sink_bias, o, lse, B, T, T_cap, HQ, H, K, V, chunk_size);
+    if (st != WALL_OK) return st;
     if (!aligned(workspace, 256)) return WALL_ERR_INVALID_ARG;
-    const DecodeLayout L = decode_layout(B, T, HQ, V);
-    if (workspace_bytes < L.total) return WALL_ERR_INVALID_ARG;
-    DecodeArgs a{};
-    a.q = q;
-    a.v = v;
-    a.pc = p_curr;
-    a.pc_bs = p_curr_batch_stride ? p_curr_batch_stride : HQ * K;
-    a.kt = k_tilde;
-    a.r = r_cache;
-    a.sink = sink_bias;
-    a.o = o;
-    a.lse = lse;
-    a.part = static_cast<float *>(workspace);
-    a.B = (int32_t)B;
-    a.T = (int32_t)T;
-    a.Tcap = (int32_t)T_cap;
-    a.HQ = (int32_t)HQ;
-    a.H = (int32_t)H;
-    a.K = (int32_t)K;
-    a.V = (int32_t)V;
-    a.C = (int32_t)chunk_size;
-    a.nsplit = (int32_t)L.nsplit;
-    a.S = (int32_t)L.S;
-    // the query heads of one kv head share a block (the largest divisor of HQ/H up to 4)
-    a.nwg = 1;
-    for (int32_t d = 4; d >= 1; --d)
-        if ((HQ / H) % d == 0) {
-            a.nwg = d;
-            break;
-        }
-    a.qscale = scale * LOG2E;
-    return launched(launch_decode(a, dtype == WALL_BF16, stream));
+    if (workspace_bytes < wall::decode_layout(B, T, HQ, V).total) return WALL_ERR_INVALID_ARG;
+    return wall::decode_launch(q, v, dtype, p_curr, p_curr_batch_stride, k_tilde, r_cache, sink_bias, o, lse, B, T,
+                               T_cap, HQ, H, K, V, chunk_size, scale, static_cast<float *>(workspace), stream);
 }
 
 }  // extern "C"

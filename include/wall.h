@@ -53,6 +53,7 @@ typedef enum {
     WALL_ERR_INVALID_ARG = 1, /* null required pointer, bad size, bad alignment, short workspace */
     WALL_ERR_UNSUPPORTED = 2, /* valid but not implemented: a head size or dtype with no kernel */
     WALL_ERR_LAUNCH = 3,      /* a kernel launch failed; hipGetLastError() is reported */
+    WALL_ERR_SCRATCH = 4,     /* a no-allocation entry point would need more than its fixed scratch */
 } wall_status_t;
 
 /* Human-readable name of a status (static storage, never NULL). */
@@ -412,6 +413,33 @@ wall_status_t wall_attn_decode(const void *q, const void *v, wall_dtype_t dtype,
                                int64_t K, int64_t V, int64_t chunk_size, float scale,
                                void *workspace, size_t workspace_bytes,
                                hipStream_t stream);
+
+/* ------------------------------------------------------------------ decode without allocation
+ *
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * decode step as wall_attn_decode, same arguments without the workspace,
+ * same kernels and results bit for bit.  The split partials live in a fixed
+ * device array of the library, WALL_DECODE_SCRATCH_BYTES per GPU, that each
+ * GPU the library runs on holds until the process ends; its address is
+ * taken once per device (the device current at the call, which must own
+ * `stream`).  Nothing is allocated and nothing needs clearing: every call
+ * writes the partials it reads.  Calls that overlap on one GPU (other
+ * streams, other threads) share that array and race: order them.
+ * Errors: those of wall_attn_decode (other than the workspace's);
+ * WALL_ERR_SCRATCH when wall_attn_decode_workspace_size(B, T, HQ, V) would
+ * exceed WALL_DECODE_SCRATCH_BYTES (about B * HQ <= 6000 at V = 128);
+ * UNSUPPORTED for a device index of 64 or more; LAUNCH when the array's
+ * address cannot be taken or a launch fails. */
+#define WALL_DECODE_SCRATCH_BYTES ((size_t)4 << 20)
+
+wall_status_t wall_attn_decode_noalloc(const void *q, const void *v, wall_dtype_t dtype,
+                                       const float *p_curr, int64_t p_curr_batch_stride,
+                                       const void *k_tilde, const float *r_cache,
+                                       const float *sink_bias, void *o, float *lse,
+                                       int64_t B, int64_t T, int64_t T_cap, int64_t HQ, int64_t H,
+                                       int64_t K, int64_t V, int64_t chunk_size, float scale,
+                                       hipStream_t stream);
 
 #ifdef __cplusplus
 }

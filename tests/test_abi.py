@@ -186,6 +186,44 @@ def test_decode_rejects_unsupported_shapes(kw):
     assert decode(**kw) == UNSUPPORTED
 
 
+def decode_noalloc(q=FAKE, v=FAKE, dtype=B.WALL_BF16, pc=FAKE, pcs=0, kt=FAKE, r=FAKE, sink=None, o=FAKE,
+                   lse=None, b=2, t=300, tcap=512, hq=4, h=2, kk=128, vv=128, c=64):
+    return wall.lib().wall_attn_decode_noalloc(P(q), P(v), dtype, P(pc), pcs, P(kt), P(r), P(sink), P(o),
+                                               P(lse), b, t, tcap, hq, h, kk, vv, c, 0.088, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(q=None), dict(v=None), dict(pc=None), dict(kt=None), dict(r=None), dict(o=None),
+    dict(b=0), dict(t=0), dict(tcap=0), dict(hq=0), dict(h=0), dict(hq=6, h=4), dict(t=513),
+    dict(b=8192, hq=16, h=4), dict(q=FAKE + 2), dict(sink=FAKE + 4), dict(lse=FAKE + 8), dict(pcs=100),
+])
+def test_decode_noalloc_rejects_invalid_arguments(kw):
+    assert decode_noalloc(**kw) == INVALID
+
+
+@pytest.mark.parametrize("kw", [dict(kk=96), dict(vv=32), dict(c=32), dict(dtype=5)])
+def test_decode_noalloc_rejects_unsupported_shapes(kw):
+    assert decode_noalloc(**kw) == UNSUPPORTED
+
+
+@pytest.mark.parametrize("b,hq,vv", [(512, 16, 128), (8192, 2, 64), (64, 128, 128)])
+def test_decode_noalloc_rejects_what_outgrows_its_scratch(b, hq, vv):
+    """A call whose split partials would not fit the fixed scratch is refused
+    before any device work, with its own status."""
+    L = wall.lib()
+    assert L.wall_attn_decode_workspace_size(b, 64, hq, vv) > wall.WALL_DECODE_SCRATCH_BYTES
+    assert decode_noalloc(b=b, t=64, tcap=64, hq=hq, h=1, vv=vv) == wall.WALL_ERR_SCRATCH
+    assert wall.status_string(wall.WALL_ERR_SCRATCH) == "WALL_ERR_SCRATCH"
+
+
+def test_decode_noalloc_scratch_covers_the_decode_workload():
+    """The decode workload (16 sequences, 16 query heads, V = 128) fits at any
+    cache length."""
+    L = wall.lib()
+    for t in (1, 64, 8192, 1 << 20):
+        assert L.wall_attn_decode_workspace_size(16, t, 16, 128) <= wall.WALL_DECODE_SCRATCH_BYTES
+
+
 def bwd(q=FAKE, k=FAKE, v=FAKE, dtype=B.WALL_BF16, Pp=FAKE, G=None, sink=None, o=FAKE, lse=FAKE, do=FAKE,
         dq=FAKE, dk=FAKE, dv=FAKE, dg=FAKE, dgs=None, gdt=B.WALL_BF16, dsink=None, b=1, t=256, hq=4, h=2,
         kk=128, vv=128, window=0, cu=None, nseq=0, maxlen=0, ws=FAKE, wsb=None):
