@@ -165,8 +165,7 @@ def wall_prefix_scan(x: torch.Tensor, cu_seqlens: Optional[torch.Tensor] = None,
     nbytes = prefix_scan_workspace_size(B, T, C)
     if workspace is None:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-    cu = None if cu_seqlens is None else _dense(cu_seqlens.to(torch.int32))
-    nseq = 0 if cu is None else cu.numel() - 1
+    cu, nseq, _ = _varlen(cu_seqlens, B, T, None)
     _check(lib().wall_prefix_scan(_ptr(x), _dtype(x), _ptr(out), B, T, C, _ptr(cu), nseq,
                                   float(scale), _ptr(workspace), workspace.numel(), _stream(dev)),
            "wall_prefix_scan")
@@ -271,10 +270,7 @@ def wall_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, P: torch.Te
             raise ValueError("sink_bias must be [HQ]")
     if scale is None:
         scale = K ** -0.5
-    cu = None if cu_seqlens is None else _dense(cu_seqlens.to(torch.int32))
-    nseq = 0 if cu is None else cu.numel() - 1
-    if cu is not None and max_seqlen is None:
-        max_seqlen = int((cu[1:] - cu[:-1]).max().item())
+    cu, nseq, max_seqlen = _varlen(cu_seqlens, B, T, max_seqlen)
     out = _out(out, (B, T, HQ, V), q.dtype, dev, "out")
     if lse is not None or return_lse:
         lse = _out(lse, (B, T, HQ), torch.float32, dev, "lse")
@@ -301,6 +297,20 @@ def check_cu_seqlens(cu_seqlens: torch.Tensor, B: int, T: int) -> int:
     return int((cu[1:] - cu[:-1]).max())
 
 
+def _varlen(cu_seqlens: Optional[torch.Tensor], B: int, T: int, max_seqlen: Optional[int]):
+    """(cu as dense int32, number of sequences, max_seqlen) after the host checks:
+    the C ABI trusts device-side offsets and max_seqlen, so they are checked here."""
+    if cu_seqlens is None:
+        return None, 0, max_seqlen
+    longest = check_cu_seqlens(cu_seqlens, B, T)
+    if max_seqlen is None:
+        max_seqlen = longest
+    elif not longest <= int(max_seqlen) <= T:
+        raise ValueError(f"max_seqlen {max_seqlen} must lie between the longest sequence ({longest}) and T ({T})")
+    cu = _dense(cu_seqlens.to(torch.int32))
+    return cu, cu.numel() - 1, int(max_seqlen)
+
+
 def wall_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, P: torch.Tensor, o: torch.Tensor,
                   lse: torch.Tensor, dout: torch.Tensor, G: Optional[torch.Tensor] = None,
                   sink_bias: Optional[torch.Tensor] = None, scale: Optional[float] = None,
@@ -322,10 +332,7 @@ def wall_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, P: torch.Te
     if scale is None:
         scale = K ** -0.5
     gd = q.dtype if g_dtype is None else g_dtype
-    cu = None if cu_seqlens is None else _dense(cu_seqlens.to(torch.int32))
-    nseq = 0 if cu is None else cu.numel() - 1
-    if cu is not None and max_seqlen is None:
-        max_seqlen = int((cu[1:] - cu[:-1]).max().item())
+    cu, nseq, max_seqlen = _varlen(cu_seqlens, B, T, max_seqlen)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     dg = torch.empty((B, T, HQ, K), dtype=gd, device=dev)
     dgs = None if G is None else torch.empty((B, T, HQ), dtype=gd, device=dev)

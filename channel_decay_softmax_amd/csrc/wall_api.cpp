@@ -89,7 +89,7 @@ wall_status_t decode_launch(const void *q, const void *v, wall_dtype_t dtype, co
 
 extern "C" {
 
-const char *wall_status_string(wall_status_t s) {
+const char *wall_status_string(int s) {
     switch (s) {
         case WALL_OK: return "WALL_OK";
         case WALL_ERR_INVALID_ARG: return "WALL_ERR_INVALID_ARG";

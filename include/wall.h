@@ -26,7 +26,13 @@
  *   - Argument checks run before any HIP call, so an invalid call returns its
  *     status without touching the device.  Contents of device buffers (e.g.
  *     cu_seqlens) cannot be checked without a synchronisation and are the
- *     caller's responsibility; they are listed under each call.
+ *     caller's responsibility; they are listed under each call.  The library
+ *     trusts the device-side sequence offsets and the max_seqlen it is given:
+ *     offsets that are not as documented, or a max_seqlen below the longest
+ *     sequence, give wrong results or out-of-range accesses.  (The Python
+ *     wrappers wall_prefix_scan, wall_attn_fwd, wall_attn_bwd and wall_attn
+ *     check both on the host; the stage wrappers wall_attn_fwd_prepare and
+ *     wall_attn_fwd_run do not.)
  *   - Two calls that share a workspace or an output buffer must be ordered on
  *     one stream; calls on different streams with separate buffers are
  *     independent.
@@ -43,12 +49,21 @@
 extern "C" {
 #endif
 
-typedef enum {
+/* The enums are int-sized; in C++ they have int as their fixed underlying
+ * type, so that any int value (e.g. an unsupported dtype, which the entry
+ * points reject) is a valid value of the type. */
+#ifdef __cplusplus
+#define WALL_ENUM_INT : int
+#else
+#define WALL_ENUM_INT
+#endif
+
+typedef enum WALL_ENUM_INT {
     WALL_F32 = 0,  /* IEEE binary32 */
     WALL_BF16 = 1, /* bfloat16 (1-8-7) */
 } wall_dtype_t;
 
-typedef enum {
+typedef enum WALL_ENUM_INT {
     WALL_OK = 0,
     WALL_ERR_INVALID_ARG = 1, /* null required pointer, bad size, bad alignment, short workspace */
     WALL_ERR_UNSUPPORTED = 2, /* valid but not implemented: a head size or dtype with no kernel */
@@ -56,8 +71,9 @@ typedef enum {
     WALL_ERR_SCRATCH = 4,     /* a no-allocation entry point would need more than its fixed scratch */
 } wall_status_t;
 
-/* Human-readable name of a status (static storage, never NULL). */
-const char *wall_status_string(wall_status_t s);
+/* Human-readable name of a status value (static storage, never NULL); any
+ * int is accepted, "WALL_ERR_UNKNOWN" for one that names no status. */
+const char *wall_status_string(int s);
 
 /* Library version as 10000*major + 100*minor + patch. */
 int wall_version(void);

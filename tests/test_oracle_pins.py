@@ -428,8 +428,9 @@ def _fd_check(oracle_mod, args, kw, grads, rng, eps=1e-6, rtol=1e-6):
 
 @pytest.mark.parametrize("case", ["plain", "gqa_window_fox_sink", "varlen", "positive_gate", "single_token"])
 def test_backward_matches_central_differences(oracle_mod, case):
-    """README: the g / g_scalar gradients are verified against central finite
-    differences; every gradient of the oracle's backward is held to that."""
+    """The README checks its gate gradients with finite differences; here every
+    gradient of the oracle's backward is held to central differences of the
+    forward oracle."""
     rng = np.random.default_rng(41)
     B, T, HQ, H, K, V = 2, 29, 4, 2, 5, 3
     kw = dict(scale=0.45)
