@@ -3,8 +3,10 @@
     python bench.py [--steps K] [--warmup W] [--workload long_bf16] [--gpus 1]
 
 A step is one pass of the whole hot path over one batch of synthetic inputs
-already resident in HBM: the log2 prefix scan of g (and of g_scalar when the
-workload has one), the key-cache preparation and the fused forward kernel.
+already resident in HBM: the log2 prefix of g with the key-cache preparation
+(wall_attn_fwd_prepare_gate, one combined pass on the long-context workload),
+the prefix scan of g_scalar when the workload has one, and the fused forward
+kernel.
 The default workload is the long-context causal case (B=1, T=8192, HQ=16,
 H=4, K=V=128, bf16, bimodal gate), on which the headline metric is quoted.
 
@@ -16,8 +18,11 @@ first ~40 ms of work after idle do not reach); ``roofline`` prices the fused
 forward kernel alone, timed with HIP events on the stream it is launched on
 over a second pass of the same K steps (an event record leaves a gap on the
 stream, so none sits in the timed region), against the dense bf16 MFMA peak;
-``cpu_baseline`` times the fp64 oracle on a bounded row sample of the same
-workload on this host.
+``call`` beside it prices the forward's C-ABI calls (prefix and preparation,
+fused kernel) the same way; float32 workloads are priced against the vector
+fp32 peak (``bound: "alu"``).  ``cpu_baseline`` times the fp64 oracle on this
+host on every row of the workload when that takes at most about a minute
+(the long-context workload), else on a fixed row sample.
 """
 
 from __future__ import annotations
@@ -90,8 +95,24 @@ def load_traffic(workload, path=TRAFFIC_FILE, sources=FWD_KERNEL_SOURCES):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(inp, flop_per_pair, target_s):
-    """Time the fp64 oracle (as it stands) on a bounded sample of query rows."""
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(inp, flop_per_pair, full_limit_s):
+    """Time the fp64 oracle (as it stands) on every query row of the workload
+    when a calibration predicts at most ``full_limit_s`` seconds for that,
+    else on the first rows of a fixed seeded permutation sized to that time
+    (the same rows on every run of one host).  Timed with time.perf_counter,
+    the monotonic high-resolution clock."""
     import numpy as np
 
     import oracle
@@ -114,8 +135,7 @@ def cpu_baseline(inp, flop_per_pair, target_s):
     keys = np.arange(B * T) - starts + 1
     if W:
         keys = np.minimum(keys, W)
-    rng = np.random.default_rng(0)
-    order = rng.permutation(B * T)
+    order = np.random.default_rng(0).permutation(B * T)
 
     def run(rows):
         t0 = time.perf_counter()
@@ -124,25 +144,29 @@ def cpu_baseline(inp, flop_per_pair, target_s):
                                 cu_seqlens=inp.cu_seqlens, rows=rows)
         return time.perf_counter() - t0
 
-    # calibrate on a small sample, then size the timed sample to about target_s
-    cal = order[:64]
-    t_cal = run(cal)
-    pairs_cal = int(keys[cal].sum()) * HQ
-    rate = pairs_cal / max(t_cal, 1e-6)
-    want_pairs = rate * target_s
-    csum = np.cumsum(keys[order]) * HQ
-    n = int(min(B * T, max(64, np.searchsorted(csum, want_pairs) + 1)))
-    rows = np.sort(order[:n])
+    # calibrate on the last rows (the most keys), then run every row if it fits
+    cal = np.arange(B * T - 64, B * T)
+    rate = int(keys[cal].sum()) * HQ / max(run(cal), 1e-6)
+    total_pairs = int(keys.sum()) * HQ
+    if total_pairs / rate <= full_limit_s:
+        rows = None
+        n = B * T
+        pairs = total_pairs
+    else:
+        csum = np.cumsum(keys[order]) * HQ
+        n = int(min(B * T, max(64, np.searchsorted(csum, rate * full_limit_s) + 1)))
+        rows = np.sort(order[:n])
+        pairs = int(keys[rows].sum()) * HQ
     t = run(rows)
-    pairs = int(keys[rows].sum()) * HQ
     return {
         "value": pairs * flop_per_pair / t / 1e12,
         "unit": "TFLOP/s",
         "cores": oracle.num_threads(),
         "kind": "oracle",
         "sample": f"{n} of {B * T} query rows (all {HQ} heads), {pairs} visible pairs, "
-                  f"{t:.1f} s fp64 product form",
+                  f"{t:.1f} s fp64 product form, time.perf_counter",
         "seconds": t,
+        "cpu": cpu_model(),
     }
 
 
@@ -412,7 +436,9 @@ def main():
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="long_bf16")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=60.0,
+                    help="the oracle runs every row of the workload when predicted to take at most this long, "
+                         "else a fixed sample sized to it")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward (wall_attn_bwd) of the workload instead of the forward hot path")
@@ -474,12 +500,12 @@ def main():
     def step(marks=None):
         if marks:
             marks[0].record()
-        wall.wall_prefix_scan(d.g, cu, out=P, workspace=ws_scan)
         if G is not None:
             wall.wall_prefix_scan(d.g_scalar, cu, out=G, workspace=ws_scan)
         if marks:
             marks[1].record()
-        wall.wall_attn_fwd_prepare(d.q, d.k, d.v, P, ws_fwd, scale=d.scale, cu_seqlens=cu)
+        # the prefix of g and the preparation (one combined pass where the layout allows)
+        wall.wall_attn_fwd_prepare_gate(d.q, d.k, d.v, d.g, P, ws_fwd, scale=d.scale, cu_seqlens=cu)
         if marks:
             marks[2].record()
         wall.wall_attn_fwd_run(d.q, d.k, d.v, P, ws_fwd, o, lse, G=G, sink_bias=d.sink_bias,
@@ -522,8 +548,8 @@ def main():
     achieved = flop / (run_avg * 1e-3) / 1e12
     value = flop / (ms_step * 1e-3) / 1e12
     traffic = load_traffic(args.workload)
-    print(f"[bench] step {ms_step:.3f} ms: scan {statistics.fmean(scan_ms)*1e3:.1f} us, "
-          f"prepare {statistics.fmean(prep_ms)*1e3:.1f} us, fused {run_avg*1e3:.1f} us "
+    print(f"[bench] step {ms_step:.3f} ms: scalar-gate scan {statistics.fmean(scan_ms)*1e3:.1f} us, "
+          f"prefix + prepare {statistics.fmean(prep_ms)*1e3:.1f} us, fused {run_avg*1e3:.1f} us "
           f"(min {min(run_ms)*1e3:.1f}) -> fused {achieved:.1f} TFLOP/s", file=sys.stderr, flush=True)
 
     cpu = None
@@ -532,6 +558,13 @@ def main():
         cpu = cpu_baseline(inp, flop_per_pair, args.cpu_seconds)
 
     dtype = {torch.bfloat16: "bf16", torch.float32: "f32"}[d.q.dtype]
+    # bf16 runs on the matrix cores; float32 runs on the vector ALUs
+    if dtype == "bf16":
+        kname, bound, peak = ("fwd_bf16_kernel<128,128>" if K == 128 else "fwd_bf16_kernel"), "mfma", PEAK_BF16_TFLOPS
+    else:
+        kname, bound, peak = "fwd_f32_kernel", "alu", PEAK_F32_VALU_TFLOPS
+    prep_avg = statistics.fmean(prep_ms)
+    call_tflops = flop / ((prep_avg + run_avg) * 1e-3) / 1e12
     rec = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -549,14 +582,17 @@ def main():
                    "causal": True, "window_size": inp.window_size,
                    "g_scalar": inp.g_scalar is not None, "sink": inp.sink_bias is not None,
                    "num_seqs": nseq or None, "visible_pairs": pairs, "counted_flop": flop},
-        "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
-        "stages_us": {"prefix_scan": round(statistics.fmean(scan_ms) * 1e3, 2),
-                      "prepare": round(statistics.fmean(prep_ms) * 1e3, 2),
+        "pct_of_peak": round(100.0 * value / peak, 2),
+        "stages_us": {"scalar_gate_scan": round(statistics.fmean(scan_ms) * 1e3, 2),
+                      "prefix_and_prepare": round(prep_avg * 1e3, 2),
                       "fused_fwd": round(run_avg * 1e3, 2)},
-        "roofline": {"kernel": "fwd_bf16_kernel<128,128>" if K == 128 else "fwd_bf16_kernel",
-                     "bound": "mfma", "achieved": round(achieved, 3),
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
+        "roofline": {"kernel": kname, "bound": bound, "achieved": round(achieved, 3),
+                     "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": traffic if dtype == "bf16" else None,
+                     # the C-ABI calls of the forward from the gate: prefix and preparation, fused kernel
+                     "call": {"what": "wall_attn_fwd_prepare_gate + wall_attn_fwd_run",
+                              "us": round((prep_avg + run_avg) * 1e3, 2),
+                              "achieved": round(call_tflops, 3), "frac": round(call_tflops / peak, 4)}},
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

@@ -29,7 +29,9 @@ from ._binding import (  # noqa: F401
     wall_attn_bwd,
     wall_attn_decode,
     wall_attn_fwd,
+    wall_attn_fwd_gate,
     wall_attn_fwd_prepare,
+    wall_attn_fwd_prepare_gate,
     wall_attn_fwd_run,
     wall_prefix_scan,
     wall_prefix_append,

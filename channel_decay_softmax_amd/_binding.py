@@ -28,7 +28,7 @@ EXPORTS = (
     "wall_status_string", "wall_version",
     "wall_prefix_scan_workspace_size", "wall_prefix_scan", "wall_prefix_append", "wall_stream_append",
     "wall_attn_fwd_workspace_size", "wall_attn_fwd",
-    "wall_attn_fwd_prepare", "wall_attn_fwd_run",
+    "wall_attn_fwd_prepare", "wall_attn_fwd_prepare_gate", "wall_attn_fwd_run",
     "wall_attn_bwd_workspace_size", "wall_attn_bwd",
     "wall_kv_cache_build", "wall_attn_decode_workspace_size", "wall_attn_decode",
     "wall_attn_decode_noalloc",
@@ -70,6 +70,8 @@ def lib() -> ctypes.CDLL:
         L.wall_attn_fwd.restype = E
         L.wall_attn_fwd_prepare.argtypes = [P, P, P, E, P, I, I, I, I, I, I, F, P, I, P, S, P]
         L.wall_attn_fwd_prepare.restype = E
+        L.wall_attn_fwd_prepare_gate.argtypes = [P, P, P, E, P, E, P, I, I, I, I, I, I, F, P, I, P, S, P]
+        L.wall_attn_fwd_prepare_gate.restype = E
         L.wall_attn_fwd_run.argtypes = [P, P, P, E, P, P, P, P, P, I, I, I, I, I, I, F, I, P, I, I,
                                         P, S, P]
         L.wall_attn_fwd_run.restype = E
@@ -348,15 +350,45 @@ def wall_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, P: torch.Te
     return dq, dk, dv, dg, dgs, dsink
 
 
+def wall_attn_fwd_gate(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                       G: Optional[torch.Tensor] = None, sink_bias: Optional[torch.Tensor] = None,
+                       scale: Optional[float] = None, window_size: Optional[int] = None,
+                       cu_seqlens: Optional[torch.Tensor] = None, max_seqlen: Optional[int] = None):
+    """The forward from the natural-log gate g: wall_attn_fwd_prepare_gate (P and the
+    prepared workspace in one call) then wall_attn_fwd_run.  Returns (o, lse, P)."""
+    dev = _on_gpu(q, k, v, g, G, sink_bias, cu_seqlens)
+    q, k, v, g, G = _dense(q), _dense(k), _dense(v), _dense(g), _dense(G)
+    B, T, HQ, K = q.shape
+    H, V = k.shape[2], v.shape[3]
+    if k.shape != (B, T, H, K) or v.shape != (B, T, H, V) or g.shape != (B, T, HQ, K):
+        raise ValueError("shapes must be q [B,T,HQ,K], k [B,T,H,K], v [B,T,H,V], g [B,T,HQ,K]")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v share one dtype")
+    if G is not None and (G.shape != (B, T, HQ) or G.dtype != torch.float32):
+        raise ValueError("G must be float32 [B,T,HQ]")
+    if sink_bias is not None:
+        sink_bias = _dense(sink_bias.to(torch.float32))
+        if sink_bias.shape != (HQ,):
+            raise ValueError("sink_bias must be [HQ]")
+    if scale is None:
+        scale = K ** -0.5
+    cu, nseq, max_seqlen = _varlen(cu_seqlens, B, T, max_seqlen)
+    P = torch.empty((B, T, HQ, K), dtype=torch.float32, device=dev)
+    ws = torch.empty(attn_fwd_workspace_size(q.dtype, B, T, HQ, H, K, V, nseq), dtype=torch.uint8, device=dev)
+    wall_attn_fwd_prepare_gate(q, k, v, g, P, ws, scale, cu)
+    o = torch.empty((B, T, HQ, V), dtype=q.dtype, device=dev)
+    lse = torch.empty((B, T, HQ), dtype=torch.float32, device=dev)
+    wall_attn_fwd_run(q, k, v, P, ws, o, lse, G, sink_bias, scale, window_size, cu, max_seqlen)
+    return o, lse, P
+
+
 class _WallAttn(torch.autograd.Function):
     """wall_attn with its gradients (q, k, v, g, g_scalar, sink_bias)."""
 
     @staticmethod
     def forward(ctx, q, k, v, g, g_scalar, sink_bias, scale, window_size, cu_seqlens, max_seqlen):
-        P = wall_prefix_scan(g, cu_seqlens)
         G = None if g_scalar is None else wall_prefix_scan(g_scalar, cu_seqlens)
-        o, lse = wall_attn_fwd(q, k, v, P, G, sink_bias, scale, window_size, cu_seqlens, max_seqlen,
-                               return_lse=True)
+        o, lse, P = wall_attn_fwd_gate(q, k, v, g, G, sink_bias, scale, window_size, cu_seqlens, max_seqlen)
         ctx.save_for_backward(q, k, v, P, G, sink_bias, o, lse, cu_seqlens)
         ctx.set_materialize_grads(False)  # an unused lse gets no gradient tensor
         ctx.opts = (scale, window_size, max_seqlen, g.dtype, g_scalar is not None, sink_bias is not None)
@@ -412,6 +444,23 @@ def wall_attn_fwd_prepare(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, P: 
     _check(lib().wall_attn_fwd_prepare(_ptr(q), _ptr(k), _ptr(v), _dtype(k), _ptr(P), B, T, HQ, H, K, V,
                                        float(K ** -0.5 if scale is None else scale), _ptr(cu_seqlens), nseq,
                                        _ptr(workspace), workspace.numel(), _stream(dev)), "wall_attn_fwd_prepare")
+
+
+def wall_attn_fwd_prepare_gate(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                               P: torch.Tensor, workspace: torch.Tensor, scale: Optional[float] = None,
+                               cu_seqlens: Optional[torch.Tensor] = None) -> None:
+    """Stage 1 of the forward from the gate: writes P = cumsum(g) / ln 2 (float32,
+    [B,T,HQ,K]) and prepares ``workspace`` from it (one combined pass for B
+    sequences of T rows with T a multiple of 128 and bf16 inputs).  All tensors
+    must already be dense and on one device (no copies are made here)."""
+    dev = _on_gpu(q, k, v, g, P, workspace, cu_seqlens)
+    B, T, HQ, K = q.shape
+    H, V = k.shape[2], v.shape[3]
+    nseq = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
+    _check(lib().wall_attn_fwd_prepare_gate(
+        _ptr(q), _ptr(k), _ptr(v), _dtype(q), _ptr(g), _dtype(g), _ptr(P), B, T, HQ, H, K, V,
+        float(K ** -0.5 if scale is None else scale), _ptr(cu_seqlens), nseq, _ptr(workspace), workspace.numel(),
+        _stream(dev)), "wall_attn_fwd_prepare_gate")
 
 
 def wall_attn_fwd_run(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, P: torch.Tensor,

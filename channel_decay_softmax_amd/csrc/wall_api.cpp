@@ -243,6 +243,46 @@ wall_status_t wall_attn_fwd_prepare(const void *q, const void *k, const void *v,
     return enqueue_prepare(q, k, v, dtype, P, scale, s, cu_seqlens, workspace, stream);
 }
 
+wall_status_t wall_attn_fwd_prepare_gate(const void *q, const void *k, const void *v, wall_dtype_t dtype,
+                                         const void *g, wall_dtype_t g_dtype, float *P, int64_t B, int64_t T,
+                                         int64_t HQ, int64_t H, int64_t K, int64_t V, float scale,
+                                         const int32_t *cu_seqlens, int64_t num_seqs, void *workspace,
+                                         size_t workspace_bytes, hipStream_t stream) {
+    if (!q || !k || !v || !g || !P) return WALL_ERR_INVALID_ARG;
+    const FwdShape s{B, T, HQ, H, K, V, cu_seqlens ? num_seqs : 0, T};
+    const wall_status_t st = check_fwd(dtype, s, cu_seqlens, num_seqs, T, workspace, workspace_bytes);
+    if (st != WALL_OK) return st;
+    if (g_dtype != WALL_BF16 && g_dtype != WALL_F32) return WALL_ERR_UNSUPPORTED;
+    const void *ptrs[] = {q, k, v, g, P};
+    for (const void *p : ptrs)
+        if (!aligned(p, 16)) return WALL_ERR_INVALID_ARG;
+    if (static_cast<const void *>(P) == g) return WALL_ERR_INVALID_ARG;
+    const FwdLayout L = fwd_layout(esize_of(dtype), B, T, HQ, H, K, V, s.nseq);
+    char *ws = static_cast<char *>(workspace);
+    void *sws = ws + L.off_scan;
+    const float pscale = 1.4426950408889634f;  // 1 / ln 2: P in log2 units
+    // one pass for B sequences of T rows (T a multiple of the tile) with bf16 inputs
+    if (!cu_seqlens && dtype == WALL_BF16 && g_dtype == WALL_BF16 && T % TILE == 0 && (HQ * K) % 8 == 0) {
+        wall_status_t sc = launched(launch_scan_carry(g, true, B, T, HQ * K, sws, stream));
+        if (sc != WALL_OK) return sc;
+        const ScanLayout SL = scan_layout(B, T, HQ * K);
+        PrepArgs pa{q, k, v, P, reinterpret_cast<SegInfo *>(ws + L.off_seg), nullptr,
+                    reinterpret_cast<float *>(ws + L.off_anchor), reinterpret_cast<uint32_t *>(ws + L.off_rec),
+                    ws + L.off_kt, ws + L.off_vt, ws + L.off_kd, ws + L.off_qd,
+                    reinterpret_cast<uint32_t *>(ws + L.off_drec), scale * LOG2E, L.nseg, L.tiles, HQ, H, K, V, T};
+        pa.g = g;
+        pa.Pw = P;
+        pa.carry = reinterpret_cast<const float *>(static_cast<const char *>(sws) + SL.off_carry);
+        pa.pscale = pscale;
+        return launched(launch_scan_prep(pa, stream));
+    }
+    // otherwise the scan, then the preparation
+    wall_status_t sc = launched(launch_scan(g, g_dtype == WALL_BF16, P, B, T, HQ * K, cu_seqlens,
+                                            cu_seqlens ? num_seqs : 0, pscale, sws, stream));
+    if (sc != WALL_OK) return sc;
+    return enqueue_prepare(q, k, v, dtype, P, scale, s, cu_seqlens, workspace, stream);
+}
+
 wall_status_t wall_attn_fwd_run(const void *q, const void *k, const void *v, wall_dtype_t dtype,
                                 const float *P, const float *G, const float *sink_bias, void *o, float *lse,
                                 int64_t B, int64_t T, int64_t HQ, int64_t H, int64_t K, int64_t V,

@@ -450,7 +450,9 @@ __global__ __launch_bounds__(NTH_KV) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
             const float gj = (HAS_G && jok) ? a.G[tj * HQ + hq] : 0.f;
             // one query tile: S, dP, A, dS and dk += dS^T q~; S from the wave's k~
             // operands kget and the staged q~ rows passed through qget
-            auto tile = [&](int it, auto kget, auto qget) {
+            // FULL: the tile may skip the masks when every pair is visible (the
+            // own tile's few blocks always take the masked copy: one copy less code)
+            auto tile = [&](int it, auto kget, auto qget, auto FULL) {
                 const int cur = it & 1;
                 const int q0 = tile_q0(it);
                 const int qrow = swap23(l32);
@@ -498,7 +500,7 @@ __global__ __launch_bounds__(NTH_KV) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
                         db[c] = __builtin_convertvector(d8, bf16x8);
                     }
                 };
-                if (full)
+                if (decltype(FULL)::value && full)
                     softmax(std::false_type{});
                 else
                     softmax(std::true_type{});
@@ -520,7 +522,7 @@ __global__ __launch_bounds__(NTH_KV) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
                 for (int s = 0; s < K / 16; ++s) kop[s] = move(kop[s], s, NBK, wr + 1);
                 acc_to(NBK);
                 for (; it < n_off; ++it) {
-                    tile(it, [&](int s) { return kop[s]; }, [&](bf16x8 x, int) { return x; });
+                    tile(it, [&](int s) { return kop[s]; }, [&](bf16x8 x, int) { return x; }, std::true_type{});
                     __syncthreads();
                 }
             }
@@ -533,7 +535,7 @@ __global__ __launch_bounds__(NTH_KV) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
                         acc_to(x);
                         // q~ 2^(sA[x] - sA[wr + 1]): at most 1 for a later block
                         tile(it, [&](int s) { return kst[s]; },
-                             [&](bf16x8 qv, int s) { return move(qv, s, x, wr + 1); });
+                             [&](bf16x8 qv, int s) { return move(qv, s, x, wr + 1); }, std::false_type{});
                     }
                     __syncthreads();
                 }
@@ -742,7 +744,8 @@ __global__ __launch_bounds__(NTH, 2) void bwd_dq_mfma(BwdArgs a, int nblk) {
 
     // one key tile: S, dP, dS and dq += dS k~; S from the wave's q~ operands
     // qget and the staged k~ rows passed through kget
-    auto tile = [&](int k0, int cur, auto qget, auto kget) {
+    // FULL: as in the dk/dv kernel
+    auto tile = [&](int k0, int cur, auto qget, auto kget, auto FULL) {
         f32x16 S = 0.f, dP = 0.f;
         const int krow = swap23(l32);
 #pragma unroll
@@ -780,7 +783,7 @@ __global__ __launch_bounds__(NTH, 2) void bwd_dq_mfma(BwdArgs a, int nblk) {
                 db[c] = __builtin_convertvector(d8, bf16x8);
             }
         };
-        if (full)
+        if (decltype(FULL)::value && full)
             softmax(std::false_type{});
         else
             softmax(std::true_type{});
@@ -814,7 +817,7 @@ __global__ __launch_bounds__(NTH, 2) void bwd_dq_mfma(BwdArgs a, int nblk) {
         for (int s = 0; s < K / 16; ++s) qop[s] = lower_q(qop[s], s, w, 0);
         acc_to(0);
         for (; k0 < i0; k0 += BT, ++it) {
-            tile(k0, it & 1, [&](int s) { return qop[s]; }, [&](bf16x8 x, int) { return x; });
+            tile(k0, it & 1, [&](int s) { return qop[s]; }, [&](bf16x8 x, int) { return x; }, std::true_type{});
             advance(k0, it & 1);
         }
     }
@@ -828,7 +831,7 @@ __global__ __launch_bounds__(NTH, 2) void bwd_dq_mfma(BwdArgs a, int nblk) {
                 acc_to(x);
                 // k~ 2^(sA[w] - sA[x]): at most 1 for an earlier block
                 tile(k0, it & 1, [&](int s) { return qst[s]; },
-                     [&](bf16x8 kv, int s) { return lower_q(kv, s, w, x); });
+                     [&](bf16x8 kv, int s) { return lower_q(kv, s, w, x); }, std::false_type{});
             }
             advance(k0, it & 1);
         }

@@ -73,13 +73,34 @@ constexpr int DBLK = 32;
 // negative (a prefix that grows; the kernel then rebuilds q~ from q and P).
 constexpr int DREC_N = 2 * (TILE / DBLK);
 
+// Scan workspace: chunk tail sums | exclusive chunk carries | chunk flags.
+struct ScanLayout {
+    int64_t nchunk;
+    size_t off_sum, off_carry, off_flag, total;
+};
+
+inline ScanLayout scan_layout(int64_t B, int64_t T, int64_t C) {
+    ScanLayout L;
+    L.nchunk = cdiv(B * T, SCAN_CHUNK);
+    size_t o = 0;
+    L.off_sum = o;
+    o = align_up(o + sizeof(float) * (size_t)(L.nchunk * C), 256);
+    L.off_carry = o;
+    o = align_up(o + sizeof(float) * (size_t)(L.nchunk * C), 256);
+    L.off_flag = o;
+    o = align_up(o + sizeof(int32_t) * (size_t)L.nchunk, 256);
+    L.total = o;
+    return L;
+}
+
 // Forward workspace: segment table | anchors | carry records | rescaled key
 // tiles | transposed value tiles | block-anchored key and query tiles | the
-// diagonal phase's carry records (all but the table for bf16 inputs only).
+// diagonal phase's carry records (all but the table for bf16 inputs only) |
+// a scan workspace for the prefix of wall_attn_fwd_prepare_gate.
 struct FwdLayout {
     int64_t nseg;        // sequences (num_seqs with packing, else B)
     int64_t tiles;       // upper bound on sum_s ceil(len_s / TILE)
-    size_t off_seg, off_anchor, off_rec, off_kt, off_vt, off_kd, off_qd, off_drec, total;
+    size_t off_seg, off_anchor, off_rec, off_kt, off_vt, off_kd, off_qd, off_drec, off_scan, total;
 };
 
 inline FwdLayout fwd_layout(int64_t esize, int64_t B, int64_t T, int64_t HQ, int64_t H,
@@ -105,26 +126,9 @@ inline FwdLayout fwd_layout(int64_t esize, int64_t B, int64_t T, int64_t HQ, int
     o = align_up(o + (size_t)esize * (size_t)(L.tiles * HQ * TILE * K), 256);
     L.off_drec = o;
     o = align_up(o + sizeof(uint32_t) * (size_t)(L.tiles * HQ * DREC_N * (K / 2)), 256);
-    L.total = o;
-    return L;
-}
-
-// Scan workspace: chunk tail sums | exclusive chunk carries | chunk flags.
-struct ScanLayout {
-    int64_t nchunk;
-    size_t off_sum, off_carry, off_flag, total;
-};
-
-inline ScanLayout scan_layout(int64_t B, int64_t T, int64_t C) {
-    ScanLayout L;
-    L.nchunk = cdiv(B * T, SCAN_CHUNK);
-    size_t o = 0;
-    L.off_sum = o;
-    o = align_up(o + sizeof(float) * (size_t)(L.nchunk * C), 256);
-    L.off_carry = o;
-    o = align_up(o + sizeof(float) * (size_t)(L.nchunk * C), 256);
-    L.off_flag = o;
-    o = align_up(o + sizeof(int32_t) * (size_t)L.nchunk, 256);
+    // the prefix scan of wall_attn_fwd_prepare_gate
+    L.off_scan = o;
+    o = align_up(o + scan_layout(B, T, HQ * K).total, 256);
     L.total = o;
     return L;
 }
@@ -161,10 +165,28 @@ struct PrepArgs {
     uint32_t *drec;    // [tiles, HQ, DREC_N, K / 2] diagonal-phase carry records
     float qscale;      // scale * log2(e)
     int64_t nseg, tiles, HQ, H, K, V, T;
+    // the prefix built here (launch_scan_prep): the bf16 gate g [rows, HQ, K],
+    // P written [rows, HQ, K], the chunk carries of the scan's first two
+    // kernels [chunks, HQ*K], and the scale of the prefix
+    const void *g;
+    float *Pw;
+    const float *carry;
+    float pscale;
 };
 // bf16: the sequence table, anchors, carry records, key and value tiles;
 // float32: the sequence table only.
 hipError_t launch_prep(const PrepArgs &a, bool bf16, hipStream_t st);
+// The same preparation with the prefix built in the same pass from a bf16 gate
+// (B sequences of T rows, T a multiple of TILE, HQ*K a multiple of 8): P is
+// written once, at the rows that end a 32-row block from the block sums (and
+// at a tile's last row from the next tile's carry), so that each anchor is the
+// floor of the P stored at its row.  Needs the chunk sums and carries of
+// launch_scan_carry first.
+hipError_t launch_scan_prep(const PrepArgs &a, hipStream_t st);
+// The scan's chunk sums and carries alone (its first two kernels), for
+// B sequences of T rows, in a scan workspace of scan_layout(B, T, C).
+hipError_t launch_scan_carry(const void *x, bool x_bf16, int64_t B, int64_t T, int64_t C, void *ws,
+                             hipStream_t st);
 
 struct FwdArgs {
     const void *q;          // [rows, HQ, K]

@@ -94,6 +94,53 @@ struct Vec8<__bf16> {
     }
 };
 
+// The records of (tile, query head) for channels 8*c8 .. +7 (anchors R of the
+// tile, A of its 32-row blocks, Lp of the previous tile; `later`: the tile is
+// not its sequence's first): the anchor table entry, the tile's carry record
+// (the shift from R to Lp, a bf16 exponent decrement) and the diagonal records
+// (each block's shift from Lp, block b+1's to block b's).  Returns bit 0 set
+// when some channel's tile shift is negative (the prefix grows) and, from bit
+// 8, the diagonal records that grow.
+template <int K>
+__device__ inline uint32_t write_records(const PrepArgs &a, int tile, int hq, int c8, bool later, f32x8 R,
+                                         const f32x8 (&A)[TILE / DBLK], f32x8 Lp) {
+    constexpr int NB = TILE / DBLK;
+    const int64_t HQ = a.HQ;
+    *reinterpret_cast<f32x8 *>(a.anchor + ((int64_t)tile * HQ + hq) * K + c8 * 8) = R;
+    auto shift = [](float d) { return (uint32_t)fminf(fmaxf(d, 0.f), 255.f) * 128u; };
+    bool up = false;
+    uint32_t dgrow = 0;
+    uint32_t *rec = a.rec + ((int64_t)tile * HQ + hq) * REC_WORDS;
+    uint32_t *drec = a.drec + ((int64_t)tile * HQ + hq) * DREC_N * (K / 2);
+    for (int e = 0; e < 8; e += 2) {
+        const int wd = (c8 * 8 + e) / 2;
+        uint32_t w = 0;
+        if (later) {
+            const float d0 = Lp[e] - R[e], d1 = Lp[e + 1] - R[e + 1];
+            up = up || d0 < 0.f || d1 < 0.f;
+            w = shift(d0) | (shift(d1) << 16);
+        }
+        rec[wd] = w;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            uint32_t x = 0;
+            if (later) {
+                const float d0 = Lp[e] - A[b][e], d1 = Lp[e + 1] - A[b][e + 1];
+                if (d0 < 0.f || d1 < 0.f) dgrow |= 1u << b;
+                x = shift(d0) | (shift(d1) << 16);
+            }
+            drec[b * (K / 2) + wd] = x;
+        }
+#pragma unroll
+        for (int b = 0; b + 1 < NB; ++b) {
+            const float d0 = A[b][e] - A[b + 1][e], d1 = A[b][e + 1] - A[b + 1][e + 1];
+            if (d0 < 0.f || d1 < 0.f) dgrow |= 1u << (NB + b);
+            drec[(NB + b) * (K / 2) + wd] = shift(d0) | (shift(d1) << 16);
+        }
+    }
+    return (up ? 1u : 0u) | (dgrow << 8);
+}
+
 template <int K>
 __device__ inline void key_tile(const PrepArgs &a, int tile, int hq, const SegInfo &sg) {
     constexpr int CPR = K / 8;          // 8-channel chunks per row
@@ -120,50 +167,15 @@ __device__ inline void key_tile(const PrepArgs &a, int tile, int hq, const SegIn
         for (int e = 0; e < 8; ++e) A[b][e] = floorf(pb[e]);
     }
     if (r0 == 0) {
-        float *ap = a.anchor + ((int64_t)tile * HQ + hq) * K + c8 * 8;
-        *reinterpret_cast<f32x8 *>(ap) = R;
-        // carry records: the shift from this tile's anchors to the previous
-        // tile's, and the diagonal phase's (each block's anchor to the previous
-        // tile's, block b+1's to block b's)
-        auto shift = [](float d) { return (uint32_t)fminf(fmaxf(d, 0.f), 255.f) * 128u; };
         f32x8 Lp = R;  // the previous tile's anchors (none for a sequence's first tile)
         if (c > 0) {
             const float *Pp = a.P + ((int64_t)(sg.start + c * TILE - 1) * HQ + hq) * K + c8 * 8;
             for (int e = 0; e < 8; ++e) Lp[e] = floorf(Pp[e]);
         }
-        bool up = false;
-        uint32_t dgrow = 0;
-        uint32_t *rec = a.rec + ((int64_t)tile * HQ + hq) * REC_WORDS;
-        uint32_t *drec = a.drec + ((int64_t)tile * HQ + hq) * DREC_N * (K / 2);
-        for (int e = 0; e < 8; e += 2) {
-            const int wd = (c8 * 8 + e) / 2;
-            uint32_t w = 0;
-            if (c > 0) {
-                const float d0 = Lp[e] - R[e], d1 = Lp[e + 1] - R[e + 1];
-                up = up || d0 < 0.f || d1 < 0.f;
-                w = shift(d0) | (shift(d1) << 16);
-            }
-            rec[wd] = w;
-#pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                uint32_t x = 0;
-                if (c > 0) {
-                    const float d0 = Lp[e] - A[b][e], d1 = Lp[e + 1] - A[b][e + 1];
-                    if (d0 < 0.f || d1 < 0.f) dgrow |= 1u << b;
-                    x = shift(d0) | (shift(d1) << 16);
-                }
-                drec[b * (K / 2) + wd] = x;
-            }
-#pragma unroll
-            for (int b = 0; b + 1 < NB; ++b) {
-                const float d0 = A[b][e] - A[b + 1][e], d1 = A[b][e + 1] - A[b + 1][e + 1];
-                if (d0 < 0.f || d1 < 0.f) dgrow |= 1u << (NB + b);
-                drec[(NB + b) * (K / 2) + wd] = shift(d0) | (shift(d1) << 16);
-            }
-        }
-        const bool any_up = __any(up);  // the r0 == 0 threads are lanes 0..K/8-1 of wave 0
-        if (threadIdx.x == 0) rec[REC_GROW] = any_up ? 1u : 0u;
-        if (dgrow) atomicOr(&sflag, dgrow << 8);
+        const uint32_t gr = write_records<K>(a, tile, hq, c8, c > 0, R, A, Lp);
+        const bool any_up = __any(gr & 1u);  // the r0 == 0 threads are lanes 0..K/8-1 of wave 0
+        if (threadIdx.x == 0) a.rec[((int64_t)tile * HQ + hq) * REC_WORDS + REC_GROW] = any_up ? 1u : 0u;
+        if (gr >> 8) atomicOr(&sflag, gr & ~0xffu);
     }
     const __bf16 *qin = static_cast<const __bf16 *>(a.q);
     const __bf16 *kin = static_cast<const __bf16 *>(a.k);
@@ -197,11 +209,11 @@ __device__ inline void key_tile(const PrepArgs &a, int tile, int hq, const SegIn
             f32x8 kl, kb, qb;
             float dev = 0.f;
             for (int e = 0; e < 8; ++e) {
-                kl[e] = kv[i][e] * exp2f(fminf(fmaxf(R[e] - pv[i][e], EXP2_LO), EXP2_HI));
+                kl[e] = kv[i][e] * __builtin_amdgcn_exp2f(fminf(fmaxf(R[e] - pv[i][e], EXP2_LO), EXP2_HI));
                 const float x = pv[i][e] - A[b][e];
                 dev = fmaxf(dev, fabsf(x));
-                kb[e] = kv[i][e] * exp2f(fminf(fmaxf(-x, EXP2_LO), EXP2_HI));
-                qb[e] = qv[i][e] * a.qscale * exp2f(fminf(fmaxf(x, EXP2_LO), EXP2_HI));
+                kb[e] = kv[i][e] * __builtin_amdgcn_exp2f(fminf(fmaxf(-x, EXP2_LO), EXP2_HI));
+                qb[e] = qv[i][e] * a.qscale * __builtin_amdgcn_exp2f(fminf(fmaxf(x, EXP2_LO), EXP2_HI));
             }
             if (valid && dev > DIAG_SPREAD) flags |= 1u << b;
             Vec8<__bf16>::store(kout + row * K + c8 * 8, kl);
@@ -256,6 +268,165 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
         value_tile<__bf16, V>(a, tile, y - (int)a.HQ, sg);
 }
 
+// ---------------------------------------------------------------- prefix and preparation in one pass
+// B sequences of T rows with T a multiple of TILE, so the scan's 128-row
+// chunks are the tiles.  Block (tile c, slice y) takes SP_CV vectors of 8
+// channels of HQ*K (one or two whole query heads), thread (sub, cv) the 8 rows
+// of subgroup sub (of 16) and channels 8*cv .. +7 of the slice.  Pass 1 sums
+// each thread's rows of g; from the tile's carry and the subgroup sums every
+// thread then knows the prefix E_b at the end of each 32-row block (the sums
+// of its four subgroups added in order to E_(b-1), E_(-1) = the carry; E_3 =
+// the next tile's carry when that tile is in the same sequence, so that the
+// next tile's Lp is the floor of the P stored here).  Pass 2 runs along the
+// thread's rows from the prefix before its subgroup: P = pscale * the running
+// sum, except P = pscale * E_b at a block's last row, so that the anchors
+// A_b = floor(pscale * E_b) and R = A_3 are the floors of the P stored at
+// their rows; it writes P and the tile's keys and queries as key_tile does.
+// Value tiles and the sequence table as in prep_kernel.
+constexpr int SP_SUB = 8;                 // rows per thread
+constexpr int SP_NSUB = TILE / SP_SUB;    // subgroups per tile
+constexpr int SP_CV = 256 / SP_NSUB;      // channel vectors per block
+__device__ inline bf16x8 raw8(const __bf16 *p) { return *reinterpret_cast<const bf16x8 *>(p); }
+template <int K>
+__device__ inline void scan_key_slice(const PrepArgs &a, int tile, int y) {
+    constexpr int NB = TILE / DBLK, SPB = DBLK / SP_SUB;  // blocks per tile, subgroups per block
+    constexpr int HPS = (SP_CV * 8 + K - 1) / K;            // query heads per slice
+    __shared__ f32x8 ssum[SP_NSUB][SP_CV];
+    __shared__ uint32_t sflag[HPS], sgrow[HPS];
+    const int tid = threadIdx.x, sub = tid / SP_CV, cv = tid % SP_CV, rb = sub / SPB;
+    const int64_t C = a.HQ * K, HQ = a.HQ;
+    const int64_t ch = ((int64_t)y * SP_CV + cv) * 8;
+    const bool on = ch < C;
+    const int hq = (int)(ch / K), hl = cv / (K / 8), c8 = (int)((ch % K) / 8);
+    const int h = hq / (int)(a.HQ / a.H);
+    const int tps = (int)(a.T / TILE), c = tile % tps;  // tile within its sequence
+    const int64_t row0 = (int64_t)tile * TILE + SP_SUB * sub;  // the thread's first flat row
+    const __bf16 *gin = static_cast<const __bf16 *>(a.g);
+    if (tid < HPS) {
+        sflag[tid] = 0u;
+        sgrow[tid] = 0u;
+    }
+    // pass 1: the sum of the thread's rows
+    f32x8 s = {};
+    if (on) {
+        bf16x8 x[SP_SUB];
+#pragma unroll
+        for (int i = 0; i < SP_SUB; ++i) x[i] = raw8(gin + (row0 + i) * C + ch);
+#pragma unroll
+        for (int i = 0; i < SP_SUB; ++i) s += __builtin_convertvector(x[i], f32x8);
+    }
+    ssum[sub][cv] = s;
+    __syncthreads();
+    bool spread = false;
+    if (on) {
+        // the running sum before the tile (the scan's carry holds the previous
+        // sequence's at a sequence's first tile: that tile starts from 0)
+        f32x8 carry = {};
+        if (c > 0) carry = *reinterpret_cast<const f32x8 *>(a.carry + (int64_t)tile * C + ch);
+        // the prefix at the end of each block and before the thread's subgroup
+        f32x8 E[NB], A[NB], run = carry;
+        f32x8 acc = carry;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+#pragma unroll
+            for (int u = 0; u < SPB; ++u) {
+                if (b * SPB + u == sub) run = acc;
+                acc += ssum[b * SPB + u][cv];
+            }
+            E[b] = acc;
+        }
+        if (c + 1 < tps) E[NB - 1] = *reinterpret_cast<const f32x8 *>(a.carry + (int64_t)(tile + 1) * C + ch);
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) A[b][e] = floorf(a.pscale * E[b][e]);
+        const f32x8 R = A[NB - 1];
+        if (sub == 0) {
+            f32x8 Lp = R;
+            if (c > 0)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) Lp[e] = floorf(a.pscale * carry[e]);
+            const uint32_t gr = write_records<K>(a, tile, hq, c8, c > 0, R, A, Lp);
+            if (gr) atomicOr(&sgrow[hl], gr);
+        }
+        // pass 2: P along the rows, then the keys and queries at the anchors
+        const f32x8 Ab = A[rb], Eb = E[rb];
+        const __bf16 *qin = static_cast<const __bf16 *>(a.q);
+        const __bf16 *kin = static_cast<const __bf16 *>(a.k);
+        const int64_t o0 = ((int64_t)tile * HQ + hq) * TILE * K + c8 * 8;
+        __bf16 *kout = static_cast<__bf16 *>(a.kt) + o0;
+        __bf16 *kdout = static_cast<__bf16 *>(a.kd) + o0;
+        __bf16 *qdout = static_cast<__bf16 *>(a.qd) + o0;
+        // the rows' loads in flight as raw bf16 before any is used
+        bf16x8 x[SP_SUB], kr[SP_SUB], qr[SP_SUB];
+#pragma unroll
+        for (int i = 0; i < SP_SUB; ++i) {
+            const int64_t r = row0 + i;
+            x[i] = raw8(gin + r * C + ch);
+            kr[i] = raw8(kin + (r * a.H + h) * K + c8 * 8);
+            qr[i] = raw8(qin + r * C + ch);
+        }
+        const bool ends_block = (sub + 1) % SPB == 0;  // the thread holds its block's last row
+#pragma unroll
+        for (int i = 0; i < SP_SUB; ++i) {
+            const int row = SP_SUB * sub + i;
+            const f32x8 kv = __builtin_convertvector(kr[i], f32x8), qv = __builtin_convertvector(qr[i], f32x8);
+            run += __builtin_convertvector(x[i], f32x8);
+            const bool last = ends_block && i == SP_SUB - 1;
+            f32x8 pv, kl, kb, qb;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                pv[e] = a.pscale * (last ? Eb[e] : run[e]);
+                kl[e] = kv[e] * __builtin_amdgcn_exp2f(fminf(fmaxf(R[e] - pv[e], EXP2_LO), EXP2_HI));
+                const float d = pv[e] - Ab[e];
+                spread = spread || fabsf(d) > DIAG_SPREAD;
+                kb[e] = kv[e] * __builtin_amdgcn_exp2f(fminf(fmaxf(-d, EXP2_LO), EXP2_HI));
+                qb[e] = qv[e] * a.qscale * __builtin_amdgcn_exp2f(fminf(fmaxf(d, EXP2_LO), EXP2_HI));
+            }
+            float *pw = a.Pw + ((int64_t)tile * TILE + row) * C + ch;
+            reinterpret_cast<f32x4 *>(pw)[0] = f32x4{pv[0], pv[1], pv[2], pv[3]};
+            reinterpret_cast<f32x4 *>(pw)[1] = f32x4{pv[4], pv[5], pv[6], pv[7]};
+            Vec8<__bf16>::store(kout + row * K, kl);
+            Vec8<__bf16>::store(kdout + row * K, kb);
+            Vec8<__bf16>::store(qdout + row * K, qb);
+        }
+    }
+    if (spread) atomicOr(&sflag[hl], 1u << rb);
+    __syncthreads();
+    if (on && c8 == 0 && sub == 0) {
+        uint32_t *rec = a.rec + ((int64_t)tile * HQ + hq) * REC_WORDS;
+        rec[REC_GROW] = sgrow[hl] & 1u;
+        rec[REC_DIAG] = sflag[hl] | (sgrow[hl] & ~0xffu);
+    }
+}
+
+// Block id = tile * (nslice + H) + y; y < nslice: keys of slice y, else the
+// values of kv head y - nslice.
+template <int K, int V>
+__global__ __launch_bounds__(256) void scan_prep_kernel(PrepArgs a, int nslice) {
+    const int nh = nslice + (int)a.H;
+    const int tile = blockIdx.x / nh, y = blockIdx.x % nh;
+    if (tile == 0 && y == 0) {
+        const int T = (int)a.T, tps = T / TILE;
+        for (int i = threadIdx.x; i < a.nseg; i += blockDim.x) a.seg[i] = SegInfo{i * T, T, i * tps, 0};
+    }
+    if (y < nslice) {
+        scan_key_slice<K>(a, tile, y);
+    } else {
+        const int T = (int)a.T, tps = T / TILE, s = tile / tps;
+        value_tile<__bf16, V>(a, tile, y - nslice, SegInfo{s * T, T, s * tps, 0});
+    }
+}
+
+template <int K, int V>
+hipError_t run_scan_prep(const PrepArgs &a, hipStream_t st) {
+    const int nslice = (int)cdiv(a.HQ * K, (int64_t)SP_CV * 8);
+    const int64_t tiles = a.nseg * (a.T / TILE);
+    hipLaunchKernelGGL((scan_prep_kernel<K, V>), dim3((unsigned)(tiles * (nslice + a.H))), dim3(256), 0, st, a,
+                       nslice);
+    return hipGetLastError();
+}
+
 // The sequence table alone (the float32 forward reads the raw tensors).
 __global__ __launch_bounds__(256) void seg_table_kernel(PrepArgs a) {
     SegInfo sg;
@@ -269,6 +440,13 @@ hipError_t run_prep(const PrepArgs &a, hipStream_t st) {
 }
 
 }  // namespace
+
+hipError_t launch_scan_prep(const PrepArgs &a, hipStream_t st) {
+    if (a.K == 64 && a.V == 64) return run_scan_prep<64, 64>(a, st);
+    if (a.K == 64 && a.V == 128) return run_scan_prep<64, 128>(a, st);
+    if (a.K == 128 && a.V == 64) return run_scan_prep<128, 64>(a, st);
+    return run_scan_prep<128, 128>(a, st);
+}
 
 hipError_t launch_prep(const PrepArgs &a, bool bf16, hipStream_t st) {
     if (!bf16) {

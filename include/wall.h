@@ -236,6 +236,33 @@ wall_status_t wall_attn_fwd_prepare(const void *q, const void *k, const void *v,
                                     void *workspace, size_t workspace_bytes,
                                     hipStream_t stream);
 
+/* wall_attn_fwd_prepare_gate: the prefix scan and the preparation in one
+ * call.  It writes P = cumsum(g) / ln 2 per sequence (what wall_prefix_scan
+ * with scale 1/ln 2 writes) and prepares `workspace` as wall_attn_fwd_prepare
+ * does with that P; wall_attn_fwd_run then takes that P.
+ *
+ *   g        [B, T, HQ, K] in g_dtype (WALL_BF16 or WALL_F32), natural-log gate
+ *   P        [B, T, HQ, K] float32 (written; may not alias g)
+ *   other arguments as for wall_attn_fwd_prepare (scale as for wall_attn_fwd)
+ *
+ * B sequences of T rows (no cu_seqlens) with T a multiple of 128, bf16 q, k,
+ * v and g and HQ*K a multiple of 8 take one combined pass: the scan's chunk
+ * sums and carries (two small kernels), then one kernel that forms P along
+ * the rows, writes it, and builds the anchored tiles from it without reading
+ * it back.  There, at the last row of each 32-row block P is formed from the
+ * block sums (at a tile's last row from the next tile's carry), so every
+ * anchor is the floor of the P stored at its row; P then differs from
+ * wall_prefix_scan's in float32 rounding only.  Any other case runs the scan
+ * and the preparation one after the other (P exactly wall_prefix_scan's).
+ * Errors: those of wall_attn_fwd_prepare; INVALID_ARG for a null g or P, P
+ * aliasing g or misaligned; UNSUPPORTED for another g_dtype. */
+wall_status_t wall_attn_fwd_prepare_gate(const void *q, const void *k, const void *v, wall_dtype_t dtype,
+                                         const void *g, wall_dtype_t g_dtype, float *P,
+                                         int64_t B, int64_t T, int64_t HQ, int64_t H, int64_t K, int64_t V,
+                                         float scale, const int32_t *cu_seqlens, int64_t num_seqs,
+                                         void *workspace, size_t workspace_bytes,
+                                         hipStream_t stream);
+
 wall_status_t wall_attn_fwd_run(const void *q, const void *k, const void *v, wall_dtype_t dtype,
                                 const float *P, const float *G, const float *sink_bias,
                                 void *o, float *lse,

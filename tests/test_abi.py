@@ -181,6 +181,26 @@ def test_decode_rejects_invalid_arguments(kw):
     assert decode(**kw) == INVALID
 
 
+def gate_prep(q=FAKE, k=FAKE, v=FAKE, dtype=B.WALL_BF16, g=FAKE * 2, gdt=B.WALL_BF16, Pw=FAKE * 3, b=1, t=256,
+              hq=4, h=2, kk=128, vv=128, cu=None, nseq=0, ws=FAKE * 4, wsb=None):
+    L = wall.lib()
+    if wsb is None:
+        wsb = L.wall_attn_fwd_workspace_size(dtype if dtype in (0, 1) else 1, b, t, hq, h, kk, vv, nseq)
+    return L.wall_attn_fwd_prepare_gate(P(q), P(k), P(v), dtype, P(g), gdt, P(Pw), b, t, hq, h, kk, vv, 0.088,
+                                        P(cu), nseq, P(ws), wsb, None)
+
+
+@pytest.mark.parametrize("kw", [dict(g=None), dict(Pw=None), dict(q=None), dict(Pw=FAKE * 2), dict(g=FAKE * 2 + 4),
+                                dict(wsb=64), dict(hq=6, h=4), dict(b=2, cu=FAKE * 5, nseq=2)])
+def test_prepare_gate_rejects_invalid_arguments(kw):
+    assert gate_prep(**kw) == INVALID
+
+
+@pytest.mark.parametrize("kw", [dict(gdt=5), dict(kk=96), dict(dtype=5)])
+def test_prepare_gate_rejects_unsupported(kw):
+    assert gate_prep(**kw) == UNSUPPORTED
+
+
 @pytest.mark.parametrize("kw", [dict(kk=96), dict(vv=32), dict(c=32), dict(c=0 + 96), dict(dtype=5)])
 def test_decode_rejects_unsupported_shapes(kw):
     assert decode(**kw) == UNSUPPORTED
@@ -261,8 +281,10 @@ def test_workspace_sizes():
     b16 = L.wall_attn_fwd_workspace_size(1, 1, 8192, 16, 4, 128, 128, 0)
     f32 = L.wall_attn_fwd_workspace_size(0, 1, 8192, 16, 4, 128, 128, 0)
     # bf16: key cache per query head + value tiles per kv head, 65 tiles bound;
-    # float32 reads the raw tensors and keeps only the sequence table
-    assert b16 >= 65 * 128 * (16 * 128 + 4 * 128) * 2 and 0 < f32 <= 256
+    # float32 reads the raw tensors and keeps the sequence table and, for
+    # wall_attn_fwd_prepare_gate, a prefix-scan workspace
+    assert b16 >= 65 * 128 * (16 * 128 + 4 * 128) * 2
+    assert a <= f32 <= a + 256
     assert L.wall_attn_fwd_workspace_size(1, 1, 1000, 2, 1, 64, 64, 9) > \
         L.wall_attn_fwd_workspace_size(1, 1, 1000, 2, 1, 64, 64, 1)
 

@@ -260,6 +260,63 @@ def test_running_max_raised_in_interior_tiles(kv):
     assert_parity(o, lse, o_ref, lse_ref, "bfloat16", what=f"raised max K={K} V={V}")
 
 
+# --------------------------------------------------------------------------- prefix and preparation from the gate
+
+GATE_CASES = {
+    # one combined pass (B sequences of T rows, T a multiple of 128, bf16)
+    "combined_3tiles": lambda: make_inputs("long_bf16", B=2, T=384, HQ=4, H=2),
+    "combined_small_gates_k64": lambda: make_inputs("gqa_bf16", B=2, T=256, HQ=8, H=4),
+    "combined_k64_v128": lambda: make_inputs("long_bf16", B=1, T=256, HQ=2, H=1, K=64, V=128),
+    "combined_options": lambda: make_inputs("options_bf16", B=2, T=256, HQ=4, H=2, window=100),
+    # the scan, then the preparation
+    "ragged_T": lambda: make_inputs("long_bf16", B=1, T=300, HQ=2, H=1),
+    "packed": lambda: _varlen(make_inputs("varlen_bf16", T=600, HQ=2, H=1, nseq=None), [0, 1, 250, 600]),
+    "float32": lambda: make_inputs("tiny_fp32", B=1, T=256, HQ=2, H=1),
+}
+
+
+def _gate_run(inp, case):
+    say(f"prefix + preparation from the gate: {case}")
+    d = inp.to(DEV)
+    G = None if d.g_scalar is None else wall.wall_prefix_scan(d.g_scalar, d.cu_seqlens)
+    o, lse, P = wall.wall_attn_fwd_gate(d.q, d.k, d.v, d.g, G, d.sink_bias, d.scale, d.window_size,
+                                        d.cu_seqlens)
+    P_scan = wall.wall_prefix_scan(d.g, d.cu_seqlens)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), lse.cpu().numpy(), P.cpu().double().numpy(), P_scan.cpu().double().numpy()
+
+
+@pytest.mark.parametrize("case", sorted(GATE_CASES))
+def test_prepare_from_gate(case):
+    """wall_attn_fwd_prepare_gate + wall_attn_fwd_run: P within float32 rounding of
+    the oracle's prefix (and of the scan's: equal to it bit for bit where the
+    scan runs first), o and lse at the forward's bar against the oracle."""
+    inp = GATE_CASES[case]()
+    o, lse, P, P_scan = _gate_run(inp, case)
+    P_ref = oracle.prefix_scan_oracle(inp.g, inp.cu_seqlens)
+    big = max(1.0, float(np.abs(P_ref).max()))
+    say(f"  max|P - oracle| = {np.abs(P - P_ref).max():.3e} (max|P| {big:.3e}); "
+        f"max|P - scan| = {np.abs(P - P_scan).max():.3e}")
+    assert np.abs(P - P_ref).max() <= 1e-5 * big
+    assert np.abs(P - P_scan).max() <= 4e-6 * big
+    if case in ("ragged_T", "packed", "float32"):
+        assert np.array_equal(P, P_scan), "the scan-then-preparation path writes the scan's P"
+    o_ref, lse_ref = run_oracle(inp)
+    assert_parity(o, lse, o_ref, lse_ref, inp.spec.dtype, what=case)
+
+
+@pytest.mark.parametrize("gate", [-5.0, -800.0])
+def test_prepare_from_gate_strong_decay(gate):
+    """The combined pass under strong uniform decay: every anchor is the floor of
+    the P stored at its row, so the forward stays exact (g = -800: the closed
+    form of the oracle, every earlier key's decay 0)."""
+    inp = make_inputs("long_bf16", B=2, T=384, HQ=2, H=1)
+    inp.g = torch.full_like(inp.g, gate)
+    o, lse, P, _ = _gate_run(inp, f"uniform g={gate}")
+    o_ref, lse_ref = run_oracle(inp)
+    assert_parity(o, lse, o_ref, lse_ref, "bfloat16", what=f"gate path g={gate}")
+
+
 # --------------------------------------------------------------------------- full sizes
 
 
