@@ -61,6 +61,16 @@
 //       max, move the scores, owe O a rescale and redo the exps;
 //   O^T += v^T p^T on the same MFMA, p as bf16.
 //
+// Channel steps that have died (K = 128).  A channel that forgets fast (the
+// blog's fast-forgetting channel group) leaves q~ = 0 in bf16 once a tile
+// or two of decay lies between the keys and the wave's queries, and the
+// carries only lower exponents further back.  At each tile boundary a wave
+// whose queries all have q~ = 0 on the upper half of the channel steps (a
+// ballot over its registers) stops issuing those steps' score products and
+// carries for the rest of the pass: the products it drops are exactly 0, so
+// the result is unchanged bit for bit.  A pass with a tile where some
+// channel's prefix grows (q~ is rebuilt there) never drops them.
+//
 // Software pipeline.  Step b of tile c runs the softmax of sub-block b, the QK
 // products of the next sub-block (b-1, or sub-block 3 of tile c-1) and the PV
 // products of the previous one (b+1, or sub-block 0 of tile c+1), as one
@@ -293,7 +303,7 @@ constexpr bool is_read(int kind) { return kind == O_PV || kind == O_QK || kind =
 template <int K, int V>
 struct TilePlan {
     static constexpr int VT = V / 32, KS = K / 16;
-    static constexpr int NPV = 2 * VT, NQK = KS, NSMD = 8, NC1 = KS / 2;
+    static constexpr int NPV = 2 * VT, NQK = KS, NSMD = 8, NCAR = KS, NC1 = NCAR / 2;
     static constexpr int MAXOPS = NSB * (NPV + NQK + KS + 16) + 4;
     using OpArr = std::array<TOp, MAXOPS>;
     // vector instructions per op (the common path), used to spread them evenly
@@ -341,11 +351,11 @@ struct TilePlan {
         int nc = 0;
         chain[nc++] = TOp{O_SMA, b, 0};
         for (int k = 0; k < NSMD; ++k) chain[nc++] = TOp{O_SMD, b, k};
-        const int c_hi = b <= 1 ? KS : 0;  // carries allowed in this step
+        const int c_hi = b <= 1 ? NCAR : 0;  // carries allowed in this step
         int ch_total = 0;
         for (int i = 0; i < nc; ++i) ch_total += cost(chain[i].kind);
         // the carries' budget and the products they are spread over
-        const int car_total = b == 1 ? NC1 * cost(O_CARRY) : b == 0 ? (KS - car) * cost(O_CARRY) : 0;
+        const int car_total = b == 1 ? NC1 * cost(O_CARRY) : b == 0 ? (NCAR - car) * cost(O_CARRY) : 0;
         const int car_slots = b == 0 ? NPV - 2 : nmfma;
         int ci = 0, ch_placed = 0, car_placed = 0, done = 0, sma_slot = -1;
         bool qk_done[KS]{};
@@ -418,7 +428,7 @@ struct TilePlan {
     static constexpr int NR = make_nr();  // LDS operand reads per tile
     // Reads kept in flight: the largest of 7..4 that divides NR, so a read has
     // the same ring slot in every tile.
-    static constexpr int NPF = NR % 7 == 0 ? 7 : NR % 6 == 0 ? 6 : NR % 5 == 0 ? 5 : 4;
+    static constexpr int NPF = (K == 128 && NR % 4 == 0) ? 4 : NR % 7 == 0 ? 7 : NR % 6 == 0 ? 6 : NR % 5 == 0 ? 5 : 4;
     static_assert(NR % NPF == 0, "reads per tile must fill whole rings");
 
     static constexpr int pos_of(int kind) {
@@ -484,6 +494,9 @@ struct Wave {
     using VL = typename LY::VL;
     using Plan = TilePlan<K, V>;
     static constexpr int VT = V / 32, KS = K / 16, NPF = Plan::NPF;
+    // K = 128: a wave whose queries' q~ is 0 on the upper half of the channel
+    // steps skips those steps' score products and carries
+    static constexpr bool HAS_HALF = K == 128;
 
     // per-lane constants
     int kbase, vbase, hl, qrow;
@@ -501,6 +514,7 @@ struct Wave {
     uint32_t Pw[2][2][4];  // Pw[b & 1][t]: packed bf16 p of that sub-block, keys 16t + 8hl + e
     bf16x8 ring[NPF];      // LDS operand reads in flight
     float ex[2][2];        // exps of the last two key pairs, packed one op later
+    bool half;             // q~ is 0 on the upper half of the channel steps (wave-uniform)
     float part[2];         // partial row sums of the current step
 
     // buffers: keys of this tile and the next (older) one, values of this tile
@@ -519,7 +533,7 @@ struct Wave {
         return __builtin_bit_cast(bf16x8, uint4{w[0], w[1], w[2], w[3]});
     }
 
-    // ---- operand address of read r (NEXT: a read of the next tile's step 3)
+    // ---- operand address of read r of plan PL (NEXT: a read of the next tile's step 3)
     template <int R>
     __device__ __forceinline__ const bf16x8 *src() const {
         constexpr bool NEXT = R >= Plan::NR;
@@ -547,6 +561,17 @@ struct Wave {
     template <int... Rs>
     __device__ __forceinline__ void read_first(std::integer_sequence<int, Rs...>) {
         (read<Rs>(), ...);
+    }
+    // every query of the wave has q~ = 0 (either sign) on the upper half of the
+    // channel steps (wave-uniform)
+    __device__ __forceinline__ bool upper_dead() const {
+        uint32_t acc = 0u;
+#pragma unroll
+        for (int s8 = KS / 2; s8 < KS; ++s8) {
+            const uint4 x = __builtin_bit_cast(uint4, qop[s8]);
+            acc |= x.x | x.y | x.z | x.w;
+        }
+        return __builtin_amdgcn_ballot_w64((acc & 0x7fff7fffu) != 0u) == 0u;
     }
 
     // ---- softmax stages of step B on S[B & 1]
@@ -738,8 +763,10 @@ struct Kernel {
         } else if constexpr (o.kind == O_QK) {
             const bf16x8 x = wv.ring[Plan::READ_OF[P] % NPF];
             f32x16 &sn = wv.S[(B + 1) & 1];
+            if (W::HAS_HALF && o.idx >= KS / 2 && wv.half) return;
             sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, wv.qop[o.idx], o.idx == 0 ? wv.negm : sn, 0, 0, 0);
         } else if constexpr (o.kind == O_CARRY) {
+            if (W::HAS_HALF && o.idx >= KS / 2 && wv.half) return;
             const bf16x8 x = wv.ring[Plan::READ_OF[P] % NPF];
             // lower each bf16 exponent field by the shift, saturating on the
             // magnitude (the four words interleaved: no op waits on the one before)
@@ -998,9 +1025,13 @@ struct Kernel {
         reads_after<P>(std::make_integer_sequence<int, NR>{});
     }
     template <int PB, bool DEAD, int... Ps>
-    __device__ __forceinline__ void run_tile(int c, std::integer_sequence<int, Ps...>) {
+    __device__ __forceinline__ void run_tile_ops(int c, std::integer_sequence<int, Ps...>) {
         (step<PB, Ps, DEAD>(c), ...);
         __builtin_amdgcn_sched_barrier(0);
+    }
+    template <int PB>
+    __device__ __forceinline__ void run_tile(int c) {
+        run_tile_ops<PB, false>(c, std::make_integer_sequence<int, N>{});
     }
 };
 
@@ -1111,6 +1142,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
         for (int vt = 0; vt < VT; ++vt) wv.O[vt] = f32x16{};
         wv.negm = f32x16{};
         wv.m = 0.f;
+        wv.half = false;
         wv.l = 0.f;
         wv.alpha = 1.f;
         wv.lim = wave_on ? -1.f : __builtin_inff();  // a wave with no rows never raises
@@ -1140,15 +1172,33 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
             wv.vprev = v1;
             wv.read_first(std::make_integer_sequence<int, NPF>{});
 
+            // A wave whose queries' q~ is 0 on the upper half of the channel
+            // steps at a tile's anchors stays so at every earlier tile's (the
+            // carries only lower exponents), unless some tile's prefix grows
+            // and q~ is rebuilt: without such a tile in the pass, the wave runs
+            // the half plan from the first tile where it finds that half dead.
+            bool half_ok = false;
+            if constexpr (W::HAS_HALF) {
+                bool grow = false;
+                for (int c0 = c_lo; c0 <= c_hi; c0 += 64) {
+                    const int ct = c0 + lane;
+                    const bool gr = ct <= c_hi &&
+                                    a.rec[((int64_t)(sg.tile_base + ct) * HQ + hq) * REC_WORDS + REC_GROW] != 0u;
+                    grow = grow || __builtin_amdgcn_ballot_w64(gr) != 0u;
+                }
+                half_ok = !grow || !wave_on;
+            }
             int c = c_hi;
             for (;;) {
                 wv.kcur = k0; wv.knext = k1; wv.vcur = v0; wv.vprev = v1;
                 kr.tile_facts(c, k0);
-                kr.template run_tile<0, false>(c, std::make_integer_sequence<int, Plan::N>{});
+                if (W::HAS_HALF && half_ok && !wv.half) wv.half = wv.upper_dead();
+                kr.template run_tile<0>(c);
                 if (--c < c_lo) break;
                 wv.kcur = k1; wv.knext = k0; wv.vcur = v1; wv.vprev = v0;
                 kr.tile_facts(c, k1);
-                kr.template run_tile<1, false>(c, std::make_integer_sequence<int, Plan::N>{});
+                if (W::HAS_HALF && half_ok && !wv.half) wv.half = wv.upper_dead();
+                kr.template run_tile<1>(c);
                 if (--c < c_lo) break;
             }
             // the loads issued past tile c_lo land before the buffers are reused

@@ -244,6 +244,29 @@ def test_strong_and_slow_channels():
     assert_parity(o, lse, o_ref, lse_ref, "bfloat16", what="channels at -3 and -0.01")
 
 
+@pytest.mark.parametrize("dtype", ["bfloat16", "float32"])
+@pytest.mark.parametrize("grow", [False, True])
+def test_dead_upper_channels(grow, dtype):
+    """Channels 64..127 forget at -3 nats per token, so a query's q~ on them is 0
+    one tile back and the waves drop their score products; channels 0..63 at
+    -0.005 carry logits across every tile.  With grow, channels 0..3 gain
+    +0.06 per token on rows 520..559 (5.4 log2 units up over 40 rows): the
+    anchors of tile 4 and of its second 32-row block lie above the ones before
+    them, so q~ is rebuilt from q and P there and the pass keeps every channel
+    step.  The rise stays small enough (decay factors below 2^4) that the
+    logits it amplifies keep the bf16 operands' relative error small."""
+    inp = make_inputs("long_bf16", dtype=dtype, B=1, T=1000, HQ=2, H=1)
+    g = torch.full(inp.g.shape, -0.005, dtype=torch.float64)
+    g[..., 64:] = -3.0
+    if grow:
+        g[:, 520:560, :, :4] = 0.06
+    inp.g = g.to(inp.g.dtype)
+    what = f"dead upper channels grow={grow} {dtype}"
+    o, lse = run_gpu(inp, what)
+    o_ref, lse_ref = run_oracle(inp)
+    assert_parity(o, lse, o_ref, lse_ref, dtype, what=what)
+
+
 @pytest.mark.parametrize("kv", [(64, 64), (64, 128), (128, 64), (128, 128)])
 def test_running_max_raised_in_interior_tiles(kv):
     """A positive scalar gate (g_scalar = +0.04 per token) makes every older key
