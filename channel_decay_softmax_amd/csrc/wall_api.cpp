@@ -189,6 +189,7 @@ wall_status_t enqueue_prepare(const void *q, const void *k, const void *v, wall_
                 reinterpret_cast<uint32_t *>(ws + L.off_rec), ws + L.off_kt, ws + L.off_vt, ws + L.off_kd,
                 ws + L.off_qd, reinterpret_cast<uint32_t *>(ws + L.off_drec), scale * LOG2E,
                 L.nseg, L.tiles, s.HQ, s.H, s.K, s.V, s.T};
+    pa.vsum = reinterpret_cast<float *>(ws + L.off_vsum);
     return launched(launch_prep(pa, dtype == WALL_BF16, stream));
 }
 
@@ -212,6 +213,7 @@ wall_status_t enqueue_run(const void *q, const void *k, const void *v, wall_dtyp
     fa.drec = reinterpret_cast<const uint32_t *>(ws + L.off_drec);
     fa.anchor = reinterpret_cast<const float *>(ws + L.off_anchor);
     fa.rec = reinterpret_cast<const uint32_t *>(ws + L.off_rec);
+    fa.vsum = reinterpret_cast<const float *>(ws + L.off_vsum);
     fa.seg = reinterpret_cast<const SegInfo *>(ws + L.off_seg);
     fa.o = o;
     fa.lse = lse;
@@ -272,6 +274,7 @@ wall_status_t wall_attn_fwd_prepare_gate(const void *q, const void *k, const voi
                     reinterpret_cast<uint32_t *>(ws + L.off_drec), scale * LOG2E, L.nseg, L.tiles, HQ, H, K, V, T};
         pa.g = g;
         pa.Pw = P;
+        pa.vsum = reinterpret_cast<float *>(ws + L.off_vsum);
         pa.carry = reinterpret_cast<const float *>(static_cast<const char *>(sws) + SL.off_carry);
         pa.pscale = pscale;
         return launched(launch_scan_prep(pa, stream));

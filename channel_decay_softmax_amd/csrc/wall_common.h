@@ -62,6 +62,13 @@ constexpr int REC_GROW = 128;
 // 2^(DIAG_SPREAD - 126).
 constexpr int REC_DIAG = 129;
 constexpr float DIAG_SPREAD = 100.0f;
+// Word REC_DMIN: the smallest shift R[t-1] - R[t] over the tile's channels
+// (clamped to [0, 255]; 0 for a sequence's first tile), so that a query's
+// largest |q~| over its channels falls by at least 2^REC_DMIN from tile t to
+// t-1.  Word REC_KMAX: the largest |k| of the tile's keys (float32 bits),
+// which bounds every |k~| of the tile for a prefix that does not grow.
+constexpr int REC_DMIN = 130;
+constexpr int REC_KMAX = 131;
 // Rows of one diagonal-phase block (one MFMA n-block of queries).
 constexpr int DBLK = 32;
 // Per (tile, query head) diagonal-phase carry records, DREC_N records of
@@ -100,7 +107,7 @@ inline ScanLayout scan_layout(int64_t B, int64_t T, int64_t C) {
 struct FwdLayout {
     int64_t nseg;        // sequences (num_seqs with packing, else B)
     int64_t tiles;       // upper bound on sum_s ceil(len_s / TILE)
-    size_t off_seg, off_anchor, off_rec, off_kt, off_vt, off_kd, off_qd, off_drec, off_scan, total;
+    size_t off_seg, off_anchor, off_rec, off_kt, off_vt, off_kd, off_qd, off_drec, off_vsum, off_scan, total;
 };
 
 inline FwdLayout fwd_layout(int64_t esize, int64_t B, int64_t T, int64_t HQ, int64_t H,
@@ -126,6 +133,8 @@ inline FwdLayout fwd_layout(int64_t esize, int64_t B, int64_t T, int64_t HQ, int
     o = align_up(o + (size_t)esize * (size_t)(L.tiles * HQ * TILE * K), 256);
     L.off_drec = o;
     o = align_up(o + sizeof(uint32_t) * (size_t)(L.tiles * HQ * DREC_N * (K / 2)), 256);
+    L.off_vsum = o;
+    o = align_up(o + sizeof(float) * (size_t)(L.tiles * H * V), 256);
     // the prefix scan of wall_attn_fwd_prepare_gate
     L.off_scan = o;
     o = align_up(o + scan_layout(B, T, HQ * K).total, 256);
@@ -172,6 +181,7 @@ struct PrepArgs {
     float *Pw;
     const float *carry;
     float pscale;
+    float *vsum;       // [tiles, H, V] float32 sums of each value tile's rows (bf16 path)
 };
 // bf16: the sequence table, anchors, carry records, key and value tiles;
 // float32: the sequence table only.
@@ -208,6 +218,7 @@ struct FwdArgs {
     int32_t nseg, max_tiles, HQ, H, K, V;
     int32_t window;         // <= 0: none
     float qscale;           // scale * log2(e)
+    const float *vsum;      // [tiles, H, V] float32 sums of each value tile's rows (bf16 path)
 };
 hipError_t launch_fwd_bf16(const FwdArgs &a, hipStream_t st);
 hipError_t launch_fwd_f32(const FwdArgs &a, hipStream_t st);

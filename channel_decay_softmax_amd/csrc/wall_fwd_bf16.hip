@@ -1,12 +1,14 @@
 // wall_fwd_bf16.hip -- fused causal Wall Attention forward, bf16 inputs, gfx950.
 //
-// Work decomposition.  A workgroup (8 waves) owns one (sequence, query head)
-// and two 256-row query blocks, u and n-1-u, so every workgroup of a causal
-// launch does about the same number of tiles.  Wave w owns the 32 query rows
-// 256u + 32w .. +31 (one MFMA n-block); waves 0-3 sit in the block's first
-// 128-row tile 2u, waves 4-7 in the second, 2u+1.  Workgroup ids are
-// remapped so each XCD receives a contiguous range of heads (their key
-// caches then share that XCD's L2).
+// Work decomposition.  A workgroup (8 waves) owns one 256-row query block u
+// of one (sequence, query head).  Blocks are dispatched farthest into their
+// sequence first, so the hardware dispatcher hands the short blocks to the
+// workgroups that finish early (the work of a block is not known in advance:
+// see the closed form below).  Wave w owns the 32 query rows 256u + 32w ..
+// +31 (one MFMA n-block); waves 0-3 sit in the block's first 128-row tile 2u,
+// waves 4-7 in the second, 2u+1.  Workgroup ids are remapped so each XCD
+// receives a contiguous range of heads (their key caches then share that
+// XCD's L2).
 //
 // Anchors.  exp2(P_i - P_j) is split as exp2(P_i - R) * exp2(R - P_j) at
 // integer per-channel anchors R (the per-tile anchors of the blog's "Fast
@@ -70,6 +72,22 @@
 // carries for the rest of the pass: the products it drops are exactly 0, so
 // the result is unchanged bit for bit.  A pass with a tile where some
 // channel's prefix grows (q~ is rebuilt there) never drops them.
+//
+// Keys in closed form.  Far enough back, every product q~ k~ of a query is
+// too small to move the score away from -m: the accumulator starts at -m, and
+// a sum of products below a quarter of m's float32 unit in the last place
+// leaves it at -m exactly, so the score is -m, p = bf16(2^-m), for each such
+// key, the value the products would have given.  The kernel bounds the sum by
+// K * max|q~| * max|k|: max|q~| of each query exactly at the start of the
+// pipeline, then lowered at each tile by the smallest shift of the tile's
+// carry record (every channel's exponent falls at least that much), max|k|
+// over the pass's key tiles from the preparation step.  With no window, no
+// scalar gate and no growing prefix in the pass, each wave votes at every tile
+// boundary; once all eight waves have voted so, the remaining tiles need only
+// p times the sum of their value rows (the preparation step's per-tile sums)
+// in O and p per key in l, and the pipeline ends there.  Under the strong
+// decay of fast-forgetting channels this leaves most key tiles of a long
+// sequence to the closed form.
 //
 // Software pipeline.  Step b of tile c runs the softmax of sub-block b, the QK
 // products of the next sub-block (b-1, or sub-block 3 of tile c-1) and the PV
@@ -240,9 +258,13 @@ __device__ __forceinline__ void dma(const void *dst, const void *base, uint32_t 
     static_assert(BYTES == 16 || BYTES == 4, "copy width");
 #if defined(__HIP_DEVICE_COMPILE__)
     const uint64_t b = reinterpret_cast<uint64_t>(base);
-    // base, stride 0, size in bytes, raw-buffer format word
-    const u32x4 rs = {(uint32_t)b, (uint32_t)(b >> 32) & 0xffffu, nbytes, 0x00020000u};
-    const uint32_t m0 = (uint32_t)(uintptr_t)(lds_void *)dst;
+    // base, stride 0, size in bytes, raw-buffer format word; the operands are
+    // wave-uniform, and readfirstlane keeps them in scalar registers even where
+    // the compiler holds such a value in a vector register
+    auto sgpr = [](uint32_t x) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)x); };
+    const u32x4 rs = {sgpr((uint32_t)b), sgpr((uint32_t)(b >> 32) & 0xffffu), sgpr(nbytes), 0x00020000u};
+    const uint32_t m0 = sgpr((uint32_t)(uintptr_t)(lds_void *)dst);
+    soff = sgpr(soff);
     if constexpr (BYTES == 16)
         asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                      :
@@ -1052,21 +1074,35 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
     __shared__ __attribute__((aligned(16))) char v0[VL::BYTES];
     __shared__ __attribute__((aligned(16))) char v1[VL::BYTES];
     __shared__ __attribute__((aligned(16))) char zrec[32 * KS];
+    // the waves' votes of the last two tiles (all queries' q~ zero), and the
+    // closed form's partial value sums
+    constexpr int NPART = NW * 64 / V;
+    __shared__ __attribute__((aligned(16))) uint32_t zvote[2][NW];
+    __shared__ __attribute__((aligned(16))) float zred[NPART][V];
 
+    // One 256-row query block per workgroup.  The blocks farthest into their
+    // sequence (the most key tiles) go first, so that workgroups that finish
+    // early take the short ones.  Workgroups are dispatched round robin over
+    // the 8 XCDs: XCD x takes a contiguous eighth of the (query head,
+    // sequence) pairs, whose keys then share its L2.
     const int nblocks_max = (a.max_tiles + 1) / 2;  // 256-row blocks of the longest sequence
-    const int npairs = (nblocks_max + 1) / 2;
-    const int nwork = a.nseg * npairs * a.HQ;
-    int bid = blockIdx.x;
-    // Workgroups are dispatched round robin over the 8 XCDs; give each XCD a
-    // contiguous range of work ids so the tiles of one head share an L2.
-    if (nwork % 8 == 0) bid = (bid % 8) * (nwork / 8) + bid / 8;
-    const int hq = bid / (a.nseg * npairs);
-    const int rem = bid % (a.nseg * npairs);
-    const int s = rem / npairs, p = rem % npairs;
+    const int nhs = a.nseg * a.HQ;
+    const int bid = blockIdx.x;
+    int rank, hs;
+    if (nhs % 8 == 0) {
+        const int per = nhs / 8, j = bid / 8;
+        rank = j / per;
+        hs = (bid % 8) * per + j % per;
+    } else {
+        rank = bid / nhs;
+        hs = bid % nhs;
+    }
+    const int hq = hs / a.nseg, s = hs % a.nseg;
     const SegInfo sg = a.seg[s];
     const int ntiles = (sg.len + TILE - 1) / TILE;
     const int nblk = (sg.len + BQ - 1) / BQ;
-    if (p >= (nblk + 1) / 2) return;
+    const int u = nblocks_max - 1 - rank;
+    if (u >= nblk) return;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar registers and branches
@@ -1086,9 +1122,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
     wv.vbase = VL::byte(col) + 16 * hl;
     wv.hl = hl;
 
-    for (int pass = 0; pass < 2; ++pass) {
-        const int u = pass == 0 ? p : nblk - 1 - p;
-        if (pass == 1 && u == p) break;
+    {
         const int qt_w = 2 * u + w / (NW / 2);
         const int q0w = BQ * u + WQ * w;
         const bool wave_on = q0w < sg.len;
@@ -1103,6 +1137,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
             c_lo = kmin > 0 ? kmin / TILE : 0;
         }
         const bool run_pipe = c_hi >= c_lo;  // uniform over the workgroup
+        int zc = c_lo - 1;  // last tile of the closed form (none: c_lo - 1)
         kr.qt_w = qt_w;
         kr.c_lo = c_lo;
         wv.qrow = qrow;
@@ -1177,35 +1212,88 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
             // carries only lower exponents), unless some tile's prefix grows
             // and q~ is rebuilt: without such a tile in the pass, the wave runs
             // the half plan from the first tile where it finds that half dead.
-            bool half_ok = false;
-            if constexpr (W::HAS_HALF) {
-                bool grow = false;
-                for (int c0 = c_lo; c0 <= c_hi; c0 += 64) {
-                    const int ct = c0 + lane;
-                    const bool gr = ct <= c_hi &&
-                                    a.rec[((int64_t)(sg.tile_base + ct) * HQ + hq) * REC_WORDS + REC_GROW] != 0u;
-                    grow = grow || __builtin_amdgcn_ballot_w64(gr) != 0u;
+            // the pass's key tiles: whether some channel's prefix grows over one
+            // of them, and the largest |k| of their keys (uniform over the workgroup)
+            bool grow = false;
+            float kbound = 0.f;
+            for (int c0 = c_lo; c0 <= c_hi; c0 += 64) {
+                const int ct = c0 + lane;
+                if (ct <= c_hi) {
+                    const uint32_t *rr = a.rec + ((int64_t)(sg.tile_base + ct) * HQ + hq) * REC_WORDS;
+                    grow = grow || rr[REC_GROW] != 0u;
+                    kbound = fmaxf(kbound, __uint_as_float(rr[REC_KMAX]));
                 }
-                half_ok = !grow || !wave_on;
             }
+            grow = __builtin_amdgcn_ballot_w64(grow) != 0u;
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) kbound = fmaxf(kbound, __shfl_xor(kbound, off));
+            const bool half_ok = W::HAS_HALF && (!grow || !wave_on);
+            // Keys whose scores come out as exactly -m (see the header): without a
+            // window or a scalar gate, and with no tile of the pass where the prefix
+            // grows, every wave votes at each tile whether every product of its
+            // queries with every key left is too small to move -m in float32, and
+            // no lane would raise its max on such keys.  qb bounds the largest |q~|
+            // of the lane's query over its channels at the current tile's anchors:
+            // exact at the start, then lowered by the smallest shift of each carry.
+            // Once all eight waves have voted so at tile c + 1, the tiles c .. c_lo
+            // are summed in closed form and the pipeline ends.
+            const bool zero_ok = !HAS_G && a.window <= 0 && !grow;
+            float qb = 0.f;
+            if (zero_ok) {
+                u16x2 mx = {0, 0};
+#pragma unroll
+                for (int s8 = 0; s8 < KS; ++s8) {
+                    const uint4 x = __builtin_bit_cast(uint4, wv.qop[s8]);
+                    const uint32_t xv[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2, xv[e] & 0x7fff7fffu));
+                }
+                qb = pair_max(__uint_as_float((uint32_t)max(mx[0], mx[1]) << 16));
+            }
+            auto zero_vote = [&](int c, const char *kc) {
+                const float p0 = (float)(__bf16)fast_exp2(-wv.m);
+                // a quarter of m's float32 unit in the last place, over the K <= 128 products
+                const float thr = __uint_as_float(__float_as_uint(wv.m) & 0x7f800000u) * 0x1p-32f;
+                const bool ok = wv.m >= 0.f && wv.lim >= 0.f && 32.f * p0 <= wv.lim && qb * kbound <= thr;
+                const bool dead = !wave_on || __builtin_amdgcn_ballot_w64(!ok) == 0u;
+                zvote[c & 1][w] = dead ? 1u : 0u;  // every lane stores the same word
+                // q~ after this tile's carries (a wave carries on the tiles before its own, down to c_lo + 1)
+                if (wave_on && c < qt_w && c - 1 >= c_lo)
+                    qb = __builtin_amdgcn_ldexpf(qb, -(int)reinterpret_cast<const uint32_t *>(kc + LY::REC_OFF)[REC_DMIN]);
+            };
+            auto zero_all = [&](int c) {  // every wave voted at tile c + 1
+                const uint4 x = reinterpret_cast<const uint4 *>(zvote[(c + 1) & 1])[0];
+                const uint4 y = reinterpret_cast<const uint4 *>(zvote[(c + 1) & 1])[1];
+                return __builtin_amdgcn_readfirstlane(x.x & x.y & x.z & x.w & y.x & y.y & y.z & y.w) != 0u;
+            };
             int c = c_hi;
             for (;;) {
                 wv.kcur = k0; wv.knext = k1; wv.vcur = v0; wv.vprev = v1;
+                if (zero_ok) {
+                    if (c < c_hi && zero_all(c)) { zc = c; break; }
+                    zero_vote(c, k0);
+                }
                 kr.tile_facts(c, k0);
                 if (W::HAS_HALF && half_ok && !wv.half) wv.half = wv.upper_dead();
                 kr.template run_tile<0>(c);
                 if (--c < c_lo) break;
                 wv.kcur = k1; wv.knext = k0; wv.vcur = v1; wv.vprev = v0;
+                if (zero_ok) {
+                    if (zero_all(c)) { zc = c; break; }
+                    zero_vote(c, k1);
+                }
                 kr.tile_facts(c, k1);
                 if (W::HAS_HALF && half_ok && !wv.half) wv.half = wv.upper_dead();
                 kr.template run_tile<1>(c);
                 if (--c < c_lo) break;
             }
-            // the loads issued past tile c_lo land before the buffers are reused
+            // the loads issued past the last tile land before the buffers are reused
             wait_vm<0>();
-            // the last sub-block's PV products (sub-block 0 of tile c_lo, p in Pw[0])
+            // the last sub-block's PV products (sub-block 0 of tile zc + 1, p in
+            // Pw[0]): values in the buffer of that tile's parity
             {
-                const char *vb = ((c_hi - c_lo) & 1 ? v1 : v0) + wv.vbase;
+                const char *vb = ((c_hi - zc - 1) & 1 ? v1 : v0) + wv.vbase;
 #pragma unroll
                 for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -1215,6 +1303,29 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
                         wv.O[vt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, W::as_bf16(wv.Pw[0][t]), wv.O[vt], 0, 0, 0);
                     }
             }
+        }
+
+        // ---- the keys of tiles c_lo .. zc in closed form: every logit is 0, so
+        // each key's p is bf16(2^-m) (the value the products would have given)
+        // and O gains p times the keys' value sums, l p per key (each lane holds
+        // half of a query's sum).  The per-tile sums of the preparation step,
+        // summed in NPART interleaved parts.
+        zc = __builtin_amdgcn_readfirstlane(zc);
+        if (zc >= c_lo) {  // uniform over the workgroup
+            const int ch = tid % V, part = tid / V;
+            const float *vs = a.vsum + ((int64_t)sg.tile_base * a.H + kr.h) * V + ch;
+            float acc = 0.f;
+            for (int c0 = c_lo; c0 <= zc; c0 += 16 * NPART) {  // a uniform trip count
+                float x[16];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int c2 = c0 + part + i * NPART;
+                    x[i] = c2 <= zc ? vs[(int64_t)c2 * a.H * V] : 0.f;
+                }
+#pragma unroll
+                for (int i = 0; i < 16; ++i) acc += x[i];
+            }
+            zred[part][ch] = acc;
         }
 
         // ---- the diagonal phase: the block's two tiles, waves 0-3 in tile 2u
@@ -1235,6 +1346,22 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
             if (second)
                 load_gk(k1 + LY::GK_OFF, a.G + ((int64_t)sg.start + r0 + TILE) * HQ + hq, HQ, sg.len - r0 - TILE, w,
                         lane);
+        }
+        // the closed form's sums (in place since the barrier above)
+        if (zc >= c_lo && wave_on) {
+            const float p0 = (float)(__bf16)fast_exp2(-wv.m);
+#pragma unroll
+            for (int vt = 0; vt < VT; ++vt)
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    const int ch0 = 32 * vt + 8 * r4 + 4 * hl;
+                    f32x4 sv = *reinterpret_cast<const f32x4 *>(&zred[0][ch0]);
+#pragma unroll
+                    for (int pt = 1; pt < NPART; ++pt) sv += *reinterpret_cast<const f32x4 *>(&zred[pt][ch0]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) wv.O[vt][4 * r4 + e] = fmaf(p0, sv[e], wv.O[vt][4 * r4 + e]);
+                }
+            wv.l = fmaf(p0, (float)(64 * (zc - c_lo + 1)), wv.l);
         }
         uint32_t dflags = 0u;
         if (wave_on) {
@@ -1295,8 +1422,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
 template <int K, int V>
 hipError_t run_fwd(const FwdArgs &a, hipStream_t st) {
     const int nblocks_max = (a.max_tiles + 1) / 2;
-    const int npairs = (nblocks_max + 1) / 2;
-    const int64_t nwork = (int64_t)a.nseg * npairs * a.HQ;
+    const int64_t nwork = (int64_t)a.nseg * nblocks_max * a.HQ;
     if (a.G)
         hipLaunchKernelGGL((fwd_bf16_kernel<K, V, true>), dim3((unsigned)nwork), dim3(NW * 64), 0, st, a);
     else

@@ -27,7 +27,8 @@
 //    mask of the blocks whose rows lie more than DIAG_SPREAD from their anchor.
 // 3. values, per (tile, kv head): v transposed to [V][128] for the bf16 MFMA
 //    kernel (its PV operand reads keys contiguously, each thread transposing
-//    an 8 x 8 block in registers); zero-padded.
+//    an 8 x 8 block in registers); zero-padded; and the tile's float32 sum
+//    of its value rows per channel.
 // The float32 forward reads the raw tensors; for it only the sequence table
 // is written (one block).
 #include "wall_common.h"
@@ -103,12 +104,13 @@ struct Vec8<__bf16> {
 // 8, the diagonal records that grow.
 template <int K>
 __device__ inline uint32_t write_records(const PrepArgs &a, int tile, int hq, int c8, bool later, f32x8 R,
-                                         const f32x8 (&A)[TILE / DBLK], f32x8 Lp) {
+                                         const f32x8 (&A)[TILE / DBLK], f32x8 Lp, uint32_t &dmin) {
     constexpr int NB = TILE / DBLK;
     const int64_t HQ = a.HQ;
     *reinterpret_cast<f32x8 *>(a.anchor + ((int64_t)tile * HQ + hq) * K + c8 * 8) = R;
     auto shift = [](float d) { return (uint32_t)fminf(fmaxf(d, 0.f), 255.f) * 128u; };
     bool up = false;
+    dmin = later ? 255u : 0u;
     uint32_t dgrow = 0;
     uint32_t *rec = a.rec + ((int64_t)tile * HQ + hq) * REC_WORDS;
     uint32_t *drec = a.drec + ((int64_t)tile * HQ + hq) * DREC_N * (K / 2);
@@ -119,6 +121,7 @@ __device__ inline uint32_t write_records(const PrepArgs &a, int tile, int hq, in
             const float d0 = Lp[e] - R[e], d1 = Lp[e + 1] - R[e + 1];
             up = up || d0 < 0.f || d1 < 0.f;
             w = shift(d0) | (shift(d1) << 16);
+            dmin = min(dmin, min(shift(d0), shift(d1)) / 128u);
         }
         rec[wd] = w;
 #pragma unroll
@@ -147,12 +150,16 @@ __device__ inline void key_tile(const PrepArgs &a, int tile, int hq, const SegIn
     constexpr int RPP = 256 / CPR;      // rows per pass
     constexpr int NPASS = TILE / RPP;
     constexpr int NB = TILE / DBLK;     // 32-row blocks per tile
-    __shared__ uint32_t sflag;
+    __shared__ uint32_t sflag, sdmin, skmax;
     const int c = tile - sg.tile_base;
     const int h = hq / (int)(a.HQ / a.H);
     const int c8 = threadIdx.x % CPR, r0 = threadIdx.x / CPR;
     const int64_t HQ = a.HQ;
-    if (threadIdx.x == 0) sflag = 0u;
+    if (threadIdx.x == 0) {
+        sflag = 0u;
+        sdmin = 255u;
+        skmax = 0u;
+    }
     __syncthreads();
     // anchors: the tile's last row (keys read from later tiles) and each
     // 32-row block's last row (the fused kernel's diagonal phase)
@@ -172,10 +179,12 @@ __device__ inline void key_tile(const PrepArgs &a, int tile, int hq, const SegIn
             const float *Pp = a.P + ((int64_t)(sg.start + c * TILE - 1) * HQ + hq) * K + c8 * 8;
             for (int e = 0; e < 8; ++e) Lp[e] = floorf(Pp[e]);
         }
-        const uint32_t gr = write_records<K>(a, tile, hq, c8, c > 0, R, A, Lp);
+        uint32_t dmin;
+        const uint32_t gr = write_records<K>(a, tile, hq, c8, c > 0, R, A, Lp, dmin);
         const bool any_up = __any(gr & 1u);  // the r0 == 0 threads are lanes 0..K/8-1 of wave 0
         if (threadIdx.x == 0) a.rec[((int64_t)tile * HQ + hq) * REC_WORDS + REC_GROW] = any_up ? 1u : 0u;
         if (gr >> 8) atomicOr(&sflag, gr & ~0xffu);
+        atomicMin(&sdmin, dmin);
     }
     const __bf16 *qin = static_cast<const __bf16 *>(a.q);
     const __bf16 *kin = static_cast<const __bf16 *>(a.k);
@@ -186,6 +195,7 @@ __device__ inline void key_tile(const PrepArgs &a, int tile, int hq, const SegIn
     // the thread's rows in two batches, each batch's loads in flight before any is used
     constexpr int NH = NPASS / 2;
     uint32_t flags = 0;
+    float kmax = 0.f;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
         f32x8 kv[NH], pv[NH], qv[NH];
@@ -209,6 +219,7 @@ __device__ inline void key_tile(const PrepArgs &a, int tile, int hq, const SegIn
             f32x8 kl, kb, qb;
             float dev = 0.f;
             for (int e = 0; e < 8; ++e) {
+                kmax = fmaxf(kmax, fabsf(kv[i][e]));
                 kl[e] = kv[i][e] * __builtin_amdgcn_exp2f(fminf(fmaxf(R[e] - pv[i][e], EXP2_LO), EXP2_HI));
                 const float x = pv[i][e] - A[b][e];
                 dev = fmaxf(dev, fabsf(x));
@@ -222,19 +233,31 @@ __device__ inline void key_tile(const PrepArgs &a, int tile, int hq, const SegIn
         }
     }
     if (flags) atomicOr(&sflag, flags);
+    atomicMax(&skmax, __float_as_uint(kmax));  // non-negative floats order as their bits
     __syncthreads();
-    if (threadIdx.x == 0) a.rec[((int64_t)tile * HQ + hq) * REC_WORDS + REC_DIAG] = sflag;
+    if (threadIdx.x == 0) {
+        uint32_t *rec = a.rec + ((int64_t)tile * HQ + hq) * REC_WORDS;
+        rec[REC_DIAG] = sflag;
+        rec[REC_DMIN] = sdmin;
+        rec[REC_KMAX] = skmax;
+    }
 }
 
 // Value tile of (tile, kv head), transposed [V][TILE].  Thread (kb, db)
-// moves the 8 x 8 block of keys 8kb.. and values 8db..
+// moves the 8 x 8 block of keys 8kb.. and values 8db..  The tile's float32 sum
+// over its rows per value channel (rows past the sequence count 0) goes to
+// vsum: the fused kernel reads it for keys that every query of a block sees
+// with the same weight.  Called by every thread of a block.
 template <typename T, int V>
 __device__ inline void value_tile(const PrepArgs &a, int tile, int h, const SegInfo &sg) {
     constexpr int DB = V / 8, KB = TILE / 8;
+    static_assert(DB * KB <= 256, "one 8 x 8 block per thread");
+    __shared__ float colsum[KB][V];
     const int c = tile - sg.tile_base;
     const T *vin = static_cast<const T *>(a.v);
     T *vout = static_cast<T *>(a.vt) + ((int64_t)tile * a.H + h) * V * TILE;
-    for (int t = threadIdx.x; t < DB * KB; t += blockDim.x) {
+    const int t = threadIdx.x;
+    if (t < DB * KB) {
         const int db = t % DB, kb = t / DB;
         f32x8 x[8];
 #pragma unroll
@@ -242,6 +265,11 @@ __device__ inline void value_tile(const PrepArgs &a, int tile, int h, const SegI
             const int j = c * TILE + kb * 8 + i;
             x[i] = j < sg.len ? Vec8<T>::load(vin + ((int64_t)(sg.start + j) * a.H + h) * V + db * 8) : f32x8{};
         }
+        f32x8 cs = x[0];
+#pragma unroll
+        for (int i = 1; i < 8; ++i) cs += x[i];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) colsum[kb][db * 8 + e] = cs[e];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             f32x8 col;
@@ -249,6 +277,13 @@ __device__ inline void value_tile(const PrepArgs &a, int tile, int h, const SegI
             for (int i = 0; i < 8; ++i) col[i] = x[i][e];
             Vec8<T>::store(vout + (db * 8 + e) * TILE + kb * 8, col);
         }
+    }
+    __syncthreads();
+    if (t < V) {
+        float s = colsum[0][t];
+#pragma unroll
+        for (int kb = 1; kb < KB; ++kb) s += colsum[kb][t];
+        a.vsum[((int64_t)tile * a.H + h) * V + t] = s;
     }
 }
 
@@ -292,7 +327,7 @@ __device__ inline void scan_key_slice(const PrepArgs &a, int tile, int y) {
     constexpr int NB = TILE / DBLK, SPB = DBLK / SP_SUB;  // blocks per tile, subgroups per block
     constexpr int HPS = (SP_CV * 8 + K - 1) / K;            // query heads per slice
     __shared__ f32x8 ssum[SP_NSUB][SP_CV];
-    __shared__ uint32_t sflag[HPS], sgrow[HPS];
+    __shared__ uint32_t sflag[HPS], sgrow[HPS], sdmin[HPS], skmax[HPS];
     const int tid = threadIdx.x, sub = tid / SP_CV, cv = tid % SP_CV, rb = sub / SPB;
     const int64_t C = a.HQ * K, HQ = a.HQ;
     const int64_t ch = ((int64_t)y * SP_CV + cv) * 8;
@@ -305,6 +340,8 @@ __device__ inline void scan_key_slice(const PrepArgs &a, int tile, int y) {
     if (tid < HPS) {
         sflag[tid] = 0u;
         sgrow[tid] = 0u;
+        sdmin[tid] = 255u;
+        skmax[tid] = 0u;
     }
     // pass 1: the sum of the thread's rows
     f32x8 s = {};
@@ -346,11 +383,24 @@ __device__ inline void scan_key_slice(const PrepArgs &a, int tile, int y) {
             if (c > 0)
 #pragma unroll
                 for (int e = 0; e < 8; ++e) Lp[e] = floorf(a.pscale * carry[e]);
-            const uint32_t gr = write_records<K>(a, tile, hq, c8, c > 0, R, A, Lp);
+            uint32_t dmin;
+            const uint32_t gr = write_records<K>(a, tile, hq, c8, c > 0, R, A, Lp, dmin);
             if (gr) atomicOr(&sgrow[hl], gr);
+            atomicMin(&sdmin[hl], dmin);
         }
         // pass 2: P along the rows, then the keys and queries at the anchors
-        const f32x8 Ab = A[rb], Eb = E[rb];
+        // the thread's block's anchor and end prefix, by selects (a runtime index
+        // into the arrays would keep all of them live through pass 2)
+        f32x8 Ab = A[0], Eb = E[0];
+#pragma unroll
+        for (int b = 1; b < NB; ++b) {
+            const bool mine = rb == b;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                Ab[e] = mine ? A[b][e] : Ab[e];
+                Eb[e] = mine ? E[b][e] : Eb[e];
+            }
+        }
         const __bf16 *qin = static_cast<const __bf16 *>(a.q);
         const __bf16 *kin = static_cast<const __bf16 *>(a.k);
         const int64_t o0 = ((int64_t)tile * HQ + hq) * TILE * K + c8 * 8;
@@ -366,6 +416,7 @@ __device__ inline void scan_key_slice(const PrepArgs &a, int tile, int y) {
             kr[i] = raw8(kin + (r * a.H + h) * K + c8 * 8);
             qr[i] = raw8(qin + r * C + ch);
         }
+        float kmax = 0.f;  // the largest |k| of the thread's rows
         const bool ends_block = (sub + 1) % SPB == 0;  // the thread holds its block's last row
 #pragma unroll
         for (int i = 0; i < SP_SUB; ++i) {
@@ -376,6 +427,7 @@ __device__ inline void scan_key_slice(const PrepArgs &a, int tile, int y) {
             f32x8 pv, kl, kb, qb;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
+                kmax = fmaxf(kmax, fabsf(kv[e]));
                 pv[e] = a.pscale * (last ? Eb[e] : run[e]);
                 kl[e] = kv[e] * __builtin_amdgcn_exp2f(fminf(fmaxf(R[e] - pv[e], EXP2_LO), EXP2_HI));
                 const float d = pv[e] - Ab[e];
@@ -390,6 +442,7 @@ __device__ inline void scan_key_slice(const PrepArgs &a, int tile, int y) {
             Vec8<__bf16>::store(kdout + row * K, kb);
             Vec8<__bf16>::store(qdout + row * K, qb);
         }
+        atomicMax(&skmax[hl], __float_as_uint(kmax));  // non-negative floats order as their bits
     }
     if (spread) atomicOr(&sflag[hl], 1u << rb);
     __syncthreads();
@@ -397,6 +450,8 @@ __device__ inline void scan_key_slice(const PrepArgs &a, int tile, int y) {
         uint32_t *rec = a.rec + ((int64_t)tile * HQ + hq) * REC_WORDS;
         rec[REC_GROW] = sgrow[hl] & 1u;
         rec[REC_DIAG] = sflag[hl] | (sgrow[hl] & ~0xffu);
+        rec[REC_DMIN] = sdmin[hl];
+        rec[REC_KMAX] = skmax[hl];
     }
 }
 
