@@ -265,7 +265,7 @@ wall_status_t wall_attn_fwd_prepare_gate(const void *q, const void *k, const voi
     const float pscale = 1.4426950408889634f;  // 1 / ln 2: P in log2 units
     // one pass for B sequences of T rows (T a multiple of the tile) with bf16 inputs
     if (!cu_seqlens && dtype == WALL_BF16 && g_dtype == WALL_BF16 && T % TILE == 0 && (HQ * K) % 8 == 0) {
-        wall_status_t sc = launched(launch_scan_carry(g, true, B, T, HQ * K, sws, stream));
+        wall_status_t sc = launched(launch_scan_chunk_sums(g, true, B, T, HQ * K, sws, stream));
         if (sc != WALL_OK) return sc;
         const ScanLayout SL = scan_layout(B, T, HQ * K);
         PrepArgs pa{q, k, v, P, reinterpret_cast<SegInfo *>(ws + L.off_seg), nullptr,
@@ -275,7 +275,7 @@ wall_status_t wall_attn_fwd_prepare_gate(const void *q, const void *k, const voi
         pa.g = g;
         pa.Pw = P;
         pa.vsum = reinterpret_cast<float *>(ws + L.off_vsum);
-        pa.carry = reinterpret_cast<const float *>(static_cast<const char *>(sws) + SL.off_carry);
+        pa.csum = reinterpret_cast<const float *>(static_cast<const char *>(sws) + SL.off_sum);
         pa.pscale = pscale;
         return launched(launch_scan_prep(pa, stream));
     }

@@ -175,11 +175,11 @@ struct PrepArgs {
     float qscale;      // scale * log2(e)
     int64_t nseg, tiles, HQ, H, K, V, T;
     // the prefix built here (launch_scan_prep): the bf16 gate g [rows, HQ, K],
-    // P written [rows, HQ, K], the chunk carries of the scan's first two
-    // kernels [chunks, HQ*K], and the scale of the prefix
+    // P written [rows, HQ, K], the sums of g over each 128-row chunk of the
+    // scan's first kernel [chunks, HQ*K], and the scale of the prefix
     const void *g;
     float *Pw;
-    const float *carry;
+    const float *csum;
     float pscale;
     float *vsum;       // [tiles, H, V] float32 sums of each value tile's rows (bf16 path)
 };
@@ -190,13 +190,13 @@ hipError_t launch_prep(const PrepArgs &a, bool bf16, hipStream_t st);
 // (B sequences of T rows, T a multiple of TILE, HQ*K a multiple of 8): P is
 // written once, at the rows that end a 32-row block from the block sums (and
 // at a tile's last row from the next tile's carry), so that each anchor is the
-// floor of the P stored at its row.  Needs the chunk sums and carries of
-// launch_scan_carry first.
+// floor of the P stored at its row.  Needs the chunk sums of
+// launch_scan_chunk_sums first.
 hipError_t launch_scan_prep(const PrepArgs &a, hipStream_t st);
-// The scan's chunk sums and carries alone (its first two kernels), for
-// B sequences of T rows, in a scan workspace of scan_layout(B, T, C).
-hipError_t launch_scan_carry(const void *x, bool x_bf16, int64_t B, int64_t T, int64_t C, void *ws,
-                             hipStream_t st);
+// The scan's chunk sums alone (its first kernel), for B sequences of T rows,
+// in a scan workspace of scan_layout(B, T, C).
+hipError_t launch_scan_chunk_sums(const void *x, bool x_bf16, int64_t B, int64_t T, int64_t C, void *ws,
+                                  hipStream_t st);
 
 struct FwdArgs {
     const void *q;          // [rows, HQ, K]

@@ -312,7 +312,11 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
 // thread then knows the prefix E_b at the end of each 32-row block (the sums
 // of its four subgroups added in order to E_(b-1), E_(-1) = the carry; E_3 =
 // the next tile's carry when that tile is in the same sequence, so that the
-// next tile's Lp is the floor of the P stored here).  Pass 2 runs along the
+// next tile's Lp is the floor of the P stored here).  The carry of tile c is
+// the sum of the chunk sums of the sequence's tiles 0 .. c-1, taken as 16
+// interleaved partial sums (tiles c' = p mod 16 in order), then the parts in
+// order: every block that needs the carry of a tile forms it the same way,
+// so tile c's block and tile c+1's agree on it bit for bit.  Pass 2 runs along the
 // thread's rows from the prefix before its subgroup: P = pscale * the running
 // sum, except P = pscale * E_b at a block's last row, so that the anchors
 // A_b = floor(pscale * E_b) and R = A_3 are the floors of the P stored at
@@ -327,6 +331,7 @@ __device__ inline void scan_key_slice(const PrepArgs &a, int tile, int y) {
     constexpr int NB = TILE / DBLK, SPB = DBLK / SP_SUB;  // blocks per tile, subgroups per block
     constexpr int HPS = (SP_CV * 8 + K - 1) / K;            // query heads per slice
     __shared__ f32x8 ssum[SP_NSUB][SP_CV];
+    __shared__ f32x8 spart[2][SP_NSUB][SP_CV];  // partial carries of this tile and the next
     __shared__ uint32_t sflag[HPS], sgrow[HPS], sdmin[HPS], skmax[HPS];
     const int tid = threadIdx.x, sub = tid / SP_CV, cv = tid % SP_CV, rb = sub / SPB;
     const int64_t C = a.HQ * K, HQ = a.HQ;
@@ -343,23 +348,44 @@ __device__ inline void scan_key_slice(const PrepArgs &a, int tile, int y) {
         sdmin[tid] = 255u;
         skmax[tid] = 0u;
     }
-    // pass 1: the sum of the thread's rows
-    f32x8 s = {};
+    // pass 1: the sum of the thread's rows; meanwhile the partial carries:
+    // thread sub sums the chunk sums of the sequence's tiles sub, sub + 16, ..
+    // before this tile (pc) and before the next (pn), in tile order (the
+    // loads four at a time, zeros past the end)
+    f32x8 s = {}, pc = {};
     if (on) {
         bf16x8 x[SP_SUB];
 #pragma unroll
         for (int i = 0; i < SP_SUB; ++i) x[i] = raw8(gin + (row0 + i) * C + ch);
+        const float *cs = a.csum + (int64_t)(tile - c) * C + ch;  // the sequence's first chunk
+        for (int cc0 = sub; cc0 < c; cc0 += 4 * SP_NSUB) {
+            f32x8 t[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int cc = cc0 + j * SP_NSUB;
+                t[j] = cc < c ? *reinterpret_cast<const f32x8 *>(cs + (int64_t)cc * C) : f32x8{};
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) pc += t[j];
+        }
 #pragma unroll
         for (int i = 0; i < SP_SUB; ++i) s += __builtin_convertvector(x[i], f32x8);
     }
+    f32x8 pn = pc;
+    if (on && c % SP_NSUB == sub) pn += *reinterpret_cast<const f32x8 *>(a.csum + (int64_t)tile * C + ch);
+    spart[0][sub][cv] = pc;
+    spart[1][sub][cv] = pn;
     ssum[sub][cv] = s;
     __syncthreads();
     bool spread = false;
     if (on) {
-        // the running sum before the tile (the scan's carry holds the previous
-        // sequence's at a sequence's first tile: that tile starts from 0)
-        f32x8 carry = {};
-        if (c > 0) carry = *reinterpret_cast<const f32x8 *>(a.carry + (int64_t)tile * C + ch);
+        // the running sum before the tile (0 at a sequence's first tile)
+        f32x8 carry = spart[0][0][cv], nextc = spart[1][0][cv];
+#pragma unroll
+        for (int p = 1; p < SP_NSUB; ++p) {
+            carry += spart[0][p][cv];
+            nextc += spart[1][p][cv];
+        }
         // the prefix at the end of each block and before the thread's subgroup
         f32x8 E[NB], A[NB], run = carry;
         f32x8 acc = carry;
@@ -372,7 +398,7 @@ __device__ inline void scan_key_slice(const PrepArgs &a, int tile, int y) {
             }
             E[b] = acc;
         }
-        if (c + 1 < tps) E[NB - 1] = *reinterpret_cast<const f32x8 *>(a.carry + (int64_t)(tile + 1) * C + ch);
+        if (c + 1 < tps) E[NB - 1] = nextc;
 #pragma unroll
         for (int b = 0; b < NB; ++b)
 #pragma unroll

@@ -324,15 +324,13 @@ hipError_t launch_scan_excl(const float *x, void *out, bool out_bf16, int64_t B,
                : run_scan<float, 1, float, true>(x, o, B, T, C, cu, nseq, scale, ws, st);
 }
 
-hipError_t launch_scan_carry(const void *x, bool x_bf16, int64_t B, int64_t T, int64_t C, void *ws,
-                             hipStream_t st) {
+hipError_t launch_scan_chunk_sums(const void *x, bool x_bf16, int64_t B, int64_t T, int64_t C, void *ws,
+                                  hipStream_t st) {
     const ScanLayout L = scan_layout(B, T, C);
     char *w = static_cast<char *>(ws);
     float *csum = reinterpret_cast<float *>(w + L.off_sum);
-    float *carry = reinterpret_cast<float *>(w + L.off_carry);
     int32_t *cflag = reinterpret_cast<int32_t *>(w + L.off_flag);
     const int64_t rows = B * T;
-    hipError_t e;
     if (x_bf16 && C % 8 == 0) {
         const dim3 grid((unsigned)L.nchunk, (unsigned)cdiv(C, (int64_t)CV * 8));
         hipLaunchKernelGGL((scan_chunk_sums<__bf16, 8>), grid, dim3(256), 0, st, static_cast<const __bf16 *>(x), csum,
@@ -344,10 +342,6 @@ hipError_t launch_scan_carry(const void *x, bool x_bf16, int64_t B, int64_t T, i
     } else {
         return hipErrorInvalidValue;
     }
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((scan_chunk_carry<1>), dim3((unsigned)cdiv(C, (int64_t)CV)), dim3(CV * CARRY_GROUPS), 0, st,
-                       csum, cflag, carry, L.nchunk, C);
     return hipGetLastError();
 }
 

@@ -283,6 +283,41 @@ def test_running_max_raised_in_interior_tiles(kv):
     assert_parity(o, lse, o_ref, lse_ref, "bfloat16", what=f"raised max K={K} V={V}")
 
 
+# --------------------------------------------------------------------------- keys in closed form
+
+
+@pytest.mark.parametrize("kv", [(64, 64), (128, 64), (128, 128)])
+@pytest.mark.parametrize("variant", ["plain", "packed", "tiny_logits"])
+def test_closed_form_far_keys(kv, variant):
+    """A slow uniform gate (-0.04 nats per token on every channel): a few tiles
+    back every product q~ k~ of a query is below the float32 spacing of its
+    running max, and the fused kernel sums those keys in closed form (each
+    key's weight 2^-m times the tiles' value sums).  Each value channel has a
+    mean of its own (a ramp from -0.4 to 0.4), so the closed-form sums carry
+    most of every output and a mix-up of channels would show; keys twice as
+    large on rows 100..103 loosen the kernel's bound on |k|.  packed: two
+    sequences (the preparation after a separate scan); tiny_logits: q scaled
+    by 1e-3, so the running max is near 0 and its float32 spacing too fine for
+    the closed form to start early.  Every row against the oracle."""
+    K, V = kv
+    T = 2048
+    inp = make_inputs("long_bf16", B=1, T=T, HQ=2, H=1, K=K, V=V)
+    inp.g = torch.full_like(inp.g, -0.04)
+    ramp = torch.linspace(-0.4, 0.4, V, dtype=torch.float64)
+    inp.v = (inp.v.double() * 0.5 + ramp).to(inp.v.dtype)
+    k = inp.k.double()
+    k[:, 100:104] *= 2.0
+    inp.k = k.to(inp.k.dtype)
+    if variant == "packed":
+        inp.cu_seqlens = torch.tensor([0, 300, T], dtype=torch.int32)
+    if variant == "tiny_logits":
+        inp.q = (inp.q.double() * 1e-3).to(inp.q.dtype)
+    what = f"closed form {variant} K={K} V={V}"
+    o, lse = run_gpu(inp, what)
+    o_ref, lse_ref = run_oracle(inp)
+    assert_parity(o, lse, o_ref, lse_ref, "bfloat16", what=what)
+
+
 # --------------------------------------------------------------------------- prefix and preparation from the gate
 
 GATE_CASES = {
