@@ -1152,11 +1152,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
         // wave's own; tile c_hi into buffers 0, the keys of tile c_hi - 1 into key
         // buffer 1
         __syncthreads();  // the previous block's last reads of every buffer are done
-        if (run_pipe) {
-            kr.issue_k(k0, c_hi);
-            kr.issue_v(v0, c_hi);
-            kr.issue_k(k1, max(c_hi - 1, c_lo));
-        }
+        if (run_pipe) kr.issue_k(k0, c_hi);
         if (wave_on && qt_w > 0 && run_pipe) {
             // the prepared q~ moved from the wave's block anchor to the previous
             // tile's (an exact exponent decrement); from q and P when the block
@@ -1185,8 +1181,30 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
         for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int e = 0; e < 4; ++e) wv.Pw[0][t][e] = 0u;
+        // the pass's key tiles: whether some channel's prefix grows over one
+        // of them, and the largest |k| of their keys (uniform over the workgroup)
+        bool grow = false;
+        float kbound = 0.f;
+        for (int c0 = c_lo; run_pipe && c0 <= c_hi; c0 += 64) {
+            const int ct = c0 + lane;
+            if (ct <= c_hi) {
+                const uint32_t *rr = a.rec + ((int64_t)(sg.tile_base + ct) * HQ + hq) * REC_WORDS;
+                grow = grow || rr[REC_GROW] != 0u;
+                kbound = fmaxf(kbound, __uint_as_float(rr[REC_KMAX]));
+            }
+        }
+        grow = __builtin_amdgcn_ballot_w64(grow) != 0u;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) kbound = fmaxf(kbound, __shfl_xor(kbound, off));
+        // The keys of tile c_hi, q~ and the records are in; the values of tile
+        // c_hi and the keys of tile c_hi - 1 stay in flight into the pipeline,
+        // whose first barriers wait for them.
         __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+        if (run_pipe) {
+            kr.issue_v(v0, c_hi);
+            kr.issue_k(k1, max(c_hi - 1, c_lo));
+        }
+        tile_barrier();
 
         if (run_pipe) {
             // the scores of the first sub-block (3 of tile c_hi), S[1]
@@ -1212,21 +1230,6 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
             // carries only lower exponents), unless some tile's prefix grows
             // and q~ is rebuilt: without such a tile in the pass, the wave runs
             // the half plan from the first tile where it finds that half dead.
-            // the pass's key tiles: whether some channel's prefix grows over one
-            // of them, and the largest |k| of their keys (uniform over the workgroup)
-            bool grow = false;
-            float kbound = 0.f;
-            for (int c0 = c_lo; c0 <= c_hi; c0 += 64) {
-                const int ct = c0 + lane;
-                if (ct <= c_hi) {
-                    const uint32_t *rr = a.rec + ((int64_t)(sg.tile_base + ct) * HQ + hq) * REC_WORDS;
-                    grow = grow || rr[REC_GROW] != 0u;
-                    kbound = fmaxf(kbound, __uint_as_float(rr[REC_KMAX]));
-                }
-            }
-            grow = __builtin_amdgcn_ballot_w64(grow) != 0u;
-#pragma unroll
-            for (int off = 32; off >= 1; off >>= 1) kbound = fmaxf(kbound, __shfl_xor(kbound, off));
             const bool half_ok = W::HAS_HALF && (!grow || !wave_on);
             // Keys whose scores come out as exactly -m (see the header): without a
             // window or a scalar gate, and with no tile of the pass where the prefix
@@ -1305,6 +1308,30 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
             }
         }
 
+        // ---- the diagonal phase: the block's two tiles, waves 0-3 in tile 2u
+        // (key buffer k0, values v0), waves 4-7 in tile 2u+1 (k1, v1)
+        __syncthreads();  // every wave is past the pipeline's buffers
+        const bool second = 2 * u + 1 < ntiles;
+        char *kd = w < NW / 2 ? k0 : k1;
+        char *vd = w < NW / 2 ? v0 : v1;
+        load_tile<KL>(k0, kr.kd_tile(2 * u), kr.klane, w);
+        kr.issue_v(v0, 2 * u);
+        if (second) {
+            load_tile<KL>(k1, kr.kd_tile(2 * u + 1), kr.klane, w);
+            kr.issue_v(v1, 2 * u + 1);
+        }
+        if (HAS_G) {
+            const int r0 = BQ * u;
+            load_gk(k0 + LY::GK_OFF, a.G + ((int64_t)sg.start + r0) * HQ + hq, HQ, sg.len - r0, w, lane);
+            if (second)
+                load_gk(k1 + LY::GK_OFF, a.G + ((int64_t)sg.start + r0 + TILE) * HQ + hq, HQ, sg.len - r0 - TILE, w,
+                        lane);
+        }
+        uint32_t dflags = 0u;
+        if (wave_on) {
+            kr.load_qd(qt_w, wv.qop);
+            dflags = kr.diag_flags(qt_w);
+        }
         // ---- the keys of tiles c_lo .. zc in closed form: every logit is 0, so
         // each key's p is bf16(2^-m) (the value the products would have given)
         // and O gains p times the keys' value sums, l p per key (each lane holds
@@ -1328,25 +1355,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
             zred[part][ch] = acc;
         }
 
-        // ---- the diagonal phase: the block's two tiles, waves 0-3 in tile 2u
-        // (key buffer k0, values v0), waves 4-7 in tile 2u+1 (k1, v1)
-        __syncthreads();  // every wave is past the pipeline's buffers
-        const bool second = 2 * u + 1 < ntiles;
-        char *kd = w < NW / 2 ? k0 : k1;
-        char *vd = w < NW / 2 ? v0 : v1;
-        load_tile<KL>(k0, kr.kd_tile(2 * u), kr.klane, w);
-        kr.issue_v(v0, 2 * u);
-        if (second) {
-            load_tile<KL>(k1, kr.kd_tile(2 * u + 1), kr.klane, w);
-            kr.issue_v(v1, 2 * u + 1);
-        }
-        if (HAS_G) {
-            const int r0 = BQ * u;
-            load_gk(k0 + LY::GK_OFF, a.G + ((int64_t)sg.start + r0) * HQ + hq, HQ, sg.len - r0, w, lane);
-            if (second)
-                load_gk(k1 + LY::GK_OFF, a.G + ((int64_t)sg.start + r0 + TILE) * HQ + hq, HQ, sg.len - r0 - TILE, w,
-                        lane);
-        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
         // the closed form's sums (in place since the barrier above)
         if (zc >= c_lo && wave_on) {
             const float p0 = (float)(__bf16)fast_exp2(-wv.m);
@@ -1363,13 +1373,6 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
                 }
             wv.l = fmaf(p0, (float)(64 * (zc - c_lo + 1)), wv.l);
         }
-        uint32_t dflags = 0u;
-        if (wave_on) {
-            kr.load_qd(qt_w, wv.qop);
-            dflags = kr.diag_flags(qt_w);
-        }
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
         if (wave_on) kr.diag_walk(qt_w, q0w, dflags, kd, vd, wv.qop);
 
         // ---- epilogue: sink, normalisation, o and lse.  Every wave is past its
