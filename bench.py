@@ -19,8 +19,11 @@ forward kernel alone, timed with HIP events on the stream it is launched on
 over a second pass of the same K steps (an event record leaves a gap on the
 stream, so none sits in the timed region), against the dense bf16 MFMA peak;
 ``call`` beside it prices the forward's C-ABI calls (prefix and preparation,
-fused kernel) the same way; float32 workloads are priced against the vector
-fp32 peak (``bound: "alu"``).  ``cpu_baseline`` times the fp64 oracle on this
+fused kernel) the same way, and ``executed`` gives the matrix-core flops the
+kernel really issues (from the rocprofv3 counters under profiles/): keys
+whose scores are exactly -m in float32 are summed in closed form, so on a
+decaying gate it issues fewer than the counted ones; float32 workloads are
+priced against the vector fp32 peak (``bound: "alu"``).  ``cpu_baseline`` times the fp64 oracle on this
 host on every row of the workload when that takes at most about a minute
 (the long-context workload), else on a fixed row sample.
 """
@@ -46,6 +49,7 @@ PEAK_HBM_GBS = 8000.0
 FWD_KERNEL_SOURCES = ["channel_decay_softmax_amd/csrc/wall_fwd_bf16.hip",
                       "channel_decay_softmax_amd/csrc/wall_common.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_bf16_long_bf16_traffic.json")
+MFMA_FILE = os.path.join(ROOT, "profiles", "fwd_bf16_long_bf16_mfma.json")
 BWD_METRIC = "wall_attn_bwd causal TFLOP/s (dq, dk, dv, dg), T=8192 HQ=16 K=128"
 DECODE_METRIC = "wall_attn_decode streaming step HBM GB/s (prefix and cache append of one token, split-KV decode), B=16 T=8192 HQ=16 K=128"
 DECODE_KERNEL_SOURCES = ["channel_decay_softmax_amd/csrc/wall_decode.hip",
@@ -93,6 +97,19 @@ def load_traffic(workload, path=TRAFFIC_FILE, sources=FWD_KERNEL_SOURCES):
     if rec.get("workload") != workload or rec.get("source_hash") != source_hash(sources):
         return None
     return rec.get("bytes_per_launch")
+
+
+def load_executed(workload):
+    """Matrix-core flops the fused kernel executes per launch and its MFMA busy
+    fraction, from rocprofv3 counters (see profiles/), or None when absent or
+    taken on an older kernel source."""
+    if not os.path.exists(MFMA_FILE):
+        return None
+    with open(MFMA_FILE) as f:
+        rec = json.load(f)
+    if rec.get("workload") != workload or rec.get("source_hash") != source_hash(FWD_KERNEL_SOURCES):
+        return None
+    return rec
 
 
 def cpu_model():
@@ -565,6 +582,18 @@ def main():
         kname, bound, peak = "fwd_f32_kernel", "alu", PEAK_F32_VALU_TFLOPS
     prep_avg = statistics.fmean(prep_ms)
     call_tflops = flop / ((prep_avg + run_avg) * 1e-3) / 1e12
+    # The fused kernel forms the keys whose scores are exactly -m in closed form
+    # and skips score products of channel steps whose q~ is 0: on a decaying
+    # gate it executes fewer matrix-core flops than the counted 4K per pair.
+    # The counters' figure (same kernel source) is reported beside the counted one.
+    ex = load_executed(args.workload) if dtype == "bf16" else None
+    executed = None
+    if ex:
+        ex_tflops = ex["executed_mfma_flop_per_launch"] / (run_avg * 1e-3) / 1e12
+        executed = {"flop_per_launch": ex["executed_mfma_flop_per_launch"],
+                    "of_counted": round(ex["executed_mfma_flop_per_launch"] / flop, 4),
+                    "tflops": round(ex_tflops, 3), "frac": round(ex_tflops / peak, 4),
+                    "mfma_busy": ex["mfma_busy"], "source": "profiles/fwd_bf16_long_bf16_mfma.json"}
     rec = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -589,6 +618,8 @@ def main():
         "roofline": {"kernel": kname, "bound": bound, "achieved": round(achieved, 3),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": traffic if dtype == "bf16" else None,
+                     # matrix-core flops the kernel executes (rocprofv3 counters)
+                     "executed": executed,
                      # the C-ABI calls of the forward from the gate: prefix and preparation, fused kernel
                      "call": {"what": "wall_attn_fwd_prepare_gate + wall_attn_fwd_run",
                               "us": round((prep_avg + run_avg) * 1e3, 2),
