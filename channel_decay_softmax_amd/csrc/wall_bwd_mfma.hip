@@ -148,6 +148,7 @@ __global__ __launch_bounds__(256) void bwd_anchor_kernel(BwdArgs a, int nblk) {
     constexpr int NBK = BR / BWD_BLK;
     __shared__ float sA[NBK + 1][K];  // A_(first - 1), A_first .. A_(first + 3)
     __shared__ int sflag;
+    __shared__ uint32_t sqm[NBK], skm[NBK];
     // one block per (tile of a sequence, query head), tiles fastest
     const int tile = blockIdx.x % nblk, hs = blockIdx.x / nblk, hq = hs % a.HQ, sidx = hs / a.HQ;
     const SegInfo sg = a.seg[sidx];
@@ -158,6 +159,10 @@ __global__ __launch_bounds__(256) void bwd_anchor_kernel(BwdArgs a, int nblk) {
     const int h = hq / (a.HQ / a.H);
     const int64_t gb0 = (int64_t)(sg.tile_base + tile) * NBK;
     if (tid == 0) sflag = 0;
+    if (tid < NBK) {
+        sqm[tid] = 0u;
+        skm[tid] = 0u;
+    }
     if (tid < K) {
         const float *Pc = a.P + hq * K + tid;
         sA[0][tid] = r0 > 0 ? floorf(Pc[(s0 + r0 - 1) * HQ * K]) : 0.f;
@@ -175,6 +180,7 @@ __global__ __launch_bounds__(256) void bwd_anchor_kernel(BwdArgs a, int nblk) {
     __bf16 *qh = static_cast<__bf16 *>(a.qh);
     __bf16 *kh = static_cast<__bf16 *>(a.kh);
     int spread = 0;
+    uint32_t qm[NBK] = {}, km[NBK] = {};  // the largest stored |q~|, |k~| per block (bf16 magnitude bits)
     for (int c = tid; c < n * (K / 8); c += 256) {
         const int r = c / (K / 8), ch = 8 * (c % (K / 8)), b = r / BWD_BLK;
         const int64_t t = s0 + r0 + r, ix = (t * HQ + hq) * K + ch;
@@ -193,13 +199,158 @@ __global__ __launch_bounds__(256) void bwd_anchor_kernel(BwdArgs a, int nblk) {
             far = far || fabsf(pv - Ap) > BWD_SPREAD || fabsf(pv - Ao) > BWD_SPREAD;
         }
         if (far) spread |= 1 << b;
-        *reinterpret_cast<bf16x8 *>(qh + ix) = __builtin_convertvector(xq, bf16x8);
-        *reinterpret_cast<bf16x8 *>(kh + ix) = __builtin_convertvector(xk, bf16x8);
+        const bf16x8 bq = __builtin_convertvector(xq, bf16x8), bk = __builtin_convertvector(xk, bf16x8);
+        *reinterpret_cast<bf16x8 *>(qh + ix) = bq;
+        *reinterpret_cast<bf16x8 *>(kh + ix) = bk;
+        const uint4 uq = __builtin_bit_cast(uint4, bq), uk = __builtin_bit_cast(uint4, bk);
+        const uint32_t wq[4] = {uq.x, uq.y, uq.z, uq.w}, wk[4] = {uk.x, uk.y, uk.z, uk.w};
+        uint32_t mq = 0u, mk = 0u;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            mq = max(mq, max(wq[e] & 0x7fffu, (wq[e] >> 16) & 0x7fffu));
+            mk = max(mk, max(wk[e] & 0x7fffu, (wk[e] >> 16) & 0x7fffu));
+        }
+#pragma unroll
+        for (int bb = 0; bb < NBK; ++bb) {
+            qm[bb] = bb == b ? max(qm[bb], mq) : qm[bb];
+            km[bb] = bb == b ? max(km[bb], mk) : km[bb];
+        }
     }
     if (spread) atomicOr(&sflag, spread);
+    // the wave's maxima, then one atomic per wave and block
+#pragma unroll
+    for (int bb = 0; bb < NBK; ++bb) {
+        uint32_t x = qm[bb], y = km[bb];
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            x = max(x, (uint32_t)__shfl_xor((int)x, off));
+            y = max(y, (uint32_t)__shfl_xor((int)y, off));
+        }
+        if ((tid & 63) == 0) {
+            if (x) atomicMax(&sqm[bb], x << 16);  // as float32 bits
+            if (y) atomicMax(&skm[bb], y << 16);
+        }
+    }
     __syncthreads();
+    if (tid < NBK) {
+        uint32_t *bm = a.bmax + ((gb0 + tid) * HQ + hq) * 2;
+        bm[0] = BWD_BLK * tid < n ? sqm[tid] : 0u;
+        bm[1] = BWD_BLK * tid < n ? skm[tid] : 0u;
+    }
     // all four entries of the tile, also those of blocks past a short tail (0)
     if (tid < NBK) a.flag[(gb0 + tid) * HQ + hq] = (BWD_BLK * tid < n && ((sflag >> tid) & 1)) ? sidx + 1 : 0;
+}
+
+// ---------------------------------------------------------------- far tiles
+// A pair in different 128-row tiles is read at an anchor between its rows:
+// the dq kernel moves each key's k~ down to the anchor before its query tile,
+// the dk/dv kernel each query's q~ down to the anchor of its key tile's last
+// block.  A value stored at anchor A_b and moved to A_x is at most the
+// block's largest stored magnitude times 2^max_n(A_x,n - A_b,n); once that is
+// at most 2^-134 every moved value of the block rounds to 0 in bf16, and the
+// block's pairs have score 0 and add exactly nothing to dq, dk or X (every
+// product has a zero factor).  The dq kernel starts its walk at the first key
+// block that can survive the move.  The dk/dv kernel stops its walk after the
+// last query block that can, and the rows after it give dv_j the same
+// bf16(2^-L_i) do_i for every key: the suffix sums of those rows per block,
+// summed once per (sequence, query head) by the two kernels below.  Without a
+// scalar gate (which would make the weights depend on the key) or a window.
+//
+// The bound's exponent for a block of largest magnitude m (float bits), moved
+// by gap: the moved values round to 0 when this is at most -134.
+__device__ inline int moved_exponent(uint32_t mbits, float gap) {
+    if (mbits == 0u) return -100000;
+    int e;
+    (void)frexpf(__uint_as_float(mbits), &e);  // m < 2^e
+    return e + (int)fminf(fmaxf(gap, -100000.f), 100000.f);
+}
+// max_n (x_n - y_n) over K channels, x in global memory, y in LDS
+template <int K>
+__device__ inline float max_gap(const float *x, const float *y) {
+    float g = -3.0e38f;
+#pragma unroll 8
+    for (int n = 0; n < K; n += 4) {
+        const f32x4 a = *reinterpret_cast<const f32x4 *>(x + n), b = *reinterpret_cast<const f32x4 *>(y + n);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) g = fmaxf(g, a[e] - b[e]);
+    }
+    return g;
+}
+template <int K>
+__device__ inline float max_gap_rev(const float *x, const float *y) {  // max_n (y_n - x_n)
+    float g = -3.0e38f;
+#pragma unroll 8
+    for (int n = 0; n < K; n += 4) {
+        const f32x4 a = *reinterpret_cast<const f32x4 *>(x + n), b = *reinterpret_cast<const f32x4 *>(y + n);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) g = fmaxf(g, b[e] - a[e]);
+    }
+    return g;
+}
+
+// Per (32-row block, query head): the sum over its rows i < len of
+// bf16(2^-L_i) do_i per value channel (the weights the dk/dv kernel's products
+// give a pair of score 0), 64 threads per block, V/64 channels each.
+template <int V>
+__global__ __launch_bounds__(256) void bwd_wsum_kernel(BwdArgs a, int nblk) {
+    constexpr int NBK = BR / BWD_BLK, CPT = V / 64;
+    const int tile = blockIdx.x % nblk, hs = blockIdx.x / nblk, hq = hs % a.HQ, sidx = hs / a.HQ;
+    const SegInfo sg = a.seg[sidx];
+    const int r0 = tile * BR;
+    if (r0 >= sg.len) return;
+    const int b = threadIdx.x / 64, c0 = (threadIdx.x % 64) * CPT;
+    const int64_t HQ = a.HQ;
+    const int rb0 = r0 + BWD_BLK * b;
+    float acc[CPT] = {};
+    const __bf16 *dog = static_cast<const __bf16 *>(a.dout);
+    // eight rows' loads in flight at a time (rows past the sequence weigh 0)
+    for (int r8 = 0; r8 < BWD_BLK; r8 += 8) {
+        float p[8], x[8][CPT];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const bool in = rb0 + r8 + r < sg.len;
+            // a row past the sequence reads its last row (in bounds) with weight 0
+            const int64_t t = sg.start + min(rb0 + r8 + r, sg.len - 1);
+            p[r] = in ? (float)(__bf16)__builtin_amdgcn_exp2f(-(a.lse[t * HQ + hq] * LOG2E)) : 0.f;
+#pragma unroll
+            for (int e = 0; e < CPT; ++e) x[r][e] = (float)dog[(t * HQ + hq) * V + c0 + e];
+        }
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+#pragma unroll
+            for (int e = 0; e < CPT; ++e) acc[e] += p[r] * x[r][e];
+    }
+    const int64_t gb = (int64_t)(sg.tile_base + tile) * NBK + b;
+#pragma unroll
+    for (int e = 0; e < CPT; ++e) a.wsum[(gb * HQ + hq) * V + c0 + e] = acc[e];
+}
+
+// Per (sequence, query head): the block sums above turned, in place, into the
+// sums from each block to the sequence's end (one thread per channel).
+template <int V>
+__global__ __launch_bounds__(V) void bwd_wsuffix_kernel(BwdArgs a) {
+    constexpr int NBK = BR / BWD_BLK;
+    const int sidx = blockIdx.x / a.HQ, hq = blockIdx.x % a.HQ, c = threadIdx.x;
+    const SegInfo sg = a.seg[sidx];
+    const int nb = (sg.len + BWD_BLK - 1) / BWD_BLK;
+    const int64_t stride = (int64_t)a.HQ * V;
+    float *w = a.wsum + ((int64_t)sg.tile_base * NBK * a.HQ + hq) * V + c;
+    float acc = 0.f;
+    int b = nb - 1;
+    for (; b >= 7; b -= 8) {
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = w[(int64_t)(b - i) * stride];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            acc += x[i];
+            w[(int64_t)(b - i) * stride] = acc;
+        }
+    }
+    for (; b >= 0; --b) {
+        acc += w[(int64_t)b * stride];
+        w[(int64_t)b * stride] = acc;
+    }
 }
 
 // x * 2^d per element for integer-valued d: an exact power of two of a bf16
@@ -252,6 +403,10 @@ __global__ __launch_bounds__(NTH_KV) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
     // anchors: sA[0] = A of the block before the tile, sA[1 + b] = A of its block b
     __shared__ __attribute__((aligned(16))) float sA[NBK + 1][K];
     __shared__ int sFl[NBK];
+    // per buffer: 1 + the index of the staged query tile when some of its moved
+    // q~ is not 0 (a tile whose staged q~ is all 0 is left to the dead-tile path)
+    __shared__ int sLive[2];
+    __shared__ int sLast;  // the last query tile past the key tile that can survive the move
 
     const BlockPos bp = block_pos(a, nblk, true);
     const SegInfo sg = a.seg[bp.seg];
@@ -273,13 +428,34 @@ __global__ __launch_bounds__(NTH_KV) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
             if (BWD_BLK * b < jn) sA[b + 1][tid] = a.Ab[((gb0 + b) * HQ + hq) * K + tid];
     }
     if (tid < NBK) sFl[tid] = BWD_BLK * tid < jn ? a.flag[(gb0 + tid) * HQ + hq] : 0;
+    if (tid < 2) sLive[tid] = -1;
     __syncthreads();
 
     const int qend = a.window > 0 ? min(len, j0 + jn - 1 + a.window) : len;
     // Query tiles in the order the dk accumulators need: those after the key
     // tile (read at A of its last block, sA[NBK]), then the tile's own blocks
     // from the last down (own block bq read at the stored anchor of its q~).
-    const int n_off = qend > j0 + BR ? (qend - j0 - BR + BT - 1) / BT : 0;
+    int n_off = qend > j0 + BR ? (qend - j0 - BR + BT - 1) / BT : 0;
+    // The walk stops after the last query tile whose q~ can survive the move to
+    // the key tile's anchor (see "far tiles"); the rows after it, to the end of
+    // the sequence, reach dv through the suffix sums of bf16(2^-L_i) do_i.
+    int wcut = -1;  // the first sequence block left to the suffix sums
+    if (!HAS_G && a.window <= 0 && n_off > 0) {
+        if (tid == 0) sLast = -1;
+        __syncthreads();
+        for (int t = tid; t < n_off; t += NTH_KV) {
+            const int b = (j0 + BR + BT * t) / BWD_BLK;  // the tile's block (BT rows)
+            const int64_t gb = (int64_t)sg.tile_base * NBK + b;
+            const float gap = max_gap<K>(a.Ab + ((gb - 1) * HQ + hq) * K, sA[NBK]);  // max_n A_(b-1) - A_K
+            if (moved_exponent(a.bmax[(gb * HQ + hq) * 2], gap) > -134) atomicMax(&sLast, t);
+        }
+        __syncthreads();
+        const int keep = sLast + 1;
+        if (keep < n_off) {
+            wcut = (j0 + BR + BT * keep) / BWD_BLK;
+            n_off = keep;
+        }
+    }
     const int n_dg = (min(qend, j0 + jn) - j0 + BT - 1) / BT;
     const int ntl = n_off + n_dg;
     auto tile_q0 = [&](int it) { return it < n_off ? j0 + BR + BT * it : j0 + BT * (ntl - 1 - it); };
@@ -327,6 +503,7 @@ __global__ __launch_bounds__(NTH_KV) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
     };
     auto store_tile = [&](int buf, int it, int tix) {
         const int q0 = tile_q0(it);
+        uint32_t nz = 0u;
 #pragma unroll
         for (int u = 0; u < UK; ++u) {
             const int c = sid + NTH * u, r = c % BT, ch = 8 * (c / BT);
@@ -341,8 +518,11 @@ __global__ __launch_bounds__(NTH_KV) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
                 *reinterpret_cast<bf16x8 *>(&sQ[buf][roff<RPK>(r, ch / 8)]) = b;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) sQT[buf][(ch + e) * TP + r] = b[e];
+                const uint4 ub = __builtin_bit_cast(uint4, b);
+                nz |= ub.x | ub.y | ub.z | ub.w;
             }
         }
+        if ((nz & 0x7fff7fffu) != 0u || it >= n_off) sLive[buf] = it + 1;
 #pragma unroll
         for (int u = 0; u < UV; ++u) {
             const int c = sid + NTH * u, r = c % BT, ch = 8 * (c / BT);
@@ -510,6 +690,24 @@ __global__ __launch_bounds__(NTH_KV) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
                     for (int c = 0; c < 2; ++c)
                         acc[n] = mfma(db[c], lds8(&sQT[cur][(32 * n + l32) * TP + 16 * c + 8 * hl]), acc[n]);
             };
+            auto dead_tile = [&](int it) {
+                const int cur = it & 1, q0 = tile_q0(it);
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    const int qi0 = 16 * c + 8 * hl;
+                    f32x4 L4[2];
+#pragma unroll
+                    for (int x = 0; x < 2; ++x) L4[x] = *reinterpret_cast<const f32x4 *>(&sL[cur][qi0 + 4 * x]);
+                    f32x8 p8;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int i = q0 + qi0 + e;
+                        const bool vis = jok && i < len && (a.window <= 0 || i - j < a.window);
+                        p8[e] = vis ? __builtin_amdgcn_exp2f(-L4[e / 4][e % 4]) : 0.f;
+                    }
+                    *reinterpret_cast<bf16x8 *>(&sP[cur][wr][c][lane * 8]) = __builtin_convertvector(p8, bf16x8);
+                }
+            };
             // The query tiles after the key tile at sA[NBK], with k~ moved there
             // once; then the own tile's blocks bq: S at the stored k~'s anchor
             // sA[wr + 1], the staged q~ (at sA[bq]) moved there as it is read,
@@ -522,7 +720,16 @@ __global__ __launch_bounds__(NTH_KV) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
                 for (int s = 0; s < K / 16; ++s) kop[s] = move(kop[s], s, NBK, wr + 1);
                 acc_to(NBK);
                 for (; it < n_off; ++it) {
-                    tile(it, [&](int s) { return kop[s]; }, [&](bf16x8 x, int) { return x; }, std::true_type{});
+                    // A tile whose moved q~ is 0 on every row and channel (far
+                    // queries under strong decay): every score is exactly 0 and every
+                    // product with q~ is 0, so dk gains nothing and A is bf16(2^-L_i)
+                    // for each visible pair, written for the dv waves without the
+                    // products (the probabilities the full step would give)
+                    const bool live = HAS_G || __builtin_amdgcn_readfirstlane(sLive[it & 1]) == it + 1;
+                    if (live)
+                        tile(it, [&](int s) { return kop[s]; }, [&](bf16x8 x, int) { return x; }, std::true_type{});
+                    else
+                        dead_tile(it);
                     __syncthreads();
                 }
             }
@@ -577,7 +784,10 @@ __global__ __launch_bounds__(NTH_KV) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
                     a.X[ix] -= LN2 * shift_anchor((float)khg[ix], F, sA[wr + 1][ch]) * acc[n][r];
                 } else {
                     const int64_t ix = (t * HQ + hq) * V + ch;
-                    a.dvp[ix] = flagged ? a.dvp[ix] + acc[n][r] : acc[n][r];
+                    // the rows after the walk: the same bf16(2^-L_i) do_i for every key
+                    const float far =
+                        wcut >= 0 ? a.wsum[(((int64_t)sg.tile_base * NBK + wcut) * HQ + hq) * V + ch] : 0.f;
+                    a.dvp[ix] = (flagged ? a.dvp[ix] + acc[n][r] : acc[n][r]) + far;
                 }
             }
         }
@@ -603,6 +813,10 @@ __global__ __launch_bounds__(NTH, 2) void bwd_dq_mfma(BwdArgs a, int nblk) {
     // anchors: sA[0] = A of the block before the tile, sA[1 + b] = A of its block b
     __shared__ __attribute__((aligned(16))) float sA[NBK + 1][K];
     __shared__ int sFl[NBK];
+    // per buffer: 1 + the first row of the staged key tile when some of its
+    // moved k~ is not 0 (a tile staged as all 0 adds nothing and is skipped)
+    __shared__ int sLive[2];
+    __shared__ int sFirst;  // the first key block before the query tile that can survive the move
 
     const BlockPos bp = block_pos(a, nblk, false);
     const SegInfo sg = a.seg[bp.seg];
@@ -624,6 +838,7 @@ __global__ __launch_bounds__(NTH, 2) void bwd_dq_mfma(BwdArgs a, int nblk) {
             if (BWD_BLK * b < in_) sA[b + 1][tid] = a.Ab[((gb0 + b) * HQ + hq) * K + tid];
     }
     if (tid < NBK) sFl[tid] = BWD_BLK * tid < in_ ? a.flag[(gb0 + tid) * HQ + hq] : 0;
+    if (tid < 2) sLive[tid] = -1;
     __syncthreads();
 
     // the wave's queries as second operands
@@ -681,7 +896,22 @@ __global__ __launch_bounds__(NTH, 2) void bwd_dq_mfma(BwdArgs a, int nblk) {
     };
 
     const int ilast = i0 + in_ - 1;
-    const int klo = a.window > 0 ? max(0, i0 - a.window + 1) / BT * BT : 0;
+    int klo = a.window > 0 ? max(0, i0 - a.window + 1) / BT * BT : 0;
+    // the walk starts at the first key block whose k~ can survive the move to
+    // the query tile's anchor (see "far tiles"); the blocks before it add nothing
+    if (!HAS_G && a.window <= 0 && klo < i0) {
+        if (tid == 0) sFirst = i0 / BWD_BLK;
+        __syncthreads();
+        const int nfar = (i0 - klo) / BWD_BLK;
+        for (int t = tid; t < nfar; t += NTH) {
+            const int b = klo / BWD_BLK + t;
+            const int64_t gb = (int64_t)sg.tile_base * NBK + b;
+            const float gap = max_gap_rev<K>(a.Ab + (gb * HQ + hq) * K, sA[0]);  // max_n A_Q - A_b
+            if (moved_exponent(a.bmax[(gb * HQ + hq) * 2 + 1], gap) > -134) atomicMin(&sFirst, b);
+        }
+        __syncthreads();
+        klo = sFirst * BWD_BLK;
+    }
 
     // prefetch registers for one tile: k~ at its block's anchor and that anchor
     uint4 kraw[UK], vraw[UV];
@@ -713,6 +943,7 @@ __global__ __launch_bounds__(NTH, 2) void bwd_dq_mfma(BwdArgs a, int nblk) {
         }
     };
     auto store_tile = [&](int buf, int k0) {
+        uint32_t nz = 0u;
 #pragma unroll
         for (int u = 0; u < UK; ++u) {
             const int c = tid + NTH * u, r = c % BT, ch = 8 * (c / BT);
@@ -726,7 +957,10 @@ __global__ __launch_bounds__(NTH, 2) void bwd_dq_mfma(BwdArgs a, int nblk) {
             *reinterpret_cast<bf16x8 *>(&sK[buf][roff<RPK>(r, ch / 8)]) = b;
 #pragma unroll
             for (int e = 0; e < 8; ++e) sKT[buf][(ch + e) * TP + r] = b[e];
+            const uint4 ub = __builtin_bit_cast(uint4, b);
+            nz |= ub.x | ub.y | ub.z | ub.w;
         }
+        if ((nz & 0x7fff7fffu) != 0u || k0 >= i0) sLive[buf] = k0 + 1;
 #pragma unroll
         for (int u = 0; u < UV; ++u) {
             const int c = tid + NTH * u, r = c % BT, ch = 8 * (c / BT);
@@ -817,7 +1051,11 @@ __global__ __launch_bounds__(NTH, 2) void bwd_dq_mfma(BwdArgs a, int nblk) {
         for (int s = 0; s < K / 16; ++s) qop[s] = lower_q(qop[s], s, w, 0);
         acc_to(0);
         for (; k0 < i0; k0 += BT, ++it) {
-            tile(k0, it & 1, [&](int s) { return qop[s]; }, [&](bf16x8 x, int) { return x; }, std::true_type{});
+            // a tile staged as all 0 (far keys under strong decay) adds exactly
+            // nothing to dq and X; without a scalar gate nothing else reads it
+            const bool live = HAS_G || __builtin_amdgcn_readfirstlane(sLive[it & 1]) == k0 + 1;
+            if (live)
+                tile(k0, it & 1, [&](int s) { return qop[s]; }, [&](bf16x8 x, int) { return x; }, std::true_type{});
             advance(k0, it & 1);
         }
     }
@@ -904,6 +1142,14 @@ hipError_t run(const BwdArgs &a, hipStream_t st) {
     hipLaunchKernelGGL((bwd_anchor_kernel<K>), dim3(nb), dim3(256), 0, st, a, nblk);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (!HAS_G && a.window <= 0) {  // the dv sums of the rows the dk/dv walk may leave out
+        hipLaunchKernelGGL((bwd_wsum_kernel<V>), dim3(nb), dim3(256), 0, st, a, nblk);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((bwd_wsuffix_kernel<V>), dim3((unsigned)(a.nseg * a.HQ)), dim3(V), 0, st, a);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     // the pairs inside flagged blocks, before the kernels that add them
     e = launch_bwd_diag(a, true, false, st);
     if (e != hipSuccess) return e;

@@ -235,6 +235,8 @@ struct BwdArgs {
     void *qh, *kh;                     // workspace (bf16 path): q~ and k~ [rows, HQ, K] bf16, see BWD_BLK
     float *Ab;                         // workspace (bf16 path): block anchors [blocks, HQ, K]
     int32_t *flag;                     // workspace (bf16 path): [blocks, HQ], sequence + 1 of a spread block, else 0
+    uint32_t *bmax;                    // workspace (bf16 path): [blocks, HQ, 2] largest stored |q~|, |k~| (float bits)
+    float *wsum;                       // workspace (bf16 path): [blocks, HQ, V] sums of bf16(2^-L) do from a block on
     const SegInfo *seg;
     int32_t nseg, max_seqlen, rows, HQ, H, K, V, window;
     float scale, qscale;               // scale, scale * log2e
@@ -259,8 +261,8 @@ hipError_t launch_bwd_diag(const BwdArgs &a, bool bf16, bool all, hipStream_t st
 constexpr int64_t BWD_MAX_V = 128;
 
 struct BwdLayout {
-    size_t off_seg, off_D, off_X, off_Y, off_Z, off_part, off_dqd, off_qh, off_kh, off_rt, off_flag, off_scan,
-        total;
+    size_t off_seg, off_D, off_X, off_Y, off_Z, off_part, off_dqd, off_qh, off_kh, off_rt, off_flag, off_bmax,
+        off_wsum, off_scan, total;
 };
 inline BwdLayout bwd_layout(int64_t B, int64_t T, int64_t HQ, int64_t K, int64_t nseg) {
     BwdLayout L;
@@ -290,6 +292,10 @@ inline BwdLayout bwd_layout(int64_t B, int64_t T, int64_t HQ, int64_t K, int64_t
     o = align_up(o + sizeof(float) * blocks * HQ * K, 256);
     L.off_flag = o;
     o = align_up(o + sizeof(int32_t) * blocks * HQ, 256);
+    L.off_bmax = o;
+    o = align_up(o + sizeof(uint32_t) * blocks * HQ * 2, 256);
+    L.off_wsum = o;
+    o = align_up(o + sizeof(float) * blocks * HQ * BWD_MAX_V, 256);
     L.off_scan = o;
     o = align_up(o + scan_layout(B, T, HQ * K).total, 256);
     L.total = o;

@@ -278,6 +278,32 @@ def test_backward_strong_uniform_decay(gate, dtype, K):
     _compare(grads, ref, dtype, q=f64(inp.q))
 
 
+@pytest.mark.parametrize("kv", [(64, 128), (128, 64), (128, 128)])
+@pytest.mark.parametrize("packed", [False, True])
+def test_backward_far_tiles(kv, packed):
+    """A uniform gate of -0.1 nats per token over 2048 rows: past about 930
+    rows a key's k~ moved to a query tile's anchor (and a query's q~ moved to a
+    key tile's) rounds to 0 in bf16, so the dq kernel starts its walk late, the
+    dk/dv kernel stops early and the rows it leaves reach dv through the suffix
+    sums of bf16(2^-L_i) do_i.  Each value channel has a mean of its own, so
+    those sums carry much of dv and a mix-up of channels or blocks would show;
+    packed: two sequences (the sums restart at the second).  Every gradient
+    against the oracle."""
+    K, V = kv
+    T = 2048
+    inp = make_inputs("long_bf16", B=1, T=T, HQ=2, H=1, K=K, V=V)
+    inp.g = torch.full_like(inp.g, -0.1)
+    ramp = torch.linspace(-0.4, 0.4, V, dtype=torch.float64)
+    inp.v = (inp.v.double() * 0.5 + ramp).to(inp.v.dtype)
+    if packed:
+        inp.cu_seqlens = torch.tensor([0, 700, T], dtype=torch.int32)
+    say(f"backward far tiles K={K} V={V} packed={packed}")
+    do = _do(inp, 37)
+    grads = _bwd_gpu(inp, do)
+    ref = oracle.wall_attn_bwd_oracle(inp.q, inp.k, inp.v, inp.g, do, scale=inp.scale, cu_seqlens=inp.cu_seqlens)
+    _compare(grads, ref, "bfloat16", q=f64(inp.q))
+
+
 @pytest.mark.parametrize("dtype", ["bfloat16", "float32"])
 def test_backward_strong_decay_window(dtype):
     """g = -2 with a 50-token window and a packed start."""
