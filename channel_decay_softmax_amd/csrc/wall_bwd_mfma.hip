@@ -77,6 +77,7 @@
 // the pair-by-pair kernel's parts (dqd, dkp, dvp, X, Y) instead of
 // overwriting them.
 #include <float.h>
+#include <limits.h>
 
 #include <type_traits>
 
@@ -233,7 +234,7 @@ __global__ __launch_bounds__(256) void bwd_anchor_kernel(BwdArgs a, int nblk) {
     }
     __syncthreads();
     if (tid < NBK) {
-        uint32_t *bm = a.bmax + ((gb0 + tid) * HQ + hq) * 2;
+        uint32_t *bm = a.bmax + ((gb0 + tid) * HQ + hq) * BWD_BM;
         bm[0] = BWD_BLK * tid < n ? sqm[tid] : 0u;
         bm[1] = BWD_BLK * tid < n ? skm[tid] : 0u;
     }
@@ -245,19 +246,30 @@ __global__ __launch_bounds__(256) void bwd_anchor_kernel(BwdArgs a, int nblk) {
 // A pair in different 128-row tiles is read at an anchor between its rows:
 // the dq kernel moves each key's k~ down to the anchor before its query tile,
 // the dk/dv kernel each query's q~ down to the anchor of its key tile's last
-// block.  A value stored at anchor A_b and moved to A_x is at most the
-// block's largest stored magnitude times 2^max_n(A_x,n - A_b,n); once that is
-// at most 2^-134 every moved value of the block rounds to 0 in bf16, and the
-// block's pairs have score 0 and add exactly nothing to dq, dk or X (every
-// product has a zero factor).  The dq kernel starts its walk at the first key
-// block that can survive the move.  The dk/dv kernel stops its walk after the
-// last query block that can, and the rows after it give dv_j the same
-// bf16(2^-L_i) do_i for every key: the suffix sums of those rows per block,
-// summed once per (sequence, query head) by the two kernels below.  Without a
-// scalar gate (which would make the weights depend on the key) or a window.
+// block.  A value stored at anchor A_b and moved to A_x is below the block's
+// largest stored magnitude times 2^max_n(A_x,n - A_b,n), so a pair's score
+// S_ij = q~_i . k~_j is below K times the two moved bounds.  Without a scalar
+// gate or a window the kernels leave out the pairs of a (query block, key
+// tile) or (query tile, key block) whose bound is at most 2^(e - 32), with
+// 2^e <= L_i = lse_i log2e for every query row of the pair: there S_ij lies
+// below a 2^-8 part of half the float32 spacing of L_i, so S_ij - L_i rounds to
+// -L_i and A_ij = 2^-L_i exactly, as the products would give it.  Such a pair
+// adds bf16(2^-L_i) do_i to dv_j, which the dk/dv kernel takes from per-block
+// suffix sums of those rows (the two small kernels below); its terms of dq_i,
+// dk_j and X (each with the factor q~_i k~_j of a score below 2^(e - 32), i.e.
+// at most |dS_ij| 2^(e - 32) in X) are dropped.  Pairs whose moved values all
+// round to 0 in bf16 (bound at most 2^-134) have every such term exactly 0 and
+// are left out as well.  The dq kernel starts its walk at the first key block
+// that has to be kept; the dk/dv kernel stops after the last query block that
+// has to be kept.
 //
 // The bound's exponent for a block of largest magnitude m (float bits), moved
-// by gap: the moved values round to 0 when this is at most -134.
+// by gap: the moved values lie below 2^(this).
+template <int K>
+constexpr int LOG2K() {
+    static_assert(K == 64 || K == 128, "channel count");
+    return K == 128 ? 7 : 6;
+}
 __device__ inline int moved_exponent(uint32_t mbits, float gap) {
     if (mbits == 0u) return -100000;
     int e;
@@ -302,6 +314,7 @@ __global__ __launch_bounds__(256) void bwd_wsum_kernel(BwdArgs a, int nblk) {
     const int64_t HQ = a.HQ;
     const int rb0 = r0 + BWD_BLK * b;
     float acc[CPT] = {};
+    float lmin = FLT_MAX;  // the smallest L_i of the block's rows
     const __bf16 *dog = static_cast<const __bf16 *>(a.dout);
     // eight rows' loads in flight at a time (rows past the sequence weigh 0)
     for (int r8 = 0; r8 < BWD_BLK; r8 += 8) {
@@ -311,7 +324,9 @@ __global__ __launch_bounds__(256) void bwd_wsum_kernel(BwdArgs a, int nblk) {
             const bool in = rb0 + r8 + r < sg.len;
             // a row past the sequence reads its last row (in bounds) with weight 0
             const int64_t t = sg.start + min(rb0 + r8 + r, sg.len - 1);
-            p[r] = in ? (float)(__bf16)__builtin_amdgcn_exp2f(-(a.lse[t * HQ + hq] * LOG2E)) : 0.f;
+            const float L = a.lse[t * HQ + hq] * LOG2E;
+            p[r] = in ? (float)(__bf16)__builtin_amdgcn_exp2f(-L) : 0.f;
+            lmin = in ? fminf(lmin, L) : lmin;
 #pragma unroll
             for (int e = 0; e < CPT; ++e) x[r][e] = (float)dog[(t * HQ + hq) * V + c0 + e];
         }
@@ -323,6 +338,16 @@ __global__ __launch_bounds__(256) void bwd_wsum_kernel(BwdArgs a, int nblk) {
     const int64_t gb = (int64_t)(sg.tile_base + tile) * NBK + b;
 #pragma unroll
     for (int e = 0; e < CPT; ++e) a.wsum[(gb * HQ + hq) * V + c0 + e] = acc[e];
+    // e with 2^e <= L_i for every row of the block (the far-tile rule above);
+    // none for a block with some L_i <= 0 (or none in the sequence: no pairs)
+    if (threadIdx.x % 64 == 0) {
+        int e = BWD_NO_EXP;
+        if (lmin > 0.f && lmin < FLT_MAX) {
+            (void)frexpf(lmin, &e);  // 2^(e-1) <= lmin < 2^e
+            e -= 1;
+        }
+        a.bmax[(gb * HQ + hq) * BWD_BM + 2] = (uint32_t)e;
+    }
 }
 
 // Per (sequence, query head): the block sums above turned, in place, into the
@@ -406,7 +431,8 @@ __global__ __launch_bounds__(NTH_KV) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
     // per buffer: 1 + the index of the staged query tile when some of its moved
     // q~ is not 0 (a tile whose staged q~ is all 0 is left to the dead-tile path)
     __shared__ int sLive[2];
-    __shared__ int sLast;  // the last query tile past the key tile that can survive the move
+    __shared__ int sLast;  // the last query tile past the key tile that has to be kept
+    __shared__ int sKe;    // the exponent bound of the key tile's k~ moved to A_K
 
     const BlockPos bp = block_pos(a, nblk, true);
     const SegInfo sg = a.seg[bp.seg];
@@ -441,13 +467,24 @@ __global__ __launch_bounds__(NTH_KV) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
     // the sequence, reach dv through the suffix sums of bf16(2^-L_i) do_i.
     int wcut = -1;  // the first sequence block left to the suffix sums
     if (!HAS_G && a.window <= 0 && n_off > 0) {
-        if (tid == 0) sLast = -1;
+        if (tid == 0) {
+            sLast = -1;
+            sKe = BWD_NO_EXP;
+        }
         __syncthreads();
+        // the bound of the tile's k~ moved to A_K: block b's stored k~ times 2^(A_K - A_b)
+        if (tid < NBK && BWD_BLK * tid < jn)
+            atomicMax(&sKe, moved_exponent(a.bmax[((gb0 + tid) * HQ + hq) * BWD_BM + 1],
+                                           max_gap<K>(sA[NBK], sA[tid + 1])));
+        __syncthreads();
+        const int ke = sKe + LOG2K<K>();
         for (int t = tid; t < n_off; t += NTH_KV) {
             const int b = (j0 + BR + BT * t) / BWD_BLK;  // the tile's block (BT rows)
             const int64_t gb = (int64_t)sg.tile_base * NBK + b;
+            const uint32_t *bm = a.bmax + (gb * HQ + hq) * BWD_BM;
             const float gap = max_gap<K>(a.Ab + ((gb - 1) * HQ + hq) * K, sA[NBK]);  // max_n A_(b-1) - A_K
-            if (moved_exponent(a.bmax[(gb * HQ + hq) * 2], gap) > -134) atomicMax(&sLast, t);
+            const int mq = moved_exponent(bm[0], gap);
+            if (mq > -134 && mq + ke > (int)bm[2] - 32) atomicMax(&sLast, t);
         }
         __syncthreads();
         const int keep = sLast + 1;
@@ -816,7 +853,8 @@ __global__ __launch_bounds__(NTH, 2) void bwd_dq_mfma(BwdArgs a, int nblk) {
     // per buffer: 1 + the first row of the staged key tile when some of its
     // moved k~ is not 0 (a tile staged as all 0 adds nothing and is skipped)
     __shared__ int sLive[2];
-    __shared__ int sFirst;  // the first key block before the query tile that can survive the move
+    __shared__ int sFirst;  // the first key block before the query tile that has to be kept
+    __shared__ int sQe, sLe;  // the exponent bound of the tile's moved q~; e with 2^e <= L_i on its rows
 
     const BlockPos bp = block_pos(a, nblk, false);
     const SegInfo sg = a.seg[bp.seg];
@@ -897,17 +935,31 @@ __global__ __launch_bounds__(NTH, 2) void bwd_dq_mfma(BwdArgs a, int nblk) {
 
     const int ilast = i0 + in_ - 1;
     int klo = a.window > 0 ? max(0, i0 - a.window + 1) / BT * BT : 0;
-    // the walk starts at the first key block whose k~ can survive the move to
-    // the query tile's anchor (see "far tiles"); the blocks before it add nothing
+    // the walk starts at the first key block that has to be kept (see "far
+    // tiles"); the blocks before it add nothing to dq or X beyond the dropped terms
     if (!HAS_G && a.window <= 0 && klo < i0) {
-        if (tid == 0) sFirst = i0 / BWD_BLK;
+        if (tid == 0) {
+            sFirst = i0 / BWD_BLK;
+            sQe = BWD_NO_EXP;
+            sLe = INT_MAX;
+        }
         __syncthreads();
+        // the bound of the tile's q~ moved to sA[0] (block b's stored at sA[b]),
+        // and e with 2^e <= L_i for every row of the tile
+        if (tid < NBK && BWD_BLK * tid < in_) {
+            const uint32_t *bm = a.bmax + ((gb0 + tid) * HQ + hq) * BWD_BM;
+            atomicMax(&sQe, moved_exponent(bm[0], max_gap<K>(sA[tid], sA[0])));
+            atomicMin(&sLe, (int)bm[2]);
+        }
+        __syncthreads();
+        const int qe = sQe + LOG2K<K>(), le = sLe - 32;
         const int nfar = (i0 - klo) / BWD_BLK;
         for (int t = tid; t < nfar; t += NTH) {
             const int b = klo / BWD_BLK + t;
             const int64_t gb = (int64_t)sg.tile_base * NBK + b;
             const float gap = max_gap_rev<K>(a.Ab + (gb * HQ + hq) * K, sA[0]);  // max_n A_Q - A_b
-            if (moved_exponent(a.bmax[(gb * HQ + hq) * 2 + 1], gap) > -134) atomicMin(&sFirst, b);
+            const int mk = moved_exponent(a.bmax[(gb * HQ + hq) * BWD_BM + 1], gap);
+            if (mk > -134 && mk + qe > le) atomicMin(&sFirst, b);
         }
         __syncthreads();
         klo = sFirst * BWD_BLK;

@@ -235,7 +235,7 @@ struct BwdArgs {
     void *qh, *kh;                     // workspace (bf16 path): q~ and k~ [rows, HQ, K] bf16, see BWD_BLK
     float *Ab;                         // workspace (bf16 path): block anchors [blocks, HQ, K]
     int32_t *flag;                     // workspace (bf16 path): [blocks, HQ], sequence + 1 of a spread block, else 0
-    uint32_t *bmax;                    // workspace (bf16 path): [blocks, HQ, 2] largest stored |q~|, |k~| (float bits)
+    uint32_t *bmax;                    // workspace (bf16 path): [blocks, HQ, BWD_BM], see BWD_BM
     float *wsum;                       // workspace (bf16 path): [blocks, HQ, V] sums of bf16(2^-L) do from a block on
     const SegInfo *seg;
     int32_t nseg, max_seqlen, rows, HQ, H, K, V, window;
@@ -251,6 +251,11 @@ struct BwdArgs {
 // formed pair by pair, every other pair through anchors.
 constexpr int BWD_BLK = 32;
 constexpr float BWD_SPREAD = 64.0f;
+// Per (block, query head) record of the bf16 backward: the largest stored |q~|
+// and |k~| of the block's rows (float bits), and e with 2^e <= L_i for every
+// row of the block, L = lse log2e (int bits; BWD_NO_EXP when some L_i <= 0).
+constexpr int BWD_BM = 4;
+constexpr int BWD_NO_EXP = -100000;
 hipError_t launch_bwd_seg(SegInfo *seg, const int32_t *cu, int64_t nseg, int64_t T, hipStream_t st);
 hipError_t launch_bwd(const BwdArgs &a, bool bf16, hipStream_t st);
 hipError_t launch_bwd_mfma(const BwdArgs &a, hipStream_t st);  // the dq, dk/dv and group-sum kernels, bf16
@@ -293,7 +298,7 @@ inline BwdLayout bwd_layout(int64_t B, int64_t T, int64_t HQ, int64_t K, int64_t
     L.off_flag = o;
     o = align_up(o + sizeof(int32_t) * blocks * HQ, 256);
     L.off_bmax = o;
-    o = align_up(o + sizeof(uint32_t) * blocks * HQ * 2, 256);
+    o = align_up(o + sizeof(uint32_t) * blocks * HQ * BWD_BM, 256);
     L.off_wsum = o;
     o = align_up(o + sizeof(float) * blocks * HQ * BWD_MAX_V, 256);
     L.off_scan = o;

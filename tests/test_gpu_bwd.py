@@ -281,9 +281,10 @@ def test_backward_strong_uniform_decay(gate, dtype, K):
 @pytest.mark.parametrize("kv", [(64, 128), (128, 64), (128, 128)])
 @pytest.mark.parametrize("packed", [False, True])
 def test_backward_far_tiles(kv, packed):
-    """A uniform gate of -0.1 nats per token over 2048 rows: past about 930
-    rows a key's k~ moved to a query tile's anchor (and a query's q~ moved to a
-    key tile's) rounds to 0 in bf16, so the dq kernel starts its walk late, the
+    """A uniform gate of -0.1 nats per token over 2048 rows: past a few hundred
+    rows the bound on a pair's score (q~ and k~ moved to an anchor between the
+    rows) falls below 2^-32 of L_i = lse_i log2e, and past about 930 rows the
+    moved values round to 0 in bf16, so the dq kernel starts its walk late, the
     dk/dv kernel stops early and the rows it leaves reach dv through the suffix
     sums of bf16(2^-L_i) do_i.  Each value channel has a mean of its own, so
     those sums carry much of dv and a mix-up of channels or blocks would show;
@@ -301,6 +302,25 @@ def test_backward_far_tiles(kv, packed):
     do = _do(inp, 37)
     grads = _bwd_gpu(inp, do)
     ref = oracle.wall_attn_bwd_oracle(inp.q, inp.k, inp.v, inp.g, do, scale=inp.scale, cu_seqlens=inp.cu_seqlens)
+    _compare(grads, ref, "bfloat16", q=f64(inp.q))
+
+
+@pytest.mark.parametrize("sink", [False, True])
+def test_backward_bimodal_far_pairs(sink):
+    """The long-context gate (slow channels near -0.03 nats per token, fast
+    ones near -0.8) over 4096 rows with an upstream gradient on every row: the
+    dq and dk/dv walks leave out the far pairs whose score bound lies below
+    2^-32 of L_i (about a thousand rows back on the slow channels), with and
+    without a sink (which moves every L_i).  Every gradient against the
+    oracle."""
+    T = 4096
+    inp = make_inputs("long_bf16", B=1, T=T, HQ=2, H=1, K=128, V=128)
+    if sink:
+        inp.sink_bias = torch.tensor([0.75, -1.5], dtype=torch.float32)
+    say(f"backward bimodal gate T={T} sink={sink}")
+    do = _do(inp, 41)
+    grads = _bwd_gpu(inp, do)
+    ref = oracle.wall_attn_bwd_oracle(inp.q, inp.k, inp.v, inp.g, do, scale=inp.scale, sink_bias=inp.sink_bias)
     _compare(grads, ref, "bfloat16", q=f64(inp.q))
 
 
