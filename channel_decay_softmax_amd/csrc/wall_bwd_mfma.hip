@@ -351,18 +351,30 @@ __global__ __launch_bounds__(256) void bwd_wsum_kernel(BwdArgs a, int nblk) {
 }
 
 // Per (sequence, query head): the block sums above turned, in place, into the
-// sums from each block to the sequence's end (one thread per channel).
+// sums from each block to the sequence's end.  1024 threads: V channels times
+// 1024 / V segments of the sequence's blocks; each segment sums its blocks,
+// then walks them from its end down starting from the sum of the later
+// segments (two reads of each block sum, the second from L2).
 template <int V>
-__global__ __launch_bounds__(V) void bwd_wsuffix_kernel(BwdArgs a) {
-    constexpr int NBK = BR / BWD_BLK;
-    const int sidx = blockIdx.x / a.HQ, hq = blockIdx.x % a.HQ, c = threadIdx.x;
+__global__ __launch_bounds__(1024) void bwd_wsuffix_kernel(BwdArgs a) {
+    constexpr int NBK = BR / BWD_BLK, NS = 1024 / V;
+    __shared__ float part[NS][V];
+    const int sidx = blockIdx.x / a.HQ, hq = blockIdx.x % a.HQ;
+    const int c = threadIdx.x % V, sgi = threadIdx.x / V;
     const SegInfo sg = a.seg[sidx];
-    const int nb = (sg.len + BWD_BLK - 1) / BWD_BLK;
+    const int nb = (sg.len + BWD_BLK - 1) / BWD_BLK, per = (nb + NS - 1) / NS;
+    const int b0 = min(nb, sgi * per), b1 = min(nb, b0 + per);
     const int64_t stride = (int64_t)a.HQ * V;
     float *w = a.wsum + ((int64_t)sg.tile_base * NBK * a.HQ + hq) * V + c;
+    float s = 0.f;
+#pragma unroll 8
+    for (int b = b0; b < b1; ++b) s += w[(int64_t)b * stride];
+    part[sgi][c] = s;
+    __syncthreads();
     float acc = 0.f;
-    int b = nb - 1;
-    for (; b >= 7; b -= 8) {
+    for (int t = NS - 1; t > sgi; --t) acc += part[t][c];
+    int b = b1 - 1;
+    for (; b >= b0 + 7; b -= 8) {
         float x[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) x[i] = w[(int64_t)(b - i) * stride];
@@ -372,7 +384,7 @@ __global__ __launch_bounds__(V) void bwd_wsuffix_kernel(BwdArgs a) {
             w[(int64_t)(b - i) * stride] = acc;
         }
     }
-    for (; b >= 0; --b) {
+    for (; b >= b0; --b) {
         acc += w[(int64_t)b * stride];
         w[(int64_t)b * stride] = acc;
     }
@@ -1198,7 +1210,7 @@ hipError_t run(const BwdArgs &a, hipStream_t st) {
         hipLaunchKernelGGL((bwd_wsum_kernel<V>), dim3(nb), dim3(256), 0, st, a, nblk);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((bwd_wsuffix_kernel<V>), dim3((unsigned)(a.nseg * a.HQ)), dim3(V), 0, st, a);
+        hipLaunchKernelGGL((bwd_wsuffix_kernel<V>), dim3((unsigned)(a.nseg * a.HQ)), dim3(1024), 0, st, a);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
