@@ -474,9 +474,9 @@ __global__ __launch_bounds__(NTH_KV) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
     // tile (read at A of its last block, sA[NBK]), then the tile's own blocks
     // from the last down (own block bq read at the stored anchor of its q~).
     int n_off = qend > j0 + BR ? (qend - j0 - BR + BT - 1) / BT : 0;
-    // The walk stops after the last query tile whose q~ can survive the move to
-    // the key tile's anchor (see "far tiles"); the rows after it, to the end of
-    // the sequence, reach dv through the suffix sums of bf16(2^-L_i) do_i.
+    // The walk stops after the last query tile that has to be kept (see "far
+    // tiles"); the rows after it, to the end of the sequence, reach dv through
+    // the suffix sums of bf16(2^-L_i) do_i.
     int wcut = -1;  // the first sequence block left to the suffix sums
     if (!HAS_G && a.window <= 0 && n_off > 0) {
         if (tid == 0) {

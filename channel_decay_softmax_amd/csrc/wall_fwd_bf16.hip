@@ -1413,7 +1413,10 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
                 const uint4 x = *reinterpret_cast<const uint4 *>(ob + r * OPITCH + 16 * ch);
                 if (q0w + r < sg.len) {
                     const int64_t tok = (int64_t)sg.start + q0w + r;
-                    *reinterpret_cast<uint4 *>(static_cast<char *>(a.o) + ((tok * HQ + hq) * V) * 2 + 16 * ch) = x;
+                    // o is not read again: stored past the caches, which keep the tiles
+                    // the other workgroups still stream
+                    __builtin_nontemporal_store(__builtin_bit_cast(u32x4, x),
+                                                reinterpret_cast<u32x4 *>(static_cast<char *>(a.o) + ((tok * HQ + hq) * V) * 2 + 16 * ch));
                 }
             }
             if (qrow < sg.len && a.lse && hl == 0)

@@ -461,9 +461,11 @@ __device__ inline void scan_key_slice(const PrepArgs &a, int tile, int y) {
                 kb[e] = kv[e] * __builtin_amdgcn_exp2f(fminf(fmaxf(-d, EXP2_LO), EXP2_HI));
                 qb[e] = qv[e] * a.qscale * __builtin_amdgcn_exp2f(fminf(fmaxf(d, EXP2_LO), EXP2_HI));
             }
+            // P is not read again by the forward: stored past the caches, which
+            // keep the prepared tiles for the fused kernel
             float *pw = a.Pw + ((int64_t)tile * TILE + row) * C + ch;
-            reinterpret_cast<f32x4 *>(pw)[0] = f32x4{pv[0], pv[1], pv[2], pv[3]};
-            reinterpret_cast<f32x4 *>(pw)[1] = f32x4{pv[4], pv[5], pv[6], pv[7]};
+            __builtin_nontemporal_store(f32x4{pv[0], pv[1], pv[2], pv[3]}, reinterpret_cast<f32x4 *>(pw));
+            __builtin_nontemporal_store(f32x4{pv[4], pv[5], pv[6], pv[7]}, reinterpret_cast<f32x4 *>(pw) + 1);
             Vec8<__bf16>::store(kout + row * K, kl);
             Vec8<__bf16>::store(kdout + row * K, kb);
             Vec8<__bf16>::store(qdout + row * K, qb);

@@ -314,7 +314,14 @@ wall_status_t wall_attn_fwd_run(const void *q, const void *k, const void *v, wal
  * and dS rounded to bf16; softmax, scaling and the gate sums in float32);
  * every move of q~, k~ or an accumulator between anchors is an exact power
  * of two, and the q-side and k-side terms of dg are formed from the same
- * rounded q~ and k~, so their rounding cancels in dg's sums.  float32
+ * rounded q~ and k~, so their rounding cancels in dg's sums.  bf16 inputs
+ * without g_scalar or a window: pairs of rows in different 128-row tiles
+ * whose score is bounded (from each block's largest stored |q~|, |k~| and
+ * the anchor gaps) by 2^(e - 32), with 2^e <= lse_i log2e, are left out of
+ * the products: their probability is exactly 2^(-lse_i log2e) in float32,
+ * their dv terms come from per-block suffix sums of those weights times
+ * do_i, and their dq, dk and dg terms (each carrying that score as a
+ * factor) are dropped.  float32
  * inputs: every product in float32 on the vector ALUs, the pairs inside each
  * 32-row block always pair by pair.  Over one sequence the summands of dg
  * (and of dg_scalar) add up to zero, so the suffix sums are taken as minus
