@@ -151,7 +151,10 @@ __global__ __launch_bounds__(256) void decode_split(DecodeArgs a) {
 #pragma unroll
         for (int i = 0; i < NQ; ++i) {
             const int j = j0 + NKQ * i + gq;
-            if (j < s1) kk[i] = *reinterpret_cast<const Vec<T> *>(kt + (int64_t)j * kstride);
+            // the cached keys of each query head are read once per call: loaded
+            // past the caches, which keep the value rows the block's four query
+            // heads share
+            if (j < s1) kk[i] = __builtin_nontemporal_load(reinterpret_cast<const Vec<T> *>(kt + (int64_t)j * kstride));
             else kk[i] = Vec<T>{};
         }
         Vec<T> vv[NVL];
