@@ -828,7 +828,9 @@ __global__ __launch_bounds__(NTH_KV) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
                     const float F = sA[fx][ch];
                     float dk = LN2 * clamp2(F - a.P[ix]) * acc[n][r];
                     if (flagged) dk += a.dkp[ix];
-                    a.dkp[ix] = dk;
+                    // the partials are read once, by the group sum: stored past the
+                    // caches, which keep the rows the walks stream
+                    __builtin_nontemporal_store(dk, &a.dkp[ix]);
                     // k (.) dk^(hq) from the bf16 k~ the dq products used (see the X note above)
                     a.X[ix] -= LN2 * shift_anchor((float)khg[ix], F, sA[wr + 1][ch]) * acc[n][r];
                 } else {
@@ -836,7 +838,7 @@ __global__ __launch_bounds__(NTH_KV) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
                     // the rows after the walk: the same bf16(2^-L_i) do_i for every key
                     const float far =
                         wcut >= 0 ? a.wsum[(((int64_t)sg.tile_base * NBK + wcut) * HQ + hq) * V + ch] : 0.f;
-                    a.dvp[ix] = (flagged ? a.dvp[ix] + acc[n][r] : acc[n][r]) + far;
+                    __builtin_nontemporal_store((flagged ? a.dvp[ix] + acc[n][r] : acc[n][r]) + far, &a.dvp[ix]);
                 }
             }
         }
@@ -1165,7 +1167,7 @@ __global__ __launch_bounds__(NTH, 2) void bwd_dq_mfma(BwdArgs a, int nblk) {
                 dqv += a.dqd[ix];
                 xv += a.X[ix];
             }
-            dqg[ix] = (__bf16)dqv;
+            __builtin_nontemporal_store((__bf16)dqv, &dqg[ix]);  // a result: not read again
             a.X[ix] = xv;
         }
     }
@@ -1194,9 +1196,9 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdArgs a, int64_t nrow
     __bf16 *dkg = static_cast<__bf16 *>(a.dk) + rh * K + l * KL;
     __bf16 *dvg = static_cast<__bf16 *>(a.dv) + rh * V + l * VL;
 #pragma unroll
-    for (int e = 0; e < KL; ++e) dkg[e] = (__bf16)sk[e];
+    for (int e = 0; e < KL; ++e) __builtin_nontemporal_store((__bf16)sk[e], &dkg[e]);  // results: not read again
 #pragma unroll
-    for (int e = 0; e < VL; ++e) dvg[e] = (__bf16)sv[e];
+    for (int e = 0; e < VL; ++e) __builtin_nontemporal_store((__bf16)sv[e], &dvg[e]);
 }
 
 template <int K, int V, bool HAS_G>
