@@ -169,6 +169,22 @@ def test_backward_full_size_sampled():
         assert mx <= tmax * rmax and rms <= trms * rrms, name
 
 
+def test_backward_full_size_every_row():
+    """The long-context workload at its full size with an upstream gradient on
+    every row, in the benchmark's launch path: the dq and dk/dv walks leave
+    out the far pairs (about a thousand rows back on the slow channels) for
+    every key and query tile, and the dv of the rows past each walk comes
+    from the per-block suffix sums.  Every gradient of every row and head
+    against the oracle's full backward (about a minute on the host)."""
+    inp = make_inputs("long_bf16")
+    B, T, HQ, K = inp.q.shape
+    say(f"backward full size T={T} HQ={HQ} K={K}, upstream gradient on every row")
+    do = _do(inp, 43)
+    grads = _bwd_gpu(inp, do)
+    ref = oracle.wall_attn_bwd_oracle(inp.q, inp.k, inp.v, inp.g, do, scale=inp.scale)
+    _compare(grads, ref, "bfloat16", q=f64(inp.q))
+
+
 def test_backward_options_full_size_sampled():
     """options_bf16 at its full size (B=4, T=4096, HQ=32, H=8, window 1024,
     g_scalar, sink), upstream gradient zero after row R0 = 1536 (past the
