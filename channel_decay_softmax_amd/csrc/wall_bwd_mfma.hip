@@ -409,6 +409,60 @@ __device__ inline float shift_anchor(float x, float to, float from) {
     return ldexpf(x, (int)fminf(fmaxf(to - from, -1000.0f), 1000.0f));
 }
 
+// ---------------------------------------------------------------- moves of staged tiles
+// Every row of a tile staged by the off-tile walks moves by the same
+// per-channel power of two 2^-dec_n, dec_n = from_n - to_n for two integer
+// anchors.  A table of these moves is formed once per tile, two tiles ahead of
+// its use, by one wave (channels 2l and 2l+1 in lane l): per channel pair the
+// bf16 exponent-field decrements (min(dec, 255) << 7 in two u16) and the
+// decrements themselves (two int16), and per tile whether every decrement is
+// >= 0.  A staged bf16 value then moves by a saturating 16-bit subtract on its
+// magnitude when they all are (the same bits as ldexp for a result in the
+// normal range; 0, or a value below 2^-126, otherwise), else by ldexp.
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+constexpr int DEC_SLOTS = 4;  // tables in flight: formed at tile t - 3, read at t - 1
+struct alignas(16) DecTab {
+    uint32_t w[DEC_SLOTS][64];  // exponent-field decrements, K/2 <= 64 channel pairs
+    uint32_t s[DEC_SLOTS][64];  // signed decrements
+    int fast[DEC_SLOTS];        // every decrement of the tile >= 0
+};
+// Lane l of the forming wave (l < K/2 holds channels 2l, 2l+1 of `to` and `from`).
+template <int K>
+__device__ inline void dec_form(DecTab &t, int slot, int lane, f32x2 to, f32x2 from) {
+    bool neg = false;
+    if (lane < K / 2) {
+        const int d0 = (int)fminf(fmaxf(from[0] - to[0], -1000.f), 1000.f);
+        const int d1 = (int)fminf(fmaxf(from[1] - to[1], -1000.f), 1000.f);
+        neg = d0 < 0 || d1 < 0;
+        t.w[slot][lane] = ((uint32_t)min(max(d0, 0), 255) << 7) | ((uint32_t)min(max(d1, 0), 255) << 23);
+        t.s[slot][lane] = ((uint32_t)d0 & 0xffffu) | ((uint32_t)d1 << 16);
+    }
+    const uint64_t any = __ballot(neg);
+    if (lane == 0) t.fast[slot] = any == 0ull;
+}
+// Eight staged bf16 (raw bits) of channels ch .. ch + 7 moved by table `slot`.
+__device__ inline bf16x8 dec_apply(const DecTab &t, int slot, bool fast, int ch, uint4 raw) {
+    const uint32_t xv[4] = {raw.x, raw.y, raw.z, raw.w};
+    if (fast) {
+        const uint4 dw = *reinterpret_cast<const uint4 *>(&t.w[slot][ch / 2]);
+        const uint32_t dv[4] = {dw.x, dw.y, dw.z, dw.w};
+        uint32_t out[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const u16x2 mag = __builtin_bit_cast(u16x2, xv[e] & 0x7fff7fffu);
+            const u16x2 r = __builtin_elementwise_sub_sat(mag, __builtin_bit_cast(u16x2, dv[e]));
+            out[e] = (xv[e] & 0x80008000u) | __builtin_bit_cast(uint32_t, r);
+        }
+        return __builtin_bit_cast(bf16x8, uint4{out[0], out[1], out[2], out[3]});
+    }
+    const uint4 sw = *reinterpret_cast<const uint4 *>(&t.s[slot][ch / 2]);
+    const uint32_t sv[4] = {sw.x, sw.y, sw.z, sw.w};
+    f32x8 x = to_f32(raw);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = ldexpf(x[e], -(int)(short)(sv[e / 2] >> (16 * (e % 2))));
+    return __builtin_convertvector(x, bf16x8);
+}
+
 // ---------------------------------------------------------------- dk, dv
 // Eight waves in two roles over the same staged tiles: waves 0-3 own 32 keys
 // each for dk (S, dP, A, dS, dk += dS^T q~, and the X and Y updates), waves
@@ -445,6 +499,7 @@ __global__ __launch_bounds__(NTH_KV) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
     __shared__ int sLive[2];
     __shared__ int sLast;  // the last query tile past the key tile that has to be kept
     __shared__ int sKe;    // the exponent bound of the key tile's k~ moved to A_K
+    __shared__ DecTab sDec;  // the moves of staged q~ to A_K (tiles after the key tile)
 
     const BlockPos bp = block_pos(a, nblk, true);
     const SegInfo sg = a.seg[bp.seg];
@@ -513,25 +568,15 @@ __global__ __launch_bounds__(NTH_KV) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
     const __bf16 *khg = static_cast<const __bf16 *>(a.kh);
     // prefetch registers for one tile: q~ at its stored anchor and that anchor
     uint4 qraw[UK], oraw[UV];
-    f32x8 araw[UK];
     float il = 0.f, id = 0.f, ig = 0.f;
     const int sid = tid - NTH;  // staging thread index (dv waves)
     auto load_tile = [&](int it) {
         const int q0 = tile_q0(it);
-        // the anchor of the block before the tile's rows (a tile after the key tile only)
-        const float *ab = a.Ab + ((gb0 + q0 / BWD_BLK - bp.rb * NBK - 1) * HQ + hq) * K;
         // rows past the sequence load its last row (in bounds) and are zeroed when stored
 #pragma unroll
         for (int u = 0; u < UK; ++u) {
             const int c = sid + NTH * u, r = c % BT, ch = 8 * (c / BT), i = min(q0 + r, len - 1);
-            if (CK % NTH == 0 || c < CK) {
-                qraw[u] = *reinterpret_cast<const uint4 *>(qhg + ((s0 + i) * HQ + hq) * K + ch);
-                if (it < n_off) {
-                    const f32x4 *pp = reinterpret_cast<const f32x4 *>(ab + ch);
-                    const f32x4 p0 = pp[0], p1 = pp[1];
-                    araw[u] = f32x8{p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
-                }
-            }
+            if (CK % NTH == 0 || c < CK) qraw[u] = *reinterpret_cast<const uint4 *>(qhg + ((s0 + i) * HQ + hq) * K + ch);
         }
 #pragma unroll
         for (int u = 0; u < UV; ++u) {
@@ -553,17 +598,15 @@ __global__ __launch_bounds__(NTH_KV) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
     auto store_tile = [&](int buf, int it, int tix) {
         const int q0 = tile_q0(it);
         uint32_t nz = 0u;
+        // a tile after the key tile: q~ moved from A_(b-1) of its rows to A_K
+        const int slot = it & (DEC_SLOTS - 1);
+        const bool fast = it < n_off && sDec.fast[slot];
 #pragma unroll
         for (int u = 0; u < UK; ++u) {
             const int c = sid + NTH * u, r = c % BT, ch = 8 * (c / BT);
             if (CK % NTH == 0 || c < CK) {
-                f32x8 x = to_f32(qraw[u]);
-                if (it < n_off) {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) x[e] = shift_anchor(x[e], araw[u][e], sA[NBK][ch + e]);
-                }
-                if (q0 + r >= len) x = 0.f;
-                const bf16x8 b = __builtin_convertvector(x, bf16x8);
+                bf16x8 b = it < n_off ? dec_apply(sDec, slot, fast, ch, qraw[u]) : __builtin_bit_cast(bf16x8, qraw[u]);
+                if (q0 + r >= len) b = __builtin_bit_cast(bf16x8, uint4{0u, 0u, 0u, 0u});
                 *reinterpret_cast<bf16x8 *>(&sQ[buf][roff<RPK>(r, ch / 8)]) = b;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) sQT[buf][(ch + e) * TP + r] = b[e];
@@ -594,6 +637,24 @@ __global__ __launch_bounds__(NTH_KV) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
     // stores tile it+1 (loaded during iteration it-1) into the other buffer,
     // which every wave finished reading before the previous barrier; one
     // barrier per tile.
+    // The move tables of the tiles after the key tile: the first dv wave forms
+    // table t during iteration t - 3 (the first three before the walk) from
+    // the anchors A_(b-1) of tile t's rows, loaded one iteration before.
+    const bool former = w == NW;
+    auto tab_anchor = [&](int t) {  // A_(b-1) of tile t's rows, channels 2 lane and 2 lane + 1
+        const float *ab = a.Ab + ((gb0 + tile_q0(t) / BWD_BLK - bp.rb * NBK - 1) * HQ + hq) * K + 2 * lane;
+        return *reinterpret_cast<const f32x2 *>(ab);
+    };
+    auto tab_form = [&](int t, f32x2 to) {
+        const f32x2 from = lane < K / 2 ? *reinterpret_cast<const f32x2 *>(&sA[NBK][2 * lane]) : f32x2{0.f, 0.f};
+        dec_form<K>(sDec, t & (DEC_SLOTS - 1), lane, to, from);
+    };
+    f32x2 an = {0.f, 0.f};
+    if (former) {
+        for (int t = 0; t < min(3, n_off); ++t) tab_form(t, lane < K / 2 ? tab_anchor(t) : f32x2{0.f, 0.f});
+        if (3 < n_off && lane < K / 2) an = tab_anchor(3);
+    }
+    __syncthreads();
     const bool stager = w >= NW;
     if (stager) {
         load_tile(0);
@@ -802,6 +863,12 @@ __global__ __launch_bounds__(NTH_KV) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
                 if (it > 0 && active(it - 1)) dv_step(it - 1);
                 if (it + 1 < ntl) store_tile((it & 1) ^ 1, it + 1, it + 1);
                 __syncthreads();
+                // the table before the tile's loads: its anchors, loaded before the
+                // previous tile's, are in (store_tile waited for those)
+                if (former && it + 3 < n_off) {
+                    tab_form(it + 3, an);
+                    if (it + 4 < n_off && lane < K / 2) an = tab_anchor(it + 4);
+                }
                 if (it + 2 < ntl) load_tile(it + 2);
             }
             if (ntl > 0 && active(ntl - 1)) dv_step(ntl - 1);
@@ -869,6 +936,7 @@ __global__ __launch_bounds__(NTH, 2) void bwd_dq_mfma(BwdArgs a, int nblk) {
     __shared__ int sLive[2];
     __shared__ int sFirst;  // the first key block before the query tile that has to be kept
     __shared__ int sQe, sLe;  // the exponent bound of the tile's moved q~; e with 2^e <= L_i on its rows
+    __shared__ DecTab sDec;   // the moves of staged k~ to sA[0] (key tiles before the query tile)
 
     const BlockPos bp = block_pos(a, nblk, false);
     const SegInfo sg = a.seg[bp.seg];
@@ -981,22 +1049,14 @@ __global__ __launch_bounds__(NTH, 2) void bwd_dq_mfma(BwdArgs a, int nblk) {
 
     // prefetch registers for one tile: k~ at its block's anchor and that anchor
     uint4 kraw[UK], vraw[UV];
-    f32x8 araw[UK];
     float kgv = 0.f;
     auto load_tile = [&](int k0) {
-        // a tile before the query tile moves to sA[0]: the anchor of its block
-        const float *ab = a.Ab + ((gb0 - bp.rb * NBK + k0 / BWD_BLK) * HQ + hq) * K;
         // rows past the sequence load its last row (in bounds) and are zeroed when stored
 #pragma unroll
         for (int u = 0; u < UK; ++u) {
             const int c = tid + NTH * u, r = c % BT, ch = 8 * (c / BT);
             const int64_t t = s0 + min(k0 + r, len - 1);
             kraw[u] = *reinterpret_cast<const uint4 *>(khg + (t * HQ + hq) * K + ch);
-            if (k0 < i0) {
-                const f32x4 *pp = reinterpret_cast<const f32x4 *>(ab + ch);
-                const f32x4 p0 = pp[0], p1 = pp[1];
-                araw[u] = f32x8{p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
-            }
         }
 #pragma unroll
         for (int u = 0; u < UV; ++u) {
@@ -1010,16 +1070,14 @@ __global__ __launch_bounds__(NTH, 2) void bwd_dq_mfma(BwdArgs a, int nblk) {
     };
     auto store_tile = [&](int buf, int k0) {
         uint32_t nz = 0u;
+        // a tile before the query tile: k~ moved from the anchor of its block to sA[0]
+        const int slot = ((k0 - klo) / BT) & (DEC_SLOTS - 1);
+        const bool fast = k0 < i0 && sDec.fast[slot];
 #pragma unroll
         for (int u = 0; u < UK; ++u) {
             const int c = tid + NTH * u, r = c % BT, ch = 8 * (c / BT);
-            f32x8 x = to_f32(kraw[u]);
-            if (k0 < i0) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) x[e] = shift_anchor(x[e], sA[0][ch + e], araw[u][e]);
-            }
-            if (k0 + r >= len) x = 0.f;
-            const bf16x8 b = __builtin_convertvector(x, bf16x8);
+            bf16x8 b = k0 < i0 ? dec_apply(sDec, slot, fast, ch, kraw[u]) : __builtin_bit_cast(bf16x8, kraw[u]);
+            if (k0 + r >= len) b = __builtin_bit_cast(bf16x8, uint4{0u, 0u, 0u, 0u});
             *reinterpret_cast<bf16x8 *>(&sK[buf][roff<RPK>(r, ch / 8)]) = b;
 #pragma unroll
             for (int e = 0; e < 8; ++e) sKT[buf][(ch + e) * TP + r] = b[e];
@@ -1093,9 +1151,33 @@ __global__ __launch_bounds__(NTH, 2) void bwd_dq_mfma(BwdArgs a, int nblk) {
             for (int c = 0; c < 2; ++c)
                 dq[n] = mfma(db[c], lds8(&sKT[cur][(32 * n + l32) * TP + 16 * c + 8 * hl]), dq[n]);
     };
+    // The move tables of the key tiles before the query tile: wave 0 forms
+    // table t during iteration t - 3 (the first three before the walk) from
+    // the anchors of tile t's block, loaded one iteration before.
+    const int nofft = (i0 - klo) / BT;
+    auto tab_anchor = [&](int t) {  // A of tile t's key block, channels 2 lane and 2 lane + 1
+        const float *ab = a.Ab + ((gb0 - bp.rb * NBK + (klo + BT * t) / BWD_BLK) * HQ + hq) * K + 2 * lane;
+        return *reinterpret_cast<const f32x2 *>(ab);
+    };
+    auto tab_form = [&](int t, f32x2 from) {
+        const f32x2 to = lane < K / 2 ? *reinterpret_cast<const f32x2 *>(&sA[0][2 * lane]) : f32x2{0.f, 0.f};
+        dec_form<K>(sDec, t & (DEC_SLOTS - 1), lane, to, from);
+    };
+    f32x2 an = {0.f, 0.f};
+    if (w == 0) {
+        for (int t = 0; t < min(3, nofft); ++t) tab_form(t, lane < K / 2 ? tab_anchor(t) : f32x2{0.f, 0.f});
+        if (3 < nofft && lane < K / 2) an = tab_anchor(3);
+    }
+    __syncthreads();
     auto advance = [&](int k0, int cur) {
         if (k0 + BT <= ilast) store_tile(cur ^ 1, k0 + BT);
         __syncthreads();
+        // the table before the tile's loads (as in the dk/dv kernel)
+        const int t3 = (k0 - klo) / BT + 3;
+        if (w == 0 && t3 < nofft) {
+            tab_form(t3, an);
+            if (t3 + 1 < nofft && lane < K / 2) an = tab_anchor(t3 + 1);
+        }
         if (k0 + 2 * BT <= ilast) load_tile(k0 + 2 * BT);
     };
 
