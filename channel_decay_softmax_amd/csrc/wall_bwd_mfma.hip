@@ -35,8 +35,9 @@
 //     2^(BWD_SPREAD + 1), and the pairs of a flagged block are left to the
 //     pair-by-pair kernel of wall_bwd_diag.hip, which runs first;
 //   * every move of q~ or k~ to another anchor is an exact power of two of the
-//     stored bf16 value, so each pair's product q~ k~ is the same in both
-//     kernels; the accumulators move between anchors the same way, only ever
+//     stored bf16 value (a moved value that leaves the bf16 normal range may
+//     round differently, below 2^-126), so each pair's product q~ k~ is the
+//     same in both kernels; the accumulators move between anchors the same way, only ever
 //     downwards (the dq kernel walks the key tiles upwards, the dk/dv kernel
 //     the query tiles after its tile first, then its own tile from the last
 //     block down).
