@@ -251,14 +251,14 @@ __global__ __launch_bounds__(256) void bwd_anchor_kernel(BwdArgs a, int nblk) {
 // largest stored magnitude times 2^max_n(A_x,n - A_b,n), so a pair's score
 // S_ij = q~_i . k~_j is below K times the two moved bounds.  Without a scalar
 // gate or a window the kernels leave out the pairs of a (query block, key
-// tile) or (query tile, key block) whose bound is at most 2^(e - 32), with
+// tile) or (query tile, key block) whose bound is at most 2^(e - 26), with
 // 2^e <= L_i = lse_i log2e for every query row of the pair: there S_ij lies
-// below a 2^-8 part of half the float32 spacing of L_i, so S_ij - L_i rounds to
+// below a quarter of half the float32 spacing of L_i, so S_ij - L_i rounds to
 // -L_i and A_ij = 2^-L_i exactly, as the products would give it.  Such a pair
 // adds bf16(2^-L_i) do_i to dv_j, which the dk/dv kernel takes from per-block
 // suffix sums of those rows (the two small kernels below); its terms of dq_i,
-// dk_j and X (each with the factor q~_i k~_j of a score below 2^(e - 32), i.e.
-// at most |dS_ij| 2^(e - 32) in X) are dropped.  Pairs whose moved values all
+// dk_j and X (each with the factor q~_i k~_j of a score below 2^(e - 26), i.e.
+// at most |dS_ij| 2^(e - 26) in X) are dropped.  Pairs whose moved values all
 // round to 0 in bf16 (bound at most 2^-134) have every such term exactly 0 and
 // are left out as well.  The dq kernel starts its walk at the first key block
 // that has to be kept; the dk/dv kernel stops after the last query block that
@@ -552,7 +552,7 @@ __global__ __launch_bounds__(NTH_KV) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
             const uint32_t *bm = a.bmax + (gb * HQ + hq) * BWD_BM;
             const float gap = max_gap<K>(a.Ab + ((gb - 1) * HQ + hq) * K, sA[NBK]);  // max_n A_(b-1) - A_K
             const int mq = moved_exponent(bm[0], gap);
-            if (mq > -134 && mq + ke > (int)bm[2] - 32) atomicMax(&sLast, t);
+            if (mq > -134 && mq + ke > (int)bm[2] - 26) atomicMax(&sLast, t);
         }
         __syncthreads();
         const int keep = sLast + 1;
@@ -1035,7 +1035,7 @@ __global__ __launch_bounds__(NTH, 2) void bwd_dq_mfma(BwdArgs a, int nblk) {
             atomicMin(&sLe, (int)bm[2]);
         }
         __syncthreads();
-        const int qe = sQe + LOG2K<K>(), le = sLe - 32;
+        const int qe = sQe + LOG2K<K>(), le = sLe - 26;
         const int nfar = (i0 - klo) / BWD_BLK;
         for (int t = tid; t < nfar; t += NTH) {
             const int b = klo / BWD_BLK + t;

@@ -172,7 +172,7 @@ def test_backward_full_size_sampled():
 def test_backward_full_size_every_row():
     """The long-context workload at its full size with an upstream gradient on
     every row, in the benchmark's launch path: the dq and dk/dv walks leave
-    out the far pairs (about a thousand rows back on the slow channels) for
+    out the far pairs (some 800 rows back on the slow channels) for
     every key and query tile, and the dv of the rows past each walk comes
     from the per-block suffix sums.  Every gradient of every row and head
     against the oracle's full backward (about a minute on the host)."""
@@ -299,7 +299,7 @@ def test_backward_strong_uniform_decay(gate, dtype, K):
 def test_backward_far_tiles(kv, packed):
     """A uniform gate of -0.1 nats per token over 2048 rows: past a few hundred
     rows the bound on a pair's score (q~ and k~ moved to an anchor between the
-    rows) falls below 2^-32 of L_i = lse_i log2e, and past about 930 rows the
+    rows) falls below 2^-26 of L_i = lse_i log2e, and past about 930 rows the
     moved values round to 0 in bf16, so the dq kernel starts its walk late, the
     dk/dv kernel stops early and the rows it leaves reach dv through the suffix
     sums of bf16(2^-L_i) do_i.  Each value channel has a mean of its own, so
@@ -326,7 +326,7 @@ def test_backward_bimodal_far_pairs(sink):
     """The long-context gate (slow channels near -0.03 nats per token, fast
     ones near -0.8) over 4096 rows with an upstream gradient on every row: the
     dq and dk/dv walks leave out the far pairs whose score bound lies below
-    2^-32 of L_i (about a thousand rows back on the slow channels), with and
+    2^-26 of L_i (some 850 rows back on the slow channels), with and
     without a sink (which moves every L_i).  Every gradient against the
     oracle."""
     T = 4096
