@@ -385,6 +385,7 @@ wall_status_t wall_attn_bwd(const void *q, const void *k, const void *v, wall_dt
     a.Ab = reinterpret_cast<float *>(ws + L.off_rt);
     a.flag = reinterpret_cast<int32_t *>(ws + L.off_flag);
     a.bmax = reinterpret_cast<uint32_t *>(ws + L.off_bmax);
+    a.cmax = reinterpret_cast<uint16_t *>(ws + L.off_cmax);
     a.wsum = reinterpret_cast<float *>(ws + L.off_wsum);
     a.seg = seg;
     a.nseg = (int32_t)nseg;

@@ -92,6 +92,7 @@ constexpr int BT = 32;       // streamed rows per tile
 constexpr int NW = 4;        // waves per block
 constexpr int NTH = NW * 64;
 constexpr int TP = BT + 8;   // transposed tile row pitch (elements): 80 bytes
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 // exp2 of a clamped anchored exponent on v_exp_f32 itself: results below
 // the float32 normal range may come back as 0, which only drops terms below
@@ -151,6 +152,7 @@ __global__ __launch_bounds__(256) void bwd_anchor_kernel(BwdArgs a, int nblk) {
     __shared__ float sA[NBK + 1][K];  // A_(first - 1), A_first .. A_(first + 3)
     __shared__ int sflag;
     __shared__ uint32_t sqm[NBK], skm[NBK];
+    __shared__ uint32_t sC[2][NBK][4][K / 2];  // per wave the channels' largest |q~|, |k~| (u16 pairs)
     // one block per (tile of a sequence, query head), tiles fastest
     const int tile = blockIdx.x % nblk, hs = blockIdx.x / nblk, hq = hs % a.HQ, sidx = hs / a.HQ;
     const SegInfo sg = a.seg[sidx];
@@ -183,6 +185,9 @@ __global__ __launch_bounds__(256) void bwd_anchor_kernel(BwdArgs a, int nblk) {
     __bf16 *kh = static_cast<__bf16 *>(a.kh);
     int spread = 0;
     uint32_t qm[NBK] = {}, km[NBK] = {};  // the largest stored |q~|, |k~| per block (bf16 magnitude bits)
+    // per block the largest stored |q~|, |k~| of each of the thread's 8 channels
+    // (the thread's channel chunk, tid % (K / 8), is the same at every row)
+    u16x2 qc[NBK][4] = {}, kc[NBK][4] = {};
     for (int c = tid; c < n * (K / 8); c += 256) {
         const int r = c / (K / 8), ch = 8 * (c % (K / 8)), b = r / BWD_BLK;
         const int64_t t = s0 + r0 + r, ix = (t * HQ + hq) * K + ch;
@@ -216,8 +221,34 @@ __global__ __launch_bounds__(256) void bwd_anchor_kernel(BwdArgs a, int nblk) {
         for (int bb = 0; bb < NBK; ++bb) {
             qm[bb] = bb == b ? max(qm[bb], mq) : qm[bb];
             km[bb] = bb == b ? max(km[bb], mk) : km[bb];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const u16x2 xq = __builtin_bit_cast(u16x2, wq[e] & 0x7fff7fffu);
+                const u16x2 xk = __builtin_bit_cast(u16x2, wk[e] & 0x7fff7fffu);
+                qc[bb][e] = bb == b ? __builtin_elementwise_max(qc[bb][e], xq) : qc[bb][e];
+                kc[bb][e] = bb == b ? __builtin_elementwise_max(kc[bb][e], xk) : kc[bb][e];
+            }
         }
     }
+    // the channel maxima over the wave's lanes of the same chunk (lanes K/8 apart),
+    // then lanes 0 .. K/8 - 1 leave the wave's maxima of chunk `lane` in LDS
+#pragma unroll
+    for (int bb = 0; bb < NBK; ++bb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+#pragma unroll
+            for (int off = K / 8; off < 64; off <<= 1) {
+                qc[bb][e] = __builtin_elementwise_max(
+                    qc[bb][e], __builtin_bit_cast(u16x2, __shfl_xor(__builtin_bit_cast(int, qc[bb][e]), off)));
+                kc[bb][e] = __builtin_elementwise_max(
+                    kc[bb][e], __builtin_bit_cast(u16x2, __shfl_xor(__builtin_bit_cast(int, kc[bb][e]), off)));
+            }
+            const int lane = tid & 63;
+            if (lane < K / 8) {
+                sC[0][bb][tid >> 6][4 * lane + e] = __builtin_bit_cast(uint32_t, qc[bb][e]);
+                sC[1][bb][tid >> 6][4 * lane + e] = __builtin_bit_cast(uint32_t, kc[bb][e]);
+            }
+        }
     if (spread) atomicOr(&sflag, spread);
     // the wave's maxima, then one atomic per wave and block
 #pragma unroll
@@ -241,17 +272,26 @@ __global__ __launch_bounds__(256) void bwd_anchor_kernel(BwdArgs a, int nblk) {
     }
     // all four entries of the tile, also those of blocks past a short tail (0)
     if (tid < NBK) a.flag[(gb0 + tid) * HQ + hq] = (BWD_BLK * tid < n && ((sflag >> tid) & 1)) ? sidx + 1 : 0;
+    // the channel maxima of each block over the four waves: cmax[block, hq, {q, k}, K]
+    for (int x = tid; x < 2 * NBK * (K / 2); x += 256) {
+        const int qk = x / (NBK * (K / 2)), bb = (x / (K / 2)) % NBK, pr = x % (K / 2);
+        u16x2 m = {0, 0};
+#pragma unroll
+        for (int ww = 0; ww < 4; ++ww) m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, sC[qk][bb][ww][pr]));
+        reinterpret_cast<uint32_t *>(a.cmax + ((gb0 + bb) * HQ + hq) * 2 * K + qk * K)[pr] = __builtin_bit_cast(uint32_t, m);
+    }
 }
 
 // ---------------------------------------------------------------- far tiles
 // A pair in different 128-row tiles is read at an anchor between its rows:
 // the dq kernel moves each key's k~ down to the anchor before its query tile,
 // the dk/dv kernel each query's q~ down to the anchor of its key tile's last
-// block.  A value stored at anchor A_b and moved to A_x is below the block's
-// largest stored magnitude times 2^max_n(A_x,n - A_b,n), so a pair's score
-// S_ij = q~_i . k~_j is below K times the two moved bounds.  Without a scalar
-// gate or a window the kernels leave out the pairs of a (query block, key
-// tile) or (query tile, key block) whose bound is at most 2^(e - 26), with
+// block.  Channel n of a value stored at anchor A_b and moved to A_x is below
+// the block's largest stored magnitude of that channel (recorded by the anchor
+// pass) times 2^(A_x,n - A_b,n), so a pair's score S_ij = q~_i . k~_j is below
+// the sum over the channels of the two sides' bounds.  Without a scalar gate
+// or a window the kernels leave out the pairs of a (query block, key tile) or
+// (query tile, key block) whose bound is at most 2^(e - 26), with
 // 2^e <= L_i = lse_i log2e for every query row of the pair: there S_ij lies
 // below a quarter of half the float32 spacing of L_i, so S_ij - L_i rounds to
 // -L_i and A_ij = 2^-L_i exactly, as the products would give it.  Such a pair
@@ -259,46 +299,49 @@ __global__ __launch_bounds__(256) void bwd_anchor_kernel(BwdArgs a, int nblk) {
 // suffix sums of those rows (the two small kernels below); its terms of dq_i,
 // dk_j and X (each with the factor q~_i k~_j of a score below 2^(e - 26), i.e.
 // at most |dS_ij| 2^(e - 26) in X) are dropped.  Pairs whose moved values all
-// round to 0 in bf16 (bound at most 2^-134) have every such term exactly 0 and
-// are left out as well.  The dq kernel starts its walk at the first key block
-// that has to be kept; the dk/dv kernel stops after the last query block that
-// has to be kept.
+// round to 0 in bf16 (from the block's largest magnitude over all channels,
+// at most 2^-134 after the move) have every such term exactly 0 and are left
+// out as well.  The dq kernel starts its walk at the first key block that has
+// to be kept; the dk/dv kernel stops after the last query block that has to
+// be kept.
 //
-// The bound's exponent for a block of largest magnitude m (float bits), moved
+// The exponent bound for a block of largest magnitude m (float bits), moved
 // by gap: the moved values lie below 2^(this).
-template <int K>
-constexpr int LOG2K() {
-    static_assert(K == 64 || K == 128, "channel count");
-    return K == 128 ? 7 : 6;
-}
 __device__ inline int moved_exponent(uint32_t mbits, float gap) {
     if (mbits == 0u) return -100000;
     int e;
     (void)frexpf(__uint_as_float(mbits), &e);  // m < 2^e
     return e + (int)fminf(fmaxf(gap, -100000.f), 100000.f);
 }
-// max_n (x_n - y_n) over K channels, x in global memory, y in LDS
+
+// The far-pair test of one block against the other side's per-channel bounds
+// M_n (in LDS): the moved values of the block's channels n are below
+// c_n 2^(x_n - y_n), c_n its largest stored magnitude (bf16 bits in cm), x and y
+// the anchors the move goes between, so every score of its pairs is below
+// sum_n c_n 2^(x_n - y_n) M_n.  The pairs are left out when that bound is at
+// most 2^(e - 26) (e >= -60 from the block's rows, see above; the sum is
+// rounded and scaled by 1.001 against its float32 rounding) or when every moved
+// value rounds to 0 (max_n (x_n - y_n) past -134 below the block's largest).
 template <int K>
-__device__ inline float max_gap(const float *x, const float *y) {
-    float g = -3.0e38f;
-#pragma unroll 8
-    for (int n = 0; n < K; n += 4) {
-        const f32x4 a = *reinterpret_cast<const f32x4 *>(x + n), b = *reinterpret_cast<const f32x4 *>(y + n);
+__device__ inline bool far_block_out(const uint16_t *cm, const float *x, const float *y, const float *M,
+                                     uint32_t bmax_bits, int e) {
+    float gap = -3.0e38f, bound = 0.f;
+#pragma unroll 4
+    for (int n = 0; n < K; n += 8) {
+        const uint4 cw = *reinterpret_cast<const uint4 *>(cm + n);
+        const uint32_t cv[4] = {cw.x, cw.y, cw.z, cw.w};
+        const f32x4 x0 = *reinterpret_cast<const f32x4 *>(x + n), x1 = *reinterpret_cast<const f32x4 *>(x + n + 4);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) g = fmaxf(g, a[e] - b[e]);
+        for (int i = 0; i < 8; ++i) {
+            const float d = (i < 4 ? x0[i] : x1[i - 4]) - y[n + i];
+            gap = fmaxf(gap, d);
+            const float c = __uint_as_float((i & 1 ? cv[i / 2] >> 16 : cv[i / 2] & 0xffffu) << 16);
+            bound = fmaf(ldexpf(c, (int)fminf(fmaxf(d, -1000.f), 1000.f)), M[n + i], bound);
+        }
     }
-    return g;
-}
-template <int K>
-__device__ inline float max_gap_rev(const float *x, const float *y) {  // max_n (y_n - x_n)
-    float g = -3.0e38f;
-#pragma unroll 8
-    for (int n = 0; n < K; n += 4) {
-        const f32x4 a = *reinterpret_cast<const f32x4 *>(x + n), b = *reinterpret_cast<const f32x4 *>(y + n);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) g = fmaxf(g, b[e] - a[e]);
-    }
-    return g;
+    if (moved_exponent(bmax_bits, gap) <= -134) return true;
+    if (e < -60) return false;
+    return bound * 1.001f <= ldexpf(1.f, e - 26);  // a NaN or inf bound keeps the block
 }
 
 // Per (32-row block, query head): the sum over its rows i < len of
@@ -420,7 +463,6 @@ __device__ inline float shift_anchor(float x, float to, float from) {
 // >= 0.  A staged bf16 value then moves by a saturating 16-bit subtract on its
 // magnitude when they all are (the same bits as ldexp for a result in the
 // normal range; 0, or a value below 2^-126, otherwise), else by ldexp.
-typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 constexpr int DEC_SLOTS = 4;  // tables in flight: formed at tile t - 3, read at t - 1
 struct alignas(16) DecTab {
     uint32_t w[DEC_SLOTS][64];  // exponent-field decrements, K/2 <= 64 channel pairs
@@ -499,7 +541,7 @@ __global__ __launch_bounds__(NTH_KV) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
     // q~ is not 0 (a tile whose staged q~ is all 0 is left to the dead-tile path)
     __shared__ int sLive[2];
     __shared__ int sLast;  // the last query tile past the key tile that has to be kept
-    __shared__ int sKe;    // the exponent bound of the key tile's k~ moved to A_K
+    __shared__ float sKM[K];  // per channel the bound of the key tile's k~ moved to A_K
     __shared__ DecTab sDec;  // the moves of staged q~ to A_K (tiles after the key tile)
 
     const BlockPos bp = block_pos(a, nblk, true);
@@ -535,24 +577,27 @@ __global__ __launch_bounds__(NTH_KV) void bwd_dkdv_mfma(BwdArgs a, int nblk) {
     // the suffix sums of bf16(2^-L_i) do_i.
     int wcut = -1;  // the first sequence block left to the suffix sums
     if (!HAS_G && a.window <= 0 && n_off > 0) {
-        if (tid == 0) {
-            sLast = -1;
-            sKe = BWD_NO_EXP;
+        if (tid == 0) sLast = -1;
+        // per channel the bound of the tile's k~ moved to A_K: the largest over
+        // its blocks b of the stored |k~| times 2^(A_K - A_b)
+        if (tid < K) {
+            float m = 0.f;
+            for (int b = 0; b < NBK; ++b) {
+                if (BWD_BLK * b >= jn) break;
+                const float c = __uint_as_float((uint32_t)a.cmax[((gb0 + b) * HQ + hq) * 2 * K + K + tid] << 16);
+                m = fmaxf(m, ldexpf(c, (int)fminf(fmaxf(sA[NBK][tid] - sA[b + 1][tid], -1000.f), 1000.f)));
+            }
+            sKM[tid] = m;
         }
         __syncthreads();
-        // the bound of the tile's k~ moved to A_K: block b's stored k~ times 2^(A_K - A_b)
-        if (tid < NBK && BWD_BLK * tid < jn)
-            atomicMax(&sKe, moved_exponent(a.bmax[((gb0 + tid) * HQ + hq) * BWD_BM + 1],
-                                           max_gap<K>(sA[NBK], sA[tid + 1])));
-        __syncthreads();
-        const int ke = sKe + LOG2K<K>();
         for (int t = tid; t < n_off; t += NTH_KV) {
             const int b = (j0 + BR + BT * t) / BWD_BLK;  // the tile's block (BT rows)
             const int64_t gb = (int64_t)sg.tile_base * NBK + b;
             const uint32_t *bm = a.bmax + (gb * HQ + hq) * BWD_BM;
-            const float gap = max_gap<K>(a.Ab + ((gb - 1) * HQ + hq) * K, sA[NBK]);  // max_n A_(b-1) - A_K
-            const int mq = moved_exponent(bm[0], gap);
-            if (mq > -134 && mq + ke > (int)bm[2] - 26) atomicMax(&sLast, t);
+            // the block's q~, stored at A_(b-1), moved to A_K
+            if (!far_block_out<K>(a.cmax + (gb * HQ + hq) * 2 * K, a.Ab + ((gb - 1) * HQ + hq) * K, sA[NBK], sKM,
+                                  bm[0], (int)bm[2]))
+                atomicMax(&sLast, t);
         }
         __syncthreads();
         const int keep = sLast + 1;
@@ -936,7 +981,8 @@ __global__ __launch_bounds__(NTH, 2) void bwd_dq_mfma(BwdArgs a, int nblk) {
     // moved k~ is not 0 (a tile staged as all 0 adds nothing and is skipped)
     __shared__ int sLive[2];
     __shared__ int sFirst;  // the first key block before the query tile that has to be kept
-    __shared__ int sQe, sLe;  // the exponent bound of the tile's moved q~; e with 2^e <= L_i on its rows
+    __shared__ int sLe;        // e with 2^e <= L_i on the tile's rows
+    __shared__ float sQM[K];  // per channel the bound of the tile's q~ moved to sA[0]
     __shared__ DecTab sDec;   // the moves of staged k~ to sA[0] (key tiles before the query tile)
 
     const BlockPos bp = block_pos(a, nblk, false);
@@ -1023,26 +1069,32 @@ __global__ __launch_bounds__(NTH, 2) void bwd_dq_mfma(BwdArgs a, int nblk) {
     if (!HAS_G && a.window <= 0 && klo < i0) {
         if (tid == 0) {
             sFirst = i0 / BWD_BLK;
-            sQe = BWD_NO_EXP;
             sLe = INT_MAX;
         }
-        __syncthreads();
-        // the bound of the tile's q~ moved to sA[0] (block b's stored at sA[b]),
-        // and e with 2^e <= L_i for every row of the tile
-        if (tid < NBK && BWD_BLK * tid < in_) {
-            const uint32_t *bm = a.bmax + ((gb0 + tid) * HQ + hq) * BWD_BM;
-            atomicMax(&sQe, moved_exponent(bm[0], max_gap<K>(sA[tid], sA[0])));
-            atomicMin(&sLe, (int)bm[2]);
+        // per channel the bound of the tile's q~ moved to sA[0]: the largest over
+        // its blocks b (q~ stored at sA[b]) of the stored |q~| times 2^(sA[b] - sA[0])
+        if (tid < K) {
+            float m = 0.f;
+            for (int b = 0; b < NBK; ++b) {
+                if (BWD_BLK * b >= in_) break;
+                const float c = __uint_as_float((uint32_t)a.cmax[((gb0 + b) * HQ + hq) * 2 * K + tid] << 16);
+                m = fmaxf(m, ldexpf(c, (int)fminf(fmaxf(sA[b][tid] - sA[0][tid], -1000.f), 1000.f)));
+            }
+            sQM[tid] = m;
         }
         __syncthreads();
-        const int qe = sQe + LOG2K<K>(), le = sLe - 26;
+        // e with 2^e <= L_i for every row of the tile
+        if (tid < NBK && BWD_BLK * tid < in_) atomicMin(&sLe, (int)a.bmax[((gb0 + tid) * HQ + hq) * BWD_BM + 2]);
+        __syncthreads();
+        const int le = sLe;
         const int nfar = (i0 - klo) / BWD_BLK;
         for (int t = tid; t < nfar; t += NTH) {
             const int b = klo / BWD_BLK + t;
             const int64_t gb = (int64_t)sg.tile_base * NBK + b;
-            const float gap = max_gap_rev<K>(a.Ab + (gb * HQ + hq) * K, sA[0]);  // max_n A_Q - A_b
-            const int mk = moved_exponent(a.bmax[(gb * HQ + hq) * BWD_BM + 1], gap);
-            if (mk > -134 && mk + qe > le) atomicMin(&sFirst, b);
+            // the block's k~, stored at A_b, moved to A_Q = sA[0]
+            if (!far_block_out<K>(a.cmax + (gb * HQ + hq) * 2 * K + K, sA[0], a.Ab + (gb * HQ + hq) * K, sQM,
+                                  a.bmax[(gb * HQ + hq) * BWD_BM + 1], le))
+                atomicMin(&sFirst, b);
         }
         __syncthreads();
         klo = sFirst * BWD_BLK;

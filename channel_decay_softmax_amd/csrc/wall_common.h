@@ -236,6 +236,7 @@ struct BwdArgs {
     float *Ab;                         // workspace (bf16 path): block anchors [blocks, HQ, K]
     int32_t *flag;                     // workspace (bf16 path): [blocks, HQ], sequence + 1 of a spread block, else 0
     uint32_t *bmax;                    // workspace (bf16 path): [blocks, HQ, BWD_BM], see BWD_BM
+    uint16_t *cmax;                    // workspace (bf16 path): [blocks, HQ, 2, K] per channel the largest stored |q~|, |k~| (bf16 bits)
     float *wsum;                       // workspace (bf16 path): [blocks, HQ, V] sums of bf16(2^-L) do from a block on
     const SegInfo *seg;
     int32_t nseg, max_seqlen, rows, HQ, H, K, V, window;
@@ -267,7 +268,7 @@ constexpr int64_t BWD_MAX_V = 128;
 
 struct BwdLayout {
     size_t off_seg, off_D, off_X, off_Y, off_Z, off_part, off_dqd, off_qh, off_kh, off_rt, off_flag, off_bmax,
-        off_wsum, off_scan, total;
+        off_cmax, off_wsum, off_scan, total;
 };
 inline BwdLayout bwd_layout(int64_t B, int64_t T, int64_t HQ, int64_t K, int64_t nseg) {
     BwdLayout L;
@@ -299,6 +300,8 @@ inline BwdLayout bwd_layout(int64_t B, int64_t T, int64_t HQ, int64_t K, int64_t
     o = align_up(o + sizeof(int32_t) * blocks * HQ, 256);
     L.off_bmax = o;
     o = align_up(o + sizeof(uint32_t) * blocks * HQ * BWD_BM, 256);
+    L.off_cmax = o;
+    o = align_up(o + sizeof(uint16_t) * blocks * HQ * 2 * K, 256);
     L.off_wsum = o;
     o = align_up(o + sizeof(float) * blocks * HQ * BWD_MAX_V, 256);
     L.off_scan = o;

@@ -316,8 +316,8 @@ wall_status_t wall_attn_fwd_run(const void *q, const void *k, const void *v, wal
  * of two, and the q-side and k-side terms of dg are formed from the same
  * rounded q~ and k~, so their rounding cancels in dg's sums.  bf16 inputs
  * without g_scalar or a window: pairs of rows in different 128-row tiles
- * whose score is bounded (from each block's largest stored |q~|, |k~| and
- * the anchor gaps) by 2^(e - 26), with 2^e <= lse_i log2e, are left out of
+ * whose score is bounded (from each block's per-channel largest stored
+ * |q~|, |k~| and the anchor gaps) by 2^(e - 26), with 2^e <= lse_i log2e, are left out of
  * the products: their probability is exactly 2^(-lse_i log2e) in float32,
  * their dv terms come from per-block suffix sums of those weights times
  * do_i, and their dq, dk and dg terms (each carrying that score as a
