@@ -19,6 +19,12 @@
  *     on the current HIP device, aligned to 16 bytes.  The library keeps no
  *     pointer after a call returns, allocates nothing, never synchronises and
  *     never aborts.
+ *   - Debugging: with the environment variable WALL_DEBUG set to a value other
+ *     than "0" (read once per process), a refused call prints its entry point,
+ *     the failed check's line and the status to stderr, and each call that
+ *     launches kernels synchronises the device before returning, so that a
+ *     kernel fault is reported (as WALL_ERR_LAUNCH, with the HIP error on
+ *     stderr) by the call that launched it.
  *   - Work is enqueued on `stream` (0 = the legacy default stream) and runs
  *     asynchronously; outputs are valid once the stream reaches that point.
  *   - Token-major layouts: a token row is (b, t) with flat id b*T + t; with

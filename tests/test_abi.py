@@ -307,3 +307,37 @@ def test_cu_seqlens_host_checks():
             wall.check_cu_seqlens(torch.tensor(bad, dtype=torch.int32), 1, T)
     with pytest.raises(ValueError):
         wall.check_cu_seqlens(torch.tensor([0, 10], dtype=torch.int32), 2, T)
+
+
+_DEBUG_CALL = """
+import channel_decay_softmax_amd as wall
+from channel_decay_softmax_amd import _binding as B
+L = wall.lib()
+F = 1 << 20
+P = lambda x: None if x is None else __import__('ctypes').c_void_p(x)
+wsb = L.wall_attn_fwd_workspace_size(B.WALL_BF16, 1, 256, 6, 4, 128, 128, 0)
+rc = L.wall_attn_fwd(P(F), P(F), P(F), B.WALL_BF16, P(F), None, None, P(F), None, 1, 256, 6, 4, 128, 128,
+                     0.088, 0, None, 0, 0, P(F), wsb, None)
+print('status', rc)
+"""
+
+
+@pytest.mark.parametrize("debug", ["1", None])
+def test_wall_debug_reports_refused_calls(debug):
+    """With WALL_DEBUG set, a refused call (here HQ % H != 0) names the check
+    that failed on stderr; without it the library prints nothing."""
+    import subprocess
+    import sys
+    env = dict(os.environ)
+    env.pop("WALL_DEBUG", None)
+    if debug:
+        env["WALL_DEBUG"] = debug
+    r = subprocess.run([sys.executable, "-c", _DEBUG_CALL], cwd=ROOT, env=env, capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 0, r.stderr
+    assert f"status {INVALID}" in r.stdout
+    lines = [l for l in r.stderr.splitlines() if l.startswith("wall:")]
+    if debug:
+        assert any("refused the call: WALL_ERR_INVALID_ARG (wall_api.cpp:" in l for l in lines), r.stderr
+    else:
+        assert not lines, r.stderr
