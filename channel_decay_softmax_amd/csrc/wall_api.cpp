@@ -230,6 +230,7 @@ wall_status_t enqueue_prepare(const void *q, const void *k, const void *v, wall_
                 ws + L.off_qd, reinterpret_cast<uint32_t *>(ws + L.off_drec), scale * LOG2E,
                 L.nseg, L.tiles, s.HQ, s.H, s.K, s.V, s.T};
     pa.vsum = reinterpret_cast<float *>(ws + L.off_vsum);
+    pa.kcm = reinterpret_cast<float *>(ws + L.off_kcm);
     return launched(launch_prep(pa, dtype == WALL_BF16, stream));
 }
 
@@ -254,6 +255,7 @@ wall_status_t enqueue_run(const void *q, const void *k, const void *v, wall_dtyp
     fa.anchor = reinterpret_cast<const float *>(ws + L.off_anchor);
     fa.rec = reinterpret_cast<const uint32_t *>(ws + L.off_rec);
     fa.vsum = reinterpret_cast<const float *>(ws + L.off_vsum);
+    fa.kcm = reinterpret_cast<const float *>(ws + L.off_kcm);
     fa.seg = reinterpret_cast<const SegInfo *>(ws + L.off_seg);
     fa.o = o;
     fa.lse = lse;
@@ -315,6 +317,7 @@ wall_status_t wall_attn_fwd_prepare_gate(const void *q, const void *k, const voi
         pa.g = g;
         pa.Pw = P;
         pa.vsum = reinterpret_cast<float *>(ws + L.off_vsum);
+        pa.kcm = reinterpret_cast<float *>(ws + L.off_kcm);
         pa.csum = reinterpret_cast<const float *>(static_cast<const char *>(sws) + SL.off_sum);
         pa.pscale = pscale;
         return launched(launch_scan_prep(pa, stream));

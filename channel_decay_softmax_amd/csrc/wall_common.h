@@ -107,7 +107,8 @@ inline ScanLayout scan_layout(int64_t B, int64_t T, int64_t C) {
 struct FwdLayout {
     int64_t nseg;        // sequences (num_seqs with packing, else B)
     int64_t tiles;       // upper bound on sum_s ceil(len_s / TILE)
-    size_t off_seg, off_anchor, off_rec, off_kt, off_vt, off_kd, off_qd, off_drec, off_vsum, off_scan, total;
+    size_t off_seg, off_anchor, off_rec, off_kt, off_vt, off_kd, off_qd, off_drec, off_vsum, off_kcm, off_scan,
+        total;
 };
 
 inline FwdLayout fwd_layout(int64_t esize, int64_t B, int64_t T, int64_t HQ, int64_t H,
@@ -135,6 +136,8 @@ inline FwdLayout fwd_layout(int64_t esize, int64_t B, int64_t T, int64_t HQ, int
     o = align_up(o + sizeof(uint32_t) * (size_t)(L.tiles * HQ * DREC_N * (K / 2)), 256);
     L.off_vsum = o;
     o = align_up(o + sizeof(float) * (size_t)(L.tiles * H * V), 256);
+    L.off_kcm = o;
+    o = align_up(o + sizeof(float) * (size_t)(L.tiles * HQ * K), 256);
     // the prefix scan of wall_attn_fwd_prepare_gate
     L.off_scan = o;
     o = align_up(o + scan_layout(B, T, HQ * K).total, 256);
@@ -182,6 +185,7 @@ struct PrepArgs {
     const float *csum;
     float pscale;
     float *vsum;       // [tiles, H, V] float32 sums of each value tile's rows (bf16 path)
+    float *kcm;        // [tiles, HQ, K] per channel the largest |k| of the tile's keys (bf16 path)
 };
 // bf16: the sequence table, anchors, carry records, key and value tiles;
 // float32: the sequence table only.
@@ -219,6 +223,7 @@ struct FwdArgs {
     int32_t window;         // <= 0: none
     float qscale;           // scale * log2(e)
     const float *vsum;      // [tiles, H, V] float32 sums of each value tile's rows (bf16 path)
+    const float *kcm;       // [tiles, HQ, K] per channel the largest |k| of the tile's keys (bf16 path)
 };
 hipError_t launch_fwd_bf16(const FwdArgs &a, hipStream_t st);
 hipError_t launch_fwd_f32(const FwdArgs &a, hipStream_t st);

@@ -1078,6 +1078,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
     // closed form's partial value sums
     constexpr int NPART = NW * 64 / V;
     __shared__ __attribute__((aligned(16))) uint32_t zvote[2][NW];
+    __shared__ __attribute__((aligned(16))) uint32_t skm[K];  // per channel the largest |k| of the pass's tiles
     __shared__ __attribute__((aligned(16))) float zred[NPART][V];
 
     // One 256-row query block per workgroup.  The blocks farthest into their
@@ -1113,6 +1114,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
     // second value buffer finite contents once.
     for (int i = tid; i < VL::BYTES / 16; i += NW * 64) reinterpret_cast<uint4 *>(v1)[i] = uint4{0, 0, 0, 0};
     if (tid < 2 * KS) reinterpret_cast<uint4 *>(zrec)[tid] = uint4{0, 0, 0, 0};
+    if (tid < K) skm[tid] = 0u;
 
     KR kr{a, {}, k0, k1, v0, v1, sg, hq, hq / (a.HQ / a.H), w, lane, 0, 0,
           tile_lane_offset<KL>(lane), tile_lane_offset<VL>(lane), false};
@@ -1182,20 +1184,21 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) wv.Pw[0][t][e] = 0u;
         // the pass's key tiles: whether some channel's prefix grows over one
-        // of them, and the largest |k| of their keys (uniform over the workgroup)
+        // of them (uniform over the workgroup), and per channel the largest |k|
+        // of their keys (in LDS after the barrier below)
         bool grow = false;
-        float kbound = 0.f;
         for (int c0 = c_lo; run_pipe && c0 <= c_hi; c0 += 64) {
             const int ct = c0 + lane;
-            if (ct <= c_hi) {
-                const uint32_t *rr = a.rec + ((int64_t)(sg.tile_base + ct) * HQ + hq) * REC_WORDS;
-                grow = grow || rr[REC_GROW] != 0u;
-                kbound = fmaxf(kbound, __uint_as_float(rr[REC_KMAX]));
-            }
+            if (ct <= c_hi) grow = grow || a.rec[((int64_t)(sg.tile_base + ct) * HQ + hq) * REC_WORDS + REC_GROW] != 0u;
         }
         grow = __builtin_amdgcn_ballot_w64(grow) != 0u;
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) kbound = fmaxf(kbound, __shfl_xor(kbound, off));
+        if (!HAS_G && a.window <= 0 && run_pipe) {
+            constexpr int TPC = NW * 64 / K;  // threads per channel
+            float km = 0.f;
+            for (int ct = c_lo + tid / K; ct <= c_hi; ct += TPC)
+                km = fmaxf(km, a.kcm[((int64_t)(sg.tile_base + ct) * HQ + hq) * K + tid % K]);
+            atomicMax(&skm[tid % K], __float_as_uint(km));  // non-negative floats order as their bits
+        }
         // The keys of tile c_hi, q~ and the records are in; the values of tile
         // c_hi and the keys of tile c_hi - 1 stay in flight into the pipeline,
         // whose first barriers wait for them.
@@ -1235,30 +1238,33 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
             // window or a scalar gate, and with no tile of the pass where the prefix
             // grows, every wave votes at each tile whether every product of its
             // queries with every key left is too small to move -m in float32, and
-            // no lane would raise its max on such keys.  qb bounds the largest |q~|
-            // of the lane's query over its channels at the current tile's anchors:
-            // exact at the start, then lowered by the smallest shift of each carry.
+            // no lane would raise its max on such keys.  qb bounds the sum over the
+            // channels of the lane's query's |q~| at the current tile's anchors
+            // times the channel's largest |k| over the pass (every |k~| is at most
+            // |k| for a prefix that falls): exact q~ at the start, then lowered by
+            // the smallest shift of each carry.
             // Once all eight waves have voted so at tile c + 1, the tiles c .. c_lo
             // are summed in closed form and the pipeline ends.
             const bool zero_ok = !HAS_G && a.window <= 0 && !grow;
             float qb = 0.f;
             if (zero_ok) {
-                u16x2 mx = {0, 0};
+                // the lane's channels 16 s8 + 8 hl + e, then the other half's
+                float qs = 0.f;
 #pragma unroll
                 for (int s8 = 0; s8 < KS; ++s8) {
-                    const uint4 x = __builtin_bit_cast(uint4, wv.qop[s8]);
-                    const uint32_t xv[4] = {x.x, x.y, x.z, x.w};
+                    const f32x4 m0 = *reinterpret_cast<const f32x4 *>(&skm[16 * s8 + 8 * hl]);
+                    const f32x4 m1 = *reinterpret_cast<const f32x4 *>(&skm[16 * s8 + 8 * hl + 4]);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2, xv[e] & 0x7fff7fffu));
+                    for (int e = 0; e < 8; ++e)
+                        qs = fmaf(fabsf((float)wv.qop[s8][e]), e < 4 ? m0[e] : m1[e - 4], qs);
                 }
-                qb = pair_max(__uint_as_float((uint32_t)max(mx[0], mx[1]) << 16));
+                qb = pair_sum(qs);
             }
             auto zero_vote = [&](int c, const char *kc) {
                 const float p0 = (float)(__bf16)fast_exp2(-wv.m);
-                // a quarter of m's float32 unit in the last place, over the K <= 128 products
-                const float thr = __uint_as_float(__float_as_uint(wv.m) & 0x7f800000u) * 0x1p-32f;
-                const bool ok = wv.m >= 0.f && wv.lim >= 0.f && 32.f * p0 <= wv.lim && qb * kbound <= thr;
+                // a quarter of m's float32 unit in the last place
+                const float thr = __uint_as_float(__float_as_uint(wv.m) & 0x7f800000u) * 0x1p-25f;
+                const bool ok = wv.m >= 0.f && wv.lim >= 0.f && 32.f * p0 <= wv.lim && qb <= thr;
                 const bool dead = !wave_on || __builtin_amdgcn_ballot_w64(!ok) == 0u;
                 zvote[c & 1][w] = dead ? 1u : 0u;  // every lane stores the same word
                 // q~ after this tile's carries (a wave carries on the tiles before its own, down to c_lo + 1)

@@ -151,6 +151,7 @@ __device__ inline void key_tile(const PrepArgs &a, int tile, int hq, const SegIn
     constexpr int NPASS = TILE / RPP;
     constexpr int NB = TILE / DBLK;     // 32-row blocks per tile
     __shared__ uint32_t sflag, sdmin, skmax;
+    __shared__ uint32_t skc[K];  // per channel the largest |k| (float bits)
     const int c = tile - sg.tile_base;
     const int h = hq / (int)(a.HQ / a.H);
     const int c8 = threadIdx.x % CPR, r0 = threadIdx.x / CPR;
@@ -160,6 +161,7 @@ __device__ inline void key_tile(const PrepArgs &a, int tile, int hq, const SegIn
         sdmin = 255u;
         skmax = 0u;
     }
+    if (threadIdx.x < K) skc[threadIdx.x] = 0u;
     __syncthreads();
     // anchors: the tile's last row (keys read from later tiles) and each
     // 32-row block's last row (the fused kernel's diagonal phase)
@@ -196,6 +198,7 @@ __device__ inline void key_tile(const PrepArgs &a, int tile, int hq, const SegIn
     constexpr int NH = NPASS / 2;
     uint32_t flags = 0;
     float kmax = 0.f;
+    f32x8 kmc = {};  // per channel of the thread's chunk the largest |k| of its rows
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
         f32x8 kv[NH], pv[NH], qv[NH];
@@ -220,6 +223,7 @@ __device__ inline void key_tile(const PrepArgs &a, int tile, int hq, const SegIn
             float dev = 0.f;
             for (int e = 0; e < 8; ++e) {
                 kmax = fmaxf(kmax, fabsf(kv[i][e]));
+                kmc[e] = fmaxf(kmc[e], fabsf(kv[i][e]));
                 kl[e] = kv[i][e] * __builtin_amdgcn_exp2f(fminf(fmaxf(R[e] - pv[i][e], EXP2_LO), EXP2_HI));
                 const float x = pv[i][e] - A[b][e];
                 dev = fmaxf(dev, fabsf(x));
@@ -234,6 +238,8 @@ __device__ inline void key_tile(const PrepArgs &a, int tile, int hq, const SegIn
     }
     if (flags) atomicOr(&sflag, flags);
     atomicMax(&skmax, __float_as_uint(kmax));  // non-negative floats order as their bits
+#pragma unroll
+    for (int e = 0; e < 8; ++e) atomicMax(&skc[c8 * 8 + e], __float_as_uint(kmc[e]));
     __syncthreads();
     if (threadIdx.x == 0) {
         uint32_t *rec = a.rec + ((int64_t)tile * HQ + hq) * REC_WORDS;
@@ -241,6 +247,7 @@ __device__ inline void key_tile(const PrepArgs &a, int tile, int hq, const SegIn
         rec[REC_DMIN] = sdmin;
         rec[REC_KMAX] = skmax;
     }
+    if (threadIdx.x < K) a.kcm[((int64_t)tile * HQ + hq) * K + threadIdx.x] = __uint_as_float(skc[threadIdx.x]);
 }
 
 // Value tile of (tile, kv head), transposed [V][TILE].  Thread (kb, db)
@@ -333,6 +340,7 @@ __device__ inline void scan_key_slice(const PrepArgs &a, int tile, int y) {
     __shared__ f32x8 ssum[SP_NSUB][SP_CV];
     __shared__ f32x8 spart[2][SP_NSUB][SP_CV];  // partial carries of this tile and the next
     __shared__ uint32_t sflag[HPS], sgrow[HPS], sdmin[HPS], skmax[HPS];
+    __shared__ uint32_t skc[SP_CV * 8];  // per channel of the slice the largest |k| (float bits)
     const int tid = threadIdx.x, sub = tid / SP_CV, cv = tid % SP_CV, rb = sub / SPB;
     const int64_t C = a.HQ * K, HQ = a.HQ;
     const int64_t ch = ((int64_t)y * SP_CV + cv) * 8;
@@ -348,6 +356,7 @@ __device__ inline void scan_key_slice(const PrepArgs &a, int tile, int y) {
         sdmin[tid] = 255u;
         skmax[tid] = 0u;
     }
+    if (tid < SP_CV * 8) skc[tid] = 0u;
     // pass 1: the sum of the thread's rows; meanwhile the partial carries:
     // thread sub sums the chunk sums of the sequence's tiles sub, sub + 16, ..
     // before this tile (pc) and before the next (pn), in tile order (the
@@ -443,6 +452,7 @@ __device__ inline void scan_key_slice(const PrepArgs &a, int tile, int y) {
             qr[i] = raw8(qin + r * C + ch);
         }
         float kmax = 0.f;  // the largest |k| of the thread's rows
+        f32x8 kmc = {};    // and of each of its channels
         const bool ends_block = (sub + 1) % SPB == 0;  // the thread holds its block's last row
 #pragma unroll
         for (int i = 0; i < SP_SUB; ++i) {
@@ -454,6 +464,7 @@ __device__ inline void scan_key_slice(const PrepArgs &a, int tile, int y) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 kmax = fmaxf(kmax, fabsf(kv[e]));
+                kmc[e] = fmaxf(kmc[e], fabsf(kv[e]));
                 pv[e] = a.pscale * (last ? Eb[e] : run[e]);
                 kl[e] = kv[e] * __builtin_amdgcn_exp2f(fminf(fmaxf(R[e] - pv[e], EXP2_LO), EXP2_HI));
                 const float d = pv[e] - Ab[e];
@@ -471,9 +482,14 @@ __device__ inline void scan_key_slice(const PrepArgs &a, int tile, int y) {
             Vec8<__bf16>::store(qdout + row * K, qb);
         }
         atomicMax(&skmax[hl], __float_as_uint(kmax));  // non-negative floats order as their bits
+#pragma unroll
+        for (int e = 0; e < 8; ++e) atomicMax(&skc[cv * 8 + e], __float_as_uint(kmc[e]));
     }
     if (spread) atomicOr(&sflag[hl], 1u << rb);
     __syncthreads();
+    // [tile, HQ, K] flat over the HQ * K channels of the gate
+    if (tid < SP_CV * 8 && (int64_t)y * SP_CV * 8 + tid < C)
+        a.kcm[(int64_t)tile * C + (int64_t)y * SP_CV * 8 + tid] = __uint_as_float(skc[tid]);
     if (on && c8 == 0 && sub == 0) {
         uint32_t *rec = a.rec + ((int64_t)tile * HQ + hq) * REC_WORDS;
         rec[REC_GROW] = sgrow[hl] & 1u;
