@@ -400,20 +400,14 @@ def test_fwd_parity_full_size_every_row(name):
 
 
 def test_fwd_parity_full_size_varlen():
-    """varlen_bf16 at its full size (eight packed sequences, 32768 rows): a
-    seeded quarter of all rows plus the first and last 130 rows of every
-    sequence (its first tile, its ragged tail and the tile before it)."""
+    """varlen_bf16 at its full size (eight packed sequences, 32768 rows) through
+    the launch path the benchmark times: every row and head against the oracle
+    (about 2.7e9 visible pairs, two minutes or so of the oracle on the host's
+    threads)."""
     inp = make_inputs("varlen_bf16")
     o, lse = run_gpu(inp, "varlen_bf16 (full size)")
-    B, T = inp.q.shape[:2]
-    rng = np.random.default_rng(41)
-    rows = set(rng.choice(B * T, size=B * T // 4, replace=False).tolist())
-    for a, b in sequences(inp):
-        rows.update(range(a, min(b, a + 130)))
-        rows.update(range(max(a, b - 130), b))
-    rows = sorted(rows)
-    o_ref, lse_ref = run_oracle(inp, rows=rows)
-    assert_parity(o, lse, o_ref, lse_ref, inp.spec.dtype, rows=rows, what=f"varlen_bf16 rows={len(rows)}")
+    o_ref, lse_ref = run_oracle(inp)
+    assert_parity(o, lse, o_ref, lse_ref, inp.spec.dtype, what="varlen_bf16 every row")
 
 
 # --------------------------------------------------------------------------- invariants
